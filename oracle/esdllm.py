@@ -1,0 +1,366 @@
+"""fp64 reference of the early-skip / partial-recompute denoising loop.
+
+TEST INFRASTRUCTURE (see the package docstring): plain numpy, float64
+arithmetic, one obvious step at a time.  Library primitives used as steps:
+``numpy.matmul`` (dense products), ``numpy.exp/sqrt/sin/cos``, ``numpy.argsort``
+with a stable key (selection).  Nothing is fused, blocked or reordered beyond
+what the definitions state.
+
+Where a floating-point value decides an integer (top-k selection, unmasking,
+argmax) the decision is taken on the value rounded to float32, the precision
+the GPU kernels decide in.
+
+Model (a bidirectional pre-RMSNorm transformer; the pages only say the whole
+sequence is reprocessed each step, ES-dLLM section 1 / DyLLM section 1):
+
+    n(x)  = x / sqrt(mean(x^2) + eps) * g
+    q,k,v = n(x) Wq^T, n(x) Wk^T, n(x) Wv^T ;  q,k rotated by RoPE at the
+            token's absolute position (rotate-half pairs (j, j + dh/2),
+            angle pos * base^(-2j/dh))
+    h     = x + softmax(q k^T / sqrt(dh)) v Wo^T   (per head, all valid keys)
+    y     = h + (silu(n(h) Wg^T) * n(h) Wu^T) Wd^T
+    logits= n_final(x_L) Wlm^T
+
+Readings taken where the pages are silent or disagree (each is repeated in the
+function that uses it):
+
+* The varied tensor H in eq. I is the *input hidden state of the skip layer s*
+  (the pages allow hidden states, keys or values).  H^(t-1) is the previous
+  step's value for every row: layers below s run on all rows every step.
+* c^(t-1) is the cached maximum softmax probability of every row (stale for
+  rows skipped at the previous step); it enters eq. I with a + sign as printed
+  (one page's prose says confident tokens change less; the formula wins).
+* k = ceil(keep * |S|) on the sequence's valid length, computed exactly from
+  the float32 keep value, clamped to [1, |S|].  Ties in the score go to the
+  lower index; the selected set is returned in ascending index order.
+* A refresh step (every row through every layer) runs at each block's first
+  step, and every ``refresh_interval`` steps inside a block when non-zero.
+* Selected rows write their fresh K/V into the layer's cache *before*
+  attention; skipped rows' K/V, confidence, argmax and final hidden state are
+  reused untouched.
+* Unmasking takes, among still-masked positions of the current block, the n
+  highest cached confidences (lower index on ties) and writes the cached argmax.
+* The tiny workload's own text defines a second score: relative L2 change plus
+  (1 - c).  DyLLM's saliency (cosine similarity) gives a third: 1 - cos.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+__all__ = [
+    "rms_norm", "rope", "attention", "silu", "layer_forward", "lm_logits",
+    "conf_argmax", "score_rows", "keep_count", "select_topk", "select_threshold",
+    "unmask", "SeqState", "init_state", "denoise_step", "decode",
+    "is_refresh_step", "FLT_MIN",
+]
+
+F64 = np.float64
+FLT_MIN = float(np.finfo(np.float32).tiny)   # smallest normal float32
+
+
+# ----------------------------------------------------------------------------
+# Model pieces
+# ----------------------------------------------------------------------------
+
+def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """Row-wise RMSNorm: x / sqrt(mean(x^2) + eps) * g."""
+    x = np.asarray(x, F64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(g, F64)
+
+
+def rope(x: np.ndarray, pos: np.ndarray, n_heads: int, head_dim: int, base: float) -> np.ndarray:
+    """Rotary position embedding, rotate-half form, per head.
+
+    For pair j in [0, dh/2): theta = pos * base^(-2j/dh);
+    (x_j, x_{j+dh/2}) -> (x_j cos - x_{j+dh/2} sin, x_{j+dh/2} cos + x_j sin).
+    """
+    x = np.asarray(x, F64)
+    n = x.shape[0]
+    half = head_dim // 2
+    j = np.arange(half, dtype=F64)
+    inv_freq = np.power(F64(base), -2.0 * j / head_dim)
+    ang = np.asarray(pos, F64)[:, None] * inv_freq[None, :]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    xh = x.reshape(n, n_heads, head_dim)
+    x1, x2 = xh[..., :half], xh[..., half:]
+    out = np.empty_like(xh)
+    out[..., :half] = x1 * c - x2 * s
+    out[..., half:] = x2 * c + x1 * s
+    return out.reshape(n, n_heads * head_dim)
+
+
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, n_heads: int, head_dim: int) -> np.ndarray:
+    """Bidirectional multi-head attention of query rows against all given keys.
+
+    q: [n, H*dh]; K, V: [m, H*dh] (the sequence's valid keys).  Per head:
+    softmax over keys of q.k / sqrt(dh) (max-subtracted), times V.
+    """
+    q = np.asarray(q, F64)
+    K = np.asarray(K, F64)
+    V = np.asarray(V, F64)
+    n = q.shape[0]
+    out = np.empty((n, n_heads * head_dim), F64)
+    scale = 1.0 / math.sqrt(head_dim)
+    for h in range(n_heads):
+        sl = slice(h * head_dim, (h + 1) * head_dim)
+        s = (q[:, sl] @ K[:, sl].T) * scale          # [n, m]
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, sl] = p @ V[:, sl]
+    return out
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def layer_forward(x: np.ndarray, pos: np.ndarray, lw: dict, K_cache: np.ndarray,
+                  V_cache: np.ndarray, n_valid: int, dims) -> np.ndarray:
+    """One layer on the rows ``x`` (positions ``pos``) of one sequence.
+
+    The rows' fresh K/V are written into ``K_cache``/``V_cache`` (this layer,
+    this sequence, [S, d]) at ``pos`` *before* attention, so every row attends
+    over keys 0..n_valid-1 with fresh values for the rows recomputed now and
+    cached values for the rest (ES-dLLM section 2B: in-place cache update for
+    selected tokens, direct reuse for skipped ones).
+    """
+    H, dh = dims.n_heads, dims.head_dim
+    xn = rms_norm(x, lw["attn_norm"], dims.rms_eps)
+    q = xn @ np.asarray(lw["wq"], F64).T
+    k = xn @ np.asarray(lw["wk"], F64).T
+    v = xn @ np.asarray(lw["wv"], F64).T
+    q = rope(q, pos, H, dh, dims.rope_base)
+    k = rope(k, pos, H, dh, dims.rope_base)
+    K_cache[pos] = k
+    V_cache[pos] = v
+    o = attention(q, K_cache[:n_valid], V_cache[:n_valid], H, dh)
+    h = x + o @ np.asarray(lw["wo"], F64).T
+    hn = rms_norm(h, lw["ffn_norm"], dims.rms_eps)
+    a = silu(hn @ np.asarray(lw["w_gate"], F64).T) * (hn @ np.asarray(lw["w_up"], F64).T)
+    return h + a @ np.asarray(lw["w_down"], F64).T
+
+
+def lm_logits(x: np.ndarray, final_norm: np.ndarray, lm_head: np.ndarray, eps: float) -> np.ndarray:
+    return rms_norm(x, final_norm, eps) @ np.asarray(lm_head, F64).T
+
+
+def conf_argmax(logits: np.ndarray):
+    """Confidence = maximum softmax probability = 1 / sum_v exp(l_v - max l).
+
+    The argmax is taken on the logits rounded to float32, lowest id on ties.
+    Returns (conf fp64 [n], argmax int64 [n]).
+    """
+    logits = np.asarray(logits, F64)
+    m = logits.max(axis=1, keepdims=True)
+    conf = 1.0 / np.exp(logits - m).sum(axis=1)
+    l32 = logits.astype(np.float32)
+    amax = np.argmax(l32, axis=1).astype(np.int64)   # first maximum = lowest id
+    return conf, amax
+
+
+# ----------------------------------------------------------------------------
+# Importance score and selection (ES-dLLM section 2A/2B, DyLLM section 2A)
+# ----------------------------------------------------------------------------
+
+def score_rows(kind: str, x_cur: np.ndarray, h_prev: np.ndarray, conf: np.ndarray,
+               alpha: float = 0.5) -> np.ndarray:
+    """Per-row importance score, fp64.
+
+    esdllm        : alpha*c + (1-alpha) * ||x - h||_1 / (sqrt(d) * ||h||_2)   (eq. I)
+    rell2_invconf : ||x - h||_2 / ||h||_2 + (1 - c)      (the tiny workload's text)
+    cosine        : 1 - x.h / (||x||_2 ||h||_2)            (DyLLM saliency)
+
+    Denominators are floored at FLT_MIN so an all-zero cached row scores finite.
+    """
+    x = np.asarray(x_cur, F64)
+    h = np.asarray(h_prev, F64)
+    c = np.asarray(conf, F64)
+    d = x.shape[1]
+    diff = x - h
+    if kind == "esdllm":
+        l1 = np.abs(diff).sum(axis=1)
+        den = np.maximum(math.sqrt(d) * np.sqrt((h * h).sum(axis=1)), FLT_MIN)
+        return alpha * c + (1.0 - alpha) * l1 / den
+    if kind == "rell2_invconf":
+        num = np.sqrt((diff * diff).sum(axis=1))
+        den = np.maximum(np.sqrt((h * h).sum(axis=1)), FLT_MIN)
+        return num / den + (1.0 - c)
+    if kind == "cosine":
+        den = np.maximum(np.sqrt((x * x).sum(axis=1)) * np.sqrt((h * h).sum(axis=1)), FLT_MIN)
+        return 1.0 - (x * h).sum(axis=1) / den
+    raise ValueError(f"unknown score kind {kind!r}")
+
+
+def keep_count(keep: float, n: int) -> int:
+    """k = (1 - r)|S| with keep = 1 - r: ceil(keep * n), clamped to [1, n].
+
+    ``keep`` is taken as a float32 (the value a caller passes over the C ABI);
+    the product of a float32 and an integer below 2^29 is exact in float64,
+    so the ceiling has no rounding drift.
+    """
+    if n <= 0:
+        return 0
+    k = math.ceil(float(np.float32(keep)) * n)
+    return max(1, min(n, k))
+
+
+def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k highest scores (decided in float32), ascending.
+
+    Order key (-score, index): among equal scores the lower index is taken.
+    A NaN score is an error here (the GPU ranks NaN last).
+    """
+    s32 = np.asarray(scores, F64).astype(np.float32)
+    assert not np.isnan(s32).any(), "NaN importance score"
+    n = s32.shape[0]
+    order = np.lexsort((np.arange(n), -s32.astype(F64)))   # primary: -score, then index
+    return np.sort(order[:k]).astype(np.int64)
+
+
+def select_threshold(scores: np.ndarray, tau: float) -> np.ndarray:
+    """Rows whose float32 score is strictly above float32 tau, ascending."""
+    s32 = np.asarray(scores, F64).astype(np.float32)
+    assert not np.isnan(s32).any(), "NaN importance score"
+    return np.nonzero(s32 > np.float32(tau))[0].astype(np.int64)
+
+
+def unmask(masked: np.ndarray, conf: np.ndarray, lo: int, hi: int, n: int) -> np.ndarray:
+    """Positions to unmask: the n most confident still-masked ones in [lo, hi).
+
+    Decided on float32 confidence, lower index on ties; returned ascending.
+    """
+    cand = np.nonzero(masked[lo:hi])[0] + lo
+    if cand.size == 0 or n <= 0:
+        return np.zeros(0, np.int64)
+    c32 = np.asarray(conf, F64)[cand].astype(np.float32)
+    order = np.lexsort((cand, -c32.astype(F64)))
+    return np.sort(cand[order[:min(n, cand.size)]]).astype(np.int64)
+
+
+# ----------------------------------------------------------------------------
+# Decode state and the denoising step
+# ----------------------------------------------------------------------------
+
+@dataclass
+class SeqState:
+    """Per-sequence caches (all rows of the sequence, valid length n)."""
+    tokens: np.ndarray            # [n] int64
+    masked: np.ndarray            # [n] bool
+    prompt_len: int
+    conf: np.ndarray              # [n] fp64, max softmax probability
+    argmax: np.ndarray            # [n] int64
+    h_prev: np.ndarray            # [n, d] skip-layer input of the previous step
+    K: List[np.ndarray]           # per layer [n, d] (rotated keys)
+    V: List[np.ndarray]           # per layer [n, d]
+    h_final: np.ndarray           # [n, d] last layer output (before final norm)
+    logits: Optional[np.ndarray] = None   # [n, V] when kept
+
+
+def init_state(prompt: np.ndarray, gen_len: int, dims, mask_id: Optional[int] = None,
+               keep_logits: bool = False) -> SeqState:
+    P = int(len(prompt))
+    n = P + gen_len
+    mid = dims.vocab - 1 if mask_id is None else mask_id
+    tokens = np.concatenate([np.asarray(prompt, np.int64), np.full(gen_len, mid, np.int64)])
+    masked = np.zeros(n, bool)
+    masked[P:] = True
+    d = dims.d
+    return SeqState(tokens=tokens, masked=masked, prompt_len=P,
+                    conf=np.zeros(n, F64), argmax=np.zeros(n, np.int64),
+                    h_prev=np.zeros((n, d), F64),
+                    K=[np.zeros((n, d), F64) for _ in range(dims.n_layers)],
+                    V=[np.zeros((n, d), F64) for _ in range(dims.n_layers)],
+                    h_final=np.zeros((n, d), F64),
+                    logits=np.zeros((n, dims.vocab), F64) if keep_logits else None)
+
+
+def is_refresh_step(step: int, sched) -> bool:
+    """Refresh at each block's first step, and every refresh_interval steps."""
+    sib = step % sched.steps_per_block
+    if sib == 0:
+        return True
+    return sched.refresh_interval > 0 and sib % sched.refresh_interval == 0
+
+
+@dataclass
+class StepInfo:
+    refresh: bool
+    selected: np.ndarray          # rows recomputed in layers >= s (ascending)
+    scores: Optional[np.ndarray]  # fp64 scores (skip steps only)
+    unmasked: np.ndarray          # positions unmasked by this step
+
+
+def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = "topk",
+                 threshold: float = 0.0, force_refresh: Optional[bool] = None,
+                 keep: Optional[float] = None) -> StepInfo:
+    """One denoising step of one sequence (ES-dLLM section 2B).
+
+    Refresh step: every row through every layer; all caches rewritten.
+    Skip step: layers [0, s) on all rows give X_s; score X_s against h_prev with
+    the cached confidence; keep the top-k (or threshold) rows; h_prev <- X_s for
+    all rows; layers [s, L) on the kept rows only, each layer scattering their
+    fresh K/V into its cache first; LM head on the kept rows; scatter conf,
+    argmax, h_final (and logits) for kept rows only.  Then unmask.
+    """
+    n = st.tokens.shape[0]
+    s_layer = sched.skip_layer
+    L = dims.n_layers
+    refresh = is_refresh_step(step, sched) if force_refresh is None else force_refresh
+    keep = sched.keep if keep is None else keep
+    pos_all = np.arange(n, dtype=np.int64)
+
+    x = np.asarray(model["embed"], F64)[st.tokens]          # [n, d]
+    for li in range(s_layer):
+        x = layer_forward(x, pos_all, model["layers"][li], st.K[li], st.V[li], n, dims)
+
+    scores = None
+    if refresh:
+        sel = pos_all
+    else:
+        scores = score_rows(sched.score, x, st.h_prev, st.conf, sched.alpha)
+        if mode == "topk":
+            sel = select_topk(scores, keep_count(keep, n))
+        else:
+            sel = select_threshold(scores, threshold)
+    st.h_prev = x.copy()                                      # all rows, every step
+
+    xr = x[sel]
+    for li in range(s_layer, L):
+        xr = layer_forward(xr, sel, model["layers"][li], st.K[li], st.V[li], n, dims)
+
+    if sel.size:
+        logits = lm_logits(xr, model["final_norm"], model["lm_head"], dims.rms_eps)
+        conf, amax = conf_argmax(logits)
+        st.conf[sel] = conf
+        st.argmax[sel] = amax
+        st.h_final[sel] = xr
+        if st.logits is not None:
+            st.logits[sel] = logits
+
+    b = step // sched.steps_per_block
+    lo = st.prompt_len + b * sched.block_len
+    hi = min(lo + sched.block_len, n)
+    pos = unmask(st.masked, st.conf, lo, hi, sched.per_step)
+    st.tokens[pos] = st.argmax[pos]
+    st.masked[pos] = False
+    return StepInfo(refresh=refresh, selected=sel, scores=scores, unmasked=pos)
+
+
+def decode(model: dict, dims, prompt: np.ndarray, sched, n_steps: Optional[int] = None,
+           vanilla: bool = False, keep_logits: bool = False, mode: str = "topk",
+           threshold: float = 0.0):
+    """Run the decode loop.  ``vanilla`` refreshes every step (full recompute)."""
+    st = init_state(prompt, sched.gen_len, dims, keep_logits=keep_logits)
+    infos = []
+    T = sched.steps if n_steps is None else n_steps
+    for t in range(T):
+        infos.append(denoise_step(model, dims, st, t, sched, mode=mode, threshold=threshold,
+                                  force_refresh=True if vanilla else None))
+    return st, infos

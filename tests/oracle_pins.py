@@ -1,0 +1,374 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a
+hand-worked value (``tests/golden/``), a closed form, a brute force on tiny
+inputs, a torch library routine (``libref``), or an invariant the pages fix.
+They look the oracle up through the module object at call time, so the
+planted-mistake test can patch a function and check that some pin fails.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import libref
+import workloads
+from oracle import esdllm as E
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "score_examples.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def micro_dims(n_layers=3):
+    return workloads.ModelDims(d=32, n_heads=2, head_dim=16, d_ffn=48, vocab=40, n_layers=n_layers)
+
+
+def np_model(dims, seed=5):
+    m = workloads.make_model(dims, seed, "f32", "cpu")
+    out = {"embed": workloads.host_f64(m["embed"]), "final_norm": workloads.host_f64(m["final_norm"]),
+           "lm_head": workloads.host_f64(m["lm_head"]), "layers": []}
+    for lw in m["layers"]:
+        out["layers"].append({k: workloads.host_f64(v) for k, v in lw.items()})
+    return out
+
+
+def micro_sched(**kw):
+    base = dict(gen_len=12, block_len=6, steps=6, skip_layer=1, keep=0.35, score="esdllm")
+    base.update(kw)
+    return workloads.Schedule(**base)
+
+
+def close(a, b, rtol=1e-12, atol=1e-12):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    err = np.abs(a - b).max() if a.size else 0.0
+    assert err <= atol + rtol * (np.abs(b).max() if b.size else 0.0), f"max abs err {err}"
+
+
+# --------------------------------------------------------------------------
+# score, selection, unmasking
+# --------------------------------------------------------------------------
+
+def pin_score_golden():
+    for c in golden()["cases"]:
+        x = np.array([c["x"]], float)
+        h = np.array([c["h"]], float)
+        for kind in ("esdllm", "rell2_invconf", "cosine"):
+            got = E.score_rows(kind, x, h, np.array([c["c"]]), c["alpha"])[0]
+            assert abs(got - c[kind]) < 1e-12, (kind, c["why"], got, c[kind])
+
+
+def pin_score_closed_forms():
+    rng = np.random.default_rng(11)
+    n, d = 7, 24
+    h = rng.normal(size=(n, d))
+    c = rng.uniform(size=n)
+    # no change: only the confidence terms remain
+    close(E.score_rows("esdllm", h, h, c, 0.5), 0.5 * c)
+    close(E.score_rows("rell2_invconf", h, h, c), 1.0 - c)
+    close(E.score_rows("cosine", h, h, c), np.zeros(n), atol=1e-14)
+    # constant rows a*1 vs b*1: L1/(sqrt(d)*L2) = |a-b|/|b| = relative L2
+    a, b = 1.75, -0.5
+    xs, hs = np.full((1, d), a), np.full((1, d), b)
+    close(E.score_rows("esdllm", xs, hs, np.zeros(1), 0.0), [abs(a - b) / abs(b)])
+    close(E.score_rows("rell2_invconf", xs, hs, np.ones(1)), [abs(a - b) / abs(b)])
+    # pure scaling x = (1+eps) h: relative L2 = |eps|, cosine distance 0
+    for eps in (0.3, -0.2):
+        close(E.score_rows("rell2_invconf", (1 + eps) * h, h, np.ones(n)), np.full(n, abs(eps)))
+        close(E.score_rows("cosine", (1 + eps) * h, h, c), np.zeros(n), atol=1e-14)
+    # the variation term of eq. I is scale invariant; alpha=1 keeps only c
+    x = h + rng.normal(size=(n, d))
+    close(E.score_rows("esdllm", 3 * x, 3 * h, c, 0.0), E.score_rows("esdllm", x, h, c, 0.0))
+    close(E.score_rows("esdllm", x, h, c, 1.0), c)
+    # a zero cached row stays finite (floored denominator)
+    z = E.score_rows("esdllm", np.ones((1, 4)), np.zeros((1, 4)), np.zeros(1))
+    assert np.isfinite(z).all() and z[0] > 1e30
+
+
+def pin_keep_count():
+    for c in golden()["keep_count"]:
+        assert E.keep_count(c["keep"], c["n"]) == c["k"], c
+    assert E.keep_count(0.5, 0) == 0
+
+
+def _brute_topk(s, k):
+    s32 = np.asarray(s, np.float64).astype(np.float32)
+    order = sorted(range(len(s32)), key=lambda i: (-float(s32[i]), i))
+    return sorted(order[:k])
+
+
+def pin_select_topk():
+    for c in golden()["topk"]:
+        assert E.select_topk(np.array(c["scores"]), c["k"]).tolist() == c["selected"], c
+    rng = np.random.default_rng(3)
+    for trial in range(300):
+        n = int(rng.integers(1, 17))
+        s = rng.choice(np.array([0.1, 0.2, 0.2, 0.5, 0.9, -1.0]), size=n) if trial % 2 else rng.normal(size=n)
+        for k in range(0, n + 1):
+            got = E.select_topk(s, k).tolist()
+            assert got == _brute_topk(s, k), (s, k, got)
+    # exhaustive over all 3-valued score vectors of length 5
+    for s in itertools.product((0.0, 0.5, 1.0), repeat=5):
+        for k in range(6):
+            assert E.select_topk(np.array(s), k).tolist() == _brute_topk(s, k)
+
+
+def pin_select_threshold():
+    rng = np.random.default_rng(4)
+    for _ in range(100):
+        n = int(rng.integers(0, 20))
+        s = rng.normal(size=n)
+        tau = float(rng.normal())
+        want = [i for i in range(n) if np.float32(s[i]) > np.float32(tau)]
+        assert E.select_threshold(s, tau).tolist() == want
+
+
+def pin_unmask():
+    for c in golden()["unmask"]:
+        got = E.unmask(np.array(c["masked"]), np.array(c["conf"]), c["lo"], c["hi"], c["n"]).tolist()
+        assert got == c["positions"], (c, got)
+    rng = np.random.default_rng(6)
+    for _ in range(200):
+        n = int(rng.integers(1, 15))
+        masked = rng.uniform(size=n) < 0.6
+        conf = rng.choice(np.array([0.1, 0.3, 0.3, 0.8]), size=n)
+        lo = int(rng.integers(0, n))
+        hi = int(rng.integers(lo, n + 1))
+        m = int(rng.integers(0, 5))
+        cand = [i for i in range(lo, hi) if masked[i]]
+        want = sorted(sorted(cand, key=lambda i: (-float(np.float32(conf[i])), i))[:m])
+        assert E.unmask(masked, conf, lo, hi, m).tolist() == want
+
+
+# --------------------------------------------------------------------------
+# model pieces vs torch library routines and closed forms
+# --------------------------------------------------------------------------
+
+def pin_rms_norm():
+    rng = np.random.default_rng(7)
+    x = rng.normal(size=(5, 64)) * 3
+    g = rng.normal(size=64)
+    close(E.rms_norm(x, g, 1e-5), libref.rms(libref.t(x), libref.t(g), 1e-5).numpy())
+    y = E.rms_norm(x, np.ones(64), 1e-5)
+    ms = (x * x).mean(axis=1)
+    close(np.sqrt((y * y).mean(axis=1)), np.sqrt(ms / (ms + 1e-5)))
+    a = 0.01
+    close(E.rms_norm(np.full((1, 8), a), np.ones(8), 1e-5), np.full((1, 8), a / math.sqrt(a * a + 1e-5)))
+
+
+def pin_rope():
+    rng = np.random.default_rng(8)
+    H, dh = 3, 8
+    x = rng.normal(size=(6, H * dh))
+    pos = np.array([0, 1, 2, 5, 77, 4095])
+    y = E.rope(x, pos, H, dh, 10000.0)
+    close(y[0], x[0])                                      # position 0 is the identity
+    close(np.linalg.norm(y.reshape(6, H, dh), axis=2), np.linalg.norm(x.reshape(6, H, dh), axis=2))
+    close(y, libref.rope(libref.t(x), pos, H, dh, 10000.0).numpy())
+    # q.k depends only on the position difference
+    q, k = rng.normal(size=(1, dh)), rng.normal(size=(1, dh))
+    dots = [(E.rope(q, np.array([p + 9]), 1, dh, 10000.0) @ E.rope(k, np.array([p]), 1, dh, 10000.0).T).item()
+            for p in (0, 3, 100)]
+    close(dots, [dots[0]] * 3)
+    # head_dim 2: a plain rotation by angle pos
+    z = E.rope(np.array([[1.0, 0.0]]), np.array([1]), 1, 2, 10000.0)
+    close(z, [[math.cos(1.0), math.sin(1.0)]])
+
+
+def pin_attention():
+    rng = np.random.default_rng(9)
+    H, dh = 2, 8
+    q = rng.normal(size=(4, H * dh))
+    K = rng.normal(size=(9, H * dh))
+    V = rng.normal(size=(9, H * dh))
+    close(E.attention(q, K, V, H, dh), libref.attn(libref.t(q), libref.t(K), libref.t(V), H, dh).numpy())
+    close(E.attention(q, K[:1], V[:1], H, dh), np.repeat(V[:1], 4, axis=0))     # one key
+    Ke = np.repeat(K[:1], 9, axis=0)
+    close(E.attention(q, Ke, V, H, dh), np.repeat(V.mean(axis=0, keepdims=True), 4, axis=0))
+    close(E.attention(np.zeros_like(q), K, V, H, dh), np.repeat(V.mean(axis=0, keepdims=True), 4, axis=0))
+
+
+def pin_conf_argmax():
+    V = 37
+    c, a = E.conf_argmax(np.zeros((2, V)))
+    close(c, [1.0 / V] * 2)
+    assert a.tolist() == [0, 0]
+    rng = np.random.default_rng(10)
+    lg = rng.normal(size=(6, V)) * 4
+    lg[3, 5] = lg[3, 20] = lg[3].max() + 1.0     # exact tie: lowest id wins
+    c, a = E.conf_argmax(lg)
+    tl = torch.as_tensor(lg)
+    close(c, torch.softmax(tl, dim=1).max(dim=1).values.numpy())
+    assert a[3] == 5
+    assert a.tolist()[:3] == tl[:3].argmax(dim=1).tolist()
+    assert np.all(c >= 1.0 / V) and np.all(c <= 1.0)
+
+
+def pin_layer_full():
+    dims = micro_dims()
+    m = np_model(dims)
+    rng = np.random.default_rng(12)
+    n = 11
+    x = rng.normal(size=(n, dims.d))
+    K = np.zeros((n, dims.d))
+    V = np.zeros((n, dims.d))
+    y = E.layer_forward(x, np.arange(n), m["layers"][1], K, V, n, dims)
+    close(y, libref.full_layer(libref.t(x), m["layers"][1], dims).numpy(), rtol=1e-11)
+
+
+def pin_layer_partial():
+    """Selected rows attend over a cache whose other rows are stale."""
+    dims = micro_dims()
+    m = np_model(dims)
+    rng = np.random.default_rng(13)
+    n = 13
+    rows = np.array([1, 4, 5, 11])
+    x = rng.normal(size=(len(rows), dims.d))
+    K0 = rng.normal(size=(n, dims.d))
+    V0 = rng.normal(size=(n, dims.d))
+    K, V = K0.copy(), V0.copy()
+    y = E.layer_forward(x, rows, m["layers"][2], K, V, n, dims)
+    y_ref, K_ref, V_ref = libref.partial_layer(libref.t(x), rows, m["layers"][2], K0, V0, dims)
+    close(y, y_ref.numpy(), rtol=1e-11)
+    close(K, K_ref.numpy())
+    close(V, V_ref.numpy())
+    other = np.setdiff1d(np.arange(n), rows)
+    assert np.array_equal(K[other], K0[other]) and np.array_equal(V[other], V0[other])
+
+
+# --------------------------------------------------------------------------
+# the decode loop: invariants the pages fix
+# --------------------------------------------------------------------------
+
+def _micro_run(sched, vanilla=False, seed=5, n_steps=None):
+    dims = micro_dims()
+    m = np_model(dims, seed)
+    g = torch.Generator().manual_seed(seed)
+    prompt = torch.randint(0, dims.vocab, (9,), generator=g).numpy()
+    st, infos = E.decode(m, dims, prompt, sched, vanilla=vanilla, keep_logits=True, n_steps=n_steps)
+    return dims, m, prompt, st, infos
+
+
+def pin_refresh_is_full_forward():
+    sched = micro_sched()
+    dims = micro_dims()
+    m = np_model(dims)
+    prompt = np.arange(9) % dims.vocab
+    st = E.init_state(prompt, sched.gen_len, dims, keep_logits=True)
+    tokens0 = st.tokens.copy()
+    E.denoise_step(m, dims, st, 0, sched)
+    xs = libref.forward(tokens0, m, dims, n_layers=sched.skip_layer).numpy()
+    xL = libref.forward(tokens0, m, dims).numpy()
+    lg = libref.logits(libref.t(xL), m, dims)
+    close(st.h_prev, xs, rtol=1e-11)
+    close(st.h_final, xL, rtol=1e-11)
+    close(st.logits, lg.numpy(), rtol=1e-10)
+    close(st.conf, torch.softmax(lg, 1).max(1).values.numpy(), rtol=1e-10)
+
+
+def pin_skip_step_semantics():
+    """A skip step: h_prev <- X_s for all rows; the top-k by eq. I are the rows
+    recomputed; skipped rows keep every cached byte; recomputed rows follow the
+    stale-cache partial layers."""
+    sched = micro_sched()
+    dims = micro_dims()
+    m = np_model(dims)
+    prompt = (np.arange(9) * 7) % dims.vocab
+    st = E.init_state(prompt, sched.gen_len, dims, keep_logits=True)
+    E.denoise_step(m, dims, st, 0, sched)                    # refresh
+    before = {k: (getattr(st, k).copy()) for k in ("conf", "argmax", "h_final", "logits", "h_prev")}
+    Kb = [k.copy() for k in st.K]
+    Vb = [v.copy() for v in st.V]
+    tokens1 = st.tokens.copy()
+    info = E.denoise_step(m, dims, st, 1, sched)
+    assert not info.refresh
+    n = len(tokens1)
+    k = E.keep_count(sched.keep, n)
+    sel = info.selected
+    assert len(sel) == k and np.all(np.diff(sel) > 0) and sel[0] >= 0 and sel[-1] < n
+    # h_prev is the fresh skip-layer input of every row
+    xs = libref.forward(tokens1, m, dims, n_layers=sched.skip_layer)
+    close(st.h_prev, xs.numpy(), rtol=1e-11)
+    # the selection is the brute-force top-k of eq. I (scores recomputed in torch)
+    d = dims.d
+    hp = libref.t(before["h_prev"])
+    sc = 0.5 * libref.t(before["conf"]) + 0.5 * (xs - hp).abs().sum(1) / (math.sqrt(d) * hp.norm(dim=1))
+    assert sel.tolist() == _brute_topk(sc.numpy(), k)
+    # skipped rows: bit-identical caches
+    other = np.setdiff1d(np.arange(n), sel)
+    for key in ("conf", "argmax", "h_final", "logits"):
+        assert np.array_equal(getattr(st, key)[other], before[key][other]), key
+    for li in range(sched.skip_layer, dims.n_layers):
+        assert np.array_equal(st.K[li][other], Kb[li][other])
+        assert np.array_equal(st.V[li][other], Vb[li][other])
+    # recomputed rows: partial layers against stale caches, by torch
+    xr = xs[torch.as_tensor(sel)]
+    for li in range(sched.skip_layer, dims.n_layers):
+        xr, Kn, Vn = libref.partial_layer(xr, sel, m["layers"][li], Kb[li], Vb[li], dims)
+        close(st.K[li], Kn.numpy(), rtol=1e-11)
+        close(st.V[li], Vn.numpy(), rtol=1e-11)
+    close(st.h_final[sel], xr.numpy(), rtol=1e-11)
+    lg = libref.logits(xr, m, dims)
+    close(st.conf[sel], torch.softmax(lg, 1).max(1).values.numpy(), rtol=1e-10)
+
+
+def pin_keep_all_equals_vanilla():
+    """keep = 100% is full recomputation, bit for bit, over a whole decode."""
+    sched = micro_sched(keep=1.0)
+    _, _, _, st_a, inf_a = _micro_run(sched)
+    _, _, _, st_b, inf_b = _micro_run(sched, vanilla=True)
+    assert any(not i.refresh for i in inf_a) and all(i.refresh for i in inf_b)
+    for key in ("tokens", "masked", "conf", "argmax", "h_prev", "h_final", "logits"):
+        assert np.array_equal(getattr(st_a, key), getattr(st_b, key)), key
+    for li in range(len(st_a.K)):
+        assert np.array_equal(st_a.K[li], st_b.K[li]) and np.array_equal(st_a.V[li], st_b.V[li])
+
+
+def pin_unmask_schedule():
+    for sched in (micro_sched(), micro_sched(block_len=12, steps=4), micro_sched(keep=0.1, refresh_interval=2)):
+        dims, m, prompt, st, infos = _micro_run(sched)
+        P = len(prompt)
+        assert np.array_equal(st.tokens[:P], prompt)
+        assert not st.masked.any()
+        seen = set()
+        for t, inf in enumerate(infos):
+            assert len(inf.unmasked) == sched.per_step
+            b = t // sched.steps_per_block
+            lo, hi = P + b * sched.block_len, P + (b + 1) * sched.block_len
+            assert all(lo <= p < hi for p in inf.unmasked)
+            seen.update(inf.unmasked.tolist())
+            sib = t % sched.steps_per_block
+            assert inf.refresh == (sib == 0 or (sched.refresh_interval and sib % sched.refresh_interval == 0))
+        assert seen == set(range(P, P + sched.gen_len))
+
+
+def pin_fresh_cache_skip_is_exact():
+    """With caches fresh and no token changed, recomputed rows equal the full
+    result and the score reduces to its confidence term."""
+    sched = workloads.Schedule(gen_len=12, block_len=12, steps=12, skip_layer=1, keep=0.5, score="esdllm")
+    dims = micro_dims()
+    m = np_model(dims)
+    st = E.init_state(np.arange(9), sched.gen_len, dims, keep_logits=True)
+    tokens0, masked0 = st.tokens.copy(), st.masked.copy()
+    E.denoise_step(m, dims, st, 0, sched)                    # refresh, then unmasks
+    full = st.h_final.copy()
+    conf0 = st.conf.copy()
+    st.tokens[:] = tokens0                                  # undo the unmasking only
+    st.masked[:] = masked0
+    info = E.denoise_step(m, dims, st, 1, sched)
+    assert not info.refresh
+    close(info.scores, 0.5 * conf0, rtol=1e-14)
+    close(st.h_final[info.selected], full[info.selected], rtol=1e-11)
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,131 @@
+"""Planted mistakes in the oracle must each make some pin fail.
+
+Every mutant below is a plausible slip (a dropped term, a wrong sign, a wrong
+index or tie rule, a cache written after use, a transposed operand).  The
+mutant is planted in the oracle module, on the CPU, for the duration of one
+test; the test passes only if at least one pin raises.
+"""
+import numpy as np
+import pytest
+
+import oracle_pins
+from oracle import esdllm as E
+
+_orig = {name: getattr(E, name) for name in ("score_rows", "rms_norm", "rope", "attention", "select_topk",
+                                             "unmask", "keep_count", "conf_argmax", "silu", "layer_forward",
+                                             "select_threshold")}
+
+
+def m_score_l2(kind, x, h, c, alpha=0.5):          # L2 instead of L1 in eq. I
+    if kind != "esdllm":
+        return _orig["score_rows"](kind, x, h, c, alpha)
+    d = x.shape[1]
+    num = np.sqrt(((x - h) ** 2).sum(1))
+    return alpha * c + (1 - alpha) * num / np.maximum(np.sqrt(d) * np.sqrt((h * h).sum(1)), E.FLT_MIN)
+
+
+def m_score_csign(kind, x, h, c, alpha=0.5):       # confidence enters with the wrong sign
+    return _orig["score_rows"](kind, x, h, -np.asarray(c) if kind == "esdllm" else c, alpha)
+
+
+def m_score_nosqrtd(kind, x, h, c, alpha=0.5):     # sqrt(d) dropped from the denominator
+    s = _orig["score_rows"](kind, x, h, c, alpha)
+    if kind == "esdllm":
+        s = alpha * np.asarray(c) + (s - alpha * np.asarray(c)) * np.sqrt(x.shape[1])
+    return s
+
+
+def m_rms_noeps(x, g, eps):
+    return _orig["rms_norm"](x, g, 0.0)
+
+
+def m_rope_sign(x, pos, H, dh, base):              # rotation by -theta
+    return _orig["rope"](x, -np.asarray(pos), H, dh, base)
+
+
+def m_rope_pairs(x, pos, H, dh, base):             # wrong frequency index (j+1)
+    return _orig["rope"](x, pos, H, dh, base * 1.5)
+
+
+def m_attn_noscale(q, K, V, H, dh):
+    return _orig["attention"](np.asarray(q) * np.sqrt(dh), K, V, H, dh)
+
+
+def m_attn_swap(q, K, V, H, dh):                   # keys and values transposed in role
+    return _orig["attention"](q, V, K, H, dh)
+
+
+def m_topk_hi_tie(scores, k):                      # ties to the higher index
+    s32 = np.asarray(scores).astype(np.float32)
+    n = len(s32)
+    order = np.lexsort((-np.arange(n), -s32.astype(np.float64)))
+    return np.sort(order[:k])
+
+
+def m_topk_low(scores, k):                         # the k lowest instead of the highest
+    return _orig["select_topk"](-np.asarray(scores), k)
+
+
+def m_unmask_noblock(masked, conf, lo, hi, n):     # ignores the block boundary
+    return _orig["unmask"](masked, conf, 0, len(masked), n)
+
+
+def m_unmask_lowconf(masked, conf, lo, hi, n):
+    return _orig["unmask"](masked, -np.asarray(conf), lo, hi, n)
+
+
+def m_keep_floor(keep, n):
+    return max(1, min(n, int(np.floor(float(np.float32(keep)) * n))))
+
+
+def m_conf_maxlogit(logits):                       # softmax forgotten
+    c, a = _orig["conf_argmax"](logits)
+    return np.asarray(logits).max(1), a
+
+
+def m_silu_sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def m_layer_kv_late(x, pos, lw, K_cache, V_cache, n_valid, dims):   # cache written after attention
+    Kold, Vold = K_cache.copy(), V_cache.copy()
+    _orig["layer_forward"](x, pos, lw, K_cache, V_cache, n_valid, dims)   # fills the fresh rows
+    Knew, Vnew = K_cache.copy(), V_cache.copy()
+    H, dh = dims.n_heads, dims.head_dim
+    xn = E.rms_norm(x, lw["attn_norm"], dims.rms_eps)
+    q = E.rope(xn @ np.asarray(lw["wq"]).T, pos, H, dh, dims.rope_base)
+    o = E.attention(q, Kold[:n_valid], Vold[:n_valid], H, dh)          # stale keys for the fresh rows
+    h = x + o @ np.asarray(lw["wo"]).T
+    hn = E.rms_norm(h, lw["ffn_norm"], dims.rms_eps)
+    K_cache[:], V_cache[:] = Knew, Vnew
+    return h + (E.silu(hn @ np.asarray(lw["w_gate"]).T) * (hn @ np.asarray(lw["w_up"]).T)) @ np.asarray(lw["w_down"]).T
+
+
+def m_threshold_ge(scores, tau):
+    s32 = np.asarray(scores).astype(np.float32)
+    return np.nonzero(s32 >= np.float32(tau) - np.float32(0.05))[0]
+
+
+MUTANTS = [
+    ("score_rows", m_score_l2), ("score_rows", m_score_csign), ("score_rows", m_score_nosqrtd),
+    ("rms_norm", m_rms_noeps), ("rope", m_rope_sign), ("rope", m_rope_pairs),
+    ("attention", m_attn_noscale), ("attention", m_attn_swap),
+    ("select_topk", m_topk_hi_tie), ("select_topk", m_topk_low),
+    ("unmask", m_unmask_noblock), ("unmask", m_unmask_lowconf), ("keep_count", m_keep_floor),
+    ("conf_argmax", m_conf_maxlogit), ("silu", m_silu_sigmoid), ("layer_forward", m_layer_kv_late),
+    ("select_threshold", m_threshold_ge),
+]
+
+
+@pytest.mark.parametrize("name,mutant", MUTANTS, ids=[m.__name__ for _, m in MUTANTS])
+def test_planted_mistake_is_caught(monkeypatch, name, mutant):
+    monkeypatch.setattr(E, name, mutant)
+    failed = []
+    for pin in oracle_pins.PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed.append(pin.__name__)
+        except Exception as e:  # a crash also exposes the mutant
+            failed.append(f"{pin.__name__}:{type(e).__name__}")
+    assert failed, f"no pin caught mutant {mutant.__name__} of {name}"
