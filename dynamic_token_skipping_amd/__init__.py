@@ -1,0 +1,8 @@
+"""Early-skip partial-recompute denoising step for masked-diffusion LLMs on
+AMD Instinct MI355X: a HIP library (libdtsk, C ABI in include/dl.h) and its
+thin Python binding."""
+from ._lib import (DLError, DL_BF16, DL_F32, DL_SCORE_COSINE, DL_SCORE_ESDLLM, DL_SCORE_RELL2_INVCONF,  # noqa: F401
+                   DL_SEL_THRESHOLD, DL_SEL_TOPK, EXPORTS, SelectionTensors, dl_abi_version, dl_denoise_step,
+                   dl_ffn_rows, dl_gather, dl_lm_head_rows, dl_partial_attn, dl_scatter_cache, dl_score_select,
+                   dl_unmask, load, make_dims, workspace, workspace_bytes)
+from .decode import Decoder, DeviceModel, is_refresh_step  # noqa: F401

@@ -1,0 +1,536 @@
+// The C ABI of libdtsk: host-side validation, workspace layout and the
+// orchestration of one denoising step from the kernels of k_rows / k_gemm /
+// k_attn.  Nothing here allocates or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "launch.h"
+
+using namespace dtsk;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dl_status fail(dl_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+#define DL_CHECK_HIP(expr)                                                              \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(DL_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+#define DL_TRY(expr)               \
+  do {                             \
+    dl_status s_ = (expr);         \
+    if (s_ != DL_OK) return s_;    \
+  } while (0)
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline size_t esize(dl_dtype t) { return t == DL_BF16 ? 2 : 4; }
+inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+constexpr int kTileRows = 64;       // attention query tile
+constexpr int kLmChunk = 512;       // LM-head rows per product (bounds the logits buffer)
+
+dl_status check_ptr(const void* p, const char* what) {
+  if (!p) return fail(DL_E_ARG, "%s is NULL", what);
+  if (((uintptr_t)p) & 15) return fail(DL_E_ALIGN, "%s is not 16-byte aligned", what);
+  return DL_OK;
+}
+
+dl_status check_dims(const dl_dims* d) {
+  if (!d) return fail(DL_E_ARG, "dims is NULL");
+  if (d->B < 1 || d->S < 1 || d->d < 1 || d->n_heads < 1 || d->head_dim < 2 || d->d_ffn < 1 || d->vocab < 1 ||
+      d->n_layers < 1)
+    return fail(DL_E_ARG, "dims: every size must be positive");
+  if (d->dtype != DL_F32 && d->dtype != DL_BF16) return fail(DL_E_DTYPE, "dims.dtype %d unknown", (int)d->dtype);
+  if (d->n_heads * d->head_dim != d->d)
+    return fail(DL_E_SHAPE, "d (%d) != n_heads (%d) * head_dim (%d)", d->d, d->n_heads, d->head_dim);
+  if (d->head_dim % 2) return fail(DL_E_SHAPE, "head_dim must be even");
+  if (d->B > 1024) return fail(DL_E_UNSUPPORTED, "B > 1024");
+  if (!(d->rms_eps > 0.f)) return fail(DL_E_ARG, "rms_eps must be positive");
+  if (!(d->rope_base > 0.f)) return fail(DL_E_ARG, "rope_base must be positive");
+  if (!attention_supported(d->dtype, d->S, d->head_dim))
+    return fail(DL_E_UNSUPPORTED, "attention for S=%d head_dim=%d not built", d->S, d->head_dim);
+  if ((size_t)d->d * esize(d->dtype) % 16 != 0) return fail(DL_E_SHAPE, "d * element size must be a multiple of 16 bytes");
+  return DL_OK;
+}
+
+dl_status check_sel(const dl_selection* s, const char* what) {
+  if (!s) return fail(DL_E_ARG, "%s is NULL", what);
+  DL_TRY(check_ptr(s->sel_idx, "sel_idx"));
+  DL_TRY(check_ptr(s->sel_count, "sel_count"));
+  DL_TRY(check_ptr(s->row_off, "row_off"));
+  return DL_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspace layout
+// ---------------------------------------------------------------------------
+struct RowMapMem {
+  size_t row_pos, row_seq, n_rows, tile_row0, tile_rows;
+};
+
+struct Layout {
+  int R;                    // row capacity (valid rows over the batch)
+  int T;                    // attention tile capacity
+  size_t sel_idx, sel_count, row_off;  // identity selection of every valid row
+  RowMapMem map_all, map_sel;
+  size_t x_all, x_sel;      // fp32 [R, d]
+  size_t act;               // T [R, max(d, F)]
+  size_t q, attn;           // T [R, d]
+  size_t P;                 // fp32 GEMM partials
+  size_t scores;            // fp32 [B*S]
+  size_t rope;              // float2 [S, head_dim/2]
+  size_t total;
+};
+
+size_t gemm_partial_floats(dl_dtype dt, int R, int N, int K) {
+  // worst case over every row bound the planner can see (1..R)
+  size_t best = 0;
+  for (int m = 128;; m += 128) {
+    const int M = std::min(m, R);
+    const GemmPlan p = plan_gemm(dt, M, N, K);
+    best = std::max(best, (size_t)p.splits * (size_t)M * (size_t)N);
+    if (M == R) break;
+  }
+  return best;
+}
+
+Layout make_layout(const dl_dims& d, int R) {
+  Layout L{};
+  const int B = d.B, S = d.S;
+  L.R = std::max(R, 1);
+  L.T = cdiv(L.R, kTileRows) + B;
+  const size_t es = esize(d.dtype);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  L.sel_idx = take(sizeof(int32_t) * (size_t)B * S);
+  L.sel_count = take(sizeof(int32_t) * B);
+  L.row_off = take(sizeof(int32_t) * (B + 1));
+  for (RowMapMem* m : {&L.map_all, &L.map_sel}) {
+    m->row_pos = take(sizeof(int32_t) * L.R);
+    m->row_seq = take(sizeof(int32_t) * L.R);
+    m->n_rows = take(sizeof(int32_t));
+    m->tile_row0 = take(sizeof(int32_t) * L.T);
+    m->tile_rows = take(sizeof(int32_t) * L.T);
+  }
+  L.x_all = take(sizeof(float) * (size_t)L.R * d.d);
+  L.x_sel = take(sizeof(float) * (size_t)L.R * d.d);
+  L.act = take(es * (size_t)L.R * std::max(d.d, d.d_ffn));
+  L.q = take(es * (size_t)L.R * d.d);
+  L.attn = take(es * (size_t)L.R * d.d);
+  size_t pf = 0;
+  pf = std::max(pf, gemm_partial_floats(d.dtype, L.R, 3 * d.d, d.d));
+  pf = std::max(pf, gemm_partial_floats(d.dtype, L.R, d.d, d.d));
+  pf = std::max(pf, gemm_partial_floats(d.dtype, L.R, 2 * d.d_ffn, d.d));
+  pf = std::max(pf, gemm_partial_floats(d.dtype, L.R, d.d, d.d_ffn));
+  pf = std::max(pf, gemm_partial_floats(d.dtype, std::min(L.R, kLmChunk), d.vocab, d.d));
+  L.P = take(sizeof(float) * pf);
+  L.scores = take(sizeof(float) * (size_t)B * S);
+  L.rope = take(sizeof(float) * 2 * (size_t)S * (d.head_dim / 2));
+  L.total = off;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+RowMap rowmap_at(void* ws, const RowMapMem& m, int R_max, int T_max) {
+  RowMap r;
+  r.row_pos = at<int32_t>(ws, m.row_pos);
+  r.row_seq = at<int32_t>(ws, m.row_seq);
+  r.n_rows = at<int32_t>(ws, m.n_rows);
+  r.tile_row0 = at<int32_t>(ws, m.tile_row0);
+  r.tile_rows = at<int32_t>(ws, m.tile_rows);
+  r.R_max = R_max;
+  r.T_max = T_max;
+  r.tq = kTileRows;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// layer pieces on packed rows
+// ---------------------------------------------------------------------------
+struct Ctx {
+  const dl_dims* d;
+  void* ws;
+  const Layout* L;
+  hipStream_t st;
+};
+
+dl_status check_layer(const dl_layer_w* w) {
+  if (!w) return fail(DL_E_ARG, "layer weights are NULL");
+  DL_TRY(check_ptr(w->attn_norm, "attn_norm"));
+  DL_TRY(check_ptr(w->wq, "wq"));
+  DL_TRY(check_ptr(w->wk, "wk"));
+  DL_TRY(check_ptr(w->wv, "wv"));
+  DL_TRY(check_ptr(w->wo, "wo"));
+  DL_TRY(check_ptr(w->ffn_norm, "ffn_norm"));
+  DL_TRY(check_ptr(w->w_gate, "w_gate"));
+  DL_TRY(check_ptr(w->w_up, "w_up"));
+  DL_TRY(check_ptr(w->w_down, "w_down"));
+  return DL_OK;
+}
+
+dl_status attn_block(const Ctx& c, const dl_layer_w* w, float* x, const RowMap& rm, const int32_t* seq_len,
+                     void* kc, void* vc) {
+  const dl_dims& d = *c.d;
+  void* act = at<void>(c.ws, c.L->act);
+  void* q = at<void>(c.ws, c.L->q);
+  void* attn = at<void>(c.ws, c.L->attn);
+  float* P = at<float>(c.ws, c.L->P);
+  const float2* rope = at<float2>(c.ws, c.L->rope);
+  DL_CHECK_HIP(launch_rmsnorm(d.dtype, x, w->attn_norm, rm, d.d, d.rms_eps, act, c.st));
+  {
+    const void* seg[4] = {w->wq, w->wk, w->wv, w->wv};
+    const GemmPlan p = plan_gemm(d.dtype, rm.R_max, 3 * d.d, d.d);
+    DL_CHECK_HIP(launch_gemm(d.dtype, p, act, rm.R_max, rm.n_rows, 0, d.d, seg, d.d, 3 * d.d, P, c.st));
+    DL_CHECK_HIP(launch_epi_qkv(d.dtype, P, p.splits, rm, d.S, d.d, d.head_dim, rope, q, kc, vc, c.st));
+  }
+  DL_CHECK_HIP(launch_attention(d.dtype, q, kc, vc, seq_len, rm, d.S, d.n_heads, d.head_dim, attn, c.st));
+  {
+    const void* seg[4] = {w->wo, w->wo, w->wo, w->wo};
+    const GemmPlan p = plan_gemm(d.dtype, rm.R_max, d.d, d.d);
+    DL_CHECK_HIP(launch_gemm(d.dtype, p, attn, rm.R_max, rm.n_rows, 0, d.d, seg, d.d, d.d, P, c.st));
+    DL_CHECK_HIP(launch_epi_residual(P, p.splits, rm, d.d, x, c.st));
+  }
+  return DL_OK;
+}
+
+dl_status ffn_block(const Ctx& c, const dl_layer_w* w, float* x, const RowMap& rm) {
+  const dl_dims& d = *c.d;
+  void* act = at<void>(c.ws, c.L->act);
+  float* P = at<float>(c.ws, c.L->P);
+  DL_CHECK_HIP(launch_rmsnorm(d.dtype, x, w->ffn_norm, rm, d.d, d.rms_eps, act, c.st));
+  {
+    const void* seg[4] = {w->w_gate, w->w_up, w->w_up, w->w_up};
+    const GemmPlan p = plan_gemm(d.dtype, rm.R_max, 2 * d.d_ffn, d.d);
+    DL_CHECK_HIP(launch_gemm(d.dtype, p, act, rm.R_max, rm.n_rows, 0, d.d, seg, d.d_ffn, 2 * d.d_ffn, P, c.st));
+    DL_CHECK_HIP(launch_epi_swiglu(d.dtype, P, p.splits, rm, d.d_ffn, act, c.st));
+  }
+  {
+    const void* seg[4] = {w->w_down, w->w_down, w->w_down, w->w_down};
+    const GemmPlan p = plan_gemm(d.dtype, rm.R_max, d.d, d.d_ffn);
+    DL_CHECK_HIP(launch_gemm(d.dtype, p, act, rm.R_max, rm.n_rows, 0, d.d_ffn, seg, d.d, d.d, P, c.st));
+    DL_CHECK_HIP(launch_epi_residual(P, p.splits, rm, d.d, x, c.st));
+  }
+  return DL_OK;
+}
+
+dl_status lm_block(const Ctx& c, const void* final_norm, const void* lm_head, const float* x, const RowMap& rm,
+                   float* conf, int32_t* argmax, void* h_final, float* logits) {
+  const dl_dims& d = *c.d;
+  void* act = at<void>(c.ws, c.L->act);
+  float* P = at<float>(c.ws, c.L->P);
+  DL_CHECK_HIP(launch_rmsnorm(d.dtype, x, final_norm, rm, d.d, d.rms_eps, act, c.st));
+  const void* seg[4] = {lm_head, lm_head, lm_head, lm_head};
+  for (int m0 = 0; m0 < rm.R_max; m0 += kLmChunk) {
+    const int rows = std::min(kLmChunk, rm.R_max - m0);
+    const GemmPlan p = plan_gemm(d.dtype, rows, d.vocab, d.d);
+    const void* A = static_cast<const char*>(act) + (size_t)m0 * d.d * esize(d.dtype);
+    DL_CHECK_HIP(launch_gemm(d.dtype, p, A, rows, rm.n_rows, m0, d.d, seg, d.vocab, d.vocab, P, c.st));
+    DL_CHECK_HIP(launch_lm_reduce(P, p.splits, rm, m0, rows, d.vocab, conf, argmax, logits, c.st));
+  }
+  DL_CHECK_HIP(launch_store_rows(d.dtype, x, d.d, rm, h_final, c.st));
+  return DL_OK;
+}
+
+size_t layer_stride_bytes(const dl_dims& d) { return (size_t)d.B * d.S * d.d * esize(d.dtype); }
+
+}  // namespace
+
+// ===========================================================================
+// exported entry points
+// ===========================================================================
+extern "C" {
+
+int32_t dl_abi_version(void) { return DL_ABI_VERSION; }
+
+const char* dl_last_error(void) { return g_err; }
+
+const char* dl_status_string(dl_status s) {
+  switch (s) {
+    case DL_OK: return "ok";
+    case DL_E_ARG: return "invalid argument";
+    case DL_E_SHAPE: return "inconsistent shape";
+    case DL_E_DTYPE: return "unsupported dtype";
+    case DL_E_ALIGN: return "misaligned pointer";
+    case DL_E_WORKSPACE: return "workspace too small";
+    case DL_E_HIP: return "HIP runtime error";
+    case DL_E_UNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+size_t dl_workspace_bytes(const dl_dims* dims, int32_t max_rows) {
+  if (check_dims(dims) != DL_OK) return 0;
+  const int R = max_rows > 0 ? max_rows : dims->B * dims->S;
+  return make_layout(*dims, R).total;
+}
+
+dl_status dl_score_select(const dl_dims* dims, const void* h_cur, const void* h_prev, const float* conf,
+                          const int32_t* seq_len, dl_score_kind kind, float alpha, dl_select_mode mode,
+                          float keep_ratio, float threshold, dl_selection* out, float* scores_or_null, void* ws,
+                          size_t ws_bytes, void* stream) {
+  DL_TRY(check_dims(dims));
+  DL_TRY(check_ptr(h_cur, "h_cur"));
+  DL_TRY(check_ptr(h_prev, "h_prev"));
+  DL_TRY(check_ptr(conf, "conf"));
+  DL_TRY(check_ptr(seq_len, "seq_len"));
+  DL_TRY(check_sel(out, "out"));
+  if (h_cur == h_prev) return fail(DL_E_ARG, "h_cur and h_prev alias");
+  if (kind < DL_SCORE_ESDLLM || kind > DL_SCORE_COSINE) return fail(DL_E_ARG, "score kind %d unknown", (int)kind);
+  if (mode != DL_SEL_TOPK && mode != DL_SEL_THRESHOLD) return fail(DL_E_ARG, "select mode %d unknown", (int)mode);
+  if (mode == DL_SEL_TOPK && !(keep_ratio > 0.f && keep_ratio <= 1.f))
+    return fail(DL_E_ARG, "keep_ratio %g outside (0, 1]", (double)keep_ratio);
+  float* scores = scores_or_null;
+  if (scores) DL_TRY(check_ptr(scores, "scores"));
+  const size_t need = dl_workspace_bytes(dims, 1);
+  if (!scores) {
+    DL_TRY(check_ptr(ws, "ws"));
+    if (ws_bytes < need) return fail(DL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    scores = at<float>(ws, make_layout(*dims, 1).scores);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  DL_CHECK_HIP(launch_score(dims->dtype, h_cur, nullptr, nullptr, const_cast<void*>(h_prev), conf, seq_len, dims->B,
+                            dims->S, dims->d, kind, alpha, scores, st));
+  DL_CHECK_HIP(launch_select(scores, seq_len, dims->B, dims->S, mode, keep_ratio, threshold, out->sel_idx,
+                             out->sel_count, st));
+  DL_CHECK_HIP(launch_row_off(out->sel_count, out->row_off, dims->B, st));
+  return DL_OK;
+}
+
+dl_status dl_gather(const dl_dims* dims, const void* src, int32_t w, dl_dtype dtype, const dl_selection* sel,
+                    int32_t k_total_max, void* dst, void* stream) {
+  DL_TRY(check_dims(dims));
+  DL_TRY(check_ptr(src, "src"));
+  DL_TRY(check_ptr(dst, "dst"));
+  DL_TRY(check_sel(sel, "sel"));
+  if (w < 1 || k_total_max < 0) return fail(DL_E_ARG, "w must be positive and k_total_max non-negative");
+  if (dtype != DL_F32 && dtype != DL_BF16) return fail(DL_E_DTYPE, "dtype %d unknown", (int)dtype);
+  if (k_total_max > dims->B * dims->S) return fail(DL_E_SHAPE, "k_total_max > B*S");
+  DL_CHECK_HIP(launch_gather_sel(esize(dtype), src, w, sel->sel_idx, sel->row_off, dims->B, dims->S, k_total_max,
+                                 dst, (hipStream_t)stream));
+  return DL_OK;
+}
+
+dl_status dl_scatter_cache(const dl_dims* dims, const void* rows, int32_t w, dl_dtype dtype, const dl_selection* sel,
+                           int32_t k_total_max, void* cache, void* stream) {
+  DL_TRY(check_dims(dims));
+  DL_TRY(check_ptr(rows, "rows"));
+  DL_TRY(check_ptr(cache, "cache"));
+  DL_TRY(check_sel(sel, "sel"));
+  if (w < 1 || k_total_max < 0) return fail(DL_E_ARG, "w must be positive and k_total_max non-negative");
+  if (dtype != DL_F32 && dtype != DL_BF16) return fail(DL_E_DTYPE, "dtype %d unknown", (int)dtype);
+  if (k_total_max > dims->B * dims->S) return fail(DL_E_SHAPE, "k_total_max > B*S");
+  DL_CHECK_HIP(launch_scatter_sel(esize(dtype), rows, w, sel->sel_idx, sel->row_off, dims->B, dims->S, k_total_max,
+                                  cache, (hipStream_t)stream));
+  return DL_OK;
+}
+
+static dl_status prep_rows(const dl_dims* dims, const dl_selection* sel, int32_t k_total_max, void* ws,
+                           size_t ws_bytes, Layout* L, RowMap* rm, hipStream_t st) {
+  DL_TRY(check_sel(sel, "sel"));
+  DL_TRY(check_ptr(ws, "ws"));
+  if (k_total_max < 0 || k_total_max > dims->B * dims->S) return fail(DL_E_SHAPE, "k_total_max outside [0, B*S]");
+  *L = make_layout(*dims, k_total_max);
+  if (ws_bytes < L->total) return fail(DL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L->total);
+  *rm = rowmap_at(ws, L->map_sel, k_total_max, L->T);
+  DL_CHECK_HIP(launch_rowmap(sel->sel_idx, sel->sel_count, sel->row_off, dims->B, dims->S, *rm, st));
+  return DL_OK;
+}
+
+dl_status dl_partial_attn(const dl_dims* dims, const dl_layer_w* layer, float* x_rows, const dl_selection* sel,
+                          const int32_t* seq_len, int32_t k_total_max, void* k_cache, void* v_cache, void* ws,
+                          size_t ws_bytes, void* stream) {
+  DL_TRY(check_dims(dims));
+  DL_TRY(check_layer(layer));
+  DL_TRY(check_ptr(x_rows, "x_rows"));
+  DL_TRY(check_ptr(seq_len, "seq_len"));
+  DL_TRY(check_ptr(k_cache, "k_cache"));
+  DL_TRY(check_ptr(v_cache, "v_cache"));
+  hipStream_t st = (hipStream_t)stream;
+  Layout L;
+  RowMap rm;
+  DL_TRY(prep_rows(dims, sel, k_total_max, ws, ws_bytes, &L, &rm, st));
+  if (k_total_max == 0) return DL_OK;
+  DL_CHECK_HIP(launch_rope_table(dims->S, dims->head_dim, dims->rope_base, at<float2>(ws, L.rope), st));
+  Ctx c{dims, ws, &L, st};
+  return attn_block(c, layer, x_rows, rm, seq_len, k_cache, v_cache);
+}
+
+dl_status dl_ffn_rows(const dl_dims* dims, const dl_layer_w* layer, float* x_rows, const dl_selection* sel,
+                      int32_t k_total_max, void* ws, size_t ws_bytes, void* stream) {
+  DL_TRY(check_dims(dims));
+  DL_TRY(check_layer(layer));
+  DL_TRY(check_ptr(x_rows, "x_rows"));
+  hipStream_t st = (hipStream_t)stream;
+  Layout L;
+  RowMap rm;
+  DL_TRY(prep_rows(dims, sel, k_total_max, ws, ws_bytes, &L, &rm, st));
+  if (k_total_max == 0) return DL_OK;
+  Ctx c{dims, ws, &L, st};
+  return ffn_block(c, layer, x_rows, rm);
+}
+
+dl_status dl_lm_head_rows(const dl_dims* dims, const void* final_norm, const void* lm_head, const float* x_rows,
+                          const dl_selection* sel, int32_t k_total_max, float* conf, int32_t* argmax, void* h_final,
+                          float* logits_or_null, void* ws, size_t ws_bytes, void* stream) {
+  DL_TRY(check_dims(dims));
+  DL_TRY(check_ptr(final_norm, "final_norm"));
+  DL_TRY(check_ptr(lm_head, "lm_head"));
+  DL_TRY(check_ptr(x_rows, "x_rows"));
+  DL_TRY(check_ptr(conf, "conf"));
+  DL_TRY(check_ptr(argmax, "argmax"));
+  DL_TRY(check_ptr(h_final, "h_final"));
+  if (logits_or_null) DL_TRY(check_ptr(logits_or_null, "logits"));
+  hipStream_t st = (hipStream_t)stream;
+  Layout L;
+  RowMap rm;
+  DL_TRY(prep_rows(dims, sel, k_total_max, ws, ws_bytes, &L, &rm, st));
+  if (k_total_max == 0) return DL_OK;
+  Ctx c{dims, ws, &L, st};
+  return lm_block(c, final_norm, lm_head, x_rows, rm, conf, argmax, h_final, logits_or_null);
+}
+
+dl_status dl_unmask(const dl_dims* dims, int32_t* tokens, uint8_t* masked, const float* conf, const int32_t* argmax,
+                    const int32_t* prompt_len, const int32_t* seq_len, int32_t block, int32_t block_len,
+                    int32_t n_unmask, void* stream) {
+  DL_TRY(check_dims(dims));
+  DL_TRY(check_ptr(tokens, "tokens"));
+  DL_TRY(check_ptr(masked, "masked"));
+  DL_TRY(check_ptr(conf, "conf"));
+  DL_TRY(check_ptr(argmax, "argmax"));
+  DL_TRY(check_ptr(prompt_len, "prompt_len"));
+  DL_TRY(check_ptr(seq_len, "seq_len"));
+  if (block < 0 || block_len < 1 || n_unmask < 0) return fail(DL_E_ARG, "block/block_len/n_unmask out of range");
+  if (block_len > 1024) return fail(DL_E_UNSUPPORTED, "block_len > 1024");
+  DL_CHECK_HIP(launch_unmask(tokens, masked, conf, argmax, prompt_len, seq_len, dims->B, dims->S, block, block_len,
+                             n_unmask, (hipStream_t)stream));
+  return DL_OK;
+}
+
+dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_params* p, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!model || !s || !p) return fail(DL_E_ARG, "model, state and params must be non-NULL");
+  const dl_dims* dims = &model->dims;
+  DL_TRY(check_dims(dims));
+  const dl_dims& d = *dims;
+  DL_TRY(check_ptr(model->embed, "embed"));
+  DL_TRY(check_ptr(model->final_norm, "final_norm"));
+  DL_TRY(check_ptr(model->lm_head, "lm_head"));
+  if (!model->layers) return fail(DL_E_ARG, "model.layers is NULL");
+  for (int l = 0; l < d.n_layers; ++l) DL_TRY(check_layer(&model->layers[l]));
+  DL_TRY(check_ptr(s->tokens, "tokens"));
+  DL_TRY(check_ptr(s->masked, "masked"));
+  DL_TRY(check_ptr(s->seq_len, "seq_len"));
+  DL_TRY(check_ptr(s->prompt_len, "prompt_len"));
+  DL_TRY(check_ptr(s->h_prev, "h_prev"));
+  DL_TRY(check_ptr(s->k_cache, "k_cache"));
+  DL_TRY(check_ptr(s->v_cache, "v_cache"));
+  DL_TRY(check_ptr(s->h_final, "h_final"));
+  DL_TRY(check_ptr(s->conf, "conf"));
+  DL_TRY(check_ptr(s->argmax, "argmax"));
+  if (s->logits) DL_TRY(check_ptr(s->logits, "logits"));
+  if (s->scores) DL_TRY(check_ptr(s->scores, "scores"));
+  DL_TRY(check_sel(&s->sel, "state.sel"));
+  DL_TRY(check_ptr(ws, "ws"));
+  if (!p->seq_len_host) return fail(DL_E_ARG, "params.seq_len_host is NULL");
+  if (p->skip_layer < 1 || p->skip_layer > d.n_layers)
+    return fail(DL_E_ARG, "skip_layer %d outside [1, %d]", p->skip_layer, d.n_layers);
+  if (p->score < DL_SCORE_ESDLLM || p->score > DL_SCORE_COSINE) return fail(DL_E_ARG, "score kind unknown");
+  if (p->mode != DL_SEL_TOPK && p->mode != DL_SEL_THRESHOLD) return fail(DL_E_ARG, "select mode unknown");
+  if (p->mode == DL_SEL_TOPK && !(p->keep_ratio > 0.f && p->keep_ratio <= 1.f))
+    return fail(DL_E_ARG, "keep_ratio %g outside (0, 1]", (double)p->keep_ratio);
+  if (p->block < 0 || p->block_len < 1 || p->n_unmask < 0) return fail(DL_E_ARG, "block schedule out of range");
+  if (p->block_len > 1024) return fail(DL_E_UNSUPPORTED, "block_len > 1024");
+  long long R_all = 0, R_sel = 0;
+  for (int b = 0; b < d.B; ++b) {
+    const int n = p->seq_len_host[b];
+    if (n < 0 || n > d.S) return fail(DL_E_SHAPE, "seq_len_host[%d] = %d outside [0, S=%d]", b, n, d.S);
+    R_all += n;
+    if (p->mode == DL_SEL_TOPK && n > 0) {
+      const double kk = ceil((double)p->keep_ratio * (double)n);
+      R_sel += kk < 1.0 ? 1 : (kk > (double)n ? n : (long long)kk);
+    }
+  }
+  if (p->mode == DL_SEL_THRESHOLD) R_sel = R_all;
+  const Layout L = make_layout(d, (int)R_all);
+  if (ws_bytes < L.total) return fail(DL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+
+  hipStream_t st = (hipStream_t)stream;
+  Ctx c{dims, ws, &L, st};
+  const bool refresh = p->full_refresh != 0;
+  const int sl = p->skip_layer;
+  int32_t* all_idx = at<int32_t>(ws, L.sel_idx);
+  int32_t* all_cnt = at<int32_t>(ws, L.sel_count);
+  int32_t* all_off = at<int32_t>(ws, L.row_off);
+  const RowMap rm_all = rowmap_at(ws, L.map_all, (int)R_all, L.T);
+  float* x_all = at<float>(ws, L.x_all);
+
+  DL_CHECK_HIP(launch_identity_sel(s->seq_len, d.B, d.S, all_idx, all_cnt, st));
+  DL_CHECK_HIP(launch_row_off(all_cnt, all_off, d.B, st));
+  DL_CHECK_HIP(launch_rowmap(all_idx, all_cnt, all_off, d.B, d.S, rm_all, st));
+  DL_CHECK_HIP(launch_rope_table(d.S, d.head_dim, d.rope_base, at<float2>(ws, L.rope), st));
+  DL_CHECK_HIP(launch_embed(d.dtype, s->tokens, rm_all, model->embed, d.d, x_all, st));
+
+  const size_t lstride = layer_stride_bytes(d);
+  auto kc = [&](int l) { return static_cast<char*>(s->k_cache) + (size_t)l * lstride; };
+  auto vc = [&](int l) { return static_cast<char*>(s->v_cache) + (size_t)l * lstride; };
+
+  const int n_full = refresh ? d.n_layers : sl;
+  for (int l = 0; l < n_full; ++l) {
+    if (refresh && l == sl) DL_CHECK_HIP(launch_store_rows(d.dtype, x_all, d.d, rm_all, s->h_prev, st));
+    DL_TRY(attn_block(c, &model->layers[l], x_all, rm_all, s->seq_len, kc(l), vc(l)));
+    DL_TRY(ffn_block(c, &model->layers[l], x_all, rm_all));
+  }
+  float* scores = s->scores ? s->scores : at<float>(ws, L.scores);
+  if (refresh) {
+    if (sl == d.n_layers) DL_CHECK_HIP(launch_store_rows(d.dtype, x_all, d.d, rm_all, s->h_prev, st));
+    DL_CHECK_HIP(hipMemcpyAsync(s->sel.sel_idx, all_idx, sizeof(int32_t) * (size_t)d.B * d.S,
+                                hipMemcpyDeviceToDevice, st));
+    DL_CHECK_HIP(hipMemcpyAsync(s->sel.sel_count, all_cnt, sizeof(int32_t) * d.B, hipMemcpyDeviceToDevice, st));
+    DL_CHECK_HIP(hipMemcpyAsync(s->sel.row_off, all_off, sizeof(int32_t) * (d.B + 1), hipMemcpyDeviceToDevice, st));
+    DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_all, rm_all, s->conf, s->argmax, s->h_final,
+                    s->logits));
+  } else {
+    // score against h_prev and overwrite it with this step's layer-s input
+    DL_CHECK_HIP(launch_score(d.dtype, nullptr, x_all, all_off, s->h_prev, s->conf, s->seq_len, d.B, d.S, d.d,
+                              p->score, p->alpha, scores, st));
+    DL_CHECK_HIP(launch_select(scores, s->seq_len, d.B, d.S, p->mode, p->keep_ratio, p->threshold, s->sel.sel_idx,
+                               s->sel.sel_count, st));
+    DL_CHECK_HIP(launch_row_off(s->sel.sel_count, s->sel.row_off, d.B, st));
+    const RowMap rm_sel = rowmap_at(ws, L.map_sel, (int)R_sel, L.T);
+    DL_CHECK_HIP(launch_rowmap(s->sel.sel_idx, s->sel.sel_count, s->sel.row_off, d.B, d.S, rm_sel, st));
+    float* x_sel = at<float>(ws, L.x_sel);
+    DL_CHECK_HIP(launch_gather(sizeof(float), x_all, all_off, d.S, d.d, rm_sel, x_sel, st));
+    for (int l = sl; l < d.n_layers; ++l) {
+      DL_TRY(attn_block(c, &model->layers[l], x_sel, rm_sel, s->seq_len, kc(l), vc(l)));
+      DL_TRY(ffn_block(c, &model->layers[l], x_sel, rm_sel));
+    }
+    DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_sel, rm_sel, s->conf, s->argmax, s->h_final,
+                    s->logits));
+  }
+  DL_CHECK_HIP(launch_unmask(s->tokens, s->masked, s->conf, s->argmax, s->prompt_len, s->seq_len, d.B, d.S, p->block,
+                             p->block_len, p->n_unmask, st));
+  return DL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Internal helpers shared by the HIP kernels of libdtsk (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dl.h"
+
+namespace dtsk {
+
+// Storage types.  bf16 is kept as raw 16-bit patterns; conversions are done
+// here so that every rounding point is explicit (round to nearest even).
+struct bf16_t {
+  uint16_t u;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(((uint32_t)x.u) << 16); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float f);
+template <>
+__device__ __forceinline__ float from_f32<float>(float f) { return f; }
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) {
+  uint32_t u = __float_as_uint(f);
+  bf16_t r;
+  if ((u & 0x7fffffffu) > 0x7f800000u) {  // NaN stays a (quiet) NaN
+    r.u = (uint16_t)((u >> 16) | 0x40u);
+  } else {
+    u += 0x7fffu + ((u >> 16) & 1u);
+    r.u = (uint16_t)(u >> 16);
+  }
+  return r;
+}
+
+// Round an fp32 value to the storage type and back (what a store + load does).
+template <typename T>
+__device__ __forceinline__ float round_to(float f) { return to_f32(from_f32<T>(f)); }
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum for blockDim.x a multiple of 64 (<= 1024).  Fixed order, so
+// the result does not depend on timing.  `red` must hold 16 floats.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = warp_sum(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+// Row maps of a packed selection: for packed row r, the flat [B,S] row
+// b*S + i it came from, and its sequence b.  Built on the device.
+struct RowMap {
+  int32_t* row_pos;   // [R_max]  (-1 beyond row_off[B])
+  int32_t* row_seq;   // [R_max]
+  int32_t* n_rows;    // [1]      = row_off[B]
+  int32_t* tile_row0; // [T_max]  attention query tiles: first packed row
+  int32_t* tile_rows; // [T_max]  rows in the tile (0 = unused)
+  int32_t R_max;
+  int32_t T_max;
+  int32_t tq;         // query rows per attention tile
+};
+
+}  // namespace dtsk

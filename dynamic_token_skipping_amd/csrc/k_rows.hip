@@ -1,0 +1,771 @@
+// Row-level kernels: selections and row maps, importance score, top-k /
+// threshold selection, embedding, gathers and scatters, RMSNorm, GEMM
+// epilogues (RoPE + K/V cache scatter, residual add, SwiGLU), LM-head
+// confidence reduction and block unmasking.
+#include <float.h>
+#include <math.h>
+
+#include "launch.h"
+
+namespace dtsk {
+
+namespace {
+
+constexpr int kRowThreads = 256;
+
+// ---------------------------------------------------------------------------
+// selections
+// ---------------------------------------------------------------------------
+__global__ void k_identity_sel(const int32_t* __restrict__ seq_len, int S, int32_t* __restrict__ sel_idx,
+                               int32_t* __restrict__ sel_count) {
+  const int b = blockIdx.y;
+  const int n = seq_len[b];
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < S; i += gridDim.x * blockDim.x)
+    sel_idx[(size_t)b * S + i] = i < n ? i : 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) sel_count[b] = n;
+}
+
+// One block: exclusive prefix of sel_count (B <= 1024).
+__global__ void k_row_off(const int32_t* __restrict__ sel_count, int32_t* __restrict__ row_off, int B) {
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int b = 0; b < B; ++b) {
+      row_off[b] = acc;
+      acc += sel_count[b];
+    }
+    row_off[B] = acc;
+  }
+}
+
+// One block: the row count and the attention query tiles (tq rows each,
+// never crossing a sequence), from an existing row_off.
+__global__ void k_tiles(const int32_t* __restrict__ sel_count, const int32_t* __restrict__ row_off, int B,
+                        int32_t* __restrict__ n_rows, int32_t* __restrict__ tile_row0,
+                        int32_t* __restrict__ tile_rows, int T_max, int tq) {
+  __shared__ int32_t toff[1025];
+  const int t = threadIdx.x;
+  if (t == 0) {
+    int tacc = 0;
+    for (int b = 0; b < B; ++b) {
+      toff[b] = tacc;
+      tacc += (sel_count[b] + tq - 1) / tq;
+    }
+    toff[B] = tacc;
+    *n_rows = row_off[B];
+  }
+  __syncthreads();
+  for (int s = t; s < T_max; s += blockDim.x) {
+    int r0 = 0, rows = 0;
+    if (s < toff[B]) {
+      int lo = 0, hi = B - 1;  // last b with toff[b] <= s
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (toff[mid] <= s) lo = mid; else hi = mid - 1;
+      }
+      const int b = lo;
+      const int j0 = (s - toff[b]) * tq;
+      r0 = row_off[b] + j0;
+      rows = min(tq, sel_count[b] - j0);
+    }
+    tile_row0[s] = r0;
+    tile_rows[s] = rows;
+  }
+}
+
+__global__ void k_rowmap(const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ row_off, int B, int S,
+                         int R_max, int32_t* __restrict__ row_pos, int32_t* __restrict__ row_seq) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R_max) return;
+  const int n = row_off[B];
+  if (r >= n) {
+    row_pos[r] = -1;
+    row_seq[r] = 0;
+    return;
+  }
+  int lo = 0, hi = B - 1;  // last b with row_off[b] <= r
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (row_off[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  row_pos[r] = b * S + sel_idx[(size_t)b * S + (r - row_off[b])];
+  row_seq[r] = b;
+}
+
+// ---------------------------------------------------------------------------
+// importance score (one wave per row)
+// ---------------------------------------------------------------------------
+template <typename T, bool kFused>
+__global__ __launch_bounds__(256) void k_score(const T* __restrict__ h_cur, const float* __restrict__ x_packed,
+                                               const int32_t* __restrict__ off_all, T* __restrict__ h_prev,
+                                               const float* __restrict__ conf, const int32_t* __restrict__ seq_len,
+                                               int S, int d, int kind, float alpha, float* __restrict__ scores) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (i >= seq_len[b]) return;
+  const size_t row = (size_t)b * S + i;
+  const T* hp = h_prev + row * d;
+  float l1 = 0.f, dd = 0.f, hh = 0.f, xx = 0.f, xh = 0.f;
+  if constexpr (kFused) {
+    const float* xr = x_packed + (size_t)(off_all[b] + i) * d;
+    T* hw = h_prev + row * d;
+    for (int c = lane; c < d; c += 64) {
+      const T xt = from_f32<T>(xr[c]);
+      const float x = to_f32(xt), h = to_f32(hp[c]);
+      const float df = x - h;
+      l1 += fabsf(df);
+      dd += df * df;
+      hh += h * h;
+      xx += x * x;
+      xh += x * h;
+      hw[c] = xt;  // each element is read before this lane overwrites it
+    }
+  } else {
+    const T* xc = h_cur + row * d;
+    for (int c = lane; c < d; c += 64) {
+      const float x = to_f32(xc[c]), h = to_f32(hp[c]);
+      const float df = x - h;
+      l1 += fabsf(df);
+      dd += df * df;
+      hh += h * h;
+      xx += x * x;
+      xh += x * h;
+    }
+  }
+  l1 = warp_sum(l1);
+  dd = warp_sum(dd);
+  hh = warp_sum(hh);
+  xx = warp_sum(xx);
+  xh = warp_sum(xh);
+  if (lane == 0) {
+    const float c = conf[row];
+    float s;
+    if (kind == DL_SCORE_ESDLLM) {
+      s = alpha * c + (1.f - alpha) * (l1 / fmaxf(sqrtf((float)d) * sqrtf(hh), FLT_MIN));
+    } else if (kind == DL_SCORE_RELL2_INVCONF) {
+      s = sqrtf(dd) / fmaxf(sqrtf(hh), FLT_MIN) + (1.f - c);
+    } else {
+      s = 1.f - xh / fmaxf(sqrtf(xx) * sqrtf(hh), FLT_MIN);
+    }
+    scores[row] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// top-k / threshold selection: one 1024-thread block per sequence
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t score_key(float f) {
+  if (isnan(f)) return 0u;           // NaN ranks last
+  if (f == 0.f) f = 0.f;             // -0 and +0 compare equal
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kSelThreads = 1024;
+
+// Exclusive block scan of one int per thread (fixed order).
+__device__ __forceinline__ int block_excl_scan(int v, int* buf, int* total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  __syncthreads();
+  if (lane == 63) buf[w] = incl;
+  __syncthreads();
+  if (t == 0) {
+    int acc = 0;
+    for (int i = 0; i < kSelThreads / 64; ++i) {
+      const int x = buf[i];
+      buf[i] = acc;
+      acc += x;
+    }
+    buf[kSelThreads / 64] = acc;
+  }
+  __syncthreads();
+  *total = buf[kSelThreads / 64];
+  return buf[w] + incl - v;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ scores,
+                                                        const int32_t* __restrict__ seq_len, int S, int mode,
+                                                        float keep, float threshold, int32_t* __restrict__ sel_idx,
+                                                        int32_t* __restrict__ sel_count) {
+  __shared__ int hist[256];
+  __shared__ int scan_buf[kSelThreads / 64 + 1];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int n = seq_len[b];
+  const float* sc = scores + (size_t)b * S;
+  const int chunk = (n + kSelThreads - 1) / kSelThreads;
+  const int i0 = min(n, t * chunk), i1 = min(n, i0 + chunk);
+
+  uint32_t thr;       // selected: key > thr, plus the first `need_eq` with key == thr
+  int need_eq;
+  if (mode == DL_SEL_TOPK) {
+    int k = 0;
+    if (n > 0) {
+      const double kk = ceil((double)keep * (double)n);
+      k = kk < 1.0 ? 1 : (kk > (double)n ? n : (int)kk);
+    }
+    if (k == 0) {
+      if (t == 0) sel_count[b] = 0;
+      return;
+    }
+    // radix select of the k-th largest key, 8 bits at a time from the top
+    if (t == 0) {
+      s_prefix = 0u;
+      s_need = k;
+    }
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
+      for (int j = t; j < 256; j += kSelThreads) hist[j] = 0;
+      __syncthreads();
+      const uint32_t prefix = s_prefix;
+      for (int i = i0; i < i1; ++i) {
+        const uint32_t key = score_key(sc[i]);
+        if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (t == 0) {
+        int need = s_need, digit = 255;
+        for (; digit > 0; --digit) {
+          if (hist[digit] >= need) break;
+          need -= hist[digit];
+        }
+        s_prefix = prefix | ((uint32_t)digit << shift);
+        s_need = need;
+      }
+      __syncthreads();
+    }
+    thr = s_prefix;
+    need_eq = s_need;  // how many rows with key == thr are taken (lowest indices)
+  } else {
+    thr = score_key(threshold);
+    need_eq = 0;
+    if (isnan(threshold)) thr = 0xffffffffu;
+  }
+  // Rows with key == thr are taken in index order until need_eq of them are
+  // in: the rank of an equal row is the number of equal rows before it.
+  const bool topk = mode == DL_SEL_TOPK;
+  int n_eq = 0;
+  for (int i = i0; i < i1; ++i) n_eq += score_key(sc[i]) == thr;
+  int tot;
+  const int eq_base = block_excl_scan(n_eq, scan_buf, &tot);
+  int n_sel = 0, er = eq_base;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = score_key(sc[i]);
+    if (key > thr) {
+      ++n_sel;
+    } else if (topk && key == thr) {
+      n_sel += er < need_eq;
+      ++er;
+    }
+  }
+  int out = block_excl_scan(n_sel, scan_buf, &tot);
+  int32_t* dst = sel_idx + (size_t)b * S;
+  er = eq_base;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = score_key(sc[i]);
+    bool take = key > thr;
+    if (!take && topk && key == thr) take = er++ < need_eq;
+    if (take) dst[out++] = i;
+  }
+  if (t == 0) sel_count[b] = tot;
+}
+
+// ---------------------------------------------------------------------------
+// embeddings, gathers, scatters
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_embed(const int32_t* __restrict__ tokens,
+                                                       const int32_t* __restrict__ row_pos,
+                                                       const T* __restrict__ E, int d, float* __restrict__ x) {
+  const int r = blockIdx.x;
+  const int p = row_pos[r];
+  if (p < 0) return;
+  const T* e = E + (size_t)tokens[p] * d;
+  float* xr = x + (size_t)r * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) xr[c] = to_f32(e[c]);
+}
+
+// 16-byte granular copy when the row width allows it, else element-wise.
+template <int kBytes>
+__global__ __launch_bounds__(kRowThreads) void k_gather(const char* __restrict__ src,
+                                                        const int32_t* __restrict__ src_off, int S, size_t row_bytes,
+                                                        const int32_t* __restrict__ row_pos,
+                                                        const int32_t* __restrict__ row_seq,
+                                                        char* __restrict__ dst) {
+  const int r = blockIdx.x;
+  const int p = row_pos[r];
+  if (p < 0) return;
+  size_t srow = (size_t)p;
+  if (src_off) {
+    const int b = row_seq[r];
+    srow = (size_t)src_off[b] + (size_t)(p - b * S);
+  }
+  const char* s = src + srow * row_bytes;
+  char* o = dst + (size_t)r * row_bytes;
+  using V = typename std::conditional<kBytes == 16, uint4, uint8_t>::type;
+  const size_t n = row_bytes / kBytes;
+  for (size_t c = threadIdx.x; c < n; c += blockDim.x) reinterpret_cast<V*>(o)[c] = reinterpret_cast<const V*>(s)[c];
+}
+
+template <int kBytes>
+__global__ __launch_bounds__(kRowThreads) void k_scatter(const char* __restrict__ rows, size_t row_bytes,
+                                                         const int32_t* __restrict__ row_pos,
+                                                         char* __restrict__ cache) {
+  const int r = blockIdx.x;
+  const int p = row_pos[r];
+  if (p < 0) return;
+  const char* s = rows + (size_t)r * row_bytes;
+  char* o = cache + (size_t)p * row_bytes;
+  using V = typename std::conditional<kBytes == 16, uint4, uint8_t>::type;
+  const size_t n = row_bytes / kBytes;
+  for (size_t c = threadIdx.x; c < n; c += blockDim.x) reinterpret_cast<V*>(o)[c] = reinterpret_cast<const V*>(s)[c];
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_store_rows(const float* __restrict__ x, int w,
+                                                            const int32_t* __restrict__ row_pos,
+                                                            T* __restrict__ dst) {
+  const int r = blockIdx.x;
+  const int p = row_pos[r];
+  if (p < 0) return;
+  const float* s = x + (size_t)r * w;
+  T* o = dst + (size_t)p * w;
+  for (int c = threadIdx.x; c < w; c += blockDim.x) o[c] = from_f32<T>(s[c]);
+}
+
+// Selection-driven row copies (ABI-level gather / scatter).
+__device__ __forceinline__ int sel_flat_row(int r, const int32_t* __restrict__ sel_idx,
+                                            const int32_t* __restrict__ row_off, int B, int S) {
+  if (r >= row_off[B]) return -1;
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (row_off[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo * S + sel_idx[(size_t)lo * S + (r - row_off[lo])];
+}
+
+template <int kBytes, bool kToCache>
+__global__ __launch_bounds__(kRowThreads) void k_copy_sel(const char* __restrict__ src, size_t row_bytes,
+                                                          const int32_t* __restrict__ sel_idx,
+                                                          const int32_t* __restrict__ row_off, int B, int S,
+                                                          char* __restrict__ dst) {
+  const int r = blockIdx.x;
+  const int p = sel_flat_row(r, sel_idx, row_off, B, S);
+  if (p < 0) return;
+  const char* s = src + (kToCache ? (size_t)r : (size_t)p) * row_bytes;
+  char* o = dst + (kToCache ? (size_t)p : (size_t)r) * row_bytes;
+  using V = typename std::conditional<kBytes == 16, uint4, uint8_t>::type;
+  const size_t n = row_bytes / kBytes;
+  for (size_t c = threadIdx.x; c < n; c += blockDim.x) reinterpret_cast<V*>(o)[c] = reinterpret_cast<const V*>(s)[c];
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm: out = T(x / sqrt(mean(x^2) + eps) * g)
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_rmsnorm(const float* __restrict__ x, const T* __restrict__ g,
+                                                         const int32_t* __restrict__ n_rows, int d, float eps,
+                                                         T* __restrict__ out) {
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  if (r >= *n_rows) return;
+  const float* xr = x + (size_t)r * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) ss += xr[c] * xr[c];
+  ss = block_sum(ss, red);
+  const float inv = 1.f / sqrtf(ss / (float)d + eps);
+  T* o = out + (size_t)r * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) o[c] = from_f32<T>(xr[c] * inv * to_f32(g[c]));
+}
+
+// RoPE table: (cos, sin) of pos * base^(-2j/dh), computed in double.
+__global__ void k_rope_table(int S, int half, int head_dim, double base, float2* __restrict__ tab) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= S * half) return;
+  const int pos = idx / half, j = idx % half;
+  const double inv = pow(base, -2.0 * (double)j / (double)head_dim);
+  double sn, cs;
+  sincos((double)pos * inv, &sn, &cs);
+  tab[idx] = make_float2((float)cs, (float)sn);
+}
+
+// q/k/v epilogue: sum the split-K partials, rotate q and k, write q rows and
+// scatter k/v into this layer's caches at the rows' positions.
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_epi_qkv(const float* __restrict__ P, int splits, int M_max,
+                                                         const int32_t* __restrict__ n_rows,
+                                                         const int32_t* __restrict__ row_pos,
+                                                         const int32_t* __restrict__ row_seq, int S, int d,
+                                                         int head_dim, const float2* __restrict__ rope,
+                                                         T* __restrict__ q_out, T* __restrict__ k_cache,
+                                                         T* __restrict__ v_cache) {
+  const int r = blockIdx.x;
+  if (r >= *n_rows) return;
+  const int p = row_pos[r];
+  const int pos = p - row_seq[r] * S;
+  const int N = 3 * d;
+  const int half = head_dim >> 1;
+  const size_t stride = (size_t)M_max * N;
+  const float* base = P + (size_t)r * N;
+  // q and k: pairs (j, j + half) of each head
+  for (int pi = threadIdx.x; pi < d; pi += blockDim.x) {   // d/2 pairs for q, d/2 for k
+    const int which = pi / (d >> 1);                        // 0 = q, 1 = k
+    const int pr = pi % (d >> 1);
+    const int h = pr / half, j = pr % half;
+    const int c1 = which * d + h * head_dim + j, c2 = c1 + half;
+    float a = 0.f, bb = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      a += base[s * stride + c1];
+      bb += base[s * stride + c2];
+    }
+    const float2 cs = rope[pos * half + j];
+    const float o1 = a * cs.x - bb * cs.y;
+    const float o2 = bb * cs.x + a * cs.y;
+    const int col = h * head_dim + j;
+    if (which == 0) {
+      q_out[(size_t)r * d + col] = from_f32<T>(o1);
+      q_out[(size_t)r * d + col + half] = from_f32<T>(o2);
+    } else {
+      k_cache[(size_t)p * d + col] = from_f32<T>(o1);
+      k_cache[(size_t)p * d + col + half] = from_f32<T>(o2);
+    }
+  }
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    float v = 0.f;
+    for (int s = 0; s < splits; ++s) v += base[s * stride + 2 * d + c];
+    v_cache[(size_t)p * d + c] = from_f32<T>(v);
+  }
+}
+
+__global__ __launch_bounds__(kRowThreads) void k_epi_residual(const float* __restrict__ P, int splits, int M_max,
+                                                              const int32_t* __restrict__ n_rows, int N,
+                                                              float* __restrict__ x) {
+  const int r = blockIdx.x;
+  if (r >= *n_rows) return;
+  const size_t stride = (size_t)M_max * N;
+  const float* base = P + (size_t)r * N;
+  float* xr = x + (size_t)r * N;
+  for (int c = threadIdx.x; c < N; c += blockDim.x) {
+    float v = 0.f;
+    for (int s = 0; s < splits; ++s) v += base[s * stride + c];
+    xr[c] += v;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_epi_swiglu(const float* __restrict__ P, int splits, int M_max,
+                                                            const int32_t* __restrict__ n_rows, int F,
+                                                            T* __restrict__ out) {
+  const int r = blockIdx.x;
+  if (r >= *n_rows) return;
+  const int N = 2 * F;
+  const size_t stride = (size_t)M_max * N;
+  const float* base = P + (size_t)r * N;
+  for (int c = threadIdx.x; c < F; c += blockDim.x) {
+    float g = 0.f, u = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      g += base[s * stride + c];
+      u += base[s * stride + F + c];
+    }
+    const float a = g / (1.f + expf(-g)) * u;
+    out[(size_t)r * F + c] = from_f32<T>(a);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LM head: per row, max / argmax (lowest id) / sum exp over the vocabulary
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRowThreads) void k_lm_reduce(const float* __restrict__ P, int splits, int M_max,
+                                                           const int32_t* __restrict__ n_rows, int m_base,
+                                                           const int32_t* __restrict__ row_pos, int V,
+                                                           float* __restrict__ conf, int32_t* __restrict__ argmax,
+                                                           float* __restrict__ logits_out) {
+  __shared__ float sm[kRowThreads / 64], ss[kRowThreads / 64];
+  __shared__ int si[kRowThreads / 64];
+  const int r = blockIdx.x;
+  if (m_base + r >= *n_rows) return;
+  const int p = row_pos[m_base + r];
+  const size_t stride = (size_t)M_max * V;
+  const float* base = P + (size_t)r * V;
+  float m = -INFINITY, sum = 0.f;
+  int am = 0x7fffffff;
+  for (int v = threadIdx.x; v < V; v += blockDim.x) {
+    float l = 0.f;
+    for (int s = 0; s < splits; ++s) l += base[s * stride + v];
+    if (logits_out) logits_out[(size_t)p * V + v] = l;
+    if (l > m) {
+      sum = sum * expf(m - l) + 1.f;
+      m = l;
+      am = v;
+    } else {
+      sum += expf(l - m);
+    }
+  }
+  // combine within the wave
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64);
+    const float s2 = __shfl_xor(sum, o, 64);
+    const int a2 = __shfl_xor(am, o, 64);
+    const float mn = fmaxf(m, m2);
+    const float sn = (m == -INFINITY ? 0.f : sum * expf(m - mn)) + (m2 == -INFINITY ? 0.f : s2 * expf(m2 - mn));
+    const int an = (m2 > m || (m2 == m && a2 < am)) ? a2 : am;
+    m = mn;
+    sum = sn;
+    am = an;
+  }
+  if (lane == 0) {
+    sm[w] = m;
+    ss[w] = sum;
+    si[w] = am;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = sm[0], Ssum = ss[0];
+    int A = si[0];
+    for (int i = 1; i < kRowThreads / 64; ++i) {
+      const float mn = fmaxf(M, sm[i]);
+      Ssum = Ssum * expf(M - mn) + ss[i] * expf(sm[i] - mn);
+      if (sm[i] > M || (sm[i] == M && si[i] < A)) A = si[i];
+      M = mn;
+    }
+    conf[p] = 1.f / Ssum;
+    argmax[p] = A;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// unmask: rank each masked candidate of the block by (conf desc, index asc)
+// ---------------------------------------------------------------------------
+constexpr int kMaxBlockLen = 1024;
+__global__ __launch_bounds__(kMaxBlockLen) void k_unmask(int32_t* __restrict__ tokens, uint8_t* __restrict__ masked,
+                                                         const float* __restrict__ conf,
+                                                         const int32_t* __restrict__ argmax,
+                                                         const int32_t* __restrict__ prompt_len,
+                                                         const int32_t* __restrict__ seq_len, int S, int block,
+                                                         int block_len, int n_unmask) {
+  __shared__ float c[kMaxBlockLen];
+  __shared__ uint8_t m[kMaxBlockLen];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int lo = prompt_len[b] + block * block_len;
+  const int hi = min(lo + block_len, seq_len[b]);
+  const int len = max(0, hi - lo);
+  const size_t base = (size_t)b * S + lo;
+  if (t < len) {
+    c[t] = conf[base + t];
+    m[t] = masked[base + t];
+  }
+  __syncthreads();
+  if (t < len && m[t]) {
+    int rank = 0;
+    const float ct = c[t];
+    for (int j = 0; j < len; ++j)
+      if (m[j] && (c[j] > ct || (c[j] == ct && j < t))) ++rank;
+    if (rank < n_unmask) {
+      tokens[base + t] = argmax[base + t];
+      masked[base + t] = 0;
+    }
+  }
+}
+
+inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+// ===========================================================================
+// launchers
+// ===========================================================================
+hipError_t launch_identity_sel(const int32_t* seq_len, int B, int S, int32_t* sel_idx, int32_t* sel_count,
+                               hipStream_t st) {
+  dim3 grid(cdiv(S, 256), B);
+  hipLaunchKernelGGL(k_identity_sel, grid, dim3(256), 0, st, seq_len, S, sel_idx, sel_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_off(const int32_t* sel_count, int32_t* row_off, int B, hipStream_t st) {
+  hipLaunchKernelGGL(k_row_off, dim3(1), dim3(64), 0, st, sel_count, row_off, B);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowmap(const int32_t* sel_idx, const int32_t* sel_count, const int32_t* row_off, int B, int S,
+                         const RowMap& rm, hipStream_t st) {
+  hipLaunchKernelGGL(k_tiles, dim3(1), dim3(256), 0, st, sel_count, row_off, B, rm.n_rows, rm.tile_row0,
+                     rm.tile_rows, rm.T_max, rm.tq);
+  hipLaunchKernelGGL(k_rowmap, dim3(cdiv(rm.R_max, 256)), dim3(256), 0, st, sel_idx, row_off, B, S, rm.R_max,
+                     rm.row_pos, rm.row_seq);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_sel(size_t elem_bytes, const void* src, int w, const int32_t* sel_idx,
+                             const int32_t* row_off, int B, int S, int R_max, void* dst, hipStream_t st) {
+  if (R_max <= 0) return hipSuccess;
+  const size_t rb = elem_bytes * (size_t)w;
+  if (rb % 16 == 0)
+    hipLaunchKernelGGL((k_copy_sel<16, false>), dim3(R_max), dim3(kRowThreads), 0, st, (const char*)src, rb, sel_idx,
+                       row_off, B, S, (char*)dst);
+  else
+    hipLaunchKernelGGL((k_copy_sel<1, false>), dim3(R_max), dim3(kRowThreads), 0, st, (const char*)src, rb, sel_idx,
+                       row_off, B, S, (char*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_sel(size_t elem_bytes, const void* rows, int w, const int32_t* sel_idx,
+                              const int32_t* row_off, int B, int S, int R_max, void* cache, hipStream_t st) {
+  if (R_max <= 0) return hipSuccess;
+  const size_t rb = elem_bytes * (size_t)w;
+  if (rb % 16 == 0)
+    hipLaunchKernelGGL((k_copy_sel<16, true>), dim3(R_max), dim3(kRowThreads), 0, st, (const char*)rows, rb, sel_idx,
+                       row_off, B, S, (char*)cache);
+  else
+    hipLaunchKernelGGL((k_copy_sel<1, true>), dim3(R_max), dim3(kRowThreads), 0, st, (const char*)rows, rb, sel_idx,
+                       row_off, B, S, (char*)cache);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(dl_dtype dt, const void* h_cur, const float* x_packed, const int32_t* off_all, void* h_prev,
+                        const float* conf, const int32_t* seq_len, int B, int S, int d, dl_score_kind kind,
+                        float alpha, float* scores, hipStream_t st) {
+  dim3 grid(cdiv(S, 4), B);
+  if (dt == DL_F32) {
+    if (x_packed)
+      hipLaunchKernelGGL((k_score<float, true>), grid, dim3(256), 0, st, (const float*)h_cur, x_packed, off_all,
+                         (float*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
+    else
+      hipLaunchKernelGGL((k_score<float, false>), grid, dim3(256), 0, st, (const float*)h_cur, x_packed, off_all,
+                         (float*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
+  } else {
+    if (x_packed)
+      hipLaunchKernelGGL((k_score<bf16_t, true>), grid, dim3(256), 0, st, (const bf16_t*)h_cur, x_packed, off_all,
+                         (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
+    else
+      hipLaunchKernelGGL((k_score<bf16_t, false>), grid, dim3(256), 0, st, (const bf16_t*)h_cur, x_packed, off_all,
+                         (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const float* scores, const int32_t* seq_len, int B, int S, dl_select_mode mode, float keep,
+                         float threshold, int32_t* sel_idx, int32_t* sel_count, hipStream_t st) {
+  hipLaunchKernelGGL(k_select, dim3(B), dim3(kSelThreads), 0, st, scores, seq_len, S, (int)mode, keep, threshold,
+                     sel_idx, sel_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(dl_dtype dt, const int32_t* tokens, const RowMap& rm, const void* E, int d, float* x,
+                        hipStream_t st) {
+  if (dt == DL_F32)
+    hipLaunchKernelGGL(k_embed<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, tokens, rm.row_pos,
+                       (const float*)E, d, x);
+  else
+    hipLaunchKernelGGL(k_embed<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, tokens, rm.row_pos,
+                       (const bf16_t*)E, d, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(size_t elem_bytes, const void* src, const int32_t* src_off, int S, int w, const RowMap& rm,
+                         void* dst, hipStream_t st) {
+  const size_t rb = elem_bytes * (size_t)w;
+  if (rb % 16 == 0)
+    hipLaunchKernelGGL(k_gather<16>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)src, src_off, S, rb,
+                       rm.row_pos, rm.row_seq, (char*)dst);
+  else
+    hipLaunchKernelGGL(k_gather<1>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)src, src_off, S, rb,
+                       rm.row_pos, rm.row_seq, (char*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(size_t elem_bytes, const void* rows, int w, const RowMap& rm, void* cache, hipStream_t st) {
+  const size_t rb = elem_bytes * (size_t)w;
+  if (rb % 16 == 0)
+    hipLaunchKernelGGL(k_scatter<16>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)rows, rb, rm.row_pos,
+                       (char*)cache);
+  else
+    hipLaunchKernelGGL(k_scatter<1>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)rows, rb, rm.row_pos,
+                       (char*)cache);
+  return hipGetLastError();
+}
+
+hipError_t launch_store_rows(dl_dtype dt, const float* x, int w, const RowMap& rm, void* dst, hipStream_t st) {
+  if (dt == DL_F32)
+    hipLaunchKernelGGL(k_store_rows<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, w, rm.row_pos, (float*)dst);
+  else
+    hipLaunchKernelGGL(k_store_rows<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, w, rm.row_pos,
+                       (bf16_t*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(dl_dtype dt, const float* x, const void* g, const RowMap& rm, int d, float eps, void* out,
+                          hipStream_t st) {
+  if (dt == DL_F32)
+    hipLaunchKernelGGL(k_rmsnorm<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, (const float*)g, rm.n_rows, d,
+                       eps, (float*)out);
+  else
+    hipLaunchKernelGGL(k_rmsnorm<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, (const bf16_t*)g, rm.n_rows,
+                       d, eps, (bf16_t*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(int S, int head_dim, float base, float2* table, hipStream_t st) {
+  const int half = head_dim / 2;
+  hipLaunchKernelGGL(k_rope_table, dim3(cdiv((long long)S * half, 256)), dim3(256), 0, st, S, half, head_dim,
+                     (double)base, table);
+  return hipGetLastError();
+}
+
+hipError_t launch_epi_qkv(dl_dtype dt, const float* P, int splits, const RowMap& rm, int S, int d, int head_dim,
+                          const float2* rope, void* q_out, void* k_cache, void* v_cache, hipStream_t st) {
+  if (dt == DL_F32)
+    hipLaunchKernelGGL(k_epi_qkv<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows,
+                       rm.row_pos, rm.row_seq, S, d, head_dim, rope, (float*)q_out, (float*)k_cache,
+                       (float*)v_cache);
+  else
+    hipLaunchKernelGGL(k_epi_qkv<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows,
+                       rm.row_pos, rm.row_seq, S, d, head_dim, rope, (bf16_t*)q_out, (bf16_t*)k_cache,
+                       (bf16_t*)v_cache);
+  return hipGetLastError();
+}
+
+hipError_t launch_epi_residual(const float* P, int splits, const RowMap& rm, int N, float* x, hipStream_t st) {
+  hipLaunchKernelGGL(k_epi_residual, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows, N, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_epi_swiglu(dl_dtype dt, const float* P, int splits, const RowMap& rm, int F, void* out,
+                             hipStream_t st) {
+  if (dt == DL_F32)
+    hipLaunchKernelGGL(k_epi_swiglu<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
+                       rm.n_rows, F, (float*)out);
+  else
+    hipLaunchKernelGGL(k_epi_swiglu<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
+                       rm.n_rows, F, (bf16_t*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_reduce(const float* P, int splits, const RowMap& rm, int m_base, int M_max, int V, float* conf,
+                            int32_t* argmax, float* logits_out, hipStream_t st) {
+  if (M_max <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_lm_reduce, dim3(M_max), dim3(kRowThreads), 0, st, P, splits, M_max, rm.n_rows, m_base,
+                     rm.row_pos, V, conf, argmax, logits_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_unmask(int32_t* tokens, uint8_t* masked, const float* conf, const int32_t* argmax,
+                         const int32_t* prompt_len, const int32_t* seq_len, int B, int S, int block, int block_len,
+                         int n_unmask, hipStream_t st) {
+  hipLaunchKernelGGL(k_unmask, dim3(B), dim3(kMaxBlockLen), 0, st, tokens, masked, conf, argmax, prompt_len, seq_len,
+                     S, block, block_len, n_unmask);
+  return hipGetLastError();
+}
+
+}  // namespace dtsk

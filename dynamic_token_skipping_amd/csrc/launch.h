@@ -1,0 +1,82 @@
+// Host-side launchers of libdtsk's kernels (internal; not part of the ABI).
+#pragma once
+
+#include "common.h"
+
+namespace dtsk {
+
+// ---- selections and row maps ------------------------------------------------
+hipError_t launch_identity_sel(const int32_t* seq_len, int B, int S, int32_t* sel_idx, int32_t* sel_count,
+                               hipStream_t st);
+// row_off = exclusive prefix of sel_count.
+hipError_t launch_row_off(const int32_t* sel_count, int32_t* row_off, int B, hipStream_t st);
+// Packed-row maps and attention query tiles of a selection with row_off set.
+hipError_t launch_rowmap(const int32_t* sel_idx, const int32_t* sel_count, const int32_t* row_off, int B, int S,
+                         const RowMap& rm, hipStream_t st);
+// Selection-driven gather / scatter (no row map needed): packed row r of
+// sequence b <-> flat row b*S + sel_idx[b*S + r - row_off[b]].
+hipError_t launch_gather_sel(size_t elem_bytes, const void* src, int w, const int32_t* sel_idx,
+                             const int32_t* row_off, int B, int S, int R_max, void* dst, hipStream_t st);
+hipError_t launch_scatter_sel(size_t elem_bytes, const void* rows, int w, const int32_t* sel_idx,
+                              const int32_t* row_off, int B, int S, int R_max, void* cache, hipStream_t st);
+
+// ---- scores and selection -----------------------------------------------------
+// Score of each valid row.  If x_packed != nullptr, the current input is the
+// fp32 packed row x_packed[off_all[b] + i] rounded to the storage type, and
+// h_prev is overwritten with it after scoring (one pass); otherwise h_cur is read.
+hipError_t launch_score(dl_dtype dt, const void* h_cur, const float* x_packed, const int32_t* off_all, void* h_prev,
+                        const float* conf, const int32_t* seq_len, int B, int S, int d, dl_score_kind kind,
+                        float alpha, float* scores, hipStream_t st);
+hipError_t launch_select(const float* scores, const int32_t* seq_len, int B, int S, dl_select_mode mode, float keep,
+                         float threshold, int32_t* sel_idx, int32_t* sel_count, hipStream_t st);
+
+// ---- row movement -------------------------------------------------------------
+hipError_t launch_embed(dl_dtype dt, const int32_t* tokens, const RowMap& rm, const void* E, int d, float* x,
+                        hipStream_t st);
+// dst[r] = src[src_row(r)]: src_row = off[row_seq] + (row_pos - row_seq*S) when
+// src_off != nullptr (packed source) else row_pos (padded [B,S,w] source).
+hipError_t launch_gather(size_t elem_bytes, const void* src, const int32_t* src_off, int S, int w, const RowMap& rm,
+                         void* dst, hipStream_t st);
+// cache[row_pos[r]] = rows[r] (same type)
+hipError_t launch_scatter(size_t elem_bytes, const void* rows, int w, const RowMap& rm, void* cache, hipStream_t st);
+// dst[row_pos[r]] = T(x[r]) for fp32 rows x
+hipError_t launch_store_rows(dl_dtype dt, const float* x, int w, const RowMap& rm, void* dst, hipStream_t st);
+
+// ---- normalisation and epilogues ------------------------------------------------
+hipError_t launch_rmsnorm(dl_dtype dt, const float* x, const void* g, const RowMap& rm, int d, float eps, void* out,
+                          hipStream_t st);
+hipError_t launch_rope_table(int S, int head_dim, float base, float2* table, hipStream_t st);
+hipError_t launch_epi_qkv(dl_dtype dt, const float* P, int splits, const RowMap& rm, int S, int d, int head_dim,
+                          const float2* rope, void* q_out, void* k_cache, void* v_cache, hipStream_t st);
+hipError_t launch_epi_residual(const float* P, int splits, const RowMap& rm, int N, float* x, hipStream_t st);
+hipError_t launch_epi_swiglu(dl_dtype dt, const float* P, int splits, const RowMap& rm, int F, void* out,
+                             hipStream_t st);
+
+// ---- GEMM: P[s][m][n] = sum_{k in split s} A[m][k] * W[n][k] ------------------------
+// W is given as up to 4 segments of n_seg rows each (segment i covers output
+// columns [i*n_seg, (i+1)*n_seg)).  Rows m >= *rm.n_rows are not computed.
+struct GemmPlan {
+  int splits;
+  int kind;  // 0 = SIMT, 1 = MFMA
+};
+GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K);
+// Rows [m_base, m_base + M_max) of A (A points at row m_base); rows at or
+// beyond *n_rows are skipped.  P is [splits][M_max][N].
+hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows,
+                       int m_base, int K, const void* const* Wseg, int n_seg, int N, float* P, hipStream_t st);
+
+// ---- attention ---------------------------------------------------------------------
+bool attention_supported(dl_dtype dt, int S, int head_dim);
+hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_len, const RowMap& rm, int S, int n_heads, int head_dim, void* out,
+                            hipStream_t st);
+
+// ---- LM head reduction and unmasking -------------------------------------------------
+// Packed rows [m_base, m_base + M_max) of the row map; P is [splits][M_max][V].
+hipError_t launch_lm_reduce(const float* P, int splits, const RowMap& rm, int m_base, int M_max, int V, float* conf,
+                            int32_t* argmax, float* logits_out, hipStream_t st);
+hipError_t launch_unmask(int32_t* tokens, uint8_t* masked, const float* conf, const int32_t* argmax,
+                         const int32_t* prompt_len, const int32_t* seq_len, int B, int S, int block, int block_len,
+                         int n_unmask, hipStream_t st);
+
+}  // namespace dtsk

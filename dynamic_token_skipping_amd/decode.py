@@ -1,0 +1,115 @@
+"""Device-side decoding driver over libdtsk: owns the caches as torch tensors
+(device memory only) and calls dl_denoise_step once per denoising step.
+
+The semi-autoregressive schedule (ES-dLLM section 1: a few most-confident
+masked tokens are unmasked per step; section 2B: a full refresh pass at set
+intervals) is host bookkeeping: which block is current, how many tokens to
+unmask, whether this step is a refresh step.  Everything computed per token
+runs in the library.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _lib as L
+
+
+class DeviceModel:
+    """Weights on the device plus the dl_model struct that points at them."""
+
+    def __init__(self, tensors: dict, n_heads: int, head_dim: int, dtype: str, rms_eps: float = 1e-5,
+                 rope_base: float = 10000.0):
+        self.t = tensors
+        emb = tensors["embed"]
+        self.vocab, self.d = emb.shape
+        self.d_ffn = tensors["layers"][0]["w_gate"].shape[0]
+        self.n_layers = len(tensors["layers"])
+        self.n_heads, self.head_dim = n_heads, head_dim
+        self.dtype = dtype
+        self.rms_eps, self.rope_base = rms_eps, rope_base
+        self._layers = (L.LayerW * self.n_layers)(*[L.layer_struct(lw) for lw in tensors["layers"]])
+
+    def dims(self, B: int, S: int) -> L.Dims:
+        return L.make_dims(B, S, self.d, self.n_heads, self.head_dim, self.d_ffn, self.vocab, self.n_layers,
+                           self.dtype, self.rms_eps, self.rope_base)
+
+    def struct(self, B: int, S: int) -> L.Model:
+        return L.Model(self.dims(B, S), L.ptr(self.t["embed"]), L.ptr(self.t["final_norm"]),
+                       L.ptr(self.t["lm_head"]), self._layers)
+
+
+def is_refresh_step(step: int, steps_per_block: int, refresh_interval: int) -> bool:
+    sib = step % steps_per_block
+    return sib == 0 or (refresh_interval > 0 and sib % refresh_interval == 0)
+
+
+class Decoder:
+    """Caches of a batch of sequences: prompt + gen_len masked positions each,
+    right-padded to S = max length."""
+
+    def __init__(self, model: DeviceModel, prompts: Sequence[torch.Tensor], sched, keep_logits: bool = False,
+                 device: str = "cuda", mask_id: Optional[int] = None):
+        self.m = model
+        self.sched = sched
+        self.B = len(prompts)
+        self.prompt_lens = [int(len(p)) for p in prompts]
+        self.seq_lens = [n + sched.gen_len for n in self.prompt_lens]
+        self.S = max(self.seq_lens)
+        B, S, d = self.B, self.S, model.d
+        mid = model.vocab - 1 if mask_id is None else mask_id
+        tdt = L.TORCH_DTYPES[L.DTYPES[model.dtype]]
+        tokens = torch.zeros((B, S), dtype=torch.int32)
+        masked = torch.zeros((B, S), dtype=torch.uint8)
+        for b, p in enumerate(prompts):
+            n = len(p)
+            tokens[b, :n] = p.to(torch.int32).cpu()
+            tokens[b, n:n + sched.gen_len] = mid
+            masked[b, n:n + sched.gen_len] = 1
+        self.tokens0, self.masked0 = tokens.to(device), masked.to(device)
+        self.tokens, self.masked = self.tokens0.clone(), self.masked0.clone()
+        self.seq_len = torch.tensor(self.seq_lens, dtype=torch.int32, device=device)
+        self.prompt_len = torch.tensor(self.prompt_lens, dtype=torch.int32, device=device)
+        self.h_prev = torch.zeros((B, S, d), dtype=tdt, device=device)
+        self.k_cache = torch.zeros((model.n_layers, B, S, d), dtype=tdt, device=device)
+        self.v_cache = torch.zeros((model.n_layers, B, S, d), dtype=tdt, device=device)
+        self.h_final = torch.zeros((B, S, d), dtype=tdt, device=device)
+        self.conf = torch.zeros((B, S), dtype=torch.float32, device=device)
+        self.argmax = torch.zeros((B, S), dtype=torch.int32, device=device)
+        self.scores = torch.zeros((B, S), dtype=torch.float32, device=device)
+        self.logits = torch.zeros((B, S, model.vocab), dtype=torch.float32, device=device) if keep_logits else None
+        self.sel = L.SelectionTensors(B, S, device)
+        self.dims = model.dims(B, S)
+        self.model_struct = model.struct(B, S)
+        self.ws = L.workspace(self.dims, sum(self.seq_lens), device)
+        self._seq_len_host = (ctypes.c_int32 * B)(*self.seq_lens)
+        self.state = L.State(L.ptr(self.tokens), L.ptr(self.masked), L.ptr(self.seq_len), L.ptr(self.prompt_len),
+                             L.ptr(self.h_prev), L.ptr(self.k_cache), L.ptr(self.v_cache), L.ptr(self.h_final),
+                             L.ptr(self.conf), L.ptr(self.argmax), L.ptr(self.logits), L.ptr(self.scores),
+                             self.sel.struct())
+        self.steps_per_block = sched.steps // (sched.gen_len // sched.block_len)
+        self.per_step = sched.block_len // self.steps_per_block
+
+    def reset(self):
+        """Back to the initial tokens and mask (caches are rebuilt by step 0's refresh)."""
+        self.tokens.copy_(self.tokens0)
+        self.masked.copy_(self.masked0)
+
+    def params(self, step: int, force_refresh: Optional[bool] = None, keep: Optional[float] = None,
+               mode: int = L.DL_SEL_TOPK, threshold: float = 0.0, n_unmask: Optional[int] = None) -> L.StepParams:
+        s = self.sched
+        refresh = (is_refresh_step(step, self.steps_per_block, s.refresh_interval) if force_refresh is None
+                   else force_refresh)
+        return L.StepParams(step // self.steps_per_block, s.block_len,
+                            self.per_step if n_unmask is None else n_unmask, s.skip_layer, int(bool(refresh)),
+                            L.SCORE_KINDS[s.score], s.alpha, mode, s.keep if keep is None else keep, threshold,
+                            ctypes.cast(self._seq_len_host, ctypes.POINTER(ctypes.c_int32)))
+
+    def step(self, step: int, **kw):
+        L.dl_denoise_step(self.model_struct, self.state, self.params(step, **kw), self.ws)
+
+    def run(self, n_steps: Optional[int] = None, **kw):
+        for t in range(self.sched.steps if n_steps is None else n_steps):
+            self.step(t, **kw)

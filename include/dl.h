@@ -1,0 +1,225 @@
+/*
+ * dl.h -- C ABI of the early-skip partial-recompute step of masked-diffusion
+ * LLM decoding, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (ES-dLLM: Efficient Inference for Diffusion Large Language Models
+ * by Early-Skipping, technical summary sections 1-2; DyLLM: Efficient Diffusion
+ * LLM Inference via Saliency-based Token Selection and Partial Attention,
+ * technical summary section 2):
+ *   at each denoising step the first s layers run on every token; at layer s
+ *   each token gets an importance score from the change of its hidden state
+ *   since the previous step and its previous confidence; only the top-k tokens
+ *   (k = (1 - r)|S|) go through layers s..L-1, whose key/value caches are
+ *   updated in place for those rows (scatter) and reused for the others; the
+ *   most confident masked tokens of the current block are then unmasked.  A
+ *   full pass over every token (refresh) runs at set intervals.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; scratch memory comes from the
+ *     caller's workspace (size from dl_workspace_bytes).
+ *   - Layouts are row-major and contiguous.  Weight matrices are [out, in].
+ *     Per-sequence tensors are padded to [B, S, ...]; row i of sequence b is at
+ *     flat row b*S + i.  Every pointer must be 16-byte aligned.
+ *   - Storage type (dims.dtype) applies to weights, embeddings, gains, the
+ *     K/V/hidden caches and the inter-kernel activations; accumulation is fp32.
+ *     The residual stream of rows in flight (x_rows) is always fp32.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls validate on
+ *     the host, enqueue, and return; device faults surface at the caller's next
+ *     synchronisation.
+ *   - On a failed validation a call returns a negative dl_status, enqueues
+ *     nothing and writes nothing.  A launch failure returns DL_E_HIP.
+ *     dl_last_error() returns a thread-local text for the last failure.
+ *   - Packed rows: a selection lists, per sequence b, sel_count[b] ascending
+ *     positions in sel_idx[b*S ...]; packed row r of sequence b is
+ *     row_off[b] + j for its j-th selected position.  Row buffers such as
+ *     x_rows are [k_total_max, width]; only the first row_off[B] rows are
+ *     touched (row_off lives on the device, so threshold selections need no
+ *     host synchronisation).
+ */
+#ifndef DL_H
+#define DL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DL_ABI_VERSION 1
+
+typedef enum {
+  DL_OK = 0,
+  DL_E_ARG = -1,        /* null pointer, bad enum, non-positive size */
+  DL_E_SHAPE = -2,      /* inconsistent dimensions (d != H*dh, k > S, ...) */
+  DL_E_DTYPE = -3,      /* unsupported storage type for this entry point */
+  DL_E_ALIGN = -4,      /* pointer not 16-byte aligned */
+  DL_E_WORKSPACE = -5,  /* workspace too small (see dl_workspace_bytes) */
+  DL_E_HIP = -6,        /* HIP runtime error (text in dl_last_error) */
+  DL_E_UNSUPPORTED = -7 /* valid request outside what this build implements */
+} dl_status;
+
+typedef enum { DL_F32 = 0, DL_BF16 = 1 } dl_dtype;
+
+/* Importance score of a row, from its current skip-layer input x, its cached
+ * previous-step input h and its cached confidence c (max softmax probability):
+ *   DL_SCORE_ESDLLM        alpha*c + (1-alpha)*||x-h||_1 / (sqrt(d)*||h||_2)
+ *                          (ES-dLLM, section 2A, eq. I; alpha = 0.5 there)
+ *   DL_SCORE_RELL2_INVCONF ||x-h||_2 / ||h||_2 + (1 - c)
+ *   DL_SCORE_COSINE        1 - x.h / (||x||_2 ||h||_2)
+ *                          (DyLLM, section 2A: low similarity = salient)
+ * Denominators are floored at FLT_MIN.  Larger score = more important. */
+typedef enum { DL_SCORE_ESDLLM = 0, DL_SCORE_RELL2_INVCONF = 1, DL_SCORE_COSINE = 2 } dl_score_kind;
+
+/* DL_SEL_TOPK: per sequence the k = ceil(keep * len) rows (clamped to
+ * [1, len], keep read as float32) with the largest scores, lower index first
+ * among equal scores, NaN ranked last (ES-dLLM section 2B: k = (1 - r_l)|S|).
+ * DL_SEL_THRESHOLD: every row with score > threshold (DyLLM section 2A). */
+typedef enum { DL_SEL_TOPK = 0, DL_SEL_THRESHOLD = 1 } dl_select_mode;
+
+typedef struct {
+  int32_t B;          /* sequences in the batch */
+  int32_t S;          /* padded row capacity per sequence */
+  int32_t d;          /* hidden size = n_heads * head_dim */
+  int32_t n_heads;
+  int32_t head_dim;   /* even */
+  int32_t d_ffn;      /* SwiGLU inner size */
+  int32_t vocab;
+  int32_t n_layers;
+  dl_dtype dtype;
+  float rms_eps;      /* RMSNorm epsilon */
+  float rope_base;    /* RoPE base (rotate-half pairs (j, j + head_dim/2)) */
+} dl_dims;
+
+typedef struct {
+  int32_t *sel_idx;   /* [B, S] device: ascending positions, first sel_count[b] valid */
+  int32_t *sel_count; /* [B] device */
+  int32_t *row_off;   /* [B + 1] device: exclusive prefix sum of sel_count */
+} dl_selection;
+
+/* One layer's weights (device, storage dtype).  Norm gains are [d]; wq, wk,
+ * wv, wo are [d, d]; w_gate, w_up are [d_ffn, d]; w_down is [d, d_ffn]. */
+typedef struct {
+  const void *attn_norm, *wq, *wk, *wv, *wo;
+  const void *ffn_norm, *w_gate, *w_up, *w_down;
+} dl_layer_w;
+
+typedef struct {
+  dl_dims dims;
+  const void *embed;          /* [vocab, d] device */
+  const void *final_norm;     /* [d] device */
+  const void *lm_head;        /* [vocab, d] device (untied) */
+  const dl_layer_w *layers;   /* HOST array of n_layers entries */
+} dl_model;
+
+/* Decoding state, all device memory owned by the caller. */
+typedef struct {
+  int32_t *tokens;            /* [B, S] current ids ([MASK] id where masked) */
+  uint8_t *masked;            /* [B, S] 1 = still masked */
+  const int32_t *seq_len;     /* [B] valid rows (prompt + generation) */
+  const int32_t *prompt_len;  /* [B] */
+  void *h_prev;               /* [B, S, d] skip-layer input of the previous step */
+  void *k_cache, *v_cache;    /* [L, B, S, d] rotated keys / values per layer
+                                 (layers < skip layer are per-step scratch) */
+  void *h_final;              /* [B, S, d] last-layer output (before final norm) */
+  float *conf;                /* [B, S] max softmax probability */
+  int32_t *argmax;            /* [B, S] most likely id (lowest id on ties) */
+  float *logits;              /* [B, S, vocab] fp32, or NULL to skip writing them */
+  float *scores;              /* [B, S] this step's scores, or NULL */
+  dl_selection sel;           /* this step's recomputed rows (written by the step) */
+} dl_state;
+
+typedef struct {
+  int32_t block;              /* current block: unmask window starts at prompt_len + block*block_len */
+  int32_t block_len;
+  int32_t n_unmask;           /* tokens unmasked per sequence this step */
+  int32_t skip_layer;         /* s: layers [0, s) on every row; 1 <= s <= n_layers */
+  int32_t full_refresh;       /* nonzero: every row through every layer */
+  dl_score_kind score;
+  float alpha;
+  dl_select_mode mode;
+  float keep_ratio;           /* in (0, 1] for DL_SEL_TOPK */
+  float threshold;            /* for DL_SEL_THRESHOLD */
+  const int32_t *seq_len_host;/* [B] HOST copy of state.seq_len, used for grid sizing only */
+} dl_step_params;
+
+/* ---------------------------------------------------------------------------
+ * Score and select (ES-dLLM section 2A eq. I and 2B top-k; DyLLM section 2A
+ * threshold).  h_cur and h_prev are [B, S, d] in dims.dtype, conf is [B, S].
+ * Writes `out` (device arrays sized as in dl_selection) and, if non-NULL,
+ * scores[B, S] (fp32; padding rows untouched).  Reads only; h_prev is not
+ * updated.  Needs dl_workspace_bytes(dims, 0) bytes of workspace.
+ * ------------------------------------------------------------------------- */
+dl_status dl_score_select(const dl_dims *dims, const void *h_cur, const void *h_prev, const float *conf,
+                          const int32_t *seq_len, dl_score_kind kind, float alpha, dl_select_mode mode,
+                          float keep_ratio, float threshold, dl_selection *out, float *scores_or_null,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* Gather selected rows (ES-dLLM section 2B: only the top-k tokens go on):
+ * dst[row_off[b] + j, :] = src[b, sel_idx[b][j], :]; src is [B, S, w] and dst
+ * [k_total_max, w], both of `dtype` (DL_F32 or DL_BF16). */
+dl_status dl_gather(const dl_dims *dims, const void *src, int32_t w, dl_dtype dtype, const dl_selection *sel,
+                    int32_t k_total_max, void *dst, void *stream);
+
+/* Scatter packed rows back into a cache (ES-dLLM section 2B: in-place update
+ * of the selected rows; other rows keep every byte):
+ * cache[b, sel_idx[b][j], :] = rows[row_off[b] + j, :]. */
+dl_status dl_scatter_cache(const dl_dims *dims, const void *rows, int32_t w, dl_dtype dtype,
+                           const dl_selection *sel, int32_t k_total_max, void *cache, void *stream);
+
+/* Attention sub-block of one layer on the selected rows (ES-dLLM section 2B,
+ * DyLLM section 2B): x_rows (fp32 [k_total_max, d], in/out) +=
+ *   Wo * Attn(RoPE(Wq n(x)), K, V), where the rows' fresh RoPE(Wk n(x)) and
+ * Wv n(x) are first written into k_cache/v_cache ([B, S, d] of this layer) at
+ * their positions, and each row attends over keys 0..seq_len[b]-1 of its own
+ * sequence (bidirectional).  n = RMSNorm with layer->attn_norm. */
+dl_status dl_partial_attn(const dl_dims *dims, const dl_layer_w *layer, float *x_rows, const dl_selection *sel,
+                          const int32_t *seq_len, int32_t k_total_max, void *k_cache, void *v_cache, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* SwiGLU FFN sub-block on packed rows: x += Wd (silu(Wg n(x)) * Wu n(x)),
+ * n = RMSNorm with layer->ffn_norm.  x_rows is fp32 [k_total_max, d]; the
+ * rows actually processed are the first sel->row_off[B]. */
+dl_status dl_ffn_rows(const dl_dims *dims, const dl_layer_w *layer, float *x_rows, const dl_selection *sel,
+                      int32_t k_total_max, void *ws, size_t ws_bytes, void *stream);
+
+/* Final norm + LM head on packed rows, then confidence (max softmax
+ * probability = 1 / sum exp(l - max)) and argmax (lowest id on ties), scattered
+ * with h_final (= x_rows in storage dtype) and, if non-NULL, the fp32 logits
+ * into the [B, S] caches at the selected positions (ES-dLLM section 2A: c is
+ * the maximum probability; section 2B: caches of skipped rows are reused). */
+dl_status dl_lm_head_rows(const dl_dims *dims, const void *final_norm, const void *lm_head, const float *x_rows,
+                          const dl_selection *sel, int32_t k_total_max, float *conf, int32_t *argmax,
+                          void *h_final, float *logits_or_null, void *ws, size_t ws_bytes, void *stream);
+
+/* Unmask (ES-dLLM section 1: only the most confident masked tokens are
+ * unmasked each step): per sequence, among masked positions in
+ * [prompt_len + block*block_len, +block_len) (clipped to seq_len), the
+ * n_unmask with the highest conf (lower index on ties) get tokens = argmax
+ * and masked = 0. */
+dl_status dl_unmask(const dl_dims *dims, int32_t *tokens, uint8_t *masked, const float *conf,
+                    const int32_t *argmax, const int32_t *prompt_len, const int32_t *seq_len, int32_t block,
+                    int32_t block_len, int32_t n_unmask, void *stream);
+
+/* One whole denoising step: embed; layers [0, s) on every valid row; then
+ *   refresh: layers [s, L) on every row, h_prev <- layer-s input of every row;
+ *   skip:    score every row against h_prev, h_prev <- layer-s input of every
+ *            row, select, layers [s, L) on the selected rows only;
+ * LM head + scatter for the rows that went through every layer; unmask.
+ * state->sel receives the selection (all rows on a refresh step). */
+dl_status dl_denoise_step(const dl_model *model, dl_state *state, const dl_step_params *params, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* Workspace bytes for any entry point above on a batch whose valid rows sum
+ * to at most max_rows (0: B*S). */
+size_t dl_workspace_bytes(const dl_dims *dims, int32_t max_rows);
+
+const char *dl_status_string(dl_status s);
+const char *dl_last_error(void);
+int32_t dl_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DL_H */

@@ -1,0 +1,100 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/dl.h declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dynamic_token_skipping_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "dl.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\S.*?\b(dl_[a-z_]+)\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTS)
+
+
+def test_abi_version(lib):
+    assert lib.dl_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in range(-7, 1):
+        assert lib.dl_status_string(code)
+
+
+def _dims(**kw):
+    base = dict(B=1, S=512, d=4096, n_heads=32, head_dim=128, d_ffn=11008, vocab=126464, n_layers=32, dtype="bf16")
+    base.update(kw)
+    return L.make_dims(**base)
+
+
+def test_workspace_bytes(lib):
+    a = L.workspace_bytes(_dims(), 128)
+    b = L.workspace_bytes(_dims(), 512)
+    assert 0 < a < b
+    assert L.workspace_bytes(_dims(d=4000)) == 0          # d != H*dh
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=4000), -2), (dict(head_dim=127, d=32 * 127), -2), (dict(dtype=7), -3), (dict(B=0), -1),
+    (dict(S=9000), -7), (dict(B=2000), -7),
+])
+def test_bad_dims_rejected(lib, kw, code):
+    d = _dims(**kw)
+    s = L.Selection(16, 16, 16)
+    r = lib.dl_score_select(ctypes.byref(d), 16, 32, 16, 16, 0, 0.5, 0, 0.25, 0.0, ctypes.byref(s), None, 16, 1 << 30,
+                            None)
+    assert r == code, lib.dl_last_error()
+
+
+def test_null_and_alignment(lib):
+    d = _dims()
+    s = L.Selection(16, 16, 16)
+    assert lib.dl_score_select(ctypes.byref(d), None, 32, 16, 16, 0, 0.5, 0, 0.25, 0.0, ctypes.byref(s), None, 16,
+                               1 << 30, None) == -1
+    assert b"h_cur" in lib.dl_last_error()
+    assert lib.dl_score_select(ctypes.byref(d), 18, 32, 16, 16, 0, 0.5, 0, 0.25, 0.0, ctypes.byref(s), None, 16,
+                               1 << 30, None) == -4
+    assert lib.dl_score_select(ctypes.byref(d), 32, 32, 16, 16, 0, 0.5, 0, 0.25, 0.0, ctypes.byref(s), None, 16,
+                               1 << 30, None) == -1                    # aliasing
+    assert lib.dl_score_select(ctypes.byref(d), 16, 32, 16, 16, 0, 0.5, 0, 1.5, 0.0, ctypes.byref(s), None, 16,
+                               1 << 30, None) == -1                    # keep > 1
+    assert lib.dl_score_select(ctypes.byref(d), 16, 32, 16, 16, 9, 0.5, 0, 0.5, 0.0, ctypes.byref(s), None, 16,
+                               1 << 30, None) == -1                    # score kind
+    assert lib.dl_score_select(ctypes.byref(d), 16, 32, 16, 16, 0, 0.5, 0, 0.5, 0.0, ctypes.byref(s), None, 16,
+                               8, None) == -5                          # workspace
+
+
+def test_step_validation(lib):
+    d = _dims(n_layers=2)
+    lw = (L.LayerW * 2)(*[L.LayerW(*([16] * 9)) for _ in range(2)])
+    m = L.Model(d, 16, 16, 16, lw)
+    st = L.State(16, 16, 16, 16, 16, 16, 16, 16, 16, 16, None, None, L.Selection(16, 16, 16))
+    lens = (ctypes.c_int32 * 1)(512)
+    p = L.StepParams(0, 32, 1, 3, 0, 0, 0.5, 0, 0.25, 0.0, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)))
+    assert lib.dl_denoise_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(p), 16, 1 << 40, None) == -1
+    assert b"skip_layer" in lib.dl_last_error()
+    p.skip_layer = 1
+    lens[0] = 600
+    assert lib.dl_denoise_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(p), 16, 1 << 40, None) == -2
+    lens[0] = 512
+    assert lib.dl_denoise_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(p), 16, 64, None) == -5
+    p.block_len = 4096
+    assert lib.dl_denoise_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(p), 16, 1 << 40, None) == -7

@@ -1,0 +1,177 @@
+"""GPU parity at the 8B-class layer shape (d 4096, 32x128 heads, FFN 11008,
+S 512): the standalone entry points against the oracle on seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import host, row_rel_err, selection_diff_ok
+from oracle import esdllm as E
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def lay():
+    import dynamic_token_skipping_amd as D
+    wl = workloads.workload("layer8b")
+    m = workloads.make_model(wl.dims, wl.seed, "bf16", "cuda")
+    st = workloads.make_layer_state(wl, "cuda")
+    S = wl.prompt_len
+    dims = D.make_dims(1, S, wl.dims.d, wl.dims.n_heads, wl.dims.head_dim, wl.dims.d_ffn, wl.dims.vocab, 1, "bf16")
+    ws = D.workspace(dims, S)
+    seq_len = torch.tensor([S], dtype=torch.int32, device="cuda")
+    lw_np = {k: host(v) for k, v in m["layers"][0].items()}
+    return dict(wl=wl, m=m, st=st, S=S, dims=dims, ws=ws, seq_len=seq_len, lw_np=lw_np, D=D,
+                h_prev=host(st["h_prev"]), h_cur=host(st["h_cur"]), conf=host(st["conf"]))
+
+
+@pytest.mark.parametrize("keep", [1.0, 0.5, 0.25, 0.125])
+def test_score_select_matches_oracle(lay, keep):
+    D = lay["D"]
+    sel = D.SelectionTensors(1, lay["S"])
+    scores = torch.zeros((1, lay["S"]), dtype=torch.float32, device="cuda")
+    D.dl_score_select(lay["dims"], lay["st"]["h_cur"], lay["st"]["h_prev"], lay["st"]["conf"], lay["seq_len"],
+                      "esdllm", 0.5, D.DL_SEL_TOPK, keep, 0.0, sel, scores=scores, ws=lay["ws"])
+    torch.cuda.synchronize()
+    o_sc = E.score_rows("esdllm", lay["h_cur"], lay["h_prev"], lay["conf"], 0.5)
+    g_sc = host(scores[0])
+    assert np.abs(g_sc - o_sc).max() <= 1e-5 * np.abs(o_sc).max()
+    k = E.keep_count(keep, lay["S"])
+    o_sel = E.select_topk(o_sc, k)
+    g_sel = sel.rows()[0]
+    assert len(g_sel) == k and g_sel == sorted(g_sel)
+    assert int(sel.row_off[1]) == k
+    ok, nd = selection_diff_ok(g_sel, o_sel, o_sc, k, band_abs=1e-4)
+    assert ok and nd == 0, f"{nd} rows differ"
+
+
+def test_changed_rows_win_when_confidence_is_flat(lay):
+    """With every confidence equal, eq. I ranks rows by their relative L1
+    change alone, so keeping as many rows as were given the large change keeps
+    exactly those rows."""
+    D = lay["D"]
+    sel = D.SelectionTensors(1, lay["S"])
+    flat = torch.full_like(lay["st"]["conf"], 0.5)
+    changed = lay["st"]["changed_rows"].tolist()
+    keep = len(changed) / lay["S"]                       # 102/512, exact in float32
+    D.dl_score_select(lay["dims"], lay["st"]["h_cur"], lay["st"]["h_prev"], flat, lay["seq_len"], "esdllm", 0.5,
+                      D.DL_SEL_TOPK, keep, 0.0, sel, ws=lay["ws"])
+    torch.cuda.synchronize()
+    assert len(changed) == E.keep_count(keep, lay["S"])
+    assert sel.rows()[0] == changed
+
+
+def test_threshold_select(lay):
+    D = lay["D"]
+    sel = D.SelectionTensors(1, lay["S"])
+    o_sc = E.score_rows("esdllm", lay["h_cur"], lay["h_prev"], lay["conf"], 0.5)
+    tau = float(np.sort(o_sc)[::-1][99] + np.sort(o_sc)[::-1][100]) / 2     # between the 100th and 101st
+    D.dl_score_select(lay["dims"], lay["st"]["h_cur"], lay["st"]["h_prev"], lay["st"]["conf"], lay["seq_len"],
+                      "esdllm", 0.5, D.DL_SEL_THRESHOLD, 1.0, tau, sel, ws=lay["ws"])
+    torch.cuda.synchronize()
+    assert sel.rows()[0] == E.select_threshold(o_sc, tau).tolist()
+
+
+@pytest.mark.parametrize("keep", [1.0, 0.25, 0.125])
+def test_partial_layer_matches_oracle(lay, keep):
+    """Attention + FFN sub-blocks on the selected rows against stale K/V."""
+    D = lay["D"]
+    wl, S, d = lay["wl"], lay["S"], lay["wl"].dims.d
+    o_sc = E.score_rows("esdllm", lay["h_cur"], lay["h_prev"], lay["conf"], 0.5)
+    rows = E.select_topk(o_sc, E.keep_count(keep, S))
+    k = len(rows)
+    sel = D.SelectionTensors(1, S)
+    sel.sel_idx[0, :k] = torch.as_tensor(rows, dtype=torch.int32)
+    sel.sel_count[0] = k
+    sel.row_off[1] = k
+    x = lay["st"]["h_cur"][0:S].float()[torch.as_tensor(rows, device="cuda")].contiguous()
+    kc = lay["st"]["k"].clone().reshape(1, S, d)
+    vc = lay["st"]["v"].clone().reshape(1, S, d)
+    lw = lay["m"]["layers"][0]
+    D.dl_partial_attn(lay["dims"], lw, x, sel, lay["seq_len"], k, kc, vc, lay["ws"])
+    D.dl_ffn_rows(lay["dims"], lw, x, sel, k, lay["ws"])
+    torch.cuda.synchronize()
+    K = host(lay["st"]["k"])
+    V = host(lay["st"]["v"])
+    y = E.layer_forward(lay["h_cur"][rows], rows, lay["lw_np"], K, V, S, wl.dims)
+    assert row_rel_err(host(x), y) <= TOL
+    assert row_rel_err(host(kc[0])[rows], K[rows]) <= TOL
+    assert row_rel_err(host(vc[0])[rows], V[rows]) <= TOL
+    other = np.setdiff1d(np.arange(S), rows)
+    assert torch.equal(kc[0][other], lay["st"]["k"][other]) and torch.equal(vc[0][other], lay["st"]["v"][other])
+
+
+def test_lm_head_rows_matches_oracle(lay):
+    D = lay["D"]
+    S, d, V = lay["S"], lay["wl"].dims.d, lay["wl"].dims.vocab
+    rows = np.arange(3, S, 4)                              # 128 rows
+    k = len(rows)
+    sel = D.SelectionTensors(1, S)
+    sel.sel_idx[0, :k] = torch.as_tensor(rows, dtype=torch.int32)
+    sel.sel_count[0] = k
+    sel.row_off[1] = k
+    x = lay["st"]["h_cur"].float()[torch.as_tensor(rows, device="cuda")].contiguous()
+    conf = torch.full((1, S), -1.0, device="cuda")
+    amax = torch.full((1, S), -1, dtype=torch.int32, device="cuda")
+    hfin = torch.zeros((1, S, d), dtype=torch.bfloat16, device="cuda")
+    logits = torch.zeros((1, S, V), dtype=torch.float32, device="cuda")
+    D.dl_lm_head_rows(lay["dims"], lay["m"]["final_norm"], lay["m"]["lm_head"], x, sel, k, conf, amax, hfin, logits,
+                      lay["ws"])
+    torch.cuda.synchronize()
+    lg = E.lm_logits(lay["h_cur"][rows], host(lay["m"]["final_norm"]), host(lay["m"]["lm_head"]), 1e-5)
+    c, a = E.conf_argmax(lg)
+    assert row_rel_err(host(logits[0])[rows], lg) <= TOL
+    assert np.abs(host(conf[0])[rows] - c).max() <= TOL * c.max()
+    srt = np.sort(lg, axis=1)
+    clear = (srt[:, -1] - srt[:, -2]) > 1e-2 * np.abs(lg).max(axis=1)
+    assert clear.sum() > k // 2
+    assert np.array_equal(amax[0].cpu().numpy()[rows][clear], a[clear])
+    other = np.setdiff1d(np.arange(S), rows)
+    assert (conf[0][other] == -1).all() and (amax[0][other] == -1).all()
+    assert torch.equal(hfin[0][torch.as_tensor(rows, device="cuda")], x.to(torch.bfloat16))
+
+
+def test_gather_scatter_roundtrip(lay):
+    D = lay["D"]
+    S, d = lay["S"], lay["wl"].dims.d
+    g = torch.Generator(device="cuda").manual_seed(5)
+    rows = torch.randperm(S, generator=g, device="cuda")[:77].sort().values.to(torch.int32)
+    sel = D.SelectionTensors(1, S)
+    sel.sel_idx[0, :77] = rows
+    sel.sel_count[0] = 77
+    sel.row_off[1] = 77
+    src = lay["st"]["h_cur"].reshape(1, S, d)
+    dst = torch.empty((77, d), dtype=torch.bfloat16, device="cuda")
+    D.dl_gather(lay["dims"], src, d, D.DL_BF16, sel, 77, dst)
+    cache = torch.zeros((1, S, d), dtype=torch.bfloat16, device="cuda")
+    D.dl_scatter_cache(lay["dims"], dst, d, D.DL_BF16, sel, 77, cache)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src[0][rows.long()])
+    assert torch.equal(cache[0][rows.long()], dst)
+    mask = torch.ones(S, dtype=torch.bool, device="cuda")
+    mask[rows.long()] = False
+    assert (cache[0][mask] == 0).all()
+
+
+def test_unmask_matches_oracle(lay):
+    D = lay["D"]
+    S = lay["S"]
+    rng = np.random.default_rng(9)
+    conf = rng.choice(np.array([0.1, 0.2, 0.2, 0.5, 0.9], np.float32), size=S)
+    masked = (rng.uniform(size=S) < 0.7).astype(np.uint8)
+    masked[:100] = 0
+    prompt = torch.tensor([100], dtype=torch.int32, device="cuda")
+    for block, bl, n in ((0, 32, 1), (2, 32, 5), (3, 64, 64), (0, 412, 7)):
+        tok = torch.full((1, S), 7, dtype=torch.int32, device="cuda")
+        am = torch.arange(S, dtype=torch.int32, device="cuda").reshape(1, S)
+        msk = torch.as_tensor(masked).reshape(1, S).cuda()
+        D.dl_unmask(lay["dims"], tok, msk, torch.as_tensor(conf).reshape(1, S).cuda(), am, prompt, lay["seq_len"],
+                    block, bl, n)
+        torch.cuda.synchronize()
+        lo = 100 + block * bl
+        want = E.unmask(masked.astype(bool), conf.astype(np.float64), lo, min(lo + bl, S), n)
+        got = np.nonzero(masked.astype(bool) & ~msk[0].cpu().numpy().astype(bool))[0]
+        assert got.tolist() == want.tolist()
+        assert (tok[0].cpu().numpy()[want] == want).all()
