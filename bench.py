@@ -1,0 +1,186 @@
+"""Benchmark: denoising steps/s and generated tokens/s of the early-skip decode
+of a 32-layer 8B-class masked-diffusion model (d 4096, 32x128 heads, FFN
+11008, vocab 126464, random-init bf16 weights) on one MI355X: batch 1,
+256 uniform prompt tokens + 256 masked, blocks of 32, 256 steps x 1 token,
+skip at layer 4 with keep = 25% (128 of 512 rows recomputed in layers 4..31).
+
+A step is one dl_denoise_step (embed, 4 full-row layers, score + top-k,
+28 partial layers on the kept rows, LM head + confidence, unmask; every 32nd
+step is a full refresh).  Inputs are resident in HBM before the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--workload", default="full8b")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, model_gpu, prompts, budget_s: float = 20.0):
+    """Time the fp64 oracle on host cores on a bounded sample of one skip step.
+
+    The sample runs, once each, the three kinds of work a skip step is made of:
+    one layer on every row (the prefix kind, 512 rows), one partial layer on the
+    kept rows (128 rows against the full K/V cache), and the LM head with
+    confidence/argmax on the kept rows; the per-step time is then
+    s * t_full + (L - s) * t_partial + t_lm + t_score.  Layer 0's weights stand
+    in for every layer (same shapes).
+    """
+    import numpy as np
+    import torch
+
+    from oracle import esdllm as E
+    import workloads
+
+    dims, sched = wl.dims, wl.sched
+    threads = len(os.sched_getaffinity(0))
+    lw = {k: workloads.host_f64(v) for k, v in model_gpu["layers"][0].items()}
+    fin = workloads.host_f64(model_gpu["final_norm"])
+    lm = workloads.host_f64(model_gpu["lm_head"])
+    emb = model_gpu["embed"]
+    n = len(prompts[0]) + sched.gen_len
+    tokens = torch.cat([prompts[0].cpu(), torch.full((sched.gen_len,), dims.vocab - 1)])
+    x = workloads.host_f64(emb[tokens.to(emb.device)])
+    K = np.zeros((n, dims.d))
+    V = np.zeros((n, dims.d))
+    pos = np.arange(n)
+    k = E.keep_count(sched.keep, n)
+    rows = np.arange(0, n, n // k)[:k]
+    conf = np.random.default_rng(0).uniform(size=n)
+    t_full = t_part = t_lm = t_sc = 0.0
+    reps = 0
+    while reps == 0 or (t_full + t_part + t_lm + t_sc < budget_s and reps < 50):
+        t0 = time.perf_counter()
+        x1 = E.layer_forward(x, pos, lw, K, V, n, dims)
+        t_full += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        E.layer_forward(x1[rows], rows, lw, K, V, n, dims)
+        t_part += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        E.conf_argmax(E.lm_logits(x1[rows], fin, lm, dims.rms_eps))
+        t_lm += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        E.select_topk(E.score_rows(sched.score, x1, x, conf, sched.alpha), k)
+        t_sc += time.perf_counter() - t0
+        reps += 1
+    measured = t_full + t_part + t_lm + t_sc
+    t_full, t_part, t_lm, t_sc = (v / reps for v in (t_full, t_part, t_lm, t_sc))
+    s = sched.skip_layer
+    per_step = s * t_full + (dims.n_layers - s) * t_part + t_lm + t_sc
+    return {"value": 1.0 / per_step, "unit": "denoise steps/s (skip step)", "cores": threads, "kind": "oracle",
+            "sample": (f"one skip step of the same workload assembled from timed pieces (mean of {reps} repeats): "
+                       f"1 full-row layer "
+                       f"({n} rows, {t_full:.2f} s) x {s}, 1 partial layer ({k} rows vs {n} keys, {t_part:.2f} s) x "
+                       f"{dims.n_layers - s}, LM head + confidence on {k} rows ({t_lm:.2f} s), score+select "
+                       f"({t_sc:.3f} s); fp64 numpy, layer 0 weights for every layer"),
+            "seconds_measured": round(measured, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import workloads
+    from dynamic_token_skipping_amd import (DL_KC_ATTN, DL_KC_GEMM, DL_KC_LMHEAD, Decoder, DeviceModel,
+                                            dl_timing_enable, dl_timing_read, dl_timing_reset)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = workloads.workload(args.workload)
+    dims, sched = wl.dims, wl.sched
+    t0 = time.time()
+    model = workloads.make_model(dims, wl.seed, wl.dtype, "cuda")
+    prompts, lens = workloads.make_prompt(wl)
+    dec = Decoder(DeviceModel(model, dims.n_heads, dims.head_dim, wl.dtype), prompts, sched)
+    torch.cuda.synchronize()
+    print(f"# setup {time.time() - t0:.1f} s: {dims.model_params() / 1e9:.2f} B params", file=sys.stderr, flush=True)
+
+    # warm-up (untimed), then restart the decode from its first step
+    for t in range(args.warmup):
+        dec.step(t % sched.steps)
+    dec.reset()
+    torch.cuda.synchronize()
+
+    dl_timing_reset()
+    for kc in (DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD):
+        dl_timing_enable(kc, True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        t = i % sched.steps
+        if t == 0 and i > 0:
+            dec.reset()
+        dec.step(t)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    for kc in (DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD):
+        dl_timing_enable(kc, False)
+    ms = start.elapsed_time(end)
+    steps_per_s = args.steps / (ms / 1e3)
+    tok_per_s = steps_per_s * dec.per_step * dec.B
+
+    g = dl_timing_read(DL_KC_GEMM)
+    a = dl_timing_read(DL_KC_ATTN)
+    lmh = dl_timing_read(DL_KC_LMHEAD)
+    gemm_gbs = g["bytes"] / (g["ms"] / 1e3) / 1e9 if g["ms"] > 0 else 0.0
+    roofline = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "k_gemm_mfma (every layer product: QKV, O, gate/up, down)",
+                "launches": g["launches"], "avg_launch_us": round(g["ms"] * 1e3 / max(g["launches"], 1), 2),
+                "alg_bytes_per_launch": round(g["bytes"] / max(g["launches"], 1))}
+    out = {
+        "metric": "denoise steps/sec & gen tokens/sec at keep=25% (8B-class); HBM GB/s vs peak",
+        "value": round(steps_per_s, 3), "unit": "denoise steps/s",
+        "gen_tokens_per_s": round(tok_per_s, 3),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: 32-layer 8B-class random-init bf16 model, batch 1, 256 prompt + 256 "
+                               f"masked, blocks of 32, 256 steps x 1 token, skip layer 4, keep 0.25",
+                   "global_batch": dec.B, "seq_len": dec.S, "keep": sched.keep, "skip_layer": sched.skip_layer},
+        "roofline": roofline,
+        "kernels": {
+            "gemm": {"ms": round(g["ms"], 3), "launches": g["launches"], "GB/s": round(gemm_gbs, 1),
+                     "TFLOP/s": round(g["flops"] / max(g["ms"], 1e-9) / 1e9, 1)},
+            "attention": {"ms": round(a["ms"], 3), "launches": a["launches"],
+                          "TFLOP/s": round(a["flops"] / max(a["ms"], 1e-9) / 1e9, 2)},
+            "lm_head": {"ms": round(lmh["ms"], 3), "launches": lmh["launches"],
+                        "GB/s": round(lmh["bytes"] / max(lmh["ms"], 1e-9) / 1e6, 1)},
+        },
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, model, prompts)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -26,7 +26,8 @@ TORCH_DTYPES = {DL_F32: torch.float32, DL_BF16: torch.bfloat16}
 
 EXPORTS = ("dl_score_select", "dl_gather", "dl_scatter_cache", "dl_partial_attn", "dl_ffn_rows", "dl_lm_head_rows",
            "dl_unmask", "dl_denoise_step", "dl_workspace_bytes", "dl_status_string", "dl_last_error",
-           "dl_abi_version")
+           "dl_abi_version", "dl_timing_enable", "dl_timing_reset", "dl_timing_read")
+DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD = 0, 1, 2
 
 
 class Dims(Structure):
@@ -60,6 +61,11 @@ class StepParams(Structure):
     _fields_ = [("block", c_int32), ("block_len", c_int32), ("n_unmask", c_int32), ("skip_layer", c_int32),
                 ("full_refresh", c_int32), ("score", c_int32), ("alpha", c_float), ("mode", c_int32),
                 ("keep_ratio", c_float), ("threshold", c_float), ("seq_len_host", POINTER(c_int32))]
+
+
+class Timing(Structure):
+    _fields_ = [("launches", ctypes.c_int64), ("dropped", ctypes.c_int64), ("ms", ctypes.c_double),
+                ("bytes", ctypes.c_double), ("flops", ctypes.c_double)]
 
 
 class DLError(RuntimeError):
@@ -104,8 +110,12 @@ def load() -> ctypes.CDLL:
     lib.dl_last_error.restype = c_char_p
     lib.dl_abi_version.argtypes = []
     lib.dl_abi_version.restype = c_int32
+    lib.dl_timing_enable.argtypes = [c_int32, c_int32]
+    lib.dl_timing_reset.argtypes = []
+    lib.dl_timing_read.argtypes = [c_int32, POINTER(Timing)]
     for name in ("dl_score_select", "dl_gather", "dl_scatter_cache", "dl_partial_attn", "dl_ffn_rows",
-                 "dl_lm_head_rows", "dl_unmask", "dl_denoise_step"):
+                 "dl_lm_head_rows", "dl_unmask", "dl_denoise_step", "dl_timing_enable", "dl_timing_reset",
+                 "dl_timing_read"):
         getattr(lib, name).restype = st
     _lib = lib
     return lib
@@ -232,3 +242,17 @@ def dl_denoise_step(model: Model, state: State, params: StepParams, ws, stream=N
 
 def dl_abi_version() -> int:
     return int(load().dl_abi_version())
+
+
+def dl_timing_enable(kc: int, enable: bool = True):
+    _check(load().dl_timing_enable(int(kc), int(bool(enable))))
+
+
+def dl_timing_reset():
+    _check(load().dl_timing_reset())
+
+
+def dl_timing_read(kc: int) -> dict:
+    t = Timing()
+    _check(load().dl_timing_read(int(kc), ctypes.byref(t)))
+    return {"launches": t.launches, "dropped": t.dropped, "ms": t.ms, "bytes": t.bytes, "flops": t.flops}

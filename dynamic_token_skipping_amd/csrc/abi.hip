@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "launch.h"
 
@@ -166,6 +167,46 @@ RowMap rowmap_at(void* ws, const RowMapMem& m, int R_max, int T_max) {
 }
 
 // ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+constexpr int kTimingPool = 8192;
+
+struct TimingClass {
+  bool enabled = false;
+  std::vector<hipEvent_t> ev;     // 2 per launch
+  int used = 0;                   // pairs recorded since reset
+  int64_t dropped = 0;
+  double bytes = 0, flops = 0;
+};
+TimingClass g_timing[DL_KC_COUNT];
+
+// Runs `launch` bracketed by events when the class is enabled.
+template <typename F>
+hipError_t timed(dl_kernel_class kc, hipStream_t st, double bytes, double flops, F&& launch) {
+  TimingClass& t = g_timing[kc];
+  if (!t.enabled) return launch();
+  if (t.used >= kTimingPool) {
+    ++t.dropped;
+    return launch();
+  }
+  hipError_t e = hipEventRecord(t.ev[2 * t.used], st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(t.ev[2 * t.used + 1], st);
+  if (e != hipSuccess) return e;
+  ++t.used;
+  t.bytes += bytes;
+  t.flops += flops;
+  return hipSuccess;
+}
+
+double gemm_bytes(const dl_dims& d, long long M, long long N, long long K) {
+  const double es = (double)esize(d.dtype);
+  return es * ((double)N * K + (double)M * K + (double)M * N);
+}
+
+// ---------------------------------------------------------------------------
 // layer pieces on packed rows
 // ---------------------------------------------------------------------------
 struct Ctx {
@@ -173,6 +214,8 @@ struct Ctx {
   void* ws;
   const Layout* L;
   hipStream_t st;
+  long long keys_total;   // sum of valid keys over the batch (host bound, timing only)
+  long long rows_x_keys;  // sum over sequences of rows x keys (host bound, timing only)
 };
 
 dl_status check_layer(const dl_layer_w* w) {
@@ -201,14 +244,26 @@ dl_status attn_block(const Ctx& c, const dl_layer_w* w, float* x, const RowMap& 
   {
     const void* seg[4] = {w->wq, w->wk, w->wv, w->wv};
     const GemmPlan p = plan_gemm(d.dtype, rm.R_max, 3 * d.d, d.d);
-    DL_CHECK_HIP(launch_gemm(d.dtype, p, act, rm.R_max, rm.n_rows, 0, d.d, seg, d.d, 3 * d.d, P, c.st));
+    DL_CHECK_HIP(timed(DL_KC_GEMM, c.st, gemm_bytes(d, rm.R_max, 3 * d.d, d.d), 2.0 * rm.R_max * 3 * d.d * d.d,
+                       [&] { return launch_gemm(d.dtype, p, act, rm.R_max, rm.n_rows, 0, d.d, seg, d.d, 3 * d.d, P,
+                                                c.st); }));
     DL_CHECK_HIP(launch_epi_qkv(d.dtype, P, p.splits, rm, d.S, d.d, d.head_dim, rope, q, kc, vc, c.st));
   }
-  DL_CHECK_HIP(launch_attention(d.dtype, q, kc, vc, seq_len, rm, d.S, d.n_heads, d.head_dim, attn, c.st));
+  {
+    // algorithmic: q rows + every valid key/value row of the sequences once + output rows
+    const double es = (double)esize(d.dtype);
+    const double keys = (double)c.keys_total;
+    DL_CHECK_HIP(timed(DL_KC_ATTN, c.st, es * ((double)rm.R_max * d.d * 2 + 2.0 * keys * d.d),
+                       4.0 * (double)c.rows_x_keys * d.d,
+                       [&] { return launch_attention(d.dtype, q, kc, vc, seq_len, rm, d.S, d.n_heads, d.head_dim,
+                                                     attn, c.st); }));
+  }
   {
     const void* seg[4] = {w->wo, w->wo, w->wo, w->wo};
     const GemmPlan p = plan_gemm(d.dtype, rm.R_max, d.d, d.d);
-    DL_CHECK_HIP(launch_gemm(d.dtype, p, attn, rm.R_max, rm.n_rows, 0, d.d, seg, d.d, d.d, P, c.st));
+    DL_CHECK_HIP(timed(DL_KC_GEMM, c.st, gemm_bytes(d, rm.R_max, d.d, d.d), 2.0 * rm.R_max * d.d * d.d,
+                       [&] { return launch_gemm(d.dtype, p, attn, rm.R_max, rm.n_rows, 0, d.d, seg, d.d, d.d, P,
+                                                c.st); }));
     DL_CHECK_HIP(launch_epi_residual(P, p.splits, rm, d.d, x, c.st));
   }
   return DL_OK;
@@ -222,13 +277,18 @@ dl_status ffn_block(const Ctx& c, const dl_layer_w* w, float* x, const RowMap& r
   {
     const void* seg[4] = {w->w_gate, w->w_up, w->w_up, w->w_up};
     const GemmPlan p = plan_gemm(d.dtype, rm.R_max, 2 * d.d_ffn, d.d);
-    DL_CHECK_HIP(launch_gemm(d.dtype, p, act, rm.R_max, rm.n_rows, 0, d.d, seg, d.d_ffn, 2 * d.d_ffn, P, c.st));
+    DL_CHECK_HIP(timed(DL_KC_GEMM, c.st, gemm_bytes(d, rm.R_max, 2 * d.d_ffn, d.d),
+                       2.0 * rm.R_max * 2 * d.d_ffn * d.d,
+                       [&] { return launch_gemm(d.dtype, p, act, rm.R_max, rm.n_rows, 0, d.d, seg, d.d_ffn,
+                                                2 * d.d_ffn, P, c.st); }));
     DL_CHECK_HIP(launch_epi_swiglu(d.dtype, P, p.splits, rm, d.d_ffn, act, c.st));
   }
   {
     const void* seg[4] = {w->w_down, w->w_down, w->w_down, w->w_down};
     const GemmPlan p = plan_gemm(d.dtype, rm.R_max, d.d, d.d_ffn);
-    DL_CHECK_HIP(launch_gemm(d.dtype, p, act, rm.R_max, rm.n_rows, 0, d.d_ffn, seg, d.d, d.d, P, c.st));
+    DL_CHECK_HIP(timed(DL_KC_GEMM, c.st, gemm_bytes(d, rm.R_max, d.d, d.d_ffn), 2.0 * rm.R_max * d.d * d.d_ffn,
+                       [&] { return launch_gemm(d.dtype, p, act, rm.R_max, rm.n_rows, 0, d.d_ffn, seg, d.d, d.d, P,
+                                                c.st); }));
     DL_CHECK_HIP(launch_epi_residual(P, p.splits, rm, d.d, x, c.st));
   }
   return DL_OK;
@@ -245,7 +305,9 @@ dl_status lm_block(const Ctx& c, const void* final_norm, const void* lm_head, co
     const int rows = std::min(kLmChunk, rm.R_max - m0);
     const GemmPlan p = plan_gemm(d.dtype, rows, d.vocab, d.d);
     const void* A = static_cast<const char*>(act) + (size_t)m0 * d.d * esize(d.dtype);
-    DL_CHECK_HIP(launch_gemm(d.dtype, p, A, rows, rm.n_rows, m0, d.d, seg, d.vocab, d.vocab, P, c.st));
+    DL_CHECK_HIP(timed(DL_KC_LMHEAD, c.st, gemm_bytes(d, rows, d.vocab, d.d), 2.0 * rows * d.vocab * d.d,
+                       [&] { return launch_gemm(d.dtype, p, A, rows, rm.n_rows, m0, d.d, seg, d.vocab, d.vocab, P,
+                                                c.st); }));
     DL_CHECK_HIP(launch_lm_reduce(P, p.splits, rm, m0, rows, d.vocab, conf, argmax, logits, c.st));
   }
   DL_CHECK_HIP(launch_store_rows(d.dtype, x, d.d, rm, h_final, c.st));
@@ -262,6 +324,45 @@ size_t layer_stride_bytes(const dl_dims& d) { return (size_t)d.B * d.S * d.d * e
 extern "C" {
 
 int32_t dl_abi_version(void) { return DL_ABI_VERSION; }
+
+dl_status dl_timing_enable(dl_kernel_class kc, int32_t enable) {
+  if (kc < 0 || kc >= DL_KC_COUNT) return fail(DL_E_ARG, "kernel class %d unknown", (int)kc);
+  TimingClass& t = g_timing[kc];
+  if (enable && t.ev.empty()) {
+    t.ev.resize(2 * kTimingPool);
+    for (auto& e : t.ev) DL_CHECK_HIP(hipEventCreate(&e));
+  }
+  t.enabled = enable != 0;
+  return DL_OK;
+}
+
+dl_status dl_timing_reset(void) {
+  for (auto& t : g_timing) {
+    t.used = 0;
+    t.dropped = 0;
+    t.bytes = t.flops = 0;
+  }
+  return DL_OK;
+}
+
+dl_status dl_timing_read(dl_kernel_class kc, dl_timing* out) {
+  if (kc < 0 || kc >= DL_KC_COUNT) return fail(DL_E_ARG, "kernel class %d unknown", (int)kc);
+  if (!out) return fail(DL_E_ARG, "out is NULL");
+  TimingClass& t = g_timing[kc];
+  double ms = 0;
+  for (int i = 0; i < t.used; ++i) {
+    DL_CHECK_HIP(hipEventSynchronize(t.ev[2 * i + 1]));
+    float m = 0.f;
+    DL_CHECK_HIP(hipEventElapsedTime(&m, t.ev[2 * i], t.ev[2 * i + 1]));
+    ms += m;
+  }
+  out->launches = t.used;
+  out->dropped = t.dropped;
+  out->ms = ms;
+  out->bytes = t.bytes;
+  out->flops = t.flops;
+  return DL_OK;
+}
 
 const char* dl_last_error(void) { return g_err; }
 
@@ -372,7 +473,7 @@ dl_status dl_partial_attn(const dl_dims* dims, const dl_layer_w* layer, float* x
   DL_TRY(prep_rows(dims, sel, k_total_max, ws, ws_bytes, &L, &rm, st));
   if (k_total_max == 0) return DL_OK;
   DL_CHECK_HIP(launch_rope_table(dims->S, dims->head_dim, dims->rope_base, at<float2>(ws, L.rope), st));
-  Ctx c{dims, ws, &L, st};
+  Ctx c{dims, ws, &L, st, (long long)dims->B * dims->S, (long long)k_total_max * dims->S};
   return attn_block(c, layer, x_rows, rm, seq_len, k_cache, v_cache);
 }
 
@@ -386,7 +487,7 @@ dl_status dl_ffn_rows(const dl_dims* dims, const dl_layer_w* layer, float* x_row
   RowMap rm;
   DL_TRY(prep_rows(dims, sel, k_total_max, ws, ws_bytes, &L, &rm, st));
   if (k_total_max == 0) return DL_OK;
-  Ctx c{dims, ws, &L, st};
+  Ctx c{dims, ws, &L, st, 0, 0};
   return ffn_block(c, layer, x_rows, rm);
 }
 
@@ -406,7 +507,7 @@ dl_status dl_lm_head_rows(const dl_dims* dims, const void* final_norm, const voi
   RowMap rm;
   DL_TRY(prep_rows(dims, sel, k_total_max, ws, ws_bytes, &L, &rm, st));
   if (k_total_max == 0) return DL_OK;
-  Ctx c{dims, ws, &L, st};
+  Ctx c{dims, ws, &L, st, 0, 0};
   return lm_block(c, final_norm, lm_head, x_rows, rm, conf, argmax, h_final, logits_or_null);
 }
 
@@ -461,22 +562,26 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
     return fail(DL_E_ARG, "keep_ratio %g outside (0, 1]", (double)p->keep_ratio);
   if (p->block < 0 || p->block_len < 1 || p->n_unmask < 0) return fail(DL_E_ARG, "block schedule out of range");
   if (p->block_len > 1024) return fail(DL_E_UNSUPPORTED, "block_len > 1024");
-  long long R_all = 0, R_sel = 0;
+  long long R_all = 0, R_sel = 0, all_x_keys = 0, sel_x_keys = 0;
   for (int b = 0; b < d.B; ++b) {
     const int n = p->seq_len_host[b];
     if (n < 0 || n > d.S) return fail(DL_E_SHAPE, "seq_len_host[%d] = %d outside [0, S=%d]", b, n, d.S);
     R_all += n;
+    all_x_keys += (long long)n * n;
+    long long kb = n;
     if (p->mode == DL_SEL_TOPK && n > 0) {
       const double kk = ceil((double)p->keep_ratio * (double)n);
-      R_sel += kk < 1.0 ? 1 : (kk > (double)n ? n : (long long)kk);
+      kb = kk < 1.0 ? 1 : (kk > (double)n ? n : (long long)kk);
     }
+    R_sel += kb;
+    sel_x_keys += kb * n;
   }
   if (p->mode == DL_SEL_THRESHOLD) R_sel = R_all;
   const Layout L = make_layout(d, (int)R_all);
   if (ws_bytes < L.total) return fail(DL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
 
   hipStream_t st = (hipStream_t)stream;
-  Ctx c{dims, ws, &L, st};
+  Ctx c{dims, ws, &L, st, R_all, all_x_keys};
   const bool refresh = p->full_refresh != 0;
   const int sl = p->skip_layer;
   int32_t* all_idx = at<int32_t>(ws, L.sel_idx);
@@ -521,6 +626,7 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
     DL_CHECK_HIP(launch_rowmap(s->sel.sel_idx, s->sel.sel_count, s->sel.row_off, d.B, d.S, rm_sel, st));
     float* x_sel = at<float>(ws, L.x_sel);
     DL_CHECK_HIP(launch_gather(sizeof(float), x_all, all_off, d.S, d.d, rm_sel, x_sel, st));
+    c.rows_x_keys = sel_x_keys;
     for (int l = sl; l < d.n_layers; ++l) {
       DL_TRY(attn_block(c, &model->layers[l], x_sel, rm_sel, s->seq_len, kc(l), vc(l)));
       DL_TRY(ffn_block(c, &model->layers[l], x_sel, rm_sel));

@@ -211,6 +211,30 @@ dl_status dl_unmask(const dl_dims *dims, int32_t *tokens, uint8_t *masked, const
 dl_status dl_denoise_step(const dl_model *model, dl_state *state, const dl_step_params *params, void *ws,
                           size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Kernel timing (measurement support, not part of the method).  While a class
+ * is enabled, every launch of that class is bracketed by two HIP events
+ * recorded on the launch's own stream, and the launch's algorithmic bytes and
+ * FLOPs are added up (for a product: weights + input rows + output rows in the
+ * storage type, 2*M*N*K FLOPs; for attention: Q + K/V rows read + output,
+ * 4*rows*keys*d FLOPs).  dl_timing_read synchronises on the recorded events
+ * and returns the sums since dl_timing_reset.  Up to 8192 launches per class
+ * are timed; later ones are counted in `dropped`.  Not thread-safe.
+ * ------------------------------------------------------------------------- */
+typedef enum { DL_KC_GEMM = 0, DL_KC_ATTN = 1, DL_KC_LMHEAD = 2, DL_KC_COUNT = 3 } dl_kernel_class;
+
+typedef struct {
+  int64_t launches;     /* launches timed */
+  int64_t dropped;      /* launches not timed (event pool full) */
+  double ms;            /* summed kernel time */
+  double bytes;         /* summed algorithmic bytes */
+  double flops;         /* summed algorithmic FLOPs */
+} dl_timing;
+
+dl_status dl_timing_enable(dl_kernel_class kc, int32_t enable);
+dl_status dl_timing_reset(void);
+dl_status dl_timing_read(dl_kernel_class kc, dl_timing *out);
+
 /* Workspace bytes for any entry point above on a batch whose valid rows sum
  * to at most max_rows (0: B*S). */
 size_t dl_workspace_bytes(const dl_dims *dims, int32_t max_rows);
