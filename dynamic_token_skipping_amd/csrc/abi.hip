@@ -88,20 +88,27 @@ struct Layout {
   size_t sel_idx, sel_count, row_off;  // identity selection of every valid row
   RowMapMem map_all, map_sel;
   size_t x_all, x_sel;      // fp32 [R, d]
-  size_t act;               // T [R, max(d, F)]
+  size_t act;               // T [R, d] normalised rows
+  size_t ffn_act;           // T [R, F] silu(gate) * up
   size_t q, attn;           // T [R, d]
   size_t P;                 // fp32 GEMM partials
+  size_t lm_part;           // float4 [min(R, kLmChunk)][ceil(V / 128)]
   size_t scores;            // fp32 [B*S]
   size_t rope;              // float2 [S, head_dim/2]
   size_t total;
 };
 
-size_t gemm_partial_floats(dl_dtype dt, int R, int N, int K) {
+size_t gemm_partial_floats(const dl_dims& d, int R, int N, int K, int epi) {
   // worst case over every row bound the planner can see (1..R)
   size_t best = 0;
+  for (int m : {16, 32, 64}) {
+    if (m >= R) break;
+    const GemmPlan p = plan_gemm(d.dtype, m, N, K, epi, d.head_dim, d.d_ffn);
+    best = std::max(best, (size_t)p.splits * (size_t)m * (size_t)N);
+  }
   for (int m = 128;; m += 128) {
     const int M = std::min(m, R);
-    const GemmPlan p = plan_gemm(dt, M, N, K);
+    const GemmPlan p = plan_gemm(d.dtype, M, N, K, epi, d.head_dim, d.d_ffn);
     best = std::max(best, (size_t)p.splits * (size_t)M * (size_t)N);
     if (M == R) break;
   }
@@ -132,16 +139,18 @@ Layout make_layout(const dl_dims& d, int R) {
   }
   L.x_all = take(sizeof(float) * (size_t)L.R * d.d);
   L.x_sel = take(sizeof(float) * (size_t)L.R * d.d);
-  L.act = take(es * (size_t)L.R * std::max(d.d, d.d_ffn));
+  L.act = take(es * (size_t)L.R * d.d);
+  L.ffn_act = take(es * (size_t)L.R * d.d_ffn);
   L.q = take(es * (size_t)L.R * d.d);
   L.attn = take(es * (size_t)L.R * d.d);
   size_t pf = 0;
-  pf = std::max(pf, gemm_partial_floats(d.dtype, L.R, 3 * d.d, d.d));
-  pf = std::max(pf, gemm_partial_floats(d.dtype, L.R, d.d, d.d));
-  pf = std::max(pf, gemm_partial_floats(d.dtype, L.R, 2 * d.d_ffn, d.d));
-  pf = std::max(pf, gemm_partial_floats(d.dtype, L.R, d.d, d.d_ffn));
-  pf = std::max(pf, gemm_partial_floats(d.dtype, std::min(L.R, kLmChunk), d.vocab, d.d));
+  pf = std::max(pf, gemm_partial_floats(d, L.R, 3 * d.d, d.d, EPI_QKV));
+  pf = std::max(pf, gemm_partial_floats(d, L.R, d.d, d.d, EPI_NONE));
+  pf = std::max(pf, gemm_partial_floats(d, L.R, 2 * d.d_ffn, d.d, EPI_SWIGLU));
+  pf = std::max(pf, gemm_partial_floats(d, L.R, d.d, d.d_ffn, EPI_NONE));
+  pf = std::max(pf, gemm_partial_floats(d, std::min(L.R, kLmChunk), d.vocab, d.d, EPI_LM));
   L.P = take(sizeof(float) * pf);
+  L.lm_part = take(16 * (size_t)std::min(L.R, kLmChunk) * cdiv(d.vocab, 128));
   L.scores = take(sizeof(float) * (size_t)B * S);
   L.rope = take(sizeof(float) * 2 * (size_t)S * (d.head_dim / 2));
   L.total = off;
@@ -232,22 +241,69 @@ dl_status check_layer(const dl_layer_w* w) {
   return DL_OK;
 }
 
+Epilogue epi_base(const Ctx& c, int kind, const RowMap& rm, int m_base) {
+  Epilogue e{};
+  e.kind = kind;
+  e.row_pos = rm.row_pos + m_base;
+  e.row_seq = rm.row_seq + m_base;
+  e.S = c.d->S;
+  e.d = c.d->d;
+  e.head_dim = c.d->head_dim;
+  e.F = c.d->d_ffn;
+  e.V = c.d->vocab;
+  e.rope = at<float2>(c.ws, c.L->rope);
+  return e;
+}
+
+// One product of rows [m_base, m_base + rows) of A with the weight segments,
+// followed by its epilogue: fused into the product on the matrix-core paths,
+// as separate kernels on the SIMT path.  EPI_NONE products leave fp32
+// partials in the workspace for launch_reduce_rows.  Returns the K split.
+dl_status product(const Ctx& c, dl_kernel_class kc, const void* A, const RowMap& rm, int m_base, int rows, int K,
+                  const void* const* seg, int n_seg, int N, const Epilogue& e, int* splits_out,
+                  float* conf = nullptr, int32_t* argmax = nullptr) {
+  const dl_dims& d = *c.d;
+  float* P = at<float>(c.ws, c.L->P);
+  const GemmPlan p = plan_gemm(d.dtype, rows, N, K, e.kind, d.head_dim, d.d_ffn);
+  if (splits_out) *splits_out = p.splits;
+  DL_CHECK_HIP(timed(kc, c.st, gemm_bytes(d, rows, N, K), 2.0 * rows * N * K, [&] {
+    return launch_gemm(d.dtype, p, A, rows, rm.n_rows, m_base, K, seg, n_seg, N, P, e, c.st);
+  }));
+  if (p.kind == GEMM_SIMT) {
+    // Separate epilogue kernels (rows addressed through the full row map).
+    switch (e.kind) {
+      case EPI_QKV:
+        DL_CHECK_HIP(launch_epi_qkv(d.dtype, P, p.splits, rm, d.S, d.d, d.head_dim, e.rope, e.q_out, e.k_cache,
+                                    e.v_cache, c.st));
+        break;
+      case EPI_SWIGLU: DL_CHECK_HIP(launch_epi_swiglu(d.dtype, P, p.splits, rm, d.d_ffn, e.act_out, c.st)); break;
+      case EPI_LM:
+        DL_CHECK_HIP(launch_lm_reduce(P, p.splits, rm, m_base, rows, d.vocab, conf, argmax, e.logits, c.st));
+        break;
+      default: break;
+    }
+  } else if (e.kind == EPI_LM) {
+    DL_CHECK_HIP(launch_lm_merge(e.lm_part, e.lm_tiles, rm, m_base, rows, conf, argmax, c.st));
+  }
+  return DL_OK;
+}
+
+// Attention sub-block.  On entry act holds RMSNorm(x, attn_norm) if act_ready.
+// On exit x has the attention residual added and act = RMSNorm(x, ffn_norm).
 dl_status attn_block(const Ctx& c, const dl_layer_w* w, float* x, const RowMap& rm, const int32_t* seq_len,
-                     void* kc, void* vc) {
+                     void* kc, void* vc, bool act_ready) {
   const dl_dims& d = *c.d;
   void* act = at<void>(c.ws, c.L->act);
   void* q = at<void>(c.ws, c.L->q);
   void* attn = at<void>(c.ws, c.L->attn);
-  float* P = at<float>(c.ws, c.L->P);
-  const float2* rope = at<float2>(c.ws, c.L->rope);
-  DL_CHECK_HIP(launch_rmsnorm(d.dtype, x, w->attn_norm, rm, d.d, d.rms_eps, act, c.st));
+  if (!act_ready) DL_CHECK_HIP(launch_rmsnorm(d.dtype, x, w->attn_norm, rm, d.d, d.rms_eps, act, c.st));
   {
     const void* seg[4] = {w->wq, w->wk, w->wv, w->wv};
-    const GemmPlan p = plan_gemm(d.dtype, rm.R_max, 3 * d.d, d.d);
-    DL_CHECK_HIP(timed(DL_KC_GEMM, c.st, gemm_bytes(d, rm.R_max, 3 * d.d, d.d), 2.0 * rm.R_max * 3 * d.d * d.d,
-                       [&] { return launch_gemm(d.dtype, p, act, rm.R_max, rm.n_rows, 0, d.d, seg, d.d, 3 * d.d, P,
-                                                c.st); }));
-    DL_CHECK_HIP(launch_epi_qkv(d.dtype, P, p.splits, rm, d.S, d.d, d.head_dim, rope, q, kc, vc, c.st));
+    Epilogue e = epi_base(c, EPI_QKV, rm, 0);
+    e.q_out = q;
+    e.k_cache = kc;
+    e.v_cache = vc;
+    DL_TRY(product(c, DL_KC_GEMM, act, rm, 0, rm.R_max, d.d, seg, d.d, 3 * d.d, e, nullptr));
   }
   {
     // algorithmic: q rows + every valid key/value row of the sequences once + output rows
@@ -260,55 +316,68 @@ dl_status attn_block(const Ctx& c, const dl_layer_w* w, float* x, const RowMap& 
   }
   {
     const void* seg[4] = {w->wo, w->wo, w->wo, w->wo};
-    const GemmPlan p = plan_gemm(d.dtype, rm.R_max, d.d, d.d);
-    DL_CHECK_HIP(timed(DL_KC_GEMM, c.st, gemm_bytes(d, rm.R_max, d.d, d.d), 2.0 * rm.R_max * d.d * d.d,
-                       [&] { return launch_gemm(d.dtype, p, attn, rm.R_max, rm.n_rows, 0, d.d, seg, d.d, d.d, P,
-                                                c.st); }));
-    DL_CHECK_HIP(launch_epi_residual(P, p.splits, rm, d.d, x, c.st));
+    const Epilogue e = epi_base(c, EPI_NONE, rm, 0);
+    int splits = 1;
+    DL_TRY(product(c, DL_KC_GEMM, attn, rm, 0, rm.R_max, d.d, seg, d.d, d.d, e, &splits));
+    DL_CHECK_HIP(launch_reduce_rows(d.dtype, at<float>(c.ws, c.L->P), splits, rm, d.d, x, w->ffn_norm, d.rms_eps,
+                                    act, c.st));
   }
   return DL_OK;
 }
 
-dl_status ffn_block(const Ctx& c, const dl_layer_w* w, float* x, const RowMap& rm) {
+// FFN sub-block; act = RMSNorm(x, ffn_norm) on entry.  On exit x has the FFN
+// residual added and, if next_norm != nullptr, act = RMSNorm(x, next_norm).
+dl_status ffn_block(const Ctx& c, const dl_layer_w* w, float* x, const RowMap& rm, const void* next_norm) {
   const dl_dims& d = *c.d;
   void* act = at<void>(c.ws, c.L->act);
-  float* P = at<float>(c.ws, c.L->P);
-  DL_CHECK_HIP(launch_rmsnorm(d.dtype, x, w->ffn_norm, rm, d.d, d.rms_eps, act, c.st));
+  void* ffn_act = at<void>(c.ws, c.L->ffn_act);
   {
     const void* seg[4] = {w->w_gate, w->w_up, w->w_up, w->w_up};
-    const GemmPlan p = plan_gemm(d.dtype, rm.R_max, 2 * d.d_ffn, d.d);
-    DL_CHECK_HIP(timed(DL_KC_GEMM, c.st, gemm_bytes(d, rm.R_max, 2 * d.d_ffn, d.d),
-                       2.0 * rm.R_max * 2 * d.d_ffn * d.d,
-                       [&] { return launch_gemm(d.dtype, p, act, rm.R_max, rm.n_rows, 0, d.d, seg, d.d_ffn,
-                                                2 * d.d_ffn, P, c.st); }));
-    DL_CHECK_HIP(launch_epi_swiglu(d.dtype, P, p.splits, rm, d.d_ffn, act, c.st));
+    Epilogue e = epi_base(c, EPI_SWIGLU, rm, 0);
+    e.act_out = ffn_act;
+    DL_TRY(product(c, DL_KC_GEMM, act, rm, 0, rm.R_max, d.d, seg, d.d_ffn, 2 * d.d_ffn, e, nullptr));
   }
   {
     const void* seg[4] = {w->w_down, w->w_down, w->w_down, w->w_down};
-    const GemmPlan p = plan_gemm(d.dtype, rm.R_max, d.d, d.d_ffn);
-    DL_CHECK_HIP(timed(DL_KC_GEMM, c.st, gemm_bytes(d, rm.R_max, d.d, d.d_ffn), 2.0 * rm.R_max * d.d * d.d_ffn,
-                       [&] { return launch_gemm(d.dtype, p, act, rm.R_max, rm.n_rows, 0, d.d_ffn, seg, d.d, d.d, P,
-                                                c.st); }));
-    DL_CHECK_HIP(launch_epi_residual(P, p.splits, rm, d.d, x, c.st));
+    const Epilogue e = epi_base(c, EPI_NONE, rm, 0);
+    int splits = 1;
+    DL_TRY(product(c, DL_KC_GEMM, ffn_act, rm, 0, rm.R_max, d.d_ffn, seg, d.d, d.d, e, &splits));
+    DL_CHECK_HIP(launch_reduce_rows(d.dtype, at<float>(c.ws, c.L->P), splits, rm, d.d, x, next_norm, d.rms_eps, act,
+                                    c.st));
+  }
+  return DL_OK;
+}
+
+// Layers [l0, l1) on the rows of rm.  act_ready: act already holds
+// RMSNorm(x, attn_norm of l0).  next_after: the gain normalised into act after
+// the last layer (nullptr: none).
+dl_status run_layers(const Ctx& c, const dl_model* model, int l0, int l1, float* x, const RowMap& rm,
+                     const int32_t* seq_len, char* k_cache, char* v_cache, bool act_ready, const void* next_after) {
+  const size_t lstride = (size_t)c.d->B * c.d->S * c.d->d * esize(c.d->dtype);
+  for (int l = l0; l < l1; ++l) {
+    const dl_layer_w* w = &model->layers[l];
+    DL_TRY(attn_block(c, w, x, rm, seq_len, k_cache + (size_t)l * lstride, v_cache + (size_t)l * lstride, act_ready));
+    const void* nn = l + 1 < l1 ? model->layers[l + 1].attn_norm : next_after;
+    DL_TRY(ffn_block(c, w, x, rm, nn));
+    act_ready = nn != nullptr;
   }
   return DL_OK;
 }
 
 dl_status lm_block(const Ctx& c, const void* final_norm, const void* lm_head, const float* x, const RowMap& rm,
-                   float* conf, int32_t* argmax, void* h_final, float* logits) {
+                   float* conf, int32_t* argmax, void* h_final, float* logits, bool act_ready) {
   const dl_dims& d = *c.d;
   void* act = at<void>(c.ws, c.L->act);
-  float* P = at<float>(c.ws, c.L->P);
-  DL_CHECK_HIP(launch_rmsnorm(d.dtype, x, final_norm, rm, d.d, d.rms_eps, act, c.st));
+  if (!act_ready) DL_CHECK_HIP(launch_rmsnorm(d.dtype, x, final_norm, rm, d.d, d.rms_eps, act, c.st));
   const void* seg[4] = {lm_head, lm_head, lm_head, lm_head};
   for (int m0 = 0; m0 < rm.R_max; m0 += kLmChunk) {
     const int rows = std::min(kLmChunk, rm.R_max - m0);
-    const GemmPlan p = plan_gemm(d.dtype, rows, d.vocab, d.d);
     const void* A = static_cast<const char*>(act) + (size_t)m0 * d.d * esize(d.dtype);
-    DL_CHECK_HIP(timed(DL_KC_LMHEAD, c.st, gemm_bytes(d, rows, d.vocab, d.d), 2.0 * rows * d.vocab * d.d,
-                       [&] { return launch_gemm(d.dtype, p, A, rows, rm.n_rows, m0, d.d, seg, d.vocab, d.vocab, P,
-                                                c.st); }));
-    DL_CHECK_HIP(launch_lm_reduce(P, p.splits, rm, m0, rows, d.vocab, conf, argmax, logits, c.st));
+    Epilogue e = epi_base(c, EPI_LM, rm, m0);
+    e.lm_part = at<float>(c.ws, c.L->lm_part);
+    e.lm_tiles = cdiv(d.vocab, 128);
+    e.logits = logits;
+    DL_TRY(product(c, DL_KC_LMHEAD, A, rm, m0, rows, d.d, seg, d.vocab, d.vocab, e, nullptr, conf, argmax));
   }
   DL_CHECK_HIP(launch_store_rows(d.dtype, x, d.d, rm, h_final, c.st));
   return DL_OK;
@@ -474,7 +543,8 @@ dl_status dl_partial_attn(const dl_dims* dims, const dl_layer_w* layer, float* x
   if (k_total_max == 0) return DL_OK;
   DL_CHECK_HIP(launch_rope_table(dims->S, dims->head_dim, dims->rope_base, at<float2>(ws, L.rope), st));
   Ctx c{dims, ws, &L, st, (long long)dims->B * dims->S, (long long)k_total_max * dims->S};
-  return attn_block(c, layer, x_rows, rm, seq_len, k_cache, v_cache);
+  DL_TRY(attn_block(c, layer, x_rows, rm, seq_len, k_cache, v_cache, false));
+  return DL_OK;
 }
 
 dl_status dl_ffn_rows(const dl_dims* dims, const dl_layer_w* layer, float* x_rows, const dl_selection* sel,
@@ -488,7 +558,9 @@ dl_status dl_ffn_rows(const dl_dims* dims, const dl_layer_w* layer, float* x_row
   DL_TRY(prep_rows(dims, sel, k_total_max, ws, ws_bytes, &L, &rm, st));
   if (k_total_max == 0) return DL_OK;
   Ctx c{dims, ws, &L, st, 0, 0};
-  return ffn_block(c, layer, x_rows, rm);
+  DL_CHECK_HIP(launch_rmsnorm(dims->dtype, x_rows, layer->ffn_norm, rm, dims->d, dims->rms_eps, at<void>(ws, L.act),
+                              st));
+  return ffn_block(c, layer, x_rows, rm, nullptr);
 }
 
 dl_status dl_lm_head_rows(const dl_dims* dims, const void* final_norm, const void* lm_head, const float* x_rows,
@@ -508,7 +580,7 @@ dl_status dl_lm_head_rows(const dl_dims* dims, const void* final_norm, const voi
   DL_TRY(prep_rows(dims, sel, k_total_max, ws, ws_bytes, &L, &rm, st));
   if (k_total_max == 0) return DL_OK;
   Ctx c{dims, ws, &L, st, 0, 0};
-  return lm_block(c, final_norm, lm_head, x_rows, rm, conf, argmax, h_final, logits_or_null);
+  return lm_block(c, final_norm, lm_head, x_rows, rm, conf, argmax, h_final, logits_or_null, false);
 }
 
 dl_status dl_unmask(const dl_dims* dims, int32_t* tokens, uint8_t* masked, const float* conf, const int32_t* argmax,
@@ -596,26 +668,23 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
   DL_CHECK_HIP(launch_rope_table(d.S, d.head_dim, d.rope_base, at<float2>(ws, L.rope), st));
   DL_CHECK_HIP(launch_embed(d.dtype, s->tokens, rm_all, model->embed, d.d, x_all, st));
 
-  const size_t lstride = layer_stride_bytes(d);
-  auto kc = [&](int l) { return static_cast<char*>(s->k_cache) + (size_t)l * lstride; };
-  auto vc = [&](int l) { return static_cast<char*>(s->v_cache) + (size_t)l * lstride; };
-
-  const int n_full = refresh ? d.n_layers : sl;
-  for (int l = 0; l < n_full; ++l) {
-    if (refresh && l == sl) DL_CHECK_HIP(launch_store_rows(d.dtype, x_all, d.d, rm_all, s->h_prev, st));
-    DL_TRY(attn_block(c, &model->layers[l], x_all, rm_all, s->seq_len, kc(l), vc(l)));
-    DL_TRY(ffn_block(c, &model->layers[l], x_all, rm_all));
-  }
+  char* kcache = static_cast<char*>(s->k_cache);
+  char* vcache = static_cast<char*>(s->v_cache);
   float* scores = s->scores ? s->scores : at<float>(ws, L.scores);
   if (refresh) {
-    if (sl == d.n_layers) DL_CHECK_HIP(launch_store_rows(d.dtype, x_all, d.d, rm_all, s->h_prev, st));
+    // every row through every layer; h_prev <- the layer-s input
+    DL_TRY(run_layers(c, model, 0, sl, x_all, rm_all, s->seq_len, kcache, vcache, false,
+                      sl < d.n_layers ? model->layers[sl].attn_norm : model->final_norm));
+    DL_CHECK_HIP(launch_store_rows(d.dtype, x_all, d.d, rm_all, s->h_prev, st));
+    DL_TRY(run_layers(c, model, sl, d.n_layers, x_all, rm_all, s->seq_len, kcache, vcache, true, model->final_norm));
     DL_CHECK_HIP(hipMemcpyAsync(s->sel.sel_idx, all_idx, sizeof(int32_t) * (size_t)d.B * d.S,
                                 hipMemcpyDeviceToDevice, st));
     DL_CHECK_HIP(hipMemcpyAsync(s->sel.sel_count, all_cnt, sizeof(int32_t) * d.B, hipMemcpyDeviceToDevice, st));
     DL_CHECK_HIP(hipMemcpyAsync(s->sel.row_off, all_off, sizeof(int32_t) * (d.B + 1), hipMemcpyDeviceToDevice, st));
-    DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_all, rm_all, s->conf, s->argmax, s->h_final,
-                    s->logits));
+    DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_all, rm_all, s->conf, s->argmax, s->h_final, s->logits,
+                    true));
   } else {
+    DL_TRY(run_layers(c, model, 0, sl, x_all, rm_all, s->seq_len, kcache, vcache, false, nullptr));
     // score against h_prev and overwrite it with this step's layer-s input
     DL_CHECK_HIP(launch_score(d.dtype, nullptr, x_all, all_off, s->h_prev, s->conf, s->seq_len, d.B, d.S, d.d,
                               p->score, p->alpha, scores, st));
@@ -627,12 +696,9 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
     float* x_sel = at<float>(ws, L.x_sel);
     DL_CHECK_HIP(launch_gather(sizeof(float), x_all, all_off, d.S, d.d, rm_sel, x_sel, st));
     c.rows_x_keys = sel_x_keys;
-    for (int l = sl; l < d.n_layers; ++l) {
-      DL_TRY(attn_block(c, &model->layers[l], x_sel, rm_sel, s->seq_len, kc(l), vc(l)));
-      DL_TRY(ffn_block(c, &model->layers[l], x_sel, rm_sel));
-    }
-    DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_sel, rm_sel, s->conf, s->argmax, s->h_final,
-                    s->logits));
+    DL_TRY(run_layers(c, model, sl, d.n_layers, x_sel, rm_sel, s->seq_len, kcache, vcache, false, model->final_norm));
+    DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_sel, rm_sel, s->conf, s->argmax, s->h_final, s->logits,
+                    sl < d.n_layers));
   }
   DL_CHECK_HIP(launch_unmask(s->tokens, s->masked, s->conf, s->argmax, s->prompt_len, s->seq_len, d.B, d.S, p->block,
                              p->block_len, p->n_unmask, st));

@@ -62,6 +62,15 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS traffic,
+// not for its global loads, so loads prefetched ahead stay in flight across
+// the barrier (a plain __syncthreads would drain them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Row maps of a packed selection: for packed row r, the flat [B,S] row
 // b*S + i it came from, and its sequence b.  Built on the device.
 struct RowMap {

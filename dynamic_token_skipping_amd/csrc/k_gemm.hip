@@ -1,15 +1,28 @@
-// Dense products of packed rows with weight matrices: P = A W^T.
+// Dense products of packed rows with weight matrices, C = A W^T, with the
+// consumer's epilogue fused in.
 //
 // A [M, K] holds the packed rows (storage dtype), W [N, K] the weights as
-// stored ([out, in]), given as up to four row segments so that Wq|Wk|Wv and
-// Wgate|Wup run as one product.  The output is fp32 partial sums, one slice
-// per K split, reduced in a fixed order by the epilogue kernels.
+// stored ([out, in]).  Weights may be given as up to four row segments so
+// that Wq|Wk|Wv run as one product (segmented: segment = n / n_seg), and
+// Wgate|Wup as one product whose every column tile holds gate rows in its
+// first half and the matching up rows in its second half (interleaved), so
+// that SwiGLU needs nothing outside the tile.
 //
-//  * k_gemm_mfma: bf16 operands on the gfx950 matrix cores
-//    (v_mfma_f32_16x16x32_bf16), 256 threads as a 2x2 grid of waves, A and W
-//    tiles staged through LDS with a double buffer.
-//  * k_gemm_simt: fp32 FMA fallback for fp32 storage and shapes the MFMA
-//    tiling does not cover.
+//  * k_gemm_skinny (bf16, M <= 128): the weight-streaming regime.  Each of
+//    the 4 waves owns BN/4 output columns for all M rows; its weight rows go
+//    from HBM straight into a ring of registers kDepth 64-wide K steps ahead
+//    (v_mfma_f32_16x16x32_bf16 B operand layout), while the A rows of each K
+//    step are staged once per workgroup in LDS (double buffer).
+//  * k_gemm_mfma (bf16, larger M): 128x128 tiles, A and W through LDS.
+//  * k_gemm_simt: fp32 FMA fallback (fp32 storage, odd shapes); its results
+//    go through the separate epilogue kernels of k_rows.
+//
+// Products whose epilogue needs only the tile's own columns (QKV + RoPE + K/V
+// scatter, gate/up + SwiGLU, LM-head statistics) run without a K split: the
+// finished tile goes to LDS and the workgroup applies the epilogue.  Products
+// with too few column tiles (the d x d and d x F projections) split K and
+// write fp32 partials; a row kernel then sums the splits in split order and
+// applies residual + RMSNorm.  No workgroup waits on another one.
 #include "launch.h"
 
 namespace dtsk {
@@ -19,160 +32,436 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-struct WSeg {
+// Weight row of output column n.
+//  mode 0 segmented:   segment n / n_seg, row n % n_seg
+//  mode 1 interleaved: each BN-wide tile holds rows [t*BN/2, (t+1)*BN/2) of
+//                      segment 0 then the same rows of segment 1 (gate | up)
+//  mode 2 rope pairs:  segmented, and inside each 128-row head a 64-wide tile
+//                      holds dims [32p, 32p+32) then [64+32p, 64+32p+32), so
+//                      that RoPE partners j and j+64 share the tile
+struct WMap {
   const void* p[4];
+  int mode;
+  int n_seg;
+  int seg_bytes;  // bytes of one segment (buffer range of the skinny path)
 };
+
+template <int BN>
+__device__ __forceinline__ void wrow_index(const WMap& w, int n, int& sg, int& r) {
+  if (w.mode == 1) {
+    const int c = n % BN;
+    sg = c / (BN / 2);
+    r = (n / BN) * (BN / 2) + c % (BN / 2);
+    return;
+  }
+  sg = n / w.n_seg;
+  r = n - sg * w.n_seg;
+  if (w.mode == 2) {      // 64-wide tiles inside 128-dim heads
+    const int head = r >> 7, part = (r >> 6) & 1, c = r & 63;
+    r = head * 128 + (c >> 5) * 64 + part * 32 + (c & 31);
+  }
+}
+
+template <int BN>
+__device__ __forceinline__ const uint16_t* wrow(const WMap& w, int n, int K) {
+  int sg, r;
+  wrow_index<BN>(w, n, sg, r);
+  return reinterpret_cast<const uint16_t*>(w.p[sg]) + (size_t)r * K;
+}
 
 inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Spread consecutive tiles over the 8 XCDs in contiguous runs: hardware hands
-// workgroup i to XCD i % 8, so tile t runs on XCD (t / per_xcd).
-__device__ __forceinline__ int xcd_swizzle(int bid, int nb) {
-  if ((nb & 7) != 0) return bid;
-  return (bid & 7) * (nb >> 3) + (bid >> 3);
-}
-
 // ---------------------------------------------------------------------------
-// MFMA bf16 GEMM
+// fused epilogues on a finished tile held in LDS: T[m][c], rows [0, M),
+// tile columns c whose output column is n0 + c in W-map order
 // ---------------------------------------------------------------------------
-template <int BM, int BN>
-struct MfmaCfg {
-  static constexpr int BK = 64;
-  static constexpr int LDS_STRIDE = BK + 8;       // bf16 elements per LDS row (16-byte skew)
-  static constexpr int WM = BM / 2, WN = BN / 2;  // per-wave tile
-  static constexpr int MI = WM / 16, NI = WN / 16;
-  static constexpr int A_CHUNKS = BM * BK / 8 / 256;  // uint4 loads per thread
-  static constexpr int W_CHUNKS = BN * BK / 8 / 256;
-  static constexpr int LDS_BYTES = 2 * (BM + BN) * LDS_STRIDE * 2;
-};
-
-template <int BM, int BN>
-__global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ A, int M_max,
-                                                   const int32_t* __restrict__ n_rows, int m_base, int K, WSeg W,
-                                                   int n_seg,
-                                                   int N, int k_per_split, int n_mt, int n_nt,
-                                                   float* __restrict__ P) {
-  using C = MfmaCfg<BM, BN>;
-  extern __shared__ __align__(16) uint16_t lds[];
-  uint16_t* As = lds;                                   // [2][BM][LDS_STRIDE]
-  uint16_t* Ws = lds + 2 * BM * C::LDS_STRIDE;          // [2][BN][LDS_STRIDE]
-
-  const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int mt = bid % n_mt;
-  const int nt = (bid / n_mt) % n_nt;
-  const int split = bid / (n_mt * n_nt);
-  const int M = min(*n_rows - m_base, M_max);
-  const int m0 = mt * BM;
-  if (m0 >= M) return;
-  const int n0 = nt * BN;
-  const int k_begin = split * k_per_split;
-  const int k_end = min(K, k_begin + k_per_split);
-  const int nk = (k_end - k_begin) / C::BK;
-
+template <int BN, int TS>
+__device__ __forceinline__ void tile_epilogue(const Epilogue& e, const float* __restrict__ T, const WMap& w, int n0,
+                                              int M) {
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int wm0 = (wave >> 1) * C::WM, wn0 = (wave & 1) * C::WN;
-
-  // global -> register staging
-  uint4 ra[C::A_CHUNKS], rw[C::W_CHUNKS];
-  auto load_tiles = [&](int kt) {
-    const int kb = k_begin + kt * C::BK;
-#pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) {
-      const int c = t + i * 256;
-      const int row = c >> 3, kc = (c & 7) * 8;
-      const int m = m0 + row;
-      if (m < M)
-        ra[i] = *reinterpret_cast<const uint4*>(A + (size_t)m * K + kb + kc);
-      else
-        ra[i] = make_uint4(0, 0, 0, 0);
+  if (e.kind == EPI_SWIGLU) {            // mode 1: gate in [0, BN/2), up in [BN/2, BN)
+    constexpr int H = BN / 2;
+    uint16_t* out = reinterpret_cast<uint16_t*>(e.act_out);
+    for (int idx = t; idx < M * H; idx += 256) {
+      const int m = idx / H, c = idx % H;
+      const float gt = T[m * TS + c], up = T[m * TS + H + c];
+      out[(size_t)m * e.F + (n0 / BN) * H + c] = from_f32<bf16_t>(gt / (1.f + expf(-gt)) * up).u;
     }
-#pragma unroll
-    for (int i = 0; i < C::W_CHUNKS; ++i) {
-      const int c = t + i * 256;
-      const int row = c >> 3, kc = (c & 7) * 8;
-      const int n = n0 + row;
-      const int sg = n / n_seg;
-      const uint16_t* wp = reinterpret_cast<const uint16_t*>(W.p[sg]) + (size_t)(n - sg * n_seg) * K;
-      rw[i] = *reinterpret_cast<const uint4*>(wp + kb + kc);
+  } else if (e.kind == EPI_QKV) {
+    int sg, r0;
+    wrow_index<BN>(w, n0, sg, r0);                  // segment of the tile: 0 q, 1 k, 2 v
+    const int hd = e.head_dim, half = hd / 2;
+    if (sg == 2) {
+      uint16_t* vc = reinterpret_cast<uint16_t*>(e.v_cache);
+      for (int idx = t; idx < M * BN; idx += 256) {
+        const int m = idx / BN, c = idx % BN;
+        int s2, r;
+        wrow_index<BN>(w, n0 + c, s2, r);
+        vc[(size_t)e.row_pos[m] * e.d + r] = from_f32<bf16_t>(T[m * TS + c]).u;
+      }
+    } else {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(sg == 0 ? e.q_out : e.k_cache);
+      for (int idx = t; idx < M * (BN / 2); idx += 256) {
+        const int m = idx / (BN / 2), pr = idx % (BN / 2);
+        // tile columns of the pair: mode 2 -> (pr, pr + BN/2); else inside each head of the tile
+        int c1, c2;
+        if (w.mode == 2) {
+          c1 = pr;
+          c2 = pr + BN / 2;
+        } else {
+          c1 = (pr / half) * hd + pr % half;
+          c2 = c1 + half;
+        }
+        int s2, r1;
+        wrow_index<BN>(w, n0 + c1, s2, r1);         // dim j (< half) of its head; the partner is j + half
+        const int j = r1 % hd;
+        const float a = T[m * TS + c1], b = T[m * TS + c2];
+        const int p = e.row_pos[m];
+        const int pos = p - e.row_seq[m] * e.S;
+        const float2 cs = e.rope[pos * half + j];
+        const float o1 = a * cs.x - b * cs.y, o2 = b * cs.x + a * cs.y;
+        const size_t rowoff = sg == 0 ? (size_t)m * e.d : (size_t)p * e.d;
+        dst[rowoff + r1] = from_f32<bf16_t>(o1).u;
+        dst[rowoff + r1 + half] = from_f32<bf16_t>(o2).u;
+      }
     }
-  };
-  auto store_tiles = [&](int buf) {
-    uint16_t* a = As + buf * BM * C::LDS_STRIDE;
-    uint16_t* w = Ws + buf * BN * C::LDS_STRIDE;
+  } else if (e.kind == EPI_LM) {
+    // per row: (max, sum exp(l - max), lowest argmax) over this tile's columns
+    const int lane = t & 63, wave = t >> 6;
+    const int tile = n0 / BN;
+    for (int m = wave; m < M; m += 4) {
+      float mx = -INFINITY, sm = 0.f;
+      int am = 0x7fffffff;
+      for (int c = lane; c < BN; c += 64) {
+        const float l = T[m * TS + c];
+        if (e.logits) e.logits[(size_t)e.row_pos[m] * e.V + n0 + c] = l;
+        if (l > mx) {
+          sm = sm * expf(mx - l) + 1.f;
+          mx = l;
+          am = n0 + c;
+        } else {
+          sm += expf(l - mx);
+        }
+      }
 #pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) {
-      const int c = t + i * 256;
-      *reinterpret_cast<uint4*>(a + (c >> 3) * C::LDS_STRIDE + (c & 7) * 8) = ra[i];
+      for (int o = 32; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(mx, o, 64), s2 = __shfl_xor(sm, o, 64);
+        const int a2 = __shfl_xor(am, o, 64);
+        const float mn = fmaxf(mx, m2);
+        const float sn = (mx == -INFINITY ? 0.f : sm * expf(mx - mn)) + (m2 == -INFINITY ? 0.f : s2 * expf(m2 - mn));
+        am = (m2 > mx || (m2 == mx && a2 < am)) ? a2 : am;
+        mx = mn;
+        sm = sn;
+      }
+      if (lane == 0)
+        reinterpret_cast<float4*>(e.lm_part)[(size_t)m * e.lm_tiles + tile] =
+            make_float4(mx, sm, __int_as_float(am), 0.f);
     }
-#pragma unroll
-    for (int i = 0; i < C::W_CHUNKS; ++i) {
-      const int c = t + i * 256;
-      *reinterpret_cast<uint4*>(w + (c >> 3) * C::LDS_STRIDE + (c & 7) * 8) = rw[i];
-    }
-  };
-
-  f32x4 acc[C::MI][C::NI];
-#pragma unroll
-  for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < C::NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (nk > 0) {
-    load_tiles(0);
-    store_tiles(0);
   }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tiles(kt + 1);
-    const uint16_t* a = As + buf * BM * C::LDS_STRIDE;
-    const uint16_t* w = Ws + buf * BN * C::LDS_STRIDE;
-#pragma unroll
-    for (int ks = 0; ks < C::BK / 32; ++ks) {
-      const int koff = ks * 32 + (lane >> 4) * 8;
-      bf16x8 fa[C::MI], fb[C::NI];
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i) {
-        const uint4 v = *reinterpret_cast<const uint4*>(a + (wm0 + i * 16 + (lane & 15)) * C::LDS_STRIDE + koff);
-        fa[i] = __builtin_bit_cast(bf16x8, v);
-      }
-#pragma unroll
-      for (int j = 0; j < C::NI; ++j) {
-        const uint4 v = *reinterpret_cast<const uint4*>(w + (wn0 + j * 16 + (lane & 15)) * C::LDS_STRIDE + koff);
-        fb[j] = __builtin_bit_cast(bf16x8, v);
-      }
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-        for (int j = 0; j < C::NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_tiles(buf ^ 1);
-    __syncthreads();
-  }
+}
 
-  // C fragment: lane holds rows (lane/16)*4 + e, column lane%16 of each 16x16 block
-  float* Pout = P + (size_t)split * M_max * N;
-#pragma unroll
-  for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm0 + i * 16 + (lane >> 4) * 4 + e;
-        const int n = n0 + wn0 + j * 16 + (lane & 15);
-        if (m < M) Pout[(size_t)m * N + n] = acc[i][j][e];
-      }
+// Workgroup order: the splits of one column tile get block ids that are equal
+// mod 8, i.e. run on the same XCD (hardware deals block i to XCD i % 8), so
+// that they share the rows of A in that XCD's L2.
+__device__ __forceinline__ void tile_of_block(int bid, int splits, int& tile, int& split) {
+  const int xcd = bid & 7, r = bid >> 3;
+  split = r % splits;
+  tile = (r / splits) * 8 + xcd;
 }
 
 // ---------------------------------------------------------------------------
-// SIMT fallback: 64x64 tile, 4x4 outputs per thread, fp32 FMA
+// skinny weight-streaming GEMM (M <= 16 * MI <= 128)
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 GiB each)
+constexpr int kDepth = 4;                // 64-wide K steps fetched ahead
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// The K steps of a split are padded up to a multiple of kDepth; padding steps
+// and rows >= M read through out-of-range buffer offsets, which return zeros
+// without a memory access, so the pipeline below has no data-dependent
+// branches and every wait on the load counter is exact.
+template <int MI, int BN>
+__global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict__ A, int M_max,
+                                                     const int32_t* __restrict__ n_rows, int m_base, int K, WMap W,
+                                                     int N, int splits, int n_nt, float* __restrict__ P,
+                                                     Epilogue epi) {
+  constexpr int NB = BN / 64;               // 16-column blocks per wave
+  constexpr int MP = MI * 16;               // padded rows
+  constexpr int AS = 64 + 8;                // LDS row stride (bf16)
+  constexpr int A_ITEMS = MP * 8;           // 16-byte items per A step
+  constexpr int AP = (A_ITEMS + 255) / 256; // A items per thread per step
+  constexpr int TS = BN + 4;                // LDS row stride of the finished tile (fp32)
+  constexpr int A_BYTES = 2 * MP * AS * 2, T_BYTES = MP * TS * 4;
+  __shared__ __align__(16) char lds_raw[A_BYTES > T_BYTES ? A_BYTES : T_BYTES];
+  uint16_t (*As)[MP * AS] = reinterpret_cast<uint16_t (*)[MP * AS]>(lds_raw);
+
+  int tile, split;
+  tile_of_block(blockIdx.x, splits, tile, split);
+  if (tile >= n_nt) return;
+  const int M = min(*n_rows - m_base, M_max);
+  if (M <= 0) return;
+  const int n0 = tile * BN;
+  const int nk_all = K / 64;
+  const int ks0 = split * nk_all / splits, ks1 = (split + 1) * nk_all / splits;
+  const int nk = ks1 - ks0;
+  const int nk_pad = (nk + kDepth - 1) / kDepth * kDepth;
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+
+  // weight rows of this wave: 16-row runs inside one segment (the planner
+  // checks the tiling); rows of block nb are row0[nb] + l16
+  const int ncol0 = n0 + wave * (BN / 4);
+  int seg, row0[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) wrow_index<BN>(W, ncol0 + nb * 16, seg, row0[nb]);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(W.p[seg]), (short)0,
+                                                                      W.seg_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), (short)0,
+                                                                      M * K * 2, 0x00020000);
+  uint32_t woff[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) woff[nb] = (uint32_t)(((row0[nb] + l16) * K + ks0 * 64 + g * 8) * 2);
+  uint32_t aoff[AP];
+#pragma unroll
+  for (int i = 0; i < AP; ++i) {
+    const int c = t + i * 256;
+    aoff[i] = (uint32_t)((((c >> 3) * K) + ks0 * 64 + (c & 7) * 8) * 2);
+  }
+
+  uint4 ring[kDepth][NB][2];
+  uint4 aring[kDepth][AP];
+  auto issue = [&](int step, uint4 (&w)[NB][2], uint4 (&a)[AP]) {
+    const bool in = step < nk;
+    const uint32_t ks = (uint32_t)step * 128u;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint32_t o = in ? woff[nb] + ks : kOob;
+      w[nb][0] = buf_load16(wr, o);
+      w[nb][1] = buf_load16(wr, in ? o + 64u : kOob);
+    }
+#pragma unroll
+    for (int i = 0; i < AP; ++i) a[i] = buf_load16(ar, in ? aoff[i] + ks : kOob);
+  };
+  auto store_a = [&](int buf, const uint4 (&a)[AP]) {
+#pragma unroll
+    for (int i = 0; i < AP; ++i) {
+      const int c = t + i * 256;
+      if (A_ITEMS % 256 == 0 || c < A_ITEMS) *reinterpret_cast<uint4*>(&As[buf][(c >> 3) * AS + (c & 7) * 8]) = a[i];
+    }
+  };
+
+  f32x4 acc[MI][NB];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < kDepth - 1; ++s) issue(s, ring[s], aring[s]);
+  store_a(0, aring[0]);
+  lds_barrier();
+
+  for (int kt = 0; kt < nk_pad; kt += kDepth) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      issue(kt + u + kDepth - 1, ring[(u + kDepth - 1) % kDepth], aring[(u + kDepth - 1) % kDepth]);
+      const uint16_t* a = As[u & 1];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const uint4 av = *reinterpret_cast<const uint4*>(a + (i * 16 + l16) * AS + kc * 32 + g * 8);
+          const bf16x8 fa = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[i][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, __builtin_bit_cast(bf16x8, ring[u][nb][kc]),
+                                                                 acc[i][nb], 0, 0, 0);
+        }
+      }
+      store_a((u + 1) & 1, aring[(u + 1) % kDepth]);
+      lds_barrier();
+    }
+  }
+
+  // C fragment: rows i*16 + g*4 + r, column l16 of each 16-column block
+  if (epi.kind == EPI_NONE) {              // partial sums of this split
+    float* Ps = P + (size_t)split * M_max * N;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = i * 16 + g * 4 + r;
+          if (m < M) Ps[(size_t)m * N + n0 + wave * (BN / 4) + nb * 16 + l16] = acc[i][nb][r];
+        }
+    return;
+  }
+  float* T = reinterpret_cast<float*>(lds_raw);   // the A buffers are free after the last barrier
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) T[(i * 16 + g * 4 + r) * TS + wave * (BN / 4) + nb * 16 + l16] = acc[i][nb][r];
+  lds_barrier();
+  tile_epilogue<BN, TS>(epi, T, W, n0, M);
+}
+
+// ---------------------------------------------------------------------------
+// 128x128-tile MFMA GEMM for many rows: A and W tiles go through LDS (double
+// buffer), fetched kDepth - 1 steps ahead into register rings with buffer
+// loads (rows >= M and padding steps read as zeros)
+// ---------------------------------------------------------------------------
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kLds = kBK + 8;
+
+__global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ A, int M_max,
+                                                   const int32_t* __restrict__ n_rows, int m_base, int K, WMap W,
+                                                   int N, int splits, int n_mt, int n_nt, float* __restrict__ P,
+                                                   Epilogue epi) {
+  constexpr int WM = kBM / 2, WN = kBN / 2, MI = WM / 16, NI = WN / 16;
+  constexpr int CH = kBM * kBK / 8 / 256;      // 16-byte items per thread per operand per step (4)
+  extern __shared__ __align__(16) uint16_t lds[];
+  uint16_t* As = lds;                          // [2][kBM][kLds]
+  uint16_t* Ws = lds + 2 * kBM * kLds;         // [2][kBN][kLds]
+
+  int tile, split;
+  tile_of_block(blockIdx.x, splits, tile, split);
+  if (tile >= n_mt * n_nt) return;
+  const int mt = tile % n_mt, nt = tile / n_mt;
+  static_assert(2 * (kBM + kBN) * kLds * 2 >= kBM * (kBN + 4) * 4, "epilogue tile must fit the LDS buffers");
+  const int M = min(*n_rows - m_base, M_max);
+  const int m0 = mt * kBM;
+  if (m0 >= M) return;
+  const int n0 = nt * kBN;
+  const int nk_all = K / kBK;
+  const int ks0 = split * nk_all / splits, ks1 = (split + 1) * nk_all / splits;
+  const int nk = ks1 - ks0;
+  const int nk_pad = (nk + kDepth - 1) / kDepth * kDepth;
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+
+  // item i of thread t covers tile row (t >> 3) + 32 i, columns ((t & 7) * 8, +8)
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A) + (size_t)m0 * K, (short)0, (min(M - m0, kBM)) * K * 2, 0x00020000);
+  __amdgpu_buffer_rsrc_t wr[CH];
+  uint32_t aoff[CH], woff[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int row = (t >> 3) + 32 * i, kc = (t & 7) * 8;
+    aoff[i] = (uint32_t)((row * K + ks0 * kBK + kc) * 2);
+    int sg, r;
+    wrow_index<kBN>(W, n0 + row, sg, r);        // rows 32i..32i+31 share a segment for every mode
+    sg = __builtin_amdgcn_readfirstlane(sg);
+    wr[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(W.p[sg]), (short)0, W.seg_bytes, 0x00020000);
+    woff[i] = (uint32_t)((r * K + ks0 * kBK + kc) * 2);
+  }
+  uint4 ra[kDepth][CH], rw[kDepth][CH];
+  auto issue = [&](int step, uint4 (&a)[CH], uint4 (&w)[CH]) {
+    const bool in = step < nk;
+    const uint32_t ks = (uint32_t)step * (kBK * 2);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      a[i] = buf_load16(ar, in ? aoff[i] + ks : kOob);
+      w[i] = buf_load16(wr[i], in ? woff[i] + ks : kOob);
+    }
+  };
+  auto store = [&](int buf, const uint4 (&a)[CH], const uint4 (&w)[CH]) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int row = (t >> 3) + 32 * i, kc = (t & 7) * 8;
+      *reinterpret_cast<uint4*>(As + buf * kBM * kLds + row * kLds + kc) = a[i];
+      *reinterpret_cast<uint4*>(Ws + buf * kBN * kLds + row * kLds + kc) = w[i];
+    }
+  };
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < kDepth - 1; ++s) issue(s, ra[s], rw[s]);
+  store(0, ra[0], rw[0]);
+  lds_barrier();
+  for (int kt = 0; kt < nk_pad; kt += kDepth) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      issue(kt + u + kDepth - 1, ra[(u + kDepth - 1) % kDepth], rw[(u + kDepth - 1) % kDepth]);
+      const uint16_t* a = As + (u & 1) * kBM * kLds;
+      const uint16_t* w = Ws + (u & 1) * kBN * kLds;
+#pragma unroll
+      for (int ks = 0; ks < kBK / 32; ++ks) {
+        const int koff = ks * 32 + (lane >> 4) * 8;
+        bf16x8 fa[MI], fb[NI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          fa[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(a + (wm0 + i * 16 + (lane & 15)) * kLds + koff));
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          fb[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(w + (wn0 + j * 16 + (lane & 15)) * kLds + koff));
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+      store((u + 1) & 1, ra[(u + 1) % kDepth], rw[(u + 1) % kDepth]);
+      lds_barrier();
+    }
+  }
+
+  if (epi.kind == EPI_NONE) {
+    float* Ps = P + (size_t)split * M_max * N;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm0 + i * 16 + (lane >> 4) * 4 + r;
+          if (m < M) Ps[(size_t)m * N + n0 + wn0 + j * 16 + (lane & 15)] = acc[i][j][r];
+        }
+    return;
+  }
+  // finished tile to LDS (rows relative to m0), then the epilogue on a view
+  // whose row 0 is packed row m0
+  constexpr int TS = kBN + 4;
+  float* T = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        T[(wm0 + i * 16 + (lane >> 4) * 4 + r) * TS + wn0 + j * 16 + (lane & 15)] = acc[i][j][r];
+  lds_barrier();
+  Epilogue e = epi;
+  const int Mt = min(kBM, M - m0);
+  if (e.kind == EPI_SWIGLU) e.act_out = reinterpret_cast<uint16_t*>(e.act_out) + (size_t)m0 * e.F;
+  if (e.kind == EPI_QKV) e.q_out = reinterpret_cast<uint16_t*>(e.q_out) + (size_t)m0 * e.d;
+  if (e.row_pos) e.row_pos += m0;
+  if (e.row_seq) e.row_seq += m0;
+  if (e.kind == EPI_LM) e.lm_part += (size_t)m0 * e.lm_tiles * 4;
+  tile_epilogue<kBN, TS>(e, T, W, n0, Mt);
+}
+
+// ---------------------------------------------------------------------------
+// SIMT fallback: 64x64 tile, 4x4 outputs per thread, fp32 FMA, no epilogue
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_gemm_simt(const T* __restrict__ A, int M_max,
-                                                   const int32_t* __restrict__ n_rows, int m_base, int K, WSeg W,
-                                                   int n_seg, int N, float* __restrict__ P) {
+                                                   const int32_t* __restrict__ n_rows, int m_base, int K, WMap W,
+                                                   int N, float* __restrict__ P) {
   constexpr int TB = 64, BK = 16;
   __shared__ float As[BK][TB + 4];
   __shared__ float Ws[BK][TB + 4];
@@ -188,8 +477,8 @@ __global__ __launch_bounds__(256) void k_gemm_simt(const T* __restrict__ A, int 
       float av = 0.f, wv = 0.f;
       if (m < M && k < K) av = to_f32(A[(size_t)m * K + k]);
       if (n < N && k < K) {
-        const int sg = n / n_seg;
-        wv = to_f32(reinterpret_cast<const T*>(W.p[sg])[(size_t)(n - sg * n_seg) * K + k]);
+        const int sg = n / W.n_seg;
+        wv = to_f32(reinterpret_cast<const T*>(W.p[sg])[(size_t)(n - sg * W.n_seg) * K + k]);
       }
       As[kk][row] = av;
       Ws[kk][row] = wv;
@@ -219,52 +508,117 @@ __global__ __launch_bounds__(256) void k_gemm_simt(const T* __restrict__ A, int 
     }
 }
 
-constexpr int kBM = 128, kBN = 128;
+template <int MI, int BN>
+hipError_t launch_skinny(const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows, int m_base, int K,
+                         const WMap& w, int N, float* P, const Epilogue& epi, hipStream_t st) {
+  const int n_nt = N / BN;
+  const int grid = cdiv(n_nt, 8) * 8 * plan.splits;
+  hipLaunchKernelGGL((k_gemm_skinny<MI, BN>), dim3(grid), dim3(256), 0, st, (const uint16_t*)A, M_max, n_rows, m_base,
+                     K, w, N, plan.splits, n_nt, P, epi);
+  return hipGetLastError();
+}
+
+template <int BN>
+hipError_t launch_skinny_bn(const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows, int m_base, int K,
+                            const WMap& w, int N, float* P, const Epilogue& epi, hipStream_t st) {
+  switch (plan.mi) {
+    case 1: return launch_skinny<1, BN>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+    case 2: return launch_skinny<2, BN>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+    case 4: return launch_skinny<4, BN>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+    default: return launch_skinny<8, BN>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+  }
+}
 
 }  // namespace
 
-GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K) {
-  GemmPlan p{1, 0};
-  if (dt == DL_BF16 && K % 64 == 0 && N % kBN == 0) {
-    p.kind = 1;
-    // Split K until the grid covers the 256 CUs about once (at most 8 ways,
-    // each split a whole number of 64-wide K steps).
+GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim, int F) {
+  const GemmPlan simt{GEMM_SIMT, 1, 128, 8, 0};
+  GemmPlan p = simt;
+  if (dt != DL_BF16 || K % 64 != 0 || M <= 0) return p;
+  const int nk = K / 64;
+  const int n_seg = epi_kind == EPI_QKV ? N / 3 : epi_kind == EPI_SWIGLU ? N / 2 : N;
+  if (M <= 128 && (long long)n_seg * K * 2 < 0x7fff0000LL && 128LL * K * 2 < 0x7fff0000LL) {
+    p.kind = GEMM_SKINNY;
+    p.mi = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+    switch (epi_kind) {
+      case EPI_QKV:
+        if (head_dim == 128 && n_seg % 128 == 0) {
+          p.bn = 64;
+          p.wmode = 2;
+        } else if (head_dim % 2 == 0 && 128 % head_dim == 0 && n_seg % 128 == 0) {
+          p.bn = 128;
+        } else {
+          return simt;
+        }
+        break;
+      case EPI_SWIGLU:
+        if (F % 32 != 0) return simt;
+        p.bn = 64;
+        p.wmode = 1;
+        break;
+      case EPI_LM:
+        p.bn = 128;
+        break;
+      default: {  // partial sums: split K until the grid covers the CUs about once
+        p.bn = 64;
+        if (N % 64 != 0) return simt;
+        const int tiles = N / 64;
+        p.splits = std::max(1, std::min(std::min((256 + tiles - 1) / tiles, 16), nk));
+      }
+    }
+    if (N % p.bn != 0) return simt;
+    return p;
+  }
+  if (N % kBN != 0) return p;
+  if (epi_kind == EPI_SWIGLU && F % (kBN / 2) != 0) return p;
+  if (epi_kind == EPI_QKV && !(head_dim % 2 == 0 && 128 % head_dim == 0 && (N / 3) % kBN == 0)) return p;
+  p.kind = GEMM_LARGE;
+  p.bn = kBN;
+  p.wmode = epi_kind == EPI_SWIGLU ? 1 : 0;
+  if (epi_kind == EPI_NONE) {
     const int tiles = cdiv(M, kBM) * (N / kBN);
     int s = 1;
-    while (tiles * s < 256 && s < 8 && (K / 64) % (s * 2) == 0) s *= 2;
+    while (tiles * s < 256 && s < 8 && s * 2 <= nk) s *= 2;
     p.splits = s;
   }
   return p;
 }
 
 hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows,
-                       int m_base, int K, const void* const* Wseg, int n_seg, int N, float* P, hipStream_t st) {
-  WSeg w;
+                       int m_base, int K, const void* const* Wseg, int n_seg, int N, float* P, const Epilogue& epi,
+                       hipStream_t st) {
+  WMap w;
   for (int i = 0; i < 4; ++i) w.p[i] = Wseg[i];
+  w.mode = plan.wmode;
+  w.n_seg = n_seg;
+  w.seg_bytes = (int)std::min<long long>((long long)(plan.wmode == 1 ? N / 2 : n_seg) * K * 2, 0x7fffffffLL);
   if (M_max <= 0) return hipSuccess;
-  if (plan.kind == 1) {
-    using C = MfmaCfg<kBM, kBN>;
+  if (plan.kind == GEMM_SKINNY) {
+    if (plan.bn == 64) return launch_skinny_bn<64>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+    return launch_skinny_bn<128>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+  }
+  if (plan.kind == GEMM_LARGE) {
+    const int lds_bytes = 2 * (kBM + kBN) * kLds * 2;
     static bool attr_set = false;  // the tile needs more than the default 64 KiB of LDS
     if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma<kBM, kBN>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+      hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         lds_bytes);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
     const int n_mt = cdiv(M_max, kBM), n_nt = N / kBN;
-    const int kps = K / plan.splits;
-    const int grid = n_mt * n_nt * plan.splits;
-    hipLaunchKernelGGL((k_gemm_mfma<kBM, kBN>), dim3(grid), dim3(256), C::LDS_BYTES, st, (const uint16_t*)A, M_max,
-                       n_rows, m_base, K, w, n_seg, N, kps, n_mt, n_nt, P);
-  } else {
-    dim3 grid(cdiv(N, 64), cdiv(M_max, 64));
-    if (dt == DL_F32)
-      hipLaunchKernelGGL(k_gemm_simt<float>, grid, dim3(256), 0, st, (const float*)A, M_max, n_rows, m_base, K, w,
-                         n_seg, N, P);
-    else
-      hipLaunchKernelGGL(k_gemm_simt<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)A, M_max, n_rows, m_base, K, w,
-                         n_seg, N, P);
+    const int grid = cdiv(n_mt * n_nt, 8) * 8 * plan.splits;
+    hipLaunchKernelGGL(k_gemm_mfma, dim3(grid), dim3(256), lds_bytes, st, (const uint16_t*)A, M_max, n_rows, m_base,
+                       K, w, N, plan.splits, n_mt, n_nt, P, epi);
+    return hipGetLastError();
   }
+  dim3 grid(cdiv(N, 64), cdiv(M_max, 64));
+  if (dt == DL_F32)
+    hipLaunchKernelGGL(k_gemm_simt<float>, grid, dim3(256), 0, st, (const float*)A, M_max, n_rows, m_base, K, w, N,
+                       P);
+  else
+    hipLaunchKernelGGL(k_gemm_simt<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)A, M_max, n_rows, m_base, K, w, N,
+                       P);
   return hipGetLastError();
 }
 

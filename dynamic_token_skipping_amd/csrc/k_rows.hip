@@ -5,6 +5,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "launch.h"
 
 namespace dtsk {
@@ -388,6 +390,83 @@ __global__ __launch_bounds__(kRowThreads) void k_rmsnorm(const float* __restrict
   for (int c = threadIdx.x; c < d; c += blockDim.x) o[c] = from_f32<T>(xr[c] * inv * to_f32(g[c]));
 }
 
+// Split sum + residual + (optional) RMSNorm of the next sub-block, one block
+// per packed row: x += sum_s P[s]; out = T(x / sqrt(mean(x^2) + eps) * g).
+template <typename T, int kChunks>
+__global__ __launch_bounds__(kRowThreads) void k_reduce_rows(const float* __restrict__ P, int splits, int M_max,
+                                                             const int32_t* __restrict__ n_rows, int d,
+                                                             float* __restrict__ x, const T* __restrict__ g, float eps,
+                                                             T* __restrict__ out) {
+  // d == kChunks * 4 * kRowThreads: every thread owns kChunks float4 of the row,
+  // and all of its loads are issued before any is used
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  if (r >= *n_rows) return;
+  const size_t sstride = (size_t)M_max * d;
+  float4* xr = reinterpret_cast<float4*>(x + (size_t)r * d);
+  const float4* pr = reinterpret_cast<const float4*>(P + (size_t)r * d);
+  float4 v[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) v[c] = xr[threadIdx.x + c * kRowThreads];
+  for (int s = 0; s < splits; ++s) {
+    float4 ps[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) ps[c] = pr[s * (sstride / 4) + threadIdx.x + c * kRowThreads];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      v[c].x += ps[c].x;
+      v[c].y += ps[c].y;
+      v[c].z += ps[c].z;
+      v[c].w += ps[c].w;
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    xr[threadIdx.x + c * kRowThreads] = v[c];
+    ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+  }
+  if (!g) return;
+  ss = block_sum(ss, red);
+  const float inv = 1.f / sqrtf(ss / (float)d + eps);
+  T* o = out + (size_t)r * d;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int col = (threadIdx.x + c * kRowThreads) * 4;
+    o[col] = from_f32<T>(v[c].x * inv * to_f32(g[col]));
+    o[col + 1] = from_f32<T>(v[c].y * inv * to_f32(g[col + 1]));
+    o[col + 2] = from_f32<T>(v[c].z * inv * to_f32(g[col + 2]));
+    o[col + 3] = from_f32<T>(v[c].w * inv * to_f32(g[col + 3]));
+  }
+}
+
+// Any width: the plain loop.
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_reduce_rows_any(const float* __restrict__ P, int splits, int M_max,
+                                                                 const int32_t* __restrict__ n_rows, int d,
+                                                                 float* __restrict__ x, const T* __restrict__ g,
+                                                                 float eps, T* __restrict__ out) {
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  if (r >= *n_rows) return;
+  const size_t sstride = (size_t)M_max * d;
+  float* xr = x + (size_t)r * d;
+  const float* pr = P + (size_t)r * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < splits; ++s) acc += pr[s * sstride + c];
+    const float v = xr[c] + acc;
+    xr[c] = v;
+    ss += v * v;
+  }
+  if (!g) return;
+  ss = block_sum(ss, red);
+  const float inv = 1.f / sqrtf(ss / (float)d + eps);
+  T* o = out + (size_t)r * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) o[c] = from_f32<T>(xr[c] * inv * to_f32(g[c]));
+}
+
 // RoPE table: (cos, sin) of pos * base^(-2j/dh), computed in double.
 __global__ void k_rope_table(int S, int half, int head_dim, double base, float2* __restrict__ tab) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -543,6 +622,57 @@ __global__ __launch_bounds__(kRowThreads) void k_lm_reduce(const float* __restri
     conf[p] = 1.f / Ssum;
     argmax[p] = A;
   }
+}
+
+// Merge per-tile (max, sum exp, argmax) statistics of a row, in tile order.
+__device__ __forceinline__ void lm_merge(float& m, float& s, int& a, float m2, float s2, int a2) {
+  const float mn = fmaxf(m, m2);
+  const float sn = (m == -INFINITY ? 0.f : s * expf(m - mn)) + (m2 == -INFINITY ? 0.f : s2 * expf(m2 - mn));
+  a = (m2 > m || (m2 == m && a2 < a)) ? a2 : a;
+  m = mn;
+  s = sn;
+}
+
+__global__ __launch_bounds__(kRowThreads) void k_lm_merge(const float4* __restrict__ part, int tiles,
+                                                          const int32_t* __restrict__ n_rows, int m_base,
+                                                          const int32_t* __restrict__ row_pos,
+                                                          float* __restrict__ conf, int32_t* __restrict__ argmax) {
+  __shared__ float sm[kRowThreads / 64], ss[kRowThreads / 64];
+  __shared__ int sa[kRowThreads / 64];
+  const int r = blockIdx.x;
+  if (m_base + r >= *n_rows) return;
+  float m = -INFINITY, s = 0.f;
+  int a = 0x7fffffff;
+  const float4* pr = part + (size_t)r * tiles;
+  for (int i = threadIdx.x; i < tiles; i += blockDim.x) {
+    const float4 v = pr[i];
+    lm_merge(m, s, a, v.x, v.y, __float_as_int(v.z));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    const int a2 = __shfl_xor(a, o, 64);
+    lm_merge(m, s, a, m2, s2, a2);
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) {
+    sm[w] = m;
+    ss[w] = s;
+    sa[w] = a;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = sm[0], Ssum = ss[0];
+    int A = sa[0];
+    for (int i = 1; i < kRowThreads / 64; ++i) lm_merge(M, Ssum, A, sm[i], ss[i], sa[i]);
+    const int p = row_pos[m_base + r];
+    conf[p] = 1.f / Ssum;
+    argmax[p] = A;
+  }
+}
+
+__global__ void k_fill_i32(int32_t* __restrict__ p, int32_t v, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -757,6 +887,48 @@ hipError_t launch_lm_reduce(const float* P, int splits, const RowMap& rm, int m_
   if (M_max <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_lm_reduce, dim3(M_max), dim3(kRowThreads), 0, st, P, splits, M_max, rm.n_rows, m_base,
                      rm.row_pos, V, conf, argmax, logits_out);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t reduce_rows_t(const float* P, int splits, const RowMap& rm, int d, float* x, const void* g,
+                                float eps, void* out, hipStream_t st) {
+  const T* gg = (const T*)g;
+  T* oo = (T*)out;
+  if (d == 4096)
+    hipLaunchKernelGGL((k_reduce_rows<T, 4>), dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
+                       rm.n_rows, d, x, gg, eps, oo);
+  else if (d == 2048)
+    hipLaunchKernelGGL((k_reduce_rows<T, 2>), dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
+                       rm.n_rows, d, x, gg, eps, oo);
+  else if (d == 1024)
+    hipLaunchKernelGGL((k_reduce_rows<T, 1>), dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
+                       rm.n_rows, d, x, gg, eps, oo);
+  else
+    hipLaunchKernelGGL(k_reduce_rows_any<T>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows,
+                       d, x, gg, eps, oo);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_rows(dl_dtype dt, const float* P, int splits, const RowMap& rm, int d, float* x,
+                              const void* g, float eps, void* out, hipStream_t st) {
+  if (rm.R_max <= 0) return hipSuccess;
+  if (dt == DL_F32) return reduce_rows_t<float>(P, splits, rm, d, x, g, eps, out, st);
+  return reduce_rows_t<bf16_t>(P, splits, rm, d, x, g, eps, out, st);
+}
+
+hipError_t launch_lm_merge(const float* lm_part, int lm_tiles, const RowMap& rm, int m_base, int M_max, float* conf,
+                           int32_t* argmax, hipStream_t st) {
+  if (M_max <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_lm_merge, dim3(M_max), dim3(kRowThreads), 0, st, (const float4*)lm_part, lm_tiles, rm.n_rows,
+                     m_base, rm.row_pos, conf, argmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)std::min<size_t>(1024, (n + 255) / 256);
+  hipLaunchKernelGGL(k_fill_i32, dim3(blocks), dim3(256), 0, st, p, v, n);
   return hipGetLastError();
 }
 

@@ -52,18 +52,55 @@ hipError_t launch_epi_residual(const float* P, int splits, const RowMap& rm, int
 hipError_t launch_epi_swiglu(dl_dtype dt, const float* P, int splits, const RowMap& rm, int F, void* out,
                              hipStream_t st);
 
-// ---- GEMM: P[s][m][n] = sum_{k in split s} A[m][k] * W[n][k] ------------------------
-// W is given as up to 4 segments of n_seg rows each (segment i covers output
-// columns [i*n_seg, (i+1)*n_seg)).  Rows m >= *rm.n_rows are not computed.
-struct GemmPlan {
-  int splits;
-  int kind;  // 0 = SIMT, 1 = MFMA
+// ---- GEMM with fused epilogue -----------------------------------------------------
+enum EpiKind { EPI_NONE = 0, EPI_QKV = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_LM = 4 };
+
+// What the last workgroup of a column tile does with the summed tile.  Row m
+// of the product is packed row m of the row map (pointers already offset to
+// the product's first row).
+struct Epilogue {
+  int kind;
+  float* x;                       // EPI_RESID: x[m][n] += C[m][n] (row stride N)
+  void* q_out;                    // EPI_QKV: rotated q rows [M, d]
+  void* k_cache;                  // EPI_QKV: this layer's [B*S, d]
+  void* v_cache;
+  const int32_t* row_pos;         // flat [B*S] row of packed row m
+  const int32_t* row_seq;
+  int S, d, head_dim;
+  const float2* rope;             // (cos, sin) [S, head_dim/2]
+  void* act_out;                  // EPI_SWIGLU: silu(gate) * up rows [M, F]
+  int F;
+  float* lm_part;                 // EPI_LM: float4 (max, sum exp, argmax bits, 0) [M][lm_tiles]
+  int lm_tiles;
+  float* logits;                  // EPI_LM: optional fp32 logits [B*S, V] at row_pos
+  int V;
 };
-GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K);
+
+enum GemmKind { GEMM_SIMT = 0, GEMM_LARGE = 1, GEMM_SKINNY = 2 };
+struct GemmPlan {
+  int kind;
+  int splits;  // > 1 only with EPI_NONE: fp32 partials reduced by launch_reduce_rows
+  int bn;      // column tile
+  int mi;      // skinny: 16-row blocks of A
+  int wmode;   // weight-row order: 0 segmented, 1 gate|up interleaved, 2 RoPE pairs
+};
+// The epilogue kind decides the tile the fused epilogue needs; a GEMM_SIMT
+// plan leaves the epilogue to the separate kernels below.
+GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim, int F);
 // Rows [m_base, m_base + M_max) of A (A points at row m_base); rows at or
-// beyond *n_rows are skipped.  P is [splits][M_max][N].
+// beyond *n_rows are skipped.  With EPI_NONE or a GEMM_SIMT plan, P receives
+// [splits][M_max][N] fp32 partials; otherwise the epilogue consumes the tile.
 hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows,
-                       int m_base, int K, const void* const* Wseg, int n_seg, int N, float* P, hipStream_t st);
+                       int m_base, int K, const void* const* Wseg, int n_seg, int N, float* P, const Epilogue& epi,
+                       hipStream_t st);
+// x[r] += sum over splits of P[s][r] (in split order); then, if g != nullptr,
+// out[r] = T(x[r] / sqrt(mean(x[r]^2) + eps) * g).  Packed rows of the map.
+hipError_t launch_reduce_rows(dl_dtype dt, const float* P, int splits, const RowMap& rm, int d, float* x,
+                              const void* g, float eps, void* out, hipStream_t st);
+// Merge the per-tile LM statistics of rows [m_base, m_base + M_max) into conf / argmax.
+hipError_t launch_lm_merge(const float* lm_part, int lm_tiles, const RowMap& rm, int m_base, int M_max, float* conf,
+                           int32_t* argmax, hipStream_t st);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t st);
 
 // ---- attention ---------------------------------------------------------------------
 bool attention_supported(dl_dtype dt, int S, int head_dim);

@@ -54,7 +54,7 @@ def test_workspace_bytes(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(d=4000), -2), (dict(head_dim=127, d=32 * 127), -2), (dict(dtype=7), -3), (dict(B=0), -1),
-    (dict(S=9000), -7), (dict(B=2000), -7),
+    (dict(S=9000, dtype="f32"), -7), (dict(B=2000), -7),
 ])
 def test_bad_dims_rejected(lib, kw, code):
     d = _dims(**kw)
