@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--workload", default="full8b")
+    ap.add_argument("--timing-stride", type=int, default=8,
+                    help="time about one launch in this many of each kernel class (1: every launch)")
     return ap.parse_args()
 
 
@@ -106,8 +108,8 @@ def main():
     import torch
 
     import workloads
-    from dynamic_token_skipping_amd import (DL_KC_ATTN, DL_KC_GEMM, DL_KC_LMHEAD, Decoder, DeviceModel,
-                                            dl_timing_enable, dl_timing_read, dl_timing_reset)
+    from dynamic_token_skipping_amd import (DL_KC_ATTN, DL_KC_GEMM, DL_KC_GEMM_TILED, DL_KC_LMHEAD, Decoder,
+                                            DeviceModel, dl_timing_enable, dl_timing_read, dl_timing_reset)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = workloads.workload(args.workload)
@@ -126,8 +128,9 @@ def main():
     torch.cuda.synchronize()
 
     dl_timing_reset()
-    for kc in (DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD):
-        dl_timing_enable(kc, True)
+    classes = (DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD, DL_KC_GEMM_TILED)
+    for kc in classes:
+        dl_timing_enable(kc, 1 if kc == DL_KC_LMHEAD else max(1, args.timing_stride))
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -140,8 +143,8 @@ def main():
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    for kc in (DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD):
-        dl_timing_enable(kc, False)
+    for kc in classes:
+        dl_timing_enable(kc, 0)
     ms = start.elapsed_time(end)
     steps_per_s = args.steps / (ms / 1e3)
     tok_per_s = steps_per_s * dec.per_step * dec.B
@@ -149,11 +152,13 @@ def main():
     g = dl_timing_read(DL_KC_GEMM)
     a = dl_timing_read(DL_KC_ATTN)
     lmh = dl_timing_read(DL_KC_LMHEAD)
+    gt = dl_timing_read(DL_KC_GEMM_TILED)
     gemm_gbs = g["bytes"] / (g["ms"] / 1e3) / 1e9 if g["ms"] > 0 else 0.0
     roofline = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": "k_gemm_mfma (every layer product: QKV, O, gate/up, down)",
-                "launches": g["launches"], "avg_launch_us": round(g["ms"] * 1e3 / max(g["launches"], 1), 2),
+                "kernel": "k_gemm_skinny (layer products on the kept rows: QKV, O, gate/up, down)",
+                "launches_timed": g["launches"], "launches_total": g["launches"] + g["dropped"],
+                "avg_launch_us": round(g["ms"] * 1e3 / max(g["launches"], 1), 2),
                 "alg_bytes_per_launch": round(g["bytes"] / max(g["launches"], 1))}
     out = {
         "metric": "denoise steps/sec & gen tokens/sec at keep=25% (8B-class); HBM GB/s vs peak",
@@ -166,11 +171,15 @@ def main():
                    "global_batch": dec.B, "seq_len": dec.S, "keep": sched.keep, "skip_layer": sched.skip_layer},
         "roofline": roofline,
         "kernels": {
-            "gemm": {"ms": round(g["ms"], 3), "launches": g["launches"], "GB/s": round(gemm_gbs, 1),
+            "gemm": {"ms_timed": round(g["ms"], 3), "launches_timed": g["launches"], "GB/s": round(gemm_gbs, 1),
                      "TFLOP/s": round(g["flops"] / max(g["ms"], 1e-9) / 1e9, 1)},
-            "attention": {"ms": round(a["ms"], 3), "launches": a["launches"],
+            "gemm_tiled": {"ms_timed": round(gt["ms"], 3), "launches_timed": gt["launches"],
+                           "GB/s": round(gt["bytes"] / max(gt["ms"], 1e-9) / 1e6, 1),
+                           "TFLOP/s": round(gt["flops"] / max(gt["ms"], 1e-9) / 1e9, 1)},
+            "attention": {"ms_timed": round(a["ms"], 3), "launches_timed": a["launches"],
+                          "avg_launch_us": round(a["ms"] * 1e3 / max(a["launches"], 1), 2),
                           "TFLOP/s": round(a["flops"] / max(a["ms"], 1e-9) / 1e9, 2)},
-            "lm_head": {"ms": round(lmh["ms"], 3), "launches": lmh["launches"],
+            "lm_head": {"ms_timed": round(lmh["ms"], 3), "launches_timed": lmh["launches"],
                         "GB/s": round(lmh["bytes"] / max(lmh["ms"], 1e-9) / 1e6, 1)},
         },
         "wall_s": round(wall, 3),

@@ -27,7 +27,7 @@ TORCH_DTYPES = {DL_F32: torch.float32, DL_BF16: torch.bfloat16}
 EXPORTS = ("dl_score_select", "dl_gather", "dl_scatter_cache", "dl_partial_attn", "dl_ffn_rows", "dl_lm_head_rows",
            "dl_unmask", "dl_denoise_step", "dl_workspace_bytes", "dl_status_string", "dl_last_error",
            "dl_abi_version", "dl_timing_enable", "dl_timing_reset", "dl_timing_read")
-DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD = 0, 1, 2
+DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD, DL_KC_GEMM_TILED = 0, 1, 2, 3
 
 
 class Dims(Structure):
@@ -244,8 +244,9 @@ def dl_abi_version() -> int:
     return int(load().dl_abi_version())
 
 
-def dl_timing_enable(kc: int, enable: bool = True):
-    _check(load().dl_timing_enable(int(kc), int(bool(enable))))
+def dl_timing_enable(kc: int, stride: int = 1):
+    """Time about one launch in `stride` of class kc (1: every launch, 0 or False: off)."""
+    _check(load().dl_timing_enable(int(kc), int(stride)))
 
 
 def dl_timing_reset():

@@ -178,10 +178,12 @@ RowMap rowmap_at(void* ws, const RowMapMem& m, int R_max, int T_max) {
 // ---------------------------------------------------------------------------
 // kernel timing
 // ---------------------------------------------------------------------------
-constexpr int kTimingPool = 8192;
+constexpr int kTimingPool = 1 << 16;
 
 struct TimingClass {
   bool enabled = false;
+  uint32_t stride = 1;            // sample about one launch in `stride`
+  uint32_t seq = 0;               // launches seen since reset
   std::vector<hipEvent_t> ev;     // 2 per launch
   int used = 0;                   // pairs recorded since reset
   int64_t dropped = 0;
@@ -194,7 +196,8 @@ template <typename F>
 hipError_t timed(dl_kernel_class kc, hipStream_t st, double bytes, double flops, F&& launch) {
   TimingClass& t = g_timing[kc];
   if (!t.enabled) return launch();
-  if (t.used >= kTimingPool) {
+  const uint32_t i = t.seq++;
+  if (t.used >= kTimingPool || (t.stride > 1 && ((i * 2654435761u) >> 13) % t.stride != 0)) {
     ++t.dropped;
     return launch();
   }
@@ -266,6 +269,7 @@ dl_status product(const Ctx& c, dl_kernel_class kc, const void* A, const RowMap&
   float* P = at<float>(c.ws, c.L->P);
   const GemmPlan p = plan_gemm(d.dtype, rows, N, K, e.kind, d.head_dim, d.d_ffn);
   if (splits_out) *splits_out = p.splits;
+  if (kc == DL_KC_GEMM && p.kind != GEMM_SKINNY) kc = DL_KC_GEMM_TILED;
   DL_CHECK_HIP(timed(kc, c.st, gemm_bytes(d, rows, N, K), 2.0 * rows * N * K, [&] {
     return launch_gemm(d.dtype, p, A, rows, rm.n_rows, m_base, K, seg, n_seg, N, P, e, c.st);
   }));
@@ -394,20 +398,23 @@ extern "C" {
 
 int32_t dl_abi_version(void) { return DL_ABI_VERSION; }
 
-dl_status dl_timing_enable(dl_kernel_class kc, int32_t enable) {
+dl_status dl_timing_enable(dl_kernel_class kc, int32_t stride) {
   if (kc < 0 || kc >= DL_KC_COUNT) return fail(DL_E_ARG, "kernel class %d unknown", (int)kc);
+  if (stride < 0) return fail(DL_E_ARG, "sampling stride %d < 0", (int)stride);
   TimingClass& t = g_timing[kc];
-  if (enable && t.ev.empty()) {
+  if (stride && t.ev.empty()) {
     t.ev.resize(2 * kTimingPool);
     for (auto& e : t.ev) DL_CHECK_HIP(hipEventCreate(&e));
   }
-  t.enabled = enable != 0;
+  t.enabled = stride != 0;
+  t.stride = stride ? (uint32_t)stride : 1u;
   return DL_OK;
 }
 
 dl_status dl_timing_reset(void) {
   for (auto& t : g_timing) {
     t.used = 0;
+    t.seq = 0;
     t.dropped = 0;
     t.bytes = t.flops = 0;
   }

@@ -174,7 +174,47 @@ __device__ __forceinline__ void tile_of_block(int bid, int splits, int& tile, in
 // ---------------------------------------------------------------------------
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 GiB each)
-constexpr int kDepth = 4;                // 64-wide K steps fetched ahead
+#ifndef DTSK_SKINNY_DEPTH
+#define DTSK_SKINNY_DEPTH 4
+#endif
+#ifndef DTSK_LARGE_DEPTH
+#define DTSK_LARGE_DEPTH 4
+#endif
+#ifndef DTSK_LDS_SWIZZLE
+#define DTSK_LDS_SWIZZLE 1
+#endif
+#ifndef DTSK_KROT
+#define DTSK_KROT 1
+#endif
+
+// K-step order of a tile.  Weight rows are K*2 bytes apart (a power of two in
+// the 8B-class shapes); if every tile walked K from the same start, all of
+// them would address the same low address bits at the same time.  Starting
+// each tile at its own K step spreads the requests over the HBM channels.
+// The order is a fixed function of the tile, so results stay deterministic.
+__device__ __forceinline__ int k_rotation(int tile, int nk) {
+#if DTSK_KROT
+  return nk > 0 ? (int)(((unsigned)tile * 2654435761u) >> 16) % nk : 0;
+#else
+  return 0;
+#endif
+}
+constexpr int kDepth = DTSK_SKINNY_DEPTH;      // 64-wide K steps fetched ahead (even)
+constexpr int kDepthL = DTSK_LARGE_DEPTH;
+static_assert(kDepth % 2 == 0 && kDepthL % 2 == 0, "the LDS double buffer needs an even pipeline depth");
+
+// LDS layout of a 64-wide bf16 K step: row r, 16-byte chunk c.  With the XOR
+// swizzle a row is 128 bytes and chunk c lives in slot c ^ ((r >> 1) & 7):
+// 16 lanes reading one chunk of 16 consecutive rows, or 8 lanes writing the 8
+// chunks of a row, touch 16 (8) distinct 16-byte slots of the 256-byte bank
+// row.  Without it rows are padded to 144 bytes.
+#if DTSK_LDS_SWIZZLE
+constexpr int kRowElems = 64;
+__device__ __forceinline__ int lds_idx(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
+#else
+constexpr int kRowElems = 72;
+__device__ __forceinline__ int lds_idx(int r, int c) { return r * 72 + (c << 3); }
+#endif
 
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
@@ -192,7 +232,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
                                                      Epilogue epi) {
   constexpr int NB = BN / 64;               // 16-column blocks per wave
   constexpr int MP = MI * 16;               // padded rows
-  constexpr int AS = 64 + 8;                // LDS row stride (bf16)
+  constexpr int AS = kRowElems;             // LDS row stride (bf16)
   constexpr int A_ITEMS = MP * 8;           // 16-byte items per A step
   constexpr int AP = (A_ITEMS + 255) / 256; // A items per thread per step
   constexpr int TS = BN + 4;                // LDS row stride of the finished tile (fp32)
@@ -237,9 +277,11 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
 
   uint4 ring[kDepth][NB][2];
   uint4 aring[kDepth][AP];
+  const int rot = k_rotation(tile, nk);
   auto issue = [&](int step, uint4 (&w)[NB][2], uint4 (&a)[AP]) {
     const bool in = step < nk;
-    const uint32_t ks = (uint32_t)step * 128u;
+    const int sr = step + rot >= nk ? step + rot - nk : step + rot;
+    const uint32_t ks = (uint32_t)sr * 128u;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const uint32_t o = in ? woff[nb] + ks : kOob;
@@ -253,7 +295,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < AP; ++i) {
       const int c = t + i * 256;
-      if (A_ITEMS % 256 == 0 || c < A_ITEMS) *reinterpret_cast<uint4*>(&As[buf][(c >> 3) * AS + (c & 7) * 8]) = a[i];
+      if (A_ITEMS % 256 == 0 || c < A_ITEMS) *reinterpret_cast<uint4*>(&As[buf][lds_idx(c >> 3, c & 7)]) = a[i];
     }
   };
 
@@ -277,7 +319,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
       for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-          const uint4 av = *reinterpret_cast<const uint4*>(a + (i * 16 + l16) * AS + kc * 32 + g * 8);
+          const uint4 av = *reinterpret_cast<const uint4*>(a + lds_idx(i * 16 + l16, kc * 4 + g));
           const bf16x8 fa = __builtin_bit_cast(bf16x8, av);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
@@ -316,12 +358,25 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// register-tiled GEMM for few rows (M <= 16 * MI <= 128): the 4 waves of a
+// workgroup split the K steps of the tile (wave w takes steps w, w+4, ...);
+// each wave loads its A-row and weight fragments straight into registers
+// (B/A operand layouts of v_mfma_f32_16x16x32_bf16) with no LDS traffic and
+// no barrier in the main loop, every A fragment feeding NBW products and
+// every weight fragment MI.  The four partial tiles are summed through LDS
+// in wave order at the end.
+// ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
 // 128x128-tile MFMA GEMM for many rows: A and W tiles go through LDS (double
 // buffer), fetched kDepth - 1 steps ahead into register rings with buffer
 // loads (rows >= M and padding steps read as zeros)
 // ---------------------------------------------------------------------------
 constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kLds = kBK + 8;
+constexpr int kLds = kRowElems;
+// dynamic LDS of the large kernel: the A/W double buffers, or the finished
+// fp32 tile of the epilogue, whichever is larger
+constexpr int kLargeLds = 2 * (kBM + kBN) * kLds * 2 > kBM * (kBN + 4) * 4 ? 2 * (kBM + kBN) * kLds * 2
+                                                                            : kBM * (kBN + 4) * 4;
 
 __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ A, int M_max,
                                                    const int32_t* __restrict__ n_rows, int m_base, int K, WMap W,
@@ -337,7 +392,6 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
   tile_of_block(blockIdx.x, splits, tile, split);
   if (tile >= n_mt * n_nt) return;
   const int mt = tile % n_mt, nt = tile / n_mt;
-  static_assert(2 * (kBM + kBN) * kLds * 2 >= kBM * (kBN + 4) * 4, "epilogue tile must fit the LDS buffers");
   const int M = min(*n_rows - m_base, M_max);
   const int m0 = mt * kBM;
   if (m0 >= M) return;
@@ -345,7 +399,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
   const int nk_all = K / kBK;
   const int ks0 = split * nk_all / splits, ks1 = (split + 1) * nk_all / splits;
   const int nk = ks1 - ks0;
-  const int nk_pad = (nk + kDepth - 1) / kDepth * kDepth;
+  const int nk_pad = (nk + kDepthL - 1) / kDepthL * kDepthL;
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
@@ -365,10 +419,12 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
     wr[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(W.p[sg]), (short)0, W.seg_bytes, 0x00020000);
     woff[i] = (uint32_t)((r * K + ks0 * kBK + kc) * 2);
   }
-  uint4 ra[kDepth][CH], rw[kDepth][CH];
+  uint4 ra[kDepthL][CH], rw[kDepthL][CH];
+  const int rot = k_rotation(tile, nk);
   auto issue = [&](int step, uint4 (&a)[CH], uint4 (&w)[CH]) {
     const bool in = step < nk;
-    const uint32_t ks = (uint32_t)step * (kBK * 2);
+    const int sr = step + rot >= nk ? step + rot - nk : step + rot;
+    const uint32_t ks = (uint32_t)sr * (kBK * 2);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       a[i] = buf_load16(ar, in ? aoff[i] + ks : kOob);
@@ -379,8 +435,8 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int row = (t >> 3) + 32 * i, kc = (t & 7) * 8;
-      *reinterpret_cast<uint4*>(As + buf * kBM * kLds + row * kLds + kc) = a[i];
-      *reinterpret_cast<uint4*>(Ws + buf * kBN * kLds + row * kLds + kc) = w[i];
+      *reinterpret_cast<uint4*>(As + buf * kBM * kLds + lds_idx(row, kc >> 3)) = a[i];
+      *reinterpret_cast<uint4*>(Ws + buf * kBN * kLds + lds_idx(row, kc >> 3)) = w[i];
     }
   };
 
@@ -391,31 +447,31 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
     for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int s = 0; s < kDepth - 1; ++s) issue(s, ra[s], rw[s]);
+  for (int s = 0; s < kDepthL - 1; ++s) issue(s, ra[s], rw[s]);
   store(0, ra[0], rw[0]);
   lds_barrier();
-  for (int kt = 0; kt < nk_pad; kt += kDepth) {
+  for (int kt = 0; kt < nk_pad; kt += kDepthL) {
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
-      issue(kt + u + kDepth - 1, ra[(u + kDepth - 1) % kDepth], rw[(u + kDepth - 1) % kDepth]);
+    for (int u = 0; u < kDepthL; ++u) {
+      issue(kt + u + kDepthL - 1, ra[(u + kDepthL - 1) % kDepthL], rw[(u + kDepthL - 1) % kDepthL]);
       const uint16_t* a = As + (u & 1) * kBM * kLds;
       const uint16_t* w = Ws + (u & 1) * kBN * kLds;
 #pragma unroll
       for (int ks = 0; ks < kBK / 32; ++ks) {
-        const int koff = ks * 32 + (lane >> 4) * 8;
+        const int kch = ks * 4 + (lane >> 4);
         bf16x8 fa[MI], fb[NI];
 #pragma unroll
         for (int i = 0; i < MI; ++i)
-          fa[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(a + (wm0 + i * 16 + (lane & 15)) * kLds + koff));
+          fa[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(a + lds_idx(wm0 + i * 16 + (lane & 15), kch)));
 #pragma unroll
         for (int j = 0; j < NI; ++j)
-          fb[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(w + (wn0 + j * 16 + (lane & 15)) * kLds + koff));
+          fb[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(w + lds_idx(wn0 + j * 16 + (lane & 15), kch)));
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < NI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
-      store((u + 1) & 1, ra[(u + 1) % kDepth], rw[(u + 1) % kDepth]);
+      store((u + 1) & 1, ra[(u + 1) % kDepthL], rw[(u + 1) % kDepthL]);
       lds_barrier();
     }
   }
@@ -598,7 +654,7 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
     return launch_skinny_bn<128>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
   }
   if (plan.kind == GEMM_LARGE) {
-    const int lds_bytes = 2 * (kBM + kBN) * kLds * 2;
+    const int lds_bytes = kLargeLds;
     static bool attr_set = false;  // the tile needs more than the default 64 KiB of LDS
     if (!attr_set) {
       hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma, hipFuncAttributeMaxDynamicSharedMemorySize,

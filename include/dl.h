@@ -213,25 +213,35 @@ dl_status dl_denoise_step(const dl_model *model, dl_state *state, const dl_step_
 
 /* ---------------------------------------------------------------------------
  * Kernel timing (measurement support, not part of the method).  While a class
- * is enabled, every launch of that class is bracketed by two HIP events
- * recorded on the launch's own stream, and the launch's algorithmic bytes and
- * FLOPs are added up (for a product: weights + input rows + output rows in the
- * storage type, 2*M*N*K FLOPs; for attention: Q + K/V rows read + output,
- * 4*rows*keys*d FLOPs).  dl_timing_read synchronises on the recorded events
- * and returns the sums since dl_timing_reset.  Up to 8192 launches per class
- * are timed; later ones are counted in `dropped`.  Not thread-safe.
+ * is enabled with sampling stride n >= 1, about one launch in n of that class
+ * (chosen by a fixed hash of the launch's sequence number, so that launches of
+ * every shape are sampled) is bracketed by two HIP events recorded on the
+ * launch's own stream, and that launch's algorithmic bytes and FLOPs are
+ * added up (for a product: weights + input rows + output rows in the storage
+ * type, 2*M*N*K FLOPs; for attention: Q + K/V rows read + output,
+ * 4*rows*keys*d FLOPs).  n = 1 times every launch; n = 0 disables the class.
+ * dl_timing_read synchronises on the recorded events and returns the sums
+ * since dl_timing_reset.  Up to 65536 launches per class are timed; launches
+ * not timed (not sampled, or the event pool is full) are counted in
+ * `dropped`.  Not thread-safe.
  * ------------------------------------------------------------------------- */
-typedef enum { DL_KC_GEMM = 0, DL_KC_ATTN = 1, DL_KC_LMHEAD = 2, DL_KC_COUNT = 3 } dl_kernel_class;
+typedef enum {
+  DL_KC_GEMM = 0,        /* layer products on <= 128 rows (weight-streaming kernel) */
+  DL_KC_ATTN = 1,        /* attention */
+  DL_KC_LMHEAD = 2,      /* LM head product with its confidence statistics */
+  DL_KC_GEMM_TILED = 3,  /* layer products on more rows (tiled kernel) and the fp32 path */
+  DL_KC_COUNT = 4
+} dl_kernel_class;
 
 typedef struct {
   int64_t launches;     /* launches timed */
-  int64_t dropped;      /* launches not timed (event pool full) */
+  int64_t dropped;      /* launches of the class not timed (not sampled, or pool full) */
   double ms;            /* summed kernel time */
   double bytes;         /* summed algorithmic bytes */
   double flops;         /* summed algorithmic FLOPs */
 } dl_timing;
 
-dl_status dl_timing_enable(dl_kernel_class kc, int32_t enable);
+dl_status dl_timing_enable(dl_kernel_class kc, int32_t stride);
 dl_status dl_timing_reset(void);
 dl_status dl_timing_read(dl_kernel_class kc, dl_timing *out);
 
