@@ -93,10 +93,16 @@ struct Layout {
   size_t q, attn;           // T [R, d]
   size_t P;                 // fp32 GEMM partials
   size_t lm_part;           // float4 [min(R, kLmChunk)][ceil(V / 128)]
+  int R_part;               // rows of the attention key-chunk partials (0: none)
+  int attn_splits;          // key chunks the partials have room for
+  size_t attn_o;            // fp32 [attn_splits][R_part][d]
+  size_t attn_ml;           // float2 [attn_splits][R_part][n_heads]
   size_t scores;            // fp32 [B*S]
   size_t rope;              // float2 [S, head_dim/2]
   size_t total;
 };
+
+constexpr int kAttnPartRows = 1024;  // packed-row bound for split-key attention
 
 size_t gemm_partial_floats(const dl_dims& d, int R, int N, int K, int epi) {
   // worst case over every row bound the planner can see (1..R)
@@ -151,6 +157,10 @@ Layout make_layout(const dl_dims& d, int R) {
   pf = std::max(pf, gemm_partial_floats(d, std::min(L.R, kLmChunk), d.vocab, d.d, EPI_LM));
   L.P = take(sizeof(float) * pf);
   L.lm_part = take(16 * (size_t)std::min(L.R, kLmChunk) * cdiv(d.vocab, 128));
+  L.attn_splits = std::min(kAttnMaxSplits, std::max(1, S / 128));
+  L.R_part = (d.dtype == DL_BF16 && d.head_dim == 128 && L.attn_splits > 1) ? std::min(L.R, kAttnPartRows) : 0;
+  L.attn_o = take(sizeof(float) * (size_t)L.attn_splits * L.R_part * d.d);
+  L.attn_ml = take(sizeof(float) * 2 * (size_t)L.attn_splits * L.R_part * d.n_heads);
   L.scores = take(sizeof(float) * (size_t)B * S);
   L.rope = take(sizeof(float) * 2 * (size_t)S * (d.head_dim / 2));
   L.total = off;
@@ -315,8 +325,13 @@ dl_status attn_block(const Ctx& c, const dl_layer_w* w, float* x, const RowMap& 
     const double keys = (double)c.keys_total;
     DL_CHECK_HIP(timed(DL_KC_ATTN, c.st, es * ((double)rm.R_max * d.d * 2 + 2.0 * keys * d.d),
                        4.0 * (double)c.rows_x_keys * d.d,
-                       [&] { return launch_attention(d.dtype, q, kc, vc, seq_len, rm, d.S, d.n_heads, d.head_dim,
-                                                     attn, c.st); }));
+                       [&] {
+                         const int splits = std::min(
+                             c.L->attn_splits, attention_splits(d.dtype, d.head_dim, d.S, d.n_heads, rm, c.L->R_part));
+                         return launch_attention(d.dtype, q, kc, vc, seq_len, rm, d.S, d.n_heads, d.head_dim, splits,
+                                                 at<float>(c.ws, c.L->attn_o), at<float2>(c.ws, c.L->attn_ml),
+                                                 c.L->R_part, attn, c.st);
+                       }));
   }
   {
     const void* seg[4] = {w->wo, w->wo, w->wo, w->wo};
@@ -529,7 +544,7 @@ static dl_status prep_rows(const dl_dims* dims, const dl_selection* sel, int32_t
   if (k_total_max < 0 || k_total_max > dims->B * dims->S) return fail(DL_E_SHAPE, "k_total_max outside [0, B*S]");
   *L = make_layout(*dims, k_total_max);
   if (ws_bytes < L->total) return fail(DL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L->total);
-  *rm = rowmap_at(ws, L->map_sel, k_total_max, L->T);
+  *rm = rowmap_at(ws, L->map_sel, k_total_max, std::min(L->T, cdiv(k_total_max, kTileRows) + dims->B));
   DL_CHECK_HIP(launch_rowmap(sel->sel_idx, sel->sel_count, sel->row_off, dims->B, dims->S, *rm, st));
   return DL_OK;
 }
@@ -698,7 +713,7 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
     DL_CHECK_HIP(launch_select(scores, s->seq_len, d.B, d.S, p->mode, p->keep_ratio, p->threshold, s->sel.sel_idx,
                                s->sel.sel_count, st));
     DL_CHECK_HIP(launch_row_off(s->sel.sel_count, s->sel.row_off, d.B, st));
-    const RowMap rm_sel = rowmap_at(ws, L.map_sel, (int)R_sel, L.T);
+    const RowMap rm_sel = rowmap_at(ws, L.map_sel, (int)R_sel, std::min(L.T, cdiv(R_sel, kTileRows) + d.B));
     DL_CHECK_HIP(launch_rowmap(s->sel.sel_idx, s->sel.sel_count, s->sel.row_off, d.B, d.S, rm_sel, st));
     float* x_sel = at<float>(ws, L.x_sel);
     DL_CHECK_HIP(launch_gather(sizeof(float), x_all, all_off, d.S, d.d, rm_sel, x_sel, st));

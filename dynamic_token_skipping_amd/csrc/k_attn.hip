@@ -82,27 +82,43 @@ constexpr int kDh = 128;          // head_dim of the MFMA kernel
 constexpr int kTQ = 64;           // query rows per workgroup (16 per wave)
 constexpr int kTK = 64;           // keys per LDS tile
 constexpr int kKStride = kDh + 8; // LDS row stride of K (bf16 elements)
-constexpr int kVStride = kTK + 8; // LDS row stride of V^T
+constexpr int kVStride = kTK + 8; // LDS row stride of V^T (bf16 elements)
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)from_f32<bf16_t>(a).u | ((uint32_t)from_f32<bf16_t>(b).u << 16);
 }
 
+// V^T tile: row = dim (kVStride bf16), 32-bit word = a pair of keys.  Pair
+// kp of dim row `dim` lives in word slot kp ^ (((dim >> 3) & 7) << 2): the
+// stores of one instruction (4 key pairs x 16 dim chunks) then hit 32
+// distinct banks, and the readers' 8-byte pair loads stay contiguous because
+// the XOR leaves bit 0 of the slot alone.
+__device__ __forceinline__ int vt_word(int dim, int kp) { return dim * (kVStride / 2) + (kp ^ (((dim >> 3) & 7) << 2)); }
+
+// One workgroup = (64-query tile, head, key chunk [kbeg, kbeg + chunk)).
+// With one chunk the normalised output goes straight to `out`; with several,
+// the chunk's unnormalised O and its (running max, sum) go to o_part/ml_part
+// and k_attn_combine merges them.
 __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
                                                    const uint16_t* __restrict__ Vc,
                                                    const int32_t* __restrict__ seq_len,
                                                    const int32_t* __restrict__ row_seq,
                                                    const int32_t* __restrict__ tile_row0,
-                                                   const int32_t* __restrict__ tile_rows, int S, int d,
-                                                   float scale_log2, uint16_t* __restrict__ out) {
+                                                   const int32_t* __restrict__ tile_rows, int S, int d, int n_heads,
+                                                   float scale_log2, int chunk, uint16_t* __restrict__ out,
+                                                   float* __restrict__ o_part, float2* __restrict__ ml_part,
+                                                   int R_part) {
   __shared__ __align__(16) uint16_t Ks[kTK * kKStride];
-  __shared__ __align__(16) uint16_t Vt[kDh * kVStride];
-  const int tile = blockIdx.x, h = blockIdx.y;
+  __shared__ __align__(16) uint32_t Vt[kDh * kVStride / 2];
+  const int tile = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
   const int nrows = tile_rows[tile];
   if (nrows <= 0) return;
   const int r0 = tile_row0[tile];
   const int b = row_seq[r0];
   const int n = seq_len[b];
+  const int kbeg = split * chunk;
+  if (kbeg >= n) return;                           // the combine only reads chunks below n
+  const int kend = min(n, kbeg + chunk);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int ql = lane & 15, g = lane >> 4;
   const int qrow = wave * 16 + ql;                 // query row within the tile
@@ -125,35 +141,45 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 
   const uint16_t* Kb = Kc + (size_t)b * S * d + col0;
   const uint16_t* Vb = Vc + (size_t)b * S * d + col0;
-  for (int k0 = 0; k0 < n; k0 += kTK) {
-    lds_barrier();  // previous tile fully consumed
-    // K tile: 64 keys x 128 dims, 16 B per thread-chunk
+  // per thread and tile: 4 K chunks (key c >> 4, dims (c & 15) * 8) and 2 x 2 V
+  // chunks (keys 2kp, 2kp + 1 of key pair kp = c >> 4, dims (c & 15) * 8)
+  uint4 kr[4], va[2], vb[2];
+  auto fetch = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = t + i * 256;
-      const int key = c >> 4, dc = (c & 15) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (k0 + key < n) v = *reinterpret_cast<const uint4*>(Kb + (size_t)(k0 + key) * d + dc);
-      *reinterpret_cast<uint4*>(Ks + key * kKStride + dc) = v;
+      const int key = k0 + (c >> 4), dc = (c & 15) * 8;
+      kr[i] = key < kend ? *reinterpret_cast<const uint4*>(Kb + (size_t)key * d + dc) : make_uint4(0, 0, 0, 0);
     }
-    // V tile transposed: pairs of keys packed into 32-bit words of V^T[dim][key]
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int c = t + i * 256;                    // 512 items: 32 key pairs x 16 dim chunks
+      const int c = t + i * 256;
+      const int key = k0 + (c >> 4) * 2, dc = (c & 15) * 8;
+      va[i] = key < kend ? *reinterpret_cast<const uint4*>(Vb + (size_t)key * d + dc) : make_uint4(0, 0, 0, 0);
+      vb[i] = key + 1 < kend ? *reinterpret_cast<const uint4*>(Vb + (size_t)(key + 1) * d + dc)
+                             : make_uint4(0, 0, 0, 0);
+    }
+  };
+  fetch(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += kTK) {
+    lds_barrier();  // previous tile fully consumed
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = t + i * 256;
+      *reinterpret_cast<uint4*>(Ks + (c >> 4) * kKStride + (c & 15) * 8) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = t + i * 256;
       const int kp = c >> 4, dc = (c & 15) * 8;
-      const int key = kp * 2;
-      uint4 a = make_uint4(0, 0, 0, 0), bq = make_uint4(0, 0, 0, 0);
-      if (k0 + key < n) a = *reinterpret_cast<const uint4*>(Vb + (size_t)(k0 + key) * d + dc);
-      if (k0 + key + 1 < n) bq = *reinterpret_cast<const uint4*>(Vb + (size_t)(k0 + key + 1) * d + dc);
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {bq.x, bq.y, bq.z, bq.w};
+      const uint32_t aw[4] = {va[i].x, va[i].y, va[i].z, va[i].w}, bw[4] = {vb[i].x, vb[i].y, vb[i].z, vb[i].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (aw[e] & 0xffffu) | (bw[e] << 16);          // dim dc+2e:   keys key, key+1
-        const uint32_t hi = (aw[e] >> 16) | (bw[e] & 0xffff0000u);      // dim dc+2e+1: keys key, key+1
-        *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * e) * kVStride + key) = lo;
-        *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * e + 1) * kVStride + key) = hi;
+        Vt[vt_word(dc + 2 * e, kp)] = (aw[e] & 0xffffu) | (bw[e] << 16);          // dim dc+2e:   keys 2kp, 2kp+1
+        Vt[vt_word(dc + 2 * e + 1, kp)] = (aw[e] >> 16) | (bw[e] & 0xffff0000u);  // dim dc+2e+1
       }
     }
+    if (k0 + kTK < kend) fetch(k0 + kTK);          // next tile in flight during this one's math
     lds_barrier();
 
     // S^T blocks: keys kb*16 + g*4 + i (i < 4), query ql
@@ -175,7 +201,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
       for (int i = 0; i < 4; ++i) {
         const int key = k0 + kb * 16 + g * 4 + i;
         float v = st[kb][i] * scale_log2;
-        if (key >= n) v = -INFINITY;
+        if (key >= kend) v = -INFINITY;
         st[kb][i] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -207,9 +233,9 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
       const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk) {
-        const uint16_t* vr = Vt + (blk * 16 + ql) * kVStride + c * 32 + g * 4;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+        const int dim = blk * 16 + ql;
+        const uint2 lo = *reinterpret_cast<const uint2*>(&Vt[vt_word(dim, c * 16 + g * 2)]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&Vt[vt_word(dim, c * 16 + 8 + g * 2)]);
         const uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
         o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[blk], 0, 0, 0);
       }
@@ -219,14 +245,60 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (!qvalid) return;
-  const float inv = 1.f / l_run;
-  uint16_t* orow = out + (size_t)(r0 + qrow) * d + col0;
+  const int r = r0 + qrow;
+  if (gridDim.z == 1) {
+    const float inv = 1.f / l_run;
+    uint16_t* orow = out + (size_t)r * d + col0;
 #pragma unroll
-  for (int blk = 0; blk < 8; ++blk) {
-    uint2 w;
-    w.x = pack_bf16x2(o[blk][0] * inv, o[blk][1] * inv);
-    w.y = pack_bf16x2(o[blk][2] * inv, o[blk][3] * inv);
-    *reinterpret_cast<uint2*>(orow + blk * 16 + g * 4) = w;
+    for (int blk = 0; blk < 8; ++blk) {
+      uint2 w;
+      w.x = pack_bf16x2(o[blk][0] * inv, o[blk][1] * inv);
+      w.y = pack_bf16x2(o[blk][2] * inv, o[blk][3] * inv);
+      *reinterpret_cast<uint2*>(orow + blk * 16 + g * 4) = w;
+    }
+    return;
+  }
+  float* prow = o_part + ((size_t)split * R_part + r) * d + col0;
+#pragma unroll
+  for (int blk = 0; blk < 8; ++blk)
+    *reinterpret_cast<float4*>(prow + blk * 16 + g * 4) = make_float4(o[blk][0], o[blk][1], o[blk][2], o[blk][3]);
+  if (g == 0) ml_part[((size_t)split * R_part + r) * n_heads + h] = make_float2(m_run, l_run);
+}
+
+// Merge the key chunks of each (row, head): O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
+// One workgroup per packed row; thread t covers columns 4t + 1024j.
+__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ o_part,
+                                                      const float2* __restrict__ ml_part,
+                                                      const int32_t* __restrict__ n_rows,
+                                                      const int32_t* __restrict__ row_seq,
+                                                      const int32_t* __restrict__ seq_len, int d, int n_heads,
+                                                      int chunk, int splits, int R_part,
+                                                      uint16_t* __restrict__ out) {
+  const int r = blockIdx.x;
+  if (r >= *n_rows) return;
+  const int n = seq_len[row_seq[r]];
+  const int ns = min(splits, (n + chunk - 1) / chunk);
+  for (int col = threadIdx.x * 4; col < d; col += 1024) {
+    const int h = col / kDh;
+    float M = -INFINITY;
+    for (int c = 0; c < ns; ++c) M = fmaxf(M, ml_part[((size_t)c * R_part + r) * n_heads + h].x);
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < ns; ++c) {
+      const float2 ml = ml_part[((size_t)c * R_part + r) * n_heads + h];
+      const float w = exp2f(ml.x - M);
+      L += w * ml.y;
+      const float4 v = *reinterpret_cast<const float4*>(o_part + ((size_t)c * R_part + r) * d + col);
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+      acc.z += w * v.z;
+      acc.w += w * v.w;
+    }
+    const float inv = 1.f / L;
+    uint2 w2;
+    w2.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+    w2.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+    *reinterpret_cast<uint2*>(out + (size_t)r * d + col) = w2;
   }
 }
 
@@ -239,17 +311,31 @@ bool attention_supported(dl_dtype dt, int S, int head_dim) {
   return head_dim <= 128 && head_dim % 2 == 0 && S <= kMaxKeysSimt;
 }
 
+int attention_splits(dl_dtype dt, int head_dim, int S, int n_heads, const RowMap& rm, int R_part) {
+  if (!use_mfma_attention(dt, head_dim) || rm.R_max > R_part) return 1;
+  const int base = std::max(1, rm.T_max * n_heads);
+  int s = std::min(kAttnMaxSplits, std::max(1, kAttnTargetBlocks / base));
+  s = std::min(s, std::max(1, S / (2 * kTK)));     // at least two key tiles per chunk
+  return s;
+}
+
 hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* seq_len, const RowMap& rm, int S, int n_heads, int head_dim, void* out,
-                            hipStream_t st) {
+                            const int32_t* seq_len, const RowMap& rm, int S, int n_heads, int head_dim, int splits,
+                            float* o_part, float2* ml_part, int R_part, void* out, hipStream_t st) {
   const int d = n_heads * head_dim;
   const float scale = 1.f / sqrtf((float)head_dim);
   if (use_mfma_attention(dt, head_dim)) {
-    if (rm.tq != kTQ) return hipErrorInvalidValue;
+    if (rm.tq != kTQ || rm.T_max <= 0) return rm.T_max < 0 ? hipErrorInvalidValue : hipSuccess;
+    if (splits < 1 || splits > kAttnMaxSplits || (splits > 1 && (!o_part || !ml_part || rm.R_max > R_part)))
+      return hipErrorInvalidValue;
+    const int chunk = (S + splits * kTK - 1) / (splits * kTK) * kTK;
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(k_attn_mfma, dim3(rm.T_max, n_heads), dim3(256), 0, st, (const uint16_t*)q,
+    hipLaunchKernelGGL(k_attn_mfma, dim3(rm.T_max, n_heads, splits), dim3(256), 0, st, (const uint16_t*)q,
                        (const uint16_t*)k_cache, (const uint16_t*)v_cache, seq_len, rm.row_seq, rm.tile_row0,
-                       rm.tile_rows, S, d, scale_log2, (uint16_t*)out);
+                       rm.tile_rows, S, d, n_heads, scale_log2, chunk, (uint16_t*)out, o_part, ml_part, R_part);
+    if (splits > 1 && rm.R_max > 0)
+      hipLaunchKernelGGL(k_attn_combine, dim3(rm.R_max), dim3(256), 0, st, o_part, ml_part, rm.n_rows, rm.row_seq,
+                         seq_len, d, n_heads, chunk, splits, R_part, (uint16_t*)out);
     return hipGetLastError();
   }
   dim3 grid(rm.R_max, n_heads);

@@ -104,9 +104,16 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t st);
 
 // ---- attention ---------------------------------------------------------------------
 bool attention_supported(dl_dtype dt, int S, int head_dim);
+// Key chunks for the matrix-core kernel: enough workgroups to fill the chip,
+// at most kAttnMaxSplits, and only when every packed row fits the R_part rows
+// of the partial buffers.
+constexpr int kAttnMaxSplits = 8;
+constexpr int kAttnTargetBlocks = 2048;
+int attention_splits(dl_dtype dt, int head_dim, int S, int n_heads, const RowMap& rm, int R_part);
+// o_part [kAttnMaxSplits][R_part][d] fp32, ml_part [kAttnMaxSplits][R_part][n_heads]
 hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* seq_len, const RowMap& rm, int S, int n_heads, int head_dim, void* out,
-                            hipStream_t st);
+                            const int32_t* seq_len, const RowMap& rm, int S, int n_heads, int head_dim, int splits,
+                            float* o_part, float2* ml_part, int R_part, void* out, hipStream_t st);
 
 // ---- LM head reduction and unmasking -------------------------------------------------
 // Packed rows [m_base, m_base + M_max) of the row map; P is [splits][M_max][V].
