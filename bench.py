@@ -99,6 +99,26 @@ def cpu_baseline(wl, model_gpu, prompts, budget_s: float = 20.0):
             "seconds_measured": round(measured, 2)}
 
 
+def copy_probe(torch, n_bytes: int = 1 << 30, reps: int = 5):
+    """Device-to-device copy of n_bytes, reps times, timed with events: the
+    HBM bandwidth a plain streaming kernel reaches (read + write bytes / s).
+    Its dispatches also calibrate the FETCH_SIZE / WRITE_SIZE counters."""
+    src = torch.empty(n_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * n_bytes * reps / (a.elapsed_time(b) / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_per_copy": n_bytes, "GB/s": round(gbs, 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -121,6 +141,7 @@ def main():
     torch.cuda.synchronize()
     print(f"# setup {time.time() - t0:.1f} s: {dims.model_params() / 1e9:.2f} B params", file=sys.stderr, flush=True)
 
+    copy = copy_probe(torch)
     # warm-up (untimed), then restart the decode from its first step
     for t in range(args.warmup):
         dec.step(t % sched.steps)
@@ -182,6 +203,7 @@ def main():
             "lm_head": {"ms_timed": round(lmh["ms"], 3), "launches_timed": lmh["launches"],
                         "GB/s": round(lmh["bytes"] / max(lmh["ms"], 1e-9) / 1e6, 1)},
         },
+        "copy_probe": copy,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu:

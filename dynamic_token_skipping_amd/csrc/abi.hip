@@ -280,10 +280,12 @@ dl_status product(const Ctx& c, dl_kernel_class kc, const void* A, const RowMap&
   const GemmPlan p = plan_gemm(d.dtype, rows, N, K, e.kind, d.head_dim, d.d_ffn);
   if (splits_out) *splits_out = p.splits;
   if (kc == DL_KC_GEMM && p.kind != GEMM_SKINNY) kc = DL_KC_GEMM_TILED;
+  Epilogue ge = e;
+  if (p.sep_epi && e.kind != EPI_NONE) ge.kind = EPI_NONE;   // partials; the epilogue kernel finishes
   DL_CHECK_HIP(timed(kc, c.st, gemm_bytes(d, rows, N, K), 2.0 * rows * N * K, [&] {
-    return launch_gemm(d.dtype, p, A, rows, rm.n_rows, m_base, K, seg, n_seg, N, P, e, c.st);
+    return launch_gemm(d.dtype, p, A, rows, rm.n_rows, m_base, K, seg, n_seg, N, P, ge, c.st);
   }));
-  if (p.kind == GEMM_SIMT) {
+  if (p.sep_epi) {
     // Separate epilogue kernels (rows addressed through the full row map).
     switch (e.kind) {
       case EPI_QKV:

@@ -105,12 +105,19 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
                                                    const int32_t* __restrict__ row_seq,
                                                    const int32_t* __restrict__ tile_row0,
                                                    const int32_t* __restrict__ tile_rows, int S, int d, int n_heads,
-                                                   float scale_log2, int chunk, uint16_t* __restrict__ out,
-                                                   float* __restrict__ o_part, float2* __restrict__ ml_part,
-                                                   int R_part) {
+                                                   float scale_log2, int chunk, int n_split, int n_tiles,
+                                                   uint16_t* __restrict__ out, float* __restrict__ o_part,
+                                                   float2* __restrict__ ml_part, int R_part) {
   __shared__ __align__(16) uint16_t Ks[kTK * kKStride];
   __shared__ __align__(16) uint32_t Vt[kDh * kVStride / 2];
-  const int tile = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
+  // Block order: (head, chunk) pair p runs on XCD p % 8, and on that XCD the
+  // query tiles of one pair get consecutive block ids, so the tiles that read
+  // the same keys and values do so through one L2.
+  const int xcd = blockIdx.x & 7, rb = blockIdx.x >> 3;
+  const int pq = rb / n_tiles, tile = rb - pq * n_tiles;
+  const int pair = pq * 8 + xcd;
+  if (pair >= n_heads * n_split) return;
+  const int h = pair % n_heads, split = pair / n_heads;
   const int nrows = tile_rows[tile];
   if (nrows <= 0) return;
   const int r0 = tile_row0[tile];
@@ -246,7 +253,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   l_run += __shfl_xor(l_run, 32, 64);
   if (!qvalid) return;
   const int r = r0 + qrow;
-  if (gridDim.z == 1) {
+  if (n_split == 1) {
     const float inv = 1.f / l_run;
     uint16_t* orow = out + (size_t)r * d + col0;
 #pragma unroll
@@ -330,9 +337,10 @@ hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, con
       return hipErrorInvalidValue;
     const int chunk = (S + splits * kTK - 1) / (splits * kTK) * kTK;
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(k_attn_mfma, dim3(rm.T_max, n_heads, splits), dim3(256), 0, st, (const uint16_t*)q,
-                       (const uint16_t*)k_cache, (const uint16_t*)v_cache, seq_len, rm.row_seq, rm.tile_row0,
-                       rm.tile_rows, S, d, n_heads, scale_log2, chunk, (uint16_t*)out, o_part, ml_part, R_part);
+    const int grid = (n_heads * splits + 7) / 8 * 8 * rm.T_max;
+    hipLaunchKernelGGL(k_attn_mfma, dim3(grid), dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k_cache,
+                       (const uint16_t*)v_cache, seq_len, rm.row_seq, rm.tile_row0, rm.tile_rows, S, d, n_heads,
+                       scale_log2, chunk, splits, rm.T_max, (uint16_t*)out, o_part, ml_part, R_part);
     if (splits > 1 && rm.R_max > 0)
       hipLaunchKernelGGL(k_attn_combine, dim3(rm.R_max), dim3(256), 0, st, o_part, ml_part, rm.n_rows, rm.row_seq,
                          seq_len, d, n_heads, chunk, splits, R_part, (uint16_t*)out);

@@ -75,14 +75,13 @@ inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 // fused epilogues on a finished tile held in LDS: T[m][c], rows [0, M),
 // tile columns c whose output column is n0 + c in W-map order
 // ---------------------------------------------------------------------------
-template <int BN, int TS>
-__device__ __forceinline__ void tile_epilogue(const Epilogue& e, const float* __restrict__ T, const WMap& w, int n0,
-                                              int M) {
+template <int BN, int TS, int NT = 256, int MAXM = 128>
+__device__ __forceinline__ void tile_epilogue(const Epilogue& e, float* __restrict__ T, const WMap& w, int n0, int M) {
   const int t = threadIdx.x;
   if (e.kind == EPI_SWIGLU) {            // mode 1: gate in [0, BN/2), up in [BN/2, BN)
     constexpr int H = BN / 2;
     uint16_t* out = reinterpret_cast<uint16_t*>(e.act_out);
-    for (int idx = t; idx < M * H; idx += 256) {
+    for (int idx = t; idx < M * H; idx += NT) {
       const int m = idx / H, c = idx % H;
       const float gt = T[m * TS + c], up = T[m * TS + H + c];
       out[(size_t)m * e.F + (n0 / BN) * H + c] = from_f32<bf16_t>(gt / (1.f + expf(-gt)) * up).u;
@@ -91,20 +90,45 @@ __device__ __forceinline__ void tile_epilogue(const Epilogue& e, const float* __
     int sg, r0;
     wrow_index<BN>(w, n0, sg, r0);                  // segment of the tile: 0 q, 1 k, 2 v
     const int hd = e.head_dim, half = hd / 2;
+    // each row's cache position and sequence position, read once into the
+    // tile's padding columns, so that the loops below issue no dependent loads
+    int* Ti = reinterpret_cast<int*>(T);
+    for (int m = t; m < M; m += NT) {
+      const int p = e.row_pos[m];
+      Ti[m * TS + BN] = p;
+      Ti[m * TS + BN + 1] = p - e.row_seq[m] * e.S;
+    }
+    lds_barrier();
+    // Fast column map: a 64-wide rope-pair tile (mode 2) holds dims r0 + [0, 32)
+    // and r0 + 64 + [0, 32) of one head; a BN-wide segmented tile with
+    // head_dim == BN holds one whole head r0 + [0, BN).  Other shapes take the
+    // general map.
+    const bool fast = (w.mode == 2 && BN == 64 && hd == 128) || (w.mode == 0 && hd == BN);
     if (sg == 2) {
       uint16_t* vc = reinterpret_cast<uint16_t*>(e.v_cache);
-      for (int idx = t; idx < M * BN; idx += 256) {
+      for (int idx = t; idx < M * BN; idx += NT) {
         const int m = idx / BN, c = idx % BN;
-        int s2, r;
-        wrow_index<BN>(w, n0 + c, s2, r);
-        vc[(size_t)e.row_pos[m] * e.d + r] = from_f32<bf16_t>(T[m * TS + c]).u;
+        int r;
+        if (fast) {
+          r = w.mode == 2 ? r0 + ((c >> 5) << 6) + (c & 31) : r0 + c;
+        } else {
+          int s2;
+          wrow_index<BN>(w, n0 + c, s2, r);
+        }
+        vc[(size_t)Ti[m * TS + BN] * e.d + r] = from_f32<bf16_t>(T[m * TS + c]).u;
       }
     } else {
       uint16_t* dst = reinterpret_cast<uint16_t*>(sg == 0 ? e.q_out : e.k_cache);
-      for (int idx = t; idx < M * (BN / 2); idx += 256) {
-        const int m = idx / (BN / 2), pr = idx % (BN / 2);
-        // tile columns of the pair: mode 2 -> (pr, pr + BN/2); else inside each head of the tile
-        int c1, c2;
+      constexpr int kIt = (MAXM * (BN / 2) + NT - 1) / NT;   // pairs per thread
+      // pair pr: tile columns (c1, c2) and the weight row r1 of c1 (dim j = r1 % hd
+      // of its head; the partner dim is j + half)
+      auto pair_map = [&](int pr, int& c1, int& c2, int& r1) {
+        if (fast) {
+          c1 = pr;
+          c2 = pr + BN / 2;
+          r1 = r0 + pr;
+          return;
+        }
         if (w.mode == 2) {
           c1 = pr;
           c2 = pr + BN / 2;
@@ -112,24 +136,43 @@ __device__ __forceinline__ void tile_epilogue(const Epilogue& e, const float* __
           c1 = (pr / half) * hd + pr % half;
           c2 = c1 + half;
         }
-        int s2, r1;
-        wrow_index<BN>(w, n0 + c1, s2, r1);         // dim j (< half) of its head; the partner is j + half
-        const int j = r1 % hd;
-        const float a = T[m * TS + c1], b = T[m * TS + c2];
-        const int p = e.row_pos[m];
-        const int pos = p - e.row_seq[m] * e.S;
-        const float2 cs = e.rope[pos * half + j];
-        const float o1 = a * cs.x - b * cs.y, o2 = b * cs.x + a * cs.y;
-        const size_t rowoff = sg == 0 ? (size_t)m * e.d : (size_t)p * e.d;
-        dst[rowoff + r1] = from_f32<bf16_t>(o1).u;
-        dst[rowoff + r1 + half] = from_f32<bf16_t>(o2).u;
+        int s2;
+        wrow_index<BN>(w, n0 + c1, s2, r1);
+      };
+      const int j0 = fast ? r0 % hd : 0;
+      float2 cs[kIt];
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {            // every rotation factor first: independent loads
+        const int idx = t + it * NT;
+        cs[it] = make_float2(1.f, 0.f);
+        if (idx < M * (BN / 2)) {
+          const int m = idx / (BN / 2), pr = idx % (BN / 2);
+          int c1, c2, r1;
+          pair_map(pr, c1, c2, r1);
+          const int j = fast ? j0 + pr : r1 % hd;
+          cs[it] = e.rope[Ti[m * TS + BN + 1] * half + j];
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {
+        const int idx = t + it * NT;
+        if (idx < M * (BN / 2)) {
+          const int m = idx / (BN / 2), pr = idx % (BN / 2);
+          int c1, c2, r1;
+          pair_map(pr, c1, c2, r1);
+          const float a = T[m * TS + c1], b = T[m * TS + c2];
+          const float o1 = a * cs[it].x - b * cs[it].y, o2 = b * cs[it].x + a * cs[it].y;
+          const size_t rowoff = sg == 0 ? (size_t)m * e.d : (size_t)Ti[m * TS + BN] * e.d;
+          dst[rowoff + r1] = from_f32<bf16_t>(o1).u;
+          dst[rowoff + r1 + half] = from_f32<bf16_t>(o2).u;
+        }
       }
     }
   } else if (e.kind == EPI_LM) {
     // per row: (max, sum exp(l - max), lowest argmax) over this tile's columns
     const int lane = t & 63, wave = t >> 6;
     const int tile = n0 / BN;
-    for (int m = wave; m < M; m += 4) {
+    for (int m = wave; m < M; m += NT / 64) {
       float mx = -INFINITY, sm = 0.f;
       int am = 0x7fffffff;
       for (int c = lane; c < BN; c += 64) {
@@ -167,6 +210,19 @@ __device__ __forceinline__ void tile_of_block(int bid, int splits, int& tile, in
   const int xcd = bid & 7, r = bid >> 3;
   split = r % splits;
   tile = (r / splits) * 8 + xcd;
+}
+
+// Tiled kernel: column tile nt runs on XCD nt % 8, and on that XCD the row
+// tiles (and splits) of one column tile get consecutive block ids, so they
+// run together and read the column tile's weights through one L2 instead of
+// one per XCD.
+__device__ __forceinline__ void tile_of_block_mn(int bid, int n_mt, int splits, int& mt, int& nt, int& split) {
+  const int xcd = bid & 7, r = bid >> 3;
+  const int per_nt = n_mt * splits;
+  const int q = r / per_nt, rem = r - q * per_nt;
+  nt = q * 8 + xcd;
+  mt = rem / splits;
+  split = rem - mt * splits;
 }
 
 // ---------------------------------------------------------------------------
@@ -354,7 +410,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
 #pragma unroll
       for (int r = 0; r < 4; ++r) T[(i * 16 + g * 4 + r) * TS + wave * (BN / 4) + nb * 16 + l16] = acc[i][nb][r];
   lds_barrier();
-  tile_epilogue<BN, TS>(epi, T, W, n0, M);
+  tile_epilogue<BN, TS, 256, MP>(epi, T, W, n0, M);
 }
 
 // ---------------------------------------------------------------------------
@@ -388,10 +444,9 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
   uint16_t* As = lds;                          // [2][kBM][kLds]
   uint16_t* Ws = lds + 2 * kBM * kLds;         // [2][kBN][kLds]
 
-  int tile, split;
-  tile_of_block(blockIdx.x, splits, tile, split);
-  if (tile >= n_mt * n_nt) return;
-  const int mt = tile % n_mt, nt = tile / n_mt;
+  int mt, nt, split;
+  tile_of_block_mn(blockIdx.x, n_mt, splits, mt, nt, split);
+  if (nt >= n_nt) return;
   const int M = min(*n_rows - m_base, M_max);
   const int m0 = mt * kBM;
   if (m0 >= M) return;
@@ -420,7 +475,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
     woff[i] = (uint32_t)((r * K + ks0 * kBK + kc) * 2);
   }
   uint4 ra[kDepthL][CH], rw[kDepthL][CH];
-  const int rot = k_rotation(tile, nk);
+  const int rot = k_rotation(nt, nk);   // the row tiles of a column tile walk K together
   auto issue = [&](int step, uint4 (&a)[CH], uint4 (&w)[CH]) {
     const bool in = step < nk;
     const int sr = step + rot >= nk ? step + rot - nk : step + rot;
@@ -508,7 +563,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
   if (e.row_pos) e.row_pos += m0;
   if (e.row_seq) e.row_seq += m0;
   if (e.kind == EPI_LM) e.lm_part += (size_t)m0 * e.lm_tiles * 4;
-  tile_epilogue<kBN, TS>(e, T, W, n0, Mt);
+  tile_epilogue<kBN, TS, 256, kBM>(e, T, W, n0, Mt);
 }
 
 // ---------------------------------------------------------------------------
@@ -588,13 +643,14 @@ hipError_t launch_skinny_bn(const GemmPlan& plan, const void* A, int M_max, cons
 }  // namespace
 
 GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim, int F) {
-  const GemmPlan simt{GEMM_SIMT, 1, 128, 8, 0};
+  const GemmPlan simt{GEMM_SIMT, 1, 128, 8, 0, 1};
   GemmPlan p = simt;
   if (dt != DL_BF16 || K % 64 != 0 || M <= 0) return p;
   const int nk = K / 64;
   const int n_seg = epi_kind == EPI_QKV ? N / 3 : epi_kind == EPI_SWIGLU ? N / 2 : N;
   if (M <= 128 && (long long)n_seg * K * 2 < 0x7fff0000LL && 128LL * K * 2 < 0x7fff0000LL) {
     p.kind = GEMM_SKINNY;
+    p.sep_epi = 0;
     p.mi = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
     switch (epi_kind) {
       case EPI_QKV:
@@ -629,6 +685,7 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
   if (epi_kind == EPI_SWIGLU && F % (kBN / 2) != 0) return p;
   if (epi_kind == EPI_QKV && !(head_dim % 2 == 0 && 128 % head_dim == 0 && (N / 3) % kBN == 0)) return p;
   p.kind = GEMM_LARGE;
+  p.sep_epi = 0;
   p.bn = kBN;
   p.wmode = epi_kind == EPI_SWIGLU ? 1 : 0;
   if (epi_kind == EPI_NONE) {
@@ -663,7 +720,7 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
       attr_set = true;
     }
     const int n_mt = cdiv(M_max, kBM), n_nt = N / kBN;
-    const int grid = cdiv(n_mt * n_nt, 8) * 8 * plan.splits;
+    const int grid = cdiv(n_nt, 8) * 8 * n_mt * plan.splits;
     hipLaunchKernelGGL(k_gemm_mfma, dim3(grid), dim3(256), lds_bytes, st, (const uint16_t*)A, M_max, n_rows, m_base,
                        K, w, N, plan.splits, n_mt, n_nt, P, epi);
     return hipGetLastError();

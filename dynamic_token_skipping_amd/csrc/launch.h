@@ -83,6 +83,7 @@ struct GemmPlan {
   int bn;      // column tile
   int mi;      // skinny: 16-row blocks of A
   int wmode;   // weight-row order: 0 segmented, 1 gate|up interleaved, 2 RoPE pairs
+  int sep_epi; // 1: the product writes fp32 partials and the separate epilogue kernels finish
 };
 // The epilogue kind decides the tile the fused epilogue needs; a GEMM_SIMT
 // plan leaves the epilogue to the separate kernels below.
