@@ -700,7 +700,8 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
     DL_TRY(run_layers(c, model, 0, sl, x_all, rm_all, s->seq_len, kcache, vcache, false,
                       sl < d.n_layers ? model->layers[sl].attn_norm : model->final_norm));
     DL_CHECK_HIP(launch_store_rows(d.dtype, x_all, d.d, rm_all, s->h_prev, st));
-    DL_TRY(run_layers(c, model, sl, d.n_layers, x_all, rm_all, s->seq_len, kcache, vcache, true, model->final_norm));
+    DL_TRY(run_layers(c, model, sl, d.n_layers, x_all, rm_all, s->seq_len, kcache, vcache, sl > 0,
+                      model->final_norm));
     DL_CHECK_HIP(hipMemcpyAsync(s->sel.sel_idx, all_idx, sizeof(int32_t) * (size_t)d.B * d.S,
                                 hipMemcpyDeviceToDevice, st));
     DL_CHECK_HIP(hipMemcpyAsync(s->sel.sel_count, all_cnt, sizeof(int32_t) * d.B, hipMemcpyDeviceToDevice, st));

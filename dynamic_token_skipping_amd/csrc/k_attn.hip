@@ -273,40 +273,50 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 }
 
 // Merge the key chunks of each (row, head): O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
-// One workgroup per packed row; thread t covers columns 4t + 1024j.
-__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ o_part,
-                                                      const float2* __restrict__ ml_part,
-                                                      const int32_t* __restrict__ n_rows,
-                                                      const int32_t* __restrict__ row_seq,
-                                                      const int32_t* __restrict__ seq_len, int d, int n_heads,
-                                                      int chunk, int splits, int R_part,
-                                                      uint16_t* __restrict__ out) {
+// Grid (packed row, 256-column group); thread t covers 4 columns.
+__global__ __launch_bounds__(64) void k_attn_combine(const float* __restrict__ o_part,
+                                                     const float2* __restrict__ ml_part,
+                                                     const int32_t* __restrict__ n_rows,
+                                                     const int32_t* __restrict__ row_seq,
+                                                     const int32_t* __restrict__ seq_len, int d, int n_heads,
+                                                     int chunk, int splits, int R_part, uint16_t* __restrict__ out) {
   const int r = blockIdx.x;
-  if (r >= *n_rows) return;
+  const int col = blockIdx.y * 256 + threadIdx.x * 4;
+  if (r >= *n_rows || col >= d) return;
   const int n = seq_len[row_seq[r]];
   const int ns = min(splits, (n + chunk - 1) / chunk);
-  for (int col = threadIdx.x * 4; col < d; col += 1024) {
-    const int h = col / kDh;
-    float M = -INFINITY;
-    for (int c = 0; c < ns; ++c) M = fmaxf(M, ml_part[((size_t)c * R_part + r) * n_heads + h].x);
-    float L = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int c = 0; c < ns; ++c) {
-      const float2 ml = ml_part[((size_t)c * R_part + r) * n_heads + h];
-      const float w = exp2f(ml.x - M);
-      L += w * ml.y;
-      const float4 v = *reinterpret_cast<const float4*>(o_part + ((size_t)c * R_part + r) * d + col);
-      acc.x += w * v.x;
-      acc.y += w * v.y;
-      acc.z += w * v.z;
-      acc.w += w * v.w;
+  const int h = col / kDh;
+  float2 ml[kAttnMaxSplits];
+  float4 v[kAttnMaxSplits];
+#pragma unroll
+  for (int c = 0; c < kAttnMaxSplits; ++c) {      // all loads first
+    if (c < ns) {
+      ml[c] = ml_part[((size_t)c * R_part + r) * n_heads + h];
+      v[c] = *reinterpret_cast<const float4*>(o_part + ((size_t)c * R_part + r) * d + col);
     }
-    const float inv = 1.f / L;
-    uint2 w2;
-    w2.x = pack_bf16x2(acc.x * inv, acc.y * inv);
-    w2.y = pack_bf16x2(acc.z * inv, acc.w * inv);
-    *reinterpret_cast<uint2*>(out + (size_t)r * d + col) = w2;
   }
+  float M = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < kAttnMaxSplits; ++c)
+    if (c < ns) M = fmaxf(M, ml[c].x);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int c = 0; c < kAttnMaxSplits; ++c) {
+    if (c < ns) {
+      const float w = exp2f(ml[c].x - M);
+      L += w * ml[c].y;
+      acc.x += w * v[c].x;
+      acc.y += w * v[c].y;
+      acc.z += w * v[c].z;
+      acc.w += w * v[c].w;
+    }
+  }
+  const float inv = 1.f / L;
+  uint2 w2;
+  w2.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+  w2.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2*>(out + (size_t)r * d + col) = w2;
 }
 
 }  // namespace
@@ -342,8 +352,8 @@ hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, con
                        (const uint16_t*)v_cache, seq_len, rm.row_seq, rm.tile_row0, rm.tile_rows, S, d, n_heads,
                        scale_log2, chunk, splits, rm.T_max, (uint16_t*)out, o_part, ml_part, R_part);
     if (splits > 1 && rm.R_max > 0)
-      hipLaunchKernelGGL(k_attn_combine, dim3(rm.R_max), dim3(256), 0, st, o_part, ml_part, rm.n_rows, rm.row_seq,
-                         seq_len, d, n_heads, chunk, splits, R_part, (uint16_t*)out);
+      hipLaunchKernelGGL(k_attn_combine, dim3(rm.R_max, (d + 255) / 256), dim3(64), 0, st, o_part, ml_part,
+                         rm.n_rows, rm.row_seq, seq_len, d, n_heads, chunk, splits, R_part, (uint16_t*)out);
     return hipGetLastError();
   }
   dim3 grid(rm.R_max, n_heads);

@@ -154,6 +154,83 @@ __global__ __launch_bounds__(256) void k_score(const T* __restrict__ h_cur, cons
   }
 }
 
+// bf16 storage, fused update, d a multiple of 512: one wave per row, each lane
+// owns 8 consecutive columns per 512-column slice.  The slices are taken four
+// at a time: every load of a group is issued before any of the group's H_prev
+// stores, so a row costs about two memory round trips instead of one per
+// column.  Same sums as k_score in a different summation order.
+__global__ __launch_bounds__(256) void k_score_bf16x8(const float* __restrict__ x_packed,
+                                                      const int32_t* __restrict__ off_all, bf16_t* __restrict__ h_prev,
+                                                      const float* __restrict__ conf,
+                                                      const int32_t* __restrict__ seq_len, int S, int d, int kind,
+                                                      float alpha, float* __restrict__ scores) {
+  constexpr int G = 4;                                // slices per load group
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (i >= seq_len[b]) return;
+  const size_t row = (size_t)b * S + i;
+  uint16_t* hp = reinterpret_cast<uint16_t*>(h_prev) + row * d;
+  const float* xr = x_packed + (size_t)(off_all[b] + i) * d;
+  float l1 = 0.f, dd = 0.f, hh = 0.f, xx = 0.f, xh = 0.f;
+  const int n_slices = d / 512;
+  for (int s0 = 0; s0 < n_slices; s0 += G) {
+    float4 xa[G], xb[G];
+    uint4 hv[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      if (s0 + gi < n_slices) {
+        const int c = (s0 + gi) * 512 + lane * 8;
+        xa[gi] = *reinterpret_cast<const float4*>(xr + c);
+        xb[gi] = *reinterpret_cast<const float4*>(xr + c + 4);
+        hv[gi] = *reinterpret_cast<const uint4*>(hp + c);
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      if (s0 + gi < n_slices) {
+        const float xs[8] = {xa[gi].x, xa[gi].y, xa[gi].z, xa[gi].w, xb[gi].x, xb[gi].y, xb[gi].z, xb[gi].w};
+        const uint32_t hw[4] = {hv[gi].x, hv[gi].y, hv[gi].z, hv[gi].w};
+        uint32_t ow[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16_t x0 = from_f32<bf16_t>(xs[2 * e]), x1 = from_f32<bf16_t>(xs[2 * e + 1]);
+          const float xf[2] = {to_f32(x0), to_f32(x1)};
+          const float hf[2] = {__uint_as_float(hw[e] << 16), __uint_as_float(hw[e] & 0xffff0000u)};
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const float df = xf[q] - hf[q];
+            l1 += fabsf(df);
+            dd += df * df;
+            hh += hf[q] * hf[q];
+            xx += xf[q] * xf[q];
+            xh += xf[q] * hf[q];
+          }
+          ow[e] = (uint32_t)x0.u | ((uint32_t)x1.u << 16);
+        }
+        *reinterpret_cast<uint4*>(hp + (s0 + gi) * 512 + lane * 8) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      }
+    }
+  }
+  l1 = warp_sum(l1);
+  dd = warp_sum(dd);
+  hh = warp_sum(hh);
+  xx = warp_sum(xx);
+  xh = warp_sum(xh);
+  if (lane == 0) {
+    const float c = conf[row];
+    float s;
+    if (kind == DL_SCORE_ESDLLM) {
+      s = alpha * c + (1.f - alpha) * (l1 / fmaxf(sqrtf((float)d) * sqrtf(hh), FLT_MIN));
+    } else if (kind == DL_SCORE_RELL2_INVCONF) {
+      s = sqrtf(dd) / fmaxf(sqrtf(hh), FLT_MIN) + (1.f - c);
+    } else {
+      s = 1.f - xh / fmaxf(sqrtf(xx) * sqrtf(hh), FLT_MIN);
+    }
+    scores[row] = s;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // top-k / threshold selection: one 1024-thread block per sequence
 // ---------------------------------------------------------------------------
@@ -234,14 +311,33 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
         if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
       }
       __syncthreads();
-      if (t == 0) {
-        int need = s_need, digit = 255;
-        for (; digit > 0; --digit) {
-          if (hist[digit] >= need) break;
-          need -= hist[digit];
+      if (t < 64) {
+        // wave 0 finds the digit holding the need-th largest key: lane l owns
+        // digits 4l..4l+3; a suffix scan gives the count of keys above them
+        const int need = s_need;
+        const int h0 = hist[4 * t], h1 = hist[4 * t + 1], h2 = hist[4 * t + 2], h3 = hist[4 * t + 3];
+        const int own = h0 + h1 + h2 + h3;
+        int incl = own;                     // keys in lanes >= t
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int u = __shfl_down(incl, o, 64);
+          if (t + o < 64) incl += u;
         }
-        s_prefix = prefix | ((uint32_t)digit << shift);
-        s_need = need;
+        int above = incl - own;             // keys with a digit above 4t + 3
+        const int hs[4] = {h3, h2, h1, h0};
+        int found = -1, rest = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {       // digits 4t+3 down to 4t
+          if (found < 0 && above < need && need <= above + hs[q]) {
+            found = 4 * t + 3 - q;
+            rest = need - above;
+          }
+          above += hs[q];
+        }
+        if (found >= 0) {                   // exactly one lane and digit qualify
+          s_prefix = prefix | ((uint32_t)found << shift);
+          s_need = rest;
+        }
       }
       __syncthreads();
     }
@@ -374,21 +470,6 @@ __global__ __launch_bounds__(kRowThreads) void k_copy_sel(const char* __restrict
 // ---------------------------------------------------------------------------
 // RMSNorm: out = T(x / sqrt(mean(x^2) + eps) * g)
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(kRowThreads) void k_rmsnorm(const float* __restrict__ x, const T* __restrict__ g,
-                                                         const int32_t* __restrict__ n_rows, int d, float eps,
-                                                         T* __restrict__ out) {
-  __shared__ float red[16];
-  const int r = blockIdx.x;
-  if (r >= *n_rows) return;
-  const float* xr = x + (size_t)r * d;
-  float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) ss += xr[c] * xr[c];
-  ss = block_sum(ss, red);
-  const float inv = 1.f / sqrtf(ss / (float)d + eps);
-  T* o = out + (size_t)r * d;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) o[c] = from_f32<T>(xr[c] * inv * to_f32(g[c]));
-}
 
 // Split sum + residual + (optional) RMSNorm of the next sub-block, one block
 // per packed row: x += sum_s P[s]; out = T(x / sqrt(mean(x^2) + eps) * g).
@@ -423,7 +504,7 @@ __global__ __launch_bounds__(kRowThreads) void k_reduce_rows(const float* __rest
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    xr[threadIdx.x + c * kRowThreads] = v[c];
+    if (splits > 0) xr[threadIdx.x + c * kRowThreads] = v[c];
     ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
   }
   if (!g) return;
@@ -454,10 +535,13 @@ __global__ __launch_bounds__(kRowThreads) void k_reduce_rows_any(const float* __
   const float* pr = P + (size_t)r * d;
   float ss = 0.f;
   for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < splits; ++s) acc += pr[s * sstride + c];
-    const float v = xr[c] + acc;
-    xr[c] = v;
+    float v = xr[c];
+    if (splits > 0) {
+      float acc = 0.f;
+      for (int s = 0; s < splits; ++s) acc += pr[s * sstride + c];
+      v += acc;
+      xr[c] = v;
+    }
     ss += v * v;
   }
   if (!g) return;
@@ -775,7 +859,10 @@ hipError_t launch_score(dl_dtype dt, const void* h_cur, const float* x_packed, c
       hipLaunchKernelGGL((k_score<float, false>), grid, dim3(256), 0, st, (const float*)h_cur, x_packed, off_all,
                          (float*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
   } else {
-    if (x_packed)
+    if (x_packed && d % 512 == 0)
+      hipLaunchKernelGGL(k_score_bf16x8, grid, dim3(256), 0, st, x_packed, off_all, (bf16_t*)h_prev, conf, seq_len,
+                         S, d, (int)kind, alpha, scores);
+    else if (x_packed)
       hipLaunchKernelGGL((k_score<bf16_t, true>), grid, dim3(256), 0, st, (const bf16_t*)h_cur, x_packed, off_all,
                          (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
     else
@@ -837,13 +924,9 @@ hipError_t launch_store_rows(dl_dtype dt, const float* x, int w, const RowMap& r
 
 hipError_t launch_rmsnorm(dl_dtype dt, const float* x, const void* g, const RowMap& rm, int d, float eps, void* out,
                           hipStream_t st) {
-  if (dt == DL_F32)
-    hipLaunchKernelGGL(k_rmsnorm<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, (const float*)g, rm.n_rows, d,
-                       eps, (float*)out);
-  else
-    hipLaunchKernelGGL(k_rmsnorm<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, (const bf16_t*)g, rm.n_rows,
-                       d, eps, (bf16_t*)out);
-  return hipGetLastError();
+  // the kernels of the split-sum reduction with no splits: the normalised rows
+  // come out bit-identical to the ones the reduction after a sub-block writes
+  return launch_reduce_rows(dt, nullptr, 0, rm, d, const_cast<float*>(x), g, eps, out, st);
 }
 
 hipError_t launch_rope_table(int S, int head_dim, float base, float2* table, hipStream_t st) {

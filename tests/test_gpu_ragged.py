@@ -13,24 +13,31 @@ from oracle import esdllm as E
 pytestmark = pytest.mark.gpu
 
 DIMS = workloads.ModelDims(d=256, n_heads=2, head_dim=128, d_ffn=512, vocab=1024, n_layers=3)
+# d a multiple of 512 takes the vectorised fused scoring kernel
+DIMS512 = workloads.ModelDims(d=512, n_heads=4, head_dim=128, d_ffn=1024, vocab=1024, n_layers=3)
 SCHED = workloads.Schedule(gen_len=32, block_len=16, steps=8, skip_layer=1, keep=0.25, score="esdllm")
 PROMPTS = (9, 45, 96)
 
 
-def _setup(dtype, sched=SCHED, seed=21):
+def _setup(dtype, sched=SCHED, seed=21, dims=DIMS):
     from dynamic_token_skipping_amd import Decoder, DeviceModel
-    m_cpu = workloads.make_model(DIMS, seed, dtype, "cpu")
+    m_cpu = workloads.make_model(dims, seed, dtype, "cpu")
     g = torch.Generator().manual_seed(seed)
-    prompts = [torch.randint(0, DIMS.vocab, (n,), generator=g) for n in PROMPTS]
-    dec = Decoder(DeviceModel(to_device(m_cpu), DIMS.n_heads, DIMS.head_dim, dtype), prompts, sched,
+    prompts = [torch.randint(0, dims.vocab, (n,), generator=g) for n in PROMPTS]
+    dec = Decoder(DeviceModel(to_device(m_cpu), dims.n_heads, dims.head_dim, dtype), prompts, sched,
                   keep_logits=True)
-    sts = [E.init_state(p.numpy(), sched.gen_len, DIMS, keep_logits=True) for p in prompts]
+    sts = [E.init_state(p.numpy(), sched.gen_len, dims, keep_logits=True) for p in prompts]
     return np_model(m_cpu), dec, sts
 
 
-@pytest.mark.parametrize("dtype,tol", [("f32", 1e-5), ("bf16", 2e-2)])
-def test_ragged_batch_decode(dtype, tol):
-    m_np, dec, sts = _setup(dtype)
+SCHED_SL = dataclasses.replace(SCHED, skip_layer=3)       # skip after the last layer: only the LM head partial
+
+
+@pytest.mark.parametrize("dtype,tol,dims,sched", [("f32", 1e-5, DIMS, SCHED), ("bf16", 2e-2, DIMS, SCHED),
+                                                  ("bf16", 2e-2, DIMS512, SCHED), ("f32", 1e-5, DIMS, SCHED_SL)])
+def test_ragged_batch_decode(dtype, tol, dims, sched):
+    DIMS, SCHED = dims, sched
+    m_np, dec, sts = _setup(dtype, sched=sched, dims=dims)
     compared = 0
     for t in range(SCHED.steps):
         if dtype == "bf16":          # every bf16 step starts from the oracle's state
@@ -47,13 +54,15 @@ def test_ragged_batch_decode(dtype, tol):
         for b, (st, info) in enumerate(zip(sts, infos)):
             n = len(st.tokens)
             g_unm = np.nonzero(before[b] & ~dec.masked[b, :n].cpu().numpy().astype(bool))[0]
-            if dtype == "f32":
-                assert g_unm.tolist() == info.unmasked.tolist(), (t, b)
-            else:
-                assert unmask_diff_ok(g_unm, info.unmasked, st.conf)[0], (t, b)
             rows = info.selected
             nd = 0
             if not info.refresh:
+                # scores of every valid row; in bf16 the GPU's X_s carries the
+                # storage rounding of its activations, which eq. I's L1 term sees
+                # as a change of up to ~1e-2 relative per element
+                s_g = host(dec.scores[b, :n])
+                s_tol = 1e-5 if dtype == "f32" else 1e-2
+                assert np.abs(s_g - info.scores).max() <= s_tol * max(1.0, np.abs(info.scores).max()), (t, b)
                 k = E.keep_count(SCHED.keep, n)
                 ok, nd = selection_diff_ok(g_rows[b], rows, info.scores, k, 1e-4, 0.0 if dtype == "f32" else 2e-2)
                 assert ok, (t, b)
@@ -63,6 +72,17 @@ def test_ragged_batch_decode(dtype, tol):
                     rows = np.array(sorted(set(g_rows[b]) & set(rows.tolist())), dtype=np.int64)
             if not nd:
                 assert g_rows[b] == rows.tolist()
+            # unmasking: exact in fp32; in bf16 within the confidence band, unless
+            # the selections differed (inside the score band), which changes which
+            # rows carry a fresh confidence
+            if dtype == "f32":
+                assert g_unm.tolist() == info.unmasked.tolist(), (t, b)
+            elif not nd:
+                diff = sorted(set(g_unm.tolist()) ^ set(info.unmasked.tolist()))
+                assert unmask_diff_ok(g_unm, info.unmasked, st.conf)[0], (
+                    t, b, diff, [float(st.conf[i]) for i in diff], host(dec.conf[b, diff]).tolist(),
+                    min(float(st.conf[i]) for i in info.unmasked))
+            assert len(g_unm) == len(info.unmasked), (t, b)
             assert row_rel_err(host(dec.h_final[b, :n])[rows], st.h_final[rows]) <= tol
             assert row_rel_err(host(dec.logits[b, :n])[rows], st.logits[rows]) <= tol
             assert row_rel_err(host(dec.h_prev[b, :n]), st.h_prev) <= tol
