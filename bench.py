@@ -99,6 +99,23 @@ def cpu_baseline(wl, model_gpu, prompts, budget_s: float = 20.0):
             "seconds_measured": round(measured, 2)}
 
 
+def recorded_traffic():
+    """HBM bytes per dispatch of the dominant kernel, from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs recorded under profiles/ (scaled by the copy
+    calibration).  None when the kernel's source changed after the counters
+    were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "k_gemm_skinny_full8b_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            sha = hashlib.sha1(f.read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["hbm_bytes_per_dispatch"] if sha == rec["source_sha1"] else None
+
+
 def copy_probe(torch, n_bytes: int = 1 << 30, reps: int = 5):
     """Device-to-device copy of n_bytes, reps times, timed with events: the
     HBM bandwidth a plain streaming kernel reaches (read + write bytes / s).
@@ -176,8 +193,8 @@ def main():
     gt = dl_timing_read(DL_KC_GEMM_TILED)
     gemm_gbs = g["bytes"] / (g["ms"] / 1e3) / 1e9 if g["ms"] > 0 else 0.0
     roofline = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": "k_gemm_skinny (layer products on the kept rows: QKV, O, gate/up, down)",
+                "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": recorded_traffic(),
+                "kernel": "k_gemm_skinny<8, 64> (layer products on the 128 kept rows: QKV, O, gate/up, down)",
                 "launches_timed": g["launches"], "launches_total": g["launches"] + g["dropped"],
                 "avg_launch_us": round(g["ms"] * 1e3 / max(g["launches"], 1), 2),
                 "alg_bytes_per_launch": round(g["bytes"] / max(g["launches"], 1))}
