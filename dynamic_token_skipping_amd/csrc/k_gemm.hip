@@ -13,7 +13,8 @@
 //    from HBM straight into a ring of registers kDepth 64-wide K steps ahead
 //    (v_mfma_f32_16x16x32_bf16 B operand layout), while the A rows of each K
 //    step are staged once per workgroup in LDS (double buffer).
-//  * k_gemm_mfma (bf16, larger M): 128x128 tiles, A and W through LDS.
+//  * k_gemm_mfma<BN> (bf16): 128 x BN tiles, A and W through LDS; BN = 128
+//    for many rows, BN = 64 for up to 128 rows (twice the column tiles).
 //  * k_gemm_simt: fp32 FMA fallback (fp32 storage, odd shapes); its results
 //    go through the separate epilogue kernels of k_rows.
 //
@@ -239,6 +240,12 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #ifndef DTSK_LDS_SWIZZLE
 #define DTSK_LDS_SWIZZLE 1
 #endif
+#ifndef DTSK_TILED_SMALL
+#define DTSK_TILED_SMALL 1
+#endif
+#ifndef DTSK_T128_MIN_TILES
+#define DTSK_T128_MIN_TILES 160
+#endif
 #ifndef DTSK_KROT
 #define DTSK_KROT 1
 #endif
@@ -423,26 +430,32 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
 // in wave order at the end.
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
-// 128x128-tile MFMA GEMM for many rows: A and W tiles go through LDS (double
-// buffer), fetched kDepth - 1 steps ahead into register rings with buffer
-// loads (rows >= M and padding steps read as zeros)
+// Tiled MFMA GEMM: 128-row x BN-column tiles (BN 128, or 64 when there are
+// few rows and the grid needs more tiles); A and W tiles go through LDS
+// (double buffer), fetched kDepthL - 1 steps ahead into register rings with
+// buffer loads (rows >= M and padding steps read as zeros).  Four waves in a
+// 2 x 2 layout, each a 64 x BN/2 sub-tile.
 // ---------------------------------------------------------------------------
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kLds = kRowElems;
-// dynamic LDS of the large kernel: the A/W double buffers, or the finished
+// dynamic LDS of the tiled kernel: the A/W double buffers, or the finished
 // fp32 tile of the epilogue, whichever is larger
-constexpr int kLargeLds = 2 * (kBM + kBN) * kLds * 2 > kBM * (kBN + 4) * 4 ? 2 * (kBM + kBN) * kLds * 2
-                                                                            : kBM * (kBN + 4) * 4;
+template <int BN>
+constexpr int large_lds() {
+  return 2 * (kBM + BN) * kLds * 2 > kBM * (BN + 4) * 4 ? 2 * (kBM + BN) * kLds * 2 : kBM * (BN + 4) * 4;
+}
 
+template <int BN>
 __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ A, int M_max,
                                                    const int32_t* __restrict__ n_rows, int m_base, int K, WMap W,
                                                    int N, int splits, int n_mt, int n_nt, float* __restrict__ P,
                                                    Epilogue epi) {
-  constexpr int WM = kBM / 2, WN = kBN / 2, MI = WM / 16, NI = WN / 16;
-  constexpr int CH = kBM * kBK / 8 / 256;      // 16-byte items per thread per operand per step (4)
+  constexpr int WM = kBM / 2, WN = BN / 2, MI = WM / 16, NI = WN / 16;
+  constexpr int CH = kBM * kBK / 8 / 256;      // 16-byte A items per thread per step (4)
+  constexpr int CW = BN * kBK / 8 / 256;       // 16-byte W items per thread per step
   extern __shared__ __align__(16) uint16_t lds[];
   uint16_t* As = lds;                          // [2][kBM][kLds]
-  uint16_t* Ws = lds + 2 * kBM * kLds;         // [2][kBN][kLds]
+  uint16_t* Ws = lds + 2 * kBM * kLds;         // [2][BN][kLds]
 
   int mt, nt, split;
   tile_of_block_mn(blockIdx.x, n_mt, splits, mt, nt, split);
@@ -450,7 +463,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
   const int M = min(*n_rows - m_base, M_max);
   const int m0 = mt * kBM;
   if (m0 >= M) return;
-  const int n0 = nt * kBN;
+  const int n0 = nt * BN;
   const int nk_all = K / kBK;
   const int ks0 = split * nk_all / splits, ks1 = (split + 1) * nk_all / splits;
   const int nk = ks1 - ks0;
@@ -462,36 +475,40 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
   // item i of thread t covers tile row (t >> 3) + 32 i, columns ((t & 7) * 8, +8)
   const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(A) + (size_t)m0 * K, (short)0, (min(M - m0, kBM)) * K * 2, 0x00020000);
-  __amdgpu_buffer_rsrc_t wr[CH];
-  uint32_t aoff[CH], woff[CH];
+  __amdgpu_buffer_rsrc_t wr[CW];
+  uint32_t aoff[CH], woff[CW];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int row = (t >> 3) + 32 * i, kc = (t & 7) * 8;
     aoff[i] = (uint32_t)((row * K + ks0 * kBK + kc) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < CW; ++i) {
+    const int row = (t >> 3) + 32 * i, kc = (t & 7) * 8;
     int sg, r;
-    wrow_index<kBN>(W, n0 + row, sg, r);        // rows 32i..32i+31 share a segment for every mode
+    wrow_index<BN>(W, n0 + row, sg, r);         // rows 32i..32i+31 share a segment for every mode
     sg = __builtin_amdgcn_readfirstlane(sg);
     wr[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(W.p[sg]), (short)0, W.seg_bytes, 0x00020000);
     woff[i] = (uint32_t)((r * K + ks0 * kBK + kc) * 2);
   }
-  uint4 ra[kDepthL][CH], rw[kDepthL][CH];
+  uint4 ra[kDepthL][CH], rw[kDepthL][CW];
   const int rot = k_rotation(nt, nk);   // the row tiles of a column tile walk K together
-  auto issue = [&](int step, uint4 (&a)[CH], uint4 (&w)[CH]) {
+  auto issue = [&](int step, uint4 (&a)[CH], uint4 (&w)[CW]) {
     const bool in = step < nk;
     const int sr = step + rot >= nk ? step + rot - nk : step + rot;
     const uint32_t ks = (uint32_t)sr * (kBK * 2);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       a[i] = buf_load16(ar, in ? aoff[i] + ks : kOob);
-      w[i] = buf_load16(wr[i], in ? woff[i] + ks : kOob);
+      if (i < CW) w[i] = buf_load16(wr[i], in ? woff[i] + ks : kOob);
     }
   };
-  auto store = [&](int buf, const uint4 (&a)[CH], const uint4 (&w)[CH]) {
+  auto store = [&](int buf, const uint4 (&a)[CH], const uint4 (&w)[CW]) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int row = (t >> 3) + 32 * i, kc = (t & 7) * 8;
       *reinterpret_cast<uint4*>(As + buf * kBM * kLds + lds_idx(row, kc >> 3)) = a[i];
-      *reinterpret_cast<uint4*>(Ws + buf * kBN * kLds + lds_idx(row, kc >> 3)) = w[i];
+      if (i < CW) *reinterpret_cast<uint4*>(Ws + buf * BN * kLds + lds_idx(row, kc >> 3)) = w[i];
     }
   };
 
@@ -510,7 +527,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
     for (int u = 0; u < kDepthL; ++u) {
       issue(kt + u + kDepthL - 1, ra[(u + kDepthL - 1) % kDepthL], rw[(u + kDepthL - 1) % kDepthL]);
       const uint16_t* a = As + (u & 1) * kBM * kLds;
-      const uint16_t* w = Ws + (u & 1) * kBN * kLds;
+      const uint16_t* w = Ws + (u & 1) * BN * kLds;
 #pragma unroll
       for (int ks = 0; ks < kBK / 32; ++ks) {
         const int kch = ks * 4 + (lane >> 4);
@@ -546,7 +563,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
   }
   // finished tile to LDS (rows relative to m0), then the epilogue on a view
   // whose row 0 is packed row m0
-  constexpr int TS = kBN + 4;
+  constexpr int TS = BN + 4;
   float* T = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -563,7 +580,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
   if (e.row_pos) e.row_pos += m0;
   if (e.row_seq) e.row_seq += m0;
   if (e.kind == EPI_LM) e.lm_part += (size_t)m0 * e.lm_tiles * 4;
-  tile_epilogue<kBN, TS, 256, kBM>(e, T, W, n0, Mt);
+  tile_epilogue<BN, TS, 256, kBM>(e, T, W, n0, Mt);
 }
 
 // ---------------------------------------------------------------------------
@@ -640,6 +657,24 @@ hipError_t launch_skinny_bn(const GemmPlan& plan, const void* A, int M_max, cons
   }
 }
 
+template <int BN>
+hipError_t launch_tiled(const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows, int m_base, int K,
+                        const WMap& w, int N, float* P, const Epilogue& epi, hipStream_t st) {
+  constexpr int lds_bytes = large_lds<BN>();
+  static bool attr_set = false;  // the tile may need more than the default 64 KiB of LDS
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma<BN>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int n_mt = cdiv(M_max, kBM), n_nt = N / BN;
+  const int grid = cdiv(n_nt, 8) * 8 * n_mt * plan.splits;
+  hipLaunchKernelGGL((k_gemm_mfma<BN>), dim3(grid), dim3(256), lds_bytes, st, (const uint16_t*)A, M_max, n_rows,
+                     m_base, K, w, N, plan.splits, n_mt, n_nt, P, epi);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim, int F) {
@@ -648,6 +683,28 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
   if (dt != DL_BF16 || K % 64 != 0 || M <= 0) return p;
   const int nk = K / 64;
   const int n_seg = epi_kind == EPI_QKV ? N / 3 : epi_kind == EPI_SWIGLU ? N / 2 : N;
+  // up to 128 rows: one 128 x 64 tile row of the tiled kernel when the shape
+  // allows it (more column tiles than 128-wide ones); else the skinny kernel
+  const bool tiled_small = DTSK_TILED_SMALL && M > 64 && M <= 128 && epi_kind != EPI_LM && N % 64 == 0 &&
+                           (epi_kind != EPI_QKV || (head_dim == 128 && n_seg % 128 == 0)) &&
+                           (epi_kind != EPI_SWIGLU || F % 32 == 0);
+  if (tiled_small) {
+    p.kind = GEMM_LARGE;
+    p.sep_epi = 0;
+    // 128-wide column tiles when there are enough of them to spread over the
+    // chip; else 64-wide ones (twice the workgroups)
+    const bool wide = N % 128 == 0 && N / 128 >= DTSK_T128_MIN_TILES && epi_kind != EPI_QKV &&
+                      (epi_kind != EPI_SWIGLU || F % 64 == 0);
+    p.bn = wide ? 128 : 64;
+    p.wmode = epi_kind == EPI_SWIGLU ? 1 : epi_kind == EPI_QKV ? 2 : 0;
+    if (epi_kind == EPI_NONE) {
+      const int tiles = N / p.bn;
+      int s = 1;
+      while (tiles * s < 256 && s < 8 && s * 2 <= nk) s *= 2;
+      p.splits = s;
+    }
+    return p;
+  }
   if (M <= 128 && (long long)n_seg * K * 2 < 0x7fff0000LL && 128LL * K * 2 < 0x7fff0000LL) {
     p.kind = GEMM_SKINNY;
     p.sep_epi = 0;
@@ -711,19 +768,8 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
     return launch_skinny_bn<128>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
   }
   if (plan.kind == GEMM_LARGE) {
-    const int lds_bytes = kLargeLds;
-    static bool attr_set = false;  // the tile needs more than the default 64 KiB of LDS
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         lds_bytes);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
-    const int n_mt = cdiv(M_max, kBM), n_nt = N / kBN;
-    const int grid = cdiv(n_nt, 8) * 8 * n_mt * plan.splits;
-    hipLaunchKernelGGL(k_gemm_mfma, dim3(grid), dim3(256), lds_bytes, st, (const uint16_t*)A, M_max, n_rows, m_base,
-                       K, w, N, plan.splits, n_mt, n_nt, P, epi);
-    return hipGetLastError();
+    if (plan.bn == 64) return launch_tiled<64>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+    return launch_tiled<kBN>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
   }
   dim3 grid(cdiv(N, 64), cdiv(M_max, 64));
   if (dt == DL_F32)
