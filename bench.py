@@ -105,7 +105,7 @@ def recorded_traffic():
     calibration).  None when the kernel's source changed after the counters
     were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "k_gemm_skinny_full8b_traffic.json")
+    path = os.path.join(ROOT, "profiles", "kept_row_products_full8b_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -194,7 +194,8 @@ def main():
     gemm_gbs = g["bytes"] / (g["ms"] / 1e3) / 1e9 if g["ms"] > 0 else 0.0
     roofline = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": recorded_traffic(),
-                "kernel": "k_gemm_skinny<8, 64> (layer products on the 128 kept rows: QKV, O, gate/up, down)",
+                "kernel": ("layer products on the 128 kept rows: k_gemm_mfma<64> (QKV, O, down) and "
+                           "k_gemm_mfma<128> (gate|up)"),
                 "launches_timed": g["launches"], "launches_total": g["launches"] + g["dropped"],
                 "avg_launch_us": round(g["ms"] * 1e3 / max(g["launches"], 1), 2),
                 "alg_bytes_per_launch": round(g["bytes"] / max(g["launches"], 1))}

@@ -279,7 +279,7 @@ dl_status product(const Ctx& c, dl_kernel_class kc, const void* A, const RowMap&
   float* P = at<float>(c.ws, c.L->P);
   const GemmPlan p = plan_gemm(d.dtype, rows, N, K, e.kind, d.head_dim, d.d_ffn);
   if (splits_out) *splits_out = p.splits;
-  if (kc == DL_KC_GEMM && p.kind != GEMM_SKINNY) kc = DL_KC_GEMM_TILED;
+  if (kc == DL_KC_GEMM && rows > 128) kc = DL_KC_GEMM_TILED;
   Epilogue ge = e;
   if (p.sep_epi && e.kind != EPI_NONE) ge.kind = EPI_NONE;   // partials; the epilogue kernel finishes
   DL_CHECK_HIP(timed(kc, c.st, gemm_bytes(d, rows, N, K), 2.0 * rows * N * K, [&] {

@@ -226,10 +226,10 @@ dl_status dl_denoise_step(const dl_model *model, dl_state *state, const dl_step_
  * `dropped`.  Not thread-safe.
  * ------------------------------------------------------------------------- */
 typedef enum {
-  DL_KC_GEMM = 0,        /* layer products on <= 128 rows (weight-streaming kernel) */
+  DL_KC_GEMM = 0,        /* layer products on at most 128 rows (the kept rows of a skip step) */
   DL_KC_ATTN = 1,        /* attention */
   DL_KC_LMHEAD = 2,      /* LM head product with its confidence statistics */
-  DL_KC_GEMM_TILED = 3,  /* layer products on more rows (tiled kernel) and the fp32 path */
+  DL_KC_GEMM_TILED = 3,  /* layer products on more rows (prefix layers, refresh steps) */
   DL_KC_COUNT = 4
 } dl_kernel_class;
 
