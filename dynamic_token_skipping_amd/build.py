@@ -23,8 +23,10 @@ SOURCES = ["abi.hip", "k_rows.hip", "k_gemm.hip", "k_attn.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
+# -amdgpu-mfma-vgpr-form: matrix-core accumulators in VGPRs (gfx950 allows
+# it), which spares the AGPR <-> VGPR copies the loops otherwise carry.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-             "-packed-fp32-ops", "-Wno-unused-result", "-munsafe-fp-atomics"]
+             "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-unused-result", "-munsafe-fp-atomics"]
 
 
 def hipcc() -> str:
