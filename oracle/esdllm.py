@@ -42,6 +42,18 @@ function that uses it):
   highest cached confidences (lower index on ties) and writes the cached argmax.
 * The tiny workload's own text defines a second score: relative L2 change plus
   (1 - c).  DyLLM's saliency (cosine similarity) gives a third: 1 - cos.
+* Two skip layers (ES-dLLM section 2B: skipping at layers 4 and 8 of 32, a
+  skip ratio r_l per layer): the second level scores the rows kept by the
+  first, at the input of layer s2, against a second cache H2 of that input,
+  and keeps k2 = ceil(keep2 * |S|) of them (|S| as for the first level, capped
+  at the first level's count).  H2 is rewritten for every row on a refresh
+  step and for the first level's rows on a skip step.
+* Response-only steps (DyLLM section 2B, strategy 3): on a skip step that is
+  not a full-context step, only the response rows (positions >= prompt length)
+  go through the prefix layers, are scored and can be kept; |S| is then the
+  response length.  Prompt rows keep every cache (their K/V at every layer
+  serve as keys).  Full-context steps are those whose in-block index is a
+  multiple of the interval; refresh steps are always full context.
 """
 from __future__ import annotations
 
@@ -55,7 +67,7 @@ __all__ = [
     "rms_norm", "rope", "attention", "silu", "layer_forward", "lm_logits",
     "conf_argmax", "score_rows", "keep_count", "select_topk", "select_threshold",
     "unmask", "SeqState", "init_state", "denoise_step", "decode",
-    "is_refresh_step", "FLT_MIN",
+    "is_refresh_step", "is_full_context_step", "candidate_rows", "level2_count", "FLT_MIN",
 ]
 
 F64 = np.float64
@@ -261,6 +273,7 @@ class SeqState:
     V: List[np.ndarray]           # per layer [n, d]
     h_final: np.ndarray           # [n, d] last layer output (before final norm)
     logits: Optional[np.ndarray] = None   # [n, V] when kept
+    h_prev2: Optional[np.ndarray] = None  # [n, d] input of the second skip layer
 
 
 def init_state(prompt: np.ndarray, gen_len: int, dims, mask_id: Optional[int] = None,
@@ -278,7 +291,8 @@ def init_state(prompt: np.ndarray, gen_len: int, dims, mask_id: Optional[int] = 
                     K=[np.zeros((n, d), F64) for _ in range(dims.n_layers)],
                     V=[np.zeros((n, d), F64) for _ in range(dims.n_layers)],
                     h_final=np.zeros((n, d), F64),
-                    logits=np.zeros((n, dims.vocab), F64) if keep_logits else None)
+                    logits=np.zeros((n, dims.vocab), F64) if keep_logits else None,
+                    h_prev2=np.zeros((n, d), F64))
 
 
 def is_refresh_step(step: int, sched) -> bool:
@@ -289,60 +303,116 @@ def is_refresh_step(step: int, sched) -> bool:
     return sched.refresh_interval > 0 and sib % sched.refresh_interval == 0
 
 
+def is_full_context_step(step: int, sched) -> bool:
+    """DyLLM response-only strategy: with an interval N > 0, a skip step takes
+    every row only when its in-block index is a multiple of N."""
+    N = getattr(sched, "response_interval", 0)
+    return N <= 0 or (step % sched.steps_per_block) % N == 0
+
+
+def candidate_rows(st: SeqState, response_only: bool) -> np.ndarray:
+    """Rows that go through the prefix layers and may be kept: every row, or
+    the response rows [prompt_len, n) on a response-only step."""
+    n = st.tokens.shape[0]
+    return np.arange(st.prompt_len if response_only else 0, n, dtype=np.int64)
+
+
+def level2_count(keep2: float, n_cand: int, n_kept1: int) -> int:
+    """Rows kept at the second skip layer: k = (1 - r_l)|S| on the step's
+    candidate count, never more than the first level kept."""
+    if n_kept1 <= 0:
+        return 0
+    return min(keep_count(keep2, n_cand), n_kept1)
+
+
 @dataclass
 class StepInfo:
     refresh: bool
     selected: np.ndarray          # rows recomputed in layers >= s (ascending)
-    scores: Optional[np.ndarray]  # fp64 scores (skip steps only)
+    scores: Optional[np.ndarray]  # fp64 scores [n] (skip steps only; -inf for non-candidates)
     unmasked: np.ndarray          # positions unmasked by this step
+    selected2: Optional[np.ndarray] = None   # rows recomputed in layers >= s2 (two levels)
+    scores2: Optional[np.ndarray] = None     # fp64 second-level scores [n] (-inf outside `selected`)
+    response_only: bool = False
 
 
 def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = "topk",
                  threshold: float = 0.0, force_refresh: Optional[bool] = None,
-                 keep: Optional[float] = None) -> StepInfo:
+                 keep: Optional[float] = None, response_only: Optional[bool] = None,
+                 mode2: str = "topk", threshold2: float = 0.0) -> StepInfo:
     """One denoising step of one sequence (ES-dLLM section 2B).
 
     Refresh step: every row through every layer; all caches rewritten.
-    Skip step: layers [0, s) on all rows give X_s; score X_s against h_prev with
-    the cached confidence; keep the top-k (or threshold) rows; h_prev <- X_s for
-    all rows; layers [s, L) on the kept rows only, each layer scattering their
-    fresh K/V into its cache first; LM head on the kept rows; scatter conf,
-    argmax, h_final (and logits) for kept rows only.  Then unmask.
+    Skip step: layers [0, s) on the candidate rows (every row, or the response
+    rows on a response-only step) give X_s; score X_s against h_prev with the
+    cached confidence; keep the top-k (or threshold) rows; h_prev <- X_s for
+    the candidates; layers [s, L) on the kept rows only, each layer scattering
+    their fresh K/V into its cache first; LM head on the kept rows; scatter
+    conf, argmax, h_final (and logits) for kept rows only.  Then unmask.
+    With a second skip layer s2, layers [s, s2) run on the first level's rows,
+    which are scored again at the input of s2 against h_prev2; only the second
+    level's rows go through [s2, L) and the LM head.
     """
     n = st.tokens.shape[0]
     s_layer = sched.skip_layer
+    s2 = getattr(sched, "skip_layer2", 0)
     L = dims.n_layers
     refresh = is_refresh_step(step, sched) if force_refresh is None else force_refresh
+    if response_only is None:
+        response_only = not is_full_context_step(step, sched)
+    response_only = bool(response_only) and not refresh
     keep = sched.keep if keep is None else keep
-    pos_all = np.arange(n, dtype=np.int64)
+    cand = candidate_rows(st, response_only)
 
-    x = np.asarray(model["embed"], F64)[st.tokens]          # [n, d]
+    x = np.asarray(model["embed"], F64)[st.tokens[cand]]     # [n_cand, d]
     for li in range(s_layer):
-        x = layer_forward(x, pos_all, model["layers"][li], st.K[li], st.V[li], n, dims)
+        x = layer_forward(x, cand, model["layers"][li], st.K[li], st.V[li], n, dims)
 
     scores = None
     if refresh:
-        sel = pos_all
+        idx = np.arange(cand.size, dtype=np.int64)
     else:
-        scores = score_rows(sched.score, x, st.h_prev, st.conf, sched.alpha)
+        sc = score_rows(sched.score, x, st.h_prev[cand], st.conf[cand], sched.alpha)
+        scores = np.full(n, -np.inf)
+        scores[cand] = sc
         if mode == "topk":
-            sel = select_topk(scores, keep_count(keep, n))
+            idx = select_topk(sc, keep_count(keep, cand.size))
         else:
-            sel = select_threshold(scores, threshold)
-    st.h_prev = x.copy()                                      # all rows, every step
+            idx = select_threshold(sc, threshold)
+    sel = cand[idx]
+    st.h_prev[cand] = x                                       # every candidate row
 
-    xr = x[sel]
-    for li in range(s_layer, L):
-        xr = layer_forward(xr, sel, model["layers"][li], st.K[li], st.V[li], n, dims)
+    xr = x[idx]
+    sel2, scores2, l_rest = None, None, s_layer
+    if s2 > 0:
+        for li in range(s_layer, s2):
+            xr = layer_forward(xr, sel, model["layers"][li], st.K[li], st.V[li], n, dims)
+        if refresh:
+            idx2 = np.arange(sel.size, dtype=np.int64)
+        else:
+            sc2 = score_rows(sched.score, xr, st.h_prev2[sel], st.conf[sel], sched.alpha)
+            scores2 = np.full(n, -np.inf)
+            scores2[sel] = sc2
+            if mode2 == "topk":
+                idx2 = select_topk(sc2, level2_count(sched.keep2, cand.size, sel.size))
+            else:
+                idx2 = select_threshold(sc2, threshold2)
+        st.h_prev2[sel] = xr                                  # every first-level row
+        sel2 = sel[idx2]
+        xr = xr[idx2]
+        l_rest = s2
+    rows = sel if sel2 is None else sel2
+    for li in range(l_rest, L):
+        xr = layer_forward(xr, rows, model["layers"][li], st.K[li], st.V[li], n, dims)
 
-    if sel.size:
+    if rows.size:
         logits = lm_logits(xr, model["final_norm"], model["lm_head"], dims.rms_eps)
         conf, amax = conf_argmax(logits)
-        st.conf[sel] = conf
-        st.argmax[sel] = amax
-        st.h_final[sel] = xr
+        st.conf[rows] = conf
+        st.argmax[rows] = amax
+        st.h_final[rows] = xr
         if st.logits is not None:
-            st.logits[sel] = logits
+            st.logits[rows] = logits
 
     b = step // sched.steps_per_block
     lo = st.prompt_len + b * sched.block_len
@@ -350,17 +420,19 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
     pos = unmask(st.masked, st.conf, lo, hi, sched.per_step)
     st.tokens[pos] = st.argmax[pos]
     st.masked[pos] = False
-    return StepInfo(refresh=refresh, selected=sel, scores=scores, unmasked=pos)
+    return StepInfo(refresh=refresh, selected=sel, scores=scores, unmasked=pos, selected2=sel2,
+                    scores2=scores2, response_only=response_only)
 
 
 def decode(model: dict, dims, prompt: np.ndarray, sched, n_steps: Optional[int] = None,
            vanilla: bool = False, keep_logits: bool = False, mode: str = "topk",
-           threshold: float = 0.0):
+           threshold: float = 0.0, mode2: str = "topk", threshold2: float = 0.0):
     """Run the decode loop.  ``vanilla`` refreshes every step (full recompute)."""
     st = init_state(prompt, sched.gen_len, dims, keep_logits=keep_logits)
     infos = []
     T = sched.steps if n_steps is None else n_steps
     for t in range(T):
         infos.append(denoise_step(model, dims, st, t, sched, mode=mode, threshold=threshold,
-                                  force_refresh=True if vanilla else None))
+                                  force_refresh=True if vanilla else None, mode2=mode2,
+                                  threshold2=threshold2))
     return st, infos

@@ -371,4 +371,179 @@ def pin_fresh_cache_skip_is_exact():
     close(st.h_final[info.selected], full[info.selected], rtol=1e-11)
 
 
+# --------------------------------------------------------------------------
+# two skip levels (ES-dLLM section 2B: skipping at two early layers, a skip
+# ratio per layer)
+# --------------------------------------------------------------------------
+
+def _eq1(conf, x, h, d):
+    """Eq. I with alpha = 0.5, written in torch."""
+    x, h = libref.t(x), libref.t(h)
+    return (0.5 * libref.t(conf) + 0.5 * (x - h).abs().sum(1) / (math.sqrt(d) * h.norm(dim=1))).numpy()
+
+
+def pin_nested_keep2_all_is_one_level():
+    """A second level that keeps everything the first kept changes nothing."""
+    one = micro_sched(keep=0.35)
+    two = micro_sched(keep=0.35, skip_layer2=2, keep2=1.0)
+    _, _, _, st_a, inf_a = _micro_run(one)
+    _, _, _, st_b, inf_b = _micro_run(two)
+    for key in ("tokens", "masked", "conf", "argmax", "h_prev", "h_final", "logits"):
+        assert np.array_equal(getattr(st_a, key), getattr(st_b, key)), key
+    for li in range(len(st_a.K)):
+        assert np.array_equal(st_a.K[li], st_b.K[li]) and np.array_equal(st_a.V[li], st_b.V[li])
+    for ia, ib in zip(inf_a, inf_b):
+        assert np.array_equal(ia.selected, ib.selected2)
+
+
+def pin_nested_full_first_level_is_one_level_at_s2():
+    """Keeping every row at s1 makes the second level a single skip at s2 whose
+    cached input is h_prev2."""
+    two = micro_sched(skip_layer=1, keep=1.0, skip_layer2=2, keep2=0.35)
+    one = micro_sched(skip_layer=2, keep=0.35)
+    _, _, _, st_a, inf_a = _micro_run(two)
+    _, _, _, st_b, inf_b = _micro_run(one)
+    assert any(not i.refresh for i in inf_b)
+    for key in ("tokens", "masked", "conf", "argmax", "h_final", "logits"):
+        assert np.array_equal(getattr(st_a, key), getattr(st_b, key)), key
+    assert np.array_equal(st_a.h_prev2, st_b.h_prev)
+    for li in range(len(st_a.K)):
+        assert np.array_equal(st_a.K[li], st_b.K[li]) and np.array_equal(st_a.V[li], st_b.V[li])
+    for ia, ib in zip(inf_a, inf_b):
+        assert np.array_equal(ia.selected2, ib.selected)
+        if not ib.refresh:
+            assert np.array_equal(ia.scores2, ib.scores)
+
+
+def pin_nested_step_semantics():
+    """One two-level skip step against torch: R1 = top-k1 of eq. I at s1,
+    layers [s1, s2) on R1 against stale caches, h_prev2 <- their s2 input,
+    R2 = top-k2 of eq. I at s2 among R1, layers [s2, L) on R2; every other row
+    keeps every cached byte."""
+    sched = micro_sched(skip_layer=1, keep=0.6, skip_layer2=2, keep2=0.3)
+    dims = micro_dims()
+    m = np_model(dims)
+    prompt = (np.arange(9) * 5 + 2) % dims.vocab
+    st = E.init_state(prompt, sched.gen_len, dims, keep_logits=True)
+    tokens0 = st.tokens.copy()
+    E.denoise_step(m, dims, st, 0, sched)                    # refresh
+    close(st.h_prev2, libref.forward(tokens0, m, dims, n_layers=2).numpy(), rtol=1e-11)
+    before = {k: getattr(st, k).copy() for k in ("conf", "argmax", "h_final", "logits", "h_prev", "h_prev2")}
+    Kb = [k.copy() for k in st.K]
+    Vb = [v.copy() for v in st.V]
+    tokens1 = st.tokens.copy()
+    info = E.denoise_step(m, dims, st, 1, sched)
+    assert not info.refresh
+    n, d = len(tokens1), dims.d
+    k1 = E.keep_count(0.6, n)
+    k2 = min(E.keep_count(0.3, n), k1)
+    R1, R2 = info.selected, info.selected2
+    assert len(R1) == k1 and len(R2) == k2 and set(R2.tolist()) <= set(R1.tolist())
+    assert np.all(np.diff(R2) > 0)
+    xs = libref.forward(tokens1, m, dims, n_layers=1)
+    assert R1.tolist() == _brute_topk(_eq1(before["conf"], xs, before["h_prev"], d), k1)
+    xr, K1, V1 = libref.partial_layer(xs[torch.as_tensor(R1)], R1, m["layers"][1], Kb[1], Vb[1], dims)
+    close(st.K[1], K1.numpy(), rtol=1e-11)
+    close(st.V[1], V1.numpy(), rtol=1e-11)
+    close(st.h_prev2[R1], xr.numpy(), rtol=1e-11)
+    out1 = np.setdiff1d(np.arange(n), R1)
+    assert np.array_equal(st.h_prev2[out1], before["h_prev2"][out1])
+    sc2 = _eq1(before["conf"][R1], xr, before["h_prev2"][R1], d)
+    close(info.scores2[R1], sc2, rtol=1e-11)
+    assert np.all(np.isneginf(info.scores2[out1]))
+    assert R2.tolist() == R1[_brute_topk(sc2, k2)].tolist()
+    x2 = xr[torch.as_tensor(np.searchsorted(R1, R2))]
+    for li in range(2, dims.n_layers):
+        x2, Kn, Vn = libref.partial_layer(x2, R2, m["layers"][li], Kb[li], Vb[li], dims)
+        close(st.K[li], Kn.numpy(), rtol=1e-11)
+        close(st.V[li], Vn.numpy(), rtol=1e-11)
+    close(st.h_final[R2], x2.numpy(), rtol=1e-11)
+    lg = libref.logits(x2, m, dims)
+    close(st.conf[R2], torch.softmax(lg, 1).max(1).values.numpy(), rtol=1e-10)
+    out2 = np.setdiff1d(np.arange(n), R2)
+    for key in ("conf", "argmax", "h_final", "logits"):
+        assert np.array_equal(getattr(st, key)[out2], before[key][out2]), key
+
+
+# --------------------------------------------------------------------------
+# response-only steps (DyLLM section 2B, strategy 3)
+# --------------------------------------------------------------------------
+
+def pin_response_only_without_prompt_is_full_context():
+    """With no prompt every row is a response row: the response-only schedule
+    decodes exactly like the full-context one."""
+    dims = micro_dims()
+    m = np_model(dims)
+    runs = []
+    for sched in (micro_sched(keep=0.4), micro_sched(keep=0.4, response_interval=2)):
+        st, infos = E.decode(m, dims, np.zeros(0, np.int64), sched, keep_logits=True)
+        runs.append((st, infos))
+    (st_a, inf_a), (st_b, inf_b) = runs
+    assert any(i.response_only for i in inf_b)
+    for key in ("tokens", "masked", "conf", "argmax", "h_prev", "h_final", "logits"):
+        assert np.array_equal(getattr(st_a, key), getattr(st_b, key)), key
+    for ia, ib in zip(inf_a, inf_b):
+        assert np.array_equal(ia.selected, ib.selected)
+
+
+def pin_response_only_step_semantics():
+    """A response-only step against torch: the response rows go through the
+    prefix against the cached prompt K/V, are scored, and k = ceil(keep * n_resp)
+    of them are kept; prompt rows keep every cached byte."""
+    sched = micro_sched(keep=0.5, response_interval=2)
+    dims = micro_dims()
+    m = np_model(dims)
+    prompt = (np.arange(9) * 3 + 1) % dims.vocab
+    P = len(prompt)
+    st = E.init_state(prompt, sched.gen_len, dims, keep_logits=True)
+    E.denoise_step(m, dims, st, 0, sched)                    # refresh
+    before = {k: getattr(st, k).copy() for k in ("conf", "argmax", "h_final", "logits", "h_prev")}
+    Kb = [k.copy() for k in st.K]
+    Vb = [v.copy() for v in st.V]
+    tokens1 = st.tokens.copy()
+    info = E.denoise_step(m, dims, st, 1, sched)
+    assert info.response_only and not info.refresh
+    n, d = len(tokens1), dims.d
+    cand = np.arange(P, n)
+    x = libref.t(m["embed"])[torch.as_tensor(tokens1[cand])]
+    for li in range(sched.skip_layer):
+        x, Kn, Vn = libref.partial_layer(x, cand, m["layers"][li], Kb[li], Vb[li], dims)
+        close(st.K[li], Kn.numpy(), rtol=1e-11)
+        assert np.array_equal(st.K[li][:P], Kb[li][:P]) and np.array_equal(st.V[li][:P], Vb[li][:P])
+    close(st.h_prev[cand], x.numpy(), rtol=1e-11)
+    assert np.array_equal(st.h_prev[:P], before["h_prev"][:P])
+    sc = _eq1(before["conf"][cand], x, before["h_prev"][cand], d)
+    close(info.scores[cand], sc, rtol=1e-11)
+    assert np.all(np.isneginf(info.scores[:P]))
+    k = E.keep_count(0.5, n - P)
+    sel = info.selected
+    assert sel.tolist() == (cand[_brute_topk(sc, k)]).tolist()
+    xr = x[torch.as_tensor(sel - P)]
+    for li in range(sched.skip_layer, dims.n_layers):
+        xr, Kn, Vn = libref.partial_layer(xr, sel, m["layers"][li], Kb[li], Vb[li], dims)
+        close(st.K[li], Kn.numpy(), rtol=1e-11)
+    close(st.h_final[sel], xr.numpy(), rtol=1e-11)
+    other = np.setdiff1d(np.arange(n), sel)
+    for key in ("conf", "argmax", "h_final", "logits"):
+        assert np.array_equal(getattr(st, key)[other], before[key][other]), key
+
+
+def pin_response_only_schedule():
+    """Refresh steps are full context; other steps are full context every
+    response_interval in-block steps and response-only otherwise."""
+    sched = micro_sched(keep=0.4, block_len=6, steps=8, gen_len=12, response_interval=3)
+    dims, m, prompt, st, infos = _micro_run(sched)
+    P, n = len(prompt), len(prompt) + sched.gen_len
+    kinds = []
+    for t, inf in enumerate(infos):
+        sib = t % sched.steps_per_block
+        kinds.append("R" if inf.refresh else ("r" if inf.response_only else "F"))
+        assert inf.response_only == (not inf.refresh and sib % 3 != 0)
+        if inf.response_only:
+            assert inf.selected.min() >= P and len(inf.selected) == E.keep_count(0.4, n - P)
+        elif not inf.refresh:
+            assert len(inf.selected) == E.keep_count(0.4, n)
+    assert kinds == list("RrrFRrrF"), kinds
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

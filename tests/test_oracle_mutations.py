@@ -13,7 +13,8 @@ from oracle import esdllm as E
 
 _orig = {name: getattr(E, name) for name in ("score_rows", "rms_norm", "rope", "attention", "select_topk",
                                              "unmask", "keep_count", "conf_argmax", "silu", "layer_forward",
-                                             "select_threshold")}
+                                             "select_threshold", "candidate_rows", "level2_count",
+                                             "is_full_context_step")}
 
 
 def m_score_l2(kind, x, h, c, alpha=0.5):          # L2 instead of L1 in eq. I
@@ -106,6 +107,23 @@ def m_threshold_ge(scores, tau):
     return np.nonzero(s32 >= np.float32(tau) - np.float32(0.05))[0]
 
 
+def m_cand_all(st, response_only):                  # prompt rows scored on response-only steps
+    return _orig["candidate_rows"](st, False)
+
+
+def m_cand_shift(st, response_only):                # response rows start one late
+    c = _orig["candidate_rows"](st, response_only)
+    return c[1:] if response_only else c
+
+
+def m_full_context_always(step, sched):             # response-only steps never happen
+    return True
+
+
+def m_level2_of_kept(keep2, n_cand, n_kept1):       # second ratio taken of the first level's count
+    return _orig["keep_count"](keep2, n_kept1) if n_kept1 > 0 else 0
+
+
 MUTANTS = [
     ("score_rows", m_score_l2), ("score_rows", m_score_csign), ("score_rows", m_score_nosqrtd),
     ("rms_norm", m_rms_noeps), ("rope", m_rope_sign), ("rope", m_rope_pairs),
@@ -114,6 +132,8 @@ MUTANTS = [
     ("unmask", m_unmask_noblock), ("unmask", m_unmask_lowconf), ("keep_count", m_keep_floor),
     ("conf_argmax", m_conf_maxlogit), ("silu", m_silu_sigmoid), ("layer_forward", m_layer_kv_late),
     ("select_threshold", m_threshold_ge),
+    ("candidate_rows", m_cand_all), ("candidate_rows", m_cand_shift),
+    ("is_full_context_step", m_full_context_always), ("level2_count", m_level2_of_kept),
 ]
 
 

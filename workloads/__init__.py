@@ -76,6 +76,9 @@ class Schedule:
     score: str             # "esdllm" | "rell2_invconf" | "cosine"
     alpha: float = 0.5
     refresh_interval: int = 0   # 0: refresh only at each block's first step
+    skip_layer2: int = 0        # second skip layer (0: one level); skip_layer < skip_layer2 <= n_layers
+    keep2: float = 1.0          # keep ratio at the second skip layer
+    response_interval: int = 0  # > 0: full-context skip steps every N in-block steps, response rows only otherwise
 
     @property
     def n_blocks(self) -> int:
