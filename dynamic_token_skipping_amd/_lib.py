@@ -54,13 +54,15 @@ class State(Structure):
     _fields_ = [("tokens", c_void_p), ("masked", c_void_p), ("seq_len", c_void_p), ("prompt_len", c_void_p),
                 ("h_prev", c_void_p), ("k_cache", c_void_p), ("v_cache", c_void_p), ("h_final", c_void_p),
                 ("conf", c_void_p), ("argmax", c_void_p), ("logits", c_void_p), ("scores", c_void_p),
-                ("sel", Selection)]
+                ("sel", Selection), ("h_prev2", c_void_p), ("scores2", c_void_p), ("sel2", Selection)]
 
 
 class StepParams(Structure):
     _fields_ = [("block", c_int32), ("block_len", c_int32), ("n_unmask", c_int32), ("skip_layer", c_int32),
                 ("full_refresh", c_int32), ("score", c_int32), ("alpha", c_float), ("mode", c_int32),
-                ("keep_ratio", c_float), ("threshold", c_float), ("seq_len_host", POINTER(c_int32))]
+                ("keep_ratio", c_float), ("threshold", c_float), ("seq_len_host", POINTER(c_int32)),
+                ("response_only", c_int32), ("prompt_len_host", POINTER(c_int32)), ("skip_layer2", c_int32),
+                ("mode2", c_int32), ("keep_ratio2", c_float), ("threshold2", c_float)]
 
 
 class Timing(Structure):

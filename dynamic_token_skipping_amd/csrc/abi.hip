@@ -85,9 +85,11 @@ struct RowMapMem {
 struct Layout {
   int R;                    // row capacity (valid rows over the batch)
   int T;                    // attention tile capacity
-  size_t sel_idx, sel_count, row_off;  // identity selection of every valid row
-  RowMapMem map_all, map_sel;
-  size_t x_all, x_sel;      // fp32 [R, d]
+  size_t sel_idx, sel_count, row_off;  // the step's candidate rows (every valid row, or the response rows)
+  RowMapMem map_all, map_sel, map_sel2;
+  size_t x_all, x_sel, x_sel2;  // fp32 [R, d]
+  size_t inv;               // int32 [B*S]: packed row of a flat position
+  size_t scores2;           // fp32 [B*S]
   size_t act;               // T [R, d] normalised rows
   size_t ffn_act;           // T [R, F] silu(gate) * up
   size_t q, attn;           // T [R, d]
@@ -136,7 +138,7 @@ Layout make_layout(const dl_dims& d, int R) {
   L.sel_idx = take(sizeof(int32_t) * (size_t)B * S);
   L.sel_count = take(sizeof(int32_t) * B);
   L.row_off = take(sizeof(int32_t) * (B + 1));
-  for (RowMapMem* m : {&L.map_all, &L.map_sel}) {
+  for (RowMapMem* m : {&L.map_all, &L.map_sel, &L.map_sel2}) {
     m->row_pos = take(sizeof(int32_t) * L.R);
     m->row_seq = take(sizeof(int32_t) * L.R);
     m->n_rows = take(sizeof(int32_t));
@@ -145,6 +147,9 @@ Layout make_layout(const dl_dims& d, int R) {
   }
   L.x_all = take(sizeof(float) * (size_t)L.R * d.d);
   L.x_sel = take(sizeof(float) * (size_t)L.R * d.d);
+  L.x_sel2 = take(sizeof(float) * (size_t)L.R * d.d);
+  L.inv = take(sizeof(int32_t) * (size_t)B * S);
+  L.scores2 = take(sizeof(float) * (size_t)B * S);
   L.act = take(es * (size_t)L.R * d.d);
   L.ffn_act = take(es * (size_t)L.R * d.d_ffn);
   L.q = take(es * (size_t)L.R * d.d);
@@ -658,35 +663,68 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
     return fail(DL_E_ARG, "keep_ratio %g outside (0, 1]", (double)p->keep_ratio);
   if (p->block < 0 || p->block_len < 1 || p->n_unmask < 0) return fail(DL_E_ARG, "block schedule out of range");
   if (p->block_len > 1024) return fail(DL_E_UNSUPPORTED, "block_len > 1024");
-  long long R_all = 0, R_sel = 0, all_x_keys = 0, sel_x_keys = 0;
+  const bool refresh = p->full_refresh != 0;
+  const bool two = p->skip_layer2 != 0;
+  if (two) {
+    if (p->skip_layer2 <= p->skip_layer || p->skip_layer2 > d.n_layers)
+      return fail(DL_E_ARG, "skip_layer2 %d outside (%d, %d]", p->skip_layer2, p->skip_layer, d.n_layers);
+    if (p->mode2 != DL_SEL_TOPK && p->mode2 != DL_SEL_THRESHOLD) return fail(DL_E_ARG, "select mode2 unknown");
+    if (p->mode2 == DL_SEL_TOPK && !(p->keep_ratio2 > 0.f && p->keep_ratio2 <= 1.f))
+      return fail(DL_E_ARG, "keep_ratio2 %g outside (0, 1]", (double)p->keep_ratio2);
+    if (p->mode == DL_SEL_TOPK && p->mode2 == DL_SEL_TOPK && p->keep_ratio2 > p->keep_ratio)
+      return fail(DL_E_ARG, "keep_ratio2 %g above keep_ratio %g", (double)p->keep_ratio2, (double)p->keep_ratio);
+    DL_TRY(check_ptr(s->h_prev2, "h_prev2"));
+    DL_TRY(check_sel(&s->sel2, "state.sel2"));
+    if (s->scores2) DL_TRY(check_ptr(s->scores2, "scores2"));
+    if (s->h_prev2 == s->h_prev) return fail(DL_E_ARG, "h_prev2 and h_prev alias");
+    if (s->sel2.sel_idx == s->sel.sel_idx || s->sel2.sel_count == s->sel.sel_count ||
+        s->sel2.row_off == s->sel.row_off)
+      return fail(DL_E_ARG, "state.sel2 and state.sel alias");
+  }
+  const bool resp = p->response_only != 0 && !refresh;
+  if (resp && !p->prompt_len_host) return fail(DL_E_ARG, "params.prompt_len_host is NULL on a response-only step");
+
+  // Host row bounds (grid sizing; exact for top-k): candidates, first and second level.
+  auto topk_count = [](float keep, long long base) -> long long {
+    if (base <= 0) return 0;
+    const double kk = ceil((double)keep * (double)base);
+    return kk < 1.0 ? 1 : (kk > (double)base ? base : (long long)kk);
+  };
+  long long R_all = 0, R_cand = 0, R_sel = 0, R_sel2 = 0;
+  long long cand_x_keys = 0, sel_x_keys = 0, sel2_x_keys = 0;
   for (int b = 0; b < d.B; ++b) {
     const int n = p->seq_len_host[b];
     if (n < 0 || n > d.S) return fail(DL_E_SHAPE, "seq_len_host[%d] = %d outside [0, S=%d]", b, n, d.S);
+    const int P0 = resp ? p->prompt_len_host[b] : 0;
+    if (P0 < 0 || P0 > n) return fail(DL_E_SHAPE, "prompt_len_host[%d] = %d outside [0, %d]", b, P0, n);
+    const long long nc = n - P0;
+    const long long k1 = p->mode == DL_SEL_TOPK && !refresh ? topk_count(p->keep_ratio, nc) : nc;
+    const long long k2 = two && p->mode2 == DL_SEL_TOPK && !refresh ? std::min(topk_count(p->keep_ratio2, nc), k1) : k1;
     R_all += n;
-    all_x_keys += (long long)n * n;
-    long long kb = n;
-    if (p->mode == DL_SEL_TOPK && n > 0) {
-      const double kk = ceil((double)p->keep_ratio * (double)n);
-      kb = kk < 1.0 ? 1 : (kk > (double)n ? n : (long long)kk);
-    }
-    R_sel += kb;
-    sel_x_keys += kb * n;
+    R_cand += nc;
+    R_sel += k1;
+    R_sel2 += k2;
+    cand_x_keys += nc * n;
+    sel_x_keys += k1 * n;
+    sel2_x_keys += k2 * n;
   }
-  if (p->mode == DL_SEL_THRESHOLD) R_sel = R_all;
   const Layout L = make_layout(d, (int)R_all);
   if (ws_bytes < L.total) return fail(DL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
 
   hipStream_t st = (hipStream_t)stream;
-  Ctx c{dims, ws, &L, st, R_all, all_x_keys};
-  const bool refresh = p->full_refresh != 0;
+  Ctx c{dims, ws, &L, st, R_all, cand_x_keys};
   const int sl = p->skip_layer;
+  const int s2 = two ? p->skip_layer2 : 0;
   int32_t* all_idx = at<int32_t>(ws, L.sel_idx);
   int32_t* all_cnt = at<int32_t>(ws, L.sel_count);
   int32_t* all_off = at<int32_t>(ws, L.row_off);
-  const RowMap rm_all = rowmap_at(ws, L.map_all, (int)R_all, L.T);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+  auto tiles = [&](long long R) { return std::min(L.T, cdiv(R, kTileRows) + d.B); };
+  const RowMap rm_all = rowmap_at(ws, L.map_all, (int)R_cand, tiles(R_cand));
   float* x_all = at<float>(ws, L.x_all);
 
-  DL_CHECK_HIP(launch_identity_sel(s->seq_len, d.B, d.S, all_idx, all_cnt, st));
+  // the step's candidate rows: every valid row, or the response rows
+  DL_CHECK_HIP(launch_identity_sel(s->seq_len, d.B, d.S, all_idx, all_cnt, st, resp ? s->prompt_len : nullptr));
   DL_CHECK_HIP(launch_row_off(all_cnt, all_off, d.B, st));
   DL_CHECK_HIP(launch_rowmap(all_idx, all_cnt, all_off, d.B, d.S, rm_all, st));
   DL_CHECK_HIP(launch_rope_table(d.S, d.head_dim, d.rope_base, at<float2>(ws, L.rope), st));
@@ -695,35 +733,81 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
   char* kcache = static_cast<char*>(s->k_cache);
   char* vcache = static_cast<char*>(s->v_cache);
   float* scores = s->scores ? s->scores : at<float>(ws, L.scores);
+  float* scores2 = s->scores2 ? s->scores2 : at<float>(ws, L.scores2);
+  auto copy_sel = [&](const dl_selection& dst) -> dl_status {
+    DL_CHECK_HIP(hipMemcpyAsync(dst.sel_idx, all_idx, sizeof(int32_t) * (size_t)d.B * d.S, hipMemcpyDeviceToDevice,
+                                st));
+    DL_CHECK_HIP(hipMemcpyAsync(dst.sel_count, all_cnt, sizeof(int32_t) * d.B, hipMemcpyDeviceToDevice, st));
+    DL_CHECK_HIP(hipMemcpyAsync(dst.row_off, all_off, sizeof(int32_t) * (d.B + 1), hipMemcpyDeviceToDevice, st));
+    return DL_OK;
+  };
   if (refresh) {
-    // every row through every layer; h_prev <- the layer-s input
-    DL_TRY(run_layers(c, model, 0, sl, x_all, rm_all, s->seq_len, kcache, vcache, false,
-                      sl < d.n_layers ? model->layers[sl].attn_norm : model->final_norm));
+    // every row through every layer; h_prev <- the layer-s input (h_prev2 <- the layer-s2 input)
+    auto norm_of = [&](int l) { return l < d.n_layers ? model->layers[l].attn_norm : model->final_norm; };
+    DL_TRY(run_layers(c, model, 0, sl, x_all, rm_all, s->seq_len, kcache, vcache, false, norm_of(sl)));
     DL_CHECK_HIP(launch_store_rows(d.dtype, x_all, d.d, rm_all, s->h_prev, st));
-    DL_TRY(run_layers(c, model, sl, d.n_layers, x_all, rm_all, s->seq_len, kcache, vcache, sl > 0,
-                      model->final_norm));
-    DL_CHECK_HIP(hipMemcpyAsync(s->sel.sel_idx, all_idx, sizeof(int32_t) * (size_t)d.B * d.S,
-                                hipMemcpyDeviceToDevice, st));
-    DL_CHECK_HIP(hipMemcpyAsync(s->sel.sel_count, all_cnt, sizeof(int32_t) * d.B, hipMemcpyDeviceToDevice, st));
-    DL_CHECK_HIP(hipMemcpyAsync(s->sel.row_off, all_off, sizeof(int32_t) * (d.B + 1), hipMemcpyDeviceToDevice, st));
+    int l0 = sl;
+    if (two) {
+      DL_TRY(run_layers(c, model, sl, s2, x_all, rm_all, s->seq_len, kcache, vcache, true, norm_of(s2)));
+      DL_CHECK_HIP(launch_store_rows(d.dtype, x_all, d.d, rm_all, s->h_prev2, st));
+      l0 = s2;
+    }
+    DL_TRY(run_layers(c, model, l0, d.n_layers, x_all, rm_all, s->seq_len, kcache, vcache, true, model->final_norm));
+    DL_TRY(copy_sel(s->sel));
+    if (two) DL_TRY(copy_sel(s->sel2));
     DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_all, rm_all, s->conf, s->argmax, s->h_final, s->logits,
                     true));
   } else {
     DL_TRY(run_layers(c, model, 0, sl, x_all, rm_all, s->seq_len, kcache, vcache, false, nullptr));
     // score against h_prev and overwrite it with this step's layer-s input
-    DL_CHECK_HIP(launch_score(d.dtype, nullptr, x_all, all_off, s->h_prev, s->conf, s->seq_len, d.B, d.S, d.d,
-                              p->score, p->alpha, scores, st));
-    DL_CHECK_HIP(launch_select(scores, s->seq_len, d.B, d.S, p->mode, p->keep_ratio, p->threshold, s->sel.sel_idx,
-                               s->sel.sel_count, st));
+    if (!resp) {
+      DL_CHECK_HIP(launch_score(d.dtype, nullptr, x_all, all_off, s->h_prev, s->conf, s->seq_len, d.B, d.S, d.d,
+                                p->score, p->alpha, scores, st));
+      DL_CHECK_HIP(launch_select(scores, s->seq_len, d.B, d.S, p->mode, p->keep_ratio, p->threshold, s->sel.sel_idx,
+                                 s->sel.sel_count, st));
+    } else {
+      DL_CHECK_HIP(launch_fill_scores(scores, -INFINITY, s->seq_len, d.B, d.S, st));
+      DL_CHECK_HIP(launch_score(d.dtype, nullptr, x_all, nullptr, s->h_prev, s->conf, s->seq_len, d.B, d.S, d.d,
+                                p->score, p->alpha, scores, st, &rm_all));
+      DL_CHECK_HIP(launch_select(scores, s->seq_len, d.B, d.S, p->mode, p->keep_ratio, p->threshold, s->sel.sel_idx,
+                                 s->sel.sel_count, st, all_idx, all_cnt, all_cnt));
+    }
     DL_CHECK_HIP(launch_row_off(s->sel.sel_count, s->sel.row_off, d.B, st));
-    const RowMap rm_sel = rowmap_at(ws, L.map_sel, (int)R_sel, std::min(L.T, cdiv(R_sel, kTileRows) + d.B));
+    const RowMap rm_sel = rowmap_at(ws, L.map_sel, (int)R_sel, tiles(R_sel));
     DL_CHECK_HIP(launch_rowmap(s->sel.sel_idx, s->sel.sel_count, s->sel.row_off, d.B, d.S, rm_sel, st));
     float* x_sel = at<float>(ws, L.x_sel);
-    DL_CHECK_HIP(launch_gather(sizeof(float), x_all, all_off, d.S, d.d, rm_sel, x_sel, st));
+    if (!resp) {
+      DL_CHECK_HIP(launch_gather(sizeof(float), x_all, all_off, d.S, d.d, rm_sel, x_sel, st));
+    } else {
+      DL_CHECK_HIP(launch_inv_rows(rm_all, d.B * d.S, inv, st));
+      DL_CHECK_HIP(launch_gather(sizeof(float), x_all, nullptr, d.S, d.d, rm_sel, x_sel, st, inv));
+    }
     c.rows_x_keys = sel_x_keys;
-    DL_TRY(run_layers(c, model, sl, d.n_layers, x_sel, rm_sel, s->seq_len, kcache, vcache, false, model->final_norm));
-    DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_sel, rm_sel, s->conf, s->argmax, s->h_final, s->logits,
-                    sl < d.n_layers));
+    if (!two) {
+      DL_TRY(run_layers(c, model, sl, d.n_layers, x_sel, rm_sel, s->seq_len, kcache, vcache, false,
+                        model->final_norm));
+      DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_sel, rm_sel, s->conf, s->argmax, s->h_final, s->logits,
+                      sl < d.n_layers));
+    } else {
+      // layers [s, s2) on sel; second score against h_prev2 (rewritten for sel) and selection among sel
+      DL_TRY(run_layers(c, model, sl, s2, x_sel, rm_sel, s->seq_len, kcache, vcache, false, nullptr));
+      DL_CHECK_HIP(launch_fill_scores(scores2, -INFINITY, s->seq_len, d.B, d.S, st));
+      DL_CHECK_HIP(launch_score(d.dtype, nullptr, x_sel, nullptr, s->h_prev2, s->conf, s->seq_len, d.B, d.S, d.d,
+                                p->score, p->alpha, scores2, st, &rm_sel));
+      DL_CHECK_HIP(launch_select(scores2, s->seq_len, d.B, d.S, p->mode2, p->keep_ratio2, p->threshold2,
+                                 s->sel2.sel_idx, s->sel2.sel_count, st, s->sel.sel_idx, s->sel.sel_count, all_cnt));
+      DL_CHECK_HIP(launch_row_off(s->sel2.sel_count, s->sel2.row_off, d.B, st));
+      const RowMap rm_sel2 = rowmap_at(ws, L.map_sel2, (int)R_sel2, tiles(R_sel2));
+      DL_CHECK_HIP(launch_rowmap(s->sel2.sel_idx, s->sel2.sel_count, s->sel2.row_off, d.B, d.S, rm_sel2, st));
+      float* x_sel2 = at<float>(ws, L.x_sel2);
+      DL_CHECK_HIP(launch_inv_rows(rm_sel, d.B * d.S, inv, st));
+      DL_CHECK_HIP(launch_gather(sizeof(float), x_sel, nullptr, d.S, d.d, rm_sel2, x_sel2, st, inv));
+      c.rows_x_keys = sel2_x_keys;
+      DL_TRY(run_layers(c, model, s2, d.n_layers, x_sel2, rm_sel2, s->seq_len, kcache, vcache, false,
+                        model->final_norm));
+      DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_sel2, rm_sel2, s->conf, s->argmax, s->h_final,
+                      s->logits, s2 < d.n_layers));
+    }
   }
   DL_CHECK_HIP(launch_unmask(s->tokens, s->masked, s->conf, s->argmax, s->prompt_len, s->seq_len, d.B, d.S, p->block,
                              p->block_len, p->n_unmask, st));

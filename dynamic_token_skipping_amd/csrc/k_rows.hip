@@ -18,13 +18,15 @@ constexpr int kRowThreads = 256;
 // ---------------------------------------------------------------------------
 // selections
 // ---------------------------------------------------------------------------
-__global__ void k_identity_sel(const int32_t* __restrict__ seq_len, int S, int32_t* __restrict__ sel_idx,
-                               int32_t* __restrict__ sel_count) {
+// positions [start[b], seq_len[b]) of each sequence (start = 0 without `start`)
+__global__ void k_identity_sel(const int32_t* __restrict__ seq_len, const int32_t* __restrict__ start, int S,
+                               int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count) {
   const int b = blockIdx.y;
   const int n = seq_len[b];
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < S; i += gridDim.x * blockDim.x)
-    sel_idx[(size_t)b * S + i] = i < n ? i : 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0) sel_count[b] = n;
+  const int p0 = start ? min(max(start[b], 0), n) : 0;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < S; j += gridDim.x * blockDim.x)
+    sel_idx[(size_t)b * S + j] = j < n - p0 ? p0 + j : 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) sel_count[b] = n - p0;
 }
 
 // One block: exclusive prefix of sel_count (B <= 1024).
@@ -97,20 +99,41 @@ __global__ void k_rowmap(const int32_t* __restrict__ sel_idx, const int32_t* __r
 // ---------------------------------------------------------------------------
 // importance score (one wave per row)
 // ---------------------------------------------------------------------------
+// Which row a scoring wave takes: with a row map (rm_pos != nullptr) wave w of
+// block x takes packed row r = 4x + w, i.e. flat row rm_pos[r] and input row
+// x_packed[r]; otherwise position i = 4x + w of sequence blockIdx.y, input row
+// x_packed[off_all[b] + i].  Returns false when the wave has no row.
+__device__ __forceinline__ bool score_row(const int32_t* __restrict__ rm_pos, const int32_t* __restrict__ rm_n,
+                                          const int32_t* __restrict__ off_all, const int32_t* __restrict__ seq_len,
+                                          int S, size_t* row, size_t* xrow) {
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rm_pos) {
+    if (w >= *rm_n) return false;
+    *row = (size_t)rm_pos[w];
+    *xrow = (size_t)w;
+    return true;
+  }
+  const int b = blockIdx.y;
+  if (w >= seq_len[b]) return false;
+  *row = (size_t)b * S + w;
+  *xrow = off_all ? (size_t)(off_all[b] + w) : 0;
+  return true;
+}
+
 template <typename T, bool kFused>
 __global__ __launch_bounds__(256) void k_score(const T* __restrict__ h_cur, const float* __restrict__ x_packed,
-                                               const int32_t* __restrict__ off_all, T* __restrict__ h_prev,
-                                               const float* __restrict__ conf, const int32_t* __restrict__ seq_len,
-                                               int S, int d, int kind, float alpha, float* __restrict__ scores) {
+                                               const int32_t* __restrict__ off_all,
+                                               const int32_t* __restrict__ rm_pos, const int32_t* __restrict__ rm_n,
+                                               T* __restrict__ h_prev, const float* __restrict__ conf,
+                                               const int32_t* __restrict__ seq_len, int S, int d, int kind,
+                                               float alpha, float* __restrict__ scores) {
   const int lane = threadIdx.x & 63;
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int b = blockIdx.y;
-  if (i >= seq_len[b]) return;
-  const size_t row = (size_t)b * S + i;
+  size_t row, xrow;
+  if (!score_row(rm_pos, rm_n, off_all, seq_len, S, &row, &xrow)) return;
   const T* hp = h_prev + row * d;
   float l1 = 0.f, dd = 0.f, hh = 0.f, xx = 0.f, xh = 0.f;
   if constexpr (kFused) {
-    const float* xr = x_packed + (size_t)(off_all[b] + i) * d;
+    const float* xr = x_packed + xrow * d;
     T* hw = h_prev + row * d;
     for (int c = lane; c < d; c += 64) {
       const T xt = from_f32<T>(xr[c]);
@@ -160,18 +183,18 @@ __global__ __launch_bounds__(256) void k_score(const T* __restrict__ h_cur, cons
 // stores, so a row costs about two memory round trips instead of one per
 // column.  Same sums as k_score in a different summation order.
 __global__ __launch_bounds__(256) void k_score_bf16x8(const float* __restrict__ x_packed,
-                                                      const int32_t* __restrict__ off_all, bf16_t* __restrict__ h_prev,
+                                                      const int32_t* __restrict__ off_all,
+                                                      const int32_t* __restrict__ rm_pos,
+                                                      const int32_t* __restrict__ rm_n, bf16_t* __restrict__ h_prev,
                                                       const float* __restrict__ conf,
                                                       const int32_t* __restrict__ seq_len, int S, int d, int kind,
                                                       float alpha, float* __restrict__ scores) {
   constexpr int G = 4;                                // slices per load group
   const int lane = threadIdx.x & 63;
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int b = blockIdx.y;
-  if (i >= seq_len[b]) return;
-  const size_t row = (size_t)b * S + i;
+  size_t row, xrow;
+  if (!score_row(rm_pos, rm_n, off_all, seq_len, S, &row, &xrow)) return;
   uint16_t* hp = reinterpret_cast<uint16_t*>(h_prev) + row * d;
-  const float* xr = x_packed + (size_t)(off_all[b] + i) * d;
+  const float* xr = x_packed + xrow * d;
   float l1 = 0.f, dd = 0.f, hh = 0.f, xx = 0.f, xh = 0.f;
   const int n_slices = d / 512;
   for (int s0 = 0; s0 < n_slices; s0 += G) {
@@ -269,17 +292,27 @@ __device__ __forceinline__ int block_excl_scan(int v, int* buf, int* total) {
   return buf[w] + incl - v;
 }
 
+// Candidates of sequence b: positions 0..seq_len[b]-1, or with a candidate
+// list the cand_cnt[b] ascending positions cand_idx[b*S ...].  Top-k keeps
+// k = ceil(keep * base) of them, clamped to [1, base] and to the candidate
+// count, where base = k_base[b] (default: the candidate count).
 __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ scores,
                                                         const int32_t* __restrict__ seq_len, int S, int mode,
-                                                        float keep, float threshold, int32_t* __restrict__ sel_idx,
+                                                        float keep, float threshold,
+                                                        const int32_t* __restrict__ cand_idx,
+                                                        const int32_t* __restrict__ cand_cnt,
+                                                        const int32_t* __restrict__ k_base,
+                                                        int32_t* __restrict__ sel_idx,
                                                         int32_t* __restrict__ sel_count) {
   __shared__ int hist[256];
   __shared__ int scan_buf[kSelThreads / 64 + 1];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
   const int b = blockIdx.x, t = threadIdx.x;
-  const int n = seq_len[b];
+  const int n = cand_idx ? cand_cnt[b] : seq_len[b];     // candidates
   const float* sc = scores + (size_t)b * S;
+  const int32_t* cl = cand_idx ? cand_idx + (size_t)b * S : nullptr;
+  auto pos = [&](int j) { return cl ? cl[j] : j; };
   const int chunk = (n + kSelThreads - 1) / kSelThreads;
   const int i0 = min(n, t * chunk), i1 = min(n, i0 + chunk);
 
@@ -287,9 +320,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   int need_eq;
   if (mode == DL_SEL_TOPK) {
     int k = 0;
-    if (n > 0) {
-      const double kk = ceil((double)keep * (double)n);
-      k = kk < 1.0 ? 1 : (kk > (double)n ? n : (int)kk);
+    const int base = k_base ? k_base[b] : n;
+    if (base > 0 && n > 0) {
+      const double kk = ceil((double)keep * (double)base);
+      k = kk < 1.0 ? 1 : (kk > (double)base ? base : (int)kk);
+      k = min(k, n);
     }
     if (k == 0) {
       if (t == 0) sel_count[b] = 0;
@@ -307,7 +342,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
       __syncthreads();
       const uint32_t prefix = s_prefix;
       for (int i = i0; i < i1; ++i) {
-        const uint32_t key = score_key(sc[i]);
+        const uint32_t key = score_key(sc[pos(i)]);
         if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
       }
       __syncthreads();
@@ -352,12 +387,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   // in: the rank of an equal row is the number of equal rows before it.
   const bool topk = mode == DL_SEL_TOPK;
   int n_eq = 0;
-  for (int i = i0; i < i1; ++i) n_eq += score_key(sc[i]) == thr;
+  for (int i = i0; i < i1; ++i) n_eq += score_key(sc[pos(i)]) == thr;
   int tot;
   const int eq_base = block_excl_scan(n_eq, scan_buf, &tot);
   int n_sel = 0, er = eq_base;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t key = score_key(sc[i]);
+    const uint32_t key = score_key(sc[pos(i)]);
     if (key > thr) {
       ++n_sel;
     } else if (topk && key == thr) {
@@ -369,10 +404,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   int32_t* dst = sel_idx + (size_t)b * S;
   er = eq_base;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t key = score_key(sc[i]);
+    const uint32_t key = score_key(sc[pos(i)]);
     bool take = key > thr;
     if (!take && topk && key == thr) take = er++ < need_eq;
-    if (take) dst[out++] = i;
+    if (take) dst[out++] = pos(i);
   }
   if (t == 0) sel_count[b] = tot;
 }
@@ -395,7 +430,8 @@ __global__ __launch_bounds__(kRowThreads) void k_embed(const int32_t* __restrict
 // 16-byte granular copy when the row width allows it, else element-wise.
 template <int kBytes>
 __global__ __launch_bounds__(kRowThreads) void k_gather(const char* __restrict__ src,
-                                                        const int32_t* __restrict__ src_off, int S, size_t row_bytes,
+                                                        const int32_t* __restrict__ src_off,
+                                                        const int32_t* __restrict__ src_inv, int S, size_t row_bytes,
                                                         const int32_t* __restrict__ row_pos,
                                                         const int32_t* __restrict__ row_seq,
                                                         char* __restrict__ dst) {
@@ -403,7 +439,11 @@ __global__ __launch_bounds__(kRowThreads) void k_gather(const char* __restrict__
   const int p = row_pos[r];
   if (p < 0) return;
   size_t srow = (size_t)p;
-  if (src_off) {
+  if (src_inv) {
+    const int q = src_inv[p];
+    if (q < 0) return;
+    srow = (size_t)q;
+  } else if (src_off) {
     const int b = row_seq[r];
     srow = (size_t)src_off[b] + (size_t)(p - b * S);
   }
@@ -759,6 +799,19 @@ __global__ void k_fill_i32(int32_t* __restrict__ p, int32_t v, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+// inv[row_pos[r]] = r for the packed rows of a row map
+__global__ void k_inv_rows(const int32_t* __restrict__ row_pos, const int32_t* __restrict__ n_rows, int R_max,
+                           int32_t* __restrict__ inv) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < R_max && r < *n_rows) inv[row_pos[r]] = r;
+}
+
+// v at the valid positions of every sequence ([B, S] array)
+__global__ void k_fill_valid(float* __restrict__ p, float v, const int32_t* __restrict__ seq_len, int S) {
+  const int b = blockIdx.y, i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < seq_len[b]) p[(size_t)b * S + i] = v;
+}
+
 // ---------------------------------------------------------------------------
 // unmask: rank each masked candidate of the block by (conf desc, index asc)
 // ---------------------------------------------------------------------------
@@ -801,9 +854,9 @@ inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 // launchers
 // ===========================================================================
 hipError_t launch_identity_sel(const int32_t* seq_len, int B, int S, int32_t* sel_idx, int32_t* sel_count,
-                               hipStream_t st) {
+                               hipStream_t st, const int32_t* start) {
   dim3 grid(cdiv(S, 256), B);
-  hipLaunchKernelGGL(k_identity_sel, grid, dim3(256), 0, st, seq_len, S, sel_idx, sel_count);
+  hipLaunchKernelGGL(k_identity_sel, grid, dim3(256), 0, st, seq_len, start, S, sel_idx, sel_count);
   return hipGetLastError();
 }
 
@@ -849,33 +902,37 @@ hipError_t launch_scatter_sel(size_t elem_bytes, const void* rows, int w, const 
 
 hipError_t launch_score(dl_dtype dt, const void* h_cur, const float* x_packed, const int32_t* off_all, void* h_prev,
                         const float* conf, const int32_t* seq_len, int B, int S, int d, dl_score_kind kind,
-                        float alpha, float* scores, hipStream_t st) {
-  dim3 grid(cdiv(S, 4), B);
+                        float alpha, float* scores, hipStream_t st, const RowMap* rm) {
+  const int32_t* rp = rm ? rm->row_pos : nullptr;
+  const int32_t* rn = rm ? rm->n_rows : nullptr;
+  if (rm && (!x_packed || rm->R_max <= 0)) return rm->R_max <= 0 ? hipSuccess : hipErrorInvalidValue;
+  dim3 grid = rm ? dim3(cdiv(rm->R_max, 4)) : dim3(cdiv(S, 4), B);
   if (dt == DL_F32) {
     if (x_packed)
-      hipLaunchKernelGGL((k_score<float, true>), grid, dim3(256), 0, st, (const float*)h_cur, x_packed, off_all,
-                         (float*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
+      hipLaunchKernelGGL((k_score<float, true>), grid, dim3(256), 0, st, (const float*)h_cur, x_packed, off_all, rp,
+                         rn, (float*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
     else
-      hipLaunchKernelGGL((k_score<float, false>), grid, dim3(256), 0, st, (const float*)h_cur, x_packed, off_all,
-                         (float*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
+      hipLaunchKernelGGL((k_score<float, false>), grid, dim3(256), 0, st, (const float*)h_cur, x_packed, off_all, rp,
+                         rn, (float*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
   } else {
     if (x_packed && d % 512 == 0)
-      hipLaunchKernelGGL(k_score_bf16x8, grid, dim3(256), 0, st, x_packed, off_all, (bf16_t*)h_prev, conf, seq_len,
-                         S, d, (int)kind, alpha, scores);
+      hipLaunchKernelGGL(k_score_bf16x8, grid, dim3(256), 0, st, x_packed, off_all, rp, rn, (bf16_t*)h_prev, conf,
+                         seq_len, S, d, (int)kind, alpha, scores);
     else if (x_packed)
-      hipLaunchKernelGGL((k_score<bf16_t, true>), grid, dim3(256), 0, st, (const bf16_t*)h_cur, x_packed, off_all,
-                         (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
+      hipLaunchKernelGGL((k_score<bf16_t, true>), grid, dim3(256), 0, st, (const bf16_t*)h_cur, x_packed, off_all, rp,
+                         rn, (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
     else
       hipLaunchKernelGGL((k_score<bf16_t, false>), grid, dim3(256), 0, st, (const bf16_t*)h_cur, x_packed, off_all,
-                         (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
+                         rp, rn, (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_select(const float* scores, const int32_t* seq_len, int B, int S, dl_select_mode mode, float keep,
-                         float threshold, int32_t* sel_idx, int32_t* sel_count, hipStream_t st) {
+                         float threshold, int32_t* sel_idx, int32_t* sel_count, hipStream_t st,
+                         const int32_t* cand_idx, const int32_t* cand_cnt, const int32_t* k_base) {
   hipLaunchKernelGGL(k_select, dim3(B), dim3(kSelThreads), 0, st, scores, seq_len, S, (int)mode, keep, threshold,
-                     sel_idx, sel_count);
+                     cand_idx, cand_cnt, k_base, sel_idx, sel_count);
   return hipGetLastError();
 }
 
@@ -891,14 +948,27 @@ hipError_t launch_embed(dl_dtype dt, const int32_t* tokens, const RowMap& rm, co
 }
 
 hipError_t launch_gather(size_t elem_bytes, const void* src, const int32_t* src_off, int S, int w, const RowMap& rm,
-                         void* dst, hipStream_t st) {
+                         void* dst, hipStream_t st, const int32_t* src_inv) {
+  if (rm.R_max <= 0) return hipSuccess;
   const size_t rb = elem_bytes * (size_t)w;
   if (rb % 16 == 0)
-    hipLaunchKernelGGL(k_gather<16>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)src, src_off, S, rb,
-                       rm.row_pos, rm.row_seq, (char*)dst);
+    hipLaunchKernelGGL(k_gather<16>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)src, src_off, src_inv, S,
+                       rb, rm.row_pos, rm.row_seq, (char*)dst);
   else
-    hipLaunchKernelGGL(k_gather<1>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)src, src_off, S, rb,
-                       rm.row_pos, rm.row_seq, (char*)dst);
+    hipLaunchKernelGGL(k_gather<1>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)src, src_off, src_inv, S,
+                       rb, rm.row_pos, rm.row_seq, (char*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_inv_rows(const RowMap& rm, int BS, int32_t* inv, hipStream_t st) {
+  hipLaunchKernelGGL(k_fill_i32, dim3(cdiv(BS, 256)), dim3(256), 0, st, inv, -1, (size_t)BS);
+  if (rm.R_max > 0)
+    hipLaunchKernelGGL(k_inv_rows, dim3(cdiv(rm.R_max, 256)), dim3(256), 0, st, rm.row_pos, rm.n_rows, rm.R_max, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_scores(float* scores, float v, const int32_t* seq_len, int B, int S, hipStream_t st) {
+  hipLaunchKernelGGL(k_fill_valid, dim3(cdiv(S, 256), B), dim3(256), 0, st, scores, v, seq_len, S);
   return hipGetLastError();
 }
 

@@ -6,8 +6,9 @@
 namespace dtsk {
 
 // ---- selections and row maps ------------------------------------------------
+// Positions [start[b], seq_len[b]) of each sequence (start == nullptr: from 0).
 hipError_t launch_identity_sel(const int32_t* seq_len, int B, int S, int32_t* sel_idx, int32_t* sel_count,
-                               hipStream_t st);
+                               hipStream_t st, const int32_t* start = nullptr);
 // row_off = exclusive prefix of sel_count.
 hipError_t launch_row_off(const int32_t* sel_count, int32_t* row_off, int B, hipStream_t st);
 // Packed-row maps and attention query tiles of a selection with row_off set.
@@ -24,19 +25,34 @@ hipError_t launch_scatter_sel(size_t elem_bytes, const void* rows, int w, const 
 // Score of each valid row.  If x_packed != nullptr, the current input is the
 // fp32 packed row x_packed[off_all[b] + i] rounded to the storage type, and
 // h_prev is overwritten with it after scoring (one pass); otherwise h_cur is read.
+// With a row map, only its packed rows are scored: input x_packed[r], flat row
+// rm->row_pos[r] of scores and h_prev.
 hipError_t launch_score(dl_dtype dt, const void* h_cur, const float* x_packed, const int32_t* off_all, void* h_prev,
                         const float* conf, const int32_t* seq_len, int B, int S, int d, dl_score_kind kind,
-                        float alpha, float* scores, hipStream_t st);
+                        float alpha, float* scores, hipStream_t st, const RowMap* rm = nullptr);
+// Selection among every valid row, or among the candidate lists (cand_idx,
+// cand_cnt: ascending positions per sequence, a selection's layout); top-k
+// keeps ceil(keep * k_base[b]) (default base: the candidate count), at most
+// the candidate count.  sel_idx must not alias cand_idx.
 hipError_t launch_select(const float* scores, const int32_t* seq_len, int B, int S, dl_select_mode mode, float keep,
-                         float threshold, int32_t* sel_idx, int32_t* sel_count, hipStream_t st);
+                         float threshold, int32_t* sel_idx, int32_t* sel_count, hipStream_t st,
+                         const int32_t* cand_idx = nullptr, const int32_t* cand_cnt = nullptr,
+                         const int32_t* k_base = nullptr);
+// v at positions [0, seq_len[b]) of a [B, S] array.
+hipError_t launch_fill_scores(float* scores, float v, const int32_t* seq_len, int B, int S, hipStream_t st);
 
 // ---- row movement -------------------------------------------------------------
 hipError_t launch_embed(dl_dtype dt, const int32_t* tokens, const RowMap& rm, const void* E, int d, float* x,
                         hipStream_t st);
-// dst[r] = src[src_row(r)]: src_row = off[row_seq] + (row_pos - row_seq*S) when
-// src_off != nullptr (packed source) else row_pos (padded [B,S,w] source).
+// dst[r] = src[src_row(r)]: src_row = src_inv[row_pos] when src_inv != nullptr
+// (rows whose entry is negative are left alone), else off[row_seq] +
+// (row_pos - row_seq*S) when src_off != nullptr (packed source), else row_pos
+// (padded [B,S,w] source).
 hipError_t launch_gather(size_t elem_bytes, const void* src, const int32_t* src_off, int S, int w, const RowMap& rm,
-                         void* dst, hipStream_t st);
+                         void* dst, hipStream_t st, const int32_t* src_inv = nullptr);
+// inv[p] = the packed row of flat position p in the row map, -1 for positions
+// outside it (inv has BS = B*S entries).
+hipError_t launch_inv_rows(const RowMap& rm, int BS, int32_t* inv, hipStream_t st);
 // cache[row_pos[r]] = rows[r] (same type)
 hipError_t launch_scatter(size_t elem_bytes, const void* rows, int w, const RowMap& rm, void* cache, hipStream_t st);
 // dst[row_pos[r]] = T(x[r]) for fp32 rows x

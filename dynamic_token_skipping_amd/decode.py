@@ -46,6 +46,12 @@ def is_refresh_step(step: int, steps_per_block: int, refresh_interval: int) -> b
     return sib == 0 or (refresh_interval > 0 and sib % refresh_interval == 0)
 
 
+def is_full_context_step(step: int, steps_per_block: int, response_interval: int) -> bool:
+    """DyLLM response-only strategy: with an interval N > 0 only every N-th
+    in-block step takes the prompt rows too."""
+    return response_interval <= 0 or (step % steps_per_block) % response_interval == 0
+
+
 class Decoder:
     """Caches of a batch of sequences: prompt + gen_len masked positions each,
     right-padded to S = max length."""
@@ -81,14 +87,20 @@ class Decoder:
         self.scores = torch.zeros((B, S), dtype=torch.float32, device=device)
         self.logits = torch.zeros((B, S, model.vocab), dtype=torch.float32, device=device) if keep_logits else None
         self.sel = L.SelectionTensors(B, S, device)
+        two = getattr(sched, "skip_layer2", 0) > 0
+        self.h_prev2 = torch.zeros((B, S, d), dtype=tdt, device=device) if two else None
+        self.scores2 = torch.zeros((B, S), dtype=torch.float32, device=device) if two else None
+        self.sel2 = L.SelectionTensors(B, S, device) if two else None
         self.dims = model.dims(B, S)
         self.model_struct = model.struct(B, S)
         self.ws = L.workspace(self.dims, sum(self.seq_lens), device)
         self._seq_len_host = (ctypes.c_int32 * B)(*self.seq_lens)
+        self._prompt_len_host = (ctypes.c_int32 * B)(*self.prompt_lens)
         self.state = L.State(L.ptr(self.tokens), L.ptr(self.masked), L.ptr(self.seq_len), L.ptr(self.prompt_len),
                              L.ptr(self.h_prev), L.ptr(self.k_cache), L.ptr(self.v_cache), L.ptr(self.h_final),
                              L.ptr(self.conf), L.ptr(self.argmax), L.ptr(self.logits), L.ptr(self.scores),
-                             self.sel.struct())
+                             self.sel.struct(), L.ptr(self.h_prev2), L.ptr(self.scores2),
+                             self.sel2.struct() if two else L.Selection())
         self.steps_per_block = sched.steps // (sched.gen_len // sched.block_len)
         self.per_step = sched.block_len // self.steps_per_block
 
@@ -98,14 +110,22 @@ class Decoder:
         self.masked.copy_(self.masked0)
 
     def params(self, step: int, force_refresh: Optional[bool] = None, keep: Optional[float] = None,
-               mode: int = L.DL_SEL_TOPK, threshold: float = 0.0, n_unmask: Optional[int] = None) -> L.StepParams:
+               mode: int = L.DL_SEL_TOPK, threshold: float = 0.0, n_unmask: Optional[int] = None,
+               response_only: Optional[bool] = None, keep2: Optional[float] = None, mode2: int = L.DL_SEL_TOPK,
+               threshold2: float = 0.0) -> L.StepParams:
         s = self.sched
         refresh = (is_refresh_step(step, self.steps_per_block, s.refresh_interval) if force_refresh is None
                    else force_refresh)
+        if response_only is None:
+            response_only = not is_full_context_step(step, self.steps_per_block, getattr(s, "response_interval", 0))
+        s2 = getattr(s, "skip_layer2", 0)
         return L.StepParams(step // self.steps_per_block, s.block_len,
                             self.per_step if n_unmask is None else n_unmask, s.skip_layer, int(bool(refresh)),
                             L.SCORE_KINDS[s.score], s.alpha, mode, s.keep if keep is None else keep, threshold,
-                            ctypes.cast(self._seq_len_host, ctypes.POINTER(ctypes.c_int32)))
+                            ctypes.cast(self._seq_len_host, ctypes.POINTER(ctypes.c_int32)),
+                            int(bool(response_only) and not refresh),
+                            ctypes.cast(self._prompt_len_host, ctypes.POINTER(ctypes.c_int32)), s2, mode2,
+                            getattr(s, "keep2", 1.0) if keep2 is None else keep2, threshold2)
 
     def step(self, step: int, **kw):
         L.dl_denoise_step(self.model_struct, self.state, self.params(step, **kw), self.ws)

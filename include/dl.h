@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DL_ABI_VERSION 1
+#define DL_ABI_VERSION 2
 
 typedef enum {
   DL_OK = 0,
@@ -126,8 +126,13 @@ typedef struct {
   float *conf;                /* [B, S] max softmax probability */
   int32_t *argmax;            /* [B, S] most likely id (lowest id on ties) */
   float *logits;              /* [B, S, vocab] fp32, or NULL to skip writing them */
-  float *scores;              /* [B, S] this step's scores, or NULL */
+  float *scores;              /* [B, S] this step's scores, or NULL (-inf for rows that were
+                                 not candidates: prompt rows of a response-only step) */
   dl_selection sel;           /* this step's recomputed rows (written by the step) */
+  /* second skip level (used when params.skip_layer2 > 0; may be NULL otherwise) */
+  void *h_prev2;              /* [B, S, d] input of layer skip_layer2 as last computed */
+  float *scores2;             /* [B, S] second-level scores (-inf outside sel), or NULL */
+  dl_selection sel2;          /* rows recomputed in layers [skip_layer2, L) and the LM head */
 } dl_state;
 
 typedef struct {
@@ -142,6 +147,26 @@ typedef struct {
   float keep_ratio;           /* in (0, 1] for DL_SEL_TOPK */
   float threshold;            /* for DL_SEL_THRESHOLD */
   const int32_t *seq_len_host;/* [B] HOST copy of state.seq_len, used for grid sizing only */
+  /* DyLLM response-only step (technical summary section 2B, strategy 3): on a
+   * skip step, only positions [prompt_len[b], seq_len[b]) go through layers
+   * [0, s), are scored and can be kept, and keep_ratio applies to their count;
+   * prompt rows keep every cache.  Ignored on a refresh step. */
+  int32_t response_only;
+  const int32_t *prompt_len_host; /* [B] HOST copy of state.prompt_len (response_only only) */
+  /* Second skip level (ES-dLLM technical summary section 2B: skipping at two
+   * early layers with a skip ratio per layer).  0: one level.  Otherwise
+   * skip_layer < skip_layer2 <= n_layers: the rows in sel go through layers
+   * [s, s2); at the input of s2 they are scored against state.h_prev2 (same
+   * score kind and cached confidence) and h_prev2 is rewritten for them; the
+   * DL_SEL_TOPK level keeps ceil(keep_ratio2 * count) of them, count being
+   * what keep_ratio applies to, at most as many as sel holds (keep_ratio2 <=
+   * keep_ratio when the first level is also DL_SEL_TOPK); only those go
+   * through [s2, L) and the LM head.  A refresh step rewrites h_prev2 for
+   * every row. */
+  int32_t skip_layer2;
+  dl_select_mode mode2;
+  float keep_ratio2;
+  float threshold2;
 } dl_step_params;
 
 /* ---------------------------------------------------------------------------
@@ -202,12 +227,17 @@ dl_status dl_unmask(const dl_dims *dims, int32_t *tokens, uint8_t *masked, const
                     const int32_t *argmax, const int32_t *prompt_len, const int32_t *seq_len, int32_t block,
                     int32_t block_len, int32_t n_unmask, void *stream);
 
-/* One whole denoising step: embed; layers [0, s) on every valid row; then
- *   refresh: layers [s, L) on every row, h_prev <- layer-s input of every row;
- *   skip:    score every row against h_prev, h_prev <- layer-s input of every
- *            row, select, layers [s, L) on the selected rows only;
+/* One whole denoising step: embed; layers [0, s) on every valid row (on the
+ * response rows only on a response-only step); then
+ *   refresh: layers [s, L) on every row, h_prev <- layer-s input of every row
+ *            (and h_prev2 <- layer-s2 input of every row with two levels);
+ *   skip:    score the candidate rows against h_prev, h_prev <- their layer-s
+ *            input, select, layers [s, L) on the selected rows only (with two
+ *            levels: [s, s2) on sel, second score and selection, [s2, L) on
+ *            sel2);
  * LM head + scatter for the rows that went through every layer; unmask.
- * state->sel receives the selection (all rows on a refresh step). */
+ * state->sel receives the selection (all rows on a refresh step), and
+ * state->sel2 the second-level selection when there is one. */
 dl_status dl_denoise_step(const dl_model *model, dl_state *state, const dl_step_params *params, void *ws,
                           size_t ws_bytes, void *stream);
 

@@ -86,3 +86,5 @@ def sync_from_oracle(dec, b: int, st) -> None:
         put(dec.v_cache[li, b, :n], st.V[li].astype(np.float32), dt)
     if dec.logits is not None and st.logits is not None:
         put(dec.logits[b, :n], st.logits.astype(np.float32))
+    if getattr(dec, "h_prev2", None) is not None and st.h_prev2 is not None:
+        put(dec.h_prev2[b, :n], st.h_prev2.astype(np.float32), dt)

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.dl_abi_version() == 1
+    assert lib.dl_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -98,3 +98,44 @@ def test_step_validation(lib):
     assert lib.dl_denoise_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(p), 16, 64, None) == -5
     p.block_len = 4096
     assert lib.dl_denoise_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(p), 16, 1 << 40, None) == -7
+
+
+def test_step_validation_two_levels_and_response_only(lib):
+    d = _dims(n_layers=4)
+    lw = (L.LayerW * 4)(*[L.LayerW(*([16] * 9)) for _ in range(4)])
+    m = L.Model(d, 16, 16, 16, lw)
+    lens = (ctypes.c_int32 * 1)(512)
+    plen = (ctypes.c_int32 * 1)(256)
+
+    def state(h_prev2=48, sel2=(64, 64, 64)):
+        return L.State(16, 16, 16, 16, 16, 16, 16, 16, 16, 16, None, None, L.Selection(16, 16, 16), h_prev2, None,
+                       L.Selection(*sel2))
+
+    def params(**kw):
+        p = L.StepParams(0, 32, 1, 1, 0, 0, 0.5, 0, 0.5, 0.0, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)),
+                         0, ctypes.cast(plen, ctypes.POINTER(ctypes.c_int32)), 2, 0, 0.25, 0.0)
+        for k, v in kw.items():
+            setattr(p, k, v)
+        return p
+
+    def run(st, p, ws_bytes=1 << 40):
+        return lib.dl_denoise_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(p), 16, ws_bytes, None)
+
+    assert run(state(), params(), 64) == -5                      # valid up to the workspace size
+    assert run(state(), params(skip_layer2=1)) == -1             # s2 must exceed s
+    assert b"skip_layer2" in lib.dl_last_error()
+    assert run(state(), params(skip_layer2=5)) == -1             # beyond n_layers
+    assert run(state(), params(keep_ratio2=0.75)) == -1          # keeps more than the first level
+    assert run(state(), params(keep_ratio2=0.0)) == -1
+    assert run(state(), params(mode2=7)) == -1
+    assert run(state(h_prev2=None), params()) == -1              # h_prev2 needed with two levels
+    assert run(state(h_prev2=16), params()) == -1                # aliases h_prev
+    assert run(state(sel2=(16, 64, 64)), params()) == -1         # sel2 aliases sel
+    assert b"alias" in lib.dl_last_error()
+    assert run(state(h_prev2=None), params(skip_layer2=0), 64) == -5   # one level: h_prev2 unused
+    p = params(skip_layer2=0, response_only=1, prompt_len_host=None)
+    assert run(state(), p) == -1                                 # response-only needs host prompt lengths
+    plen[0] = 600
+    assert run(state(), params(skip_layer2=0, response_only=1)) == -2
+    plen[0] = 256
+    assert run(state(), params(skip_layer2=0, response_only=1), 64) == -5

@@ -1,0 +1,181 @@
+"""GPU parity of the two-level nested skip (ES-dLLM section 2B: skipping at two
+early layers with a ratio per layer) and of DyLLM's response-only steps
+(section 2B, strategy 3) against the oracle, on a ragged batch of 3 sequences,
+plus their invariants at the full 8B-class shape."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import host, np_model, row_rel_err, selection_diff_ok, sync_from_oracle, to_device
+from oracle import esdllm as E
+
+pytestmark = pytest.mark.gpu
+
+DIMS = workloads.ModelDims(d=256, n_heads=2, head_dim=128, d_ffn=512, vocab=1024, n_layers=3)
+BASE = workloads.Schedule(gen_len=32, block_len=16, steps=8, skip_layer=1, keep=0.5, score="esdllm")
+NESTED = dataclasses.replace(BASE, skip_layer2=2, keep2=0.25)
+RESP = dataclasses.replace(BASE, response_interval=2)
+BOTH = dataclasses.replace(NESTED, response_interval=2)
+NESTED_LAST = dataclasses.replace(BASE, skip_layer2=3, keep2=0.25)    # second level feeds the LM head only
+PROMPTS = (9, 45, 96)
+
+
+def _setup(dtype, sched, seed=23):
+    from dynamic_token_skipping_amd import Decoder, DeviceModel
+    m_cpu = workloads.make_model(DIMS, seed, dtype, "cpu")
+    g = torch.Generator().manual_seed(seed)
+    prompts = [torch.randint(0, DIMS.vocab, (n,), generator=g) for n in PROMPTS]
+    dec = Decoder(DeviceModel(to_device(m_cpu), DIMS.n_heads, DIMS.head_dim, dtype), prompts, sched,
+                  keep_logits=True)
+    sts = [E.init_state(p.numpy(), sched.gen_len, DIMS, keep_logits=True) for p in prompts]
+    return np_model(m_cpu), dec, sts
+
+
+def _scores_ok(g, o, tol):
+    cand = np.isfinite(o)
+    if not np.array_equal(np.isfinite(g), cand):
+        return False
+    return np.abs(g[cand] - o[cand]).max(initial=0.0) <= tol * max(1.0, np.abs(o[cand]).max(initial=0.0))
+
+
+@pytest.mark.parametrize("dtype,tol", [("f32", 1e-5), ("bf16", 2e-2)])
+@pytest.mark.parametrize("sched", [NESTED, RESP, BOTH, NESTED_LAST], ids=["nested", "resp", "both", "nested_last"])
+def test_decode_matches_oracle(dtype, tol, sched):
+    m_np, dec, sts = _setup(dtype, sched)
+    two = sched.skip_layer2 > 0
+    s_tol = 1e-5 if dtype == "f32" else 1e-2
+    exact_steps = 0
+    kinds = set()
+    for t in range(sched.steps):
+        if dtype == "bf16":
+            for b, st in enumerate(sts):
+                sync_from_oracle(dec, b, st)
+        infos = [E.denoise_step(m_np, DIMS, st, t, sched) for st in sts]
+        dec.step(t)
+        torch.cuda.synchronize()
+        g1 = dec.sel.rows()
+        g2 = dec.sel2.rows() if two else g1
+        same = True
+        for b, (st, info) in enumerate(zip(sts, infos)):
+            n = len(st.tokens)
+            kinds.add("R" if info.refresh else ("r" if info.response_only else "F"))
+            o1 = info.selected
+            o2 = info.selected2 if two else o1
+            if info.refresh:
+                assert g1[b] == list(range(n)) and g2[b] == list(range(n)), (t, b)
+            else:
+                assert _scores_ok(host(dec.scores[b, :n]), info.scores, s_tol), (t, b)
+                n_cand = int(np.isfinite(info.scores).sum())
+                ok, nd = selection_diff_ok(g1[b], o1, info.scores, E.keep_count(sched.keep, n_cand), 1e-4,
+                                           0.0 if dtype == "f32" else 2e-2)
+                assert ok, (t, b, "level 1")
+                if nd:
+                    same = False
+                    continue
+                assert g1[b] == o1.tolist(), (t, b)
+                if two:
+                    assert _scores_ok(host(dec.scores2[b, :n]), info.scores2, s_tol), (t, b)
+                    assert set(g2[b]) <= set(g1[b])
+                    k2 = E.level2_count(sched.keep2, n_cand, len(o1))
+                    ok, nd = selection_diff_ok(g2[b], o2, info.scores2, k2, 1e-4, 0.0 if dtype == "f32" else 2e-2)
+                    assert ok, (t, b, "level 2")
+                    if nd:
+                        same = False
+                        continue
+                    assert g2[b] == o2.tolist(), (t, b)
+            rows = np.asarray(o2)
+            assert row_rel_err(host(dec.h_prev[b, :n]), st.h_prev) <= tol, (t, b)
+            if two:
+                assert row_rel_err(host(dec.h_prev2[b, :n]), st.h_prev2) <= tol, (t, b)
+            assert row_rel_err(host(dec.h_final[b, :n])[rows], st.h_final[rows]) <= tol, (t, b)
+            assert row_rel_err(host(dec.logits[b, :n])[rows], st.logits[rows]) <= tol, (t, b)
+            for li in range(DIMS.n_layers):
+                assert row_rel_err(host(dec.k_cache[li, b, :n]), st.K[li]) <= tol, (t, b, li)
+                assert row_rel_err(host(dec.v_cache[li, b, :n]), st.V[li]) <= tol, (t, b, li)
+            if dtype == "f32":
+                assert np.array_equal(dec.tokens[b, :n].cpu().numpy(), st.tokens), (t, b)
+        exact_steps += same
+    if dtype == "f32":
+        assert exact_steps == sched.steps
+    if sched.response_interval:
+        assert kinds == {"R", "r", "F"}
+
+
+def test_second_level_threshold_mode():
+    """Threshold at the second level: exactly the first-level rows whose
+    second score exceeds tau (here every one of them, then none)."""
+    import dynamic_token_skipping_amd as D
+    m_np, dec, sts = _setup("bf16", NESTED)
+    dec.step(0)
+    dec.step(1, mode2=D.DL_SEL_THRESHOLD, threshold2=-1e30)
+    torch.cuda.synchronize()
+    assert dec.sel2.rows() == dec.sel.rows()
+    dec.step(2, mode2=D.DL_SEL_THRESHOLD, threshold2=1e30)
+    torch.cuda.synchronize()
+    assert [len(r) for r in dec.sel2.rows()] == [0, 0, 0]
+    assert all(len(r) > 0 for r in dec.sel.rows())
+
+
+# ---------------------------------------------------------------------------
+# full 8B-class shape: invariants of a nested and of a response-only step
+# ---------------------------------------------------------------------------
+def _decoder8b(sched):
+    from dynamic_token_skipping_amd import Decoder, DeviceModel
+    wl = workloads.workload("full8b")
+    model = workloads.make_model(wl.dims, wl.seed, wl.dtype, "cuda")
+    prompts, _ = workloads.make_prompt(wl)
+    return wl, model, Decoder(DeviceModel(model, wl.dims.n_heads, wl.dims.head_dim, wl.dtype), prompts, sched)
+
+
+def _topk_ok(scores, rows, k):
+    order = np.lexsort((np.arange(len(scores)), -scores))
+    return sorted(order[:k].tolist()) == rows
+
+
+def test_full8b_nested_and_response_only_steps():
+    wl = workloads.workload("full8b")
+    sched = dataclasses.replace(wl.sched, keep=0.5, skip_layer2=8, keep2=0.25, response_interval=2)
+    _, model, dec = _decoder8b(sched)
+    n, P = dec.seq_lens[0], dec.prompt_lens[0]
+    dec.step(0)
+    torch.cuda.synchronize()
+    for t in (1, 2, 3):
+        before = {k: getattr(dec, k).clone() for k in ("conf", "argmax", "h_final", "h_prev", "h_prev2")}
+        kb, vb = dec.k_cache.clone(), dec.v_cache.clone()
+        dec.step(t)
+        torch.cuda.synchronize()
+        resp = t % 2 == 1
+        n_cand = n - P if resp else n
+        lo = P if resp else 0
+        R1, R2 = dec.sel.rows()[0], dec.sel2.rows()[0]
+        k1 = E.keep_count(sched.keep, n_cand)
+        assert len(R1) == k1 and min(R1) >= lo
+        sc = host(dec.scores[0, :n]).astype(np.float32)
+        assert np.all(np.isneginf(sc[:lo])) and np.all(np.isfinite(sc[lo:]))
+        assert _topk_ok(sc[lo:], [r - lo for r in R1], k1)
+        k2 = E.level2_count(sched.keep2, n_cand, k1)
+        assert len(R2) == k2 and set(R2) <= set(R1)
+        sc2 = host(dec.scores2[0, :n]).astype(np.float32)
+        assert np.all(np.isfinite(sc2[R1])) and int(np.isfinite(sc2).sum()) == k1
+        assert _topk_ok(sc2[R1], [R1.index(r) for r in R2], k2)
+        out1 = torch.ones(dec.S, dtype=torch.bool, device="cuda")
+        out1[torch.as_tensor(R1, device="cuda")] = False
+        out2 = torch.ones(dec.S, dtype=torch.bool, device="cuda")
+        out2[torch.as_tensor(R2, device="cuda")] = False
+        for name in ("conf", "argmax", "h_final"):
+            assert torch.equal(getattr(dec, name)[0][out2], before[name][0][out2]), (t, name)
+        assert torch.equal(dec.h_prev2[0][out1], before["h_prev2"][0][out1])
+        if resp:
+            assert torch.equal(dec.h_prev[0, :P], before["h_prev"][0, :P])
+            assert torch.equal(dec.k_cache[:, 0, :P], kb[:, 0, :P]) and torch.equal(dec.v_cache[:, 0, :P], vb[:, 0, :P])
+        for li in range(sched.skip_layer, sched.skip_layer2):
+            assert torch.equal(dec.k_cache[li, 0][out1], kb[li, 0][out1]), (t, li)
+        for li in range(sched.skip_layer2, wl.dims.n_layers):
+            assert torch.equal(dec.k_cache[li, 0][out2], kb[li, 0][out2]), (t, li)
+            assert torch.equal(dec.v_cache[li, 0][out2], vb[li, 0][out2]), (t, li)
+    del model, dec
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
