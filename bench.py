@@ -8,9 +8,11 @@ A step is one dl_denoise_step (embed, 4 full-row layers, score + top-k,
 28 partial layers on the kept rows, LM head + confidence, unmask; every 32nd
 step is a full refresh).  Inputs are resident in HBM before the timed region.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-variants]
 
-Prints one JSON line.
+Prints one JSON line.  After the timed headline steps it also times, on the
+same model and prompt, the nested two-level skip and the response-only
+schedule ("variants"; their own steps/s, not part of `value`).
 """
 from __future__ import annotations
 
@@ -36,7 +38,53 @@ def parse():
     ap.add_argument("--workload", default="full8b")
     ap.add_argument("--timing-stride", type=int, default=8,
                     help="time about one launch in this many of each kernel class (1: every launch)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the nested-skip and response-only variant timings")
     return ap.parse_args()
+
+
+def variant_schedules(sched):
+    """Schedules of the method's variants timed beside the headline step on the
+    same model and prompt: a second skip level at layer 8 (keep 50% at layer 4,
+    25% at layer 8; ES-dLLM section 2B) and DyLLM's response-only steps with a
+    full-context step every 4 steps (section 2B, strategy 3)."""
+    import dataclasses
+    return {
+        "nested_s4_keep0.5_s8_keep0.25": dataclasses.replace(sched, keep=0.5, skip_layer2=8, keep2=0.25),
+        "response_only_full_every4": dataclasses.replace(sched, response_interval=4),
+    }
+
+
+def time_variant(torch, Decoder, dev_model, prompts, sched, steps: int, warmup: int):
+    """steps/s of one variant schedule (fresh caches; warm-up, then `steps`
+    steps from the decode's first step, refresh steps included)."""
+    dec = Decoder(dev_model, prompts, sched)
+    for t in range(warmup):
+        dec.step(t % sched.steps)
+    dec.reset()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        t = i % sched.steps
+        if t == 0 and i > 0:
+            dec.reset()
+        dec.step(t)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    kinds = {"refresh": 0, "response_only": 0, "full_context": 0}
+    for i in range(steps):
+        t = i % sched.steps
+        p = dec.params(t)
+        kinds["refresh" if p.full_refresh else ("response_only" if p.response_only else "full_context")] += 1
+    out = {"steps_per_s": round(steps / (ms / 1e3), 3), "ms_per_step": round(ms / steps, 4),
+           "gen_tokens_per_s": round(steps / (ms / 1e3) * dec.per_step * dec.B, 3), "steps": steps,
+           "step_kinds": kinds, "keep": sched.keep, "skip_layer": sched.skip_layer,
+           "skip_layer2": sched.skip_layer2, "keep2": sched.keep2, "response_interval": sched.response_interval}
+    del dec
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(wl, model_gpu, prompts, budget_s: float = 20.0):
@@ -224,6 +272,12 @@ def main():
         "copy_probe": copy,
         "wall_s": round(wall, 3),
     }
+    if not args.no_variants and wl.name == "full8b":
+        dev_model = dec.m
+        del dec
+        torch.cuda.empty_cache()
+        out["variants"] = {name: time_variant(torch, Decoder, dev_model, prompts, vs, min(args.steps, 128), 8)
+                           for name, vs in variant_schedules(sched).items()}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, model, prompts)
     else:
