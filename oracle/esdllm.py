@@ -48,6 +48,10 @@ function that uses it):
   and keeps k2 = ceil(keep2 * |S|) of them (|S| as for the first level, capped
   at the first level's count).  H2 is rewritten for every row on a refresh
   step and for the first level's rows on a skip step.
+* Keys or values as the varied tensor (ES-dLLM section 2A allows hidden
+  states, keys or values): H is then the key (rotated, as cached) or value row
+  of layer s, computed from X_s for every candidate row; h_prev holds its
+  previous value instead of the hidden state.
 * Response-only steps (DyLLM section 2B, strategy 3): on a skip step that is
   not a full-context step, only the response rows (positions >= prompt length)
   go through the prefix layers, are scored and can be kept; |S| is then the
@@ -67,7 +71,7 @@ __all__ = [
     "rms_norm", "rope", "attention", "silu", "layer_forward", "lm_logits",
     "conf_argmax", "score_rows", "keep_count", "select_topk", "select_threshold",
     "unmask", "SeqState", "init_state", "denoise_step", "decode",
-    "is_refresh_step", "is_full_context_step", "candidate_rows", "level2_count", "FLT_MIN",
+    "is_refresh_step", "is_full_context_step", "candidate_rows", "level2_count", "scored_tensor", "FLT_MIN",
 ]
 
 F64 = np.float64
@@ -268,7 +272,7 @@ class SeqState:
     prompt_len: int
     conf: np.ndarray              # [n] fp64, max softmax probability
     argmax: np.ndarray            # [n] int64
-    h_prev: np.ndarray            # [n, d] skip-layer input of the previous step
+    h_prev: np.ndarray            # [n, d] previous value of the scored tensor (the skip-layer input by default)
     K: List[np.ndarray]           # per layer [n, d] (rotated keys)
     V: List[np.ndarray]           # per layer [n, d]
     h_final: np.ndarray           # [n, d] last layer output (before final norm)
@@ -301,6 +305,20 @@ def is_refresh_step(step: int, sched) -> bool:
     if sib == 0:
         return True
     return sched.refresh_interval > 0 and sib % sched.refresh_interval == 0
+
+
+def scored_tensor(which: str, x: np.ndarray, pos: np.ndarray, lw: dict, dims) -> np.ndarray:
+    """The tensor whose change eq. I measures, for rows x = X_s at positions pos
+    (ES-dLLM section 2A: hidden states, keys or values): X_s itself, or layer
+    s's key rows RoPE(n(X_s) Wk^T) / value rows n(X_s) Wv^T."""
+    if which == "hidden":
+        return np.asarray(x, F64)
+    xn = rms_norm(x, lw["attn_norm"], dims.rms_eps)
+    if which == "key":
+        return rope(xn @ np.asarray(lw["wk"], F64).T, pos, dims.n_heads, dims.head_dim, dims.rope_base)
+    if which == "value":
+        return xn @ np.asarray(lw["wv"], F64).T
+    raise ValueError(f"unknown scored tensor {which!r}")
 
 
 def is_full_context_step(step: int, sched) -> bool:
@@ -368,11 +386,14 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
     for li in range(s_layer):
         x = layer_forward(x, cand, model["layers"][li], st.K[li], st.V[li], n, dims)
 
+    which = getattr(sched, "score_tensor", "hidden")
+    assert which == "hidden" or s_layer < L, "a key/value score needs layer s to exist"
+    T = scored_tensor(which, x, cand, model["layers"][s_layer], dims) if which != "hidden" else x
     scores = None
     if refresh:
         idx = np.arange(cand.size, dtype=np.int64)
     else:
-        sc = score_rows(sched.score, x, st.h_prev[cand], st.conf[cand], sched.alpha)
+        sc = score_rows(sched.score, T, st.h_prev[cand], st.conf[cand], sched.alpha)
         scores = np.full(n, -np.inf)
         scores[cand] = sc
         if mode == "topk":
@@ -380,7 +401,7 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
         else:
             idx = select_threshold(sc, threshold)
     sel = cand[idx]
-    st.h_prev[cand] = x                                       # every candidate row
+    st.h_prev[cand] = T                                       # every candidate row
 
     xr = x[idx]
     sel2, scores2, l_rest = None, None, s_layer

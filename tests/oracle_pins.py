@@ -546,4 +546,56 @@ def pin_response_only_schedule():
     assert kinds == list("RrrFRrrF"), kinds
 
 
+# --------------------------------------------------------------------------
+# keys or values as the scored tensor (ES-dLLM section 2A)
+# --------------------------------------------------------------------------
+
+def _kv_step(which, model_fix=None):
+    sched = micro_sched(keep=0.4, score_tensor=which)
+    dims = micro_dims()
+    m = np_model(dims)
+    if model_fix:
+        model_fix(m, dims)
+    prompt = (np.arange(9) * 4 + 3) % dims.vocab
+    st = E.init_state(prompt, sched.gen_len, dims, keep_logits=True)
+    tokens0 = st.tokens.copy()
+    E.denoise_step(m, dims, st, 0, sched)                    # refresh
+    h0 = st.h_prev.copy()
+    conf0 = st.conf.copy()
+    tokens1 = st.tokens.copy()
+    info = E.denoise_step(m, dims, st, 1, sched)
+    return sched, dims, m, tokens0, tokens1, h0, conf0, st, info
+
+
+def pin_value_score_with_identity_projection():
+    """Layer s's Wv = I (gains 1): the scored value rows are RMSNorm(X_s)."""
+    def fix(m, dims):
+        m["layers"][1]["wv"] = np.eye(dims.d)
+    sched, dims, m, tokens0, tokens1, h0, conf0, st, info = _kv_step("value", fix)
+    def rn(tokens):
+        x = libref.forward(tokens, m, dims, n_layers=sched.skip_layer)
+        return libref.rms(x, libref.t(np.ones(dims.d)), dims.rms_eps)
+    v0, v1 = rn(tokens0), rn(tokens1)
+    close(h0, v0.numpy(), rtol=1e-11)
+    close(st.h_prev, v1.numpy(), rtol=1e-11)
+    close(info.scores, _eq1(conf0, v1, v0, dims.d), rtol=1e-11)
+    assert info.selected.tolist() == _brute_topk(info.scores, E.keep_count(sched.keep, len(tokens1)))
+
+
+def pin_key_and_value_scores_against_torch():
+    """Keys (rotated, as cached) or values of layer s, from torch's projection
+    and complex-multiplication RoPE, at the refresh and at the next step."""
+    for which, slot in (("key", 1), ("value", 2)):
+        sched, dims, m, tokens0, tokens1, h0, conf0, st, info = _kv_step(which)
+        s = sched.skip_layer
+        def tens(tokens):
+            x = libref.forward(tokens, m, dims, n_layers=s)
+            return libref.qkv(x, torch.arange(len(tokens)), m["layers"][s], dims)[slot]
+        t0, t1 = tens(tokens0), tens(tokens1)
+        close(h0, t0.numpy(), rtol=1e-11)
+        close(st.h_prev, t1.numpy(), rtol=1e-11)
+        close(info.scores, _eq1(conf0, t1, t0, dims.d), rtol=1e-11)
+        assert info.selected.tolist() == _brute_topk(info.scores, E.keep_count(sched.keep, len(tokens1)))
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

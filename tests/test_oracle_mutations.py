@@ -14,7 +14,7 @@ from oracle import esdllm as E
 _orig = {name: getattr(E, name) for name in ("score_rows", "rms_norm", "rope", "attention", "select_topk",
                                              "unmask", "keep_count", "conf_argmax", "silu", "layer_forward",
                                              "select_threshold", "candidate_rows", "level2_count",
-                                             "is_full_context_step")}
+                                             "is_full_context_step", "scored_tensor")}
 
 
 def m_score_l2(kind, x, h, c, alpha=0.5):          # L2 instead of L1 in eq. I
@@ -124,6 +124,24 @@ def m_level2_of_kept(keep2, n_cand, n_kept1):       # second ratio taken of the 
     return _orig["keep_count"](keep2, n_kept1) if n_kept1 > 0 else 0
 
 
+def m_key_from_wq(which, x, pos, lw, dims):         # query projection scored as the key
+    if which == "key":
+        lw = dict(lw, wk=lw["wq"])
+    return _orig["scored_tensor"](which, x, pos, lw, dims)
+
+
+def m_key_unrotated(which, x, pos, lw, dims):       # keys scored before RoPE
+    if which == "key":
+        return E.rms_norm(x, lw["attn_norm"], dims.rms_eps) @ np.asarray(lw["wk"]).T
+    return _orig["scored_tensor"](which, x, pos, lw, dims)
+
+
+def m_kv_unnormed(which, x, pos, lw, dims):         # projection of X_s without its RMSNorm
+    if which == "value":
+        return np.asarray(x) @ np.asarray(lw["wv"]).T
+    return _orig["scored_tensor"](which, x, pos, lw, dims)
+
+
 MUTANTS = [
     ("score_rows", m_score_l2), ("score_rows", m_score_csign), ("score_rows", m_score_nosqrtd),
     ("rms_norm", m_rms_noeps), ("rope", m_rope_sign), ("rope", m_rope_pairs),
@@ -134,6 +152,7 @@ MUTANTS = [
     ("select_threshold", m_threshold_ge),
     ("candidate_rows", m_cand_all), ("candidate_rows", m_cand_shift),
     ("is_full_context_step", m_full_context_always), ("level2_count", m_level2_of_kept),
+    ("scored_tensor", m_key_from_wq), ("scored_tensor", m_key_unrotated), ("scored_tensor", m_kv_unnormed),
 ]
 
 

@@ -79,6 +79,7 @@ class Schedule:
     skip_layer2: int = 0        # second skip layer (0: one level); skip_layer < skip_layer2 <= n_layers
     keep2: float = 1.0          # keep ratio at the second skip layer
     response_interval: int = 0  # > 0: full-context skip steps every N in-block steps, response rows only otherwise
+    score_tensor: str = "hidden"  # tensor whose change is scored: "hidden" (layer-s input), "key" or "value" of layer s
 
     @property
     def n_blocks(self) -> int:
