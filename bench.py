@@ -39,19 +39,21 @@ def parse():
     ap.add_argument("--timing-stride", type=int, default=8,
                     help="time about one launch in this many of each kernel class (1: every launch)")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the nested-skip and response-only variant timings")
+                    help="skip the nested-skip, response-only and key-score variant timings")
     return ap.parse_args()
 
 
 def variant_schedules(sched):
     """Schedules of the method's variants timed beside the headline step on the
     same model and prompt: a second skip level at layer 8 (keep 50% at layer 4,
-    25% at layer 8; ES-dLLM section 2B) and DyLLM's response-only steps with a
-    full-context step every 4 steps (section 2B, strategy 3)."""
+    25% at layer 8; ES-dLLM section 2B), DyLLM's response-only steps with a
+    full-context step every 4 steps (section 2B, strategy 3), and eq. I on
+    layer 4's rotated keys instead of its input (ES-dLLM section 2A)."""
     import dataclasses
     return {
         "nested_s4_keep0.5_s8_keep0.25": dataclasses.replace(sched, keep=0.5, skip_layer2=8, keep2=0.25),
         "response_only_full_every4": dataclasses.replace(sched, response_interval=4),
+        "key_rows_scored": dataclasses.replace(sched, score_tensor="key"),
     }
 
 
@@ -81,7 +83,8 @@ def time_variant(torch, Decoder, dev_model, prompts, sched, steps: int, warmup: 
     out = {"steps_per_s": round(steps / (ms / 1e3), 3), "ms_per_step": round(ms / steps, 4),
            "gen_tokens_per_s": round(steps / (ms / 1e3) * dec.per_step * dec.B, 3), "steps": steps,
            "step_kinds": kinds, "keep": sched.keep, "skip_layer": sched.skip_layer,
-           "skip_layer2": sched.skip_layer2, "keep2": sched.keep2, "response_interval": sched.response_interval}
+           "skip_layer2": sched.skip_layer2, "keep2": sched.keep2, "response_interval": sched.response_interval,
+           "score_tensor": sched.score_tensor}
     del dec
     torch.cuda.empty_cache()
     return out

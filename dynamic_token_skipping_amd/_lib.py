@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libdtsk.so")
 DL_F32, DL_BF16 = 0, 1
 DL_SCORE_ESDLLM, DL_SCORE_RELL2_INVCONF, DL_SCORE_COSINE = 0, 1, 2
 DL_SEL_TOPK, DL_SEL_THRESHOLD = 0, 1
+DL_TENSOR_HIDDEN, DL_TENSOR_KEY, DL_TENSOR_VALUE = 0, 1, 2
+SCORE_TENSORS = {"hidden": DL_TENSOR_HIDDEN, "key": DL_TENSOR_KEY, "value": DL_TENSOR_VALUE}
 SCORE_KINDS = {"esdllm": DL_SCORE_ESDLLM, "rell2_invconf": DL_SCORE_RELL2_INVCONF, "cosine": DL_SCORE_COSINE}
 DTYPES = {"f32": DL_F32, "bf16": DL_BF16}
 TORCH_DTYPES = {DL_F32: torch.float32, DL_BF16: torch.bfloat16}
@@ -62,7 +64,7 @@ class StepParams(Structure):
                 ("full_refresh", c_int32), ("score", c_int32), ("alpha", c_float), ("mode", c_int32),
                 ("keep_ratio", c_float), ("threshold", c_float), ("seq_len_host", POINTER(c_int32)),
                 ("response_only", c_int32), ("prompt_len_host", POINTER(c_int32)), ("skip_layer2", c_int32),
-                ("mode2", c_int32), ("keep_ratio2", c_float), ("threshold2", c_float)]
+                ("mode2", c_int32), ("keep_ratio2", c_float), ("threshold2", c_float), ("score_tensor", c_int32)]
 
 
 class Timing(Structure):

@@ -88,6 +88,7 @@ struct Layout {
   size_t sel_idx, sel_count, row_off;  // the step's candidate rows (every valid row, or the response rows)
   RowMapMem map_all, map_sel, map_sel2;
   size_t x_all, x_sel, x_sel2;  // fp32 [R, d]
+  size_t t_rows;            // fp32 [R, d]: key / value rows of the skip layer when they are scored
   size_t inv;               // int32 [B*S]: packed row of a flat position
   size_t scores2;           // fp32 [B*S]
   size_t act;               // T [R, d] normalised rows
@@ -148,6 +149,7 @@ Layout make_layout(const dl_dims& d, int R) {
   L.x_all = take(sizeof(float) * (size_t)L.R * d.d);
   L.x_sel = take(sizeof(float) * (size_t)L.R * d.d);
   L.x_sel2 = take(sizeof(float) * (size_t)L.R * d.d);
+  L.t_rows = take(sizeof(float) * (size_t)L.R * d.d);
   L.inv = take(sizeof(int32_t) * (size_t)B * S);
   L.scores2 = take(sizeof(float) * (size_t)B * S);
   L.act = take(es * (size_t)L.R * d.d);
@@ -410,6 +412,25 @@ dl_status lm_block(const Ctx& c, const void* final_norm, const void* lm_head, co
 }
 
 size_t layer_stride_bytes(const dl_dims& d) { return (size_t)d.B * d.S * d.d * esize(d.dtype); }
+
+// The key (rotated) or value rows of layer l for the packed rows of rm, in
+// fp32, from act = RMSNorm(x, attn_norm of l) (already in the workspace):
+// one product with Wk or Wv, its split-K partials summed in order, then RoPE
+// at each row's position for keys.
+dl_status scored_kv_rows(const Ctx& c, const dl_layer_w* w, dl_score_tensor which, const RowMap& rm, float* t) {
+  const dl_dims& d = *c.d;
+  const void* W = which == DL_TENSOR_KEY ? w->wk : w->wv;
+  const void* seg[4] = {W, W, W, W};
+  const Epilogue e = epi_base(c, EPI_NONE, rm, 0);
+  int splits = 1;
+  DL_TRY(product(c, DL_KC_GEMM, at<void>(c.ws, c.L->act), rm, 0, rm.R_max, d.d, seg, d.d, d.d, e, &splits));
+  DL_CHECK_HIP(launch_fill_i32(reinterpret_cast<int32_t*>(t), 0, (size_t)rm.R_max * d.d, c.st));
+  DL_CHECK_HIP(launch_reduce_rows(d.dtype, at<float>(c.ws, c.L->P), splits, rm, d.d, t, nullptr, d.rms_eps, nullptr,
+                                  c.st));
+  if (which == DL_TENSOR_KEY)
+    DL_CHECK_HIP(launch_rope_rows(t, rm, d.S, d.d, d.head_dim, at<float2>(c.ws, c.L->rope), c.st));
+  return DL_OK;
+}
 
 }  // namespace
 
@@ -681,6 +702,11 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
         s->sel2.row_off == s->sel.row_off)
       return fail(DL_E_ARG, "state.sel2 and state.sel alias");
   }
+  if (p->score_tensor < DL_TENSOR_HIDDEN || p->score_tensor > DL_TENSOR_VALUE)
+    return fail(DL_E_ARG, "score_tensor %d unknown", (int)p->score_tensor);
+  const bool kv = p->score_tensor != DL_TENSOR_HIDDEN;
+  if (kv && p->skip_layer >= d.n_layers)
+    return fail(DL_E_ARG, "a key/value score needs skip_layer (%d) < n_layers (%d)", p->skip_layer, d.n_layers);
   const bool resp = p->response_only != 0 && !refresh;
   if (resp && !p->prompt_len_host) return fail(DL_E_ARG, "params.prompt_len_host is NULL on a response-only step");
 
@@ -745,7 +771,13 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
     // every row through every layer; h_prev <- the layer-s input (h_prev2 <- the layer-s2 input)
     auto norm_of = [&](int l) { return l < d.n_layers ? model->layers[l].attn_norm : model->final_norm; };
     DL_TRY(run_layers(c, model, 0, sl, x_all, rm_all, s->seq_len, kcache, vcache, false, norm_of(sl)));
-    DL_CHECK_HIP(launch_store_rows(d.dtype, x_all, d.d, rm_all, s->h_prev, st));
+    if (kv) {
+      float* t = at<float>(ws, L.t_rows);
+      DL_TRY(scored_kv_rows(c, &model->layers[sl], p->score_tensor, rm_all, t));
+      DL_CHECK_HIP(launch_store_rows(d.dtype, t, d.d, rm_all, s->h_prev, st));
+    } else {
+      DL_CHECK_HIP(launch_store_rows(d.dtype, x_all, d.d, rm_all, s->h_prev, st));
+    }
     int l0 = sl;
     if (two) {
       DL_TRY(run_layers(c, model, sl, s2, x_all, rm_all, s->seq_len, kcache, vcache, true, norm_of(s2)));
@@ -758,16 +790,23 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
     DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_all, rm_all, s->conf, s->argmax, s->h_final, s->logits,
                     true));
   } else {
-    DL_TRY(run_layers(c, model, 0, sl, x_all, rm_all, s->seq_len, kcache, vcache, false, nullptr));
-    // score against h_prev and overwrite it with this step's layer-s input
+    DL_TRY(run_layers(c, model, 0, sl, x_all, rm_all, s->seq_len, kcache, vcache, false,
+                      kv ? model->layers[sl].attn_norm : nullptr));
+    // score against h_prev and overwrite it with this step's value of the scored tensor
+    const float* xs = x_all;
+    if (kv) {
+      float* t = at<float>(ws, L.t_rows);
+      DL_TRY(scored_kv_rows(c, &model->layers[sl], p->score_tensor, rm_all, t));
+      xs = t;
+    }
     if (!resp) {
-      DL_CHECK_HIP(launch_score(d.dtype, nullptr, x_all, all_off, s->h_prev, s->conf, s->seq_len, d.B, d.S, d.d,
+      DL_CHECK_HIP(launch_score(d.dtype, nullptr, xs, all_off, s->h_prev, s->conf, s->seq_len, d.B, d.S, d.d,
                                 p->score, p->alpha, scores, st));
       DL_CHECK_HIP(launch_select(scores, s->seq_len, d.B, d.S, p->mode, p->keep_ratio, p->threshold, s->sel.sel_idx,
                                  s->sel.sel_count, st));
     } else {
       DL_CHECK_HIP(launch_fill_scores(scores, -INFINITY, s->seq_len, d.B, d.S, st));
-      DL_CHECK_HIP(launch_score(d.dtype, nullptr, x_all, nullptr, s->h_prev, s->conf, s->seq_len, d.B, d.S, d.d,
+      DL_CHECK_HIP(launch_score(d.dtype, nullptr, xs, nullptr, s->h_prev, s->conf, s->seq_len, d.B, d.S, d.d,
                                 p->score, p->alpha, scores, st, &rm_all));
       DL_CHECK_HIP(launch_select(scores, s->seq_len, d.B, d.S, p->mode, p->keep_ratio, p->threshold, s->sel.sel_idx,
                                  s->sel.sel_count, st, all_idx, all_cnt, all_cnt));

@@ -806,6 +806,28 @@ __global__ void k_inv_rows(const int32_t* __restrict__ row_pos, const int32_t* _
   if (r < R_max && r < *n_rows) inv[row_pos[r]] = r;
 }
 
+// RoPE applied in place to fp32 packed rows [R, d] of a row map (rotate-half
+// pairs (j, j + dh/2) of every head, angle table (cos, sin) [S, dh/2] at the
+// row's position in its sequence).
+__global__ __launch_bounds__(kRowThreads) void k_rope_rows(float* __restrict__ x, const int32_t* __restrict__ row_pos,
+                                                           const int32_t* __restrict__ row_seq, int S, int d,
+                                                           int head_dim, const float2* __restrict__ tab) {
+  const int r = blockIdx.x;
+  const int p = row_pos[r];
+  if (p < 0) return;
+  const int pos = p - row_seq[r] * S;
+  const int half = head_dim / 2;
+  float* xr = x + (size_t)r * d;
+  for (int idx = threadIdx.x; idx < d / 2; idx += blockDim.x) {
+    const int h = idx / half, j = idx - h * half;
+    float* xh = xr + h * head_dim;
+    const float a = xh[j], b = xh[j + half];
+    const float2 cs = tab[(size_t)pos * half + j];
+    xh[j] = a * cs.x - b * cs.y;
+    xh[j + half] = b * cs.x + a * cs.y;
+  }
+}
+
 // v at the valid positions of every sequence ([B, S] array)
 __global__ void k_fill_valid(float* __restrict__ p, float v, const int32_t* __restrict__ seq_len, int S) {
   const int b = blockIdx.y, i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -964,6 +986,14 @@ hipError_t launch_inv_rows(const RowMap& rm, int BS, int32_t* inv, hipStream_t s
   hipLaunchKernelGGL(k_fill_i32, dim3(cdiv(BS, 256)), dim3(256), 0, st, inv, -1, (size_t)BS);
   if (rm.R_max > 0)
     hipLaunchKernelGGL(k_inv_rows, dim3(cdiv(rm.R_max, 256)), dim3(256), 0, st, rm.row_pos, rm.n_rows, rm.R_max, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_rows(float* x, const RowMap& rm, int S, int d, int head_dim, const float2* rope,
+                            hipStream_t st) {
+  if (rm.R_max <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope_rows, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, rm.row_pos, rm.row_seq, S, d, head_dim,
+                     rope);
   return hipGetLastError();
 }
 

@@ -62,6 +62,9 @@ hipError_t launch_store_rows(dl_dtype dt, const float* x, int w, const RowMap& r
 hipError_t launch_rmsnorm(dl_dtype dt, const float* x, const void* g, const RowMap& rm, int d, float eps, void* out,
                           hipStream_t st);
 hipError_t launch_rope_table(int S, int head_dim, float base, float2* table, hipStream_t st);
+// RoPE in place on fp32 packed rows [R_max, d] of the row map, at each row's position.
+hipError_t launch_rope_rows(float* x, const RowMap& rm, int S, int d, int head_dim, const float2* rope,
+                            hipStream_t st);
 hipError_t launch_epi_qkv(dl_dtype dt, const float* P, int splits, const RowMap& rm, int S, int d, int head_dim,
                           const float2* rope, void* q_out, void* k_cache, void* v_cache, hipStream_t st);
 hipError_t launch_epi_residual(const float* P, int splits, const RowMap& rm, int N, float* x, hipStream_t st);

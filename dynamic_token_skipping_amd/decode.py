@@ -125,7 +125,8 @@ class Decoder:
                             ctypes.cast(self._seq_len_host, ctypes.POINTER(ctypes.c_int32)),
                             int(bool(response_only) and not refresh),
                             ctypes.cast(self._prompt_len_host, ctypes.POINTER(ctypes.c_int32)), s2, mode2,
-                            getattr(s, "keep2", 1.0) if keep2 is None else keep2, threshold2)
+                            getattr(s, "keep2", 1.0) if keep2 is None else keep2, threshold2,
+                            L.SCORE_TENSORS[getattr(s, "score_tensor", "hidden")])
 
     def step(self, step: int, **kw):
         L.dl_denoise_step(self.model_struct, self.state, self.params(step, **kw), self.ws)

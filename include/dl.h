@@ -78,6 +78,13 @@ typedef enum { DL_SCORE_ESDLLM = 0, DL_SCORE_RELL2_INVCONF = 1, DL_SCORE_COSINE 
  * DL_SEL_THRESHOLD: every row with score > threshold (DyLLM section 2A). */
 typedef enum { DL_SEL_TOPK = 0, DL_SEL_THRESHOLD = 1 } dl_select_mode;
 
+/* The tensor whose change between steps the score measures (ES-dLLM section
+ * 2A: hidden states, keys or values may serve): the input of the skip layer
+ * s, or layer s's key rows RoPE(n(x) Wk^T) (rotated, as cached) or value rows
+ * n(x) Wv^T, n = RMSNorm with layer s's attn_norm.  state.h_prev holds the
+ * previous value of that tensor. */
+typedef enum { DL_TENSOR_HIDDEN = 0, DL_TENSOR_KEY = 1, DL_TENSOR_VALUE = 2 } dl_score_tensor;
+
 typedef struct {
   int32_t B;          /* sequences in the batch */
   int32_t S;          /* padded row capacity per sequence */
@@ -119,7 +126,8 @@ typedef struct {
   uint8_t *masked;            /* [B, S] 1 = still masked */
   const int32_t *seq_len;     /* [B] valid rows (prompt + generation) */
   const int32_t *prompt_len;  /* [B] */
-  void *h_prev;               /* [B, S, d] skip-layer input of the previous step */
+  void *h_prev;               /* [B, S, d] previous value of the scored tensor (the skip-layer
+                                 input unless params.score_tensor says otherwise) */
   void *k_cache, *v_cache;    /* [L, B, S, d] rotated keys / values per layer
                                  (layers < skip layer are per-step scratch) */
   void *h_final;              /* [B, S, d] last-layer output (before final norm) */
@@ -167,6 +175,9 @@ typedef struct {
   dl_select_mode mode2;
   float keep_ratio2;
   float threshold2;
+  /* Tensor scored at the first level (DL_TENSOR_KEY / DL_TENSOR_VALUE need
+   * skip_layer < n_layers).  The second level always scores hidden states. */
+  dl_score_tensor score_tensor;
 } dl_step_params;
 
 /* ---------------------------------------------------------------------------

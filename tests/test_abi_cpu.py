@@ -139,3 +139,8 @@ def test_step_validation_two_levels_and_response_only(lib):
     assert run(state(), params(skip_layer2=0, response_only=1)) == -2
     plen[0] = 256
     assert run(state(), params(skip_layer2=0, response_only=1), 64) == -5
+    assert run(state(), params(score_tensor=3)) == -1             # unknown scored tensor
+    assert run(state(), params(skip_layer2=0, score_tensor=1), 64) == -5
+    p = params(skip_layer2=0, score_tensor=2)
+    p.skip_layer = 4                                              # no layer s to take keys / values from
+    assert run(state(), p) == -1 and b"key/value" in lib.dl_last_error()

@@ -1,7 +1,8 @@
 """GPU parity of the two-level nested skip (ES-dLLM section 2B: skipping at two
-early layers with a ratio per layer) and of DyLLM's response-only steps
-(section 2B, strategy 3) against the oracle, on a ragged batch of 3 sequences,
-plus their invariants at the full 8B-class shape."""
+early layers with a ratio per layer), of DyLLM's response-only steps (section
+2B, strategy 3) and of key / value rows as the scored tensor (ES-dLLM section
+2A) against the oracle, on a ragged batch of 3 sequences, plus their
+invariants at the full 8B-class shape."""
 import dataclasses
 
 import numpy as np
@@ -20,6 +21,9 @@ NESTED = dataclasses.replace(BASE, skip_layer2=2, keep2=0.25)
 RESP = dataclasses.replace(BASE, response_interval=2)
 BOTH = dataclasses.replace(NESTED, response_interval=2)
 NESTED_LAST = dataclasses.replace(BASE, skip_layer2=3, keep2=0.25)    # second level feeds the LM head only
+KEY = dataclasses.replace(BASE, score_tensor="key")                   # eq. I on layer s's rotated keys
+VALUE = dataclasses.replace(BASE, score_tensor="value", score="cosine")
+KEY_RESP_NESTED = dataclasses.replace(BOTH, score_tensor="key")
 PROMPTS = (9, 45, 96)
 
 
@@ -42,7 +46,8 @@ def _scores_ok(g, o, tol):
 
 
 @pytest.mark.parametrize("dtype,tol", [("f32", 1e-5), ("bf16", 2e-2)])
-@pytest.mark.parametrize("sched", [NESTED, RESP, BOTH, NESTED_LAST], ids=["nested", "resp", "both", "nested_last"])
+@pytest.mark.parametrize("sched", [NESTED, RESP, BOTH, NESTED_LAST, KEY, VALUE, KEY_RESP_NESTED],
+                         ids=["nested", "resp", "both", "nested_last", "key", "value", "key_resp_nested"])
 def test_decode_matches_oracle(dtype, tol, sched):
     m_np, dec, sts = _setup(dtype, sched)
     two = sched.skip_layer2 > 0
@@ -176,6 +181,30 @@ def test_full8b_nested_and_response_only_steps():
         for li in range(sched.skip_layer2, wl.dims.n_layers):
             assert torch.equal(dec.k_cache[li, 0][out2], kb[li, 0][out2]), (t, li)
             assert torch.equal(dec.v_cache[li, 0][out2], vb[li, 0][out2]), (t, li)
+    del model, dec
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_full8b_key_score_step():
+    """Keys of layer s scored: h_prev holds this step's rotated keys of every
+    row, which for the kept rows agree with the keys layer s wrote into its
+    cache (two separate computations: the fused QKV epilogue and the product
+    + RoPE kernel); the selection is the exact top-k of the step's scores."""
+    wl = workloads.workload("full8b")
+    sched = dataclasses.replace(wl.sched, score_tensor="key")
+    _, model, dec = _decoder8b(sched)
+    n, s = dec.seq_lens[0], sched.skip_layer
+    dec.step(0)
+    torch.cuda.synchronize()
+    assert row_rel_err(host(dec.h_prev[0, :n]), host(dec.k_cache[s, 0, :n])) <= 2e-2
+    dec.step(1)
+    torch.cuda.synchronize()
+    rows = dec.sel.rows()[0]
+    k = E.keep_count(sched.keep, n)
+    assert len(rows) == k
+    assert _topk_ok(host(dec.scores[0, :n]).astype(np.float32), rows, k)
+    assert row_rel_err(host(dec.h_prev[0, :n])[rows], host(dec.k_cache[s, 0, :n])[rows]) <= 2e-2
     del model, dec
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
