@@ -52,6 +52,15 @@ function that uses it):
   states, keys or values): H is then the key (rotated, as cached) or value row
   of layer s, computed from X_s for every candidate row; h_prev holds its
   previous value instead of the hidden state.
+* Per-layer re-selection (DyLLM section 2B): at every layer from s on, the
+  active rows (those whose layer input was recomputed: the ES selection at
+  layer s, the previous layer's salient rows above it) get fresh q/K/V and
+  exact attention; every other row's context is updated as C + S dV with S
+  from its cached query and normaliser and the active rows' previous keys.
+  The rows with the largest 1 - cos(C_new, C_cached) (top-k at keep_layer, or
+  above a threshold) go through Wo and the FFN; the others keep their cached
+  layer output.  The context cache takes C_new for every row; query and
+  normaliser caches change for the active rows only.
 * Response-only steps (DyLLM section 2B, strategy 3): on a skip step that is
   not a full-context step, only the response rows (positions >= prompt length)
   go through the prefix layers, are scored and can be kept; |S| is then the
@@ -72,6 +81,7 @@ __all__ = [
     "conf_argmax", "score_rows", "keep_count", "select_topk", "select_threshold",
     "unmask", "SeqState", "init_state", "denoise_step", "decode",
     "is_refresh_step", "is_full_context_step", "candidate_rows", "level2_count", "scored_tensor", "FLT_MIN",
+    "attention_lse", "finish_layer", "layer_parts", "approx_context", "layer_input_rows",
 ]
 
 F64 = np.float64
@@ -161,6 +171,78 @@ def layer_forward(x: np.ndarray, pos: np.ndarray, lw: dict, K_cache: np.ndarray,
     hn = rms_norm(h, lw["ffn_norm"], dims.rms_eps)
     a = silu(hn @ np.asarray(lw["w_gate"], F64).T) * (hn @ np.asarray(lw["w_up"], F64).T)
     return h + a @ np.asarray(lw["w_down"], F64).T
+
+
+# ----------------------------------------------------------------------------
+# DyLLM pieces (DyLLM section 2B): per-layer intermediates and the approximate
+# context update of rows whose query did not change
+# ----------------------------------------------------------------------------
+
+def attention_lse(q: np.ndarray, K: np.ndarray, n_heads: int, head_dim: int) -> np.ndarray:
+    """Per row and head, log sum_j exp(q.k_j / sqrt(dh)) over the given keys:
+    the softmax normaliser of ``attention`` in log form.  [n, H]."""
+    q = np.asarray(q, F64)
+    K = np.asarray(K, F64)
+    scale = 1.0 / math.sqrt(head_dim)
+    out = np.empty((q.shape[0], n_heads), F64)
+    for h in range(n_heads):
+        sl = slice(h * head_dim, (h + 1) * head_dim)
+        s = (q[:, sl] @ K[:, sl].T) * scale
+        m = s.max(axis=1)
+        out[:, h] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    return out
+
+
+def finish_layer(x: np.ndarray, ctx: np.ndarray, lw: dict, dims) -> np.ndarray:
+    """The rest of a layer from its attention context (before Wo):
+    h = x + ctx Wo^T; y = h + (silu(n(h) Wg^T) * n(h) Wu^T) Wd^T."""
+    h = np.asarray(x, F64) + np.asarray(ctx, F64) @ np.asarray(lw["wo"], F64).T
+    hn = rms_norm(h, lw["ffn_norm"], dims.rms_eps)
+    a = silu(hn @ np.asarray(lw["w_gate"], F64).T) * (hn @ np.asarray(lw["w_up"], F64).T)
+    return h + a @ np.asarray(lw["w_down"], F64).T
+
+
+def layer_parts(x: np.ndarray, pos: np.ndarray, lw: dict, K_cache: np.ndarray, V_cache: np.ndarray,
+                n_valid: int, dims):
+    """``layer_forward`` with its intermediates: returns (y, q, ctx, lse) where
+    q is the rows' rotated query, ctx their attention context (before Wo) and
+    lse its per-head log normaliser.  Writes the rows' K/V first, as there."""
+    H, dh = dims.n_heads, dims.head_dim
+    xn = rms_norm(x, lw["attn_norm"], dims.rms_eps)
+    q = rope(xn @ np.asarray(lw["wq"], F64).T, pos, H, dh, dims.rope_base)
+    k = rope(xn @ np.asarray(lw["wk"], F64).T, pos, H, dh, dims.rope_base)
+    v = xn @ np.asarray(lw["wv"], F64).T
+    K_cache[pos] = k
+    V_cache[pos] = v
+    ctx = attention(q, K_cache[:n_valid], V_cache[:n_valid], H, dh)
+    lse = attention_lse(q, K_cache[:n_valid], H, dh)
+    return finish_layer(x, ctx, lw, dims), q, ctx, lse
+
+
+def approx_context(C: np.ndarray, q: np.ndarray, lse: np.ndarray, K_act: np.ndarray, dV_act: np.ndarray,
+                   n_heads: int, head_dim: int) -> np.ndarray:
+    """DyLLM's saliency-aware approximate attention for rows with cached context
+    C, query q and normaliser lse: C + S dV, with S_ij = exp(q_i.k_j/sqrt(dh) -
+    lse_i) the cached attention probability of key j and dV_j the change of its
+    value row, over the active rows j (keys K_act as they were when C was
+    formed).  Exact when only those value rows changed."""
+    C = np.array(C, F64, copy=True)
+    q = np.asarray(q, F64)
+    K_act = np.asarray(K_act, F64)
+    dV_act = np.asarray(dV_act, F64)
+    scale = 1.0 / math.sqrt(head_dim)
+    for h in range(n_heads):
+        sl = slice(h * head_dim, (h + 1) * head_dim)
+        S = np.exp((q[:, sl] @ K_act[:, sl].T) * scale - np.asarray(lse, F64)[:, h:h + 1])
+        C[:, sl] += S @ dV_act[:, sl]
+    return C
+
+
+def layer_input_rows(st, X_s: np.ndarray, layer: int, s_layer: int, rows: np.ndarray) -> np.ndarray:
+    """Inputs of ``rows`` at ``layer`` in a per-layer step: the fresh skip-layer
+    input at layer s, else the cached output of the layer below (rewritten
+    this step for the rows that layer recomputed)."""
+    return np.asarray(X_s, F64)[rows] if layer == s_layer else st.Y[layer - 1][rows]
 
 
 def lm_logits(x: np.ndarray, final_norm: np.ndarray, lm_head: np.ndarray, eps: float) -> np.ndarray:
@@ -278,6 +360,12 @@ class SeqState:
     h_final: np.ndarray           # [n, d] last layer output (before final norm)
     logits: Optional[np.ndarray] = None   # [n, V] when kept
     h_prev2: Optional[np.ndarray] = None  # [n, d] input of the second skip layer
+    # per-layer caches of the DyLLM variant (layers >= s): rotated query,
+    # attention context, its per-head log normaliser, layer output
+    Q: Optional[List[np.ndarray]] = None      # per layer [n, d]
+    C: Optional[List[np.ndarray]] = None      # per layer [n, d]
+    LSE: Optional[List[np.ndarray]] = None    # per layer [n, H]
+    Y: Optional[List[np.ndarray]] = None      # per layer [n, d]
 
 
 def init_state(prompt: np.ndarray, gen_len: int, dims, mask_id: Optional[int] = None,
@@ -296,7 +384,11 @@ def init_state(prompt: np.ndarray, gen_len: int, dims, mask_id: Optional[int] = 
                     V=[np.zeros((n, d), F64) for _ in range(dims.n_layers)],
                     h_final=np.zeros((n, d), F64),
                     logits=np.zeros((n, dims.vocab), F64) if keep_logits else None,
-                    h_prev2=np.zeros((n, d), F64))
+                    h_prev2=np.zeros((n, d), F64),
+                    Q=[np.zeros((n, d), F64) for _ in range(dims.n_layers)],
+                    C=[np.zeros((n, d), F64) for _ in range(dims.n_layers)],
+                    LSE=[np.zeros((n, dims.n_heads), F64) for _ in range(dims.n_layers)],
+                    Y=[np.zeros((n, d), F64) for _ in range(dims.n_layers)])
 
 
 def is_refresh_step(step: int, sched) -> bool:
@@ -352,12 +444,15 @@ class StepInfo:
     selected2: Optional[np.ndarray] = None   # rows recomputed in layers >= s2 (two levels)
     scores2: Optional[np.ndarray] = None     # fp64 second-level scores [n] (-inf outside `selected`)
     response_only: bool = False
+    layer_selected: Optional[list] = None    # per-layer variant: rows through O-proj + FFN of each layer >= s
+    layer_scores: Optional[list] = None      # per-layer variant: 1 - cos of each layer's context change
 
 
 def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = "topk",
                  threshold: float = 0.0, force_refresh: Optional[bool] = None,
                  keep: Optional[float] = None, response_only: Optional[bool] = None,
-                 mode2: str = "topk", threshold2: float = 0.0) -> StepInfo:
+                 mode2: str = "topk", threshold2: float = 0.0, mode_l: str = "topk",
+                 threshold_l: float = 0.0) -> StepInfo:
     """One denoising step of one sequence (ES-dLLM section 2B).
 
     Refresh step: every row through every layer; all caches rewritten.
@@ -369,7 +464,9 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
     conf, argmax, h_final (and logits) for kept rows only.  Then unmask.
     With a second skip layer s2, layers [s, s2) run on the first level's rows,
     which are scored again at the input of s2 against h_prev2; only the second
-    level's rows go through [s2, L) and the LM head.
+    level's rows go through [s2, L) and the LM head.  With the per-layer
+    variant (DyLLM section 2B), every layer from s on re-selects its salient
+    rows by the change of the attention context (``_per_layer``).
     """
     n = st.tokens.shape[0]
     s_layer = sched.skip_layer
@@ -404,6 +501,11 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
     st.h_prev[cand] = T                                       # every candidate row
 
     xr = x[idx]
+    if getattr(sched, "per_layer", False):
+        assert s_layer < L and getattr(sched, "skip_layer2", 0) == 0 and not response_only
+        rows, xr, lsel, lsc = _per_layer(model, dims, st, sched, sel, xr, x, refresh, mode_l, threshold_l)
+        return _finish_step(model, dims, st, step, sched, rows, xr, StepInfo(
+            refresh=refresh, selected=sel, scores=scores, unmasked=None, layer_selected=lsel, layer_scores=lsc))
     sel2, scores2, l_rest = None, None, s_layer
     if s2 > 0:
         for li in range(s_layer, s2):
@@ -425,7 +527,15 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
     rows = sel if sel2 is None else sel2
     for li in range(l_rest, L):
         xr = layer_forward(xr, rows, model["layers"][li], st.K[li], st.V[li], n, dims)
+    return _finish_step(model, dims, st, step, sched, rows, xr, StepInfo(
+        refresh=refresh, selected=sel, scores=scores, unmasked=None, selected2=sel2, scores2=scores2,
+        response_only=response_only))
 
+
+def _finish_step(model, dims, st, step, sched, rows, xr, info: StepInfo) -> StepInfo:
+    """LM head on the rows that went through every layer, scatter of their
+    confidence, argmax, final state (and logits), then unmasking."""
+    n = st.tokens.shape[0]
     if rows.size:
         logits = lm_logits(xr, model["final_norm"], model["lm_head"], dims.rms_eps)
         conf, amax = conf_argmax(logits)
@@ -441,13 +551,51 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
     pos = unmask(st.masked, st.conf, lo, hi, sched.per_step)
     st.tokens[pos] = st.argmax[pos]
     st.masked[pos] = False
-    return StepInfo(refresh=refresh, selected=sel, scores=scores, unmasked=pos, selected2=sel2,
-                    scores2=scores2, response_only=response_only)
+    info.unmasked = pos
+    return info
+
+
+def _per_layer(model, dims, st, sched, A, xA, X_s, refresh, mode_l, threshold_l):
+    """Layers [s, L) of the per-layer variant (DyLLM section 2B).  A: the rows
+    whose input of layer s is fresh (every row on a refresh step), xA their
+    inputs.  Returns (rows through the last layer, their outputs, the salient
+    rows of each layer, each layer's scores)."""
+    n = st.tokens.shape[0]
+    H, dh = dims.n_heads, dims.head_dim
+    s_layer, L = sched.skip_layer, dims.n_layers
+    keep_l = getattr(sched, "keep_layer", 0.0) or sched.keep
+    lsel, lsc = [], []
+    for li in range(s_layer, L):
+        lw = model["layers"][li]
+        if refresh:
+            y, q, ctx, lse = layer_parts(xA, A, lw, st.K[li], st.V[li], n, dims)
+            st.Q[li][A], st.C[li][A], st.LSE[li][A], st.Y[li][A] = q, ctx, lse, y
+            lsel.append(A)
+            lsc.append(None)
+            xA = y
+            continue
+        K_old = st.K[li][A].copy()
+        V_old = st.V[li][A].copy()
+        y_unused, q, ctx, lse = layer_parts(xA, A, lw, st.K[li], st.V[li], n, dims)
+        C_new = approx_context(st.C[li], st.Q[li], st.LSE[li], K_old, st.V[li][A] - V_old, H, dh)
+        C_new[A] = ctx
+        sig = score_rows("cosine", C_new, st.C[li], st.conf)
+        R = select_topk(sig, keep_count(keep_l, n)) if mode_l == "topk" else select_threshold(sig, threshold_l)
+        st.C[li] = C_new
+        st.Q[li][A] = q
+        st.LSE[li][A] = lse
+        y = finish_layer(layer_input_rows(st, X_s, li, s_layer, R), C_new[R], lw, dims)
+        st.Y[li][R] = y
+        lsel.append(R)
+        lsc.append(sig)
+        A, xA = R, y
+    return A, xA, lsel, lsc
 
 
 def decode(model: dict, dims, prompt: np.ndarray, sched, n_steps: Optional[int] = None,
            vanilla: bool = False, keep_logits: bool = False, mode: str = "topk",
-           threshold: float = 0.0, mode2: str = "topk", threshold2: float = 0.0):
+           threshold: float = 0.0, mode2: str = "topk", threshold2: float = 0.0, mode_l: str = "topk",
+           threshold_l: float = 0.0):
     """Run the decode loop.  ``vanilla`` refreshes every step (full recompute)."""
     st = init_state(prompt, sched.gen_len, dims, keep_logits=keep_logits)
     infos = []
@@ -455,5 +603,5 @@ def decode(model: dict, dims, prompt: np.ndarray, sched, n_steps: Optional[int] 
     for t in range(T):
         infos.append(denoise_step(model, dims, st, t, sched, mode=mode, threshold=threshold,
                                   force_refresh=True if vanilla else None, mode2=mode2,
-                                  threshold2=threshold2))
+                                  threshold2=threshold2, mode_l=mode_l, threshold_l=threshold_l))
     return st, infos

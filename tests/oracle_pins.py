@@ -598,4 +598,128 @@ def pin_key_and_value_scores_against_torch():
         assert info.selected.tolist() == _brute_topk(info.scores, E.keep_count(sched.keep, len(tokens1)))
 
 
+# --------------------------------------------------------------------------
+# per-layer re-selection with approximate attention (DyLLM section 2B)
+# --------------------------------------------------------------------------
+
+def _rand_attn(seed=3, n=11, m=13, H=2, dh=8):
+    rng = np.random.default_rng(seed)
+    return rng.normal(size=(n, H * dh)), rng.normal(size=(m, H * dh)), rng.normal(size=(m, H * dh)), H, dh
+
+
+def pin_attention_lse_torch():
+    q, K, _, H, dh = _rand_attn()
+    lse = E.attention_lse(q, K, H, dh)
+    qt, Kt = libref.t(q), libref.t(K)
+    for h in range(H):
+        sl = slice(h * dh, (h + 1) * dh)
+        close(lse[:, h], torch.logsumexp(qt[:, sl] @ Kt[:, sl].T / math.sqrt(dh), dim=1).numpy())
+
+
+def pin_approx_context_exact_when_only_values_change():
+    """Delta C = S Delta V holds exactly when only value rows change (keys and
+    queries fixed): checked against torch's attention before and after."""
+    q, K, V, H, dh = _rand_attn(seed=4)
+    A = np.array([1, 4, 5, 11])
+    V2 = V.copy()
+    V2[A] += np.random.default_rng(9).normal(size=(len(A), V.shape[1]))
+    C0 = libref.attn(libref.t(q), libref.t(K), libref.t(V), H, dh).numpy()
+    C1 = libref.attn(libref.t(q), libref.t(K), libref.t(V2), H, dh).numpy()
+    got = E.approx_context(C0, q, E.attention_lse(q, K, H, dh), K[A], V2[A] - V[A], H, dh)
+    close(got, C1, rtol=1e-12, atol=1e-12)
+    assert np.abs(C1 - C0).max() > 1e-3
+
+
+def pin_layer_parts_against_torch():
+    dims = micro_dims()
+    m = np_model(dims)
+    lw = m["layers"][1]
+    n = 14
+    x = np.random.default_rng(2).normal(size=(n, dims.d))
+    pos = np.arange(n)
+    K = np.zeros((n, dims.d))
+    V = np.zeros((n, dims.d))
+    y, q, ctx, lse = E.layer_parts(x, pos, lw, K, V, n, dims)
+    qt, kt, vt = libref.qkv(libref.t(x), torch.as_tensor(pos), lw, dims)
+    close(q, qt.numpy(), rtol=1e-12)
+    close(ctx, libref.attn(qt, kt, vt, dims.n_heads, dims.head_dim).numpy(), rtol=1e-11)
+    close(y, libref.full_layer(libref.t(x), lw, dims).numpy(), rtol=1e-11)
+    close(E.finish_layer(x, ctx, lw, dims), y, rtol=1e-13)
+    K2, V2 = np.zeros_like(K), np.zeros_like(V)
+    assert np.array_equal(E.layer_forward(x, pos, lw, K2, V2, n, dims), y)
+
+
+def pin_per_layer_keep_all_is_vanilla():
+    """Every row kept at layer s and at every layer: the per-layer variant is
+    full recomputation, bit for bit, over a whole decode."""
+    sched = micro_sched(keep=1.0, per_layer=True, keep_layer=1.0)
+    _, _, _, st_a, inf_a = _micro_run(sched)
+    _, _, _, st_b, _ = _micro_run(micro_sched(keep=1.0), vanilla=True)
+    assert any(not i.refresh for i in inf_a)
+    for key in ("tokens", "masked", "conf", "argmax", "h_prev", "h_final", "logits"):
+        assert np.array_equal(getattr(st_a, key), getattr(st_b, key)), key
+    for li in range(len(st_a.K)):
+        assert np.array_equal(st_a.K[li], st_b.K[li]) and np.array_equal(st_a.V[li], st_b.V[li])
+
+
+def pin_per_layer_step_against_torch():
+    """One per-layer step after a refresh, layer by layer in torch: fresh q/K/V
+    and exact attention for the active rows; C + S dV for the others from the
+    cached query, normaliser and previous keys; salient rows = brute-force
+    top-k of 1 - cos; Wo + FFN on them from the right inputs; caches."""
+    sched = micro_sched(keep=0.4, per_layer=True, keep_layer=0.3)
+    dims = micro_dims()
+    m = np_model(dims)
+    H, dh, d = dims.n_heads, dims.head_dim, dims.d
+    prompt = (np.arange(9) * 2 + 5) % dims.vocab
+    st = E.init_state(prompt, sched.gen_len, dims, keep_logits=True)
+    tokens0 = st.tokens.copy()
+    E.denoise_step(m, dims, st, 0, sched)                    # refresh: every cache of every layer
+    s = sched.skip_layer
+    x = libref.forward(tokens0, m, dims, n_layers=s)
+    for li in range(s, dims.n_layers):
+        lw = m["layers"][li]
+        q, k, v = libref.qkv(x, torch.arange(len(tokens0)), lw, dims)
+        close(st.Q[li], q.numpy(), rtol=1e-11)
+        close(st.C[li], libref.attn(q, k, v, H, dh).numpy(), rtol=1e-11)
+        x = libref.full_layer(x, lw, dims)
+        close(st.Y[li], x.numpy(), rtol=1e-11)
+    old = {k: [a.copy() for a in getattr(st, k)] for k in ("K", "V", "Q", "C", "LSE", "Y")}
+    before = {k: getattr(st, k).copy() for k in ("conf", "h_prev", "h_final", "argmax")}
+    tokens1 = st.tokens.copy()
+    info = E.denoise_step(m, dims, st, 1, sched)
+    n = len(tokens1)
+    Xs = libref.forward(tokens1, m, dims, n_layers=s)
+    A = np.array(_brute_topk(_eq1(before["conf"], Xs, before["h_prev"], d), E.keep_count(0.4, n)))
+    assert info.selected.tolist() == A.tolist()
+    xA = Xs[torch.as_tensor(A)]
+    k_l = E.keep_count(0.3, n)
+    for i, li in enumerate(range(s, dims.n_layers)):
+        lw = m["layers"][li]
+        q, k, v = libref.qkv(xA, torch.as_tensor(A), lw, dims)
+        Kn, Vn = libref.t(old["K"][li]).clone(), libref.t(old["V"][li]).clone()
+        Kn[A], Vn[A] = k, v
+        C = libref.t(old["C"][li]).clone()
+        Qc, lse = libref.t(old["Q"][li]), libref.t(old["LSE"][li])
+        dV = v - libref.t(old["V"][li][A])
+        for h in range(H):
+            sl = slice(h * dh, (h + 1) * dh)
+            P = torch.exp(Qc[:, sl] @ libref.t(old["K"][li][A])[:, sl].T / math.sqrt(dh) - lse[:, h:h + 1])
+            C[:, sl] += P @ dV[:, sl]
+        C[A] = libref.attn(q, Kn, Vn, H, dh)
+        sig = (1.0 - torch.nn.functional.cosine_similarity(C, libref.t(old["C"][li]), dim=1)).numpy()
+        R = np.array(_brute_topk(sig, k_l))
+        assert info.layer_selected[i].tolist() == R.tolist(), li
+        close(info.layer_scores[i], sig, rtol=1e-10, atol=1e-12)
+        close(st.C[li], C.numpy(), rtol=1e-11)
+        close(st.K[li], Kn.numpy(), rtol=1e-11)
+        x_in = Xs[torch.as_tensor(R)] if li == s else libref.t(st.Y[li - 1][R])
+        y = libref.finish_layer(x_in, C[torch.as_tensor(R)], lw, dims)
+        close(st.Y[li][R], y.numpy(), rtol=1e-11)
+        other = np.setdiff1d(np.arange(n), R)
+        assert np.array_equal(st.Y[li][other], old["Y"][li][other])
+        A, xA = R, y
+    close(st.h_final[A], xA.numpy(), rtol=1e-11)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

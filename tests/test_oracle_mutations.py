@@ -14,7 +14,8 @@ from oracle import esdllm as E
 _orig = {name: getattr(E, name) for name in ("score_rows", "rms_norm", "rope", "attention", "select_topk",
                                              "unmask", "keep_count", "conf_argmax", "silu", "layer_forward",
                                              "select_threshold", "candidate_rows", "level2_count",
-                                             "is_full_context_step", "scored_tensor")}
+                                             "is_full_context_step", "scored_tensor", "approx_context",
+                                             "attention_lse", "layer_input_rows", "finish_layer")}
 
 
 def m_score_l2(kind, x, h, c, alpha=0.5):          # L2 instead of L1 in eq. I
@@ -142,6 +143,26 @@ def m_kv_unnormed(which, x, pos, lw, dims):         # projection of X_s without 
     return _orig["scored_tensor"](which, x, pos, lw, dims)
 
 
+def m_approx_sign(C, q, lse, K_act, dV_act, H, dh):   # the value change subtracted
+    return _orig["approx_context"](C, q, lse, K_act, -np.asarray(dV_act), H, dh)
+
+
+def m_approx_nolse(C, q, lse, K_act, dV_act, H, dh):  # probabilities left unnormalised
+    return _orig["approx_context"](C, q, np.zeros_like(np.asarray(lse)), K_act, dV_act, H, dh)
+
+
+def m_lse_noscale(q, K, H, dh):                       # normaliser of unscaled scores
+    return _orig["attention_lse"](np.asarray(q) * np.sqrt(dh), K, H, dh)
+
+
+def m_input_always_xs(st, X_s, layer, s_layer, rows):  # every layer fed the skip-layer input
+    return np.asarray(X_s)[rows]
+
+
+def m_finish_noresid(x, ctx, lw, dims):               # attention residual dropped
+    return _orig["finish_layer"](np.zeros_like(np.asarray(x)), ctx, lw, dims)
+
+
 MUTANTS = [
     ("score_rows", m_score_l2), ("score_rows", m_score_csign), ("score_rows", m_score_nosqrtd),
     ("rms_norm", m_rms_noeps), ("rope", m_rope_sign), ("rope", m_rope_pairs),
@@ -153,6 +174,8 @@ MUTANTS = [
     ("candidate_rows", m_cand_all), ("candidate_rows", m_cand_shift),
     ("is_full_context_step", m_full_context_always), ("level2_count", m_level2_of_kept),
     ("scored_tensor", m_key_from_wq), ("scored_tensor", m_key_unrotated), ("scored_tensor", m_kv_unnormed),
+    ("approx_context", m_approx_sign), ("approx_context", m_approx_nolse), ("attention_lse", m_lse_noscale),
+    ("layer_input_rows", m_input_always_xs), ("finish_layer", m_finish_noresid),
 ]
 
 

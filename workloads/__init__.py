@@ -80,6 +80,8 @@ class Schedule:
     keep2: float = 1.0          # keep ratio at the second skip layer
     response_interval: int = 0  # > 0: full-context skip steps every N in-block steps, response rows only otherwise
     score_tensor: str = "hidden"  # tensor whose change is scored: "hidden" (layer-s input), "key" or "value" of layer s
+    per_layer: bool = False     # DyLLM-style re-selection at every layer >= skip_layer by the context change
+    keep_layer: float = 0.0     # keep ratio of that re-selection (0: same as keep)
 
     @property
     def n_blocks(self) -> int:
