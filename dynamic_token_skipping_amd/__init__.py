@@ -6,5 +6,5 @@ from ._lib import (DLError, DL_BF16, DL_F32, DL_SCORE_COSINE, DL_SCORE_ESDLLM, D
                    dl_ffn_rows, dl_gather, dl_lm_head_rows, dl_partial_attn, dl_scatter_cache, dl_score_select,
                    dl_unmask, load, make_dims, workspace, workspace_bytes, dl_timing_enable, dl_timing_read,
                    dl_timing_reset, DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD,
-                   DL_KC_GEMM_TILED)
+                   DL_KC_GEMM_TILED, DL_KC_APPROX)
 from .decode import Decoder, DeviceModel, is_refresh_step  # noqa: F401

@@ -29,7 +29,7 @@ TORCH_DTYPES = {DL_F32: torch.float32, DL_BF16: torch.bfloat16}
 EXPORTS = ("dl_score_select", "dl_gather", "dl_scatter_cache", "dl_partial_attn", "dl_ffn_rows", "dl_lm_head_rows",
            "dl_unmask", "dl_denoise_step", "dl_workspace_bytes", "dl_status_string", "dl_last_error",
            "dl_abi_version", "dl_timing_enable", "dl_timing_reset", "dl_timing_read")
-DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD, DL_KC_GEMM_TILED = 0, 1, 2, 3
+DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD, DL_KC_GEMM_TILED, DL_KC_APPROX = 0, 1, 2, 3, 4
 
 
 class Dims(Structure):
@@ -56,7 +56,9 @@ class State(Structure):
     _fields_ = [("tokens", c_void_p), ("masked", c_void_p), ("seq_len", c_void_p), ("prompt_len", c_void_p),
                 ("h_prev", c_void_p), ("k_cache", c_void_p), ("v_cache", c_void_p), ("h_final", c_void_p),
                 ("conf", c_void_p), ("argmax", c_void_p), ("logits", c_void_p), ("scores", c_void_p),
-                ("sel", Selection), ("h_prev2", c_void_p), ("scores2", c_void_p), ("sel2", Selection)]
+                ("sel", Selection), ("h_prev2", c_void_p), ("scores2", c_void_p), ("sel2", Selection),
+                ("q_cache", c_void_p), ("ctx_cache", c_void_p), ("lse_cache", c_void_p), ("y_cache", c_void_p),
+                ("layer_scores", c_void_p), ("sel_l", Selection)]
 
 
 class StepParams(Structure):
@@ -64,7 +66,8 @@ class StepParams(Structure):
                 ("full_refresh", c_int32), ("score", c_int32), ("alpha", c_float), ("mode", c_int32),
                 ("keep_ratio", c_float), ("threshold", c_float), ("seq_len_host", POINTER(c_int32)),
                 ("response_only", c_int32), ("prompt_len_host", POINTER(c_int32)), ("skip_layer2", c_int32),
-                ("mode2", c_int32), ("keep_ratio2", c_float), ("threshold2", c_float), ("score_tensor", c_int32)]
+                ("mode2", c_int32), ("keep_ratio2", c_float), ("threshold2", c_float), ("score_tensor", c_int32),
+                ("per_layer", c_int32), ("mode_l", c_int32), ("keep_ratio_l", c_float), ("threshold_l", c_float)]
 
 
 class Timing(Structure):

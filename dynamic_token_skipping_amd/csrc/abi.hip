@@ -89,6 +89,11 @@ struct Layout {
   RowMapMem map_all, map_sel, map_sel2;
   size_t x_all, x_sel, x_sel2;  // fp32 [R, d]
   size_t t_rows;            // fp32 [R, d]: key / value rows of the skip layer when they are scored
+  // per-layer re-selection
+  size_t k_act, v_old, dv;  // T [R, d]: the active rows' previous keys / values, their value change
+  size_t ctx_new;           // fp32 [R, d]: every row's new context, packed over all rows
+  size_t lsel_idx[2], lsel_count[2], lsel_off[2];  // two selections used in turn
+  RowMapMem map_l[2];
   size_t inv;               // int32 [B*S]: packed row of a flat position
   size_t scores2;           // fp32 [B*S]
   size_t act;               // T [R, d] normalised rows
@@ -139,7 +144,7 @@ Layout make_layout(const dl_dims& d, int R) {
   L.sel_idx = take(sizeof(int32_t) * (size_t)B * S);
   L.sel_count = take(sizeof(int32_t) * B);
   L.row_off = take(sizeof(int32_t) * (B + 1));
-  for (RowMapMem* m : {&L.map_all, &L.map_sel, &L.map_sel2}) {
+  for (RowMapMem* m : {&L.map_all, &L.map_sel, &L.map_sel2, &L.map_l[0], &L.map_l[1]}) {
     m->row_pos = take(sizeof(int32_t) * L.R);
     m->row_seq = take(sizeof(int32_t) * L.R);
     m->n_rows = take(sizeof(int32_t));
@@ -150,6 +155,15 @@ Layout make_layout(const dl_dims& d, int R) {
   L.x_sel = take(sizeof(float) * (size_t)L.R * d.d);
   L.x_sel2 = take(sizeof(float) * (size_t)L.R * d.d);
   L.t_rows = take(sizeof(float) * (size_t)L.R * d.d);
+  L.k_act = take(es * (size_t)L.R * d.d);
+  L.v_old = take(es * (size_t)L.R * d.d);
+  L.dv = take(es * (size_t)L.R * d.d);
+  L.ctx_new = take(sizeof(float) * (size_t)L.R * d.d);
+  for (int i = 0; i < 2; ++i) {
+    L.lsel_idx[i] = take(sizeof(int32_t) * (size_t)B * S);
+    L.lsel_count[i] = take(sizeof(int32_t) * B);
+    L.lsel_off[i] = take(sizeof(int32_t) * (B + 1));
+  }
   L.inv = take(sizeof(int32_t) * (size_t)B * S);
   L.scores2 = take(sizeof(float) * (size_t)B * S);
   L.act = take(es * (size_t)L.R * d.d);
@@ -412,6 +426,135 @@ dl_status lm_block(const Ctx& c, const void* final_norm, const void* lm_head, co
 }
 
 size_t layer_stride_bytes(const dl_dims& d) { return (size_t)d.B * d.S * d.d * esize(d.dtype); }
+
+// Layers [s, L) of the per-layer variant (DyLLM section 2B).  The active rows
+// (sel_A / rm_A, inputs x_A packed in fp32, act = their RMSNorm for layer s
+// when act_ready) are every row on a refresh step, the first selection
+// otherwise.  rm_all / all_off: every valid row, packed by sequence offsets
+// (x_all holds their layer-s inputs).  On return *rows / *x_rows / *sel_out
+// describe the rows through the last layer, and act holds their final norm.
+struct LayerSel {
+  int32_t *idx, *cnt, *off;
+};
+
+dl_status per_layer_layers(const Ctx& c, const dl_model* model, const dl_state* s, const dl_step_params* p,
+                           bool refresh, LayerSel sel_A, RowMap rm_A, float* x_A, bool act_ready,
+                           const RowMap& rm_all, const int32_t* all_off, float* x_all, long long R_l,
+                           long long A_x_keys, long long R_x_keys, RowMap* rows_out, float** x_out,
+                           LayerSel* sel_out) {
+  const dl_dims& d = *c.d;
+  const Layout& L = *c.L;
+  const size_t es = esize(d.dtype);
+  const size_t lstride = (size_t)d.B * d.S * d.d * es;
+  const size_t fstride = (size_t)d.B * d.S * d.d;
+  const size_t hstride = (size_t)d.B * d.S * d.n_heads;
+  void* act = at<void>(c.ws, L.act);
+  void* q = at<void>(c.ws, L.q);
+  void* attn = at<void>(c.ws, L.attn);
+  void* k_act = at<void>(c.ws, L.k_act);
+  void* v_old = at<void>(c.ws, L.v_old);
+  void* dv = at<void>(c.ws, L.dv);
+  float* ctx_new = at<float>(c.ws, L.ctx_new);
+  int32_t* inv = at<int32_t>(c.ws, L.inv);
+  float* lscores = s->layer_scores ? s->layer_scores : at<float>(c.ws, L.scores2);
+  float* xbuf[2] = {at<float>(c.ws, L.x_sel), at<float>(c.ws, L.x_sel2)};
+  int turn = x_A == xbuf[0] ? 1 : 0;             // the salient rows never land on the active rows' buffer
+  const int sl = p->skip_layer;
+  for (int l = sl; l < d.n_layers; ++l) {
+    const long long ax = l == sl ? A_x_keys : R_x_keys;   // sum over sequences of active rows x keys (timing)
+    const dl_layer_w* w = &model->layers[l];
+    char* kc = static_cast<char*>(s->k_cache) + (size_t)l * lstride;
+    char* vc = static_cast<char*>(s->v_cache) + (size_t)l * lstride;
+    char* qc = static_cast<char*>(s->q_cache) + (size_t)l * lstride;
+    float* ctx_l = s->ctx_cache + (size_t)l * fstride;
+    float* lse_l = s->lse_cache + (size_t)l * hstride;
+    float* y_l = s->y_cache + (size_t)l * fstride;
+    if (!act_ready) DL_CHECK_HIP(launch_rmsnorm(d.dtype, x_A, w->attn_norm, rm_A, d.d, d.rms_eps, act, c.st));
+    if (!refresh) {
+      // the active rows' keys and values as the cached contexts saw them
+      DL_CHECK_HIP(launch_gather(es, kc, nullptr, d.S, d.d, rm_A, k_act, c.st));
+      DL_CHECK_HIP(launch_gather(es, vc, nullptr, d.S, d.d, rm_A, v_old, c.st));
+    }
+    {  // fresh q / k / v of the active rows; their K/V rows into the caches
+      const void* seg[4] = {w->wq, w->wk, w->wv, w->wv};
+      Epilogue e = epi_base(c, EPI_QKV, rm_A, 0);
+      e.q_out = q;
+      e.k_cache = kc;
+      e.v_cache = vc;
+      DL_TRY(product(c, DL_KC_GEMM, act, rm_A, 0, rm_A.R_max, d.d, seg, d.d, 3 * d.d, e, nullptr));
+    }
+    // exact contexts (fp32, packed over all rows) and normalisers of the active rows
+    {
+      const double kk = (double)c.keys_total;
+      DL_CHECK_HIP(timed(DL_KC_ATTN, c.st, (double)es * ((double)rm_A.R_max * d.d * 2 + 2.0 * kk * d.d),
+                         4.0 * (double)ax * d.d, [&] {
+                           const int splits = std::min(L.attn_splits, attention_splits(d.dtype, d.head_dim, d.S,
+                                                                                      d.n_heads, rm_A, L.R_part));
+                           return launch_attention(d.dtype, q, kc, vc, s->seq_len, rm_A, d.S, d.n_heads, d.head_dim,
+                                                   splits, at<float>(c.ws, L.attn_o), at<float2>(c.ws, L.attn_ml),
+                                                   L.R_part, attn, c.st, ctx_new, all_off, lse_l);
+                         }));
+    }
+    RowMap rm_R = rm_A;
+    LayerSel sel_R = sel_A;
+    float* x_R = x_A;
+    if (refresh) {
+      DL_CHECK_HIP(launch_scatter(sizeof(float), ctx_new, d.d, rm_all, ctx_l, c.st));
+    } else {
+      // approximate contexts of every other row, then saliency and ctx cache <- new
+      DL_CHECK_HIP(launch_value_change(d.dtype, vc, v_old, rm_A, d.d, dv, c.st));
+      DL_CHECK_HIP(launch_inv_rows(rm_A, d.B * d.S, inv, c.st));
+      DL_CHECK_HIP(timed(DL_KC_APPROX, c.st,
+                         (double)es * ((double)rm_all.R_max * d.d + 2.0 * rm_A.R_max * d.d) +
+                             8.0 * rm_all.R_max * d.d,
+                         4.0 * (double)ax * d.d, [&] {
+                           return launch_attention_approx(d.dtype, qc, k_act, dv, sel_A.off, sel_A.cnt, lse_l, inv,
+                                                          ctx_l, ctx_new, rm_all, d.S, d.n_heads, d.head_dim, c.st);
+                         }));
+      DL_CHECK_HIP(launch_score(DL_F32, nullptr, ctx_new, all_off, ctx_l, s->conf, s->seq_len, d.B, d.S, d.d,
+                                DL_SCORE_COSINE, 0.f, lscores, c.st));
+      const int tsel = turn;
+      sel_R = LayerSel{at<int32_t>(c.ws, L.lsel_idx[tsel]), at<int32_t>(c.ws, L.lsel_count[tsel]),
+                       at<int32_t>(c.ws, L.lsel_off[tsel])};
+      DL_CHECK_HIP(launch_select(lscores, s->seq_len, d.B, d.S, p->mode_l, p->keep_ratio_l, p->threshold_l, sel_R.idx,
+                                 sel_R.cnt, c.st));
+      DL_CHECK_HIP(launch_row_off(sel_R.cnt, sel_R.off, d.B, c.st));
+      rm_R = rowmap_at(c.ws, L.map_l[tsel], (int)R_l, std::min(L.T, cdiv(R_l, kTileRows) + d.B));
+      DL_CHECK_HIP(launch_rowmap(sel_R.idx, sel_R.cnt, sel_R.off, d.B, d.S, rm_R, c.st));
+      // inputs of the salient rows: X_s at layer s, the cached output of the layer below above it
+      x_R = xbuf[tsel];
+      if (l == sl)
+        DL_CHECK_HIP(launch_gather(sizeof(float), x_all, all_off, d.S, d.d, rm_R, x_R, c.st));
+      else
+        DL_CHECK_HIP(launch_gather(sizeof(float), s->y_cache + (size_t)(l - 1) * fstride, nullptr, d.S, d.d, rm_R,
+                                   x_R, c.st));
+      turn ^= 1;
+    }
+    // the active rows' queries into the cache
+    DL_CHECK_HIP(launch_scatter(es, q, d.d, rm_A, qc, c.st));
+    // Wo and the FFN on the salient rows, from their new contexts
+    DL_CHECK_HIP(launch_gather_cvt(d.dtype, ctx_new, all_off, d.S, d.d, rm_R, attn, c.st));
+    {
+      const void* seg[4] = {w->wo, w->wo, w->wo, w->wo};
+      const Epilogue e = epi_base(c, EPI_NONE, rm_R, 0);
+      int splits = 1;
+      DL_TRY(product(c, DL_KC_GEMM, attn, rm_R, 0, rm_R.R_max, d.d, seg, d.d, d.d, e, &splits));
+      DL_CHECK_HIP(launch_reduce_rows(d.dtype, at<float>(c.ws, L.P), splits, rm_R, d.d, x_R, w->ffn_norm, d.rms_eps,
+                                      act, c.st));
+    }
+    const void* nn = l + 1 < d.n_layers ? model->layers[l + 1].attn_norm : model->final_norm;
+    DL_TRY(ffn_block(c, w, x_R, rm_R, nn));
+    DL_CHECK_HIP(launch_scatter(sizeof(float), x_R, d.d, rm_R, y_l, c.st));
+    rm_A = rm_R;
+    sel_A = sel_R;
+    x_A = x_R;
+    act_ready = true;
+  }
+  *rows_out = rm_A;
+  *x_out = x_A;
+  *sel_out = sel_A;
+  return DL_OK;
+}
 
 // The key (rotated) or value rows of layer l for the packed rows of rm, in
 // fp32, from act = RMSNorm(x, attn_norm of l) (already in the workspace):
@@ -709,6 +852,26 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
     return fail(DL_E_ARG, "a key/value score needs skip_layer (%d) < n_layers (%d)", p->skip_layer, d.n_layers);
   const bool resp = p->response_only != 0 && !refresh;
   if (resp && !p->prompt_len_host) return fail(DL_E_ARG, "params.prompt_len_host is NULL on a response-only step");
+  const bool per_layer = p->per_layer != 0;
+  if (per_layer) {
+    if (p->skip_layer >= d.n_layers)
+      return fail(DL_E_ARG, "per-layer re-selection needs skip_layer (%d) < n_layers (%d)", p->skip_layer,
+                  d.n_layers);
+    if (two) return fail(DL_E_UNSUPPORTED, "per-layer re-selection with a second skip level");
+    if (p->response_only) return fail(DL_E_UNSUPPORTED, "per-layer re-selection on a response-only step");
+    if (p->mode_l != DL_SEL_TOPK && p->mode_l != DL_SEL_THRESHOLD) return fail(DL_E_ARG, "select mode_l unknown");
+    if (p->mode_l == DL_SEL_TOPK && !(p->keep_ratio_l > 0.f && p->keep_ratio_l <= 1.f))
+      return fail(DL_E_ARG, "keep_ratio_l %g outside (0, 1]", (double)p->keep_ratio_l);
+    DL_TRY(check_ptr(s->q_cache, "q_cache"));
+    DL_TRY(check_ptr(s->ctx_cache, "ctx_cache"));
+    DL_TRY(check_ptr(s->lse_cache, "lse_cache"));
+    DL_TRY(check_ptr(s->y_cache, "y_cache"));
+    if (s->layer_scores) DL_TRY(check_ptr(s->layer_scores, "layer_scores"));
+    DL_TRY(check_sel(&s->sel_l, "state.sel_l"));
+    if (s->sel_l.sel_idx == s->sel.sel_idx || s->sel_l.sel_count == s->sel.sel_count ||
+        s->sel_l.row_off == s->sel.row_off)
+      return fail(DL_E_ARG, "state.sel_l and state.sel alias");
+  }
 
   // Host row bounds (grid sizing; exact for top-k): candidates, first and second level.
   auto topk_count = [](float keep, long long base) -> long long {
@@ -716,8 +879,8 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
     const double kk = ceil((double)keep * (double)base);
     return kk < 1.0 ? 1 : (kk > (double)base ? base : (long long)kk);
   };
-  long long R_all = 0, R_cand = 0, R_sel = 0, R_sel2 = 0;
-  long long cand_x_keys = 0, sel_x_keys = 0, sel2_x_keys = 0;
+  long long R_all = 0, R_cand = 0, R_sel = 0, R_sel2 = 0, R_l = 0;
+  long long cand_x_keys = 0, sel_x_keys = 0, sel2_x_keys = 0, l_x_keys = 0;
   for (int b = 0; b < d.B; ++b) {
     const int n = p->seq_len_host[b];
     if (n < 0 || n > d.S) return fail(DL_E_SHAPE, "seq_len_host[%d] = %d outside [0, S=%d]", b, n, d.S);
@@ -730,6 +893,9 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
     R_cand += nc;
     R_sel += k1;
     R_sel2 += k2;
+    const long long kl = per_layer && p->mode_l == DL_SEL_TOPK && !refresh ? topk_count(p->keep_ratio_l, n) : n;
+    R_l += kl;
+    l_x_keys += kl * n;
     cand_x_keys += nc * n;
     sel_x_keys += k1 * n;
     sel2_x_keys += k2 * n;
@@ -784,7 +950,17 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
       DL_CHECK_HIP(launch_store_rows(d.dtype, x_all, d.d, rm_all, s->h_prev2, st));
       l0 = s2;
     }
-    DL_TRY(run_layers(c, model, l0, d.n_layers, x_all, rm_all, s->seq_len, kcache, vcache, true, model->final_norm));
+    if (per_layer) {
+      RowMap rm_out;
+      float* x_out;
+      LayerSel so;
+      DL_TRY(per_layer_layers(c, model, s, p, true, LayerSel{all_idx, all_cnt, all_off}, rm_all, x_all, true, rm_all,
+                              all_off, x_all, R_all, cand_x_keys, cand_x_keys, &rm_out, &x_out, &so));
+      DL_TRY(copy_sel(s->sel_l));
+    } else {
+      DL_TRY(run_layers(c, model, l0, d.n_layers, x_all, rm_all, s->seq_len, kcache, vcache, true,
+                        model->final_norm));
+    }
     DL_TRY(copy_sel(s->sel));
     if (two) DL_TRY(copy_sel(s->sel2));
     DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_all, rm_all, s->conf, s->argmax, s->h_final, s->logits,
@@ -822,7 +998,20 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
       DL_CHECK_HIP(launch_gather(sizeof(float), x_all, nullptr, d.S, d.d, rm_sel, x_sel, st, inv));
     }
     c.rows_x_keys = sel_x_keys;
-    if (!two) {
+    if (per_layer) {
+      RowMap rm_out;
+      float* x_out;
+      LayerSel so;
+      DL_TRY(per_layer_layers(c, model, s, p, false, LayerSel{s->sel.sel_idx, s->sel.sel_count, s->sel.row_off},
+                              rm_sel, x_sel, false, rm_all, all_off, x_all, R_l, sel_x_keys, l_x_keys, &rm_out,
+                              &x_out, &so));
+      DL_CHECK_HIP(hipMemcpyAsync(s->sel_l.sel_idx, so.idx, sizeof(int32_t) * (size_t)d.B * d.S,
+                                  hipMemcpyDeviceToDevice, st));
+      DL_CHECK_HIP(hipMemcpyAsync(s->sel_l.sel_count, so.cnt, sizeof(int32_t) * d.B, hipMemcpyDeviceToDevice, st));
+      DL_CHECK_HIP(hipMemcpyAsync(s->sel_l.row_off, so.off, sizeof(int32_t) * (d.B + 1), hipMemcpyDeviceToDevice, st));
+      DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_out, rm_out, s->conf, s->argmax, s->h_final, s->logits,
+                      true));
+    } else if (!two) {
       DL_TRY(run_layers(c, model, sl, d.n_layers, x_sel, rm_sel, s->seq_len, kcache, vcache, false,
                         model->final_norm));
       DL_TRY(lm_block(c, model->final_norm, model->lm_head, x_sel, rm_sel, s->conf, s->argmax, s->h_final, s->logits,

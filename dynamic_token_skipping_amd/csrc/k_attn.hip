@@ -24,13 +24,45 @@ namespace {
 constexpr int kSimtThreads = 128;
 constexpr int kMaxKeysSimt = 8192;
 
+// Optional fp32 outputs of the exact attention: the normalised context of a
+// query row goes to ctx[row(r) * d + ...] (row = ctx_off[b] + position in the
+// sequence, i.e. the packed row of an all-rows map) instead of the storage-type
+// output, and its per-head log normaliser log sum_j exp(q.k_j * scale) to
+// lse[row_pos[r] * n_heads + h].
+struct CtxOut {
+  float* ctx;
+  float* lse;
+  const int32_t* row_pos;
+  const int32_t* ctx_off;
+  __device__ __forceinline__ size_t row(int r, int b, int S) const {
+    return (size_t)ctx_off[b] + (size_t)(row_pos[r] - b * S);
+  }
+};
+
+// Inputs of the approximate context update (see k_attn_approx_simt).
+struct ApproxIn {
+  const void* q;              // [B*S, d] cached rotated queries of the layer
+  const void* k;              // packed previous keys of the active rows
+  const void* dv;             // packed value changes of the active rows
+  const int32_t* key_off;     // [B + 1] active rows' packed offsets
+  const int32_t* key_cnt;     // [B] active rows per sequence
+  const float* lse;           // [B*S, H] cached log normalisers
+  const int32_t* inv;         // [B*S] packed active row of a position, -1 if none
+  const float* ctx_cache;     // [B*S, d] cached contexts
+  float* ctx_new;             // [R_all, d] new contexts, packed like the query map
+  const int32_t* n_rows;      // query map (every valid row)
+  const int32_t* row_pos;
+  const int32_t* row_seq;
+};
+
 template <typename T>
 __global__ __launch_bounds__(kSimtThreads) void k_attn_simt(const T* __restrict__ q, const T* __restrict__ Kc,
                                                             const T* __restrict__ Vc,
                                                             const int32_t* __restrict__ seq_len,
                                                             const int32_t* __restrict__ n_rows,
                                                             const int32_t* __restrict__ row_seq, int S, int d,
-                                                            int head_dim, float scale, T* __restrict__ out) {
+                                                            int head_dim, float scale, T* __restrict__ out,
+                                                            CtxOut co) {
   __shared__ float qs[128];
   __shared__ float sc[kMaxKeysSimt];
   __shared__ float red[16];
@@ -68,10 +100,52 @@ __global__ __launch_bounds__(kSimtThreads) void k_attn_simt(const T* __restrict_
   __syncthreads();
   sum = block_sum(sum, red + 8);
   const float inv = 1.f / sum;
+  float* crow = co.ctx ? co.ctx + co.row(r, b, S) * d + col0 : nullptr;
   for (int e = t; e < head_dim; e += blockDim.x) {
     float o = 0.f;
     for (int j = 0; j < n; ++j) o = fmaf(sc[j], to_f32(Vb[(size_t)j * d + e]), o);
-    out[(size_t)r * d + col0 + e] = from_f32<T>(o * inv);
+    if (crow) crow[e] = o * inv;
+    else out[(size_t)r * d + col0 + e] = from_f32<T>(o * inv);
+  }
+  if (co.lse && t == 0) co.lse[(size_t)co.row_pos[r] * gridDim.y + h] = m + logf(sum);
+}
+
+// Approximate context of rows whose query is unchanged (fp32, any head size):
+// C_new = C_cached + sum_j exp(q.k_j * scale - lse) dV_j over the active rows j
+// of the row's sequence (keys and value changes packed by the active rows'
+// selection offsets).  One workgroup per (packed row of the all-rows map,
+// head); active rows (inv >= 0) are left to the exact path.
+template <typename T>
+__global__ __launch_bounds__(kSimtThreads) void k_attn_approx_simt(ApproxIn a, int S, int d, int head_dim,
+                                                                   float scale) {
+  __shared__ float qs[128];
+  __shared__ float sc[kMaxKeysSimt];
+  const int r = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  if (r >= *a.n_rows) return;
+  const int pos = a.row_pos[r];
+  if (a.inv[pos] >= 0) return;
+  const int b = a.row_seq[r];
+  const int n = a.key_cnt[b];
+  const size_t col0 = (size_t)h * head_dim;
+  const T* qc = reinterpret_cast<const T*>(a.q) + (size_t)pos * d + col0;
+  for (int e = t; e < head_dim; e += blockDim.x) qs[e] = to_f32(qc[e]);
+  __syncthreads();
+  const float lse = a.lse[(size_t)pos * gridDim.y + h];
+  const T* Kb = reinterpret_cast<const T*>(a.k) + (size_t)a.key_off[b] * d + col0;
+  const T* Vb = reinterpret_cast<const T*>(a.dv) + (size_t)a.key_off[b] * d + col0;
+  for (int j = t; j < n; j += blockDim.x) {
+    const T* kr = Kb + (size_t)j * d;
+    float s = 0.f;
+    for (int e = 0; e < head_dim; ++e) s = fmaf(qs[e], to_f32(kr[e]), s);
+    sc[j] = expf(s * scale - lse);
+  }
+  __syncthreads();
+  const float* cold = a.ctx_cache + (size_t)pos * d + col0;
+  float* cnew = a.ctx_new + (size_t)r * d + col0;
+  for (int e = t; e < head_dim; e += blockDim.x) {
+    float o = 0.f;
+    for (int j = 0; j < n; ++j) o = fmaf(sc[j], to_f32(Vb[(size_t)j * d + e]), o);
+    cnew[e] = cold[e] + o;
   }
 }
 
@@ -96,9 +170,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ int vt_word(int dim, int kp) { return dim * (kVStride / 2) + (kp ^ (((dim >> 3) & 7) << 2)); }
 
 // One workgroup = (64-query tile, head, key chunk [kbeg, kbeg + chunk)).
-// With one chunk the normalised output goes straight to `out`; with several,
-// the chunk's unnormalised O and its (running max, sum) go to o_part/ml_part
-// and k_attn_combine merges them.
+// With one chunk the normalised output goes straight to `out` (or in fp32 to
+// co.ctx with the log normaliser to co.lse); with several, the chunk's
+// unnormalised O and its (running max, sum) go to o_part/ml_part and
+// k_attn_combine merges them.
+// kApprox: the approximate context update instead (DyLLM's saliency-aware
+// approximate attention): the query tiles are those of the all-rows map, each
+// row's cached query is read at its position, the keys and values are the
+// active rows' previous keys and value changes (packed, a.key_off / a.key_cnt),
+// and the softmax has the row's cached normaliser in place of the running one:
+// C_new = C_cached + sum_j 2^(s_j - lse2) dV_j, written for non-active rows.
+template <bool kApprox>
 __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
                                                    const uint16_t* __restrict__ Vc,
                                                    const int32_t* __restrict__ seq_len,
@@ -107,7 +189,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
                                                    const int32_t* __restrict__ tile_rows, int S, int d, int n_heads,
                                                    float scale_log2, int chunk, int n_split, int n_tiles,
                                                    uint16_t* __restrict__ out, float* __restrict__ o_part,
-                                                   float2* __restrict__ ml_part, int R_part) {
+                                                   float2* __restrict__ ml_part, int R_part, CtxOut co, ApproxIn a) {
   __shared__ __align__(16) uint16_t Ks[kTK * kKStride];
   __shared__ __align__(16) uint32_t Vt[kDh * kVStride / 2];
   // Block order: (head, chunk) pair p runs on XCD p % 8, and on that XCD the
@@ -122,9 +204,9 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   if (nrows <= 0) return;
   const int r0 = tile_row0[tile];
   const int b = row_seq[r0];
-  const int n = seq_len[b];
+  const int n = kApprox ? a.key_cnt[b] : seq_len[b];
   const int kbeg = split * chunk;
-  if (kbeg >= n) return;                           // the combine only reads chunks below n
+  if (!kApprox && kbeg >= n) return;               // the combine only reads chunks below n
   const int kend = min(n, kbeg + chunk);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int ql = lane & 15, g = lane >> 4;
@@ -133,11 +215,19 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   const size_t col0 = (size_t)h * kDh;
 
   // Q^T fragments (B operand): query ql, dims c*32 + g*8 .. +8
+  size_t qsrc_row = (size_t)(r0 + qrow);
+  const uint16_t* qsrc = q;
+  float lse2 = 0.f;                                // kApprox: the row's cached normaliser (log2 units)
+  if constexpr (kApprox) {
+    qsrc = static_cast<const uint16_t*>(a.q);
+    qsrc_row = qvalid ? (size_t)a.row_pos[r0 + qrow] : 0;
+    if (qvalid) lse2 = a.lse[qsrc_row * n_heads + h] * 1.4426950408889634f;
+  }
   bf16x8 qf[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (qvalid) v = *reinterpret_cast<const uint4*>(q + (size_t)(r0 + qrow) * d + col0 + c * 32 + g * 8);
+    if (qvalid) v = *reinterpret_cast<const uint4*>(qsrc + qsrc_row * d + col0 + c * 32 + g * 8);
     qf[c] = __builtin_bit_cast(bf16x8, v);
   }
 
@@ -146,8 +236,10 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const uint16_t* Kb = Kc + (size_t)b * S * d + col0;
-  const uint16_t* Vb = Vc + (size_t)b * S * d + col0;
+  const uint16_t* Kb = kApprox ? static_cast<const uint16_t*>(a.k) + (size_t)a.key_off[b] * d + col0
+                               : Kc + (size_t)b * S * d + col0;
+  const uint16_t* Vb = kApprox ? static_cast<const uint16_t*>(a.dv) + (size_t)a.key_off[b] * d + col0
+                               : Vc + (size_t)b * S * d + col0;
   // per thread and tile: 4 K chunks (key c >> 4, dims (c & 15) * 8) and 2 x 2 V
   // chunks (keys 2kp, 2kp + 1 of key pair kp = c >> 4, dims (c & 15) * 8)
   uint4 kr[4], va[2], vb[2];
@@ -200,6 +292,16 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
         st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c], st[kb], 0, 0, 0);
       }
     }
+    if constexpr (kApprox) {
+      // cached probabilities: 2^(s - lse2), no running normaliser
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + kb * 16 + g * 4 + i;
+          st[kb][i] = key < kend ? exp2f(st[kb][i] * scale_log2 - lse2) : 0.f;
+        }
+    } else {
     // online softmax for query ql over this tile
     float tmax = -INFINITY;
 #pragma unroll
@@ -229,6 +331,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     l_run = l_run * corr + psum;
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) o[blk] *= corr;
+    }
     // O^T += V^T P^T over the two 32-key chunks
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -248,11 +351,36 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
       }
     }
   }
+  if constexpr (kApprox) {
+    if (!qvalid) return;
+    const int r = r0 + qrow;
+    const size_t pos = (size_t)a.row_pos[r];
+    if (a.inv[pos] >= 0) return;                   // active rows take the exact path
+    const float* cold = a.ctx_cache + pos * d + col0;
+    float* cnew = a.ctx_new + (size_t)r * d + col0;
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      const float4 c = *reinterpret_cast<const float4*>(cold + blk * 16 + g * 4);
+      *reinterpret_cast<float4*>(cnew + blk * 16 + g * 4) =
+          make_float4(c.x + o[blk][0], c.y + o[blk][1], c.z + o[blk][2], c.w + o[blk][3]);
+    }
+    return;
+  }
   // full row sum over the 4 lanes sharing this query
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (!qvalid) return;
   const int r = r0 + qrow;
+  if (n_split == 1 && co.ctx) {
+    const float inv = 1.f / l_run;
+    float* crow = co.ctx + co.row(r, b, S) * d + col0;
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk)
+      *reinterpret_cast<float4*>(crow + blk * 16 + g * 4) =
+          make_float4(o[blk][0] * inv, o[blk][1] * inv, o[blk][2] * inv, o[blk][3] * inv);
+    if (g == 0) co.lse[(size_t)co.row_pos[r] * n_heads + h] = (m_run + log2f(l_run)) * 0.6931471805599453f;
+    return;
+  }
   if (n_split == 1) {
     const float inv = 1.f / l_run;
     uint16_t* orow = out + (size_t)r * d + col0;
@@ -279,7 +407,8 @@ __global__ __launch_bounds__(64) void k_attn_combine(const float* __restrict__ o
                                                      const int32_t* __restrict__ n_rows,
                                                      const int32_t* __restrict__ row_seq,
                                                      const int32_t* __restrict__ seq_len, int d, int n_heads,
-                                                     int chunk, int splits, int R_part, uint16_t* __restrict__ out) {
+                                                     int chunk, int splits, int R_part, uint16_t* __restrict__ out,
+                                                     CtxOut co, int S) {
   const int r = blockIdx.x;
   const int col = blockIdx.y * 256 + threadIdx.x * 4;
   if (r >= *n_rows || col >= d) return;
@@ -313,6 +442,13 @@ __global__ __launch_bounds__(64) void k_attn_combine(const float* __restrict__ o
     }
   }
   const float inv = 1.f / L;
+  if (co.ctx) {
+    const int b = row_seq[r];
+    *reinterpret_cast<float4*>(co.ctx + co.row(r, b, S) * d + col) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (col % kDh == 0) co.lse[(size_t)co.row_pos[r] * n_heads + h] = (M + log2f(L)) * 0.6931471805599453f;
+    return;
+  }
   uint2 w2;
   w2.x = pack_bf16x2(acc.x * inv, acc.y * inv);
   w2.y = pack_bf16x2(acc.z * inv, acc.w * inv);
@@ -338,9 +474,12 @@ int attention_splits(dl_dtype dt, int head_dim, int S, int n_heads, const RowMap
 
 hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* seq_len, const RowMap& rm, int S, int n_heads, int head_dim, int splits,
-                            float* o_part, float2* ml_part, int R_part, void* out, hipStream_t st) {
+                            float* o_part, float2* ml_part, int R_part, void* out, hipStream_t st, float* ctx_out,
+                            const int32_t* ctx_off, float* lse_out) {
   const int d = n_heads * head_dim;
   const float scale = 1.f / sqrtf((float)head_dim);
+  const CtxOut co{ctx_out, lse_out, rm.row_pos, ctx_off};
+  if (ctx_out && (!lse_out || !ctx_off)) return hipErrorInvalidValue;
   if (use_mfma_attention(dt, head_dim)) {
     if (rm.tq != kTQ || rm.T_max <= 0) return rm.T_max < 0 ? hipErrorInvalidValue : hipSuccess;
     if (splits < 1 || splits > kAttnMaxSplits || (splits > 1 && (!o_part || !ml_part || rm.R_max > R_part)))
@@ -348,22 +487,50 @@ hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, con
     const int chunk = (S + splits * kTK - 1) / (splits * kTK) * kTK;
     const float scale_log2 = scale * 1.4426950408889634f;
     const int grid = (n_heads * splits + 7) / 8 * 8 * rm.T_max;
-    hipLaunchKernelGGL(k_attn_mfma, dim3(grid), dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k_cache,
+    hipLaunchKernelGGL(k_attn_mfma<false>, dim3(grid), dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k_cache,
                        (const uint16_t*)v_cache, seq_len, rm.row_seq, rm.tile_row0, rm.tile_rows, S, d, n_heads,
-                       scale_log2, chunk, splits, rm.T_max, (uint16_t*)out, o_part, ml_part, R_part);
+                       scale_log2, chunk, splits, rm.T_max, (uint16_t*)out, o_part, ml_part, R_part, co, ApproxIn{});
     if (splits > 1 && rm.R_max > 0)
       hipLaunchKernelGGL(k_attn_combine, dim3(rm.R_max, (d + 255) / 256), dim3(64), 0, st, o_part, ml_part,
-                         rm.n_rows, rm.row_seq, seq_len, d, n_heads, chunk, splits, R_part, (uint16_t*)out);
+                         rm.n_rows, rm.row_seq, seq_len, d, n_heads, chunk, splits, R_part, (uint16_t*)out, co, S);
     return hipGetLastError();
   }
   dim3 grid(rm.R_max, n_heads);
+  if (rm.R_max <= 0) return hipSuccess;
   if (dt == DL_F32)
     hipLaunchKernelGGL(k_attn_simt<float>, grid, dim3(kSimtThreads), 0, st, (const float*)q, (const float*)k_cache,
-                       (const float*)v_cache, seq_len, rm.n_rows, rm.row_seq, S, d, head_dim, scale, (float*)out);
+                       (const float*)v_cache, seq_len, rm.n_rows, rm.row_seq, S, d, head_dim, scale, (float*)out, co);
   else
     hipLaunchKernelGGL(k_attn_simt<bf16_t>, grid, dim3(kSimtThreads), 0, st, (const bf16_t*)q,
                        (const bf16_t*)k_cache, (const bf16_t*)v_cache, seq_len, rm.n_rows, rm.row_seq, S, d,
-                       head_dim, scale, (bf16_t*)out);
+                       head_dim, scale, (bf16_t*)out, co);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_approx(dl_dtype dt, const void* q_cache, const void* k_act, const void* dv_act,
+                                   const int32_t* key_off, const int32_t* key_cnt, const float* lse,
+                                   const int32_t* inv, const float* ctx_cache, float* ctx_new, const RowMap& rm_all,
+                                   int S, int n_heads, int head_dim, hipStream_t st) {
+  const int d = n_heads * head_dim;
+  const float scale = 1.f / sqrtf((float)head_dim);
+  const ApproxIn a{q_cache, k_act, dv_act, key_off, key_cnt, lse, inv, ctx_cache, ctx_new,
+                   rm_all.n_rows, rm_all.row_pos, rm_all.row_seq};
+  if (rm_all.R_max <= 0) return hipSuccess;
+  if (use_mfma_attention(dt, head_dim)) {
+    if (rm_all.tq != kTQ || rm_all.T_max <= 0) return rm_all.T_max < 0 ? hipErrorInvalidValue : hipSuccess;
+    const float scale_log2 = scale * 1.4426950408889634f;
+    const int grid = (n_heads + 7) / 8 * 8 * rm_all.T_max;
+    hipLaunchKernelGGL(k_attn_mfma<true>, dim3(grid), dim3(256), 0, st, nullptr, nullptr, nullptr, nullptr,
+                       rm_all.row_seq, rm_all.tile_row0, rm_all.tile_rows, S, d, n_heads, scale_log2, S, 1,
+                       rm_all.T_max, nullptr, nullptr, nullptr, 0, CtxOut{}, a);
+    return hipGetLastError();
+  }
+  if (S > kMaxKeysSimt) return hipErrorInvalidValue;
+  dim3 grid(rm_all.R_max, n_heads);
+  if (dt == DL_F32)
+    hipLaunchKernelGGL(k_attn_approx_simt<float>, grid, dim3(kSimtThreads), 0, st, a, S, d, head_dim, scale);
+  else
+    hipLaunchKernelGGL(k_attn_approx_simt<bf16_t>, grid, dim3(kSimtThreads), 0, st, a, S, d, head_dim, scale);
   return hipGetLastError();
 }
 

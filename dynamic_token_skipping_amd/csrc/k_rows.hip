@@ -828,6 +828,37 @@ __global__ __launch_bounds__(kRowThreads) void k_rope_rows(float* __restrict__ x
   }
 }
 
+// dst[r] = T(src[src_off[b] + position]) for the packed rows of a row map
+// (fp32 rows packed by sequence offsets -> storage-type rows).
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_gather_cvt(const float* __restrict__ src,
+                                                            const int32_t* __restrict__ src_off, int S, int d,
+                                                            const int32_t* __restrict__ row_pos,
+                                                            const int32_t* __restrict__ row_seq, T* __restrict__ dst) {
+  const int r = blockIdx.x;
+  const int p = row_pos[r];
+  if (p < 0) return;
+  const int b = row_seq[r];
+  const float* sr = src + ((size_t)src_off[b] + (size_t)(p - b * S)) * d;
+  T* o = dst + (size_t)r * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) o[c] = from_f32<T>(sr[c]);
+}
+
+// dv[r] = T(V[row_pos[r]] - v_old[r]): the change of an active row's value
+// (the layer's cache already holds the new one), difference taken in fp32.
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_value_change(const T* __restrict__ V, const T* __restrict__ v_old,
+                                                              const int32_t* __restrict__ row_pos, int d,
+                                                              T* __restrict__ dv) {
+  const int r = blockIdx.x;
+  const int p = row_pos[r];
+  if (p < 0) return;
+  const T* vn = V + (size_t)p * d;
+  const T* vo = v_old + (size_t)r * d;
+  T* o = dv + (size_t)r * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) o[c] = from_f32<T>(to_f32(vn[c]) - to_f32(vo[c]));
+}
+
 // v at the valid positions of every sequence ([B, S] array)
 __global__ void k_fill_valid(float* __restrict__ p, float v, const int32_t* __restrict__ seq_len, int S) {
   const int b = blockIdx.y, i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -994,6 +1025,30 @@ hipError_t launch_rope_rows(float* x, const RowMap& rm, int S, int d, int head_d
   if (rm.R_max <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_rope_rows, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, rm.row_pos, rm.row_seq, S, d, head_dim,
                      rope);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_cvt(dl_dtype dt, const float* src, const int32_t* src_off, int S, int d, const RowMap& rm,
+                             void* dst, hipStream_t st) {
+  if (rm.R_max <= 0) return hipSuccess;
+  if (dt == DL_F32)
+    hipLaunchKernelGGL(k_gather_cvt<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, src, src_off, S, d, rm.row_pos,
+                       rm.row_seq, (float*)dst);
+  else
+    hipLaunchKernelGGL(k_gather_cvt<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, src, src_off, S, d,
+                       rm.row_pos, rm.row_seq, (bf16_t*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_value_change(dl_dtype dt, const void* V, const void* v_old, const RowMap& rm, int d, void* dv,
+                               hipStream_t st) {
+  if (rm.R_max <= 0) return hipSuccess;
+  if (dt == DL_F32)
+    hipLaunchKernelGGL(k_value_change<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const float*)V,
+                       (const float*)v_old, rm.row_pos, d, (float*)dv);
+  else
+    hipLaunchKernelGGL(k_value_change<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const bf16_t*)V,
+                       (const bf16_t*)v_old, rm.row_pos, d, (bf16_t*)dv);
   return hipGetLastError();
 }
 

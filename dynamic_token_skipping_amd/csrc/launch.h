@@ -50,6 +50,13 @@ hipError_t launch_embed(dl_dtype dt, const int32_t* tokens, const RowMap& rm, co
 // (padded [B,S,w] source).
 hipError_t launch_gather(size_t elem_bytes, const void* src, const int32_t* src_off, int S, int w, const RowMap& rm,
                          void* dst, hipStream_t st, const int32_t* src_inv = nullptr);
+// dst[r] = T(src[src_off[b] + position of r]): fp32 rows packed by sequence
+// offsets, converted to the storage type, for the packed rows of rm.
+hipError_t launch_gather_cvt(dl_dtype dt, const float* src, const int32_t* src_off, int S, int d, const RowMap& rm,
+                             void* dst, hipStream_t st);
+// dv[r] = V[row_pos[r]] - v_old[r] (storage type, difference in fp32).
+hipError_t launch_value_change(dl_dtype dt, const void* V, const void* v_old, const RowMap& rm, int d, void* dv,
+                               hipStream_t st);
 // inv[p] = the packed row of flat position p in the row map, -1 for positions
 // outside it (inv has BS = B*S entries).
 hipError_t launch_inv_rows(const RowMap& rm, int BS, int32_t* inv, hipStream_t st);
@@ -130,10 +137,22 @@ bool attention_supported(dl_dtype dt, int S, int head_dim);
 constexpr int kAttnMaxSplits = 8;
 constexpr int kAttnTargetBlocks = 2048;
 int attention_splits(dl_dtype dt, int head_dim, int S, int n_heads, const RowMap& rm, int R_part);
-// o_part [kAttnMaxSplits][R_part][d] fp32, ml_part [kAttnMaxSplits][R_part][n_heads]
+// o_part [kAttnMaxSplits][R_part][d] fp32, ml_part [kAttnMaxSplits][R_part][n_heads].
+// With ctx_out, the normalised context goes there in fp32 instead of `out`, at
+// row ctx_off[b] + position (the packed row of an all-rows map), and each
+// (row, head)'s log normaliser to lse_out[row_pos * n_heads + head].
 hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* seq_len, const RowMap& rm, int S, int n_heads, int head_dim, int splits,
-                            float* o_part, float2* ml_part, int R_part, void* out, hipStream_t st);
+                            float* o_part, float2* ml_part, int R_part, void* out, hipStream_t st,
+                            float* ctx_out = nullptr, const int32_t* ctx_off = nullptr, float* lse_out = nullptr);
+// Approximate context of every row of rm_all that is not active (inv < 0):
+// ctx_new[r] = ctx_cache[pos] + sum_j exp(q_cache[pos].k_j / sqrt(dh) - lse[pos]) dv_j
+// per head, j over the active rows of the row's sequence (k_act / dv_act packed
+// by key_off, key_cnt of them).
+hipError_t launch_attention_approx(dl_dtype dt, const void* q_cache, const void* k_act, const void* dv_act,
+                                   const int32_t* key_off, const int32_t* key_cnt, const float* lse,
+                                   const int32_t* inv, const float* ctx_cache, float* ctx_new, const RowMap& rm_all,
+                                   int S, int n_heads, int head_dim, hipStream_t st);
 
 // ---- LM head reduction and unmasking -------------------------------------------------
 // Packed rows [m_base, m_base + M_max) of the row map; P is [splits][M_max][V].

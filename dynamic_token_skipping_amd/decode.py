@@ -91,6 +91,15 @@ class Decoder:
         self.h_prev2 = torch.zeros((B, S, d), dtype=tdt, device=device) if two else None
         self.scores2 = torch.zeros((B, S), dtype=torch.float32, device=device) if two else None
         self.sel2 = L.SelectionTensors(B, S, device) if two else None
+        per_layer = bool(getattr(sched, "per_layer", False))
+        Ln = model.n_layers
+        self.q_cache = torch.zeros((Ln, B, S, d), dtype=tdt, device=device) if per_layer else None
+        self.ctx_cache = torch.zeros((Ln, B, S, d), dtype=torch.float32, device=device) if per_layer else None
+        self.lse_cache = (torch.zeros((Ln, B, S, model.n_heads), dtype=torch.float32, device=device)
+                          if per_layer else None)
+        self.y_cache = torch.zeros((Ln, B, S, d), dtype=torch.float32, device=device) if per_layer else None
+        self.layer_scores = torch.zeros((B, S), dtype=torch.float32, device=device) if per_layer else None
+        self.sel_l = L.SelectionTensors(B, S, device) if per_layer else None
         self.dims = model.dims(B, S)
         self.model_struct = model.struct(B, S)
         self.ws = L.workspace(self.dims, sum(self.seq_lens), device)
@@ -100,7 +109,9 @@ class Decoder:
                              L.ptr(self.h_prev), L.ptr(self.k_cache), L.ptr(self.v_cache), L.ptr(self.h_final),
                              L.ptr(self.conf), L.ptr(self.argmax), L.ptr(self.logits), L.ptr(self.scores),
                              self.sel.struct(), L.ptr(self.h_prev2), L.ptr(self.scores2),
-                             self.sel2.struct() if two else L.Selection())
+                             self.sel2.struct() if two else L.Selection(), L.ptr(self.q_cache),
+                             L.ptr(self.ctx_cache), L.ptr(self.lse_cache), L.ptr(self.y_cache),
+                             L.ptr(self.layer_scores), self.sel_l.struct() if per_layer else L.Selection())
         self.steps_per_block = sched.steps // (sched.gen_len // sched.block_len)
         self.per_step = sched.block_len // self.steps_per_block
 
@@ -112,7 +123,7 @@ class Decoder:
     def params(self, step: int, force_refresh: Optional[bool] = None, keep: Optional[float] = None,
                mode: int = L.DL_SEL_TOPK, threshold: float = 0.0, n_unmask: Optional[int] = None,
                response_only: Optional[bool] = None, keep2: Optional[float] = None, mode2: int = L.DL_SEL_TOPK,
-               threshold2: float = 0.0) -> L.StepParams:
+               threshold2: float = 0.0, mode_l: int = L.DL_SEL_TOPK, threshold_l: float = 0.0) -> L.StepParams:
         s = self.sched
         refresh = (is_refresh_step(step, self.steps_per_block, s.refresh_interval) if force_refresh is None
                    else force_refresh)
@@ -126,7 +137,9 @@ class Decoder:
                             int(bool(response_only) and not refresh),
                             ctypes.cast(self._prompt_len_host, ctypes.POINTER(ctypes.c_int32)), s2, mode2,
                             getattr(s, "keep2", 1.0) if keep2 is None else keep2, threshold2,
-                            L.SCORE_TENSORS[getattr(s, "score_tensor", "hidden")])
+                            L.SCORE_TENSORS[getattr(s, "score_tensor", "hidden")],
+                            int(bool(getattr(s, "per_layer", False))), mode_l,
+                            getattr(s, "keep_layer", 0.0) or s.keep, threshold_l)
 
     def step(self, step: int, **kw):
         L.dl_denoise_step(self.model_struct, self.state, self.params(step, **kw), self.ws)

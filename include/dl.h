@@ -141,6 +141,14 @@ typedef struct {
   void *h_prev2;              /* [B, S, d] input of layer skip_layer2 as last computed */
   float *scores2;             /* [B, S] second-level scores (-inf outside sel), or NULL */
   dl_selection sel2;          /* rows recomputed in layers [skip_layer2, L) and the LM head */
+  /* per-layer re-selection (used when params.per_layer != 0; may be NULL
+   * otherwise).  Layers below skip_layer are not used. */
+  void *q_cache;              /* [L, B, S, d] rotated queries of each layer */
+  float *ctx_cache;           /* [L, B, S, d] fp32 attention contexts (before Wo) */
+  float *lse_cache;           /* [L, B, S, n_heads] fp32 log softmax normalisers of those contexts */
+  float *y_cache;             /* [L, B, S, d] fp32 layer outputs */
+  float *layer_scores;        /* [B, S] the last layer's saliency 1 - cos, or NULL */
+  dl_selection sel_l;         /* rows through the last layer and the LM head */
 } dl_state;
 
 typedef struct {
@@ -178,6 +186,22 @@ typedef struct {
   /* Tensor scored at the first level (DL_TENSOR_KEY / DL_TENSOR_VALUE need
    * skip_layer < n_layers).  The second level always scores hidden states. */
   dl_score_tensor score_tensor;
+  /* DyLLM per-layer re-selection (technical summary section 2B): from layer
+   * skip_layer on, the active rows (sel at layer s, then the previous layer's
+   * salient rows) get fresh q/K/V and exact attention; every other row's
+   * context is updated approximately as C + S dV, S_ij = exp(q_i.k_j /
+   * sqrt(dh) - lse_i) from its cached query and normaliser and the active
+   * rows' previous keys, dV_j the change of their values; the rows with the
+   * largest 1 - cos(C_new, C_cached) (top-k of keep_ratio_l of the valid
+   * length, or above threshold_l) go through Wo and the FFN, the others keep
+   * their cached output.  ctx_cache takes every row's new context; q_cache
+   * and lse_cache change for the active rows.  A refresh step fills every
+   * cache for every row.  Needs skip_layer < n_layers, one skip level and
+   * full-context steps. */
+  int32_t per_layer;
+  dl_select_mode mode_l;
+  float keep_ratio_l;
+  float threshold_l;
 } dl_step_params;
 
 /* ---------------------------------------------------------------------------
@@ -271,7 +295,8 @@ typedef enum {
   DL_KC_ATTN = 1,        /* attention */
   DL_KC_LMHEAD = 2,      /* LM head product with its confidence statistics */
   DL_KC_GEMM_TILED = 3,  /* layer products on more rows (prefix layers, refresh steps) */
-  DL_KC_COUNT = 4
+  DL_KC_APPROX = 4,      /* approximate context update of the per-layer variant */
+  DL_KC_COUNT = 5
 } dl_kernel_class;
 
 typedef struct {

@@ -88,3 +88,9 @@ def sync_from_oracle(dec, b: int, st) -> None:
         put(dec.logits[b, :n], st.logits.astype(np.float32))
     if getattr(dec, "h_prev2", None) is not None and st.h_prev2 is not None:
         put(dec.h_prev2[b, :n], st.h_prev2.astype(np.float32), dt)
+    if getattr(dec, "ctx_cache", None) is not None and st.C is not None:
+        for li in range(len(st.C)):
+            put(dec.q_cache[li, b, :n], st.Q[li].astype(np.float32), dt)
+            put(dec.ctx_cache[li, b, :n], st.C[li].astype(np.float32))
+            put(dec.lse_cache[li, b, :n], st.LSE[li].astype(np.float32))
+            put(dec.y_cache[li, b, :n], st.Y[li].astype(np.float32))
