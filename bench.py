@@ -11,8 +11,10 @@ step is a full refresh).  Inputs are resident in HBM before the timed region.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-variants]
 
 Prints one JSON line.  After the timed headline steps it also times, on the
-same model and prompt, the nested two-level skip and the response-only
-schedule ("variants"; their own steps/s, not part of `value`).
+same model, the nested two-level skip, the response-only schedule and the key
+score on the same prompt, and the long-context shape (4096 + 512) with the
+plain skip and with DyLLM's per-layer re-selection ("variants"; their own
+steps/s, not part of `value`).
 """
 from __future__ import annotations
 
@@ -57,13 +59,31 @@ def variant_schedules(sched):
     }
 
 
-def time_variant(torch, Decoder, dev_model, prompts, sched, steps: int, warmup: int):
+def long_context_schedules():
+    """The long-context shape (4096 prompt + 512 masked tokens, blocks of 64,
+    keep 1/8: 576 of 4608 rows) with the plain early skip and with DyLLM's
+    per-layer re-selection at keep 1/8 (section 2B)."""
+    import dataclasses
+    import workloads
+    wl = workloads.workload("long8b")
+    return wl, {
+        "long_context_skip": wl.sched,
+        "long_context_per_layer": dataclasses.replace(wl.sched, per_layer=True, keep_layer=wl.sched.keep),
+    }
+
+
+def time_variant(torch, Decoder, dev_model, prompts, sched, steps: int, warmup: int, timed_classes=()):
     """steps/s of one variant schedule (fresh caches; warm-up, then `steps`
-    steps from the decode's first step, refresh steps included)."""
+    steps from the decode's first step, refresh steps included).  The kernel
+    classes in timed_classes are timed (one launch in 8) and reported."""
+    from dynamic_token_skipping_amd import dl_timing_enable, dl_timing_read, dl_timing_reset
     dec = Decoder(dev_model, prompts, sched)
     for t in range(warmup):
         dec.step(t % sched.steps)
     dec.reset()
+    dl_timing_reset()
+    for kc in timed_classes:
+        dl_timing_enable(kc, 8)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -74,6 +94,8 @@ def time_variant(torch, Decoder, dev_model, prompts, sched, steps: int, warmup: 
         dec.step(t)
     end.record()
     torch.cuda.synchronize()
+    for kc in timed_classes:
+        dl_timing_enable(kc, 0)
     ms = start.elapsed_time(end)
     kinds = {"refresh": 0, "response_only": 0, "full_context": 0}
     for i in range(steps):
@@ -84,7 +106,14 @@ def time_variant(torch, Decoder, dev_model, prompts, sched, steps: int, warmup: 
            "gen_tokens_per_s": round(steps / (ms / 1e3) * dec.per_step * dec.B, 3), "steps": steps,
            "step_kinds": kinds, "keep": sched.keep, "skip_layer": sched.skip_layer,
            "skip_layer2": sched.skip_layer2, "keep2": sched.keep2, "response_interval": sched.response_interval,
-           "score_tensor": sched.score_tensor}
+           "score_tensor": sched.score_tensor, "per_layer": sched.per_layer, "keep_layer": sched.keep_layer,
+           "rows": dec.S, "batch": dec.B}
+    for kc in timed_classes:
+        tm = dl_timing_read(kc)
+        out[f"kernel_class_{kc}"] = {"launches_timed": tm["launches"],
+                                     "avg_launch_us": round(tm["ms"] * 1e3 / max(tm["launches"], 1), 2),
+                                     "TFLOP/s": round(tm["flops"] / max(tm["ms"], 1e-9) / 1e9, 1),
+                                     "GB/s": round(tm["bytes"] / max(tm["ms"], 1e-9) / 1e6, 1)}
     del dec
     torch.cuda.empty_cache()
     return out
@@ -196,8 +225,8 @@ def main():
     import torch
 
     import workloads
-    from dynamic_token_skipping_amd import (DL_KC_ATTN, DL_KC_GEMM, DL_KC_GEMM_TILED, DL_KC_LMHEAD, Decoder,
-                                            DeviceModel, dl_timing_enable, dl_timing_read, dl_timing_reset)
+    from dynamic_token_skipping_amd import (DL_KC_APPROX, DL_KC_ATTN, DL_KC_GEMM, DL_KC_GEMM_TILED, DL_KC_LMHEAD,
+                                            Decoder, DeviceModel, dl_timing_enable, dl_timing_read, dl_timing_reset)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = workloads.workload(args.workload)
@@ -281,6 +310,13 @@ def main():
         torch.cuda.empty_cache()
         out["variants"] = {name: time_variant(torch, Decoder, dev_model, prompts, vs, min(args.steps, 128), 8)
                            for name, vs in variant_schedules(sched).items()}
+        # long context on the same weights: one block of 64 steps (its refresh included)
+        lwl, lscheds = long_context_schedules()
+        lprompts, _ = workloads.make_prompt(lwl)
+        for name, vs in lscheds.items():
+            out["variants"][name] = time_variant(torch, Decoder, dev_model, lprompts, vs, 64, 4,
+                                                 (DL_KC_ATTN, DL_KC_APPROX) if vs.per_layer else (DL_KC_ATTN,))
+        out["variants"]["kernel_classes"] = {str(DL_KC_ATTN): "attention", str(DL_KC_APPROX): "approximate context"}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, model, prompts)
     else:
