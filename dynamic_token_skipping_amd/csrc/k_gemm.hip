@@ -472,10 +472,13 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
 
-  // item i of thread t covers tile row (t >> 3) + 32 i, columns ((t & 7) * 8, +8)
-  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(A) + (size_t)m0 * K, (short)0, (min(M - m0, kBM)) * K * 2, 0x00020000);
-  __amdgpu_buffer_rsrc_t wr[CW];
+  // item i of thread t covers tile row (t >> 3) + 32 i, columns ((t & 7) * 8, +8).
+  // The per-lane offsets are fixed; each K step moves the buffer descriptors'
+  // base (scalar arithmetic only), and a padding step gets descriptors with no
+  // records, so every lane reads zeros through the range check.
+  const char* abase = reinterpret_cast<const char*>(A + (size_t)m0 * K);
+  const int arec = min(M - m0, kBM) * K * 2;   // rows >= M are past the records at every step
+  const char* wbase[CW];
   uint32_t aoff[CH], woff[CW];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
@@ -488,7 +491,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
     int sg, r;
     wrow_index<BN>(W, n0 + row, sg, r);         // rows 32i..32i+31 share a segment for every mode
     sg = __builtin_amdgcn_readfirstlane(sg);
-    wr[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(W.p[sg]), (short)0, W.seg_bytes, 0x00020000);
+    wbase[i] = static_cast<const char*>(W.p[sg]);
     woff[i] = (uint32_t)((r * K + ks0 * kBK + kc) * 2);
   }
   uint4 ra[kDepthL][CH], rw[kDepthL][CW];
@@ -496,11 +499,17 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
   auto issue = [&](int step, uint4 (&a)[CH], uint4 (&w)[CW]) {
     const bool in = step < nk;
     const int sr = step + rot >= nk ? step + rot - nk : step + rot;
-    const uint32_t ks = (uint32_t)sr * (kBK * 2);
+    const int ks = in ? sr * (kBK * 2) : 0;
+    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase) + ks, (short)0,
+                                                                         in ? arec - ks : 0, 0x00020000);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      a[i] = buf_load16(ar, in ? aoff[i] + ks : kOob);
-      if (i < CW) w[i] = buf_load16(wr[i], in ? woff[i] + ks : kOob);
+      a[i] = buf_load16(ar, aoff[i]);
+      if (i < CW) {
+        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(wbase[i]) + ks, (short)0, in ? (int)W.seg_bytes - ks : 0, 0x00020000);
+        w[i] = buf_load16(wr, woff[i]);
+      }
     }
   };
   auto store = [&](int buf, const uint4 (&a)[CH], const uint4 (&w)[CW]) {
