@@ -464,10 +464,14 @@ bool attention_supported(dl_dtype dt, int S, int head_dim) {
   return head_dim <= 128 && head_dim % 2 == 0 && S <= kMaxKeysSimt;
 }
 
+#ifndef DTSK_ATTN_SPLIT_CAP
+#define DTSK_ATTN_SPLIT_CAP kAttnMaxSplits
+#endif
+
 int attention_splits(dl_dtype dt, int head_dim, int S, int n_heads, const RowMap& rm, int R_part) {
   if (!use_mfma_attention(dt, head_dim) || rm.R_max > R_part) return 1;
   const int base = std::max(1, rm.T_max * n_heads);
-  int s = std::min(kAttnMaxSplits, std::max(1, kAttnTargetBlocks / base));
+  int s = std::min(std::min(kAttnMaxSplits, DTSK_ATTN_SPLIT_CAP), std::max(1, kAttnTargetBlocks / base));
   s = std::min(s, std::max(1, S / (2 * kTK)));     // at least two key tiles per chunk
   return s;
 }

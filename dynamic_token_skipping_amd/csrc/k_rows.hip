@@ -513,34 +513,69 @@ __global__ __launch_bounds__(kRowThreads) void k_copy_sel(const char* __restrict
 
 // Split sum + residual + (optional) RMSNorm of the next sub-block, one block
 // per packed row: x += sum_s P[s]; out = T(x / sqrt(mean(x^2) + eps) * g).
+// 4 consecutive storage-type values <-> float4
+template <typename T>
+__device__ __forceinline__ float4 load4(const T* p) {
+  if constexpr (sizeof(T) == 4) {
+    return *reinterpret_cast<const float4*>(p);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                       __uint_as_float(w.y & 0xffff0000u));
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float4 v) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(p) = v;
+  } else {
+    const uint32_t a = (uint32_t)from_f32<T>(v.x).u | ((uint32_t)from_f32<T>(v.y).u << 16);
+    const uint32_t b = (uint32_t)from_f32<T>(v.z).u | ((uint32_t)from_f32<T>(v.w).u << 16);
+    *reinterpret_cast<uint2*>(p) = make_uint2(a, b);
+  }
+}
+
+constexpr int kRedSplits = 8;   // partials loaded together (more are added in a second loop)
+
 template <typename T, int kChunks>
 __global__ __launch_bounds__(kRowThreads) void k_reduce_rows(const float* __restrict__ P, int splits, int M_max,
                                                              const int32_t* __restrict__ n_rows, int d,
                                                              float* __restrict__ x, const T* __restrict__ g, float eps,
                                                              T* __restrict__ out) {
-  // d == kChunks * 4 * kRowThreads: every thread owns kChunks float4 of the row,
-  // and all of its loads are issued before any is used
+  // d == kChunks * 4 * kRowThreads: every thread owns kChunks float4 of the
+  // row; its row, partial and gain loads are all issued before the first is
+  // used, and the partials are added in split order
   __shared__ float red[16];
   const int r = blockIdx.x;
   if (r >= *n_rows) return;
   const size_t sstride = (size_t)M_max * d;
   float4* xr = reinterpret_cast<float4*>(x + (size_t)r * d);
   const float4* pr = reinterpret_cast<const float4*>(P + (size_t)r * d);
-  float4 v[kChunks];
+  float4 v[kChunks], ps[kRedSplits][kChunks], gv[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) v[c] = xr[threadIdx.x + c * kRowThreads];
-  for (int s = 0; s < splits; ++s) {
-    float4 ps[kChunks];
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) ps[c] = pr[s * (sstride / 4) + threadIdx.x + c * kRowThreads];
+  for (int s = 0; s < kRedSplits; ++s)
+    if (s < splits)
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      v[c].x += ps[c].x;
-      v[c].y += ps[c].y;
-      v[c].z += ps[c].z;
-      v[c].w += ps[c].w;
-    }
-  }
+      for (int c = 0; c < kChunks; ++c) ps[s][c] = pr[s * (sstride / 4) + threadIdx.x + c * kRowThreads];
+  if (g)
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) gv[c] = load4(g + (threadIdx.x + c * kRowThreads) * 4);
+  auto add = [&](float4& a, const float4& b) {
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+  };
+#pragma unroll
+  for (int s = 0; s < kRedSplits; ++s)
+    if (s < splits)
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) add(v[c], ps[s][c]);
+  for (int s = kRedSplits; s < splits; ++s)
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) add(v[c], pr[s * (sstride / 4) + threadIdx.x + c * kRowThreads]);
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
@@ -552,13 +587,10 @@ __global__ __launch_bounds__(kRowThreads) void k_reduce_rows(const float* __rest
   const float inv = 1.f / sqrtf(ss / (float)d + eps);
   T* o = out + (size_t)r * d;
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const int col = (threadIdx.x + c * kRowThreads) * 4;
-    o[col] = from_f32<T>(v[c].x * inv * to_f32(g[col]));
-    o[col + 1] = from_f32<T>(v[c].y * inv * to_f32(g[col + 1]));
-    o[col + 2] = from_f32<T>(v[c].z * inv * to_f32(g[col + 2]));
-    o[col + 3] = from_f32<T>(v[c].w * inv * to_f32(g[col + 3]));
-  }
+  for (int c = 0; c < kChunks; ++c)
+    store4(o + (threadIdx.x + c * kRowThreads) * 4,
+           make_float4(v[c].x * inv * gv[c].x, v[c].y * inv * gv[c].y, v[c].z * inv * gv[c].z,
+                       v[c].w * inv * gv[c].w));
 }
 
 // Any width: the plain loop.
