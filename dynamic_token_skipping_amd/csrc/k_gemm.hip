@@ -246,6 +246,10 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #ifndef DTSK_T128_MIN_TILES
 #define DTSK_T128_MIN_TILES 160
 #endif
+// the LM head on up to 128 rows through the tiled kernel (else the skinny one)
+#ifndef DTSK_TILED_LM
+#define DTSK_TILED_LM 1
+#endif
 #ifndef DTSK_KROT
 #define DTSK_KROT 1
 #endif
@@ -694,7 +698,8 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
   const int n_seg = epi_kind == EPI_QKV ? N / 3 : epi_kind == EPI_SWIGLU ? N / 2 : N;
   // up to 128 rows: one 128 x 64 tile row of the tiled kernel when the shape
   // allows it (more column tiles than 128-wide ones); else the skinny kernel
-  const bool tiled_small = DTSK_TILED_SMALL && M > 64 && M <= 128 && epi_kind != EPI_LM && N % 64 == 0 &&
+  const bool tiled_small = DTSK_TILED_SMALL && M > 64 && M <= 128 && (DTSK_TILED_LM || epi_kind != EPI_LM) &&
+                           N % 64 == 0 && (epi_kind != EPI_LM || N % 128 == 0) &&
                            (epi_kind != EPI_QKV || (head_dim == 128 && n_seg % 128 == 0)) &&
                            (epi_kind != EPI_SWIGLU || F % 32 == 0);
   if (tiled_small) {
@@ -702,8 +707,9 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
     p.sep_epi = 0;
     // 128-wide column tiles when there are enough of them to spread over the
     // chip; else 64-wide ones (twice the workgroups)
-    const bool wide = N % 128 == 0 && N / 128 >= DTSK_T128_MIN_TILES && epi_kind != EPI_QKV &&
-                      (epi_kind != EPI_SWIGLU || F % 64 == 0);
+    // (the LM statistics are kept per 128-wide column tile)
+    const bool wide = epi_kind == EPI_LM || (N % 128 == 0 && N / 128 >= DTSK_T128_MIN_TILES && epi_kind != EPI_QKV &&
+                                             (epi_kind != EPI_SWIGLU || F % 64 == 0));
     p.bn = wide ? 128 : 64;
     p.wmode = epi_kind == EPI_SWIGLU ? 1 : epi_kind == EPI_QKV ? 2 : 0;
     if (epi_kind == EPI_NONE) {
