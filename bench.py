@@ -29,6 +29,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+# full8b step rooflines: the sum over a step's stages of max(algorithmic bytes /
+# 8 TB/s, FLOPs / 2.5 PFLOP/s).  A skip step moves ~15.1 GB (28 kept-row layers,
+# 4 full prefix layers, the LM head on the kept rows): 1.98 ms; a refresh step
+# ~16.6 GB and 7.3 TFLOP (every layer and the LM head on all 512 rows): 2.92 ms.
+ROOFLINE_SKIP_MS = 1.98
+ROOFLINE_REFRESH_MS = 2.92
 
 
 def parse():
@@ -116,6 +122,37 @@ def time_variant(torch, Decoder, dev_model, prompts, sched, steps: int, warmup: 
                                      "GB/s": round(tm["bytes"] / max(tm["ms"], 1e-9) / 1e6, 1)}
     del dec
     torch.cuda.empty_cache()
+    return out
+
+
+def time_step_kinds(torch, dec, sched, n_steps: int):
+    """Median time of the skip steps and of the refresh steps among the
+    decode's first n_steps steps, each step bracketed by its own pair of HIP
+    events on the decode stream."""
+    dec.reset()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
+    for t in range(n_steps):
+        ev[t][0].record()
+        dec.step(t)
+        ev[t][1].record()
+    torch.cuda.synchronize()
+    times = {"refresh": [], "skip": []}
+    for t in range(n_steps):
+        times["refresh" if dec.params(t).full_refresh else "skip"].append(ev[t][0].elapsed_time(ev[t][1]))
+
+    def med(v):
+        v = sorted(v)
+        return round(v[len(v) // 2], 4) if v else None
+    out = {"sample": f"steps 0..{n_steps - 1} of the decode, one event pair per step",
+           "skip_steps": len(times["skip"]), "refresh_steps": len(times["refresh"]),
+           "skip_ms_median": med(times["skip"]), "refresh_ms_median": med(times["refresh"]),
+           "roofline_skip_ms": ROOFLINE_SKIP_MS, "roofline_refresh_ms": ROOFLINE_REFRESH_MS}
+    if out["skip_ms_median"]:
+        out["skip_frac_of_roofline"] = round(ROOFLINE_SKIP_MS / out["skip_ms_median"], 4)
+    if out["refresh_ms_median"]:
+        out["refresh_frac_of_roofline"] = round(ROOFLINE_REFRESH_MS / out["refresh_ms_median"], 4)
+    dec.reset()
     return out
 
 
@@ -304,6 +341,8 @@ def main():
         "copy_probe": copy,
         "wall_s": round(wall, 3),
     }
+    if wl.name == "full8b":
+        out["step_times"] = time_step_kinds(torch, dec, sched, 2 * sched.steps_per_block)
     if not args.no_variants and wl.name == "full8b":
         dev_model = dec.m
         del dec
