@@ -40,15 +40,39 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 //  mode 2 rope pairs:  segmented, and inside each 128-row head a 64-wide tile
 //                      holds dims [32p, 32p+32) then [64+32p, 64+32p+32), so
 //                      that RoPE partners j and j+64 share the tile
+//  mode 3 ragged interleaved: the n_seg rows of each of the two segments are
+//                      cut into n_tiles runs, run t = [t*n_seg/n_tiles,
+//                      (t+1)*n_seg/n_tiles) of at most BN/2 rows; tile t holds
+//                      run t of segment 0 from column 0 and run t of segment 1
+//                      from column BN/2; the columns past each run are empty
+//                      (their weights read as zeros).  With n_tiles = the
+//                      compute units, every unit streams the same share.
 struct WMap {
   const void* p[4];
   int mode;
   int n_seg;
   int seg_bytes;  // bytes of one segment (buffer range of the skinny path)
+  int n_tiles;    // mode 3: column tiles
 };
 
+// Mode 3: the rows [a, a + h) of each segment that tile t holds.
+__device__ __forceinline__ void ragged_run(const WMap& w, int t, int& a, int& h) {
+  a = (int)((long long)t * w.n_seg / w.n_tiles);
+  h = (int)((long long)(t + 1) * w.n_seg / w.n_tiles) - a;
+}
+
+// r < 0: an empty column of a mode 3 tile.
 template <int BN>
 __device__ __forceinline__ void wrow_index(const WMap& w, int n, int& sg, int& r) {
+  if (w.mode == 3) {
+    const int c = n % BN;
+    int a, h;
+    ragged_run(w, n / BN, a, h);
+    sg = c / (BN / 2);
+    const int j = c % (BN / 2);
+    r = j < h ? a + j : -1;
+    return;
+  }
   if (w.mode == 1) {
     const int c = n % BN;
     sg = c / (BN / 2);
@@ -79,13 +103,15 @@ inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 template <int BN, int TS, int NT = 256, int MAXM = 128>
 __device__ __forceinline__ void tile_epilogue(const Epilogue& e, float* __restrict__ T, const WMap& w, int n0, int M) {
   const int t = threadIdx.x;
-  if (e.kind == EPI_SWIGLU) {            // mode 1: gate in [0, BN/2), up in [BN/2, BN)
+  if (e.kind == EPI_SWIGLU) {            // modes 1, 3: gate in [0, BN/2), up in [BN/2, BN)
     constexpr int H = BN / 2;
+    int a = (n0 / BN) * H, h = H;         // the tile's inner columns [a, a + h)
+    if (w.mode == 3) ragged_run(w, n0 / BN, a, h);
     uint16_t* out = reinterpret_cast<uint16_t*>(e.act_out);
-    for (int idx = t; idx < M * H; idx += NT) {
-      const int m = idx / H, c = idx % H;
+    for (int idx = t; idx < M * h; idx += NT) {
+      const int m = idx / h, c = idx - m * h;
       const float gt = T[m * TS + c], up = T[m * TS + H + c];
-      out[(size_t)m * e.F + (n0 / BN) * H + c] = from_f32<bf16_t>(gt / (1.f + expf(-gt)) * up).u;
+      out[(size_t)m * e.F + a + c] = from_f32<bf16_t>(gt / (1.f + expf(-gt)) * up).u;
     }
   } else if (e.kind == EPI_QKV) {
     int sg, r0;
@@ -249,6 +275,9 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 // the LM head on up to 128 rows through the tiled kernel (else the skinny one)
 #ifndef DTSK_TILED_LM
 #define DTSK_TILED_LM 1
+#endif
+#ifndef DTSK_RAGGED
+#define DTSK_RAGGED 1
 #endif
 #ifndef DTSK_KROT
 #define DTSK_KROT 1
@@ -441,6 +470,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
 // 2 x 2 layout, each a 64 x BN/2 sub-tile.
 // ---------------------------------------------------------------------------
 constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kRaggedTiles = 256;   // ragged column tiles: one per compute unit
 constexpr int kLds = kRowElems;
 // dynamic LDS of the tiled kernel: the A/W double buffers, or the finished
 // fp32 tile of the epilogue, whichever is larger
@@ -496,7 +526,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
     wrow_index<BN>(W, n0 + row, sg, r);         // rows 32i..32i+31 share a segment for every mode
     sg = __builtin_amdgcn_readfirstlane(sg);
     wbase[i] = static_cast<const char*>(W.p[sg]);
-    woff[i] = (uint32_t)((r * K + ks0 * kBK + kc) * 2);
+    woff[i] = r < 0 ? kOob : (uint32_t)((r * K + ks0 * kBK + kc) * 2);   // empty columns read zeros
   }
   uint4 ra[kDepthL][CH], rw[kDepthL][CW];
   const int rot = k_rotation(nt, nk);   // the row tiles of a column tile walk K together
@@ -681,7 +711,7 @@ hipError_t launch_tiled(const GemmPlan& plan, const void* A, int M_max, const in
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int n_mt = cdiv(M_max, kBM), n_nt = N / BN;
+  const int n_mt = cdiv(M_max, kBM), n_nt = plan.tiles > 0 ? plan.tiles : N / BN;
   const int grid = cdiv(n_nt, 8) * 8 * n_mt * plan.splits;
   hipLaunchKernelGGL((k_gemm_mfma<BN>), dim3(grid), dim3(256), lds_bytes, st, (const uint16_t*)A, M_max, n_rows,
                      m_base, K, w, N, plan.splits, n_mt, n_nt, P, epi);
@@ -712,6 +742,13 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
                                              (epi_kind != EPI_SWIGLU || F % 64 == 0));
     p.bn = wide ? 128 : 64;
     p.wmode = epi_kind == EPI_SWIGLU ? 1 : epi_kind == EPI_QKV ? 2 : 0;
+    // gate|up: one ragged column tile per compute unit (each holding F / 256
+    // gate rows and the matching up rows) when that is at least 32 rows
+    if (DTSK_RAGGED && epi_kind == EPI_SWIGLU && F >= 32 * kRaggedTiles && F <= 64 * kRaggedTiles) {
+      p.bn = 128;
+      p.wmode = 3;
+      p.tiles = kRaggedTiles;
+    }
     if (epi_kind == EPI_NONE) {
       const int tiles = N / p.bn;
       int s = 1;
@@ -776,7 +813,10 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
   for (int i = 0; i < 4; ++i) w.p[i] = Wseg[i];
   w.mode = plan.wmode;
   w.n_seg = n_seg;
-  w.seg_bytes = (int)std::min<long long>((long long)(plan.wmode == 1 ? N / 2 : n_seg) * K * 2, 0x7fffffffLL);
+  w.seg_bytes = (int)std::min<long long>((long long)(plan.wmode == 1 || plan.wmode == 3 ? N / 2 : n_seg) * K * 2,
+                                          0x7fffffffLL);
+  w.n_tiles = plan.tiles;
+  if (plan.wmode == 3) w.n_seg = N / 2;
   if (M_max <= 0) return hipSuccess;
   if (plan.kind == GEMM_SKINNY) {
     if (plan.bn == 64) return launch_skinny_bn<64>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);

@@ -108,8 +108,10 @@ struct GemmPlan {
   int splits;  // > 1 only with EPI_NONE: fp32 partials reduced by launch_reduce_rows
   int bn;      // column tile
   int mi;      // skinny: 16-row blocks of A
-  int wmode;   // weight-row order: 0 segmented, 1 gate|up interleaved, 2 RoPE pairs
+  int wmode;   // weight-row order: 0 segmented, 1 gate|up interleaved, 2 RoPE pairs,
+               // 3 gate|up interleaved over `tiles` ragged column tiles
   int sep_epi; // 1: the product writes fp32 partials and the separate epilogue kernels finish
+  int tiles;   // column tiles when they are not N / bn (wmode 3), else 0
 };
 // The epilogue kind decides the tile the fused epilogue needs; a GEMM_SIMT
 // plan leaves the epilogue to the separate kernels below.
