@@ -6,7 +6,10 @@
 // that Wq|Wk|Wv run as one product (segmented: segment = n / n_seg), and
 // Wgate|Wup as one product whose every column tile holds gate rows in its
 // first half and the matching up rows in its second half (interleaved), so
-// that SwiGLU needs nothing outside the tile.
+// that SwiGLU needs nothing outside the tile.  On up to 128 rows the gate|up
+// product is cut into exactly one column tile per compute unit, each holding
+// d_ffn / 256 gate rows and the matching up rows (ragged, the rest of the
+// tile empty), so that every unit streams the same share of the weights.
 //
 //  * k_gemm_skinny (bf16, M <= 128): the weight-streaming regime.  Each of
 //    the 4 waves owns BN/4 output columns for all M rows; its weight rows go
