@@ -156,6 +156,61 @@ def time_step_kinds(torch, dec, sched, n_steps: int):
     return out
 
 
+def time_layer_steps(torch, model, n_steps: int = 30, warmup: int = 3):
+    """One layer step of the 8B-class layer per keep ratio, on the layer8b
+    inputs (cached and current hidden states, K/V caches, confidences):
+    score + top-k over the 512 rows, gather of the kept fp32 rows, the partial
+    attention sub-block and the FFN on them.  Consecutive steps take layers 4,
+    5 and 6 of the loaded model in turn (1.2 GB of distinct weights), so the
+    weights stream from HBM.  Algorithmic bytes: the layer's weights, its K/V
+    cache and the two score inputs read once, and the kept fp32 rows read and
+    written; FLOPs: 2 * params * k + 4 * k * S * d."""
+    import workloads
+    from dynamic_token_skipping_amd import (DL_F32, DL_SEL_TOPK, SelectionTensors, dl_ffn_rows, dl_gather,
+                                            dl_partial_attn, dl_score_select, make_dims, workspace)
+    wl = workloads.workload("layer8b")
+    dims, S = wl.dims, wl.prompt_len
+    d = dims.d
+    st = workloads.make_layer_state(wl, "cuda")
+    dl = make_dims(1, S, d, dims.n_heads, dims.head_dim, dims.d_ffn, dims.vocab, 1, "bf16")
+    ws = workspace(dl, S)
+    seq = torch.tensor([S], dtype=torch.int32, device="cuda")
+    x_s = st["h_cur"].float()                      # the fp32 layer input the kept rows are gathered from
+    kc, vc = st["k"].clone(), st["v"].clone()
+    layers = [model["layers"][i] for i in (4, 5, 6)]
+    params = dims.layer_params()
+    sel = SelectionTensors(1, S)
+    x_rows = torch.empty((S, d), dtype=torch.float32, device="cuda")
+    out = {"sample": f"{n_steps} layer steps per keep after {warmup} warm-up steps, one event pair around them"}
+    for keep in (1.0, 0.5, 0.25, 0.125):
+        k = max(1, min(S, int(keep * S + 0.999999)))
+
+        def one(i):
+            lw = layers[i % len(layers)]
+            dl_score_select(dl, st["h_cur"], st["h_prev"], st["conf"], seq, "esdllm", 0.5, DL_SEL_TOPK, keep, 0.0,
+                            sel, ws=ws)
+            dl_gather(dl, x_s, d, DL_F32, sel, k, x_rows)
+            dl_partial_attn(dl, lw, x_rows, sel, seq, k, kc, vc, ws)
+            dl_ffn_rows(dl, lw, x_rows, sel, k, ws)
+        for i in range(warmup):
+            one(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n_steps):
+            one(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n_steps
+        alg = 2 * params + 2 * (2 * S * d * 2) + k * d * 8
+        flops = 2 * params * k + 4 * k * S * d
+        out[f"keep_{keep}"] = {"rows": k, "us": round(us, 2), "alg_MB": round(alg / 1e6, 1),
+                               "GB/s": round(alg / us / 1e3, 1), "frac_hbm": round(alg / us / 1e3 / PEAK_HBM_GBS, 4),
+                               "TFLOP/s": round(flops / us / 1e6, 1),
+                               "frac_mfma": round(flops / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
 def cpu_baseline(wl, model_gpu, prompts, budget_s: float = 20.0):
     """Time the fp64 oracle on host cores on a bounded sample of one skip step.
 
@@ -343,6 +398,7 @@ def main():
     }
     if wl.name == "full8b":
         out["step_times"] = time_step_kinds(torch, dec, sched, 2 * sched.steps_per_block)
+        out["layer_steps"] = time_layer_steps(torch, model)
     if not args.no_variants and wl.name == "full8b":
         dev_model = dec.m
         del dec
