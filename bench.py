@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--timing-stride", type=int, default=8,
                     help="time about one launch in this many of each kernel class (1: every launch)")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the nested-skip, response-only and key-score variant timings")
+                    help="only the headline decode: skip the per-step, one-layer and variant timings")
     return ap.parse_args()
 
 
@@ -396,7 +396,7 @@ def main():
         "copy_probe": copy,
         "wall_s": round(wall, 3),
     }
-    if wl.name == "full8b":
+    if wl.name == "full8b" and not args.no_variants:
         out["step_times"] = time_step_kinds(torch, dec, sched, 2 * sched.steps_per_block)
         out["layer_steps"] = time_layer_steps(torch, model)
     if not args.no_variants and wl.name == "full8b":
