@@ -303,23 +303,21 @@ dl_status product(const Ctx& c, dl_kernel_class kc, const void* A, const RowMap&
   if (kc == DL_KC_GEMM && rows > 128) kc = DL_KC_GEMM_TILED;
   Epilogue ge = e;
   if (p.sep_epi && e.kind != EPI_NONE) ge.kind = EPI_NONE;   // partials; the epilogue kernel finishes
+  // the timed region holds the product and, when it has one, its separate
+  // epilogue kernel (rows addressed through the full row map)
   DL_CHECK_HIP(timed(kc, c.st, gemm_bytes(d, rows, N, K), 2.0 * rows * N * K, [&] {
-    return launch_gemm(d.dtype, p, A, rows, rm.n_rows, m_base, K, seg, n_seg, N, P, ge, c.st);
-  }));
-  if (p.sep_epi) {
-    // Separate epilogue kernels (rows addressed through the full row map).
+    hipError_t err = launch_gemm(d.dtype, p, A, rows, rm.n_rows, m_base, K, seg, n_seg, N, P, ge, c.st);
+    if (err != hipSuccess || !p.sep_epi) return err;
     switch (e.kind) {
       case EPI_QKV:
-        DL_CHECK_HIP(launch_epi_qkv(d.dtype, P, p.splits, rm, d.S, d.d, d.head_dim, e.rope, e.q_out, e.k_cache,
-                                    e.v_cache, c.st));
-        break;
-      case EPI_SWIGLU: DL_CHECK_HIP(launch_epi_swiglu(d.dtype, P, p.splits, rm, d.d_ffn, e.act_out, c.st)); break;
-      case EPI_LM:
-        DL_CHECK_HIP(launch_lm_reduce(P, p.splits, rm, m_base, rows, d.vocab, conf, argmax, e.logits, c.st));
-        break;
-      default: break;
+        return launch_epi_qkv(d.dtype, P, p.splits, rm, d.S, d.d, d.head_dim, e.rope, e.q_out, e.k_cache, e.v_cache,
+                              c.st);
+      case EPI_SWIGLU: return launch_epi_swiglu(d.dtype, P, p.splits, rm, d.d_ffn, e.act_out, c.st);
+      case EPI_LM: return launch_lm_reduce(P, p.splits, rm, m_base, rows, d.vocab, conf, argmax, e.logits, c.st);
+      default: return hipSuccess;
     }
-  } else if (e.kind == EPI_LM) {
+  }));
+  if (!p.sep_epi && e.kind == EPI_LM) {
     DL_CHECK_HIP(launch_lm_merge(e.lm_part, e.lm_tiles, rm, m_base, rows, conf, argmax, c.st));
   }
   return DL_OK;

@@ -279,6 +279,9 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #ifndef DTSK_TILED_LM
 #define DTSK_TILED_LM 1
 #endif
+#ifndef DTSK_QKV_SPLIT
+#define DTSK_QKV_SPLIT 1
+#endif
 #ifndef DTSK_RAGGED
 #define DTSK_RAGGED 1
 #endif
@@ -745,6 +748,17 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
                                              (epi_kind != EPI_SWIGLU || F % 64 == 0));
     p.bn = wide ? 128 : 64;
     p.wmode = epi_kind == EPI_SWIGLU ? 1 : epi_kind == EPI_QKV ? 2 : 0;
+    // Wq|Wk|Wv: 128-wide tiles of natural column order and a K split in two
+    // (192 workgroups, half the A rows each); k_epi_qkv_heads sums the two
+    // partials and applies RoPE and the cache writes
+    if (DTSK_QKV_SPLIT && epi_kind == EPI_QKV && head_dim <= 128 && n_seg % 128 == 0 && (N / 128) * 2 <= 256 &&
+        nk >= 2) {
+      p.bn = 128;
+      p.wmode = 0;
+      p.sep_epi = 1;
+      p.splits = 2;
+      return p;
+    }
     // gate|up: one ragged column tile per compute unit (each holding F / 256
     // gate rows and the matching up rows) when that is at least 32 rows
     if (DTSK_RAGGED && epi_kind == EPI_SWIGLU && F >= 32 * kRaggedTiles && F <= 64 * kRaggedTiles) {

@@ -682,6 +682,56 @@ __global__ __launch_bounds__(kRowThreads) void k_epi_qkv(const float* __restrict
   }
 }
 
+// The same epilogue with one workgroup per (packed row, segment, head):
+// thread j takes the pair (j, j + head_dim/2) of its head (for v, those two
+// dims), loads every split's partial before the first add, sums them in split
+// order from 0 (the result equals k_epi_qkv's bit for bit) and writes.
+constexpr int kEpiMaxSplits = 8;
+template <typename T>
+__global__ __launch_bounds__(64) void k_epi_qkv_heads(const float* __restrict__ P, int splits, int M_max,
+                                                      const int32_t* __restrict__ n_rows,
+                                                      const int32_t* __restrict__ row_pos,
+                                                      const int32_t* __restrict__ row_seq, int S, int d, int n_heads,
+                                                      int head_dim, const float2* __restrict__ rope,
+                                                      T* __restrict__ q_out, T* __restrict__ k_cache,
+                                                      T* __restrict__ v_cache) {
+  const int r = blockIdx.x;
+  if (r >= *n_rows) return;
+  const int seg = blockIdx.y / n_heads, h = blockIdx.y - seg * n_heads;
+  const int half = head_dim >> 1, j = threadIdx.x;
+  if (j >= half) return;
+  const int p = row_pos[r];
+  const size_t stride = (size_t)M_max * 3 * d;
+  const float* base = P + (size_t)r * 3 * d + seg * d + h * head_dim + j;
+  float v1[kEpiMaxSplits], v2[kEpiMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kEpiMaxSplits; ++s)
+    if (s < splits) {
+      v1[s] = base[s * stride];
+      v2[s] = base[s * stride + half];
+    }
+  float a = 0.f, bb = 0.f;
+#pragma unroll
+  for (int s = 0; s < kEpiMaxSplits; ++s)
+    if (s < splits) {
+      a += v1[s];
+      bb += v2[s];
+    }
+  const size_t col = (size_t)h * head_dim + j;
+  if (seg == 2) {
+    v_cache[(size_t)p * d + col] = from_f32<T>(a);
+    v_cache[(size_t)p * d + col + half] = from_f32<T>(bb);
+    return;
+  }
+  const int pos = p - row_seq[r] * S;
+  const float2 cs = rope[pos * half + j];
+  const float o1 = a * cs.x - bb * cs.y;
+  const float o2 = bb * cs.x + a * cs.y;
+  T* dst = seg == 0 ? q_out + (size_t)r * d : k_cache + (size_t)p * d;
+  dst[col] = from_f32<T>(o1);
+  dst[col + half] = from_f32<T>(o2);
+}
+
 __global__ __launch_bounds__(kRowThreads) void k_epi_residual(const float* __restrict__ P, int splits, int M_max,
                                                               const int32_t* __restrict__ n_rows, int N,
                                                               float* __restrict__ x) {
@@ -1125,6 +1175,19 @@ hipError_t launch_rope_table(int S, int head_dim, float base, float2* table, hip
 
 hipError_t launch_epi_qkv(dl_dtype dt, const float* P, int splits, const RowMap& rm, int S, int d, int head_dim,
                           const float2* rope, void* q_out, void* k_cache, void* v_cache, hipStream_t st) {
+  if (rm.R_max <= 0) return hipSuccess;
+  if (head_dim <= 128 && d % head_dim == 0 && splits >= 1 && splits <= kEpiMaxSplits) {
+    const dim3 grid(rm.R_max, 3 * (d / head_dim));
+    if (dt == DL_F32)
+      hipLaunchKernelGGL(k_epi_qkv_heads<float>, grid, dim3(64), 0, st, P, splits, rm.R_max, rm.n_rows, rm.row_pos,
+                         rm.row_seq, S, d, d / head_dim, head_dim, rope, (float*)q_out, (float*)k_cache,
+                         (float*)v_cache);
+    else
+      hipLaunchKernelGGL(k_epi_qkv_heads<bf16_t>, grid, dim3(64), 0, st, P, splits, rm.R_max, rm.n_rows, rm.row_pos,
+                         rm.row_seq, S, d, d / head_dim, head_dim, rope, (bf16_t*)q_out, (bf16_t*)k_cache,
+                         (bf16_t*)v_cache);
+    return hipGetLastError();
+  }
   if (dt == DL_F32)
     hipLaunchKernelGGL(k_epi_qkv<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows,
                        rm.row_pos, rm.row_seq, S, d, head_dim, rope, (float*)q_out, (float*)k_cache,
