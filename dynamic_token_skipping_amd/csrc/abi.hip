@@ -12,6 +12,10 @@
 
 using namespace dtsk;
 
+namespace dtsk {
+thread_local DispatchEvents* g_region_events = nullptr;
+}
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -222,9 +226,11 @@ struct TimingClass {
 };
 TimingClass g_timing[DL_KC_COUNT];
 
-// Runs `launch` bracketed by events when the class is enabled.
+// Runs `launch`; when the class is enabled and the launch is sampled, the
+// region's kernels carry the event pair on their dispatch packets.
 template <typename F>
 hipError_t timed(dl_kernel_class kc, hipStream_t st, double bytes, double flops, F&& launch) {
+  (void)st;  // the events follow the kernels' own stream
   TimingClass& t = g_timing[kc];
   if (!t.enabled) return launch();
   const uint32_t i = t.seq++;
@@ -232,12 +238,15 @@ hipError_t timed(dl_kernel_class kc, hipStream_t st, double bytes, double flops,
     ++t.dropped;
     return launch();
   }
-  hipError_t e = hipEventRecord(t.ev[2 * t.used], st);
+  DispatchEvents de{t.ev[2 * t.used], t.ev[2 * t.used + 1]};
+  g_region_events = &de;
+  const hipError_t e = launch();
+  g_region_events = nullptr;
   if (e != hipSuccess) return e;
-  e = launch();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(t.ev[2 * t.used + 1], st);
-  if (e != hipSuccess) return e;
+  if (de.start != nullptr) {  // no kernel of the region took the events
+    ++t.dropped;
+    return hipSuccess;
+  }
   ++t.used;
   t.bytes += bytes;
   t.flops += flops;

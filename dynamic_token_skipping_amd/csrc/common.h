@@ -1,6 +1,7 @@
 // Internal helpers shared by the HIP kernels of libdtsk (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,6 +34,33 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) {
   }
   return r;
 }
+
+// Kernel timing by dispatch timestamps.  While a timed region of the calling
+// thread is open, `g_region_events` points at its event pair: every launch
+// through DTSK_LAUNCH then binds `stop` to its own dispatch packet, and the
+// first one also binds `start` (which it clears), so the pair spans the
+// region's kernels from the first one's start to the last one's end, with no
+// marker packets between the launches.
+struct DispatchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+extern thread_local DispatchEvents* g_region_events;
+
+template <typename F, typename... Args>
+inline void launch_with_events(DispatchEvents* ev, F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st,
+                               Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev->start, ev->stop, 0u, args...);
+  ev->start = nullptr;
+}
+
+#define DTSK_LAUNCH(kernel, grid, block, lds, st, ...)                                              \
+  do {                                                                                              \
+    if (::dtsk::DispatchEvents* ev_ = ::dtsk::g_region_events)                                      \
+      ::dtsk::launch_with_events(ev_, kernel, dim3(grid), dim3(block), (uint32_t)(lds), st, __VA_ARGS__); \
+    else                                                                                            \
+      hipLaunchKernelGGL(kernel, grid, block, lds, st, __VA_ARGS__);                                \
+  } while (0)
 
 // Round an fp32 value to the storage type and back (what a store + load does).
 template <typename T>

@@ -491,21 +491,21 @@ hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, con
     const int chunk = (S + splits * kTK - 1) / (splits * kTK) * kTK;
     const float scale_log2 = scale * 1.4426950408889634f;
     const int grid = (n_heads * splits + 7) / 8 * 8 * rm.T_max;
-    hipLaunchKernelGGL(k_attn_mfma<false>, dim3(grid), dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k_cache,
+    DTSK_LAUNCH(k_attn_mfma<false>, dim3(grid), dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k_cache,
                        (const uint16_t*)v_cache, seq_len, rm.row_seq, rm.tile_row0, rm.tile_rows, S, d, n_heads,
                        scale_log2, chunk, splits, rm.T_max, (uint16_t*)out, o_part, ml_part, R_part, co, ApproxIn{});
     if (splits > 1 && rm.R_max > 0)
-      hipLaunchKernelGGL(k_attn_combine, dim3(rm.R_max, (d + 255) / 256), dim3(64), 0, st, o_part, ml_part,
+      DTSK_LAUNCH(k_attn_combine, dim3(rm.R_max, (d + 255) / 256), dim3(64), 0, st, o_part, ml_part,
                          rm.n_rows, rm.row_seq, seq_len, d, n_heads, chunk, splits, R_part, (uint16_t*)out, co, S);
     return hipGetLastError();
   }
   dim3 grid(rm.R_max, n_heads);
   if (rm.R_max <= 0) return hipSuccess;
   if (dt == DL_F32)
-    hipLaunchKernelGGL(k_attn_simt<float>, grid, dim3(kSimtThreads), 0, st, (const float*)q, (const float*)k_cache,
+    DTSK_LAUNCH(k_attn_simt<float>, grid, dim3(kSimtThreads), 0, st, (const float*)q, (const float*)k_cache,
                        (const float*)v_cache, seq_len, rm.n_rows, rm.row_seq, S, d, head_dim, scale, (float*)out, co);
   else
-    hipLaunchKernelGGL(k_attn_simt<bf16_t>, grid, dim3(kSimtThreads), 0, st, (const bf16_t*)q,
+    DTSK_LAUNCH(k_attn_simt<bf16_t>, grid, dim3(kSimtThreads), 0, st, (const bf16_t*)q,
                        (const bf16_t*)k_cache, (const bf16_t*)v_cache, seq_len, rm.n_rows, rm.row_seq, S, d,
                        head_dim, scale, (bf16_t*)out, co);
   return hipGetLastError();
@@ -524,7 +524,7 @@ hipError_t launch_attention_approx(dl_dtype dt, const void* q_cache, const void*
     if (rm_all.tq != kTQ || rm_all.T_max <= 0) return rm_all.T_max < 0 ? hipErrorInvalidValue : hipSuccess;
     const float scale_log2 = scale * 1.4426950408889634f;
     const int grid = (n_heads + 7) / 8 * 8 * rm_all.T_max;
-    hipLaunchKernelGGL(k_attn_mfma<true>, dim3(grid), dim3(256), 0, st, nullptr, nullptr, nullptr, nullptr,
+    DTSK_LAUNCH(k_attn_mfma<true>, dim3(grid), dim3(256), 0, st, nullptr, nullptr, nullptr, nullptr,
                        rm_all.row_seq, rm_all.tile_row0, rm_all.tile_rows, S, d, n_heads, scale_log2, S, 1,
                        rm_all.T_max, nullptr, nullptr, nullptr, 0, CtxOut{}, a);
     return hipGetLastError();
@@ -532,9 +532,9 @@ hipError_t launch_attention_approx(dl_dtype dt, const void* q_cache, const void*
   if (S > kMaxKeysSimt) return hipErrorInvalidValue;
   dim3 grid(rm_all.R_max, n_heads);
   if (dt == DL_F32)
-    hipLaunchKernelGGL(k_attn_approx_simt<float>, grid, dim3(kSimtThreads), 0, st, a, S, d, head_dim, scale);
+    DTSK_LAUNCH(k_attn_approx_simt<float>, grid, dim3(kSimtThreads), 0, st, a, S, d, head_dim, scale);
   else
-    hipLaunchKernelGGL(k_attn_approx_simt<bf16_t>, grid, dim3(kSimtThreads), 0, st, a, S, d, head_dim, scale);
+    DTSK_LAUNCH(k_attn_approx_simt<bf16_t>, grid, dim3(kSimtThreads), 0, st, a, S, d, head_dim, scale);
   return hipGetLastError();
 }
 

@@ -690,7 +690,7 @@ hipError_t launch_skinny(const GemmPlan& plan, const void* A, int M_max, const i
                          const WMap& w, int N, float* P, const Epilogue& epi, hipStream_t st) {
   const int n_nt = N / BN;
   const int grid = cdiv(n_nt, 8) * 8 * plan.splits;
-  hipLaunchKernelGGL((k_gemm_skinny<MI, BN>), dim3(grid), dim3(256), 0, st, (const uint16_t*)A, M_max, n_rows, m_base,
+  DTSK_LAUNCH((k_gemm_skinny<MI, BN>), dim3(grid), dim3(256), 0, st, (const uint16_t*)A, M_max, n_rows, m_base,
                      K, w, N, plan.splits, n_nt, P, epi);
   return hipGetLastError();
 }
@@ -719,7 +719,7 @@ hipError_t launch_tiled(const GemmPlan& plan, const void* A, int M_max, const in
   }
   const int n_mt = cdiv(M_max, kBM), n_nt = plan.tiles > 0 ? plan.tiles : N / BN;
   const int grid = cdiv(n_nt, 8) * 8 * n_mt * plan.splits;
-  hipLaunchKernelGGL((k_gemm_mfma<BN>), dim3(grid), dim3(256), lds_bytes, st, (const uint16_t*)A, M_max, n_rows,
+  DTSK_LAUNCH((k_gemm_mfma<BN>), dim3(grid), dim3(256), lds_bytes, st, (const uint16_t*)A, M_max, n_rows,
                      m_base, K, w, N, plan.splits, n_mt, n_nt, P, epi);
   return hipGetLastError();
 }
@@ -845,10 +845,10 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
   }
   dim3 grid(cdiv(N, 64), cdiv(M_max, 64));
   if (dt == DL_F32)
-    hipLaunchKernelGGL(k_gemm_simt<float>, grid, dim3(256), 0, st, (const float*)A, M_max, n_rows, m_base, K, w, N,
+    DTSK_LAUNCH(k_gemm_simt<float>, grid, dim3(256), 0, st, (const float*)A, M_max, n_rows, m_base, K, w, N,
                        P);
   else
-    hipLaunchKernelGGL(k_gemm_simt<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)A, M_max, n_rows, m_base, K, w, N,
+    DTSK_LAUNCH(k_gemm_simt<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)A, M_max, n_rows, m_base, K, w, N,
                        P);
   return hipGetLastError();
 }

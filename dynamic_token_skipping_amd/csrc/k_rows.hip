@@ -991,20 +991,20 @@ inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 hipError_t launch_identity_sel(const int32_t* seq_len, int B, int S, int32_t* sel_idx, int32_t* sel_count,
                                hipStream_t st, const int32_t* start) {
   dim3 grid(cdiv(S, 256), B);
-  hipLaunchKernelGGL(k_identity_sel, grid, dim3(256), 0, st, seq_len, start, S, sel_idx, sel_count);
+  DTSK_LAUNCH(k_identity_sel, grid, dim3(256), 0, st, seq_len, start, S, sel_idx, sel_count);
   return hipGetLastError();
 }
 
 hipError_t launch_row_off(const int32_t* sel_count, int32_t* row_off, int B, hipStream_t st) {
-  hipLaunchKernelGGL(k_row_off, dim3(1), dim3(64), 0, st, sel_count, row_off, B);
+  DTSK_LAUNCH(k_row_off, dim3(1), dim3(64), 0, st, sel_count, row_off, B);
   return hipGetLastError();
 }
 
 hipError_t launch_rowmap(const int32_t* sel_idx, const int32_t* sel_count, const int32_t* row_off, int B, int S,
                          const RowMap& rm, hipStream_t st) {
-  hipLaunchKernelGGL(k_tiles, dim3(1), dim3(256), 0, st, sel_count, row_off, B, rm.n_rows, rm.tile_row0,
+  DTSK_LAUNCH(k_tiles, dim3(1), dim3(256), 0, st, sel_count, row_off, B, rm.n_rows, rm.tile_row0,
                      rm.tile_rows, rm.T_max, rm.tq);
-  hipLaunchKernelGGL(k_rowmap, dim3(cdiv(rm.R_max, 256)), dim3(256), 0, st, sel_idx, row_off, B, S, rm.R_max,
+  DTSK_LAUNCH(k_rowmap, dim3(cdiv(rm.R_max, 256)), dim3(256), 0, st, sel_idx, row_off, B, S, rm.R_max,
                      rm.row_pos, rm.row_seq);
   return hipGetLastError();
 }
@@ -1014,10 +1014,10 @@ hipError_t launch_gather_sel(size_t elem_bytes, const void* src, int w, const in
   if (R_max <= 0) return hipSuccess;
   const size_t rb = elem_bytes * (size_t)w;
   if (rb % 16 == 0)
-    hipLaunchKernelGGL((k_copy_sel<16, false>), dim3(R_max), dim3(kRowThreads), 0, st, (const char*)src, rb, sel_idx,
+    DTSK_LAUNCH((k_copy_sel<16, false>), dim3(R_max), dim3(kRowThreads), 0, st, (const char*)src, rb, sel_idx,
                        row_off, B, S, (char*)dst);
   else
-    hipLaunchKernelGGL((k_copy_sel<1, false>), dim3(R_max), dim3(kRowThreads), 0, st, (const char*)src, rb, sel_idx,
+    DTSK_LAUNCH((k_copy_sel<1, false>), dim3(R_max), dim3(kRowThreads), 0, st, (const char*)src, rb, sel_idx,
                        row_off, B, S, (char*)dst);
   return hipGetLastError();
 }
@@ -1027,10 +1027,10 @@ hipError_t launch_scatter_sel(size_t elem_bytes, const void* rows, int w, const 
   if (R_max <= 0) return hipSuccess;
   const size_t rb = elem_bytes * (size_t)w;
   if (rb % 16 == 0)
-    hipLaunchKernelGGL((k_copy_sel<16, true>), dim3(R_max), dim3(kRowThreads), 0, st, (const char*)rows, rb, sel_idx,
+    DTSK_LAUNCH((k_copy_sel<16, true>), dim3(R_max), dim3(kRowThreads), 0, st, (const char*)rows, rb, sel_idx,
                        row_off, B, S, (char*)cache);
   else
-    hipLaunchKernelGGL((k_copy_sel<1, true>), dim3(R_max), dim3(kRowThreads), 0, st, (const char*)rows, rb, sel_idx,
+    DTSK_LAUNCH((k_copy_sel<1, true>), dim3(R_max), dim3(kRowThreads), 0, st, (const char*)rows, rb, sel_idx,
                        row_off, B, S, (char*)cache);
   return hipGetLastError();
 }
@@ -1044,20 +1044,20 @@ hipError_t launch_score(dl_dtype dt, const void* h_cur, const float* x_packed, c
   dim3 grid = rm ? dim3(cdiv(rm->R_max, 4)) : dim3(cdiv(S, 4), B);
   if (dt == DL_F32) {
     if (x_packed)
-      hipLaunchKernelGGL((k_score<float, true>), grid, dim3(256), 0, st, (const float*)h_cur, x_packed, off_all, rp,
+      DTSK_LAUNCH((k_score<float, true>), grid, dim3(256), 0, st, (const float*)h_cur, x_packed, off_all, rp,
                          rn, (float*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
     else
-      hipLaunchKernelGGL((k_score<float, false>), grid, dim3(256), 0, st, (const float*)h_cur, x_packed, off_all, rp,
+      DTSK_LAUNCH((k_score<float, false>), grid, dim3(256), 0, st, (const float*)h_cur, x_packed, off_all, rp,
                          rn, (float*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
   } else {
     if (x_packed && d % 512 == 0)
-      hipLaunchKernelGGL(k_score_bf16x8, grid, dim3(256), 0, st, x_packed, off_all, rp, rn, (bf16_t*)h_prev, conf,
+      DTSK_LAUNCH(k_score_bf16x8, grid, dim3(256), 0, st, x_packed, off_all, rp, rn, (bf16_t*)h_prev, conf,
                          seq_len, S, d, (int)kind, alpha, scores);
     else if (x_packed)
-      hipLaunchKernelGGL((k_score<bf16_t, true>), grid, dim3(256), 0, st, (const bf16_t*)h_cur, x_packed, off_all, rp,
+      DTSK_LAUNCH((k_score<bf16_t, true>), grid, dim3(256), 0, st, (const bf16_t*)h_cur, x_packed, off_all, rp,
                          rn, (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
     else
-      hipLaunchKernelGGL((k_score<bf16_t, false>), grid, dim3(256), 0, st, (const bf16_t*)h_cur, x_packed, off_all,
+      DTSK_LAUNCH((k_score<bf16_t, false>), grid, dim3(256), 0, st, (const bf16_t*)h_cur, x_packed, off_all,
                          rp, rn, (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
   }
   return hipGetLastError();
@@ -1066,7 +1066,7 @@ hipError_t launch_score(dl_dtype dt, const void* h_cur, const float* x_packed, c
 hipError_t launch_select(const float* scores, const int32_t* seq_len, int B, int S, dl_select_mode mode, float keep,
                          float threshold, int32_t* sel_idx, int32_t* sel_count, hipStream_t st,
                          const int32_t* cand_idx, const int32_t* cand_cnt, const int32_t* k_base) {
-  hipLaunchKernelGGL(k_select, dim3(B), dim3(kSelThreads), 0, st, scores, seq_len, S, (int)mode, keep, threshold,
+  DTSK_LAUNCH(k_select, dim3(B), dim3(kSelThreads), 0, st, scores, seq_len, S, (int)mode, keep, threshold,
                      cand_idx, cand_cnt, k_base, sel_idx, sel_count);
   return hipGetLastError();
 }
@@ -1074,10 +1074,10 @@ hipError_t launch_select(const float* scores, const int32_t* seq_len, int B, int
 hipError_t launch_embed(dl_dtype dt, const int32_t* tokens, const RowMap& rm, const void* E, int d, float* x,
                         hipStream_t st) {
   if (dt == DL_F32)
-    hipLaunchKernelGGL(k_embed<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, tokens, rm.row_pos,
+    DTSK_LAUNCH(k_embed<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, tokens, rm.row_pos,
                        (const float*)E, d, x);
   else
-    hipLaunchKernelGGL(k_embed<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, tokens, rm.row_pos,
+    DTSK_LAUNCH(k_embed<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, tokens, rm.row_pos,
                        (const bf16_t*)E, d, x);
   return hipGetLastError();
 }
@@ -1087,25 +1087,25 @@ hipError_t launch_gather(size_t elem_bytes, const void* src, const int32_t* src_
   if (rm.R_max <= 0) return hipSuccess;
   const size_t rb = elem_bytes * (size_t)w;
   if (rb % 16 == 0)
-    hipLaunchKernelGGL(k_gather<16>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)src, src_off, src_inv, S,
+    DTSK_LAUNCH(k_gather<16>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)src, src_off, src_inv, S,
                        rb, rm.row_pos, rm.row_seq, (char*)dst);
   else
-    hipLaunchKernelGGL(k_gather<1>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)src, src_off, src_inv, S,
+    DTSK_LAUNCH(k_gather<1>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)src, src_off, src_inv, S,
                        rb, rm.row_pos, rm.row_seq, (char*)dst);
   return hipGetLastError();
 }
 
 hipError_t launch_inv_rows(const RowMap& rm, int BS, int32_t* inv, hipStream_t st) {
-  hipLaunchKernelGGL(k_fill_i32, dim3(cdiv(BS, 256)), dim3(256), 0, st, inv, -1, (size_t)BS);
+  DTSK_LAUNCH(k_fill_i32, dim3(cdiv(BS, 256)), dim3(256), 0, st, inv, -1, (size_t)BS);
   if (rm.R_max > 0)
-    hipLaunchKernelGGL(k_inv_rows, dim3(cdiv(rm.R_max, 256)), dim3(256), 0, st, rm.row_pos, rm.n_rows, rm.R_max, inv);
+    DTSK_LAUNCH(k_inv_rows, dim3(cdiv(rm.R_max, 256)), dim3(256), 0, st, rm.row_pos, rm.n_rows, rm.R_max, inv);
   return hipGetLastError();
 }
 
 hipError_t launch_rope_rows(float* x, const RowMap& rm, int S, int d, int head_dim, const float2* rope,
                             hipStream_t st) {
   if (rm.R_max <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rope_rows, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, rm.row_pos, rm.row_seq, S, d, head_dim,
+  DTSK_LAUNCH(k_rope_rows, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, rm.row_pos, rm.row_seq, S, d, head_dim,
                      rope);
   return hipGetLastError();
 }
@@ -1114,10 +1114,10 @@ hipError_t launch_gather_cvt(dl_dtype dt, const float* src, const int32_t* src_o
                              void* dst, hipStream_t st) {
   if (rm.R_max <= 0) return hipSuccess;
   if (dt == DL_F32)
-    hipLaunchKernelGGL(k_gather_cvt<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, src, src_off, S, d, rm.row_pos,
+    DTSK_LAUNCH(k_gather_cvt<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, src, src_off, S, d, rm.row_pos,
                        rm.row_seq, (float*)dst);
   else
-    hipLaunchKernelGGL(k_gather_cvt<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, src, src_off, S, d,
+    DTSK_LAUNCH(k_gather_cvt<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, src, src_off, S, d,
                        rm.row_pos, rm.row_seq, (bf16_t*)dst);
   return hipGetLastError();
 }
@@ -1126,35 +1126,35 @@ hipError_t launch_value_change(dl_dtype dt, const void* V, const void* v_old, co
                                hipStream_t st) {
   if (rm.R_max <= 0) return hipSuccess;
   if (dt == DL_F32)
-    hipLaunchKernelGGL(k_value_change<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const float*)V,
+    DTSK_LAUNCH(k_value_change<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const float*)V,
                        (const float*)v_old, rm.row_pos, d, (float*)dv);
   else
-    hipLaunchKernelGGL(k_value_change<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const bf16_t*)V,
+    DTSK_LAUNCH(k_value_change<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const bf16_t*)V,
                        (const bf16_t*)v_old, rm.row_pos, d, (bf16_t*)dv);
   return hipGetLastError();
 }
 
 hipError_t launch_fill_scores(float* scores, float v, const int32_t* seq_len, int B, int S, hipStream_t st) {
-  hipLaunchKernelGGL(k_fill_valid, dim3(cdiv(S, 256), B), dim3(256), 0, st, scores, v, seq_len, S);
+  DTSK_LAUNCH(k_fill_valid, dim3(cdiv(S, 256), B), dim3(256), 0, st, scores, v, seq_len, S);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter(size_t elem_bytes, const void* rows, int w, const RowMap& rm, void* cache, hipStream_t st) {
   const size_t rb = elem_bytes * (size_t)w;
   if (rb % 16 == 0)
-    hipLaunchKernelGGL(k_scatter<16>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)rows, rb, rm.row_pos,
+    DTSK_LAUNCH(k_scatter<16>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)rows, rb, rm.row_pos,
                        (char*)cache);
   else
-    hipLaunchKernelGGL(k_scatter<1>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)rows, rb, rm.row_pos,
+    DTSK_LAUNCH(k_scatter<1>, dim3(rm.R_max), dim3(kRowThreads), 0, st, (const char*)rows, rb, rm.row_pos,
                        (char*)cache);
   return hipGetLastError();
 }
 
 hipError_t launch_store_rows(dl_dtype dt, const float* x, int w, const RowMap& rm, void* dst, hipStream_t st) {
   if (dt == DL_F32)
-    hipLaunchKernelGGL(k_store_rows<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, w, rm.row_pos, (float*)dst);
+    DTSK_LAUNCH(k_store_rows<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, w, rm.row_pos, (float*)dst);
   else
-    hipLaunchKernelGGL(k_store_rows<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, w, rm.row_pos,
+    DTSK_LAUNCH(k_store_rows<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, w, rm.row_pos,
                        (bf16_t*)dst);
   return hipGetLastError();
 }
@@ -1168,7 +1168,7 @@ hipError_t launch_rmsnorm(dl_dtype dt, const float* x, const void* g, const RowM
 
 hipError_t launch_rope_table(int S, int head_dim, float base, float2* table, hipStream_t st) {
   const int half = head_dim / 2;
-  hipLaunchKernelGGL(k_rope_table, dim3(cdiv((long long)S * half, 256)), dim3(256), 0, st, S, half, head_dim,
+  DTSK_LAUNCH(k_rope_table, dim3(cdiv((long long)S * half, 256)), dim3(256), 0, st, S, half, head_dim,
                      (double)base, table);
   return hipGetLastError();
 }
@@ -1179,38 +1179,38 @@ hipError_t launch_epi_qkv(dl_dtype dt, const float* P, int splits, const RowMap&
   if (head_dim <= 128 && d % head_dim == 0 && splits >= 1 && splits <= kEpiMaxSplits) {
     const dim3 grid(rm.R_max, 3 * (d / head_dim));
     if (dt == DL_F32)
-      hipLaunchKernelGGL(k_epi_qkv_heads<float>, grid, dim3(64), 0, st, P, splits, rm.R_max, rm.n_rows, rm.row_pos,
+      DTSK_LAUNCH(k_epi_qkv_heads<float>, grid, dim3(64), 0, st, P, splits, rm.R_max, rm.n_rows, rm.row_pos,
                          rm.row_seq, S, d, d / head_dim, head_dim, rope, (float*)q_out, (float*)k_cache,
                          (float*)v_cache);
     else
-      hipLaunchKernelGGL(k_epi_qkv_heads<bf16_t>, grid, dim3(64), 0, st, P, splits, rm.R_max, rm.n_rows, rm.row_pos,
+      DTSK_LAUNCH(k_epi_qkv_heads<bf16_t>, grid, dim3(64), 0, st, P, splits, rm.R_max, rm.n_rows, rm.row_pos,
                          rm.row_seq, S, d, d / head_dim, head_dim, rope, (bf16_t*)q_out, (bf16_t*)k_cache,
                          (bf16_t*)v_cache);
     return hipGetLastError();
   }
   if (dt == DL_F32)
-    hipLaunchKernelGGL(k_epi_qkv<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows,
+    DTSK_LAUNCH(k_epi_qkv<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows,
                        rm.row_pos, rm.row_seq, S, d, head_dim, rope, (float*)q_out, (float*)k_cache,
                        (float*)v_cache);
   else
-    hipLaunchKernelGGL(k_epi_qkv<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows,
+    DTSK_LAUNCH(k_epi_qkv<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows,
                        rm.row_pos, rm.row_seq, S, d, head_dim, rope, (bf16_t*)q_out, (bf16_t*)k_cache,
                        (bf16_t*)v_cache);
   return hipGetLastError();
 }
 
 hipError_t launch_epi_residual(const float* P, int splits, const RowMap& rm, int N, float* x, hipStream_t st) {
-  hipLaunchKernelGGL(k_epi_residual, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows, N, x);
+  DTSK_LAUNCH(k_epi_residual, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows, N, x);
   return hipGetLastError();
 }
 
 hipError_t launch_epi_swiglu(dl_dtype dt, const float* P, int splits, const RowMap& rm, int F, void* out,
                              hipStream_t st) {
   if (dt == DL_F32)
-    hipLaunchKernelGGL(k_epi_swiglu<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
+    DTSK_LAUNCH(k_epi_swiglu<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
                        rm.n_rows, F, (float*)out);
   else
-    hipLaunchKernelGGL(k_epi_swiglu<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
+    DTSK_LAUNCH(k_epi_swiglu<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
                        rm.n_rows, F, (bf16_t*)out);
   return hipGetLastError();
 }
@@ -1218,7 +1218,7 @@ hipError_t launch_epi_swiglu(dl_dtype dt, const float* P, int splits, const RowM
 hipError_t launch_lm_reduce(const float* P, int splits, const RowMap& rm, int m_base, int M_max, int V, float* conf,
                             int32_t* argmax, float* logits_out, hipStream_t st) {
   if (M_max <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_lm_reduce, dim3(M_max), dim3(kRowThreads), 0, st, P, splits, M_max, rm.n_rows, m_base,
+  DTSK_LAUNCH(k_lm_reduce, dim3(M_max), dim3(kRowThreads), 0, st, P, splits, M_max, rm.n_rows, m_base,
                      rm.row_pos, V, conf, argmax, logits_out);
   return hipGetLastError();
 }
@@ -1229,16 +1229,16 @@ static hipError_t reduce_rows_t(const float* P, int splits, const RowMap& rm, in
   const T* gg = (const T*)g;
   T* oo = (T*)out;
   if (d == 4096)
-    hipLaunchKernelGGL((k_reduce_rows<T, 4>), dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
+    DTSK_LAUNCH((k_reduce_rows<T, 4>), dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
                        rm.n_rows, d, x, gg, eps, oo);
   else if (d == 2048)
-    hipLaunchKernelGGL((k_reduce_rows<T, 2>), dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
+    DTSK_LAUNCH((k_reduce_rows<T, 2>), dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
                        rm.n_rows, d, x, gg, eps, oo);
   else if (d == 1024)
-    hipLaunchKernelGGL((k_reduce_rows<T, 1>), dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
+    DTSK_LAUNCH((k_reduce_rows<T, 1>), dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
                        rm.n_rows, d, x, gg, eps, oo);
   else
-    hipLaunchKernelGGL(k_reduce_rows_any<T>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows,
+    DTSK_LAUNCH(k_reduce_rows_any<T>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows,
                        d, x, gg, eps, oo);
   return hipGetLastError();
 }
@@ -1253,7 +1253,7 @@ hipError_t launch_reduce_rows(dl_dtype dt, const float* P, int splits, const Row
 hipError_t launch_lm_merge(const float* lm_part, int lm_tiles, const RowMap& rm, int m_base, int M_max, float* conf,
                            int32_t* argmax, hipStream_t st) {
   if (M_max <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_lm_merge, dim3(M_max), dim3(kRowThreads), 0, st, (const float4*)lm_part, lm_tiles, rm.n_rows,
+  DTSK_LAUNCH(k_lm_merge, dim3(M_max), dim3(kRowThreads), 0, st, (const float4*)lm_part, lm_tiles, rm.n_rows,
                      m_base, rm.row_pos, conf, argmax);
   return hipGetLastError();
 }
@@ -1261,14 +1261,14 @@ hipError_t launch_lm_merge(const float* lm_part, int lm_tiles, const RowMap& rm,
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
   const int blocks = (int)std::min<size_t>(1024, (n + 255) / 256);
-  hipLaunchKernelGGL(k_fill_i32, dim3(blocks), dim3(256), 0, st, p, v, n);
+  DTSK_LAUNCH(k_fill_i32, dim3(blocks), dim3(256), 0, st, p, v, n);
   return hipGetLastError();
 }
 
 hipError_t launch_unmask(int32_t* tokens, uint8_t* masked, const float* conf, const int32_t* argmax,
                          const int32_t* prompt_len, const int32_t* seq_len, int B, int S, int block, int block_len,
                          int n_unmask, hipStream_t st) {
-  hipLaunchKernelGGL(k_unmask, dim3(B), dim3(kMaxBlockLen), 0, st, tokens, masked, conf, argmax, prompt_len, seq_len,
+  DTSK_LAUNCH(k_unmask, dim3(B), dim3(kMaxBlockLen), 0, st, tokens, masked, conf, argmax, prompt_len, seq_len,
                      S, block, block_len, n_unmask);
   return hipGetLastError();
 }

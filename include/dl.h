@@ -280,9 +280,11 @@ dl_status dl_denoise_step(const dl_model *model, dl_state *state, const dl_step_
  * Kernel timing (measurement support, not part of the method).  While a class
  * is enabled with sampling stride n >= 1, about one launch in n of that class
  * (chosen by a fixed hash of the launch's sequence number, so that launches of
- * every shape are sampled) is bracketed by two HIP events recorded on the
- * launch's own stream, and that launch's algorithmic bytes and FLOPs are
- * added up (for a product: weights + input rows + output rows in the storage
+ * every shape are sampled) is timed by two HIP events bound to its kernels'
+ * own dispatch packets on the launch's stream (from the start of its first
+ * kernel to the end of its last, as hipExtLaunchKernel records them, so no
+ * marker packet sits between the kernels), and that launch's algorithmic
+ * bytes and FLOPs are added up (for a product: weights + input rows + output rows in the storage
  * type, 2*M*N*K FLOPs; for attention: Q + K/V rows read + output,
  * 4*rows*keys*d FLOPs).  n = 1 times every launch; n = 0 disables the class.
  * dl_timing_read synchronises on the recorded events and returns the sums
