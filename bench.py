@@ -55,13 +55,17 @@ def variant_schedules(sched):
     """Schedules of the method's variants timed beside the headline step on the
     same model and prompt: a second skip level at layer 8 (keep 50% at layer 4,
     25% at layer 8; ES-dLLM section 2B), DyLLM's response-only steps with a
-    full-context step every 4 steps (section 2B, strategy 3), and eq. I on
-    layer 4's rotated keys instead of its input (ES-dLLM section 2A)."""
+    full-context step every 4 steps (section 2B, strategy 3), eq. I on
+    layer 4's rotated keys instead of its input (ES-dLLM section 2A), and the
+    more frequent full refresh of ES-dLLM* (every 16 or every 8 steps inside a
+    block, besides each block's first step; ES-dLLM section 2B and its results)."""
     import dataclasses
     return {
         "nested_s4_keep0.5_s8_keep0.25": dataclasses.replace(sched, keep=0.5, skip_layer2=8, keep2=0.25),
         "response_only_full_every4": dataclasses.replace(sched, response_interval=4),
         "key_rows_scored": dataclasses.replace(sched, score_tensor="key"),
+        "refresh_every16": dataclasses.replace(sched, refresh_interval=16),
+        "refresh_every8": dataclasses.replace(sched, refresh_interval=8),
     }
 
 
@@ -112,6 +116,7 @@ def time_variant(torch, Decoder, dev_model, prompts, sched, steps: int, warmup: 
            "gen_tokens_per_s": round(steps / (ms / 1e3) * dec.per_step * dec.B, 3), "steps": steps,
            "step_kinds": kinds, "keep": sched.keep, "skip_layer": sched.skip_layer,
            "skip_layer2": sched.skip_layer2, "keep2": sched.keep2, "response_interval": sched.response_interval,
+           "refresh_interval": sched.refresh_interval,
            "score_tensor": sched.score_tensor, "per_layer": sched.per_layer, "keep_layer": sched.keep_layer,
            "rows": dec.S, "batch": dec.B}
     for kc in timed_classes:

@@ -62,10 +62,16 @@ def _compare_step(dec, st, info, wl, sched, tol, t):
     return same
 
 
-def test_tiny_fp32_full_decode_matches_oracle():
-    wl, sched, m_np, dec, st = _setup("f32")
+@pytest.mark.parametrize("refresh_interval", [0, 2])
+def test_tiny_fp32_full_decode_matches_oracle(refresh_interval):
+    """The whole decode; with refresh_interval 2 every other step inside a
+    block is a full refresh as well (ES-dLLM*'s more frequent refresh)."""
+    wl = workloads.workload("tiny")
+    wl, sched, m_np, dec, st = _setup("f32", dataclasses.replace(wl.sched, refresh_interval=refresh_interval))
+    refreshes = 0
     for t in range(sched.steps):
         info = E.denoise_step(m_np, wl.dims, st, t, sched)
+        refreshes += bool(info.refresh)
         dec.step(t)
         torch.cuda.synchronize()
         assert _compare_step(dec, st, info, wl, sched, TOL_F32, t)
@@ -73,6 +79,8 @@ def test_tiny_fp32_full_decode_matches_oracle():
         assert np.array_equal(dec.masked[0].cpu().numpy().astype(bool), st.masked)
         assert np.array_equal(dec.argmax[0].cpu().numpy()[info.selected], st.argmax[info.selected])
     assert not dec.masked.any()
+    n_blocks = -(-sched.gen_len // sched.block_len)
+    assert refreshes > n_blocks if refresh_interval else refreshes == n_blocks
 
 
 def test_tiny_bf16_decode_steps():
