@@ -16,8 +16,10 @@
 //    from HBM straight into a ring of registers kDepth 64-wide K steps ahead
 //    (v_mfma_f32_16x16x32_bf16 B operand layout), while the A rows of each K
 //    step are staged once per workgroup in LDS (double buffer).
-//  * k_gemm_mfma<BN> (bf16): 128 x BN tiles, A and W through LDS; BN = 128
-//    for many rows, BN = 64 for up to 128 rows (twice the column tiles).
+//  * k_gemm_mfma<BN, BM, waves, depth> (bf16): BM x BN tiles, A and W
+//    through LDS; 128 x 128 for many rows, 128 x 64 for up to 128 rows (twice
+//    the column tiles), 256-row tiles with 8 waves for gate|up (192-wide
+//    ragged tiles) and the split-K products on 257..512 rows.
 //  * k_gemm_simt: fp32 FMA fallback (fp32 storage, odd shapes); its results
 //    go through the separate epilogue kernels of k_rows.
 //
@@ -103,10 +105,12 @@ inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 // fused epilogues on a finished tile held in LDS: T[m][c], rows [0, M),
 // tile columns c whose output column is n0 + c in W-map order
 // ---------------------------------------------------------------------------
-template <int BN, int TS, int NT = 256, int MAXM = 128>
+// SWIGLU_ONLY: a tile shape that only gate|up products use (the other
+// branches are left out of its code).
+template <int BN, int TS, int NT = 256, int MAXM = 128, bool SWIGLU_ONLY = false>
 __device__ __forceinline__ void tile_epilogue(const Epilogue& e, float* __restrict__ T, const WMap& w, int n0, int M) {
   const int t = threadIdx.x;
-  if (e.kind == EPI_SWIGLU) {            // modes 1, 3: gate in [0, BN/2), up in [BN/2, BN)
+  if (SWIGLU_ONLY || e.kind == EPI_SWIGLU) {   // modes 1, 3: gate in [0, BN/2), up in [BN/2, BN)
     constexpr int H = BN / 2;
     int a = (n0 / BN) * H, h = H;         // the tile's inner columns [a, a + h)
     if (w.mode == 3) ragged_run(w, n0 / BN, a, h);
@@ -116,7 +120,10 @@ __device__ __forceinline__ void tile_epilogue(const Epilogue& e, float* __restri
       const float gt = T[m * TS + c], up = T[m * TS + H + c];
       out[(size_t)m * e.F + a + c] = from_f32<bf16_t>(gt / (1.f + expf(-gt)) * up).u;
     }
-  } else if (e.kind == EPI_QKV) {
+    return;
+  }
+  if constexpr (SWIGLU_ONLY) return;
+  if (e.kind == EPI_QKV) {
     int sg, r0;
     wrow_index<BN>(w, n0, sg, r0);                  // segment of the tile: 0 q, 1 k, 2 v
     const int hd = e.head_dim, half = hd / 2;
@@ -288,6 +295,13 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #ifndef DTSK_KROT
 #define DTSK_KROT 1
 #endif
+// products on more than 256 rows through 256-row tiles
+#ifndef DTSK_BIG_TILES
+#define DTSK_BIG_TILES 1
+#endif
+#ifndef DTSK_BIG_DEPTH192
+#define DTSK_BIG_DEPTH192 3
+#endif
 
 // K-step order of a tile.  Weight rows are K*2 bytes apart (a power of two in
 // the 8B-class shapes); if every tile walked K from the same start, all of
@@ -303,7 +317,8 @@ __device__ __forceinline__ int k_rotation(int tile, int nk) {
 }
 constexpr int kDepth = DTSK_SKINNY_DEPTH;      // 64-wide K steps fetched ahead (even)
 constexpr int kDepthL = DTSK_LARGE_DEPTH;
-static_assert(kDepth % 2 == 0 && kDepthL % 2 == 0, "the LDS double buffer needs an even pipeline depth");
+constexpr int kBigDepth192 = DTSK_BIG_DEPTH192;   // register ring of the 256 x 192 tile
+static_assert(kDepth % 2 == 0, "the skinny kernel's LDS double buffer needs an even pipeline depth");
 
 // LDS layout of a 64-wide bf16 K step: row r, 16-byte chunk c.  With the XOR
 // swizzle a row is 128 bytes and chunk c lives in slot c ^ ((r >> 1) & 7):
@@ -469,72 +484,84 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
 // in wave order at the end.
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
-// Tiled MFMA GEMM: 128-row x BN-column tiles (BN 128, or 64 when there are
-// few rows and the grid needs more tiles); A and W tiles go through LDS
-// (double buffer), fetched kDepthL - 1 steps ahead into register rings with
-// buffer loads (rows >= M and padding steps read as zeros).  Four waves in a
-// 2 x 2 layout, each a 64 x BN/2 sub-tile.
+// Tiled MFMA GEMM: BM-row x BN-column tiles.  BM = 128 with 4 waves (2 x 2,
+// each 64 x BN/2), or BM = 256 with 8 waves (4 x 2, each 64 x BN/2) for
+// products on more than 256 rows, where the larger tile halves the weight
+// re-reads per output.  A and W tiles go through LDS (double buffer),
+// fetched DEPTH - 1 steps ahead into register rings with buffer loads (rows
+// >= M and padding steps read as zeros).
 // ---------------------------------------------------------------------------
 constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBigBM = 256, kBigWaves = 8;   // the 256-row tile
 constexpr int kRaggedTiles = 256;   // ragged column tiles: one per compute unit
+constexpr int kBigRagged = 128;     // ragged gate|up tiles of the 256-row tile
 constexpr int kLds = kRowElems;
-// dynamic LDS of the tiled kernel: the A/W double buffers, or the finished
-// fp32 tile of the epilogue, whichever is larger
-template <int BN>
+// rows of the finished tile that one epilogue pass stages in LDS
+template <int BM>
+constexpr int epi_rows() { return BM > 128 ? 128 : BM; }
+// dynamic LDS of the tiled kernel: the A/W double buffers, or one epilogue
+// pass of the finished fp32 tile, whichever is larger
+template <int BN, int BM = kBM>
 constexpr int large_lds() {
-  return 2 * (kBM + BN) * kLds * 2 > kBM * (BN + 4) * 4 ? 2 * (kBM + BN) * kLds * 2 : kBM * (BN + 4) * 4;
+  return 2 * (BM + BN) * kLds * 2 > epi_rows<BM>() * (BN + 4) * 4 ? 2 * (BM + BN) * kLds * 2
+                                                                   : epi_rows<BM>() * (BN + 4) * 4;
 }
 
-template <int BN>
-__global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ A, int M_max,
-                                                   const int32_t* __restrict__ n_rows, int m_base, int K, WMap W,
-                                                   int N, int splits, int n_mt, int n_nt, float* __restrict__ P,
-                                                   Epilogue epi) {
-  constexpr int WM = kBM / 2, WN = BN / 2, MI = WM / 16, NI = WN / 16;
-  constexpr int CH = kBM * kBK / 8 / 256;      // 16-byte A items per thread per step (4)
-  constexpr int CW = BN * kBK / 8 / 256;       // 16-byte W items per thread per step
+template <int BN, int BM, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restrict__ A, int M_max,
+                                                       const int32_t* __restrict__ n_rows, int m_base, int K, WMap W,
+                                                       int N, int splits, int n_mt, int n_nt, float* __restrict__ P,
+                                                       Epilogue epi) {
+  constexpr int NT = NW * 64;                  // threads
+  constexpr int WM = BM / (NW / 2), WN = BN / 2, MI = WM / 16, NI = WN / 16;
+  constexpr int IR = NT / 8;                   // tile rows per load item (8 threads per 128-byte row)
+  constexpr int CH = BM / IR;                  // 16-byte A items per thread per step
+  constexpr int CW = BN / IR;                  // 16-byte W items per thread per step
+  static_assert(CW <= CH && BM % IR == 0 && BN % IR == 0 && WM == 64, "tile shape");
   extern __shared__ __align__(16) uint16_t lds[];
-  uint16_t* As = lds;                          // [2][kBM][kLds]
-  uint16_t* Ws = lds + 2 * kBM * kLds;         // [2][BN][kLds]
+  uint16_t* As = lds;                          // [2][BM][kLds]
+  uint16_t* Ws = lds + 2 * BM * kLds;          // [2][BN][kLds]
 
   int mt, nt, split;
   tile_of_block_mn(blockIdx.x, n_mt, splits, mt, nt, split);
   if (nt >= n_nt) return;
   const int M = min(*n_rows - m_base, M_max);
-  const int m0 = mt * kBM;
+  const int m0 = mt * BM;
   if (m0 >= M) return;
   const int n0 = nt * BN;
   const int nk_all = K / kBK;
   const int ks0 = split * nk_all / splits, ks1 = (split + 1) * nk_all / splits;
   const int nk = ks1 - ks0;
-  const int nk_pad = (nk + kDepthL - 1) / kDepthL * kDepthL;
+  const int nk_pad = (nk + DEPTH - 1) / DEPTH * DEPTH;
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
 
-  // item i of thread t covers tile row (t >> 3) + 32 i, columns ((t & 7) * 8, +8).
+  // item i of thread t covers tile row (t >> 3) + IR i, columns ((t & 7) * 8, +8);
+  // the 8 rows a wave loads for one item never straddle a weight segment
+  // (segments and the gate/up halves of a tile start at multiples of 8 rows).
   // The per-lane offsets are fixed; each K step moves the buffer descriptors'
   // base (scalar arithmetic only), and a padding step gets descriptors with no
   // records, so every lane reads zeros through the range check.
   const char* abase = reinterpret_cast<const char*>(A + (size_t)m0 * K);
-  const int arec = min(M - m0, kBM) * K * 2;   // rows >= M are past the records at every step
+  const int arec = min(M - m0, BM) * K * 2;    // rows >= M are past the records at every step
   const char* wbase[CW];
   uint32_t aoff[CH], woff[CW];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int row = (t >> 3) + 32 * i, kc = (t & 7) * 8;
+    const int row = (t >> 3) + IR * i, kc = (t & 7) * 8;
     aoff[i] = (uint32_t)((row * K + ks0 * kBK + kc) * 2);
   }
 #pragma unroll
   for (int i = 0; i < CW; ++i) {
-    const int row = (t >> 3) + 32 * i, kc = (t & 7) * 8;
+    const int row = (t >> 3) + IR * i, kc = (t & 7) * 8;
     int sg, r;
-    wrow_index<BN>(W, n0 + row, sg, r);         // rows 32i..32i+31 share a segment for every mode
+    wrow_index<BN>(W, n0 + row, sg, r);
     sg = __builtin_amdgcn_readfirstlane(sg);
     wbase[i] = static_cast<const char*>(W.p[sg]);
     woff[i] = r < 0 ? kOob : (uint32_t)((r * K + ks0 * kBK + kc) * 2);   // empty columns read zeros
   }
-  uint4 ra[kDepthL][CH], rw[kDepthL][CW];
+  uint4 ra[DEPTH][CH], rw[DEPTH][CW];
   const int rot = k_rotation(nt, nk);   // the row tiles of a column tile walk K together
   auto issue = [&](int step, uint4 (&a)[CH], uint4 (&w)[CW]) {
     const bool in = step < nk;
@@ -555,8 +582,8 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
   auto store = [&](int buf, const uint4 (&a)[CH], const uint4 (&w)[CW]) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int row = (t >> 3) + 32 * i, kc = (t & 7) * 8;
-      *reinterpret_cast<uint4*>(As + buf * kBM * kLds + lds_idx(row, kc >> 3)) = a[i];
+      const int row = (t >> 3) + IR * i, kc = (t & 7) * 8;
+      *reinterpret_cast<uint4*>(As + buf * BM * kLds + lds_idx(row, kc >> 3)) = a[i];
       if (i < CW) *reinterpret_cast<uint4*>(Ws + buf * BN * kLds + lds_idx(row, kc >> 3)) = w[i];
     }
   };
@@ -568,15 +595,16 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
     for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int s = 0; s < kDepthL - 1; ++s) issue(s, ra[s], rw[s]);
+  for (int s = 0; s < DEPTH - 1; ++s) issue(s, ra[s], rw[s]);
   store(0, ra[0], rw[0]);
   lds_barrier();
-  for (int kt = 0; kt < nk_pad; kt += kDepthL) {
+  for (int kt = 0; kt < nk_pad; kt += DEPTH) {
 #pragma unroll
-    for (int u = 0; u < kDepthL; ++u) {
-      issue(kt + u + kDepthL - 1, ra[(u + kDepthL - 1) % kDepthL], rw[(u + kDepthL - 1) % kDepthL]);
-      const uint16_t* a = As + (u & 1) * kBM * kLds;
-      const uint16_t* w = Ws + (u & 1) * BN * kLds;
+    for (int u = 0; u < DEPTH; ++u) {
+      issue(kt + u + DEPTH - 1, ra[(u + DEPTH - 1) % DEPTH], rw[(u + DEPTH - 1) % DEPTH]);
+      const int buf = (DEPTH % 2 == 0) ? (u & 1) : ((kt + u) & 1);   // LDS buffer of step kt + u
+      const uint16_t* a = As + buf * BM * kLds;
+      const uint16_t* w = Ws + buf * BN * kLds;
 #pragma unroll
       for (int ks = 0; ks < kBK / 32; ++ks) {
         const int kch = ks * 4 + (lane >> 4);
@@ -592,7 +620,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
 #pragma unroll
           for (int j = 0; j < NI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
-      store((u + 1) & 1, ra[(u + 1) % kDepthL], rw[(u + 1) % kDepthL]);
+      store(buf ^ 1, ra[(u + 1) % DEPTH], rw[(u + 1) % DEPTH]);
       lds_barrier();
     }
   }
@@ -610,26 +638,34 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t* __restrict__ 
         }
     return;
   }
-  // finished tile to LDS (rows relative to m0), then the epilogue on a view
-  // whose row 0 is packed row m0
-  constexpr int TS = BN + 4;
+  // finished tile to LDS in passes of ER rows (rows relative to the pass),
+  // then the epilogue on a view whose row 0 is the pass's first packed row
+  constexpr int TS = BN + 4, ER = epi_rows<BM>();
   float* T = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int pass = 0; pass < BM / ER; ++pass) {
+    const int r0 = m0 + pass * ER;
+    if (r0 >= M) continue;                     // uniform over the workgroup (and every later pass too)
+    if (pass > 0) lds_barrier();               // the previous pass has read T
+    if (wm0 / ER == pass) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        T[(wm0 + i * 16 + (lane >> 4) * 4 + r) * TS + wn0 + j * 16 + (lane & 15)] = acc[i][j][r];
-  lds_barrier();
-  Epilogue e = epi;
-  const int Mt = min(kBM, M - m0);
-  if (e.kind == EPI_SWIGLU) e.act_out = reinterpret_cast<uint16_t*>(e.act_out) + (size_t)m0 * e.F;
-  if (e.kind == EPI_QKV) e.q_out = reinterpret_cast<uint16_t*>(e.q_out) + (size_t)m0 * e.d;
-  if (e.row_pos) e.row_pos += m0;
-  if (e.row_seq) e.row_seq += m0;
-  if (e.kind == EPI_LM) e.lm_part += (size_t)m0 * e.lm_tiles * 4;
-  tile_epilogue<BN, TS, 256, kBM>(e, T, W, n0, Mt);
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            T[(wm0 - pass * ER + i * 16 + (lane >> 4) * 4 + r) * TS + wn0 + j * 16 + (lane & 15)] = acc[i][j][r];
+    }
+    lds_barrier();
+    Epilogue e = epi;
+    const int Mt = min(ER, M - r0);
+    if (e.kind == EPI_SWIGLU) e.act_out = reinterpret_cast<uint16_t*>(e.act_out) + (size_t)r0 * e.F;
+    if (e.kind == EPI_QKV) e.q_out = reinterpret_cast<uint16_t*>(e.q_out) + (size_t)r0 * e.d;
+    if (e.row_pos) e.row_pos += r0;
+    if (e.row_seq) e.row_seq += r0;
+    if (e.kind == EPI_LM) e.lm_part += (size_t)r0 * e.lm_tiles * 4;
+    tile_epilogue<BN, TS, NT, ER, (BN == 192)>(e, T, W, n0, Mt);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -706,21 +742,21 @@ hipError_t launch_skinny_bn(const GemmPlan& plan, const void* A, int M_max, cons
   }
 }
 
-template <int BN>
+template <int BN, int BM = kBM, int NW = 4, int DEPTH = kDepthL>
 hipError_t launch_tiled(const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows, int m_base, int K,
                         const WMap& w, int N, float* P, const Epilogue& epi, hipStream_t st) {
-  constexpr int lds_bytes = large_lds<BN>();
+  constexpr int lds_bytes = large_lds<BN, BM>();
   static bool attr_set = false;  // the tile may need more than the default 64 KiB of LDS
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma<BN>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       lds_bytes);
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma<BN, BM, NW, DEPTH>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int n_mt = cdiv(M_max, kBM), n_nt = plan.tiles > 0 ? plan.tiles : N / BN;
+  const int n_mt = cdiv(M_max, BM), n_nt = plan.tiles > 0 ? plan.tiles : N / BN;
   const int grid = cdiv(n_nt, 8) * 8 * n_mt * plan.splits;
-  DTSK_LAUNCH((k_gemm_mfma<BN>), dim3(grid), dim3(256), lds_bytes, st, (const uint16_t*)A, M_max, n_rows,
-                     m_base, K, w, N, plan.splits, n_mt, n_nt, P, epi);
+  DTSK_LAUNCH((k_gemm_mfma<BN, BM, NW, DEPTH>), dim3(grid), dim3(NW * 64), lds_bytes, st, (const uint16_t*)A, M_max,
+              n_rows, m_base, K, w, N, plan.splits, n_mt, n_nt, P, epi);
   return hipGetLastError();
 }
 
@@ -814,8 +850,24 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
   p.sep_epi = 0;
   p.bn = kBN;
   p.wmode = epi_kind == EPI_SWIGLU ? 1 : 0;
+  // 257..512 rows, gate|up and the split-K products: two 256-row tiles, which
+  // read every weight tile half as often as four 128-row tiles; gate|up on
+  // kBigRagged ragged 192-wide tiles (up to 96 gate rows and the matching up
+  // rows each), so that the two row tiles fill 256 compute units.  (QKV and
+  // the LM head ran slower on 256-row tiles at 512 rows, and the long-context
+  // shape, 4608 rows, ran slower with them too.)
+  const bool big = DTSK_BIG_TILES && M > kBigBM && M <= 2 * kBigBM &&
+                   (epi_kind == EPI_SWIGLU || epi_kind == EPI_NONE);
+  if (big) {
+    p.bm = kBigBM;
+    if (epi_kind == EPI_SWIGLU && F <= 96 * kBigRagged) {
+      p.bn = 192;
+      p.wmode = 3;
+      p.tiles = kBigRagged;
+    }
+  }
   if (epi_kind == EPI_NONE) {
-    const int tiles = cdiv(M, kBM) * (N / kBN);
+    const int tiles = cdiv(M, big ? kBigBM : kBM) * (N / kBN);
     int s = 1;
     while (tiles * s < 256 && s < 8 && s * 2 <= nk) s *= 2;
     p.splits = s;
@@ -840,6 +892,13 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
     return launch_skinny_bn<128>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
   }
   if (plan.kind == GEMM_LARGE) {
+    if (plan.bm == kBigBM) {
+      if (plan.bn == 192) {   // the 192-wide tile carries only the SwiGLU epilogue
+        if (epi.kind != EPI_SWIGLU) return hipErrorInvalidValue;
+        return launch_tiled<192, kBigBM, kBigWaves, kBigDepth192>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+      }
+      return launch_tiled<kBN, kBigBM, kBigWaves>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+    }
     if (plan.bn == 64) return launch_tiled<64>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
     return launch_tiled<kBN>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
   }

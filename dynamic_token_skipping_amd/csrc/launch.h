@@ -112,6 +112,7 @@ struct GemmPlan {
                // 3 gate|up interleaved over `tiles` ragged column tiles
   int sep_epi; // 1: the product writes fp32 partials and the separate epilogue kernels finish
   int tiles;   // column tiles when they are not N / bn (wmode 3), else 0
+  int bm;      // GEMM_LARGE row tile: 256 (8 waves) or 0 for 128
 };
 // The epilogue kind decides the tile the fused epilogue needs; a GEMM_SIMT
 // plan leaves the epilogue to the separate kernels below.
