@@ -312,6 +312,7 @@ dl_status product(const Ctx& c, dl_kernel_class kc, const void* A, const RowMap&
   if (kc == DL_KC_GEMM && rows > 128) kc = DL_KC_GEMM_TILED;
   Epilogue ge = e;
   if (p.sep_epi && e.kind != EPI_NONE) ge.kind = EPI_NONE;   // partials; the epilogue kernel finishes
+  if (e.kind == EPI_LM) ge.lm_tiles = cdiv(N, p.bn);          // statistics per column tile of the plan
   // the timed region holds the product and, when it has one, its separate
   // epilogue kernel (rows addressed through the full row map)
   DL_CHECK_HIP(timed(kc, c.st, gemm_bytes(d, rows, N, K), 2.0 * rows * N * K, [&] {
@@ -327,7 +328,7 @@ dl_status product(const Ctx& c, dl_kernel_class kc, const void* A, const RowMap&
     }
   }));
   if (!p.sep_epi && e.kind == EPI_LM) {
-    DL_CHECK_HIP(launch_lm_merge(e.lm_part, e.lm_tiles, rm, m_base, rows, conf, argmax, c.st));
+    DL_CHECK_HIP(launch_lm_merge(e.lm_part, ge.lm_tiles, rm, m_base, rows, conf, argmax, c.st));
   }
   return DL_OK;
 }

@@ -19,7 +19,8 @@
 //  * k_gemm_mfma<BN, BM, waves, depth> (bf16): BM x BN tiles, A and W
 //    through LDS; 128 x 128 for many rows, 128 x 64 for up to 128 rows (twice
 //    the column tiles), 256-row tiles with 8 waves for gate|up (192-wide
-//    ragged tiles) and the split-K products on 257..512 rows.
+//    ragged tiles) and the split-K products on 257..512 rows, 128 x 256
+//    tiles with 8 waves for the LM head.
 //  * k_gemm_simt: fp32 FMA fallback (fp32 storage, odd shapes); its results
 //    go through the separate epilogue kernels of k_rows.
 //
@@ -299,6 +300,9 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #ifndef DTSK_BIG_TILES
 #define DTSK_BIG_TILES 1
 #endif
+#ifndef DTSK_LM256
+#define DTSK_LM256 1
+#endif
 #ifndef DTSK_BIG_DEPTH192
 #define DTSK_BIG_DEPTH192 3
 #endif
@@ -517,7 +521,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
   constexpr int IR = NT / 8;                   // tile rows per load item (8 threads per 128-byte row)
   constexpr int CH = BM / IR;                  // 16-byte A items per thread per step
   constexpr int CW = BN / IR;                  // 16-byte W items per thread per step
-  static_assert(CW <= CH && BM % IR == 0 && BN % IR == 0 && WM == 64, "tile shape");
+  constexpr int CM = CH > CW ? CH : CW;
+  static_assert(BM % IR == 0 && BN % IR == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
   extern __shared__ __align__(16) uint16_t lds[];
   uint16_t* As = lds;                          // [2][BM][kLds]
   uint16_t* Ws = lds + 2 * BM * kLds;          // [2][BN][kLds]
@@ -570,8 +575,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
     const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase) + ks, (short)0,
                                                                          in ? arec - ks : 0, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      a[i] = buf_load16(ar, aoff[i]);
+    for (int i = 0; i < CM; ++i) {
+      if (i < CH) a[i] = buf_load16(ar, aoff[i]);
       if (i < CW) {
         const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<char*>(wbase[i]) + ks, (short)0, in ? (int)W.seg_bytes - ks : 0, 0x00020000);
@@ -581,9 +586,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
   };
   auto store = [&](int buf, const uint4 (&a)[CH], const uint4 (&w)[CW]) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
+    for (int i = 0; i < CM; ++i) {
       const int row = (t >> 3) + IR * i, kc = (t & 7) * 8;
-      *reinterpret_cast<uint4*>(As + buf * BM * kLds + lds_idx(row, kc >> 3)) = a[i];
+      if (i < CH) *reinterpret_cast<uint4*>(As + buf * BM * kLds + lds_idx(row, kc >> 3)) = a[i];
       if (i < CW) *reinterpret_cast<uint4*>(Ws + buf * BN * kLds + lds_idx(row, kc >> 3)) = w[i];
     }
   };
@@ -783,6 +788,9 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
     const bool wide = epi_kind == EPI_LM || (N % 128 == 0 && N / 128 >= DTSK_T128_MIN_TILES && epi_kind != EPI_QKV &&
                                              (epi_kind != EPI_SWIGLU || F % 64 == 0));
     p.bn = wide ? 128 : 64;
+    // the LM head: 256-wide tiles (8 waves of 32 x 128), which read the rows
+    // of A half as often as 128-wide ones
+    if (DTSK_LM256 && epi_kind == EPI_LM && N % 256 == 0) p.bn = 256;
     p.wmode = epi_kind == EPI_SWIGLU ? 1 : epi_kind == EPI_QKV ? 2 : 0;
     // Wq|Wk|Wv: 128-wide tiles of natural column order and a K split in two
     // (192 workgroups, half the A rows each); k_epi_qkv_heads sums the two
@@ -850,6 +858,7 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
   p.sep_epi = 0;
   p.bn = kBN;
   p.wmode = epi_kind == EPI_SWIGLU ? 1 : 0;
+  if (DTSK_LM256 && epi_kind == EPI_LM && N % 256 == 0) p.bn = 256;   // as on fewer rows
   // 257..512 rows, gate|up and the split-K products: two 256-row tiles, which
   // read every weight tile half as often as four 128-row tiles; gate|up on
   // kBigRagged ragged 192-wide tiles (up to 96 gate rows and the matching up
@@ -900,6 +909,7 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
       return launch_tiled<kBN, kBigBM, kBigWaves>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
     }
     if (plan.bn == 64) return launch_tiled<64>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+    if (plan.bn == 256) return launch_tiled<256, kBM, 8>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
     return launch_tiled<kBN>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
   }
   dim3 grid(cdiv(N, 64), cdiv(M_max, 64));
