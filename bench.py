@@ -372,7 +372,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": recorded_traffic(),
                 "kernel": ("layer products on the 128 kept rows (128-row tiles): k_gemm_mfma BN 64 with 4 K "
-                           "splits (O, down), BN 128 with 2 K splits + k_epi_qkv_heads (QKV), BN 128 on 256 "
+                           "splits (O, down), BN 128 with 2 K splits + k_epi_qkv_rows4 (QKV), BN 128 on 256 "
                            "ragged tiles (gate|up)"),
                 "launches_timed": g["launches"], "launches_total": g["launches"] + g["dropped"],
                 "avg_launch_us": round(g["ms"] * 1e3 / max(g["launches"], 1), 2),

@@ -793,7 +793,7 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
     if (DTSK_LM256 && epi_kind == EPI_LM && N % 256 == 0) p.bn = 256;
     p.wmode = epi_kind == EPI_SWIGLU ? 1 : epi_kind == EPI_QKV ? 2 : 0;
     // Wq|Wk|Wv: 128-wide tiles of natural column order and a K split in two
-    // (192 workgroups, half the A rows each); k_epi_qkv_heads sums the two
+    // (192 workgroups, half the A rows each); k_epi_qkv_rows4 sums the two
     // partials and applies RoPE and the cache writes
     if (DTSK_QKV_SPLIT && epi_kind == EPI_QKV && head_dim <= 128 && n_seg % 128 == 0 && (N / 128) * 2 <= 256 &&
         nk >= 2) {

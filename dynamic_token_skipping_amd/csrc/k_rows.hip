@@ -732,6 +732,59 @@ __global__ __launch_bounds__(64) void k_epi_qkv_heads(const float* __restrict__ 
   dst[col + half] = from_f32<T>(o2);
 }
 
+// The same epilogue with four RoPE pairs per thread (16-byte partial loads):
+// one workgroup per (packed row, q|k|v segment); thread t owns dims
+// [c, c + 4) and [half + c, half + c + 4) of head t / (half / 4), with
+// c = 4 (t % (half / 4)).  Same sums in the same order as k_epi_qkv_heads.
+template <typename T>
+__global__ __launch_bounds__(1024) void k_epi_qkv_rows4(const float* __restrict__ P, int splits, int M_max,
+                                                        const int32_t* __restrict__ n_rows,
+                                                        const int32_t* __restrict__ row_pos,
+                                                        const int32_t* __restrict__ row_seq, int S, int d,
+                                                        int head_dim, const float2* __restrict__ rope,
+                                                        T* __restrict__ q_out, T* __restrict__ k_cache,
+                                                        T* __restrict__ v_cache) {
+  const int r = blockIdx.x;
+  if (r >= *n_rows) return;
+  const int seg = blockIdx.y, t = threadIdx.x;
+  const int half = head_dim >> 1, tph = half >> 2;   // threads per head
+  if (t >= d >> 3) return;                           // d / 8 = heads x threads per head
+  const int h = t / tph, c = (t - h * tph) * 4;
+  const size_t stride = (size_t)M_max * 3 * d;
+  const float* base = P + (size_t)r * 3 * d + (size_t)seg * d + (size_t)h * head_dim + c;
+  float4 v1[kEpiMaxSplits], v2[kEpiMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kEpiMaxSplits; ++s)
+    if (s < splits) {
+      v1[s] = *reinterpret_cast<const float4*>(base + s * stride);
+      v2[s] = *reinterpret_cast<const float4*>(base + s * stride + half);
+    }
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+#pragma unroll
+  for (int s = 0; s < kEpiMaxSplits; ++s)
+    if (s < splits) {
+      a.x += v1[s].x; a.y += v1[s].y; a.z += v1[s].z; a.w += v1[s].w;
+      b.x += v2[s].x; b.y += v2[s].y; b.z += v2[s].z; b.w += v2[s].w;
+    }
+  const int p = row_pos[r];
+  const size_t col = (size_t)h * head_dim + c;
+  if (seg == 2) {
+    store4(v_cache + (size_t)p * d + col, a);
+    store4(v_cache + (size_t)p * d + col + half, b);
+    return;
+  }
+  const int pos = p - row_seq[r] * S;
+  const float4 c01 = *reinterpret_cast<const float4*>(rope + (size_t)pos * half + c);       // (cos, sin) of c, c + 1
+  const float4 c23 = *reinterpret_cast<const float4*>(rope + (size_t)pos * half + c + 2);   // of c + 2, c + 3
+  const float4 o1 = make_float4(a.x * c01.x - b.x * c01.y, a.y * c01.z - b.y * c01.w, a.z * c23.x - b.z * c23.y,
+                                a.w * c23.z - b.w * c23.w);
+  const float4 o2 = make_float4(b.x * c01.x + a.x * c01.y, b.y * c01.z + a.y * c01.w, b.z * c23.x + a.z * c23.y,
+                                b.w * c23.z + a.w * c23.w);
+  T* dst = seg == 0 ? q_out + (size_t)r * d : k_cache + (size_t)p * d;
+  store4(dst + col, o1);
+  store4(dst + col + half, o2);
+}
+
 __global__ __launch_bounds__(kRowThreads) void k_epi_residual(const float* __restrict__ P, int splits, int M_max,
                                                               const int32_t* __restrict__ n_rows, int N,
                                                               float* __restrict__ x) {
@@ -1176,6 +1229,16 @@ hipError_t launch_rope_table(int S, int head_dim, float base, float2* table, hip
 hipError_t launch_epi_qkv(dl_dtype dt, const float* P, int splits, const RowMap& rm, int S, int d, int head_dim,
                           const float2* rope, void* q_out, void* k_cache, void* v_cache, hipStream_t st) {
   if (rm.R_max <= 0) return hipSuccess;
+  if (head_dim % 8 == 0 && d % head_dim == 0 && d / 8 <= 1024 && splits >= 1 && splits <= kEpiMaxSplits) {
+    const dim3 grid(rm.R_max, 3), block((d / 8 + 63) / 64 * 64);
+    if (dt == DL_F32)
+      DTSK_LAUNCH(k_epi_qkv_rows4<float>, grid, block, 0, st, P, splits, rm.R_max, rm.n_rows, rm.row_pos,
+                  rm.row_seq, S, d, head_dim, rope, (float*)q_out, (float*)k_cache, (float*)v_cache);
+    else
+      DTSK_LAUNCH(k_epi_qkv_rows4<bf16_t>, grid, block, 0, st, P, splits, rm.R_max, rm.n_rows, rm.row_pos,
+                  rm.row_seq, S, d, head_dim, rope, (bf16_t*)q_out, (bf16_t*)k_cache, (bf16_t*)v_cache);
+    return hipGetLastError();
+  }
   if (head_dim <= 128 && d % head_dim == 0 && splits >= 1 && splits <= kEpiMaxSplits) {
     const dim3 grid(rm.R_max, 3 * (d / head_dim));
     if (dt == DL_F32)
