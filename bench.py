@@ -371,7 +371,7 @@ def main():
     gemm_gbs = g["bytes"] / (g["ms"] / 1e3) / 1e9 if g["ms"] > 0 else 0.0
     roofline = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": recorded_traffic(),
-                "kernel": ("layer products on the 128 kept rows (128-row tiles): k_gemm_mfma BN 64 with 4 K "
+                "kernel": ("layer products on the 128 kept rows (128-row tiles, 8 waves): k_gemm_mfma BN 64 with 4 K "
                            "splits (O, down), BN 128 with 2 K splits + k_epi_qkv_rows4 (QKV), BN 128 on 256 "
                            "ragged tiles (gate|up)"),
                 "launches_timed": g["launches"], "launches_total": g["launches"] + g["dropped"],

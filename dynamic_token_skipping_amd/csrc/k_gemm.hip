@@ -303,6 +303,20 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #ifndef DTSK_LM256
 #define DTSK_LM256 1
 #endif
+// waves and register-ring depth of the 128-row tiles on up to 128 rows
+#ifndef DTSK_SMALL_NW
+#define DTSK_SMALL_NW 8
+#endif
+#ifndef DTSK_SMALL_NW128
+#define DTSK_SMALL_NW128 DTSK_SMALL_NW
+#endif
+#ifndef DTSK_SMALL_DEPTH
+#define DTSK_SMALL_DEPTH 4
+#endif
+// waves of the 128 x 128 tiles on more than 128 rows
+#ifndef DTSK_MID_NW
+#define DTSK_MID_NW 8
+#endif
 #ifndef DTSK_BIG_DEPTH192
 #define DTSK_BIG_DEPTH192 3
 #endif
@@ -791,6 +805,7 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
     // the LM head: 256-wide tiles (8 waves of 32 x 128), which read the rows
     // of A half as often as 128-wide ones
     if (DTSK_LM256 && epi_kind == EPI_LM && N % 256 == 0) p.bn = 256;
+    if (p.bn != 256) p.nw = p.bn == 128 ? DTSK_SMALL_NW128 : DTSK_SMALL_NW;
     p.wmode = epi_kind == EPI_SWIGLU ? 1 : epi_kind == EPI_QKV ? 2 : 0;
     // Wq|Wk|Wv: 128-wide tiles of natural column order and a K split in two
     // (192 workgroups, half the A rows each); k_epi_qkv_rows4 sums the two
@@ -859,6 +874,7 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
   p.bn = kBN;
   p.wmode = epi_kind == EPI_SWIGLU ? 1 : 0;
   if (DTSK_LM256 && epi_kind == EPI_LM && N % 256 == 0) p.bn = 256;   // as on fewer rows
+  if (p.bn == kBN) p.nw = DTSK_MID_NW;
   // 257..512 rows, gate|up and the split-K products: two 256-row tiles, which
   // read every weight tile half as often as four 128-row tiles; gate|up on
   // kBigRagged ragged 192-wide tiles (up to 96 gate rows and the matching up
@@ -908,8 +924,17 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
       }
       return launch_tiled<kBN, kBigBM, kBigWaves>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
     }
-    if (plan.bn == 64) return launch_tiled<64>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
     if (plan.bn == 256) return launch_tiled<256, kBM, 8>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+#if DTSK_SMALL_NW128 == 16
+    if (plan.nw == 16 && plan.bn == kBN)
+      return launch_tiled<kBN, kBM, 16, DTSK_SMALL_DEPTH>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+#endif
+    if (plan.nw == 8) {
+      if (plan.bn == 64)
+        return launch_tiled<64, kBM, 8, DTSK_SMALL_DEPTH>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+      return launch_tiled<kBN, kBM, 8, DTSK_SMALL_DEPTH>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+    }
+    if (plan.bn == 64) return launch_tiled<64>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
     return launch_tiled<kBN>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
   }
   dim3 grid(cdiv(N, 64), cdiv(M_max, 64));

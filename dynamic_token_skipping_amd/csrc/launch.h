@@ -113,6 +113,7 @@ struct GemmPlan {
   int sep_epi; // 1: the product writes fp32 partials and the separate epilogue kernels finish
   int tiles;   // column tiles when they are not N / bn (wmode 3), else 0
   int bm;      // GEMM_LARGE row tile: 256 (8 waves) or 0 for 128
+  int nw;      // GEMM_LARGE 128-row tiles: 8 waves, or 0 for the default
 };
 // The epilogue kind decides the tile the fused epilogue needs; a GEMM_SIMT
 // plan leaves the epilogue to the separate kernels below.
