@@ -317,6 +317,9 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #ifndef DTSK_MID_NW
 #define DTSK_MID_NW 8
 #endif
+#ifndef DTSK_BIG_NW128
+#define DTSK_BIG_NW128 8
+#endif
 #ifndef DTSK_BIG_DEPTH192
 #define DTSK_BIG_DEPTH192 3
 #endif
@@ -922,7 +925,7 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
         if (epi.kind != EPI_SWIGLU) return hipErrorInvalidValue;
         return launch_tiled<192, kBigBM, kBigWaves, kBigDepth192>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
       }
-      return launch_tiled<kBN, kBigBM, kBigWaves>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+      return launch_tiled<kBN, kBigBM, DTSK_BIG_NW128>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
     }
     if (plan.bn == 256) return launch_tiled<256, kBM, 8>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
 #if DTSK_SMALL_NW128 == 16
