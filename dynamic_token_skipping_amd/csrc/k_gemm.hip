@@ -280,6 +280,10 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #ifndef DTSK_TILED_SMALL
 #define DTSK_TILED_SMALL 1
 #endif
+// the tiled kernel from this many rows up (fewer go to the skinny kernel)
+#ifndef DTSK_TILED_MIN_ROWS
+#define DTSK_TILED_MIN_ROWS 32
+#endif
 #ifndef DTSK_T128_MIN_TILES
 #define DTSK_T128_MIN_TILES 160
 #endif
@@ -790,9 +794,11 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
   if (dt != DL_BF16 || K % 64 != 0 || M <= 0) return p;
   const int nk = K / 64;
   const int n_seg = epi_kind == EPI_QKV ? N / 3 : epi_kind == EPI_SWIGLU ? N / 2 : N;
-  // up to 128 rows: one 128 x 64 tile row of the tiled kernel when the shape
-  // allows it (more column tiles than 128-wide ones); else the skinny kernel
-  const bool tiled_small = DTSK_TILED_SMALL && M > 64 && M <= 128 && (DTSK_TILED_LM || epi_kind != EPI_LM) &&
+  // 33..128 rows: one row of 128-row tiles of the tiled kernel when the shape
+  // allows it (at 64 rows it beat the skinny kernel by 7% per layer); fewer
+  // rows go to the skinny kernel
+  const bool tiled_small = DTSK_TILED_SMALL && M > DTSK_TILED_MIN_ROWS && M <= 128 &&
+                           (DTSK_TILED_LM || epi_kind != EPI_LM) &&
                            N % 64 == 0 && (epi_kind != EPI_LM || N % 128 == 0) &&
                            (epi_kind != EPI_QKV || (head_dim == 128 && n_seg % 128 == 0)) &&
                            (epi_kind != EPI_SWIGLU || F % 32 == 0);
