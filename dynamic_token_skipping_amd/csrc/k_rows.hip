@@ -535,14 +535,18 @@ __device__ __forceinline__ void store4(T* p, float4 v) {
   }
 }
 
+// threads of the row reduction at d = 4096 (512: two float4 per thread; 256
+// and 1024 measured 0.4% slower per decode step)
+#ifndef DTSK_RED_THREADS
+#define DTSK_RED_THREADS 512
+#endif
 constexpr int kRedSplits = 8;   // partials loaded together (more are added in a second loop)
 
-template <typename T, int kChunks>
-__global__ __launch_bounds__(kRowThreads) void k_reduce_rows(const float* __restrict__ P, int splits, int M_max,
-                                                             const int32_t* __restrict__ n_rows, int d,
-                                                             float* __restrict__ x, const T* __restrict__ g, float eps,
-                                                             T* __restrict__ out) {
-  // d == kChunks * 4 * kRowThreads: every thread owns kChunks float4 of the
+template <typename T, int kChunks, int NT = kRowThreads>
+__global__ __launch_bounds__(NT) void k_reduce_rows(const float* __restrict__ P, int splits, int M_max,
+                                                    const int32_t* __restrict__ n_rows, int d, float* __restrict__ x,
+                                                    const T* __restrict__ g, float eps, T* __restrict__ out) {
+  // d == kChunks * 4 * NT: every thread owns kChunks float4 of the
   // row; its row, partial and gain loads are all issued before the first is
   // used, and the partials are added in split order
   __shared__ float red[16];
@@ -553,15 +557,15 @@ __global__ __launch_bounds__(kRowThreads) void k_reduce_rows(const float* __rest
   const float4* pr = reinterpret_cast<const float4*>(P + (size_t)r * d);
   float4 v[kChunks], ps[kRedSplits][kChunks], gv[kChunks];
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) v[c] = xr[threadIdx.x + c * kRowThreads];
+  for (int c = 0; c < kChunks; ++c) v[c] = xr[threadIdx.x + c * NT];
 #pragma unroll
   for (int s = 0; s < kRedSplits; ++s)
     if (s < splits)
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) ps[s][c] = pr[s * (sstride / 4) + threadIdx.x + c * kRowThreads];
+      for (int c = 0; c < kChunks; ++c) ps[s][c] = pr[s * (sstride / 4) + threadIdx.x + c * NT];
   if (g)
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) gv[c] = load4(g + (threadIdx.x + c * kRowThreads) * 4);
+    for (int c = 0; c < kChunks; ++c) gv[c] = load4(g + (threadIdx.x + c * NT) * 4);
   auto add = [&](float4& a, const float4& b) {
     a.x += b.x;
     a.y += b.y;
@@ -575,11 +579,11 @@ __global__ __launch_bounds__(kRowThreads) void k_reduce_rows(const float* __rest
       for (int c = 0; c < kChunks; ++c) add(v[c], ps[s][c]);
   for (int s = kRedSplits; s < splits; ++s)
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) add(v[c], pr[s * (sstride / 4) + threadIdx.x + c * kRowThreads]);
+    for (int c = 0; c < kChunks; ++c) add(v[c], pr[s * (sstride / 4) + threadIdx.x + c * NT]);
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    if (splits > 0) xr[threadIdx.x + c * kRowThreads] = v[c];
+    if (splits > 0) xr[threadIdx.x + c * NT] = v[c];
     ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
   }
   if (!g) return;
@@ -588,7 +592,7 @@ __global__ __launch_bounds__(kRowThreads) void k_reduce_rows(const float* __rest
   T* o = out + (size_t)r * d;
 #pragma unroll
   for (int c = 0; c < kChunks; ++c)
-    store4(o + (threadIdx.x + c * kRowThreads) * 4,
+    store4(o + (threadIdx.x + c * NT) * 4,
            make_float4(v[c].x * inv * gv[c].x, v[c].y * inv * gv[c].y, v[c].z * inv * gv[c].z,
                        v[c].w * inv * gv[c].w));
 }
@@ -1292,8 +1296,8 @@ static hipError_t reduce_rows_t(const float* P, int splits, const RowMap& rm, in
   const T* gg = (const T*)g;
   T* oo = (T*)out;
   if (d == 4096)
-    DTSK_LAUNCH((k_reduce_rows<T, 4>), dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
-                       rm.n_rows, d, x, gg, eps, oo);
+    DTSK_LAUNCH((k_reduce_rows<T, 4096 / 4 / DTSK_RED_THREADS, DTSK_RED_THREADS>), dim3(rm.R_max),
+                dim3(DTSK_RED_THREADS), 0, st, P, splits, rm.R_max, rm.n_rows, d, x, gg, eps, oo);
   else if (d == 2048)
     DTSK_LAUNCH((k_reduce_rows<T, 2>), dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
                        rm.n_rows, d, x, gg, eps, oo);
