@@ -177,3 +177,44 @@ def test_unmask_matches_oracle(lay):
         got = np.nonzero(masked.astype(bool) & ~msk[0].cpu().numpy().astype(bool))[0]
         assert got.tolist() == want.tolist()
         assert (tok[0].cpu().numpy()[want] == want).all()
+
+
+def test_timing_counts_products_and_keeps_results(lay):
+    """Sampled kernel timing (events bound to the products' dispatch packets):
+    with stride 1 the four products of a kept-row layer are each timed once,
+    their algorithmic bytes add up to the closed form, and the layer's output
+    is bit-identical to an untimed run."""
+    D = lay["D"]
+    S, d, F = lay["S"], lay["wl"].dims.d, lay["wl"].dims.d_ffn
+    k = 128
+    rows = np.arange(0, S, S // k)[:k]
+    sel = D.SelectionTensors(1, S)
+    sel.sel_idx[0, :k] = torch.as_tensor(rows, dtype=torch.int32)
+    sel.sel_count[0] = k
+    sel.row_off[1] = k
+    lw = lay["m"]["layers"][0]
+    x0 = lay["st"]["h_cur"][0:S].float()[torch.as_tensor(rows, device="cuda")].contiguous()
+
+    def run(timed):
+        x = x0.clone()
+        kc = lay["st"]["k"].clone().reshape(1, S, d)
+        vc = lay["st"]["v"].clone().reshape(1, S, d)
+        D.dl_timing_reset()
+        D.dl_timing_enable(D.DL_KC_GEMM, 1 if timed else 0)
+        D.dl_partial_attn(lay["dims"], lw, x, sel, lay["seq_len"], k, kc, vc, lay["ws"])
+        D.dl_ffn_rows(lay["dims"], lw, x, sel, k, lay["ws"])
+        torch.cuda.synchronize()
+        t = D.dl_timing_read(D.DL_KC_GEMM)
+        D.dl_timing_enable(D.DL_KC_GEMM, 0)
+        return x, t
+
+    x_plain, t_plain = run(False)
+    x_timed, t = run(True)
+    assert t_plain["launches"] == 0
+    assert torch.equal(x_plain, x_timed)
+    assert t["launches"] == 4 and t["dropped"] == 0
+    assert 0 < t["ms"] < 10.0
+    gemm = lambda M, N, K: 2.0 * (N * K + M * K + M * N)        # bf16 weights + rows in + rows out
+    want = gemm(k, 3 * d, d) + gemm(k, d, d) + gemm(k, 2 * F, d) + gemm(k, d, F)
+    assert t["bytes"] == pytest.approx(want, rel=1e-12)
+    assert t["flops"] == pytest.approx(2.0 * k * d * (3 * d + d + 2 * F) + 2.0 * k * F * d, rel=1e-12)
