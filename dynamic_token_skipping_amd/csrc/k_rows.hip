@@ -535,6 +535,35 @@ __device__ __forceinline__ void store4(T* p, float4 v) {
   }
 }
 
+// Row copies four columns at a time (widths a multiple of 4, so every row
+// start is 8-byte aligned in bf16 and 16-byte aligned in fp32): the embedding
+// lookup and the fp32 -> storage-type row store.  Same conversions as the
+// element-wise kernels.
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_embed4(const int32_t* __restrict__ tokens,
+                                                        const int32_t* __restrict__ row_pos,
+                                                        const T* __restrict__ E, int d, float* __restrict__ x) {
+  const int r = blockIdx.x;
+  const int p = row_pos[r];
+  if (p < 0) return;
+  const T* e = E + (size_t)tokens[p] * d;
+  float* xr = x + (size_t)r * d;
+#pragma unroll 4
+  for (int c = threadIdx.x * 4; c < d; c += kRowThreads * 4) *reinterpret_cast<float4*>(xr + c) = load4(e + c);
+}
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_store_rows4(const float* __restrict__ x, int w,
+                                                             const int32_t* __restrict__ row_pos,
+                                                             T* __restrict__ dst) {
+  const int r = blockIdx.x;
+  const int p = row_pos[r];
+  if (p < 0) return;
+  const float* s = x + (size_t)r * w;
+  T* o = dst + (size_t)p * w;
+#pragma unroll 4
+  for (int c = threadIdx.x * 4; c < w; c += kRowThreads * 4) store4(o + c, *reinterpret_cast<const float4*>(s + c));
+}
+
 // threads of the row reduction at d = 4096 (512: two float4 per thread; 256
 // and 1024 measured 0.4% slower per decode step)
 #ifndef DTSK_RED_THREADS
@@ -1130,6 +1159,15 @@ hipError_t launch_select(const float* scores, const int32_t* seq_len, int B, int
 
 hipError_t launch_embed(dl_dtype dt, const int32_t* tokens, const RowMap& rm, const void* E, int d, float* x,
                         hipStream_t st) {
+  if (d % 4 == 0) {
+    if (dt == DL_F32)
+      DTSK_LAUNCH(k_embed4<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, tokens, rm.row_pos, (const float*)E, d,
+                  x);
+    else
+      DTSK_LAUNCH(k_embed4<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, tokens, rm.row_pos, (const bf16_t*)E,
+                  d, x);
+    return hipGetLastError();
+  }
   if (dt == DL_F32)
     DTSK_LAUNCH(k_embed<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, tokens, rm.row_pos,
                        (const float*)E, d, x);
@@ -1208,6 +1246,13 @@ hipError_t launch_scatter(size_t elem_bytes, const void* rows, int w, const RowM
 }
 
 hipError_t launch_store_rows(dl_dtype dt, const float* x, int w, const RowMap& rm, void* dst, hipStream_t st) {
+  if (w % 4 == 0) {
+    if (dt == DL_F32)
+      DTSK_LAUNCH(k_store_rows4<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, w, rm.row_pos, (float*)dst);
+    else
+      DTSK_LAUNCH(k_store_rows4<bf16_t>, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, w, rm.row_pos, (bf16_t*)dst);
+    return hipGetLastError();
+  }
   if (dt == DL_F32)
     DTSK_LAUNCH(k_store_rows<float>, dim3(rm.R_max), dim3(kRowThreads), 0, st, x, w, rm.row_pos, (float*)dst);
   else
