@@ -526,9 +526,8 @@ dl_status per_layer_layers(const Ctx& c, const dl_model* model, const dl_state* 
                        at<int32_t>(c.ws, L.lsel_off[tsel])};
       DL_CHECK_HIP(launch_select(lscores, s->seq_len, d.B, d.S, p->mode_l, p->keep_ratio_l, p->threshold_l, sel_R.idx,
                                  sel_R.cnt, c.st));
-      DL_CHECK_HIP(launch_row_off(sel_R.cnt, sel_R.off, d.B, c.st));
       rm_R = rowmap_at(c.ws, L.map_l[tsel], (int)R_l, std::min(L.T, cdiv(R_l, kTileRows) + d.B));
-      DL_CHECK_HIP(launch_rowmap(sel_R.idx, sel_R.cnt, sel_R.off, d.B, d.S, rm_R, c.st));
+      DL_CHECK_HIP(launch_row_off_map(sel_R.idx, sel_R.cnt, sel_R.off, d.B, d.S, rm_R, c.st));
       // inputs of the salient rows: X_s at layer s, the cached output of the layer below above it
       x_R = xbuf[tsel];
       if (l == sl)
@@ -925,8 +924,7 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
 
   // the step's candidate rows: every valid row, or the response rows
   DL_CHECK_HIP(launch_identity_sel(s->seq_len, d.B, d.S, all_idx, all_cnt, st, resp ? s->prompt_len : nullptr));
-  DL_CHECK_HIP(launch_row_off(all_cnt, all_off, d.B, st));
-  DL_CHECK_HIP(launch_rowmap(all_idx, all_cnt, all_off, d.B, d.S, rm_all, st));
+  DL_CHECK_HIP(launch_row_off_map(all_idx, all_cnt, all_off, d.B, d.S, rm_all, st));
   DL_CHECK_HIP(launch_rope_table(d.S, d.head_dim, d.rope_base, at<float2>(ws, L.rope), st));
   DL_CHECK_HIP(launch_embed(d.dtype, s->tokens, rm_all, model->embed, d.d, x_all, st));
 
@@ -995,9 +993,8 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
       DL_CHECK_HIP(launch_select(scores, s->seq_len, d.B, d.S, p->mode, p->keep_ratio, p->threshold, s->sel.sel_idx,
                                  s->sel.sel_count, st, all_idx, all_cnt, all_cnt));
     }
-    DL_CHECK_HIP(launch_row_off(s->sel.sel_count, s->sel.row_off, d.B, st));
     const RowMap rm_sel = rowmap_at(ws, L.map_sel, (int)R_sel, tiles(R_sel));
-    DL_CHECK_HIP(launch_rowmap(s->sel.sel_idx, s->sel.sel_count, s->sel.row_off, d.B, d.S, rm_sel, st));
+    DL_CHECK_HIP(launch_row_off_map(s->sel.sel_idx, s->sel.sel_count, s->sel.row_off, d.B, d.S, rm_sel, st));
     float* x_sel = at<float>(ws, L.x_sel);
     if (!resp) {
       DL_CHECK_HIP(launch_gather(sizeof(float), x_all, all_off, d.S, d.d, rm_sel, x_sel, st));
@@ -1032,9 +1029,9 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
                                 p->score, p->alpha, scores2, st, &rm_sel));
       DL_CHECK_HIP(launch_select(scores2, s->seq_len, d.B, d.S, p->mode2, p->keep_ratio2, p->threshold2,
                                  s->sel2.sel_idx, s->sel2.sel_count, st, s->sel.sel_idx, s->sel.sel_count, all_cnt));
-      DL_CHECK_HIP(launch_row_off(s->sel2.sel_count, s->sel2.row_off, d.B, st));
       const RowMap rm_sel2 = rowmap_at(ws, L.map_sel2, (int)R_sel2, tiles(R_sel2));
-      DL_CHECK_HIP(launch_rowmap(s->sel2.sel_idx, s->sel2.sel_count, s->sel2.row_off, d.B, d.S, rm_sel2, st));
+      DL_CHECK_HIP(launch_row_off_map(s->sel2.sel_idx, s->sel2.sel_count, s->sel2.row_off, d.B, d.S, rm_sel2,
+                                      st));
       float* x_sel2 = at<float>(ws, L.x_sel2);
       DL_CHECK_HIP(launch_inv_rows(rm_sel, d.B * d.S, inv, st));
       DL_CHECK_HIP(launch_gather(sizeof(float), x_sel, nullptr, d.S, d.d, rm_sel2, x_sel2, st, inv));

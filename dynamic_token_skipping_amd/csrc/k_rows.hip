@@ -41,6 +41,8 @@ __global__ void k_row_off(const int32_t* __restrict__ sel_count, int32_t* __rest
   }
 }
 
+constexpr int kMaxMapSeqs = 1024;   // sequences the one-launch row map holds in LDS
+
 // One block: the row count and the attention query tiles (tq rows each,
 // never crossing a sequence), from an existing row_off.
 __global__ void k_tiles(const int32_t* __restrict__ sel_count, const int32_t* __restrict__ row_off, int B,
@@ -94,6 +96,67 @@ __global__ void k_rowmap(const int32_t* __restrict__ sel_idx, const int32_t* __r
   const int b = lo;
   row_pos[r] = b * S + sel_idx[(size_t)b * S + (r - row_off[b])];
   row_seq[r] = b;
+}
+
+// row_off, the row map and the attention tiles of a selection in one launch:
+// every block forms row_off in LDS from sel_count; the last block writes it
+// out with n_rows and the tiles, the others fill row_pos / row_seq for 256
+// packed rows each.  Same outputs as k_row_off, k_tiles and k_rowmap.
+__global__ __launch_bounds__(256) void k_rowmap_all(const int32_t* __restrict__ sel_idx,
+                                                    const int32_t* __restrict__ sel_count, int B, int S, int R_max,
+                                                    int32_t* __restrict__ row_off, int32_t* __restrict__ n_rows,
+                                                    int32_t* __restrict__ row_pos, int32_t* __restrict__ row_seq,
+                                                    int32_t* __restrict__ tile_row0, int32_t* __restrict__ tile_rows,
+                                                    int T_max, int tq) {
+  __shared__ int32_t roff[kMaxMapSeqs + 1], toff[kMaxMapSeqs + 1];
+  const int t = threadIdx.x;
+  const bool last = blockIdx.x == gridDim.x - 1;
+  if (t == 0) {
+    int acc = 0, tacc = 0;
+    for (int b = 0; b < B; ++b) {
+      roff[b] = acc;
+      toff[b] = tacc;
+      acc += sel_count[b];
+      tacc += (sel_count[b] + tq - 1) / tq;
+    }
+    roff[B] = acc;
+    toff[B] = tacc;
+  }
+  __syncthreads();
+  if (!last) {
+    const int r = blockIdx.x * 256 + t;
+    if (r >= R_max) return;
+    if (r >= roff[B]) {
+      row_pos[r] = -1;
+      row_seq[r] = 0;
+      return;
+    }
+    int lo = 0, hi = B - 1;  // last b with roff[b] <= r
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (roff[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    row_pos[r] = lo * S + sel_idx[(size_t)lo * S + (r - roff[lo])];
+    row_seq[r] = lo;
+    return;
+  }
+  for (int b = t; b <= B; b += 256) row_off[b] = roff[b];
+  if (t == 0) *n_rows = roff[B];
+  for (int s = t; s < T_max; s += 256) {
+    int r0 = 0, rows = 0;
+    if (s < toff[B]) {
+      int lo = 0, hi = B - 1;  // last b with toff[b] <= s
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (toff[mid] <= s) lo = mid; else hi = mid - 1;
+      }
+      const int j0 = (s - toff[lo]) * tq;
+      r0 = roff[lo] + j0;
+      rows = min(tq, sel_count[lo] - j0);
+    }
+    tile_row0[s] = r0;
+    tile_rows[s] = rows;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1092,6 +1155,17 @@ hipError_t launch_rowmap(const int32_t* sel_idx, const int32_t* sel_count, const
                      rm.tile_rows, rm.T_max, rm.tq);
   DTSK_LAUNCH(k_rowmap, dim3(cdiv(rm.R_max, 256)), dim3(256), 0, st, sel_idx, row_off, B, S, rm.R_max,
                      rm.row_pos, rm.row_seq);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_off_map(const int32_t* sel_idx, const int32_t* sel_count, int32_t* row_off, int B, int S,
+                              const RowMap& rm, hipStream_t st) {
+  if (B > kMaxMapSeqs) {   // more sequences than the one-launch kernel holds in LDS
+    hipError_t e = launch_row_off(sel_count, row_off, B, st);
+    return e != hipSuccess ? e : launch_rowmap(sel_idx, sel_count, row_off, B, S, rm, st);
+  }
+  DTSK_LAUNCH(k_rowmap_all, dim3(cdiv(std::max(rm.R_max, 0), 256) + 1), dim3(256), 0, st, sel_idx, sel_count, B, S,
+              rm.R_max, row_off, rm.n_rows, rm.row_pos, rm.row_seq, rm.tile_row0, rm.tile_rows, rm.T_max, rm.tq);
   return hipGetLastError();
 }
 

@@ -14,6 +14,10 @@ hipError_t launch_row_off(const int32_t* sel_count, int32_t* row_off, int B, hip
 // Packed-row maps and attention query tiles of a selection with row_off set.
 hipError_t launch_rowmap(const int32_t* sel_idx, const int32_t* sel_count, const int32_t* row_off, int B, int S,
                          const RowMap& rm, hipStream_t st);
+// row_off, the row maps and the attention tiles of a selection in one launch
+// (launch_row_off followed by launch_rowmap, same outputs).
+hipError_t launch_row_off_map(const int32_t* sel_idx, const int32_t* sel_count, int32_t* row_off, int B, int S,
+                              const RowMap& rm, hipStream_t st);
 // Selection-driven gather / scatter (no row map needed): packed row r of
 // sequence b <-> flat row b*S + sel_idx[b*S + r - row_off[b]].
 hipError_t launch_gather_sel(size_t elem_bytes, const void* src, int w, const int32_t* sel_idx,
