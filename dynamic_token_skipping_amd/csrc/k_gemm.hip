@@ -20,7 +20,7 @@
 //    through LDS; 128 x 128 for many rows, 128 x 64 for up to 128 rows (twice
 //    the column tiles), 256-row tiles with 8 waves for gate|up (192-wide
 //    ragged tiles) and the split-K products on 257..512 rows, 128 x 256
-//    tiles with 8 waves for the LM head.
+//    tiles with 16 waves for the LM head.
 //  * k_gemm_simt: fp32 FMA fallback (fp32 storage, odd shapes); its results
 //    go through the separate epilogue kernels of k_rows.
 //
@@ -306,6 +306,9 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #endif
 #ifndef DTSK_LM256
 #define DTSK_LM256 1
+#endif
+#ifndef DTSK_LM_NW
+#define DTSK_LM_NW 16
 #endif
 // waves and register-ring depth of the 128-row tiles on up to 128 rows
 #ifndef DTSK_SMALL_NW
@@ -811,8 +814,8 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
     const bool wide = epi_kind == EPI_LM || (N % 128 == 0 && N / 128 >= DTSK_T128_MIN_TILES && epi_kind != EPI_QKV &&
                                              (epi_kind != EPI_SWIGLU || F % 64 == 0));
     p.bn = wide ? 128 : 64;
-    // the LM head: 256-wide tiles (8 waves of 32 x 128), which read the rows
-    // of A half as often as 128-wide ones
+    // the LM head: 256-wide tiles (DTSK_LM_NW = 16 waves of 16 x 128), which
+    // read the rows of A half as often as 128-wide ones
     if (DTSK_LM256 && epi_kind == EPI_LM && N % 256 == 0) p.bn = 256;
     if (p.bn != 256) p.nw = p.bn == 128 ? DTSK_SMALL_NW128 : DTSK_SMALL_NW;
     p.wmode = epi_kind == EPI_SWIGLU ? 1 : epi_kind == EPI_QKV ? 2 : 0;
@@ -933,7 +936,7 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
       }
       return launch_tiled<kBN, kBigBM, DTSK_BIG_NW128>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
     }
-    if (plan.bn == 256) return launch_tiled<256, kBM, 8>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+    if (plan.bn == 256) return launch_tiled<256, kBM, DTSK_LM_NW>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
 #if DTSK_SMALL_NW128 == 16
     if (plan.nw == 16 && plan.bn == kBN)
       return launch_tiled<kBN, kBM, 16, DTSK_SMALL_DEPTH>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
