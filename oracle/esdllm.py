@@ -448,11 +448,23 @@ class StepInfo:
     layer_scores: Optional[list] = None      # per-layer variant: 1 - cos of each layer's context change
 
 
+def _positions_in(rows_all: np.ndarray, chosen) -> np.ndarray:
+    """Indices into the ascending array ``rows_all`` of the ascending subset
+    ``chosen`` (an error if ``chosen`` is not such a subset)."""
+    chosen = np.asarray(chosen, np.int64)
+    idx = np.searchsorted(rows_all, chosen)
+    assert idx.size == 0 or (idx.max() < rows_all.size and np.array_equal(rows_all[idx], chosen)), \
+        "forced rows are not a subset of the candidates"
+    assert np.all(np.diff(chosen) > 0), "forced rows must be strictly ascending"
+    return idx.astype(np.int64)
+
+
 def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = "topk",
                  threshold: float = 0.0, force_refresh: Optional[bool] = None,
                  keep: Optional[float] = None, response_only: Optional[bool] = None,
                  mode2: str = "topk", threshold2: float = 0.0, mode_l: str = "topk",
-                 threshold_l: float = 0.0) -> StepInfo:
+                 threshold_l: float = 0.0, force_sel=None, force_sel2=None,
+                 force_layer_sel=None) -> StepInfo:
     """One denoising step of one sequence (ES-dLLM section 2B).
 
     Refresh step: every row through every layer; all caches rewritten.
@@ -467,6 +479,12 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
     level's rows go through [s2, L) and the LM head.  With the per-layer
     variant (DyLLM section 2B), every layer from s on re-selects its salient
     rows by the change of the attention context (``_per_layer``).
+
+    ``force_sel`` / ``force_sel2`` / ``force_layer_sel`` (one array per layer
+    from s) belong to the comparison protocol, not to the method: a skip step
+    then keeps the given rows instead of deciding them itself.  The scores are
+    still computed and returned, so a caller can check the given sets against
+    them; every other computation is unchanged.
     """
     n = st.tokens.shape[0]
     s_layer = sched.skip_layer
@@ -493,7 +511,9 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
         sc = score_rows(sched.score, T, st.h_prev[cand], st.conf[cand], sched.alpha)
         scores = np.full(n, -np.inf)
         scores[cand] = sc
-        if mode == "topk":
+        if force_sel is not None:
+            idx = _positions_in(cand, force_sel)
+        elif mode == "topk":
             idx = select_topk(sc, keep_count(keep, cand.size))
         else:
             idx = select_threshold(sc, threshold)
@@ -503,7 +523,8 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
     xr = x[idx]
     if getattr(sched, "per_layer", False):
         assert s_layer < L and getattr(sched, "skip_layer2", 0) == 0 and not response_only
-        rows, xr, lsel, lsc = _per_layer(model, dims, st, sched, sel, xr, x, refresh, mode_l, threshold_l)
+        rows, xr, lsel, lsc = _per_layer(model, dims, st, sched, sel, xr, x, refresh, mode_l, threshold_l,
+                                         force_layer_sel)
         return _finish_step(model, dims, st, step, sched, rows, xr, StepInfo(
             refresh=refresh, selected=sel, scores=scores, unmasked=None, layer_selected=lsel, layer_scores=lsc))
     sel2, scores2, l_rest = None, None, s_layer
@@ -516,7 +537,9 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
             sc2 = score_rows(sched.score, xr, st.h_prev2[sel], st.conf[sel], sched.alpha)
             scores2 = np.full(n, -np.inf)
             scores2[sel] = sc2
-            if mode2 == "topk":
+            if force_sel2 is not None:
+                idx2 = _positions_in(sel, force_sel2)
+            elif mode2 == "topk":
                 idx2 = select_topk(sc2, level2_count(sched.keep2, cand.size, sel.size))
             else:
                 idx2 = select_threshold(sc2, threshold2)
@@ -555,11 +578,12 @@ def _finish_step(model, dims, st, step, sched, rows, xr, info: StepInfo) -> Step
     return info
 
 
-def _per_layer(model, dims, st, sched, A, xA, X_s, refresh, mode_l, threshold_l):
+def _per_layer(model, dims, st, sched, A, xA, X_s, refresh, mode_l, threshold_l, force_layer_sel=None):
     """Layers [s, L) of the per-layer variant (DyLLM section 2B).  A: the rows
     whose input of layer s is fresh (every row on a refresh step), xA their
     inputs.  Returns (rows through the last layer, their outputs, the salient
-    rows of each layer, each layer's scores)."""
+    rows of each layer, each layer's scores).  ``force_layer_sel[l - s]``,
+    when given, replaces the salient set of layer l (comparison protocol)."""
     n = st.tokens.shape[0]
     H, dh = dims.n_heads, dims.head_dim
     s_layer, L = sched.skip_layer, dims.n_layers
@@ -580,7 +604,12 @@ def _per_layer(model, dims, st, sched, A, xA, X_s, refresh, mode_l, threshold_l)
         C_new = approx_context(st.C[li], st.Q[li], st.LSE[li], K_old, st.V[li][A] - V_old, H, dh)
         C_new[A] = ctx
         sig = score_rows("cosine", C_new, st.C[li], st.conf)
-        R = select_topk(sig, keep_count(keep_l, n)) if mode_l == "topk" else select_threshold(sig, threshold_l)
+        if force_layer_sel is not None:
+            R = _positions_in(np.arange(n, dtype=np.int64), force_layer_sel[li - s_layer])
+        elif mode_l == "topk":
+            R = select_topk(sig, keep_count(keep_l, n))
+        else:
+            R = select_threshold(sig, threshold_l)
         st.C[li] = C_new
         st.Q[li][A] = q
         st.LSE[li][A] = lse

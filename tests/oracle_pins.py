@@ -322,6 +322,70 @@ def pin_skip_step_semantics():
     close(st.conf[sel], torch.softmax(lg, 1).max(1).values.numpy(), rtol=1e-10)
 
 
+def pin_refresh_interval_schedule():
+    """Which steps are full refreshes (ES-dLLM section 2B; ES-dLLM*: more
+    frequent refreshes), written out by hand for two blocks of six steps: a
+    refresh at each block's first step, and with an interval N also at every
+    in-block index that is a multiple of N."""
+    expected = {0: "RSSSSS" "RSSSSS", 2: "RSRSRS" "RSRSRS", 4: "RSSSRS" "RSSSRS", 5: "RSSSSR" "RSSSSR"}
+    for interval, kinds in expected.items():
+        sched = micro_sched(gen_len=12, block_len=6, steps=12, refresh_interval=interval)
+        assert sched.steps_per_block == 6
+        got = "".join("R" if E.is_refresh_step(t, sched) else "S" for t in range(sched.steps))
+        assert got == kinds, (interval, got)
+        _, _, _, _, infos = _micro_run(sched)
+        assert "".join("R" if i.refresh else "S" for i in infos) == kinds, interval
+
+
+def pin_forced_selection_changes_only_the_decision():
+    """The comparison protocol's hook: a skip step told to keep its own
+    selection is bit-identical to the step left alone; told to keep another
+    set, it recomputes exactly that set with the stale-cache partial layers
+    (torch) and still reports its own scores; told to keep every row, it equals
+    the keep = 100% step bit for bit."""
+    import copy
+    sched = micro_sched()
+    dims = micro_dims()
+    m = np_model(dims)
+    prompt = (np.arange(9) * 5) % dims.vocab
+    st0 = E.init_state(prompt, sched.gen_len, dims, keep_logits=True)
+    E.denoise_step(m, dims, st0, 0, sched)                   # refresh
+    fields = ("tokens", "masked", "conf", "argmax", "h_prev", "h_final", "logits")
+
+    def same(a, b):
+        for key in fields:
+            assert np.array_equal(getattr(a, key), getattr(b, key)), key
+        for li in range(dims.n_layers):
+            assert np.array_equal(a.K[li], b.K[li]) and np.array_equal(a.V[li], b.V[li]), li
+
+    st_a, st_b = copy.deepcopy(st0), copy.deepcopy(st0)
+    ia = E.denoise_step(m, dims, st_a, 1, sched)
+    ib = E.denoise_step(m, dims, st_b, 1, sched, force_sel=ia.selected)
+    assert np.array_equal(ia.selected, ib.selected) and np.array_equal(ia.scores, ib.scores)
+    same(st_a, st_b)
+    # another set of the same size: the complement's lowest rows
+    n = len(st0.tokens)
+    other = np.setdiff1d(np.arange(n), ia.selected)[:len(ia.selected)]
+    st_c = copy.deepcopy(st0)
+    tokens1 = st0.tokens.copy()
+    ic = E.denoise_step(m, dims, st_c, 1, sched, force_sel=other)
+    assert np.array_equal(ic.selected, other)
+    close(ic.scores, ia.scores, rtol=0, atol=0)
+    xs = libref.forward(tokens1, m, dims, n_layers=sched.skip_layer)
+    xr = xs[torch.as_tensor(other)]
+    for li in range(sched.skip_layer, dims.n_layers):
+        xr, Kn, Vn = libref.partial_layer(xr, other, m["layers"][li], st0.K[li], st0.V[li], dims)
+        close(st_c.K[li], Kn.numpy(), rtol=1e-11)
+    close(st_c.h_final[other], xr.numpy(), rtol=1e-11)
+    rest = np.setdiff1d(np.arange(n), other)
+    assert np.array_equal(st_c.h_final[rest], st0.h_final[rest])
+    # every row forced == keep = 100%
+    st_d, st_e = copy.deepcopy(st0), copy.deepcopy(st0)
+    E.denoise_step(m, dims, st_d, 1, sched, force_sel=np.arange(n))
+    E.denoise_step(m, dims, st_e, 1, sched, keep=1.0)
+    same(st_d, st_e)
+
+
 def pin_keep_all_equals_vanilla():
     """keep = 100% is full recomputation, bit for bit, over a whole decode."""
     sched = micro_sched(keep=1.0)

@@ -15,7 +15,8 @@ _orig = {name: getattr(E, name) for name in ("score_rows", "rms_norm", "rope", "
                                              "unmask", "keep_count", "conf_argmax", "silu", "layer_forward",
                                              "select_threshold", "candidate_rows", "level2_count",
                                              "is_full_context_step", "scored_tensor", "approx_context",
-                                             "attention_lse", "layer_input_rows", "finish_layer")}
+                                             "attention_lse", "layer_input_rows", "finish_layer",
+                                             "is_refresh_step", "_positions_in")}
 
 
 def m_score_l2(kind, x, h, c, alpha=0.5):          # L2 instead of L1 in eq. I
@@ -163,6 +164,20 @@ def m_finish_noresid(x, ctx, lw, dims):               # attention residual dropp
     return _orig["finish_layer"](np.zeros_like(np.asarray(x)), ctx, lw, dims)
 
 
+def m_refresh_no_interval(step, sched):            # the refresh interval ignored
+    return step % sched.steps_per_block == 0
+
+
+def m_refresh_interval_off_by_one(step, sched):    # every (N+1)-th in-block step instead of every N-th
+    sib = step % sched.steps_per_block
+    return sib == 0 or (sched.refresh_interval > 0 and sib % (sched.refresh_interval + 1) == 0)
+
+
+def m_forced_shift(rows_all, chosen):               # forced rows taken one candidate late
+    idx = _orig["_positions_in"](rows_all, chosen)
+    return np.minimum(idx + 1, len(rows_all) - 1)
+
+
 MUTANTS = [
     ("score_rows", m_score_l2), ("score_rows", m_score_csign), ("score_rows", m_score_nosqrtd),
     ("rms_norm", m_rms_noeps), ("rope", m_rope_sign), ("rope", m_rope_pairs),
@@ -176,6 +191,8 @@ MUTANTS = [
     ("scored_tensor", m_key_from_wq), ("scored_tensor", m_key_unrotated), ("scored_tensor", m_kv_unnormed),
     ("approx_context", m_approx_sign), ("approx_context", m_approx_nolse), ("attention_lse", m_lse_noscale),
     ("layer_input_rows", m_input_always_xs), ("finish_layer", m_finish_noresid),
+    ("is_refresh_step", m_refresh_no_interval), ("is_refresh_step", m_refresh_interval_off_by_one),
+    ("_positions_in", m_forced_shift),
 ]
 
 
