@@ -48,6 +48,8 @@ def parse():
                     help="time about one launch in this many of each kernel class (1: every launch)")
     ap.add_argument("--no-variants", action="store_true",
                     help="only the headline decode: skip the per-step, one-layer and variant timings")
+    ap.add_argument("--no-sample", action="store_true",
+                    help="skip the sampled kernel-timing pass that follows the headline steps")
     return ap.parse_args()
 
 
@@ -128,6 +130,90 @@ def time_variant(torch, Decoder, dev_model, prompts, sched, steps: int, warmup: 
     del dec
     torch.cuda.empty_cache()
     return out
+
+
+def keep_rows(keep: float, n: int) -> int:
+    """Rows a top-k step keeps of n: ceil(keep * n) with keep read as float32,
+    clamped to [1, n] (the count the library computes)."""
+    import math
+
+    import numpy as np
+    return max(1, min(n, math.ceil(float(np.float32(keep)) * n))) if n > 0 else 0
+
+
+def decode_step_flops(dims, lens, sched, refresh: bool) -> float:
+    """Algorithmic FLOPs of one step: every layer's products on its rows
+    (2 * layer params * rows), attention (4 * d * rows * keys per sequence)
+    and the LM head (2 * vocab * d * rows) on the rows that reach it."""
+    P, d, L, s = dims.layer_params(), dims.d, dims.n_layers, sched.skip_layer
+    ks = lens if refresh else [keep_rows(sched.keep, n) for n in lens]
+    full = s * (2.0 * P * sum(lens) + 4.0 * d * sum(n * n for n in lens))
+    part = (L - s) * (2.0 * P * sum(ks) + 4.0 * d * sum(k * n for k, n in zip(ks, lens)))
+    return full + part + 2.0 * dims.vocab * d * sum(ks)
+
+
+def time_batched(torch, Decoder, dev_model, steps: int = 32, warmup: int = 4):
+    """The batched workload (16 sequences, prompts ~U{128..1024} right-padded,
+    256 generated each, blocks of 32, 128 steps x 2 tokens, keep 1/4 per
+    sequence) on the loaded weights: steps/s and tokens/s over the decode's
+    first `steps` steps (refresh steps included), and the algorithmic FLOP rate
+    against the bf16 matrix-core peak (the step is matrix-core bound: about
+    3.3k kept rows)."""
+    import workloads
+    wl = workloads.workload("batch8b")
+    prompts, lens = workloads.make_prompt(wl)
+    dec = Decoder(dev_model, prompts, wl.sched)
+    for t in range(warmup):
+        dec.step(t)
+    dec.reset()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for t in range(steps):
+        dec.step(t)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    flops = sum(decode_step_flops(wl.dims, dec.seq_lens, wl.sched, bool(dec.params(t).full_refresh))
+                for t in range(steps))
+    n_ref = sum(bool(dec.params(t).full_refresh) for t in range(steps))
+    tflops = flops / (ms / 1e3) / 1e12
+    out = {"workload": ("batch8b: 16 sequences, prompts ~U{128..1024} right-padded + 256 masked each, blocks of 32, "
+                        "128 steps x 2 tokens, skip layer 4, keep 1/4 per sequence, full8b weights"),
+           "steps": steps, "refresh_steps": n_ref, "steps_per_s": round(steps / (ms / 1e3), 3),
+           "ms_per_step": round(ms / steps, 3),
+           "gen_tokens_per_s": round(steps / (ms / 1e3) * dec.per_step * dec.B, 1),
+           "rows": sum(dec.seq_lens), "kept_rows_per_skip_step": sum(keep_rows(wl.sched.keep, n) for n in dec.seq_lens),
+           "TFLOP/s": round(tflops, 1), "frac_mfma": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    del dec
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_tiny(torch, reps: int = 40):
+    """The tiny workload (2 layers, d 64, fp32, 16 prompt + 48 masked, 8 steps
+    x 6 tokens): steps/s over `reps` whole decodes.  Launch-bound; no roofline
+    claim."""
+    import workloads
+    from dynamic_token_skipping_amd import Decoder, DeviceModel
+    wl = workloads.workload("tiny")
+    m = workloads.make_model(wl.dims, wl.seed, wl.dtype, "cuda")
+    prompts, _ = workloads.make_prompt(wl)
+    dec = Decoder(DeviceModel(m, wl.dims.n_heads, wl.dims.head_dim, wl.dtype), prompts, wl.sched)
+    dec.run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dec.reset()
+        dec.run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    n = reps * wl.sched.steps
+    return {"workload": "tiny: 2 layers, d 64, fp32, 16 prompt + 48 masked, 8 steps x 6 tokens, keep 16 of 64",
+            "steps": n, "steps_per_s": round(n / (ms / 1e3), 1), "ms_per_step": round(ms / n, 4),
+            "decodes_per_s": round(reps / (ms / 1e3), 2)}
 
 
 def time_step_kinds(torch, dec, sched, n_steps: int):
@@ -216,64 +302,57 @@ def time_layer_steps(torch, model, n_steps: int = 30, warmup: int = 3):
     return out
 
 
-def cpu_baseline(wl, model_gpu, prompts, budget_s: float = 20.0):
-    """Time the fp64 oracle on host cores on a bounded sample of one skip step.
+def blas_threads() -> int:
+    """Threads numpy's BLAS runs the oracle's products on."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
 
-    The sample runs, once each, the three kinds of work a skip step is made of:
-    one layer on every row (the prefix kind, 512 rows), one partial layer on the
-    kept rows (128 rows against the full K/V cache), and the LM head with
-    confidence/argmax on the kept rows; the per-step time is then
-    s * t_full + (L - s) * t_partial + t_lm + t_score.  Layer 0's weights stand
-    in for every layer (same shapes).
-    """
+
+def cpu_baseline(wl, model_gpu, prompts, skip_steps: int = 4):
+    """The fp64 oracle's own decode loop on the host cores, on a bounded
+    sample of the same workload: from the initial state of the first
+    sequence, its refresh step (step 0) and the next ``skip_steps`` skip steps,
+    each timed.  Every layer uses its own weights (converted to float64 once,
+    before the timed steps).  The per-step rate of a whole decode follows from
+    the schedule: each block has one refresh step and steps_per_block - 1
+    skip steps."""
     import numpy as np
     import torch
 
     from oracle import esdllm as E
-    import workloads
 
     dims, sched = wl.dims, wl.sched
-    threads = len(os.sched_getaffinity(0))
-    lw = {k: workloads.host_f64(v) for k, v in model_gpu["layers"][0].items()}
-    fin = workloads.host_f64(model_gpu["final_norm"])
-    lm = workloads.host_f64(model_gpu["lm_head"])
-    emb = model_gpu["embed"]
-    n = len(prompts[0]) + sched.gen_len
-    tokens = torch.cat([prompts[0].cpu(), torch.full((sched.gen_len,), dims.vocab - 1)])
-    x = workloads.host_f64(emb[tokens.to(emb.device)])
-    K = np.zeros((n, dims.d))
-    V = np.zeros((n, dims.d))
-    pos = np.arange(n)
-    k = E.keep_count(sched.keep, n)
-    rows = np.arange(0, n, n // k)[:k]
-    conf = np.random.default_rng(0).uniform(size=n)
-    t_full = t_part = t_lm = t_sc = 0.0
-    reps = 0
-    while reps == 0 or (t_full + t_part + t_lm + t_sc < budget_s and reps < 50):
+    t0 = time.perf_counter()
+    m_np = {"embed": model_gpu["embed"].to(torch.float64).cpu().numpy(),
+            "final_norm": model_gpu["final_norm"].to(torch.float64).cpu().numpy(),
+            "lm_head": model_gpu["lm_head"].to(torch.float64).cpu().numpy(),
+            "layers": [{k: v.to(torch.float64).cpu().numpy() for k, v in lw.items()} for lw in model_gpu["layers"]]}
+    t_convert = time.perf_counter() - t0
+    st = E.init_state(prompts[0].numpy(), sched.gen_len, dims)
+    times = []
+    for t in range(1 + skip_steps):
         t0 = time.perf_counter()
-        x1 = E.layer_forward(x, pos, lw, K, V, n, dims)
-        t_full += time.perf_counter() - t0
-        t0 = time.perf_counter()
-        E.layer_forward(x1[rows], rows, lw, K, V, n, dims)
-        t_part += time.perf_counter() - t0
-        t0 = time.perf_counter()
-        E.conf_argmax(E.lm_logits(x1[rows], fin, lm, dims.rms_eps))
-        t_lm += time.perf_counter() - t0
-        t0 = time.perf_counter()
-        E.select_topk(E.score_rows(sched.score, x1, x, conf, sched.alpha), k)
-        t_sc += time.perf_counter() - t0
-        reps += 1
-    measured = t_full + t_part + t_lm + t_sc
-    t_full, t_part, t_lm, t_sc = (v / reps for v in (t_full, t_part, t_lm, t_sc))
-    s = sched.skip_layer
-    per_step = s * t_full + (dims.n_layers - s) * t_part + t_lm + t_sc
-    return {"value": 1.0 / per_step, "unit": "denoise steps/s (skip step)", "cores": threads, "kind": "oracle",
-            "sample": (f"one skip step of the same workload assembled from timed pieces (mean of {reps} repeats): "
-                       f"1 full-row layer "
-                       f"({n} rows, {t_full:.2f} s) x {s}, 1 partial layer ({k} rows vs {n} keys, {t_part:.2f} s) x "
-                       f"{dims.n_layers - s}, LM head + confidence on {k} rows ({t_lm:.2f} s), score+select "
-                       f"({t_sc:.3f} s); fp64 numpy, layer 0 weights for every layer"),
-            "seconds_measured": round(measured, 2)}
+        info = E.denoise_step(m_np, dims, st, t, sched)
+        times.append(time.perf_counter() - t0)
+        assert info.refresh == (t == 0)
+    del m_np
+    t_ref, t_skip = times[0], sum(times[1:]) / skip_steps
+    spb = sched.steps_per_block
+    per_step = (t_ref + (spb - 1) * t_skip) / spb
+    return {"value": round(1.0 / per_step, 4), "unit": "denoise steps/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": (f"the oracle's decode loop (oracle.esdllm.denoise_step, fp64 numpy) on the first sequence "
+                       f"of the same workload with every layer's own weights: step 0 (refresh, "
+                       f"{t_ref:.2f} s) and steps 1..{skip_steps} (skip, mean {t_skip:.2f} s); a decode step "
+                       f"= (1 refresh + {spb - 1} skip) / {spb}; weights converted to float64 beforehand "
+                       f"({t_convert:.1f} s, not timed)"),
+            "refresh_step_s": round(t_ref, 3), "skip_step_s": round(t_skip, 3),
+            "seconds_measured": round(sum(times), 2)}
 
 
 def recorded_traffic():
@@ -342,10 +421,7 @@ def main():
     dec.reset()
     torch.cuda.synchronize()
 
-    dl_timing_reset()
-    classes = (DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD, DL_KC_GEMM_TILED)
-    for kc in classes:
-        dl_timing_enable(kc, 1 if kc == DL_KC_LMHEAD else max(1, args.timing_stride))
+    # the headline: K steps of the decode, no instrumentation
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -358,22 +434,39 @@ def main():
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    for kc in classes:
-        dl_timing_enable(kc, 0)
     ms = start.elapsed_time(end)
     steps_per_s = args.steps / (ms / 1e3)
     tok_per_s = steps_per_s * dec.per_step * dec.B
 
+    # a separate pass samples kernel durations: about one launch in
+    # timing_stride of each product class (every LM-head launch), each timed by
+    # HIP events bound to its own dispatch packets on the decode stream
+    classes = (DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD, DL_KC_GEMM_TILED)
+    sample_steps = min(args.steps, 2 * dec.steps_per_block)
+    dl_timing_reset()
+    if not args.no_sample:
+        for kc in classes:
+            dl_timing_enable(kc, 1 if kc == DL_KC_LMHEAD else max(1, args.timing_stride))
+        dec.reset()
+        for t in range(sample_steps):
+            dec.step(t)
+        torch.cuda.synchronize()
+        for kc in classes:
+            dl_timing_enable(kc, 0)
+        dec.reset()
     g = dl_timing_read(DL_KC_GEMM)
     a = dl_timing_read(DL_KC_ATTN)
     lmh = dl_timing_read(DL_KC_LMHEAD)
     gt = dl_timing_read(DL_KC_GEMM_TILED)
-    gemm_gbs = g["bytes"] / (g["ms"] / 1e3) / 1e9 if g["ms"] > 0 else 0.0
-    roofline = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": recorded_traffic(),
+    gemm_gbs = g["bytes"] / (g["ms"] / 1e3) / 1e9 if g["ms"] > 0 else None
+    roofline = {"bound": "hbm", "achieved": round(gemm_gbs, 1) if gemm_gbs else None, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(gemm_gbs / PEAK_HBM_GBS, 4) if gemm_gbs else None,
+                "traffic": recorded_traffic(),
                 "kernel": ("layer products on the 128 kept rows (128-row tiles, 8 waves): k_gemm_mfma BN 64 with 4 K "
                            "splits (O, down), BN 128 with 2 K splits + k_epi_qkv_rows4 (QKV), BN 128 on 256 "
                            "ragged tiles (gate|up)"),
+                "sample": (f"a separate pass of {sample_steps} decode steps after the headline steps, about one "
+                           f"launch in {max(1, args.timing_stride)} timed"),
                 "launches_timed": g["launches"], "launches_total": g["launches"] + g["dropped"],
                 "avg_launch_us": round(g["ms"] * 1e3 / max(g["launches"], 1), 2),
                 "alg_bytes_per_launch": round(g["bytes"] / max(g["launches"], 1))}
@@ -388,7 +481,8 @@ def main():
                    "global_batch": dec.B, "seq_len": dec.S, "keep": sched.keep, "skip_layer": sched.skip_layer},
         "roofline": roofline,
         "kernels": {
-            "gemm": {"ms_timed": round(g["ms"], 3), "launches_timed": g["launches"], "GB/s": round(gemm_gbs, 1),
+            "gemm": {"ms_timed": round(g["ms"], 3), "launches_timed": g["launches"],
+                     "GB/s": round(gemm_gbs, 1) if gemm_gbs else None,
                      "TFLOP/s": round(g["flops"] / max(g["ms"], 1e-9) / 1e9, 1)},
             "gemm_tiled": {"ms_timed": round(gt["ms"], 3), "launches_timed": gt["launches"],
                            "GB/s": round(gt["bytes"] / max(gt["ms"], 1e-9) / 1e6, 1),
@@ -418,6 +512,8 @@ def main():
             out["variants"][name] = time_variant(torch, Decoder, dev_model, lprompts, vs, 64, 4,
                                                  (DL_KC_ATTN, DL_KC_APPROX) if vs.per_layer else (DL_KC_ATTN,))
         out["variants"]["kernel_classes"] = {str(DL_KC_ATTN): "attention", str(DL_KC_APPROX): "approximate context"}
+        out["variants"]["batched"] = time_batched(torch, Decoder, dev_model)
+        out["variants"]["tiny"] = time_tiny(torch)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, model, prompts)
     else:

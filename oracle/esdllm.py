@@ -464,7 +464,7 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
                  keep: Optional[float] = None, response_only: Optional[bool] = None,
                  mode2: str = "topk", threshold2: float = 0.0, mode_l: str = "topk",
                  threshold_l: float = 0.0, force_sel=None, force_sel2=None,
-                 force_layer_sel=None) -> StepInfo:
+                 force_layer_sel=None, x_s=None) -> StepInfo:
     """One denoising step of one sequence (ES-dLLM section 2B).
 
     Refresh step: every row through every layer; all caches rewritten.
@@ -484,7 +484,11 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
     from s) belong to the comparison protocol, not to the method: a skip step
     then keeps the given rows instead of deciding them itself.  The scores are
     still computed and returned, so a caller can check the given sets against
-    them; every other computation is unchanged.
+    them; every other computation is unchanged.  ``x_s`` (comparison protocol
+    as well) gives the skip layer's input of the candidate rows [n_cand, d]:
+    layers [0, s) are then not run (their caches are per-step scratch) and the
+    step goes on from those rows, so that a later stage can be compared from
+    the same input as another implementation's.
     """
     n = st.tokens.shape[0]
     s_layer = sched.skip_layer
@@ -497,9 +501,13 @@ def denoise_step(model: dict, dims, st: SeqState, step: int, sched, mode: str = 
     keep = sched.keep if keep is None else keep
     cand = candidate_rows(st, response_only)
 
-    x = np.asarray(model["embed"], F64)[st.tokens[cand]]     # [n_cand, d]
-    for li in range(s_layer):
-        x = layer_forward(x, cand, model["layers"][li], st.K[li], st.V[li], n, dims)
+    if x_s is None:
+        x = np.asarray(model["embed"], F64)[st.tokens[cand]]     # [n_cand, d]
+        for li in range(s_layer):
+            x = layer_forward(x, cand, model["layers"][li], st.K[li], st.V[li], n, dims)
+    else:
+        x = np.array(x_s, F64, copy=True)
+        assert x.shape == (cand.size, dims.d), "x_s must hold the skip-layer input of every candidate row"
 
     which = getattr(sched, "score_tensor", "hidden")
     assert which == "hidden" or s_layer < L, "a key/value score needs layer s to exist"

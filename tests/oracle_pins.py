@@ -386,6 +386,45 @@ def pin_forced_selection_changes_only_the_decision():
     same(st_d, st_e)
 
 
+def pin_stage_input_hook():
+    """The comparison protocol's second hook: a step given its own skip-layer
+    input is bit-identical to the step left alone (prefix caches aside, which
+    are per-step scratch); given another input, it scores that input by eq. I
+    and runs the partial layers (torch) from it."""
+    import copy
+    sched = micro_sched()
+    dims = micro_dims()
+    m = np_model(dims)
+    prompt = (np.arange(9) * 3) % dims.vocab
+    st0 = E.init_state(prompt, sched.gen_len, dims, keep_logits=True)
+    E.denoise_step(m, dims, st0, 0, sched)
+    st_a, st_b = copy.deepcopy(st0), copy.deepcopy(st0)
+    ia = E.denoise_step(m, dims, st_a, 1, sched)
+    ib = E.denoise_step(m, dims, st_b, 1, sched, x_s=st_a.h_prev)
+    assert np.array_equal(ia.selected, ib.selected) and np.array_equal(ia.scores, ib.scores)
+    for key in ("tokens", "masked", "conf", "argmax", "h_prev", "h_final", "logits"):
+        assert np.array_equal(getattr(st_a, key), getattr(st_b, key)), key
+    for li in range(sched.skip_layer, dims.n_layers):
+        assert np.array_equal(st_a.K[li], st_b.K[li]) and np.array_equal(st_a.V[li], st_b.V[li])
+    # another input: X_s shifted by a constant row
+    n = len(st0.tokens)
+    x2 = st_a.h_prev + 0.05 * np.sin(np.arange(dims.d))[None, :]
+    st_c = copy.deepcopy(st0)
+    ic = E.denoise_step(m, dims, st_c, 1, sched, x_s=x2)
+    hp = libref.t(st0.h_prev)
+    xt = libref.t(x2)
+    sc = 0.5 * libref.t(st0.conf) + 0.5 * (xt - hp).abs().sum(1) / (math.sqrt(dims.d) * hp.norm(dim=1))
+    close(ic.scores, sc.numpy(), rtol=1e-12)
+    sel = ic.selected
+    assert sel.tolist() == _brute_topk(sc.numpy(), E.keep_count(sched.keep, n))
+    close(st_c.h_prev, x2, rtol=0, atol=0)
+    xr = xt[torch.as_tensor(sel)]
+    for li in range(sched.skip_layer, dims.n_layers):
+        xr, Kn, Vn = libref.partial_layer(xr, sel, m["layers"][li], st0.K[li], st0.V[li], dims)
+        close(st_c.K[li], Kn.numpy(), rtol=1e-11)
+    close(st_c.h_final[sel], xr.numpy(), rtol=1e-11)
+
+
 def pin_keep_all_equals_vanilla():
     """keep = 100% is full recomputation, bit for bit, over a whole decode."""
     sched = micro_sched(keep=1.0)

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import host, np_model, row_rel_err, selection_diff_ok, sync_from_oracle, to_device
+from gpu_util import bf16_step, host, np_model, row_rel_err, to_device
 from oracle import esdllm as E
 
 pytestmark = pytest.mark.gpu
@@ -45,25 +45,21 @@ def _scores_ok(g, o, tol):
     return np.abs(g[cand] - o[cand]).max(initial=0.0) <= tol * max(1.0, np.abs(o[cand]).max(initial=0.0))
 
 
-@pytest.mark.parametrize("dtype,tol", [("f32", 1e-5), ("bf16", 2e-2)])
 @pytest.mark.parametrize("sched", [NESTED, RESP, BOTH, NESTED_LAST, KEY, VALUE, KEY_RESP_NESTED],
                          ids=["nested", "resp", "both", "nested_last", "key", "value", "key_resp_nested"])
-def test_decode_matches_oracle(dtype, tol, sched):
-    m_np, dec, sts = _setup(dtype, sched)
+def test_decode_matches_oracle_f32(sched):
+    """fp32: the whole trajectory; both levels' kept sets and the tokens
+    identical to the oracle's, every value within 1e-5."""
+    tol = 1e-5
+    m_np, dec, sts = _setup("f32", sched)
     two = sched.skip_layer2 > 0
-    s_tol = 1e-5 if dtype == "f32" else 1e-2
-    exact_steps = 0
     kinds = set()
     for t in range(sched.steps):
-        if dtype == "bf16":
-            for b, st in enumerate(sts):
-                sync_from_oracle(dec, b, st)
         infos = [E.denoise_step(m_np, DIMS, st, t, sched) for st in sts]
         dec.step(t)
         torch.cuda.synchronize()
         g1 = dec.sel.rows()
         g2 = dec.sel2.rows() if two else g1
-        same = True
         for b, (st, info) in enumerate(zip(sts, infos)):
             n = len(st.tokens)
             kinds.add("R" if info.refresh else ("r" if info.response_only else "F"))
@@ -72,24 +68,10 @@ def test_decode_matches_oracle(dtype, tol, sched):
             if info.refresh:
                 assert g1[b] == list(range(n)) and g2[b] == list(range(n)), (t, b)
             else:
-                assert _scores_ok(host(dec.scores[b, :n]), info.scores, s_tol), (t, b)
-                n_cand = int(np.isfinite(info.scores).sum())
-                ok, nd = selection_diff_ok(g1[b], o1, info.scores, E.keep_count(sched.keep, n_cand), 1e-4,
-                                           0.0 if dtype == "f32" else 2e-2)
-                assert ok, (t, b, "level 1")
-                if nd:
-                    same = False
-                    continue
+                assert _scores_ok(host(dec.scores[b, :n]), info.scores, tol), (t, b)
                 assert g1[b] == o1.tolist(), (t, b)
                 if two:
-                    assert _scores_ok(host(dec.scores2[b, :n]), info.scores2, s_tol), (t, b)
-                    assert set(g2[b]) <= set(g1[b])
-                    k2 = E.level2_count(sched.keep2, n_cand, len(o1))
-                    ok, nd = selection_diff_ok(g2[b], o2, info.scores2, k2, 1e-4, 0.0 if dtype == "f32" else 2e-2)
-                    assert ok, (t, b, "level 2")
-                    if nd:
-                        same = False
-                        continue
+                    assert _scores_ok(host(dec.scores2[b, :n]), info.scores2, tol), (t, b)
                     assert g2[b] == o2.tolist(), (t, b)
             rows = np.asarray(o2)
             assert row_rel_err(host(dec.h_prev[b, :n]), st.h_prev) <= tol, (t, b)
@@ -100,13 +82,20 @@ def test_decode_matches_oracle(dtype, tol, sched):
             for li in range(DIMS.n_layers):
                 assert row_rel_err(host(dec.k_cache[li, b, :n]), st.K[li]) <= tol, (t, b, li)
                 assert row_rel_err(host(dec.v_cache[li, b, :n]), st.V[li]) <= tol, (t, b, li)
-            if dtype == "f32":
-                assert np.array_equal(dec.tokens[b, :n].cpu().numpy(), st.tokens), (t, b)
-        exact_steps += same
-    if dtype == "f32":
-        assert exact_steps == sched.steps
+            assert np.array_equal(dec.tokens[b, :n].cpu().numpy(), st.tokens), (t, b)
     if sched.response_interval:
         assert kinds == {"R", "r", "F"}
+
+
+@pytest.mark.parametrize("sched", [NESTED, RESP, BOTH, NESTED_LAST, KEY, VALUE, KEY_RESP_NESTED],
+                         ids=["nested", "resp", "both", "nested_last", "key", "value", "key_resp_nested"])
+def test_decode_matches_oracle_bf16(sched):
+    """bf16: every step from the oracle's state with the GPU's kept sets of
+    both levels forced into the oracle; selections and unmasking exact on the
+    GPU's own inputs within 1e-4, every value within 2e-2 at every step."""
+    m_np, dec, sts = _setup("bf16", sched)
+    for t in range(sched.steps):
+        bf16_step(dec, m_np, DIMS, sts, t, sched, 2e-2)
 
 
 def test_second_level_threshold_mode():

@@ -9,7 +9,9 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import host, np_model, row_rel_err, selection_diff_ok, sync_from_oracle, to_device
+from gpu_util import (check_lm_rows_exact_inputs, check_scores_exact_inputs, check_unmask_exact_inputs, host,
+                      implied_band_ok, np_model, row_rel_err, snapshot, sync_from_oracle, to_device,
+                      topk_within_band)
 from oracle import esdllm as E
 
 pytestmark = pytest.mark.gpu
@@ -31,70 +33,91 @@ def _setup(dtype, sched, seed=29):
     return np_model(m_cpu), dec, sts
 
 
+def _salient_rows(dec, y_before, li, b, n):
+    """The GPU's salient rows of layer li: those whose cached output changed."""
+    return torch.nonzero((dec.y_cache[li, b, :n] != y_before[li, b, :n]).any(dim=1)).flatten().tolist()
+
+
+def _compare_values(dec, st, b, n, rows, s, tol, t):
+    for li in range(s, DIMS.n_layers):
+        assert row_rel_err(host(dec.ctx_cache[li, b, :n]), st.C[li]) <= tol, (t, b, li, "ctx")
+        assert row_rel_err(host(dec.q_cache[li, b, :n]), st.Q[li]) <= tol, (t, b, li, "q")
+        assert row_rel_err(host(dec.y_cache[li, b, :n]), st.Y[li]) <= tol, (t, b, li, "y")
+        assert np.abs(host(dec.lse_cache[li, b, :n]) - st.LSE[li]).max() <= tol * 10, (t, b, li, "lse")
+        assert row_rel_err(host(dec.k_cache[li, b, :n]), st.K[li]) <= tol, (t, b, li, "K")
+        assert row_rel_err(host(dec.v_cache[li, b, :n]), st.V[li]) <= tol, (t, b, li, "V")
+    assert row_rel_err(host(dec.h_final[b, :n])[rows], st.h_final[rows]) <= tol, (t, b)
+    assert row_rel_err(host(dec.logits[b, :n])[rows], st.logits[rows]) <= tol, (t, b)
+
+
 @pytest.mark.parametrize("dtype,tol", [("f32", 1e-5), ("bf16", 2e-2)])
 @pytest.mark.parametrize("keep_layer", [0.25, 0.5])
 def test_per_layer_decode_matches_oracle(dtype, tol, keep_layer):
+    """Every step from the oracle's state: the first-level set and each
+    layer's salient set checked against the oracle's top-k of the scores of
+    the GPU's own inputs (eq. I on h_prev; 1 - cos of the context caches
+    before and after) within 1e-4, then forced into the oracle's step, whose
+    every value is compared within 1e-5 (fp32) or 2e-2 (bf16) at every step;
+    the oracle's own sets may differ only within 1e-4 + twice the measured
+    score difference.  The saliencies of rows whose context barely moved lie
+    within 1e-4 of each other, so even an fp32 trajectory may legitimately
+    take another of two near-equal rows; hence one step at a time in fp32
+    too."""
     sched = dataclasses.replace(SCHED, keep_layer=keep_layer)
     m_np, dec, sts = _setup(dtype, sched)
     s = sched.skip_layer
-    band = (1e-4, 0.0) if dtype == "f32" else (1e-4, 2e-2)
-    exact = 0
     for t in range(sched.steps):
-        # every step starts from the oracle's state: a within-band selection
-        # difference (1 - cos of stable rows sits close together) stays local
         for b, st in enumerate(sts):
             sync_from_oracle(dec, b, st)
+        before = snapshot(dec)
         y_before = dec.y_cache.clone()
-        infos = [E.denoise_step(m_np, DIMS, st, t, sched) for st in sts]
         dec.step(t)
         torch.cuda.synchronize()
+        after = snapshot(dec, ("tokens", "masked", "h_prev", "conf", "argmax", "scores", "ctx_cache",
+                               "layer_scores"))
         g_sel, g_last = dec.sel.rows(), dec.sel_l.rows()
-        same = True
-        for b, (st, info) in enumerate(zip(sts, infos)):
+        refresh = E.is_refresh_step(t, sched)
+        for b, st in enumerate(sts):
             n = len(st.tokens)
-            if info.refresh:
+            cand = np.arange(n, dtype=np.int64)
+            kw = {}
+            if refresh:
                 assert g_sel[b] == list(range(n)) and g_last[b] == list(range(n)), (t, b)
             else:
-                ok, nd = selection_diff_ok(g_sel[b], info.selected, info.scores, E.keep_count(sched.keep, n), *band)
-                assert ok, (t, b, "first level")
-                if nd:
-                    same = False
-                    continue
-                assert g_sel[b] == info.selected.tolist()
+                k1 = E.keep_count(sched.keep, n)
+                s1 = check_scores_exact_inputs(after["scores"][b], after["h_prev"][b], before["h_prev"][b],
+                                               before["conf"][b], sched.score, sched.alpha, cand)
+                assert topk_within_band(g_sel[b], cand, s1, k1)[0], (t, b, "level 1")
                 k_l = E.keep_count(keep_layer, n)
-                for i, li in enumerate(range(s, DIMS.n_layers)):
-                    # the GPU's salient rows of layer li: those whose cached output changed
-                    changed = torch.nonzero((dec.y_cache[li, b, :n] != y_before[li, b, :n]).any(dim=1))
-                    g_rows = changed.flatten().tolist()
-                    ok, nd = selection_diff_ok(g_rows, info.layer_selected[i], info.layer_scores[i], k_l, *band)
-                    assert ok, (t, b, li)
-                    if nd:
-                        same = False
-                        break
-                    assert g_rows == info.layer_selected[i].tolist(), (t, b, li)
-                if not same:
-                    continue
-                assert g_last[b] == info.layer_selected[-1].tolist()
-                sc = host(dec.layer_scores[b, :n])
-                o = info.layer_scores[-1]
-                assert np.abs(sc - o).max() <= (1e-5 if dtype == "f32" else 2e-2) * max(1.0, np.abs(o).max())
+                forced, s_layers = [], []
+                for li in range(s, DIMS.n_layers):
+                    g_rows = _salient_rows(dec, y_before, li, b, n)
+                    s_l = E.score_rows("cosine", after["ctx_cache"][li, b, :n], before["ctx_cache"][li, b, :n],
+                                       before["conf"][b, :n])
+                    assert topk_within_band(g_rows, cand, s_l, k_l)[0], (t, b, li)
+                    forced.append(np.asarray(g_rows, np.int64))
+                    s_layers.append(s_l)
+                assert g_last[b] == forced[-1].tolist()
+                check_scores_exact_inputs(after["layer_scores"][b], after["ctx_cache"][-1, b], before["ctx_cache"][-1, b],
+                                          before["conf"][b], "cosine", 0.5, cand)
+                kw = dict(force_sel=np.asarray(g_sel[b], np.int64), force_layer_sel=forced)
+            info = E.denoise_step(m_np, DIMS, st, t, sched, **kw)
+            if not refresh:
+                assert implied_band_ok(g_sel[b], E.select_topk(info.scores, k1), s1, info.scores, cand, k1)[0]
+                for i, s_l in enumerate(s_layers):
+                    o_rows = E.select_topk(info.layer_scores[i], k_l)
+                    assert implied_band_ok(forced[i], o_rows, s_l, info.layer_scores[i], cand, k_l)[0], (t, b, i)
             rows = info.layer_selected[-1]
-            for li in range(s, DIMS.n_layers):
-                assert row_rel_err(host(dec.ctx_cache[li, b, :n]), st.C[li]) <= tol, (t, b, li, "ctx")
-                assert row_rel_err(host(dec.q_cache[li, b, :n]), st.Q[li]) <= tol, (t, b, li, "q")
-                assert row_rel_err(host(dec.y_cache[li, b, :n]), st.Y[li]) <= tol, (t, b, li, "y")
-                assert np.abs(host(dec.lse_cache[li, b, :n]) - st.LSE[li]).max() <= tol * 10, (t, b, li, "lse")
-                assert row_rel_err(host(dec.k_cache[li, b, :n]), st.K[li]) <= tol, (t, b, li, "K")
-                assert row_rel_err(host(dec.v_cache[li, b, :n]), st.V[li]) <= tol, (t, b, li, "V")
-            assert row_rel_err(host(dec.h_final[b, :n])[rows], st.h_final[rows]) <= tol, (t, b)
-            assert row_rel_err(host(dec.logits[b, :n])[rows], st.logits[rows]) <= tol, (t, b)
-            if dtype == "f32":
-                assert np.array_equal(dec.tokens[b, :n].cpu().numpy(), st.tokens), (t, b)
-        exact += same
-    # bf16: the stable rows' saliencies carry the storage rounding of the cached
-    # queries and value changes, so within-band differences are common; every
-    # step still passes the band check, and some are compared value by value
-    assert exact >= (sched.steps - 1 if dtype == "f32" else 2), exact
+            _compare_values(dec, st, b, n, rows, s, tol, t)
+            assert row_rel_err(after["h_prev"][b, :n], st.h_prev) <= tol, (t, b, "h_prev")
+            lg = host(dec.logits[b, :n])[rows]
+            assert row_rel_err(after["conf"][b, :n][rows], st.conf[rows]) <= tol, (t, b, "conf")
+            check_lm_rows_exact_inputs(lg, after["conf"][b, :n][rows], after["argmax"][b, :n][rows])
+            blk = t // sched.steps_per_block
+            lo = st.prompt_len + blk * sched.block_len
+            check_unmask_exact_inputs(before["masked"][b, :n], before["tokens"][b, :n], after["masked"][b, :n],
+                                      after["tokens"][b, :n], after["conf"][b, :n], after["argmax"][b, :n], lo,
+                                      min(lo + sched.block_len, n), sched.per_step)
 
 
 def test_per_layer_keep_all_equals_refresh_on_device():
