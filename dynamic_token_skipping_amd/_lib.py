@@ -27,7 +27,8 @@ DTYPES = {"f32": DL_F32, "bf16": DL_BF16}
 TORCH_DTYPES = {DL_F32: torch.float32, DL_BF16: torch.bfloat16}
 
 EXPORTS = ("dl_score_select", "dl_gather", "dl_scatter_cache", "dl_partial_attn", "dl_ffn_rows", "dl_lm_head_rows",
-           "dl_unmask", "dl_denoise_step", "dl_workspace_bytes", "dl_status_string", "dl_last_error",
+           "dl_unmask", "dl_denoise_step", "dl_denoise_step_noalloc", "dl_workspace_bytes", "dl_status_string",
+           "dl_last_error",
            "dl_abi_version", "dl_timing_enable", "dl_timing_reset", "dl_timing_read")
 DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD, DL_KC_GEMM_TILED, DL_KC_APPROX = 0, 1, 2, 3, 4
 
@@ -109,6 +110,7 @@ def load() -> ctypes.CDLL:
                               c_int32, c_int32, c_void_p]
     lib.dl_denoise_step.argtypes = [POINTER(Model), POINTER(State), POINTER(StepParams), c_void_p, c_size_t,
                                     c_void_p]
+    lib.dl_denoise_step_noalloc.argtypes = [POINTER(Model), POINTER(State), POINTER(StepParams), c_void_p]
     lib.dl_workspace_bytes.argtypes = [POINTER(Dims), c_int32]
     lib.dl_workspace_bytes.restype = c_size_t
     lib.dl_status_string.argtypes = [c_int32]
@@ -121,7 +123,8 @@ def load() -> ctypes.CDLL:
     lib.dl_timing_reset.argtypes = []
     lib.dl_timing_read.argtypes = [c_int32, POINTER(Timing)]
     for name in ("dl_score_select", "dl_gather", "dl_scatter_cache", "dl_partial_attn", "dl_ffn_rows",
-                 "dl_lm_head_rows", "dl_unmask", "dl_denoise_step", "dl_timing_enable", "dl_timing_reset",
+                 "dl_lm_head_rows", "dl_unmask", "dl_denoise_step", "dl_denoise_step_noalloc", "dl_timing_enable",
+                 "dl_timing_reset",
                  "dl_timing_read"):
         getattr(lib, name).restype = st
     _lib = lib
@@ -245,6 +248,16 @@ def dl_unmask(dims: Dims, tokens, masked, conf, argmax, prompt_len, seq_len, blo
 def dl_denoise_step(model: Model, state: State, params: StepParams, ws, stream=None):
     _check(load().dl_denoise_step(ctypes.byref(model), ctypes.byref(state), ctypes.byref(params), ptr(ws),
                                   ws.numel(), stream_handle(stream)))
+
+
+def dl_denoise_step_noalloc(model: Model, state: State, params: StepParams, stream=None):
+    """dl_denoise_step with the library's built-in scratch as its workspace
+    (nothing is allocated; see include/dl.h for the size limit)."""
+    _check(load().dl_denoise_step_noalloc(ctypes.byref(model), ctypes.byref(state), ctypes.byref(params),
+                                          stream_handle(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def dl_abi_version() -> int:

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "launch.h"
@@ -584,6 +585,41 @@ dl_status scored_kv_rows(const Ctx& c, const dl_layer_w* w, dl_score_tensor whic
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// the no-allocation step's workspace: a file-scope device array.  Each device
+// the library runs on holds its own copy until the process ends.  In host code
+// the array's name is only a stand-in; host code passes the device address
+// that hipGetSymbolAddress gives for the current device.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = DL_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+dl_status scratch_on_current_device(void** out) {
+  int dev = 0;
+  DL_CHECK_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DL_E_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    DL_CHECK_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(DL_E_HIP, "hipGetSymbolAddress gave no address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DL_OK;
+}
+}  // namespace
+
 // ===========================================================================
 // exported entry points
 // ===========================================================================
@@ -1045,6 +1081,19 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
   DL_CHECK_HIP(launch_unmask(s->tokens, s->masked, s->conf, s->argmax, s->prompt_len, s->seq_len, d.B, d.S, p->block,
                              p->block_len, p->n_unmask, st));
   return DL_OK;
+}
+
+dl_status dl_denoise_step_noalloc(const dl_model* model, dl_state* state, const dl_step_params* params,
+                                  void* stream) {
+  void* ws = nullptr;
+  DL_TRY(scratch_on_current_device(&ws));
+  const dl_status st = dl_denoise_step(model, state, params, ws, kScratchBytes, stream);
+  if (st == DL_E_WORKSPACE) {
+    char detail[sizeof g_err];
+    snprintf(detail, sizeof detail, "%s", g_err);
+    return fail(DL_E_WORKSPACE, "the no-allocation step's scratch holds %zu bytes (%s)", kScratchBytes, detail);
+  }
+  return st;
 }
 
 }  // extern "C"

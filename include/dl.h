@@ -276,6 +276,22 @@ dl_status dl_unmask(const dl_dims *dims, int32_t *tokens, uint8_t *masked, const
 dl_status dl_denoise_step(const dl_model *model, dl_state *state, const dl_step_params *params, void *ws,
                           size_t ws_bytes, void *stream);
 
+/* The same step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the workspace is a file-scope device array of DL_NOALLOC_SCRATCH_BYTES
+ * inside the library, which each device the library runs on holds until the
+ * process ends, instead of the caller's.  The call allocates nothing.
+ * Arguments and results are those of dl_denoise_step; the current device must
+ * be the device of `stream`.  A step whose workspace (dl_workspace_bytes of
+ * its valid rows) exceeds the array is rejected with DL_E_WORKSPACE before
+ * anything is enqueued (the 8B-class shapes need the workspace entry point).
+ * Every call on one device shares that device's array: calls that overlap on
+ * one device (other streams, other threads) race and must be serialised by
+ * the caller. */
+#define DL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dl_status dl_denoise_step_noalloc(const dl_model *model, dl_state *state, const dl_step_params *params,
+                                  void *stream);
+
 /* ---------------------------------------------------------------------------
  * Kernel timing (measurement support, not part of the method).  While a class
  * is enabled with sampling stride n >= 1, about one launch in n of that class
