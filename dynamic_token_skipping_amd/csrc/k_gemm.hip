@@ -250,12 +250,25 @@ __device__ __forceinline__ void tile_of_block(int bid, int splits, int& tile, in
   tile = (r / splits) * 8 + xcd;
 }
 
-// Tiled kernel: column tile nt runs on XCD nt % 8, and on that XCD the row
-// tiles (and splits) of one column tile get consecutive block ids, so they
-// run together and read the column tile's weights through one L2 instead of
-// one per XCD.
+// Tiled kernel: which (row tile, column tile, K split) block `bid` computes
+// (hardware deals block i to XCD i % 8).
+//  * Without a K split, column tile nt runs on XCD nt % 8, and the row tiles
+//    of one column tile get consecutive block ids there, so they run together
+//    and read that column tile's weights through one L2.
+//  * With a K split in 2, 4 or 8, XCD x takes split x % splits only, for every
+//    (8 / splits)-th column tile: each XCD's L2 then holds the rows of A of one
+//    K range, not all of them (with the splits of a column tile on one XCD,
+//    every XCD fetched the whole of A).
+__device__ __forceinline__ bool split_major(int splits) { return splits > 1 && 8 % splits == 0; }
+
 __device__ __forceinline__ void tile_of_block_mn(int bid, int n_mt, int splits, int& mt, int& nt, int& split) {
   const int xcd = bid & 7, r = bid >> 3;
+  if (split_major(splits)) {
+    split = xcd % splits;
+    mt = r % n_mt;
+    nt = (r / n_mt) * (8 / splits) + xcd / splits;
+    return;
+  }
   const int per_nt = n_mt * splits;
   const int q = r / per_nt, rem = r - q * per_nt;
   nt = q * 8 + xcd;
@@ -330,6 +343,7 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #ifndef DTSK_BIG_DEPTH192
 #define DTSK_BIG_DEPTH192 3
 #endif
+
 
 // K-step order of a tile.  Weight rows are K*2 bytes apart (a power of two in
 // the 8B-class shapes); if every tile walked K from the same start, all of
@@ -591,7 +605,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
     woff[i] = r < 0 ? kOob : (uint32_t)((r * K + ks0 * kBK + kc) * 2);   // empty columns read zeros
   }
   uint4 ra[DEPTH][CH], rw[DEPTH][CW];
-  const int rot = k_rotation(nt, nk);   // the row tiles of a column tile walk K together
+  // K order: with one row tile, each column tile starts at its own K step
+  // (its weight rows spread over the HBM channels); with several, every tile
+  // on an XCD starts at that XCD's step, so the tiles sharing its L2 walk the
+  // rows of A together instead of pulling all of A through it at once.
+  const int rot = k_rotation(n_mt > 1 ? (int)(blockIdx.x & 7) : nt, nk);
   auto issue = [&](int step, uint4 (&a)[CH], uint4 (&w)[CW]) {
     const bool in = step < nk;
     const int sr = step + rot >= nk ? step + rot - nk : step + rot;
@@ -783,7 +801,9 @@ hipError_t launch_tiled(const GemmPlan& plan, const void* A, int M_max, const in
     attr_set = true;
   }
   const int n_mt = cdiv(M_max, BM), n_nt = plan.tiles > 0 ? plan.tiles : N / BN;
-  const int grid = cdiv(n_nt, 8) * 8 * n_mt * plan.splits;
+  // one block per (row tile, column tile, split), in tile_of_block_mn's order
+  const bool by_split = plan.splits > 1 && 8 % plan.splits == 0;
+  const int grid = by_split ? cdiv(n_nt, 8 / plan.splits) * n_mt * 8 : cdiv(n_nt, 8) * 8 * n_mt * plan.splits;
   DTSK_LAUNCH((k_gemm_mfma<BN, BM, NW, DEPTH>), dim3(grid), dim3(NW * 64), lds_bytes, st, (const uint16_t*)A, M_max,
               n_rows, m_base, K, w, N, plan.splits, n_mt, n_nt, P, epi);
   return hipGetLastError();
