@@ -1,7 +1,9 @@
 """GPU parity of the attention sub-block on a ragged batch at sizes where the
 matrix-core kernel splits the keys of each sequence into chunks (and, at
-keep 1, where it does not): dl_partial_attn + dl_ffn_rows against the oracle
-layer on every selected row, and the K/V rows it must leave alone."""
+keep 1, where it does not), and with 32 heads, where enough (query tile,
+head) pairs take the single-pass kernel that covers every key of a pair in
+one workgroup: dl_partial_attn + dl_ffn_rows against the oracle layer on
+every selected row, and the K/V rows it must leave alone."""
 import numpy as np
 import pytest
 import torch
@@ -17,9 +19,16 @@ S = 640
 LENS = (640, 333, 77)     # full, ragged last chunk, shorter than one chunk
 
 
-@pytest.fixture(scope="module")
-def setup():
+# 32 heads: 448 + 333 + 77 rows make 15 query tiles, 480 (tile, head) pairs
+DIMS32 = workloads.ModelDims(d=4096, n_heads=32, head_dim=128, d_ffn=1024, vocab=256, n_layers=1)
+LENS32 = (448, 333, 77)
+
+
+@pytest.fixture(scope="module", params=["4_heads", "32_heads"])
+def setup(request):
     import dynamic_token_skipping_amd as D
+    DIMS, S, LENS = (globals()["DIMS"], globals()["S"], globals()["LENS"]) if request.param == "4_heads" else (
+        DIMS32, max(LENS32), LENS32)
     m = workloads.make_model(DIMS, 31, "bf16", "cuda")
     g = torch.Generator(device="cuda").manual_seed(32)
     B = len(LENS)
@@ -30,12 +39,14 @@ def setup():
     ws = D.workspace(dims, B * S)
     seq_len = torch.tensor(LENS, dtype=torch.int32, device="cuda")
     lw_np = {k: host(v) for k, v in m["layers"][0].items()}
-    return dict(D=D, m=m, kc0=kc0, vc0=vc0, x0=x0, dims=dims, ws=ws, seq_len=seq_len, lw_np=lw_np)
+    return dict(D=D, m=m, kc0=kc0, vc0=vc0, x0=x0, dims=dims, ws=ws, seq_len=seq_len, lw_np=lw_np, DIMS=DIMS, S=S,
+                LENS=LENS)
 
 
-@pytest.mark.parametrize("keep", [1.0, 0.5, 0.25, 0.05])
+@pytest.mark.parametrize("keep", [1.0, 0.75, 0.5, 0.25, 0.05])
 def test_ragged_partial_layer_matches_oracle(setup, keep):
     D = setup["D"]
+    DIMS, S, LENS = setup["DIMS"], setup["S"], setup["LENS"]
     B = len(LENS)
     sel = D.SelectionTensors(B, S)
     rows = []
