@@ -69,6 +69,19 @@ dl_status check_dims(const dl_dims* d) {
   if (!attention_supported(d->dtype, d->S, d->head_dim))
     return fail(DL_E_UNSUPPORTED, "attention for S=%d head_dim=%d not built", d->S, d->head_dim);
   if ((size_t)d->d * esize(d->dtype) % 16 != 0) return fail(DL_E_SHAPE, "d * element size must be a multiple of 16 bytes");
+  if (d->dtype == DL_BF16) {
+    // The bf16 products read one weight matrix (vocab, d_ffn or d rows of d
+    // columns, or d rows of d_ffn) through one buffer resource, and the
+    // attention kernels one sequence's keys or values (S rows of d, plus the
+    // tiles their prefetch runs past the end): 32-bit byte offsets.
+    const long long wmax = (long long)std::max(std::max(d->vocab, d->d_ffn), d->d) * d->d * 2;
+    const long long kv = ((long long)d->S + 512) * d->d * 2;
+    if (wmax > kMaxBufBytes)
+      return fail(DL_E_UNSUPPORTED, "a bf16 weight matrix of %lld bytes: one product reads at most 2 GiB - 1", wmax);
+    if (kv > kMaxBufBytes)
+      return fail(DL_E_UNSUPPORTED, "one sequence's keys (S=%d, d=%d) exceed what one attention read spans (2 GiB)",
+                  d->S, d->d);
+  }
   return DL_OK;
 }
 

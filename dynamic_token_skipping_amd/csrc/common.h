@@ -99,6 +99,25 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Raw buffer loads.  A resource covers `bytes` bytes from `base`; a 16-byte
+// load whose byte offset runs past them returns zeros without touching
+// memory (the range check of raw buffer addressing), so a masked load needs
+// no branch.  That matters for prefetch rings: a load under an exec branch
+// leaves the compiler unable to count the loads in flight, and it then waits
+// for all of them (vmcnt(0)) right after issuing the next tile's.  Offsets
+// and sizes are 32-bit: one resource spans less than 2 GiB.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufWord3 = 0x00020000;   // resource word 3 on CDNA: 32-bit data format, no swizzle
+constexpr long long kMaxBufBytes = 0x7fffffffLL;   // the largest range one resource here covers
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Row maps of a packed selection: for packed row r, the flat [B,S] row
 // b*S + i it came from, and its sequence b.  Built on the device.
 struct RowMap {

@@ -279,7 +279,6 @@ __device__ __forceinline__ void tile_of_block_mn(int bid, int n_mt, int splits, 
 // ---------------------------------------------------------------------------
 // skinny weight-streaming GEMM (M <= 16 * MI <= 128)
 // ---------------------------------------------------------------------------
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 GiB each)
 #ifndef DTSK_SKINNY_DEPTH
 #define DTSK_SKINNY_DEPTH 4
@@ -375,11 +374,6 @@ constexpr int kRowElems = 72;
 __device__ __forceinline__ int lds_idx(int r, int c) { return r * 72 + (c << 3); }
 #endif
 
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 // The K steps of a split are padded up to a multiple of kDepth; padding steps
 // and rows >= M read through out-of-range buffer offsets, which return zeros
 // without a memory access, so the pipeline below has no data-dependent
@@ -421,9 +415,9 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) wrow_index<BN>(W, ncol0 + nb * 16, seg, row0[nb]);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(W.p[seg]), (short)0,
-                                                                      W.seg_bytes, 0x00020000);
+                                                                      W.seg_bytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), (short)0,
-                                                                      M * K * 2, 0x00020000);
+                                                                      M * K * 2, kBufWord3);
   uint32_t woff[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) woff[nb] = (uint32_t)(((row0[nb] + l16) * K + ks0 * 64 + g * 8) * 2);
@@ -615,13 +609,13 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
     const int sr = step + rot >= nk ? step + rot - nk : step + rot;
     const int ks = in ? sr * (kBK * 2) : 0;
     const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase) + ks, (short)0,
-                                                                         in ? arec - ks : 0, 0x00020000);
+                                                                         in ? arec - ks : 0, kBufWord3);
 #pragma unroll
     for (int i = 0; i < CM; ++i) {
       if (i < CH) a[i] = buf_load16(ar, aoff[i]);
       if (i < CW) {
         const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char*>(wbase[i]) + ks, (short)0, in ? (int)W.seg_bytes - ks : 0, 0x00020000);
+            const_cast<char*>(wbase[i]) + ks, (short)0, in ? (int)W.seg_bytes - ks : 0, kBufWord3);
         w[i] = buf_load16(wr, woff[i]);
       }
     }
@@ -939,8 +933,11 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
   for (int i = 0; i < 4; ++i) w.p[i] = Wseg[i];
   w.mode = plan.wmode;
   w.n_seg = n_seg;
-  w.seg_bytes = (int)std::min<long long>((long long)(plan.wmode == 1 || plan.wmode == 3 ? N / 2 : n_seg) * K * 2,
-                                          0x7fffffffLL);
+  const long long seg_bytes = (long long)(plan.wmode == 1 || plan.wmode == 3 ? N / 2 : n_seg) * K * 2;
+  // the tiled and skinny kernels address a segment through one buffer
+  // resource with 32-bit offsets; larger segments are refused by the dims check
+  if (plan.kind != GEMM_SIMT && seg_bytes > kMaxBufBytes) return hipErrorInvalidValue;
+  w.seg_bytes = (int)std::min<long long>(seg_bytes, kMaxBufBytes);
   w.n_tiles = plan.tiles;
   if (plan.wmode == 3) w.n_seg = N / 2;
   if (M_max <= 0) return hipSuccess;

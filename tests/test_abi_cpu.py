@@ -55,6 +55,7 @@ def test_workspace_bytes(lib):
 @pytest.mark.parametrize("kw,code", [
     (dict(d=4000), -2), (dict(head_dim=127, d=32 * 127), -2), (dict(dtype=7), -3), (dict(B=0), -1),
     (dict(S=9000, dtype="f32"), -7), (dict(B=2000), -7),
+    (dict(vocab=262144), -7), (dict(S=261632), -7),
 ])
 def test_bad_dims_rejected(lib, kw, code):
     d = _dims(**kw)
@@ -62,6 +63,17 @@ def test_bad_dims_rejected(lib, kw, code):
     r = lib.dl_score_select(ctypes.byref(d), 16, 32, 16, 16, 0, 0.5, 0, 0.25, 0.0, ctypes.byref(s), None, 16, 1 << 30,
                             None)
     assert r == code, lib.dl_last_error()
+
+
+def test_buffer_range_limits():
+    """bf16: one weight matrix and one sequence's keys (plus 512 rows of
+    prefetch slack) must stay below 2 GiB, the span of one buffer read; the
+    largest accepted shapes sit one row below the limit."""
+    assert L.workspace_bytes(_dims(vocab=262143), 64) > 0         # 262143 * 4096 * 2 < 2^31
+    assert L.workspace_bytes(_dims(vocab=262144), 64) == 0        # = 2^31
+    assert L.workspace_bytes(_dims(S=261631), 64) > 0             # (S + 512) * 4096 * 2 < 2^31
+    assert L.workspace_bytes(_dims(S=261632), 64) == 0
+    assert L.workspace_bytes(_dims(vocab=262144, dtype="f32"), 64) > 0   # fp32 products index with 64 bits
 
 
 def test_null_and_alignment(lib):
