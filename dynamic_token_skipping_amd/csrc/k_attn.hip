@@ -10,6 +10,15 @@
 //    of every 32-key chunk (g = lane / 16): exactly the B operand of
 //    O^T = V^T P^T when the MFMA reduction index is ordered the same way on
 //    the V^T side.  Online softmax in fp32 (exp2 with the scale folded in).
+//    With key chunks over several workgroups, k_attn_combine merges them.
+//  * k_attn_rows (bf16, head_dim 128, up to kRowsMaxKeys keys): every key of
+//    a (query rows, head) in one workgroup, the key range split over the
+//    waves within each tile and the waves' softmax states merged in LDS, so
+//    nothing is merged afterwards.  64 queries per workgroup over 64-key
+//    tiles when the query tiles fill the chip; else 16 queries over 128-key
+//    tiles with 8 waves (the kept rows of one sequence).
+//  * K/V tiles come through buffer loads whose range ends at the sequence's
+//    last key (zeros past it, no branches), several tiles ahead in registers.
 //  * k_attn_simt: one workgroup per (query row, head); scores staged in LDS,
 //    max-subtracted softmax in fp32.  Used for fp32 storage and head sizes the
 //    matrix-core kernel does not cover.
@@ -158,16 +167,40 @@ constexpr int kTK = 64;           // keys per LDS tile
 constexpr int kKStride = kDh + 8; // LDS row stride of K (bf16 elements)
 constexpr int kVStride = kTK + 8; // LDS row stride of V^T (bf16 elements)
 
+// Two fp32 values to a bf16 pair, round to nearest even: one
+// v_cvt_pk_bf16_f32 (the same bits as from_f32<bf16_t> for every non-NaN
+// value; a NaN stays a NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)from_f32<bf16_t>(a).u | ((uint32_t)from_f32<bf16_t>(b).u << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
+// 2^x for the softmax: one v_exp_f32 (2^-inf = 0).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // V^T tile: row = dim (kVStride bf16), 32-bit word = a pair of keys.  Pair
 // kp of dim row `dim` lives in word slot kp ^ (((dim >> 3) & 7) << 2): the
 // stores of one instruction (4 key pairs x 16 dim chunks) then hit 32
 // distinct banks, and the readers' 8-byte pair loads stay contiguous because
 // the XOR leaves bit 0 of the slot alone.
-__device__ __forceinline__ int vt_word(int dim, int kp) { return dim * (kVStride / 2) + (kp ^ (((dim >> 3) & 7) << 2)); }
+template <int TK>   // keys per tile: a V^T row holds TK + 8 bf16
+__device__ __forceinline__ int vt_word_t(int dim, int kp) { return dim * ((TK + 8) / 2) + (kp ^ (((dim >> 3) & 7) << 2)); }
+__device__ __forceinline__ int vt_word(int dim, int kp) { return vt_word_t<kTK>(dim, kp); }
+// The V^T words of two keys' rows a (key 2kp) and b (key 2kp + 1), each
+// holding dims 2e, 2e + 1: low halves (dim 2e) and high halves (dim 2e + 1),
+// key 2kp in the low half of the word.  One v_perm_b32 each.
+__device__ __forceinline__ uint32_t vt_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t vt_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// Unit (head, or (head, key chunk) pair) of the pq-th block group on XCD
+// `xcd`, or -1 past the last: unit pq * 8 + xcd, so that units x, x + 8, ...
+// run on XCD x and the query tiles of one unit share that XCD's L2.
+// (Consecutive units per XCD, which put a head's 256-byte K/V row slices in
+// other L2 channels, measured the same.)
+__device__ __forceinline__ int unit_on_xcd(int pq, int xcd, int n_units) {
+  const int u = pq * 8 + xcd;
+  return u < n_units ? u : -1;
+}
 
 // One workgroup = (64-query tile, head, key chunk [kbeg, kbeg + chunk)).
 // With one chunk the normalised output goes straight to `out` (or in fp32 to
@@ -197,14 +230,14 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   // the same keys and values do so through one L2.
   const int xcd = blockIdx.x & 7, rb = blockIdx.x >> 3;
   const int pq = rb / n_tiles, tile = rb - pq * n_tiles;
-  const int pair = pq * 8 + xcd;
-  if (pair >= n_heads * n_split) return;
+  const int pair = unit_on_xcd(pq, xcd, n_heads * n_split);
+  if (pair < 0) return;
   const int h = pair % n_heads, split = pair / n_heads;
-  const int nrows = tile_rows[tile];
+  const int nrows = __builtin_amdgcn_readfirstlane(tile_rows[tile]);
   if (nrows <= 0) return;
-  const int r0 = tile_row0[tile];
-  const int b = row_seq[r0];
-  const int n = kApprox ? a.key_cnt[b] : seq_len[b];
+  const int r0 = __builtin_amdgcn_readfirstlane(tile_row0[tile]);
+  const int b = __builtin_amdgcn_readfirstlane(row_seq[r0]);   // uniform: the resources below stay scalar
+  const int n = __builtin_amdgcn_readfirstlane(kApprox ? a.key_cnt[b] : seq_len[b]);
   const int kbeg = split * chunk;
   if (!kApprox && kbeg >= n) return;               // the combine only reads chunks below n
   const int kend = min(n, kbeg + chunk);
@@ -236,27 +269,42 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const uint16_t* Kb = kApprox ? static_cast<const uint16_t*>(a.k) + (size_t)a.key_off[b] * d + col0
-                               : Kc + (size_t)b * S * d + col0;
-  const uint16_t* Vb = kApprox ? static_cast<const uint16_t*>(a.dv) + (size_t)a.key_off[b] * d + col0
-                               : Vc + (size_t)b * S * d + col0;
-  // per thread and tile: 4 K chunks (key c >> 4, dims (c & 15) * 8) and 2 x 2 V
-  // chunks (keys 2kp, 2kp + 1 of key pair kp = c >> 4, dims (c & 15) * 8)
+  const int koff_b = kApprox ? __builtin_amdgcn_readfirstlane(a.key_off[b]) : 0;
+  const uint16_t* Kb = kApprox ? static_cast<const uint16_t*>(a.k) + (size_t)koff_b * d : Kc + (size_t)b * S * d;
+  const uint16_t* Vb = kApprox ? static_cast<const uint16_t*>(a.dv) + (size_t)koff_b * d : Vc + (size_t)b * S * d;
+  // K and V rows of the sequence through buffer resources ending at key kend
+  // (the chunk's end): keys past it read as zeros with no branch, so the next
+  // tile's loads stay in flight during this tile's math.  Per thread and
+  // tile: 4 K chunks (key c >> 4, dims (c & 15) * 8 of head h) and 2 x 2 V
+  // chunks (keys 2kp, 2kp + 1 of key pair kp = c >> 4).
+  // The per-lane offsets within a tile are fixed; each tile moves the
+  // resources' base (scalar arithmetic only) and shrinks their range to the
+  // keys left before kend.
+  const uint32_t row_bytes = (uint32_t)d * 2;
+  const uint32_t coff = (uint32_t)(col0 + (t & 15) * 8) * 2;
+  uint32_t kofs[4], vofs[2], vofs1[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kofs[i] = (uint32_t)((t >> 4) + i * 16) * row_bytes + coff;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    vofs[i] = (uint32_t)((t >> 4) * 2 + i * 32) * row_bytes + coff;
+    vofs1[i] = vofs[i] + row_bytes;
+  }
   uint4 kr[4], va[2], vb[2];
   auto fetch = [&](int k0) {
+    // keys left as a signed max (a scalar instruction; an unsigned "a < b ?
+    // b - a : 0" becomes a vector-only saturating subtract, and a resource
+    // in vector registers costs a waterfall loop around every load)
+    const uint32_t tb = (uint32_t)k0 * row_bytes;
+    const uint32_t rec = (uint32_t)max(kend - k0, 0) * row_bytes;
+    const __amdgpu_buffer_rsrc_t k_rs = buf_rsrc(reinterpret_cast<const char*>(Kb) + tb, rec);
+    const __amdgpu_buffer_rsrc_t v_rs = buf_rsrc(reinterpret_cast<const char*>(Vb) + tb, rec);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = t + i * 256;
-      const int key = k0 + (c >> 4), dc = (c & 15) * 8;
-      kr[i] = key < kend ? *reinterpret_cast<const uint4*>(Kb + (size_t)key * d + dc) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i) kr[i] = buf_load16(k_rs, kofs[i]);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int c = t + i * 256;
-      const int key = k0 + (c >> 4) * 2, dc = (c & 15) * 8;
-      va[i] = key < kend ? *reinterpret_cast<const uint4*>(Vb + (size_t)key * d + dc) : make_uint4(0, 0, 0, 0);
-      vb[i] = key + 1 < kend ? *reinterpret_cast<const uint4*>(Vb + (size_t)(key + 1) * d + dc)
-                             : make_uint4(0, 0, 0, 0);
+      va[i] = buf_load16(v_rs, vofs[i]);
+      vb[i] = buf_load16(v_rs, vofs1[i]);
     }
   };
   fetch(kbeg);
@@ -274,11 +322,11 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
       const uint32_t aw[4] = {va[i].x, va[i].y, va[i].z, va[i].w}, bw[4] = {vb[i].x, vb[i].y, vb[i].z, vb[i].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        Vt[vt_word(dc + 2 * e, kp)] = (aw[e] & 0xffffu) | (bw[e] << 16);          // dim dc+2e:   keys 2kp, 2kp+1
-        Vt[vt_word(dc + 2 * e + 1, kp)] = (aw[e] >> 16) | (bw[e] & 0xffff0000u);  // dim dc+2e+1
+        Vt[vt_word(dc + 2 * e, kp)] = vt_lo(aw[e], bw[e]);       // dim dc+2e:   keys 2kp, 2kp+1
+        Vt[vt_word(dc + 2 * e + 1, kp)] = vt_hi(aw[e], bw[e]);   // dim dc+2e+1
       }
     }
-    if (k0 + kTK < kend) fetch(k0 + kTK);          // next tile in flight during this one's math
+    fetch(k0 + kTK);                               // next tile in flight during this one's math (past kend: zeros)
     lds_barrier();
 
     // S^T blocks: keys kb*16 + g*4 + i (i < 4), query ql
@@ -299,7 +347,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + kb * 16 + g * 4 + i;
-          st[kb][i] = key < kend ? exp2f(st[kb][i] * scale_log2 - lse2) : 0.f;
+          st[kb][i] = key < kend ? exp2_fast(st[kb][i] * scale_log2 - lse2) : 0.f;
         }
     } else {
     // online softmax for query ql over this tile
@@ -317,14 +365,14 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m_run, tmax);
-    const float corr = exp2f(m_run - m_new);
+    const float corr = exp2_fast(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(st[kb][i] - m_new);
+        const float p = exp2_fast(st[kb][i] - m_new);
         st[kb][i] = p;
         psum += p;
       }
@@ -400,52 +448,71 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   if (g == 0) ml_part[((size_t)split * R_part + r) * n_heads + h] = make_float2(m_run, l_run);
 }
 
-// Attention over every key without key chunks: one workgroup = (64-query
-// tile, head), 8 waves.  Wave w serves the 16 queries of group w % 4 and the
-// half h = w / 4 of every key tile (keys 32h .. 32h + 31 of each 64-key
-// tile); the tile's K and V^T are staged once in LDS for all 8 waves, and the
-// next kAhead tiles are in flight in registers meanwhile.  At the end the two
-// halves' softmax states (m, l, O) of each query are merged through LDS:
-// O = (2^(m0 - M) O0 + 2^(m1 - M) O1) / (2^(m0 - M) l0 + 2^(m1 - M) l1).
+// Attention over every key without key chunks: one workgroup = (16 G queries
+// of a 64-row query tile, head), G x H waves.  Wave w serves the 16 queries
+// of group w % G and part p = w / G of every 64-key tile (keys p * 64 / H to
+// (p + 1) * 64 / H - 1 of each tile); the tile's K and V^T are staged once in
+// LDS for all waves, and the next A tiles are in flight in registers
+// meanwhile.  At the end the H parts' softmax states (m, l, O) of each query
+// are merged through LDS: O = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p.
 // No partial results leave the workgroup.  Same S^T = K Q^T / O^T += V^T P^T
-// fragments as k_attn_mfma.
-constexpr int kRowsThreads = 512;
-constexpr int kRowsAhead = 2;       // key tiles in flight beyond the one in LDS
+// fragments as k_attn_mfma; with 16 keys per wave (H = 4) the P^T operand of
+// a lane is exactly the four probabilities its S^T block left it (keys
+// 4g .. 4g + 3 of query ql), fed to the 16x16x16 MFMA.
+// G = 4, H = 2: 64 queries per workgroup, for many query rows.  G = 1, H = 4:
+// four workgroups per query tile, for few query rows (the kept rows of one
+// sequence), where it replaces the key chunks and their merge kernel.
 constexpr int kRowsMaxKeys = 1024;  // longer sequences take the key-chunk kernel (batched: 1280 keys, 3% slower)
-constexpr int kRowsMinBlocks = 256; // fewer (query tile, head) pairs take the key-chunk kernel
+constexpr int kRowsMinBlocks = 256; // (query tile, head) pairs from which 64-query workgroups fill the chip
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(kRowsThreads) void k_attn_rows(const uint16_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ Kc,
-                                                            const uint16_t* __restrict__ Vc,
-                                                            const int32_t* __restrict__ seq_len,
-                                                            const int32_t* __restrict__ row_seq,
-                                                            const int32_t* __restrict__ tile_row0,
-                                                            const int32_t* __restrict__ tile_rows, int S, int d,
-                                                            int n_heads, float scale_log2, int n_tiles,
-                                                            uint16_t* __restrict__ out) {
-  // one LDS block: the K tile and the V^T tile, later the second halves' O^T
-  constexpr int kKsBytes = kTK * kKStride * 2, kVtBytes = kDh * kVStride * 2;
-  constexpr int kMergeBytes = 4 * 8 * 16 * 16 * 4;   // [grp][blk][g*4 + i][ql] floats
-  static_assert(kMergeBytes <= kKsBytes + kVtBytes, "merge buffer");
+template <int G, int H, int A, int TK>   // A: key tiles in flight beyond the one in LDS; TK keys per tile
+__global__ __launch_bounds__(G * H * 64) void k_attn_rows(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ Kc,
+                                                          const uint16_t* __restrict__ Vc,
+                                                          const int32_t* __restrict__ seq_len,
+                                                          const int32_t* __restrict__ row_seq,
+                                                          const int32_t* __restrict__ tile_row0,
+                                                          const int32_t* __restrict__ tile_rows, int S, int d,
+                                                          int n_heads, float scale_log2, int n_tiles,
+                                                          uint16_t* __restrict__ out) {
+  constexpr int NT = G * H * 64;               // threads
+  constexpr int KW = TK / H;                   // keys of a tile per wave
+  constexpr int NSB = KW / 16;                 // S^T blocks per wave and tile
+  constexpr int SUB = kTQ / (16 * G);          // workgroups per 64-row query tile
+  constexpr int KC = TK * 16 / NT;             // 16-byte K chunks per thread and tile
+  constexpr int VC = TK * 8 / NT;              // V key-pair chunks per thread and tile
+  static_assert((NSB == 1 || NSB == 2) && SUB >= 1 && KC >= 1 && VC >= 1, "workgroup shape");
+  // one LDS block: the K tile and the V^T tile, later the other parts' O^T
+  constexpr int kKsBytes = TK * kKStride * 2, kVtBytes = kDh * (TK + 8) * 2;
+  // Merge through LDS: when every part's O^T fits (kAllMerge), all waves
+  // write theirs and each then merges 8 / H of the 8 dim blocks; otherwise
+  // parts 1 .. H-1 write and part 0 merges all blocks.
+  constexpr bool kAllMerge = H * G * 8 * 16 * 16 * 4 <= kKsBytes + kVtBytes;
+  constexpr int kMergeParts = kAllMerge ? H : H - 1;   // parts whose state goes through LDS
+  static_assert(kMergeParts * G * 8 * 16 * 16 * 4 <= kKsBytes + kVtBytes, "merge buffer");
+  static_assert(!kAllMerge || 8 % H == 0, "dim blocks per wave");
   __shared__ __align__(16) char smem[kKsBytes + kVtBytes];
-  __shared__ float merge_ml[4][16][2];     // (m, l) of the second half's queries
+  __shared__ float merge_ml[kMergeParts * G][16][2];   // (m, l) of the parts' queries
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
   uint32_t* Vt = reinterpret_cast<uint32_t*>(smem + kKsBytes);
-  // Block order: head p runs on XCD p % 8 and its query tiles get consecutive
-  // block ids there, so the tiles reading the same keys share one L2.
+  // Block order: head p runs on XCD p % 8 and its query tiles (and their
+  // sub-tiles) get consecutive block ids there, so the workgroups reading the
+  // same keys share one L2.
   const int xcd = blockIdx.x & 7, rb = blockIdx.x >> 3;
-  const int pq = rb / n_tiles, tile = rb - pq * n_tiles;
-  const int h = pq * 8 + xcd;
-  if (h >= n_heads) return;
-  const int nrows = tile_rows[tile];
-  if (nrows <= 0) return;
-  const int r0 = tile_row0[tile];
-  const int b = row_seq[r0];
-  const int n = seq_len[b];
+  const int pq = rb / (n_tiles * SUB), rem = rb - pq * (n_tiles * SUB);
+  const int tile = rem / SUB, sub = rem - tile * SUB;
+  const int h = unit_on_xcd(pq, xcd, n_heads);
+  if (h < 0) return;
+  const int nrows = __builtin_amdgcn_readfirstlane(tile_rows[tile]);
+  if (nrows <= sub * 16 * G) return;               // also an unused tile (0 rows)
+  const int r0 = __builtin_amdgcn_readfirstlane(tile_row0[tile]);
+  const int b = __builtin_amdgcn_readfirstlane(row_seq[r0]);   // uniform: the resources below stay scalar
+  const int n = __builtin_amdgcn_readfirstlane(seq_len[b]);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int grp = wave & 3, half = wave >> 2;
+  const int grp = wave % G, part = wave / G;
   const int ql = lane & 15, g = lane >> 4;
-  const int qrow = grp * 16 + ql;
+  const int qrow = sub * 16 * G + grp * 16 + ql;   // query row within the 64-row tile
   const bool qvalid = qrow < nrows;
   const size_t col0 = (size_t)h * kDh;
 
@@ -461,58 +528,84 @@ __global__ __launch_bounds__(kRowsThreads) void k_attn_rows(const uint16_t* __re
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const uint16_t* Kb = Kc + (size_t)b * S * d + col0;
-  const uint16_t* Vb = Vc + (size_t)b * S * d + col0;
-  // per thread and tile: 2 K chunks (key c >> 4, dims (c & 15) * 8) and the
-  // two keys of one V key pair (kp = t >> 4, dims (t & 15) * 8)
-  uint4 kr[kRowsAhead + 1][2], va[kRowsAhead + 1], vb[kRowsAhead + 1];
+  // K and V rows of this sequence through buffer resources ending at key n:
+  // keys >= n (the last tile's tail, the tiles fetched past the end) read as
+  // zeros with no branch, so the loads of every ring slot stay countable and
+  // in flight together.  Per thread and tile: KC K chunks (chunk c = t + i NT:
+  // key c >> 4, dims (c & 15) * 8 of head h) and VC V key pairs (the two keys
+  // of pair c >> 4, same dims).
+  // The per-lane offsets within a tile are fixed; each tile moves the
+  // resources' base (scalar arithmetic only) and shrinks their range to the
+  // keys left before n.
+  const uint32_t row_bytes = (uint32_t)d * 2;
+  const char* kseq = reinterpret_cast<const char*>(Kc + (size_t)b * S * d);
+  const char* vseq = reinterpret_cast<const char*>(Vc + (size_t)b * S * d);
+  const uint32_t coff = (uint32_t)(col0 + (t & 15) * 8) * 2;
+  uint32_t kofs[KC], vofs[VC], vofs1[VC];
+#pragma unroll
+  for (int i = 0; i < KC; ++i) kofs[i] = (uint32_t)((t >> 4) + i * (NT >> 4)) * row_bytes + coff;
+#pragma unroll
+  for (int i = 0; i < VC; ++i) {
+    vofs[i] = (uint32_t)((t >> 4) * 2 + i * (NT >> 3)) * row_bytes + coff;
+    vofs1[i] = vofs[i] + row_bytes;
+  }
+  uint4 kr[A + 1][KC], va[A + 1][VC], vb[A + 1][VC];
   auto fetch = [&](int k0, int slot) {
+    const uint32_t tb = (uint32_t)k0 * row_bytes;
+    const uint32_t rec = (uint32_t)max(n - k0, 0) * row_bytes;   // scalar (see k_attn_mfma)
+    const __amdgpu_buffer_rsrc_t k_rs = buf_rsrc(kseq + tb, rec);
+    const __amdgpu_buffer_rsrc_t v_rs = buf_rsrc(vseq + tb, rec);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = t + i * kRowsThreads;
-      const int key = k0 + (c >> 4), dc = (c & 15) * 8;
-      kr[slot][i] = key < n ? *reinterpret_cast<const uint4*>(Kb + (size_t)key * d + dc) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < KC; ++i) kr[slot][i] = buf_load16(k_rs, kofs[i]);
+#pragma unroll
+    for (int i = 0; i < VC; ++i) {
+      va[slot][i] = buf_load16(v_rs, vofs[i]);
+      vb[slot][i] = buf_load16(v_rs, vofs1[i]);
     }
-    const int key = k0 + (t >> 4) * 2, dc = (t & 15) * 8;
-    va[slot] = key < n ? *reinterpret_cast<const uint4*>(Vb + (size_t)key * d + dc) : make_uint4(0, 0, 0, 0);
-    vb[slot] = key + 1 < n ? *reinterpret_cast<const uint4*>(Vb + (size_t)(key + 1) * d + dc)
-                           : make_uint4(0, 0, 0, 0);
   };
-  const int n_kt = (n + kTK - 1) / kTK;
-  constexpr int kRing = kRowsAhead + 1;
+  const int n_kt = (n + TK - 1) / TK;
+  constexpr int kRing = A + 1;
 #pragma unroll
-  for (int a = 0; a < kRowsAhead; ++a)
-    if (a < n_kt) fetch(a * kTK, a);
-  // unrolled by the ring length so that every ring slot is a fixed register set
+  for (int a = 0; a < A; ++a) {
+    fetch(a * TK, a);
+    __builtin_amdgcn_sched_barrier(0);   // slot by slot, the order the ring's waits count in
+  }
+  // Unrolled by the ring length so that every ring slot is a fixed register
+  // set.  The ring runs over whole ring lengths of tiles: every pass issues
+  // and consumes its loads on every path (the tiles past n_kt read zeros), so
+  // the count of loads in flight is the same at every join and the waits stay
+  // partial; only the math of a tile past the end is skipped.
   for (int kt0 = 0; kt0 < n_kt; kt0 += kRing) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
     const int kt = kt0 + u;
-    if (kt >= n_kt) break;                         // uniform over the workgroup
-    const int k0 = kt * kTK;
-    if (kt + kRowsAhead < n_kt) fetch((kt + kRowsAhead) * kTK, (u + kRowsAhead) % kRing);
+    const int k0 = kt * TK;
+    fetch((kt + A) * TK, (u + A) % kRing);   // past the end: zeros, no memory access
     lds_barrier();  // previous tile fully consumed
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = t + i * kRowsThreads;
+    for (int i = 0; i < KC; ++i) {
+      const int c = t + i * NT;
       *reinterpret_cast<uint4*>(Ks + (c >> 4) * kKStride + (c & 15) * 8) = kr[u][i];
     }
-    {
-      const int kp = t >> 4, dc = (t & 15) * 8;
-      const uint32_t aw[4] = {va[u].x, va[u].y, va[u].z, va[u].w};
-      const uint32_t bw[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
+#pragma unroll
+    for (int i = 0; i < VC; ++i) {
+      const int c = t + i * NT;
+      const int kp = c >> 4, dc = (c & 15) * 8;
+      const uint32_t aw[4] = {va[u][i].x, va[u][i].y, va[u][i].z, va[u][i].w};
+      const uint32_t bw[4] = {vb[u][i].x, vb[u][i].y, vb[u][i].z, vb[u][i].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        Vt[vt_word(dc + 2 * e, kp)] = (aw[e] & 0xffffu) | (bw[e] << 16);
-        Vt[vt_word(dc + 2 * e + 1, kp)] = (aw[e] >> 16) | (bw[e] & 0xffff0000u);
+        Vt[vt_word_t<TK>(dc + 2 * e, kp)] = vt_lo(aw[e], bw[e]);
+        Vt[vt_word_t<TK>(dc + 2 * e + 1, kp)] = vt_hi(aw[e], bw[e]);
       }
     }
     lds_barrier();
-    // this wave's 32 keys of the tile: S^T blocks kb = 2 half + j, keys kb*16 + g*4 + i
-    f32x4 st[2];
+    if (kt >= n_kt) continue;                      // uniform over the workgroup
+    // this wave's keys of the tile: S^T blocks kb = NSB part + j, keys kb*16 + g*4 + i
+    f32x4 st[NSB];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int kb = 2 * half + j;
+    for (int j = 0; j < NSB; ++j) {
+      const int kb = NSB * part + j;
       st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -522,79 +615,168 @@ __global__ __launch_bounds__(kRowsThreads) void k_attn_rows(const uint16_t* __re
     }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NSB; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = k0 + (2 * half + j) * 16 + g * 4 + i;
-        float v = st[j][i] * scale_log2;
-        if (key >= n) v = -INFINITY;
-        st[j][i] = v;
-        tmax = fmaxf(tmax, v);
+        st[j][i] *= scale_log2;
+        tmax = fmaxf(tmax, st[j][i]);
       }
+    if (k0 + TK > n) {                            // the tile that crosses n (uniform): mask the keys past it
+      tmax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < NSB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (k0 + (NSB * part + j) * 16 + g * 4 + i >= n) st[j][i] = -INFINITY;
+          tmax = fmaxf(tmax, st[j][i]);
+        }
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    // a half whose keys are all past n has seen no key yet: keep it empty
-    const float corr = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+    // Lazy rescale: the reference max m_run of a query moves only when a tile
+    // brings a score more than 8 above it, so p = 2^(s - m_run) <= 2^8 (exact
+    // range in fp32 and bf16) and O, l stay relative to m_run; the normalised
+    // output O / l is the same for any reference.  A wave rescales only when
+    // one of its queries moved.  A part that has seen no key keeps m_run =
+    // -inf and p = 0.
+    const bool grow = tmax > m_run + 8.f;
+    const float m_new = grow ? tmax : m_run;
+    if (__builtin_amdgcn_ballot_w64(grow)) {      // uniform over the wave
+      const float corr = grow ? exp2_fast(m_run - m_new) : 1.f;
+      l_run *= corr;
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) o[blk] *= corr;
+    }
+    m_run = m_new;
     float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NSB; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = m_new == -INFINITY ? 0.f : exp2f(st[j][i] - m_new);
+        const float p = m_new == -INFINITY ? 0.f : exp2_fast(st[j][i] - m_new);
         st[j][i] = p;
         psum += p;
       }
-    m_run = m_new;
-    l_run = l_run * corr + psum;
+    l_run += psum;
+    if constexpr (NSB == 2) {
+      // O^T += V^T P^T over this wave's 32 keys: key pairs 16 part + 2g, +1 (block 0) and 16 part + 8 + 2g, +1
+      uint4 pw;
+      pw.x = pack_bf16x2(st[0][0], st[0][1]);
+      pw.y = pack_bf16x2(st[0][2], st[0][3]);
+      pw.z = pack_bf16x2(st[1][0], st[1][1]);
+      pw.w = pack_bf16x2(st[1][2], st[1][3]);
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
-    for (int blk = 0; blk < 8; ++blk) o[blk] *= corr;
-    // O^T += V^T P^T over this wave's 32 keys (key-pair chunk `half` of the tile)
-    uint4 pw;
-    pw.x = pack_bf16x2(st[0][0], st[0][1]);
-    pw.y = pack_bf16x2(st[0][2], st[0][3]);
-    pw.z = pack_bf16x2(st[1][0], st[1][1]);
-    pw.w = pack_bf16x2(st[1][2], st[1][3]);
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+      for (int blk = 0; blk < 8; ++blk) {
+        const int dim = blk * 16 + ql;
+        const uint2 lo = *reinterpret_cast<const uint2*>(&Vt[vt_word_t<TK>(dim, part * 16 + g * 2)]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&Vt[vt_word_t<TK>(dim, part * 16 + 8 + g * 2)]);
+        const uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[blk], 0, 0, 0);
+      }
+    } else {
+      // O^T += V^T P^T over this wave's 16 keys: lane (g, ql) holds keys 4g .. 4g + 3 (key pairs 8 part + 2g, +1)
+      uint2 pw;
+      pw.x = pack_bf16x2(st[0][0], st[0][1]);
+      pw.y = pack_bf16x2(st[0][2], st[0][3]);
+      const s16x4 pf = __builtin_bit_cast(s16x4, pw);
 #pragma unroll
-    for (int blk = 0; blk < 8; ++blk) {
-      const int dim = blk * 16 + ql;
-      const uint2 lo = *reinterpret_cast<const uint2*>(&Vt[vt_word(dim, half * 16 + g * 2)]);
-      const uint2 hi = *reinterpret_cast<const uint2*>(&Vt[vt_word(dim, half * 16 + 8 + g * 2)]);
-      const uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[blk], 0, 0, 0);
+      for (int blk = 0; blk < 8; ++blk) {
+        const int dim = blk * 16 + ql;
+        const uint2 vv = *reinterpret_cast<const uint2*>(&Vt[vt_word_t<TK>(dim, part * 8 + g * 2)]);
+        o[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pf, o[blk], 0, 0, 0);
+      }
     }
   }
   }
   // row sums over the 4 lanes sharing a query
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  // merge the halves: the second half's waves hand (m, l, O) to the first's
   lds_barrier();                                  // the last tile's V^T reads are done: reuse the K/V space
-  float* mo = reinterpret_cast<float*>(smem);     // O^T of the second halves: [grp][blk][g*4 + i][ql]
-  if (half == 1) {
+  if constexpr (kAllMerge) {
+    // every part hands (m, l, O) over; part p then merges dim blocks p * 8 / H .. of its group's queries
+    float* mo = reinterpret_cast<float*>(smem);   // [part][grp][blk][g*4 + i][ql]
+    const int slot = part * G + grp;
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mo[((grp * 8 + blk) * 16 + g * 4 + i) * 16 + ql] = o[blk][i];
+      for (int i = 0; i < 4; ++i) mo[((slot * 8 + blk) * 16 + g * 4 + i) * 16 + ql] = o[blk][i];
     if (g == 0) {
-      merge_ml[grp][ql][0] = m_run;
-      merge_ml[grp][ql][1] = l_run;
+      merge_ml[slot][ql][0] = m_run;
+      merge_ml[slot][ql][1] = l_run;
+    }
+    lds_barrier();
+    if (!qvalid) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < H; ++p) M = fmaxf(M, merge_ml[p * G + grp][ql][0]);
+    float w[H], den = 0.f;
+#pragma unroll
+    for (int p = 0; p < H; ++p) {
+      const float mp = merge_ml[p * G + grp][ql][0];
+      w[p] = mp == -INFINITY ? 0.f : exp2f(mp - M);
+      den += w[p] * merge_ml[p * G + grp][ql][1];
+    }
+    const float inv = 1.f / den;
+    uint16_t* orow = out + (size_t)(r0 + qrow) * d + col0;
+    constexpr int BPW = 8 / H;
+#pragma unroll
+    for (int bb = 0; bb < BPW; ++bb) {
+      const int blk = part * BPW + bb;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float acc = 0.f;
+#pragma unroll
+        for (int p = 0; p < H; ++p) acc += w[p] * mo[(((p * G + grp) * 8 + blk) * 16 + g * 4 + i) * 16 + ql];
+        v[i] = acc * inv;
+      }
+      uint2 wv;
+      wv.x = pack_bf16x2(v[0], v[1]);
+      wv.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(orow + blk * 16 + g * 4) = wv;
+    }
+    return;
+  }
+  // parts 1 .. H-1 hand (m, l, O) to part 0's wave of the same group
+  float* mo = reinterpret_cast<float*>(smem);     // O^T of parts 1 ..: [part-1][grp][blk][g*4 + i][ql]
+  if (part > 0) {
+    const int slot = (part - 1) * G + grp;
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mo[((slot * 8 + blk) * 16 + g * 4 + i) * 16 + ql] = o[blk][i];
+    if (g == 0) {
+      merge_ml[slot][ql][0] = m_run;
+      merge_ml[slot][ql][1] = l_run;
     }
   }
   lds_barrier();
-  if (half == 1 || !qvalid) return;
-  const float m1 = merge_ml[grp][ql][0], l1 = merge_ml[grp][ql][1];
-  const float M = fmaxf(m_run, m1);
-  const float w0 = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
-  const float w1 = m1 == -INFINITY ? 0.f : exp2f(m1 - M);
-  const float inv = 1.f / (w0 * l_run + w1 * l1);
+  if (part > 0 || !qvalid) return;
+  float M = m_run;
+#pragma unroll
+  for (int p = 1; p < H; ++p) M = fmaxf(M, merge_ml[(p - 1) * G + grp][ql][0]);
+  float w[H];
+  w[0] = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
+  float den = w[0] * l_run;
+#pragma unroll
+  for (int p = 1; p < H; ++p) {
+    const float mp = merge_ml[(p - 1) * G + grp][ql][0];
+    w[p] = mp == -INFINITY ? 0.f : exp2f(mp - M);
+    den += w[p] * merge_ml[(p - 1) * G + grp][ql][1];
+  }
+  const float inv = 1.f / den;
   uint16_t* orow = out + (size_t)(r0 + qrow) * d + col0;
 #pragma unroll
   for (int blk = 0; blk < 8; ++blk) {
     float v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (w0 * o[blk][i] + w1 * mo[((grp * 8 + blk) * 16 + g * 4 + i) * 16 + ql]) * inv;
+    for (int i = 0; i < 4; ++i) {
+      float s = w[0] * o[blk][i];
+#pragma unroll
+      for (int p = 1; p < H; ++p) s += w[p] * mo[((((p - 1) * G + grp) * 8 + blk) * 16 + g * 4 + i) * 16 + ql];
+      v[i] = s * inv;
+    }
     uint2 wv;
     wv.x = pack_bf16x2(v[0], v[1]);
     wv.y = pack_bf16x2(v[2], v[3]);
@@ -669,6 +851,18 @@ bool attention_supported(dl_dtype dt, int S, int head_dim) {
 #ifndef DTSK_ATTN_ROWS
 #define DTSK_ATTN_ROWS 1
 #endif
+#ifndef DTSK_ATTN_Q16
+#define DTSK_ATTN_Q16 1
+#endif
+#ifndef DTSK_ROWS_AHEAD
+#define DTSK_ROWS_AHEAD 2
+#endif
+#ifndef DTSK_Q16_PARTS
+#define DTSK_Q16_PARTS 8
+#endif
+#ifndef DTSK_Q16_AHEAD
+#define DTSK_Q16_AHEAD 3
+#endif
 #ifndef DTSK_ATTN_SPLIT_CAP
 #define DTSK_ATTN_SPLIT_CAP kAttnMaxSplits
 #endif
@@ -694,18 +888,26 @@ hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, con
     if (splits < 1 || splits > kAttnMaxSplits || (splits > 1 && (!o_part || !ml_part || rm.R_max > R_part)))
       return hipErrorInvalidValue;
     const float scale_log2 = scale * 1.4426950408889634f;
-    // Every key of a (query tile, head) in one workgroup, with nothing to
-    // merge afterwards, when the query tiles alone give the chip enough
-    // workgroups; with fewer (the kept rows of one sequence: 2 tiles x 32
-    // heads) key chunks over more workgroups plus the merge finish sooner
-    // (measured 17.6 against 21.5 us at 128 rows, 31.7 against 22.3 us at 512).
+    // Every key of a (query rows, head) in one workgroup, with nothing to
+    // merge afterwards: 64 queries per workgroup when the query tiles alone
+    // give the chip enough workgroups, else 16 (the kept rows of one
+    // sequence: 2 tiles x 32 heads x 4); key chunks plus a merge kernel only
+    // past kRowsMaxKeys keys or for a context output.
     const long long query_tiles = ((long long)rm.R_max + kTQ - 1) / kTQ;
-    if (DTSK_ATTN_ROWS && !ctx_out && S <= kRowsMaxKeys && query_tiles * n_heads >= kRowsMinBlocks) {
+    if (DTSK_ATTN_ROWS && !ctx_out && S <= kRowsMaxKeys) {
       const int grid = (n_heads + 7) / 8 * 8 * rm.T_max;
-      DTSK_LAUNCH(k_attn_rows, dim3(grid), dim3(kRowsThreads), 0, st, (const uint16_t*)q, (const uint16_t*)k_cache,
-                  (const uint16_t*)v_cache, seq_len, rm.row_seq, rm.tile_row0, rm.tile_rows, S, d, n_heads,
-                  scale_log2, rm.T_max, (uint16_t*)out);
-      return hipGetLastError();
+      if (query_tiles * n_heads >= kRowsMinBlocks) {
+        DTSK_LAUNCH((k_attn_rows<4, 2, DTSK_ROWS_AHEAD, 64>), dim3(grid), dim3(512), 0, st, (const uint16_t*)q, (const uint16_t*)k_cache,
+                    (const uint16_t*)v_cache, seq_len, rm.row_seq, rm.tile_row0, rm.tile_rows, S, d, n_heads,
+                    scale_log2, rm.T_max, (uint16_t*)out);
+        return hipGetLastError();
+      }
+      if (DTSK_ATTN_Q16) {
+        DTSK_LAUNCH((k_attn_rows<1, DTSK_Q16_PARTS, DTSK_Q16_AHEAD, DTSK_Q16_PARTS * 16>), dim3(grid * (kTQ / 16)), dim3(DTSK_Q16_PARTS * 64), 0, st, (const uint16_t*)q,
+                    (const uint16_t*)k_cache, (const uint16_t*)v_cache, seq_len, rm.row_seq, rm.tile_row0,
+                    rm.tile_rows, S, d, n_heads, scale_log2, rm.T_max, (uint16_t*)out);
+        return hipGetLastError();
+      }
     }
     const int chunk = (S + splits * kTK - 1) / (splits * kTK) * kTK;
     const int grid = (n_heads * splits + 7) / 8 * 8 * rm.T_max;
