@@ -250,8 +250,9 @@ def time_step_kinds(torch, dec, sched, n_steps: int):
 def time_layer_steps(torch, model, n_steps: int = 30, warmup: int = 3):
     """One layer step of the 8B-class layer per keep ratio, on the layer8b
     inputs (cached and current hidden states, K/V caches, confidences):
-    score + top-k over the 512 rows, gather of the kept fp32 rows, the partial
-    attention sub-block and the FFN on them.  Consecutive steps take layers 4,
+    score + top-k over the 512 rows (the selection's row map built with
+    row_off, for the row entry points to reuse), gather of the kept fp32 rows,
+    the partial attention sub-block and the FFN on them.  Consecutive steps take layers 4,
     5 and 6 of the loaded model in turn (1.2 GB of distinct weights), so the
     weights stream from HBM.  Algorithmic bytes: the layer's weights, its K/V
     cache and the two score inputs read once, and the kept fp32 rows read and
@@ -270,7 +271,7 @@ def time_layer_steps(torch, model, n_steps: int = 30, warmup: int = 3):
     kc, vc = st["k"].clone(), st["v"].clone()
     layers = [model["layers"][i] for i in (4, 5, 6)]
     params = dims.layer_params()
-    sel = SelectionTensors(1, S)
+    sel = SelectionTensors(1, S, row_map=True)
     x_rows = torch.empty((S, d), dtype=torch.float32, device="cuda")
     out = {"sample": f"{n_steps} layer steps per keep after {warmup} warm-up steps, one event pair around them"}
     for keep in (1.0, 0.5, 0.25, 0.125):

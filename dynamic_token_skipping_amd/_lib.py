@@ -29,7 +29,7 @@ TORCH_DTYPES = {DL_F32: torch.float32, DL_BF16: torch.bfloat16}
 EXPORTS = ("dl_score_select", "dl_gather", "dl_scatter_cache", "dl_partial_attn", "dl_ffn_rows", "dl_lm_head_rows",
            "dl_unmask", "dl_denoise_step", "dl_denoise_step_noalloc", "dl_workspace_bytes", "dl_status_string",
            "dl_last_error",
-           "dl_abi_version", "dl_timing_enable", "dl_timing_reset", "dl_timing_read")
+           "dl_abi_version", "dl_row_map_ints", "dl_timing_enable", "dl_timing_reset", "dl_timing_read")
 DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD, DL_KC_GEMM_TILED, DL_KC_APPROX = 0, 1, 2, 3, 4
 
 
@@ -40,7 +40,7 @@ class Dims(Structure):
 
 
 class Selection(Structure):
-    _fields_ = [("sel_idx", c_void_p), ("sel_count", c_void_p), ("row_off", c_void_p)]
+    _fields_ = [("sel_idx", c_void_p), ("sel_count", c_void_p), ("row_off", c_void_p), ("row_map", c_void_p)]
 
 
 class LayerW(Structure):
@@ -119,6 +119,8 @@ def load() -> ctypes.CDLL:
     lib.dl_last_error.restype = c_char_p
     lib.dl_abi_version.argtypes = []
     lib.dl_abi_version.restype = c_int32
+    lib.dl_row_map_ints.argtypes = [c_int32, c_int32]
+    lib.dl_row_map_ints.restype = ctypes.c_int64
     lib.dl_timing_enable.argtypes = [c_int32, c_int32]
     lib.dl_timing_reset.argtypes = []
     lib.dl_timing_read.argtypes = [c_int32, POINTER(Timing)]
@@ -156,15 +158,20 @@ def make_dims(B, S, d, n_heads, head_dim, d_ffn, vocab, n_layers, dtype, rms_eps
 
 
 class SelectionTensors:
-    """Device arrays of a selection: sel_idx [B,S], sel_count [B], row_off [B+1] (int32)."""
+    """Device arrays of a selection: sel_idx [B,S], sel_count [B], row_off [B+1]
+    (int32) and, with ``row_map=True``, the row map that dl_score_select fills
+    for the row entry points (leave it off for selections a decode step writes)."""
 
-    def __init__(self, B: int, S: int, device="cuda"):
+    def __init__(self, B: int, S: int, device="cuda", row_map: bool = False):
         self.sel_idx = torch.zeros((B, S), dtype=torch.int32, device=device)
         self.sel_count = torch.zeros((B,), dtype=torch.int32, device=device)
         self.row_off = torch.zeros((B + 1,), dtype=torch.int32, device=device)
+        self.row_map = (torch.zeros((int(load().dl_row_map_ints(B, S)),), dtype=torch.int32, device=device)
+                        if row_map else None)
 
     def struct(self) -> Selection:
-        return Selection(ptr(self.sel_idx), ptr(self.sel_count), ptr(self.row_off))
+        return Selection(ptr(self.sel_idx), ptr(self.sel_count), ptr(self.row_off),
+                         ptr(self.row_map) if self.row_map is not None else None)
 
     def rows(self):
         """Host list of selected positions per sequence (synchronises)."""
@@ -262,6 +269,10 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 
 def dl_abi_version() -> int:
     return int(load().dl_abi_version())
+
+
+def dl_row_map_ints(B: int, S: int) -> int:
+    return int(load().dl_row_map_ints(int(B), int(S)))
 
 
 def dl_timing_enable(kc: int, stride: int = 1):

@@ -90,6 +90,7 @@ dl_status check_sel(const dl_selection* s, const char* what) {
   DL_TRY(check_ptr(s->sel_idx, "sel_idx"));
   DL_TRY(check_ptr(s->sel_count, "sel_count"));
   DL_TRY(check_ptr(s->row_off, "row_off"));
+  if (((uintptr_t)s->row_map) & 3) return fail(DL_E_ALIGN, "%s.row_map is not 4-byte aligned", what);
   return DL_OK;
 }
 
@@ -209,6 +210,25 @@ Layout make_layout(const dl_dims& d, int R) {
 template <typename P>
 P* at(void* ws, size_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+// A selection's own row map (dl_selection.row_map): n_rows, then row_pos and
+// row_seq for B*S rows, then tile_row0 and tile_rows for the tile capacity.
+int64_t row_map_tiles(int B, int S) { return cdiv((long long)B * S, kTileRows) + B; }
+
+RowMap rowmap_of_sel(const dl_selection* sel, int B, int S, int R_max) {
+  const int64_t bs = (int64_t)B * S, tc = row_map_tiles(B, S);
+  RowMap r;
+  r.n_rows = sel->row_map;
+  r.row_pos = sel->row_map + 1;
+  r.row_seq = sel->row_map + 1 + bs;
+  r.tile_row0 = sel->row_map + 1 + 2 * bs;
+  r.tile_rows = sel->row_map + 1 + 2 * bs + tc;
+  r.R_max = R_max;
+  // tiles fill in order, so the first cdiv(R_max, kTileRows) + B hold every row of R_max
+  r.T_max = (int)std::min<int64_t>(tc, cdiv(R_max, kTileRows) + B);
+  r.tq = kTileRows;
+  return r;
 }
 
 RowMap rowmap_at(void* ws, const RowMapMem& m, int R_max, int T_max) {
@@ -640,6 +660,11 @@ extern "C" {
 
 int32_t dl_abi_version(void) { return DL_ABI_VERSION; }
 
+int64_t dl_row_map_ints(int32_t B, int32_t S) {
+  if (B < 1 || S < 1) return 0;
+  return 1 + 2 * (int64_t)B * S + 2 * row_map_tiles(B, S);
+}
+
 dl_status dl_timing_enable(dl_kernel_class kc, int32_t stride) {
   if (kc < 0 || kc >= DL_KC_COUNT) return fail(DL_E_ARG, "kernel class %d unknown", (int)kc);
   if (stride < 0) return fail(DL_E_ARG, "sampling stride %d < 0", (int)stride);
@@ -732,7 +757,12 @@ dl_status dl_score_select(const dl_dims* dims, const void* h_cur, const void* h_
                             dims->S, dims->d, kind, alpha, scores, st));
   DL_CHECK_HIP(launch_select(scores, seq_len, dims->B, dims->S, mode, keep_ratio, threshold, out->sel_idx,
                              out->sel_count, st));
-  DL_CHECK_HIP(launch_row_off(out->sel_count, out->row_off, dims->B, st));
+  if (out->row_map) {
+    const RowMap rm = rowmap_of_sel(out, dims->B, dims->S, dims->B * dims->S);
+    DL_CHECK_HIP(launch_row_off_map(out->sel_idx, out->sel_count, out->row_off, dims->B, dims->S, rm, st));
+  } else {
+    DL_CHECK_HIP(launch_row_off(out->sel_count, out->row_off, dims->B, st));
+  }
   return DL_OK;
 }
 
@@ -771,6 +801,10 @@ static dl_status prep_rows(const dl_dims* dims, const dl_selection* sel, int32_t
   if (k_total_max < 0 || k_total_max > dims->B * dims->S) return fail(DL_E_SHAPE, "k_total_max outside [0, B*S]");
   *L = make_layout(*dims, k_total_max);
   if (ws_bytes < L->total) return fail(DL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L->total);
+  if (sel->row_map) {   // written by dl_score_select with row_off
+    *rm = rowmap_of_sel(sel, dims->B, dims->S, k_total_max);
+    return DL_OK;
+  }
   *rm = rowmap_at(ws, L->map_sel, k_total_max, std::min(L->T, cdiv(k_total_max, kTileRows) + dims->B));
   DL_CHECK_HIP(launch_rowmap(sel->sel_idx, sel->sel_count, sel->row_off, dims->B, dims->S, *rm, st));
   return DL_OK;

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DL_ABI_VERSION 2
+#define DL_ABI_VERSION 3
 
 typedef enum {
   DL_OK = 0,
@@ -103,6 +103,15 @@ typedef struct {
   int32_t *sel_idx;   /* [B, S] device: ascending positions, first sel_count[b] valid */
   int32_t *sel_count; /* [B] device */
   int32_t *row_off;   /* [B + 1] device: exclusive prefix sum of sel_count */
+  int32_t *row_map;   /* optional device array of dl_row_map_ints(B, S) int32: the packed
+                         rows' map (each row's flat position and sequence, the attention
+                         query tiles).  dl_score_select writes it with row_off in the same
+                         launch; dl_partial_attn, dl_ffn_rows and dl_lm_head_rows then read
+                         it instead of building one in their workspace.  It describes the
+                         selection as dl_score_select last wrote it: a selection written by
+                         other means (dl_denoise_step neither reads nor writes row_map)
+                         leaves it stale, so pass NULL there.  NULL: each call builds its
+                         own. */
 } dl_selection;
 
 /* One layer's weights (device, storage dtype).  Norm gains are [d]; wq, wk,
@@ -336,6 +345,10 @@ size_t dl_workspace_bytes(const dl_dims *dims, int32_t max_rows);
 const char *dl_status_string(dl_status s);
 const char *dl_last_error(void);
 int32_t dl_abi_version(void);
+
+/* Size, in int32 elements, of a selection's row map (dl_selection.row_map)
+ * for B sequences of row capacity S; 0 when B or S is below 1. */
+int64_t dl_row_map_ints(int32_t B, int32_t S);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.dl_abi_version() == 2
+    assert lib.dl_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -63,6 +63,25 @@ def test_bad_dims_rejected(lib, kw, code):
     r = lib.dl_score_select(ctypes.byref(d), 16, 32, 16, 16, 0, 0.5, 0, 0.25, 0.0, ctypes.byref(s), None, 16, 1 << 30,
                             None)
     assert r == code, lib.dl_last_error()
+
+
+def test_row_map_size(lib):
+    """A selection's row map: n_rows, row_pos and row_seq for B*S rows, and two
+    arrays over the attention tile capacity (B*S / 64 rounded up, plus one per
+    sequence); 0 for an empty shape."""
+    assert lib.dl_row_map_ints(1, 512) == 1 + 2 * 512 + 2 * (8 + 1)
+    assert lib.dl_row_map_ints(16, 1280) == 1 + 2 * 16 * 1280 + 2 * (320 + 16)
+    assert lib.dl_row_map_ints(3, 65) == 1 + 2 * 195 + 2 * (4 + 3)
+    assert lib.dl_row_map_ints(0, 512) == 0 and lib.dl_row_map_ints(2, 0) == 0
+    assert ctypes.sizeof(L.Selection) == 4 * ctypes.sizeof(ctypes.c_void_p)
+
+
+def test_misaligned_row_map_rejected(lib):
+    d = _dims()
+    s = L.Selection(16, 16, 16, 18)
+    r = lib.dl_score_select(ctypes.byref(d), 16, 32, 16, 16, 0, 0.5, 0, 0.25, 0.0, ctypes.byref(s), None, 16, 1 << 30,
+                            None)
+    assert r == -4 and b"row_map" in lib.dl_last_error()
 
 
 def test_buffer_range_limits():

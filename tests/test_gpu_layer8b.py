@@ -218,3 +218,54 @@ def test_timing_counts_products_and_keeps_results(lay):
     want = gemm(k, 3 * d, d) + gemm(k, d, d) + gemm(k, 2 * F, d) + gemm(k, d, F)
     assert t["bytes"] == pytest.approx(want, rel=1e-12)
     assert t["flops"] == pytest.approx(2.0 * k * d * (3 * d + d + 2 * F) + 2.0 * k * F * d, rel=1e-12)
+
+
+@pytest.mark.parametrize("keep", [1.0, 0.25, 0.04])
+def test_row_map_reuse_is_bit_identical(lay, keep):
+    """A selection carrying its own row map (filled by dl_score_select with
+    row_off in one launch) gives the row entry points exactly the results of
+    one without (each call building its map in the workspace); the map holds
+    each packed row's flat position and sequence, -1 / 0 past the last row,
+    and the 64-row attention tiles in order."""
+    D = lay["D"]
+    S, d, V = lay["S"], lay["wl"].dims.d, lay["wl"].dims.vocab
+    st = lay["st"]
+    sels = [D.SelectionTensors(1, S), D.SelectionTensors(1, S, row_map=True)]
+    for sel in sels:
+        D.dl_score_select(lay["dims"], st["h_cur"], st["h_prev"], st["conf"], lay["seq_len"], "esdllm", 0.5,
+                          D.DL_SEL_TOPK, keep, 0.0, sel, ws=lay["ws"])
+    torch.cuda.synchronize()
+    a, b = sels
+    assert torch.equal(a.sel_idx, b.sel_idx) and torch.equal(a.sel_count, b.sel_count)
+    assert torch.equal(a.row_off, b.row_off)
+    k = int(a.sel_count[0])
+    assert k == E.keep_count(keep, S)
+    m = b.row_map.cpu().numpy()
+    T = (S + 63) // 64 + 1
+    assert len(m) == 1 + 2 * S + 2 * T and m[0] == k
+    assert np.array_equal(m[1:1 + k], a.sel_idx[0, :k].cpu().numpy()) and (m[1 + k:1 + S] == -1).all()
+    assert (m[1 + S:1 + 2 * S] == 0).all()
+    n_t = (k + 63) // 64
+    t0, tr = m[1 + 2 * S:1 + 2 * S + T], m[1 + 2 * S + T:]
+    assert np.array_equal(t0[:n_t], np.arange(n_t) * 64) and tr[:n_t].sum() == k and (tr[n_t:] == 0).all()
+    rows = a.sel_idx[0, :k].long()
+    lw = lay["m"]["layers"][0]
+    outs = []
+    for sel in sels:
+        x = st["h_cur"][0:S].float()[rows].contiguous()
+        kc = st["k"].clone().reshape(1, S, d)
+        vc = st["v"].clone().reshape(1, S, d)
+        D.dl_partial_attn(lay["dims"], lw, x, sel, lay["seq_len"], k, kc, vc, lay["ws"])
+        D.dl_ffn_rows(lay["dims"], lw, x, sel, k, lay["ws"])
+        conf = torch.full((1, S), -1.0, device="cuda")
+        amax = torch.full((1, S), -1, dtype=torch.int32, device="cuda")
+        hfin = torch.zeros((1, S, d), dtype=torch.bfloat16, device="cuda")
+        logits = torch.zeros((1, S, V), dtype=torch.float32, device="cuda")
+        D.dl_lm_head_rows(lay["dims"], lay["m"]["final_norm"], lay["m"]["lm_head"], x, sel, k, conf, amax, hfin,
+                          logits, lay["ws"])
+        torch.cuda.synchronize()
+        outs.append((x, kc, vc, conf, amax, hfin, logits))
+    for u, v in zip(*outs):
+        assert torch.equal(u, v)
+    del outs
+    torch.cuda.empty_cache()
