@@ -289,14 +289,17 @@ def time_layer_steps(torch, model, n_steps: int = 30, warmup: int = 3):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
+        h0 = time.perf_counter()
         for i in range(n_steps):
             one(i)
+        host_us = (time.perf_counter() - h0) * 1e6 / n_steps   # enqueue time: below us, the GPU never waits
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / n_steps
         alg = 2 * params + 2 * (2 * S * d * 2) + k * d * 8
         flops = 2 * params * k + 4 * k * S * d
-        out[f"keep_{keep}"] = {"rows": k, "us": round(us, 2), "alg_MB": round(alg / 1e6, 1),
+        out[f"keep_{keep}"] = {"rows": k, "us": round(us, 2), "host_enqueue_us": round(host_us, 1),
+                               "alg_MB": round(alg / 1e6, 1),
                                "GB/s": round(alg / us / 1e3, 1), "frac_hbm": round(alg / us / 1e3 / PEAK_HBM_GBS, 4),
                                "TFLOP/s": round(flops / us / 1e6, 1),
                                "frac_mfma": round(flops / us / 1e6 / PEAK_BF16_TFLOPS, 4)}

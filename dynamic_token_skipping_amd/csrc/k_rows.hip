@@ -240,11 +240,32 @@ __global__ __launch_bounds__(256) void k_score(const T* __restrict__ h_cur, cons
   }
 }
 
-// bf16 storage, fused update, d a multiple of 512: one wave per row, each lane
-// owns 8 consecutive columns per 512-column slice.  The slices are taken four
-// at a time: every load of a group is issued before any of the group's H_prev
-// stores, so a row costs about two memory round trips instead of one per
-// column.  Same sums as k_score in a different summation order.
+// score_row for one workgroup per row: row blockIdx.x of the map, or
+// position blockIdx.x of sequence blockIdx.y.
+__device__ __forceinline__ bool score_row_wg(const int32_t* __restrict__ rm_pos, const int32_t* __restrict__ rm_n,
+                                             const int32_t* __restrict__ off_all,
+                                             const int32_t* __restrict__ seq_len, int S, size_t* row,
+                                             size_t* xrow) {
+  const int w = blockIdx.x;
+  if (rm_pos) {
+    if (w >= *rm_n) return false;
+    *row = (size_t)rm_pos[w];
+    *xrow = (size_t)w;
+    return true;
+  }
+  const int b = blockIdx.y;
+  if (w >= seq_len[b]) return false;
+  *row = (size_t)b * S + w;
+  *xrow = off_all ? (size_t)(off_all[b] + w) : 0;
+  return true;
+}
+
+// bf16 storage, fused update, d a multiple of 512: one 256-thread workgroup
+// per row (a 512-row step fills 512 workgroups, two per CU), thread t owning
+// 8 consecutive columns of every 2048-column slice.  The slices are taken
+// four at a time: every load of a group is issued before any of the group's
+// H_prev stores.  Each thread's sums, then the four waves' sums added in wave
+// order through LDS.  Same sums as k_score in a different summation order.
 __global__ __launch_bounds__(256) void k_score_bf16x8(const float* __restrict__ x_packed,
                                                       const int32_t* __restrict__ off_all,
                                                       const int32_t* __restrict__ rm_pos,
@@ -253,20 +274,21 @@ __global__ __launch_bounds__(256) void k_score_bf16x8(const float* __restrict__ 
                                                       const int32_t* __restrict__ seq_len, int S, int d, int kind,
                                                       float alpha, float* __restrict__ scores) {
   constexpr int G = 4;                                // slices per load group
-  const int lane = threadIdx.x & 63;
+  __shared__ float red[4][5];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   size_t row, xrow;
-  if (!score_row(rm_pos, rm_n, off_all, seq_len, S, &row, &xrow)) return;
+  if (!score_row_wg(rm_pos, rm_n, off_all, seq_len, S, &row, &xrow)) return;   // uniform over the workgroup
   uint16_t* hp = reinterpret_cast<uint16_t*>(h_prev) + row * d;
   const float* xr = x_packed + xrow * d;
   float l1 = 0.f, dd = 0.f, hh = 0.f, xx = 0.f, xh = 0.f;
-  const int n_slices = d / 512;
+  const int n_slices = (d + 2047) / 2048;
   for (int s0 = 0; s0 < n_slices; s0 += G) {
     float4 xa[G], xb[G];
     uint4 hv[G];
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
-      if (s0 + gi < n_slices) {
-        const int c = (s0 + gi) * 512 + lane * 8;
+      const int c = (s0 + gi) * 2048 + t * 8;
+      if (s0 + gi < n_slices && c < d) {
         xa[gi] = *reinterpret_cast<const float4*>(xr + c);
         xb[gi] = *reinterpret_cast<const float4*>(xr + c + 4);
         hv[gi] = *reinterpret_cast<const uint4*>(hp + c);
@@ -274,7 +296,8 @@ __global__ __launch_bounds__(256) void k_score_bf16x8(const float* __restrict__ 
     }
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
-      if (s0 + gi < n_slices) {
+      const int c = (s0 + gi) * 2048 + t * 8;
+      if (s0 + gi < n_slices && c < d) {
         const float xs[8] = {xa[gi].x, xa[gi].y, xa[gi].z, xa[gi].w, xb[gi].x, xb[gi].y, xb[gi].z, xb[gi].w};
         const uint32_t hw[4] = {hv[gi].x, hv[gi].y, hv[gi].z, hv[gi].w};
         uint32_t ow[4];
@@ -294,7 +317,7 @@ __global__ __launch_bounds__(256) void k_score_bf16x8(const float* __restrict__ 
           }
           ow[e] = (uint32_t)x0.u | ((uint32_t)x1.u << 16);
         }
-        *reinterpret_cast<uint4*>(hp + (s0 + gi) * 512 + lane * 8) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+        *reinterpret_cast<uint4*>(hp + c) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
       }
     }
   }
@@ -304,6 +327,22 @@ __global__ __launch_bounds__(256) void k_score_bf16x8(const float* __restrict__ 
   xx = warp_sum(xx);
   xh = warp_sum(xh);
   if (lane == 0) {
+    red[w][0] = l1;
+    red[w][1] = dd;
+    red[w][2] = hh;
+    red[w][3] = xx;
+    red[w][4] = xh;
+  }
+  __syncthreads();
+  if (t == 0) {
+    l1 = dd = hh = xx = xh = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      l1 += red[i][0];
+      dd += red[i][1];
+      hh += red[i][2];
+      xx += red[i][3];
+      xh += red[i][4];
+    }
     const float c = conf[row];
     float s;
     if (kind == DL_SCORE_ESDLLM) {
@@ -1210,9 +1249,9 @@ hipError_t launch_score(dl_dtype dt, const void* h_cur, const float* x_packed, c
       DTSK_LAUNCH((k_score<float, false>), grid, dim3(256), 0, st, (const float*)h_cur, x_packed, off_all, rp,
                          rn, (float*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
   } else {
-    if (x_packed && d % 512 == 0)
-      DTSK_LAUNCH(k_score_bf16x8, grid, dim3(256), 0, st, x_packed, off_all, rp, rn, (bf16_t*)h_prev, conf,
-                         seq_len, S, d, (int)kind, alpha, scores);
+    if (x_packed && d % 512 == 0)   // one workgroup per row
+      DTSK_LAUNCH(k_score_bf16x8, rm ? dim3(rm->R_max) : dim3(S, B), dim3(256), 0, st, x_packed, off_all, rp, rn,
+                  (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
     else if (x_packed)
       DTSK_LAUNCH((k_score<bf16_t, true>), grid, dim3(256), 0, st, (const bf16_t*)h_cur, x_packed, off_all, rp,
                          rn, (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);

@@ -76,3 +76,61 @@ def test_ragged_partial_layer_matches_oracle(setup, keep):
         other = np.setdiff1d(np.arange(S), rows[b])
         assert torch.equal(kc[b][other], setup["kc0"][b][other])
         assert torch.equal(vc[b][other], setup["vc0"][b][other])
+
+
+@pytest.mark.parametrize("keep", [1.0, 0.25, 0.05])
+def test_ragged_row_map_reuse_is_bit_identical(setup, keep):
+    """A ragged batch selected by dl_score_select with and without the
+    selection's own row map: the map holds b * S + position and b for every
+    packed row (-1 / 0 past the last), and each sequence's rows in 64-row
+    attention tiles in order; dl_partial_attn and dl_ffn_rows give
+    bit-identical rows and caches either way."""
+    D = setup["D"]
+    DIMS, S, LENS = setup["DIMS"], setup["S"], setup["LENS"]
+    B = len(LENS)
+    g = torch.Generator(device="cuda").manual_seed(41)
+    h_prev = torch.randn((B, S, DIMS.d), generator=g, device="cuda").to(torch.bfloat16)
+    h_cur = (h_prev.float() + 0.3 * torch.randn((B, S, DIMS.d), generator=g, device="cuda")).to(torch.bfloat16)
+    conf = torch.rand((B, S), generator=g, device="cuda")
+    sels = [D.SelectionTensors(B, S), D.SelectionTensors(B, S, row_map=True)]
+    for sel in sels:
+        D.dl_score_select(setup["dims"], h_cur, h_prev, conf, setup["seq_len"], "esdllm", 0.5, D.DL_SEL_TOPK, keep,
+                          0.0, sel, ws=setup["ws"])
+    torch.cuda.synchronize()
+    a, b_ = sels
+    assert torch.equal(a.sel_idx, b_.sel_idx) and torch.equal(a.sel_count, b_.sel_count)
+    assert torch.equal(a.row_off, b_.row_off)
+    cnt = a.sel_count.cpu().tolist()
+    assert cnt == [E.keep_count(keep, n) for n in LENS]
+    off = a.row_off.cpu().tolist()
+    R = off[-1]
+    m = b_.row_map.cpu().numpy()
+    BS = B * S
+    T = (BS + 63) // 64 + B
+    assert len(m) == 1 + 2 * BS + 2 * T and m[0] == R
+    idx = a.sel_idx.cpu().numpy()
+    want_pos = np.concatenate([bb * S + idx[bb, :c] for bb, c in enumerate(cnt)])
+    want_seq = np.concatenate([np.full(c, bb) for bb, c in enumerate(cnt)])
+    assert np.array_equal(m[1:1 + R], want_pos) and (m[1 + R:1 + BS] == -1).all()
+    assert np.array_equal(m[1 + BS:1 + BS + R], want_seq) and (m[1 + BS + R:1 + 2 * BS] == 0).all()
+    t0, tr = m[1 + 2 * BS:1 + 2 * BS + T], m[1 + 2 * BS + T:]
+    want_t0, want_tr = [], []
+    for bb, c in enumerate(cnt):
+        for j in range(0, c, 64):
+            want_t0.append(off[bb] + j)
+            want_tr.append(min(64, c - j))
+    nt = len(want_t0)
+    assert np.array_equal(t0[:nt], want_t0) and np.array_equal(tr[:nt], want_tr) and (tr[nt:] == 0).all()
+    lw = setup["m"]["layers"][0]
+    outs = []
+    for sel in sels:
+        rows = [idx[bb, :c] for bb, c in enumerate(cnt)]
+        x = torch.cat([setup["x0"][bb, torch.as_tensor(rows[bb], device="cuda", dtype=torch.long)]
+                       for bb in range(B)]).contiguous()
+        kc, vc = setup["kc0"].clone(), setup["vc0"].clone()
+        D.dl_partial_attn(setup["dims"], lw, x, sel, setup["seq_len"], R, kc, vc, setup["ws"])
+        D.dl_ffn_rows(setup["dims"], lw, x, sel, R, setup["ws"])
+        torch.cuda.synchronize()
+        outs.append((x, kc, vc))
+    for u, v in zip(*outs):
+        assert torch.equal(u, v)
