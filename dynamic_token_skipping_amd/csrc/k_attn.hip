@@ -462,7 +462,10 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 // G = 4, H = 2: 64 queries per workgroup, for many query rows.  G = 1, H = 4:
 // four workgroups per query tile, for few query rows (the kept rows of one
 // sequence), where it replaces the key chunks and their merge kernel.
-constexpr int kRowsMaxKeys = 1024;  // longer sequences take the key-chunk kernel (batched: 1280 keys, 3% slower)
+#ifndef DTSK_ROWS_MAX_KEYS
+#define DTSK_ROWS_MAX_KEYS 1024
+#endif
+constexpr int kRowsMaxKeys = DTSK_ROWS_MAX_KEYS;  // longer sequences take the key-chunk kernel
 constexpr int kRowsMinBlocks = 256; // (query tile, head) pairs from which 64-query workgroups fill the chip
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
