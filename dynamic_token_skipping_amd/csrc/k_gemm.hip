@@ -329,6 +329,9 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #ifndef DTSK_SMALL_NW128
 #define DTSK_SMALL_NW128 DTSK_SMALL_NW
 #endif
+#ifndef DTSK_GU96
+#define DTSK_GU96 1
+#endif
 #ifndef DTSK_SMALL_DEPTH
 #define DTSK_SMALL_DEPTH 4
 #endif
@@ -552,9 +555,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
   constexpr int WM = BM / (NW / 2), WN = BN / 2, MI = WM / 16, NI = WN / 16;
   constexpr int IR = NT / 8;                   // tile rows per load item (8 threads per 128-byte row)
   constexpr int CH = BM / IR;                  // 16-byte A items per thread per step
-  constexpr int CW = BN / IR;                  // 16-byte W items per thread per step
+  constexpr int CW = (BN + IR - 1) / IR;       // 16-byte W items per thread per step (the last may be partial)
   constexpr int CM = CH > CW ? CH : CW;
-  static_assert(BM % IR == 0 && BN % IR == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
+  static_assert(BM % IR == 0 && BN % 8 == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
   extern __shared__ __align__(16) uint16_t lds[];
   uint16_t* As = lds;                          // [2][BM][kLds]
   uint16_t* Ws = lds + 2 * BM * kLds;          // [2][BN][kLds]
@@ -596,7 +599,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
     wrow_index<BN>(W, n0 + row, sg, r);
     sg = __builtin_amdgcn_readfirstlane(sg);
     wbase[i] = static_cast<const char*>(W.p[sg]);
-    woff[i] = r < 0 ? kOob : (uint32_t)((r * K + ks0 * kBK + kc) * 2);   // empty columns read zeros
+    // empty columns, and rows past BN of a partial last item (whole waves),
+    // read zeros without a memory access
+    woff[i] = r < 0 || row >= BN ? kOob : (uint32_t)((r * K + ks0 * kBK + kc) * 2);
   }
   uint4 ra[DEPTH][CH], rw[DEPTH][CW];
   // K order: with one row tile, each column tile starts at its own K step
@@ -625,7 +630,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
     for (int i = 0; i < CM; ++i) {
       const int row = (t >> 3) + IR * i, kc = (t & 7) * 8;
       if (i < CH) *reinterpret_cast<uint4*>(As + buf * BM * kLds + lds_idx(row, kc >> 3)) = a[i];
-      if (i < CW) *reinterpret_cast<uint4*>(Ws + buf * BN * kLds + lds_idx(row, kc >> 3)) = w[i];
+      if (i < CW && row < BN) *reinterpret_cast<uint4*>(Ws + buf * BN * kLds + lds_idx(row, kc >> 3)) = w[i];
     }
   };
 
@@ -850,6 +855,10 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
       p.bn = 128;
       p.wmode = 3;
       p.tiles = kRaggedTiles;
+      // up to 48 gate rows per tile: 96-wide tiles (43 + 43 live columns of
+      // 96 at F = 11008 instead of 128), a quarter fewer weight requests,
+      // LDS stores and MFMAs on empty columns
+      if (DTSK_GU96 && F <= 48 * kRaggedTiles && p.nw == 8) p.bn = 96;
     }
     if (epi_kind == EPI_NONE) {
       const int tiles = N / p.bn;
@@ -959,6 +968,8 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
       return launch_tiled<kBN, kBM, 16, DTSK_SMALL_DEPTH>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
 #endif
     if (plan.nw == 8) {
+      if (plan.bn == 96)   // the ragged gate|up tiles only
+        return launch_tiled<96, kBM, 8, DTSK_SMALL_DEPTH>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
       if (plan.bn == 64)
         return launch_tiled<64, kBM, 8, DTSK_SMALL_DEPTH>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
       return launch_tiled<kBN, kBM, 8, DTSK_SMALL_DEPTH>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
