@@ -540,10 +540,16 @@ template <int BM>
 constexpr int epi_rows() { return BM > 128 ? 128 : BM; }
 // dynamic LDS of the tiled kernel: the A/W double buffers, or one epilogue
 // pass of the finished fp32 tile, whichever is larger
-template <int BN, int BM = kBM>
+// W tile rows in LDS: BN rounded up to whole load items of NW waves (8 rows
+// per wave), so that a partial last item stores unconditionally (its rows
+// past BN are never read)
+template <int BN, int NW>
+constexpr int w_lds_rows() { return (BN + NW * 8 - 1) / (NW * 8) * (NW * 8); }
+template <int BN, int BM, int NW>
 constexpr int large_lds() {
-  return 2 * (BM + BN) * kLds * 2 > epi_rows<BM>() * (BN + 4) * 4 ? 2 * (BM + BN) * kLds * 2
-                                                                   : epi_rows<BM>() * (BN + 4) * 4;
+  return 2 * (BM + w_lds_rows<BN, NW>()) * kLds * 2 > epi_rows<BM>() * (BN + 4) * 4
+             ? 2 * (BM + w_lds_rows<BN, NW>()) * kLds * 2
+             : epi_rows<BM>() * (BN + 4) * 4;
 }
 
 template <int BN, int BM, int NW, int DEPTH>
@@ -560,7 +566,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
   static_assert(BM % IR == 0 && BN % 8 == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
   extern __shared__ __align__(16) uint16_t lds[];
   uint16_t* As = lds;                          // [2][BM][kLds]
-  uint16_t* Ws = lds + 2 * BM * kLds;          // [2][BN][kLds]
+  constexpr int WR = w_lds_rows<BN, NW>();     // W tile rows in LDS (>= BN)
+  uint16_t* Ws = lds + 2 * BM * kLds;          // [2][WR][kLds]
 
   int mt, nt, split;
   tile_of_block_mn(blockIdx.x, n_mt, splits, mt, nt, split);
@@ -630,7 +637,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
     for (int i = 0; i < CM; ++i) {
       const int row = (t >> 3) + IR * i, kc = (t & 7) * 8;
       if (i < CH) *reinterpret_cast<uint4*>(As + buf * BM * kLds + lds_idx(row, kc >> 3)) = a[i];
-      if (i < CW && row < BN) *reinterpret_cast<uint4*>(Ws + buf * BN * kLds + lds_idx(row, kc >> 3)) = w[i];
+      if (i < CW) *reinterpret_cast<uint4*>(Ws + buf * WR * kLds + lds_idx(row, kc >> 3)) = w[i];
     }
   };
 
@@ -650,7 +657,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
       issue(kt + u + DEPTH - 1, ra[(u + DEPTH - 1) % DEPTH], rw[(u + DEPTH - 1) % DEPTH]);
       const int buf = (DEPTH % 2 == 0) ? (u & 1) : ((kt + u) & 1);   // LDS buffer of step kt + u
       const uint16_t* a = As + buf * BM * kLds;
-      const uint16_t* w = Ws + buf * BN * kLds;
+      const uint16_t* w = Ws + buf * WR * kLds;
 #pragma unroll
       for (int ks = 0; ks < kBK / 32; ++ks) {
         const int kch = ks * 4 + (lane >> 4);
@@ -791,7 +798,7 @@ hipError_t launch_skinny_bn(const GemmPlan& plan, const void* A, int M_max, cons
 template <int BN, int BM = kBM, int NW = 4, int DEPTH = kDepthL>
 hipError_t launch_tiled(const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows, int m_base, int K,
                         const WMap& w, int N, float* P, const Epilogue& epi, hipStream_t st) {
-  constexpr int lds_bytes = large_lds<BN, BM>();
+  constexpr int lds_bytes = large_lds<BN, BM, NW>();
   static bool attr_set = false;  // the tile may need more than the default 64 KiB of LDS
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma<BN, BM, NW, DEPTH>,
