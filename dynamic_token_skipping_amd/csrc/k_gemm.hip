@@ -332,6 +332,9 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #ifndef DTSK_GU96
 #define DTSK_GU96 1
 #endif
+#ifndef DTSK_QKV96
+#define DTSK_QKV96 1
+#endif
 #ifndef DTSK_SMALL_DEPTH
 #define DTSK_SMALL_DEPTH 4
 #endif
@@ -851,6 +854,10 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
     if (DTSK_QKV_SPLIT && epi_kind == EPI_QKV && head_dim <= 128 && n_seg % 128 == 0 && (N / 128) * 2 <= 256 &&
         nk >= 2) {
       p.bn = 128;
+      // 96-wide tiles when they make whole rounds of 256 workgroups (d =
+      // 4096: 128 tiles x 2 splits, against 96 x 2 on 128-wide tiles); the
+      // partials stay in natural column order for the separate epilogue
+      if (DTSK_QKV96 && p.nw == 8 && N % 96 == 0 && (N / 96) * 2 <= 256 && (N / 96) * 2 > (N / 128) * 2) p.bn = 96;
       p.wmode = 0;
       p.sep_epi = 1;
       p.splits = 2;
