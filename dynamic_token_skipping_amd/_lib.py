@@ -101,7 +101,7 @@ def load() -> ctypes.CDLL:
     lib.dl_scatter_cache.argtypes = [POINTER(Dims), c_void_p, c_int32, c_int32, POINTER(Selection), c_int32,
                                      c_void_p, c_void_p]
     lib.dl_partial_attn.argtypes = [POINTER(Dims), POINTER(LayerW), c_void_p, POINTER(Selection), c_void_p, c_int32,
-                                    c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.dl_ffn_rows.argtypes = [POINTER(Dims), POINTER(LayerW), c_void_p, POINTER(Selection), c_int32, c_void_p,
                                 c_size_t, c_void_p]
     lib.dl_lm_head_rows.argtypes = [POINTER(Dims), c_void_p, c_void_p, c_void_p, POINTER(Selection), c_int32,
@@ -223,11 +223,13 @@ def dl_scatter_cache(dims: Dims, rows, w: int, dtype: int, sel: SelectionTensors
 
 
 def dl_partial_attn(dims: Dims, layer: dict, x_rows, sel: SelectionTensors, seq_len, k_total_max: int, k_cache,
-                    v_cache, ws, stream=None):
+                    v_cache, ws, stream=None, lse=None):
+    """``lse``: optional fp32 [k_total_max, n_heads] tensor for the rows' log
+    softmax normalisers."""
     lw = layer_struct(layer)
     s = sel.struct()
     _check(load().dl_partial_attn(ctypes.byref(dims), ctypes.byref(lw), ptr(x_rows), ctypes.byref(s), ptr(seq_len),
-                                  int(k_total_max), ptr(k_cache), ptr(v_cache), ptr(ws), ws.numel(),
+                                  int(k_total_max), ptr(k_cache), ptr(v_cache), ptr(lse), ptr(ws), ws.numel(),
                                   stream_handle(stream)))
 
 

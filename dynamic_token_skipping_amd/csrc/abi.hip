@@ -369,8 +369,9 @@ dl_status product(const Ctx& c, dl_kernel_class kc, const void* A, const RowMap&
 
 // Attention sub-block.  On entry act holds RMSNorm(x, attn_norm) if act_ready.
 // On exit x has the attention residual added and act = RMSNorm(x, ffn_norm).
+// lse_rows (optional): each packed row's per-head log softmax normaliser.
 dl_status attn_block(const Ctx& c, const dl_layer_w* w, float* x, const RowMap& rm, const int32_t* seq_len,
-                     void* kc, void* vc, bool act_ready) {
+                     void* kc, void* vc, bool act_ready, float* lse_rows = nullptr) {
   const dl_dims& d = *c.d;
   void* act = at<void>(c.ws, c.L->act);
   void* q = at<void>(c.ws, c.L->q);
@@ -395,7 +396,7 @@ dl_status attn_block(const Ctx& c, const dl_layer_w* w, float* x, const RowMap& 
                              c.L->attn_splits, attention_splits(d.dtype, d.head_dim, d.S, d.n_heads, rm, c.L->R_part));
                          return launch_attention(d.dtype, q, kc, vc, seq_len, rm, d.S, d.n_heads, d.head_dim, splits,
                                                  at<float>(c.ws, c.L->attn_o), at<float2>(c.ws, c.L->attn_ml),
-                                                 c.L->R_part, attn, c.st);
+                                                 c.L->R_part, attn, c.st, nullptr, nullptr, nullptr, lse_rows);
                        }));
   }
   {
@@ -811,8 +812,8 @@ static dl_status prep_rows(const dl_dims* dims, const dl_selection* sel, int32_t
 }
 
 dl_status dl_partial_attn(const dl_dims* dims, const dl_layer_w* layer, float* x_rows, const dl_selection* sel,
-                          const int32_t* seq_len, int32_t k_total_max, void* k_cache, void* v_cache, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          const int32_t* seq_len, int32_t k_total_max, void* k_cache, void* v_cache,
+                          float* lse_or_null, void* ws, size_t ws_bytes, void* stream) {
   DL_TRY(check_dims(dims));
   DL_TRY(check_layer(layer));
   DL_TRY(check_ptr(x_rows, "x_rows"));
@@ -826,7 +827,7 @@ dl_status dl_partial_attn(const dl_dims* dims, const dl_layer_w* layer, float* x
   if (k_total_max == 0) return DL_OK;
   DL_CHECK_HIP(launch_rope_table(dims->S, dims->head_dim, dims->rope_base, at<float2>(ws, L.rope), st));
   Ctx c{dims, ws, &L, st, (long long)dims->B * dims->S, (long long)k_total_max * dims->S};
-  DL_TRY(attn_block(c, layer, x_rows, rm, seq_len, k_cache, v_cache, false));
+  DL_TRY(attn_block(c, layer, x_rows, rm, seq_len, k_cache, v_cache, false, lse_or_null));
   return DL_OK;
 }
 

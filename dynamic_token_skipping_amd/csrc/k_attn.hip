@@ -37,12 +37,15 @@ constexpr int kMaxKeysSimt = 8192;
 // query row goes to ctx[row(r) * d + ...] (row = ctx_off[b] + position in the
 // sequence, i.e. the packed row of an all-rows map) instead of the storage-type
 // output, and its per-head log normaliser log sum_j exp(q.k_j * scale) to
-// lse[row_pos[r] * n_heads + h].
+// lse[row_pos[r] * n_heads + h].  Without ctx, lse_rows (if set) takes the
+// same normaliser at the packed row, lse_rows[r * n_heads + h], beside the
+// storage-type output.
 struct CtxOut {
   float* ctx;
   float* lse;
   const int32_t* row_pos;
   const int32_t* ctx_off;
+  float* lse_rows;
   __device__ __forceinline__ size_t row(int r, int b, int S) const {
     return (size_t)ctx_off[b] + (size_t)(row_pos[r] - b * S);
   }
@@ -116,7 +119,11 @@ __global__ __launch_bounds__(kSimtThreads) void k_attn_simt(const T* __restrict_
     if (crow) crow[e] = o * inv;
     else out[(size_t)r * d + col0 + e] = from_f32<T>(o * inv);
   }
-  if (co.lse && t == 0) co.lse[(size_t)co.row_pos[r] * gridDim.y + h] = m + logf(sum);
+  if (t == 0) {
+    const float ls = m + logf(sum);
+    if (co.lse) co.lse[(size_t)co.row_pos[r] * gridDim.y + h] = ls;
+    if (co.lse_rows) co.lse_rows[(size_t)r * gridDim.y + h] = ls;
+  }
 }
 
 // Approximate context of rows whose query is unchanged (fp32, any head size):
@@ -430,6 +437,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     return;
   }
   if (n_split == 1) {
+    if (co.lse_rows && g == 0)
+      co.lse_rows[(size_t)r * n_heads + h] = (m_run + log2f(l_run)) * 0.6931471805599453f;
     const float inv = 1.f / l_run;
     uint16_t* orow = out + (size_t)r * d + col0;
 #pragma unroll
@@ -459,9 +468,11 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 // fragments as k_attn_mfma; with 16 keys per wave (H = 4) the P^T operand of
 // a lane is exactly the four probabilities its S^T block left it (keys
 // 4g .. 4g + 3 of query ql), fed to the 16x16x16 MFMA.
-// G = 4, H = 2: 64 queries per workgroup, for many query rows.  G = 1, H = 4:
-// four workgroups per query tile, for few query rows (the kept rows of one
-// sequence), where it replaces the key chunks and their merge kernel.
+// G = 4, H = 2: 64 queries per workgroup, for many query rows.  G = 1, H = 8
+// (128-key tiles): four workgroups per query tile, for few query rows (the
+// kept rows of one sequence), where it replaces the key chunks and their
+// merge kernel.  With lse_rows set, each query's log normaliser
+// (M + log2 den) ln 2 of the merged state goes to lse_rows[row * n_heads + h].
 #ifndef DTSK_ROWS_MAX_KEYS
 #define DTSK_ROWS_MAX_KEYS 1024
 #endif
@@ -478,7 +489,8 @@ __global__ __launch_bounds__(G * H * 64) void k_attn_rows(const uint16_t* __rest
                                                           const int32_t* __restrict__ tile_row0,
                                                           const int32_t* __restrict__ tile_rows, int S, int d,
                                                           int n_heads, float scale_log2, int n_tiles,
-                                                          uint16_t* __restrict__ out) {
+                                                          uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse_rows) {
   constexpr int NT = G * H * 64;               // threads
   constexpr int KW = TK / H;                   // keys of a tile per wave
   constexpr int NSB = KW / 16;                 // S^T blocks per wave and tile
@@ -721,6 +733,8 @@ __global__ __launch_bounds__(G * H * 64) void k_attn_rows(const uint16_t* __rest
       den += w[p] * merge_ml[p * G + grp][ql][1];
     }
     const float inv = 1.f / den;
+    if (lse_rows && part == 0 && g == 0)
+      lse_rows[(size_t)(r0 + qrow) * n_heads + h] = (M + log2f(den)) * 0.6931471805599453f;
     uint16_t* orow = out + (size_t)(r0 + qrow) * d + col0;
     constexpr int BPW = 8 / H;
 #pragma unroll
@@ -769,6 +783,7 @@ __global__ __launch_bounds__(G * H * 64) void k_attn_rows(const uint16_t* __rest
     den += w[p] * merge_ml[(p - 1) * G + grp][ql][1];
   }
   const float inv = 1.f / den;
+  if (lse_rows && g == 0) lse_rows[(size_t)(r0 + qrow) * n_heads + h] = (M + log2f(den)) * 0.6931471805599453f;
   uint16_t* orow = out + (size_t)(r0 + qrow) * d + col0;
 #pragma unroll
   for (int blk = 0; blk < 8; ++blk) {
@@ -836,6 +851,7 @@ __global__ __launch_bounds__(64) void k_attn_combine(const float* __restrict__ o
     if (col % kDh == 0) co.lse[(size_t)co.row_pos[r] * n_heads + h] = (M + log2f(L)) * 0.6931471805599453f;
     return;
   }
+  if (co.lse_rows && col % kDh == 0) co.lse_rows[(size_t)r * n_heads + h] = (M + log2f(L)) * 0.6931471805599453f;
   uint2 w2;
   w2.x = pack_bf16x2(acc.x * inv, acc.y * inv);
   w2.y = pack_bf16x2(acc.z * inv, acc.w * inv);
@@ -881,11 +897,12 @@ int attention_splits(dl_dtype dt, int head_dim, int S, int n_heads, const RowMap
 hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* seq_len, const RowMap& rm, int S, int n_heads, int head_dim, int splits,
                             float* o_part, float2* ml_part, int R_part, void* out, hipStream_t st, float* ctx_out,
-                            const int32_t* ctx_off, float* lse_out) {
+                            const int32_t* ctx_off, float* lse_out, float* lse_rows) {
   const int d = n_heads * head_dim;
   const float scale = 1.f / sqrtf((float)head_dim);
-  const CtxOut co{ctx_out, lse_out, rm.row_pos, ctx_off};
+  const CtxOut co{ctx_out, lse_out, rm.row_pos, ctx_off, lse_rows};
   if (ctx_out && (!lse_out || !ctx_off)) return hipErrorInvalidValue;
+  if (ctx_out && lse_rows) return hipErrorInvalidValue;
   if (use_mfma_attention(dt, head_dim)) {
     if (rm.tq != kTQ || rm.T_max <= 0) return rm.T_max < 0 ? hipErrorInvalidValue : hipSuccess;
     if (splits < 1 || splits > kAttnMaxSplits || (splits > 1 && (!o_part || !ml_part || rm.R_max > R_part)))
@@ -902,13 +919,13 @@ hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, con
       if (query_tiles * n_heads >= kRowsMinBlocks) {
         DTSK_LAUNCH((k_attn_rows<4, 2, DTSK_ROWS_AHEAD, 64>), dim3(grid), dim3(512), 0, st, (const uint16_t*)q, (const uint16_t*)k_cache,
                     (const uint16_t*)v_cache, seq_len, rm.row_seq, rm.tile_row0, rm.tile_rows, S, d, n_heads,
-                    scale_log2, rm.T_max, (uint16_t*)out);
+                    scale_log2, rm.T_max, (uint16_t*)out, lse_rows);
         return hipGetLastError();
       }
       if (DTSK_ATTN_Q16) {
         DTSK_LAUNCH((k_attn_rows<1, DTSK_Q16_PARTS, DTSK_Q16_AHEAD, DTSK_Q16_PARTS * 16>), dim3(grid * (kTQ / 16)), dim3(DTSK_Q16_PARTS * 64), 0, st, (const uint16_t*)q,
                     (const uint16_t*)k_cache, (const uint16_t*)v_cache, seq_len, rm.row_seq, rm.tile_row0,
-                    rm.tile_rows, S, d, n_heads, scale_log2, rm.T_max, (uint16_t*)out);
+                    rm.tile_rows, S, d, n_heads, scale_log2, rm.T_max, (uint16_t*)out, lse_rows);
         return hipGetLastError();
       }
     }

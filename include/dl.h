@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DL_ABI_VERSION 3
+#define DL_ABI_VERSION 4
 
 typedef enum {
   DL_OK = 0,
@@ -242,10 +242,15 @@ dl_status dl_scatter_cache(const dl_dims *dims, const void *rows, int32_t w, dl_
  *   Wo * Attn(RoPE(Wq n(x)), K, V), where the rows' fresh RoPE(Wk n(x)) and
  * Wv n(x) are first written into k_cache/v_cache ([B, S, d] of this layer) at
  * their positions, and each row attends over keys 0..seq_len[b]-1 of its own
- * sequence (bidirectional).  n = RMSNorm with layer->attn_norm. */
+ * sequence (bidirectional).  n = RMSNorm with layer->attn_norm.
+ * lse_or_null (device fp32 [k_total_max, n_heads], or NULL): for each packed
+ * row r < row_off[B] and head h, the log of that row's softmax normaliser,
+ * log sum_j exp(q_rh . k_jh / sqrt(head_dim)) over the same keys (the cached
+ * normaliser of DyLLM's approximate attention, DyLLM section 2B); rows from
+ * row_off[B] on are not written.  Asking for it changes no other output. */
 dl_status dl_partial_attn(const dl_dims *dims, const dl_layer_w *layer, float *x_rows, const dl_selection *sel,
-                          const int32_t *seq_len, int32_t k_total_max, void *k_cache, void *v_cache, void *ws,
-                          size_t ws_bytes, void *stream);
+                          const int32_t *seq_len, int32_t k_total_max, void *k_cache, void *v_cache,
+                          float *lse_or_null, void *ws, size_t ws_bytes, void *stream);
 
 /* SwiGLU FFN sub-block on packed rows: x += Wd (silu(Wg n(x)) * Wu n(x)),
  * n = RMSNorm with layer->ffn_norm.  x_rows is fp32 [k_total_max, d]; the

@@ -33,6 +33,16 @@ def row_rel_err(gpu, ref) -> float:
     return float((num / den).max())
 
 
+def lse_err(gpu, ref) -> float:
+    """max over elements of |g - o| / max(|o|, 1): log normalisers are
+    compared absolutely near zero and relatively beyond."""
+    g = np.asarray(gpu, np.float64)
+    o = np.asarray(ref, np.float64).reshape(g.shape)
+    if g.size == 0:
+        return 0.0
+    return float((np.abs(g - o) / np.maximum(np.abs(o), 1.0)).max())
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 

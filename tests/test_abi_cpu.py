@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.dl_abi_version() == 3
+    assert lib.dl_abi_version() == 4
 
 
 def test_status_strings(lib):

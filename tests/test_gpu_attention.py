@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import host, row_rel_err
+from gpu_util import host, lse_err, row_rel_err
 from oracle import esdllm as E
 
 pytestmark = pytest.mark.gpu
@@ -62,15 +62,19 @@ def test_ragged_partial_layer_matches_oracle(setup, keep):
     x = torch.cat([setup["x0"][b, torch.as_tensor(rows[b], device="cuda")] for b in range(B)]).contiguous()
     kc, vc = setup["kc0"].clone(), setup["vc0"].clone()
     lw = setup["m"]["layers"][0]
-    D.dl_partial_attn(setup["dims"], lw, x, sel, setup["seq_len"], R, kc, vc, setup["ws"])
+    lse = torch.full((R + 3, DIMS.n_heads), float("nan"), dtype=torch.float32, device="cuda")
+    D.dl_partial_attn(setup["dims"], lw, x, sel, setup["seq_len"], R, kc, vc, setup["ws"], lse=lse)
     D.dl_ffn_rows(setup["dims"], lw, x, sel, R, setup["ws"])
     torch.cuda.synchronize()
     xg = host(x)
+    lg = host(lse)
+    assert np.isnan(lg[R:]).all()                      # rows past row_off[B] untouched
     for b, n in enumerate(LENS):
         K = host(setup["kc0"][b, :n])
         V = host(setup["vc0"][b, :n])
-        y = E.layer_forward(host(setup["x0"][b])[rows[b]], rows[b], setup["lw_np"], K, V, n, DIMS)
+        y, _, _, o_lse = E.layer_parts(host(setup["x0"][b])[rows[b]], rows[b], setup["lw_np"], K, V, n, DIMS)
         assert row_rel_err(xg[off[b]:off[b + 1]], y) <= TOL, f"sequence {b}"
+        assert lse_err(lg[off[b]:off[b + 1]], o_lse) <= TOL, f"sequence {b}"
         assert row_rel_err(host(kc[b])[rows[b]], K[rows[b]]) <= TOL
         assert row_rel_err(host(vc[b])[rows[b]], V[rows[b]]) <= TOL
         other = np.setdiff1d(np.arange(S), rows[b])
@@ -134,3 +138,46 @@ def test_ragged_row_map_reuse_is_bit_identical(setup, keep):
         outs.append((x, kc, vc))
     for u, v in zip(*outs):
         assert torch.equal(u, v)
+
+
+def test_fp32_partial_attn_lse_matches_oracle():
+    """fp32 storage (the SIMT attention kernel): dl_partial_attn's rows and
+    their log softmax normalisers on a ragged batch of two sequences against
+    the oracle layer, within 1e-5."""
+    import dynamic_token_skipping_amd as D
+    dims = workloads.ModelDims(d=64, n_heads=2, head_dim=32, d_ffn=128, vocab=64, n_layers=1)
+    lens = (40, 17)
+    B, S = len(lens), max(lens)
+    m = workloads.make_model(dims, 7, "f32", "cuda")
+    g = torch.Generator(device="cuda").manual_seed(8)
+    kc0 = torch.randn((B, S, dims.d), generator=g, device="cuda")
+    vc0 = torch.randn((B, S, dims.d), generator=g, device="cuda")
+    x0 = torch.randn((B, S, dims.d), generator=g, device="cuda")
+    sel = D.SelectionTensors(B, S)
+    rows = []
+    for b, n in enumerate(lens):
+        r = np.arange(1, n, 2)
+        rows.append(r)
+        sel.sel_idx[b, :len(r)] = torch.as_tensor(r, dtype=torch.int32)
+        sel.sel_count[b] = len(r)
+    off = np.concatenate([[0], np.cumsum([len(r) for r in rows])])
+    sel.row_off.copy_(torch.as_tensor(off, dtype=torch.int32))
+    R = int(off[-1])
+    x = torch.cat([x0[b, torch.as_tensor(rows[b], device="cuda")] for b in range(B)]).contiguous()
+    dl = D.make_dims(B, S, dims.d, dims.n_heads, dims.head_dim, dims.d_ffn, dims.vocab, 1, "f32")
+    ws = D.workspace(dl, R)
+    seq_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    kc, vc = kc0.clone(), vc0.clone()
+    lse = torch.full((R, dims.n_heads), float("nan"), dtype=torch.float32, device="cuda")
+    lw = m["layers"][0]
+    D.dl_partial_attn(dl, lw, x, sel, seq_len, R, kc, vc, ws, lse=lse)
+    D.dl_ffn_rows(dl, lw, x, sel, R, ws)
+    torch.cuda.synchronize()
+    lw_np = {k: host(v) for k, v in lw.items()}
+    xg, lg = host(x), host(lse)
+    for b, n in enumerate(lens):
+        K = host(kc0[b, :n])
+        V = host(vc0[b, :n])
+        y, _, _, o_lse = E.layer_parts(host(x0[b])[rows[b]], rows[b], lw_np, K, V, n, dims)
+        assert row_rel_err(xg[off[b]:off[b + 1]], y) <= 1e-5, f"sequence {b}"
+        assert lse_err(lg[off[b]:off[b + 1]], o_lse) <= 1e-5, f"sequence {b}"

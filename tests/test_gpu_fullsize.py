@@ -23,7 +23,7 @@ import torch
 
 import workloads
 from gpu_util import (check_lm_rows_exact_inputs, check_scores_exact_inputs, check_unmask_exact_inputs, host,
-                      row_rel_err, topk_within_band)
+                      lse_err, row_rel_err, topk_within_band)
 from oracle import esdllm as E
 
 pytestmark = pytest.mark.gpu
@@ -333,7 +333,8 @@ def _partial_layer_case(name, lens, sample, seed):
     ws = D.workspace(dl_dims, R)
     seq_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
     kc, vc = kc0.clone(), vc0.clone()
-    D.dl_partial_attn(dl_dims, lw, x, sel, seq_len, R, kc, vc, ws)
+    lse = torch.empty((R, dims.n_heads), dtype=torch.float32, device="cuda")
+    D.dl_partial_attn(dl_dims, lw, x, sel, seq_len, R, kc, vc, ws, lse=lse)
     D.dl_ffn_rows(dl_dims, lw, x, sel, R, ws)
     torch.cuda.synchronize()
     for b in range(B):
@@ -342,12 +343,14 @@ def _partial_layer_case(name, lens, sample, seed):
         assert torch.equal(kc[b][other], kc0[b][other]) and torch.equal(vc[b][other], vc0[b][other])
     lw_np = {k: host(v) for k, v in lw.items()}
     xg = host(x)
+    lg = host(lse)
     for b in sample:
         n = lens[b]
         K = host(kc0[b, :n])
         V = host(vc0[b, :n])
-        y = E.layer_forward(host(x0[off[b]:off[b + 1]]), rows[b], lw_np, K, V, n, dims)
+        y, _, _, o_lse = E.layer_parts(host(x0[off[b]:off[b + 1]]), rows[b], lw_np, K, V, n, dims)
         assert row_rel_err(xg[off[b]:off[b + 1]], y) <= TOL, b
+        assert lse_err(lg[off[b]:off[b + 1]], o_lse) <= TOL, b
         assert row_rel_err(host(kc[b, :n])[rows[b]], K[rows[b]]) <= TOL
         assert row_rel_err(host(vc[b, :n])[rows[b]], V[rows[b]]) <= TOL
     del model, kc, vc, kc0, vc0, ws

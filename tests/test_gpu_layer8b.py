@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import host, row_rel_err, topk_within_band
+from gpu_util import host, lse_err, row_rel_err, topk_within_band
 from oracle import esdllm as E
 
 pytestmark = pytest.mark.gpu
@@ -78,7 +78,10 @@ def test_partial_layer_matches_oracle(lay, keep):
     """Attention + FFN sub-blocks on the selected rows against stale K/V.
     384 and 282 rows leave the second 256-row tile of the gate|up and split-K
     products full up to one epilogue pass, and ragged inside it; 40 rows run
-    the 128-row tiles mostly empty, 21 rows the weight-streaming kernel."""
+    the 128-row tiles mostly empty, 21 rows the weight-streaming kernel.
+    The rows' log softmax normalisers (dl_partial_attn's optional output)
+    against the oracle's, and asking for them leaves the layer output
+    bit-identical."""
     D = lay["D"]
     wl, S, d = lay["wl"], lay["S"], lay["wl"].dims.d
     o_sc = E.score_rows("esdllm", lay["h_cur"], lay["h_prev"], lay["conf"], 0.5)
@@ -92,13 +95,19 @@ def test_partial_layer_matches_oracle(lay, keep):
     kc = lay["st"]["k"].clone().reshape(1, S, d)
     vc = lay["st"]["v"].clone().reshape(1, S, d)
     lw = lay["m"]["layers"][0]
-    D.dl_partial_attn(lay["dims"], lw, x, sel, lay["seq_len"], k, kc, vc, lay["ws"])
+    x_plain = x.clone()
+    lse = torch.full((k, wl.dims.n_heads), float("nan"), dtype=torch.float32, device="cuda")
+    D.dl_partial_attn(lay["dims"], lw, x, sel, lay["seq_len"], k, kc, vc, lay["ws"], lse=lse)
     D.dl_ffn_rows(lay["dims"], lw, x, sel, k, lay["ws"])
+    D.dl_partial_attn(lay["dims"], lw, x_plain, sel, lay["seq_len"], k, kc.clone(), vc.clone(), lay["ws"])
+    D.dl_ffn_rows(lay["dims"], lw, x_plain, sel, k, lay["ws"])
     torch.cuda.synchronize()
+    assert torch.equal(x, x_plain)
     K = host(lay["st"]["k"])
     V = host(lay["st"]["v"])
-    y = E.layer_forward(lay["h_cur"][rows], rows, lay["lw_np"], K, V, S, wl.dims)
+    y, _, _, o_lse = E.layer_parts(lay["h_cur"][rows], rows, lay["lw_np"], K, V, S, wl.dims)
     assert row_rel_err(host(x), y) <= TOL
+    assert lse_err(host(lse), o_lse) <= TOL
     assert row_rel_err(host(kc[0])[rows], K[rows]) <= TOL
     assert row_rel_err(host(vc[0])[rows], V[rows]) <= TOL
     other = np.setdiff1d(np.arange(S), rows)
