@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--weights", choices=("blocked", "row_major"), default="blocked",
+                    help="storage order of the product weights on the device (same results bit for bit)")
     ap.add_argument("--workload", default="full8b")
     ap.add_argument("--timing-stride", type=int, default=8,
                     help="time about one launch in this many of each kernel class (1: every launch)")
@@ -247,7 +249,7 @@ def time_step_kinds(torch, dec, sched, n_steps: int):
     return out
 
 
-def time_layer_steps(torch, model, n_steps: int = 30, warmup: int = 3):
+def time_layer_steps(torch, model, weight_layout: str, n_steps: int = 30, warmup: int = 3):
     """One layer step of the 8B-class layer per keep ratio, on the layer8b
     inputs (cached and current hidden states, K/V caches, confidences):
     score + top-k over the 512 rows (the selection's row map built with
@@ -264,7 +266,8 @@ def time_layer_steps(torch, model, n_steps: int = 30, warmup: int = 3):
     dims, S = wl.dims, wl.prompt_len
     d = dims.d
     st = workloads.make_layer_state(wl, "cuda")
-    dl = make_dims(1, S, d, dims.n_heads, dims.head_dim, dims.d_ffn, dims.vocab, 1, "bf16")
+    dl = make_dims(1, S, d, dims.n_heads, dims.head_dim, dims.d_ffn, dims.vocab, 1, "bf16",
+                   weight_layout=weight_layout)
     ws = workspace(dl, S)
     seq = torch.tensor([S], dtype=torch.int32, device="cuda")
     x_s = st["h_cur"].float()                      # the fp32 layer input the kept rows are gathered from
@@ -406,15 +409,20 @@ def main():
 
     import workloads
     from dynamic_token_skipping_amd import (DL_KC_APPROX, DL_KC_ATTN, DL_KC_GEMM, DL_KC_GEMM_TILED, DL_KC_LMHEAD,
-                                            Decoder, DeviceModel, dl_timing_enable, dl_timing_read, dl_timing_reset)
+                                            Decoder, DeviceModel, dl_timing_enable, dl_timing_read, dl_timing_reset,
+                                            pack_model)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = workloads.workload(args.workload)
     dims, sched = wl.dims, wl.sched
     t0 = time.time()
     model = workloads.make_model(dims, wl.seed, wl.dtype, "cuda")
+    # the decode's weights: the product weights copied into the blocked order
+    # (the row-major model stays for the host baseline's fp64 copy)
+    dev_weights = pack_model(model) if args.weights == "blocked" else model
     prompts, lens = workloads.make_prompt(wl)
-    dec = Decoder(DeviceModel(model, dims.n_heads, dims.head_dim, wl.dtype), prompts, sched)
+    dec = Decoder(DeviceModel(dev_weights, dims.n_heads, dims.head_dim, wl.dtype, weight_layout=args.weights),
+                  prompts, sched)
     torch.cuda.synchronize()
     print(f"# setup {time.time() - t0:.1f} s: {dims.model_params() / 1e9:.2f} B params", file=sys.stderr, flush=True)
 
@@ -482,7 +490,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{wl.name}: 32-layer 8B-class random-init bf16 model, batch 1, 256 prompt + 256 "
                                f"masked, blocks of 32, 256 steps x 1 token, skip layer 4, keep 0.25",
-                   "global_batch": dec.B, "seq_len": dec.S, "keep": sched.keep, "skip_layer": sched.skip_layer},
+                   "global_batch": dec.B, "seq_len": dec.S, "keep": sched.keep, "skip_layer": sched.skip_layer,
+                   "weight_layout": args.weights},
         "roofline": roofline,
         "kernels": {
             "gemm": {"ms_timed": round(g["ms"], 3), "launches_timed": g["launches"],
@@ -502,7 +511,7 @@ def main():
     }
     if wl.name == "full8b" and not args.no_variants:
         out["step_times"] = time_step_kinds(torch, dec, sched, 2 * sched.steps_per_block)
-        out["layer_steps"] = time_layer_steps(torch, model)
+        out["layer_steps"] = time_layer_steps(torch, dev_weights, args.weights)
     if not args.no_variants and wl.name == "full8b":
         dev_model = dec.m
         del dec

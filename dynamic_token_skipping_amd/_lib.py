@@ -29,14 +29,15 @@ TORCH_DTYPES = {DL_F32: torch.float32, DL_BF16: torch.bfloat16}
 EXPORTS = ("dl_score_select", "dl_gather", "dl_scatter_cache", "dl_partial_attn", "dl_ffn_rows", "dl_lm_head_rows",
            "dl_unmask", "dl_denoise_step", "dl_denoise_step_noalloc", "dl_workspace_bytes", "dl_status_string",
            "dl_last_error",
-           "dl_abi_version", "dl_row_map_ints", "dl_timing_enable", "dl_timing_reset", "dl_timing_read")
+           "dl_abi_version", "dl_row_map_ints", "dl_pack_weights", "dl_timing_enable", "dl_timing_reset",
+           "dl_timing_read")
 DL_KC_GEMM, DL_KC_ATTN, DL_KC_LMHEAD, DL_KC_GEMM_TILED, DL_KC_APPROX = 0, 1, 2, 3, 4
 
 
 class Dims(Structure):
     _fields_ = [("B", c_int32), ("S", c_int32), ("d", c_int32), ("n_heads", c_int32), ("head_dim", c_int32),
                 ("d_ffn", c_int32), ("vocab", c_int32), ("n_layers", c_int32), ("dtype", c_int32),
-                ("rms_eps", c_float), ("rope_base", c_float)]
+                ("rms_eps", c_float), ("rope_base", c_float), ("weight_layout", c_int32)]
 
 
 class Selection(Structure):
@@ -121,11 +122,13 @@ def load() -> ctypes.CDLL:
     lib.dl_abi_version.restype = c_int32
     lib.dl_row_map_ints.argtypes = [c_int32, c_int32]
     lib.dl_row_map_ints.restype = ctypes.c_int64
+    lib.dl_pack_weights.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p]
     lib.dl_timing_enable.argtypes = [c_int32, c_int32]
     lib.dl_timing_reset.argtypes = []
     lib.dl_timing_read.argtypes = [c_int32, POINTER(Timing)]
     for name in ("dl_score_select", "dl_gather", "dl_scatter_cache", "dl_partial_attn", "dl_ffn_rows",
-                 "dl_lm_head_rows", "dl_unmask", "dl_denoise_step", "dl_denoise_step_noalloc", "dl_timing_enable",
+                 "dl_lm_head_rows", "dl_unmask", "dl_denoise_step", "dl_denoise_step_noalloc", "dl_pack_weights",
+                 "dl_timing_enable",
                  "dl_timing_reset",
                  "dl_timing_read"):
         getattr(lib, name).restype = st
@@ -152,9 +155,14 @@ def stream_handle(stream=None) -> Optional[int]:
     return s.cuda_stream
 
 
-def make_dims(B, S, d, n_heads, head_dim, d_ffn, vocab, n_layers, dtype, rms_eps=1e-5, rope_base=10000.0) -> Dims:
+WEIGHT_LAYOUTS = {"row_major": 0, "blocked": 1}
+
+
+def make_dims(B, S, d, n_heads, head_dim, d_ffn, vocab, n_layers, dtype, rms_eps=1e-5, rope_base=10000.0,
+              weight_layout="row_major") -> Dims:
     dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
-    return Dims(B, S, d, n_heads, head_dim, d_ffn, vocab, n_layers, dt, rms_eps, rope_base)
+    wl = WEIGHT_LAYOUTS[weight_layout] if isinstance(weight_layout, str) else int(weight_layout)
+    return Dims(B, S, d, n_heads, head_dim, d_ffn, vocab, n_layers, dt, rms_eps, rope_base, wl)
 
 
 class SelectionTensors:
@@ -267,6 +275,14 @@ def dl_denoise_step_noalloc(model: Model, state: State, params: StepParams, stre
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def dl_pack_weights(src, dst, stream=None):
+    """dst (same shape, device) <- the blocked copy of the row-major [N, K]
+    bf16 matrix src."""
+    N, K = src.shape
+    dt = {torch.bfloat16: DL_BF16, torch.float32: DL_F32}.get(src.dtype, -1)
+    _check(load().dl_pack_weights(ptr(src), ptr(dst), int(N), int(K), dt, stream_handle(stream)))
 
 
 def dl_abi_version() -> int:

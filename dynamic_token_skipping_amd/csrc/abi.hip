@@ -82,6 +82,14 @@ dl_status check_dims(const dl_dims* d) {
       return fail(DL_E_UNSUPPORTED, "one sequence's keys (S=%d, d=%d) exceed what one attention read spans (2 GiB)",
                   d->S, d->d);
   }
+  if (d->weight_layout != DL_WEIGHTS_ROW_MAJOR && d->weight_layout != DL_WEIGHTS_BLOCKED)
+    return fail(DL_E_ARG, "dims.weight_layout %d unknown", (int)d->weight_layout);
+  if (d->weight_layout == DL_WEIGHTS_BLOCKED) {
+    if (d->dtype != DL_BF16) return fail(DL_E_DTYPE, "blocked weights are bf16 only");
+    if (d->d % 64 || d->d_ffn % 64 || d->vocab % 8)
+      return fail(DL_E_SHAPE, "blocked weights need d (%d) and d_ffn (%d) multiples of 64 and vocab (%d) of 8", d->d,
+                  d->d_ffn, d->vocab);
+  }
   return DL_OK;
 }
 
@@ -350,7 +358,8 @@ dl_status product(const Ctx& c, dl_kernel_class kc, const void* A, const RowMap&
   // the timed region holds the product and, when it has one, its separate
   // epilogue kernel (rows addressed through the full row map)
   DL_CHECK_HIP(timed(kc, c.st, gemm_bytes(d, rows, N, K), 2.0 * rows * N * K, [&] {
-    hipError_t err = launch_gemm(d.dtype, p, A, rows, rm.n_rows, m_base, K, seg, n_seg, N, P, ge, c.st);
+    hipError_t err = launch_gemm(d.dtype, p, A, rows, rm.n_rows, m_base, K, seg, n_seg, N, P, ge, c.st,
+                                 d.weight_layout);
     if (err != hipSuccess || !p.sep_epi) return err;
     switch (e.kind) {
       case EPI_QKV:
@@ -660,6 +669,19 @@ dl_status scratch_on_current_device(void** out) {
 extern "C" {
 
 int32_t dl_abi_version(void) { return DL_ABI_VERSION; }
+
+dl_status dl_pack_weights(const void* src, void* dst, int32_t N, int32_t K, dl_dtype dtype, void* stream) {
+  DL_TRY(check_ptr(src, "src"));
+  DL_TRY(check_ptr(dst, "dst"));
+  if (N < 1 || K < 1) return fail(DL_E_ARG, "N and K must be positive");
+  if (dtype != DL_BF16) return fail(DL_E_DTYPE, "blocked weights are bf16 only");
+  if (N % 8 || K % 64) return fail(DL_E_SHAPE, "blocked weights need N %% 8 == 0 and K %% 64 == 0 (N=%d, K=%d)", N, K);
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst, n = (uintptr_t)N * (uintptr_t)K * 2;
+  if (a < b + n && b < a + n) return fail(DL_E_ARG, "dst overlaps src");
+  if ((a | b) & 15) return fail(DL_E_ALIGN, "src and dst must be 16-byte aligned");
+  DL_CHECK_HIP(launch_pack_weights(src, dst, N, K, (hipStream_t)stream));
+  return DL_OK;
+}
 
 int64_t dl_row_map_ints(int32_t B, int32_t S) {
   if (B < 1 || S < 1) return 0;

@@ -59,7 +59,20 @@ struct WMap {
   int n_seg;
   int seg_bytes;  // bytes of one segment (buffer range of the skinny path)
   int n_tiles;    // mode 3: column tiles
+  int blocked;    // 1: segments in 8-row x 64-input blocks (DL_WEIGHTS_BLOCKED)
 };
+
+// Byte offset of element (r, k) in a bf16 weight segment of K inputs per row.
+// Row-major: (r K + k) 2.  Blocked: 8 x 64 blocks of 1 KB, an 8-row group's
+// blocks in K order: ((r / 8) (K / 64) + k / 64) 1024 + (r % 8) 128 + (k % 64) 2.
+// Within a block the 64 inputs of a row are contiguous, so the 16-byte pieces
+// of one 64-wide K step sit at the same offsets in both orders; a K step moves
+// a row's offset by w_step bytes.
+__device__ __forceinline__ uint32_t w_offset(bool blocked, int r, int k, int K) {
+  return blocked ? (uint32_t)((((r >> 3) * (K >> 6) + (k >> 6)) << 10) + ((r & 7) << 7) + ((k & 63) << 1))
+                 : (uint32_t)((r * K + k) * 2);
+}
+__device__ __forceinline__ uint32_t w_step(bool blocked) { return blocked ? 1024u : 128u; }
 
 // Mode 3: the rows [a, a + h) of each segment that tile t holds.
 __device__ __forceinline__ void ragged_run(const WMap& w, int t, int& a, int& h) {
@@ -426,7 +439,8 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
                                                                       M * K * 2, kBufWord3);
   uint32_t woff[NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) woff[nb] = (uint32_t)(((row0[nb] + l16) * K + ks0 * 64 + g * 8) * 2);
+  for (int nb = 0; nb < NB; ++nb) woff[nb] = w_offset(W.blocked, row0[nb] + l16, ks0 * 64 + g * 8, K);
+  const uint32_t wst = w_step(W.blocked);
   uint32_t aoff[AP];
 #pragma unroll
   for (int i = 0; i < AP; ++i) {
@@ -440,10 +454,10 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
   auto issue = [&](int step, uint4 (&w)[NB][2], uint4 (&a)[AP]) {
     const bool in = step < nk;
     const int sr = step + rot >= nk ? step + rot - nk : step + rot;
-    const uint32_t ks = (uint32_t)sr * 128u;
+    const uint32_t ks = (uint32_t)sr * 128u, ksw = (uint32_t)sr * wst;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const uint32_t o = in ? woff[nb] + ks : kOob;
+      const uint32_t o = in ? woff[nb] + ksw : kOob;
       w[nb][0] = buf_load16(wr, o);
       w[nb][1] = buf_load16(wr, in ? o + 64u : kOob);
     }
@@ -611,8 +625,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
     wbase[i] = static_cast<const char*>(W.p[sg]);
     // empty columns, and rows past BN of a partial last item (whole waves),
     // read zeros without a memory access
-    woff[i] = r < 0 || row >= BN ? kOob : (uint32_t)((r * K + ks0 * kBK + kc) * 2);
+    woff[i] = r < 0 || row >= BN ? kOob : w_offset(W.blocked, r, ks0 * kBK + kc, K);
   }
+  const int wst = (int)w_step(W.blocked);
   uint4 ra[DEPTH][CH], rw[DEPTH][CW];
   // K order: with one row tile, each column tile starts at its own K step
   // (its weight rows spread over the HBM channels); with several, every tile
@@ -622,7 +637,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
   auto issue = [&](int step, uint4 (&a)[CH], uint4 (&w)[CW]) {
     const bool in = step < nk;
     const int sr = step + rot >= nk ? step + rot - nk : step + rot;
-    const int ks = in ? sr * (kBK * 2) : 0;
+    const int ks = in ? sr * (kBK * 2) : 0, ksw = in ? sr * wst : 0;
     const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase) + ks, (short)0,
                                                                          in ? arec - ks : 0, kBufWord3);
 #pragma unroll
@@ -630,7 +645,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
       if (i < CH) a[i] = buf_load16(ar, aoff[i]);
       if (i < CW) {
         const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char*>(wbase[i]) + ks, (short)0, in ? (int)W.seg_bytes - ks : 0, kBufWord3);
+            const_cast<char*>(wbase[i]) + ksw, (short)0, in ? (int)W.seg_bytes - ksw : 0, kBufWord3);
         w[i] = buf_load16(wr, woff[i]);
       }
     }
@@ -746,8 +761,10 @@ __global__ __launch_bounds__(256) void k_gemm_simt(const T* __restrict__ A, int 
       float av = 0.f, wv = 0.f;
       if (m < M && k < K) av = to_f32(A[(size_t)m * K + k]);
       if (n < N && k < K) {
-        const int sg = n / W.n_seg;
-        wv = to_f32(reinterpret_cast<const T*>(W.p[sg])[(size_t)(n - sg * W.n_seg) * K + k]);
+        const int sg = n / W.n_seg, r = n - sg * W.n_seg;
+        const size_t idx = W.blocked ? ((size_t)(r >> 3) * (K >> 6) + (k >> 6)) * 512 + (r & 7) * 64 + (k & 63)
+                                     : (size_t)r * K + k;
+        wv = to_f32(reinterpret_cast<const T*>(W.p[sg])[idx]);
       }
       As[kk][row] = av;
       Ws[kk][row] = wv;
@@ -951,11 +968,15 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
 
 hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows,
                        int m_base, int K, const void* const* Wseg, int n_seg, int N, float* P, const Epilogue& epi,
-                       hipStream_t st) {
+                       hipStream_t st, int w_layout) {
   WMap w;
   for (int i = 0; i < 4; ++i) w.p[i] = Wseg[i];
   w.mode = plan.wmode;
   w.n_seg = n_seg;
+  w.blocked = w_layout == DL_WEIGHTS_BLOCKED;
+  // blocked weights: whole 8-row groups and 64-wide K steps (the dims check
+  // refuses other shapes)
+  if (w.blocked && (dt != DL_BF16 || K % 64 != 0 || n_seg % 8 != 0)) return hipErrorInvalidValue;
   const long long seg_bytes = (long long)(plan.wmode == 1 || plan.wmode == 3 ? N / 2 : n_seg) * K * 2;
   // the tiled and skinny kernels address a segment through one buffer
   // resource with 32-bit offsets; larger segments are refused by the dims check
@@ -998,6 +1019,29 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
   else
     DTSK_LAUNCH(k_gemm_simt<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)A, M_max, n_rows, m_base, K, w, N,
                        P);
+  return hipGetLastError();
+}
+
+// Blocked copy of a row-major [N, K] bf16 matrix (N % 8 == 0, K % 64 == 0):
+// one thread moves one 16-byte piece (8 inputs of a row), which stays
+// contiguous in the blocked order.
+__global__ __launch_bounds__(256) void k_pack_w8x64(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                    long long items, int K) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= items) return;
+  const int pieces = K >> 3;                     // 16-byte pieces per row
+  const long long r = i / pieces;
+  const int k = (int)(i - r * pieces) << 3;
+  const long long e = ((r >> 3) * (K >> 6) + (k >> 6)) * 512 + (r & 7) * 64 + (k & 63);
+  dst[e >> 3] = src[i];
+}
+
+hipError_t launch_pack_weights(const void* src, void* dst, int N, int K, hipStream_t st) {
+  const long long items = (long long)N * (K / 8);
+  if (items <= 0) return hipSuccess;
+  const long long blocks = (items + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  DTSK_LAUNCH(k_pack_w8x64, dim3((unsigned)blocks), dim3(256), 0, st, (const uint4*)src, (uint4*)dst, items, K);
   return hipGetLastError();
 }
 

@@ -127,7 +127,10 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
 // [splits][M_max][N] fp32 partials; otherwise the epilogue consumes the tile.
 hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows,
                        int m_base, int K, const void* const* Wseg, int n_seg, int N, float* P, const Epilogue& epi,
-                       hipStream_t st);
+                       hipStream_t st, int w_layout);
+// dst = the DL_WEIGHTS_BLOCKED copy of the row-major [N, K] bf16 matrix src
+// (N % 8 == 0, K % 64 == 0).
+hipError_t launch_pack_weights(const void* src, void* dst, int N, int K, hipStream_t st);
 // x[r] += sum over splits of P[s][r] (in split order); then, if g != nullptr,
 // out[r] = T(x[r] / sqrt(mean(x[r]^2) + eps) * g).  Packed rows of the map.
 hipError_t launch_reduce_rows(dl_dtype dt, const float* P, int splits, const RowMap& rm, int d, float* x,

@@ -17,12 +17,43 @@ import torch
 from . import _lib as L
 
 
+PRODUCT_WEIGHTS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+
+def pack_model(tensors: dict, free_source: bool = False, stream=None) -> dict:
+    """The same model with its product weights (every layer's wq, wk, wv, wo,
+    w_gate, w_up, w_down and the LM head) in the blocked order
+    (DL_WEIGHTS_BLOCKED), written by dl_pack_weights into new device tensors;
+    the embedding table and norm gains are shared.  With ``free_source`` the
+    dict's row-major tensors are dropped as their copies are made (the caller
+    must hold no other reference for the memory to be released)."""
+    def packed(t):
+        out = torch.empty_like(t)
+        L.dl_pack_weights(t, out, stream)
+        return out
+    out = {k: v for k, v in tensors.items() if k not in ("layers", "lm_head")}
+    layers = []
+    for i, lw in enumerate(tensors["layers"]):
+        nl = {k: (packed(v) if k in PRODUCT_WEIGHTS else v) for k, v in lw.items()}
+        layers.append(nl)
+        if free_source:
+            tensors["layers"][i] = {k: v for k, v in lw.items() if k not in PRODUCT_WEIGHTS}
+            del lw
+    out["layers"] = layers
+    out["lm_head"] = packed(tensors["lm_head"])
+    if free_source:
+        del tensors["lm_head"]
+    return out
+
+
 class DeviceModel:
-    """Weights on the device plus the dl_model struct that points at them."""
+    """Weights on the device plus the dl_model struct that points at them.
+    ``weight_layout``: "row_major", or "blocked" for tensors from pack_model."""
 
     def __init__(self, tensors: dict, n_heads: int, head_dim: int, dtype: str, rms_eps: float = 1e-5,
-                 rope_base: float = 10000.0):
+                 rope_base: float = 10000.0, weight_layout: str = "row_major"):
         self.t = tensors
+        self.weight_layout = weight_layout
         emb = tensors["embed"]
         self.vocab, self.d = emb.shape
         self.d_ffn = tensors["layers"][0]["w_gate"].shape[0]
@@ -34,7 +65,7 @@ class DeviceModel:
 
     def dims(self, B: int, S: int) -> L.Dims:
         return L.make_dims(B, S, self.d, self.n_heads, self.head_dim, self.d_ffn, self.vocab, self.n_layers,
-                           self.dtype, self.rms_eps, self.rope_base)
+                           self.dtype, self.rms_eps, self.rope_base, self.weight_layout)
 
     def struct(self, B: int, S: int) -> L.Model:
         return L.Model(self.dims(B, S), L.ptr(self.t["embed"]), L.ptr(self.t["final_norm"]),

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DL_ABI_VERSION 4
+#define DL_ABI_VERSION 5
 
 typedef enum {
   DL_OK = 0,
@@ -85,6 +85,21 @@ typedef enum { DL_SEL_TOPK = 0, DL_SEL_THRESHOLD = 1 } dl_select_mode;
  * previous value of that tensor. */
 typedef enum { DL_TENSOR_HIDDEN = 0, DL_TENSOR_KEY = 1, DL_TENSOR_VALUE = 2 } dl_score_tensor;
 
+/* Storage order of the product weights (wq, wk, wv, wo, w_gate, w_up,
+ * w_down and lm_head; the embedding table and the norm gains are always
+ * plain).  Each is logically an [N, K] matrix (N output rows of K inputs):
+ *   DL_WEIGHTS_ROW_MAJOR  element (n, k) at n*K + k.
+ *   DL_WEIGHTS_BLOCKED    blocks of 8 rows x 64 inputs, each block contiguous
+ *                         (row-major inside, 1 KiB in bf16), the blocks of an
+ *                         8-row group in input order, the groups in row order:
+ *                         element (n, k) at ((n/8)*(K/64) + k/64)*512 +
+ *                         (n%8)*64 + k%64.  bf16 only; needs N % 8 == 0 and
+ *                         K % 64 == 0 (d and d_ffn multiples of 64, vocab of 8).
+ * Both give bit-identical results; the blocked order lets a product's
+ * per-step weight reads be 1 KiB runs instead of 128-byte pieces of rows
+ * K*2 bytes apart.  dl_pack_weights writes it. */
+typedef enum { DL_WEIGHTS_ROW_MAJOR = 0, DL_WEIGHTS_BLOCKED = 1 } dl_weight_layout;
+
 typedef struct {
   int32_t B;          /* sequences in the batch */
   int32_t S;          /* padded row capacity per sequence */
@@ -97,6 +112,7 @@ typedef struct {
   dl_dtype dtype;
   float rms_eps;      /* RMSNorm epsilon */
   float rope_base;    /* RoPE base (rotate-half pairs (j, j + head_dim/2)) */
+  int32_t weight_layout; /* dl_weight_layout of the product weights */
 } dl_dims;
 
 typedef struct {
@@ -354,6 +370,12 @@ int32_t dl_abi_version(void);
 /* Size, in int32 elements, of a selection's row map (dl_selection.row_map)
  * for B sequences of row capacity S; 0 when B or S is below 1. */
 int64_t dl_row_map_ints(int32_t B, int32_t S);
+
+/* The DL_WEIGHTS_BLOCKED copy of a row-major [N, K] weight: dst (device,
+ * N*K elements, not overlapping src) receives src (device) in blocked order.
+ * bf16 only (DL_E_DTYPE otherwise); N % 8 and K % 64 must be 0 (DL_E_SHAPE).
+ * Enqueued on `stream`; src is only read. */
+dl_status dl_pack_weights(const void *src, void *dst, int32_t N, int32_t K, dl_dtype dtype, void *stream);
 
 #ifdef __cplusplus
 }

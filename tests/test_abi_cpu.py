@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.dl_abi_version() == 4
+    assert lib.dl_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -56,6 +56,8 @@ def test_workspace_bytes(lib):
     (dict(d=4000), -2), (dict(head_dim=127, d=32 * 127), -2), (dict(dtype=7), -3), (dict(B=0), -1),
     (dict(S=9000, dtype="f32"), -7), (dict(B=2000), -7),
     (dict(vocab=262144), -7), (dict(S=261632), -7),
+    (dict(weight_layout=2), -1), (dict(weight_layout="blocked", dtype="f32", S=512), -3),
+    (dict(weight_layout="blocked", d_ffn=11000), -2), (dict(weight_layout="blocked", vocab=126463), -2),
 ])
 def test_bad_dims_rejected(lib, kw, code):
     d = _dims(**kw)
@@ -63,6 +65,26 @@ def test_bad_dims_rejected(lib, kw, code):
     r = lib.dl_score_select(ctypes.byref(d), 16, 32, 16, 16, 0, 0.5, 0, 0.25, 0.0, ctypes.byref(s), None, 16, 1 << 30,
                             None)
     assert r == code, lib.dl_last_error()
+
+
+def test_blocked_layout_accepted(lib):
+    """The 8B-class shape takes blocked weights: d, d_ffn multiples of 64,
+    vocab of 8."""
+    assert L.workspace_bytes(_dims(weight_layout="blocked"), 128) == L.workspace_bytes(_dims(), 128) > 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 1 << 20, 8, 64, 1), -1),                 # NULL src
+    ((1 << 20, 1 << 24, 8, 64, 0), -3),           # fp32
+    ((1 << 20, 1 << 24, 12, 64, 1), -2),          # N % 8
+    ((1 << 20, 1 << 24, 8, 96, 1), -2),           # K % 64
+    ((1 << 20, (1 << 20) + 512, 8, 64, 1), -1),   # dst overlaps src (8 x 64 bf16 = 1 KiB)
+    ((1 << 20, (1 << 24) + 8, 8, 64, 1), -4),     # dst not 16-byte aligned
+    ((1 << 20, 1 << 24, 0, 64, 1), -1),
+])
+def test_pack_weights_validation(lib, args, code):
+    src, dst, N, K, dt = args
+    assert lib.dl_pack_weights(src, dst, N, K, dt, None) == code, lib.dl_last_error()
 
 
 def test_row_map_size(lib):

@@ -299,6 +299,42 @@ def test_full8b_step_deterministic_and_keep_all_is_refresh(full8b):
     for k in ("tokens", "masked", "h_prev", "k_cache", "v_cache", "h_final", "conf", "argmax"):
         assert torch.equal(skip_all[k], refresh[k]), k
 
+def test_full8b_blocked_weights_bit_identical(full8b):
+    """The product weights in the blocked order (DL_WEIGHTS_BLOCKED, copies
+    written by dl_pack_weights) give the refresh step and the skip steps after
+    it bit for bit as the row-major weights do: every cache, the logits, the
+    scores and the selection."""
+    from dynamic_token_skipping_amd import DeviceModel, pack_model
+    wl, model, prompts, dec = full8b
+    runs = []
+    row_major = dec.model_struct
+    packed = pack_model(model)
+    blocked = DeviceModel(packed, wl.dims.n_heads, wl.dims.head_dim, wl.dtype, weight_layout="blocked")
+    _logits(dec, True)
+    dec.reset()
+    start = _snapshot(dec)             # buffers a refresh step leaves alone (scores) start equal too
+    try:
+        for struct in (row_major, blocked.struct(dec.B, dec.S)):
+            dec.model_struct = struct
+            _restore(dec, start)
+            snaps = []
+            for t in range(3):
+                dec.step(t)
+                snap = _snapshot(dec)
+                snap["logits"] = dec.logits.clone()
+                snaps.append(snap)
+            runs.append(snaps)
+        for t in range(3):
+            for k in STATE + ("logits",):
+                assert torch.equal(runs[0][t][k], runs[1][t][k]), (t, k)
+            for a, b in zip(runs[0][t]["sel"], runs[1][t]["sel"]):
+                assert torch.equal(a, b), t
+    finally:
+        dec.model_struct = row_major
+        _logits(dec, False)
+        del runs, packed, blocked
+        _release()
+
 # ---------------------------------------------------------------------------
 # one partial layer at the batched and long-context shapes, seeded inputs
 # ---------------------------------------------------------------------------

@@ -229,6 +229,62 @@ def test_timing_counts_products_and_keeps_results(lay):
     assert t["flops"] == pytest.approx(2.0 * k * d * (3 * d + d + 2 * F) + 2.0 * k * F * d, rel=1e-12)
 
 
+def test_pack_weights_is_the_blocked_permutation(lay):
+    """dl_pack_weights puts element (n, k) of a row-major [N, K] matrix at
+    ((n/8)(K/64) + k/64)*512 + (n%8)*64 + k%64: the matrix cut into 8 x 64
+    blocks, blocks of a row group in K order."""
+    D = lay["D"]
+    for w in (lay["m"]["layers"][0]["wq"], lay["m"]["layers"][0]["w_down"], lay["m"]["lm_head"][:4104]):
+        w = w.contiguous()
+        N, K = w.shape
+        out = torch.empty_like(w)
+        D.dl_pack_weights(w, out)
+        torch.cuda.synchronize()
+        want = w.view(torch.int16).reshape(N // 8, 8, K // 64, 64).permute(0, 2, 1, 3).reshape(N, K)
+        assert torch.equal(out.view(torch.int16), want)
+
+
+@pytest.mark.parametrize("keep", [1.0, 0.25, 0.04])
+def test_blocked_weights_bit_identical(lay, keep):
+    """The one-layer entry points with the layer's product weights and the
+    LM head in the blocked order give the same rows, caches and LM outputs,
+    bit for bit, as with row-major weights (512 rows on the 128-row tiles, 128
+    kept rows, 21 rows on the weight-streaming kernel)."""
+    from dynamic_token_skipping_amd import pack_model
+    D = lay["D"]
+    wl, S, d = lay["wl"], lay["S"], lay["wl"].dims.d
+    dm = wl.dims
+    o_sc = E.score_rows("esdllm", lay["h_cur"], lay["h_prev"], lay["conf"], 0.5)
+    rows = E.select_topk(o_sc, E.keep_count(keep, S))
+    k = len(rows)
+    sel = D.SelectionTensors(1, S)
+    sel.sel_idx[0, :k] = torch.as_tensor(rows, dtype=torch.int32)
+    sel.sel_count[0] = k
+    sel.row_off[1] = k
+    x0 = lay["st"]["h_cur"][0:S].float()[torch.as_tensor(rows, device="cuda")].contiguous()
+    one = {"layers": [lay["m"]["layers"][0]], "lm_head": lay["m"]["lm_head"], "final_norm": lay["m"]["final_norm"]}
+    packed = pack_model(one)
+    outs = []
+    for layout, mw in (("row_major", one), ("blocked", packed)):
+        dims = D.make_dims(1, S, d, dm.n_heads, dm.head_dim, dm.d_ffn, dm.vocab, 1, "bf16", weight_layout=layout)
+        x = x0.clone()
+        kc = lay["st"]["k"].clone().reshape(1, S, d)
+        vc = lay["st"]["v"].clone().reshape(1, S, d)
+        conf = torch.zeros((1, S), dtype=torch.float32, device="cuda")
+        am = torch.zeros((1, S), dtype=torch.int32, device="cuda")
+        hf = torch.zeros((1, S, d), dtype=torch.bfloat16, device="cuda")
+        lg = torch.zeros((1, S, dm.vocab), dtype=torch.float32, device="cuda")
+        lw = mw["layers"][0]
+        D.dl_partial_attn(dims, lw, x, sel, lay["seq_len"], k, kc, vc, lay["ws"])
+        D.dl_ffn_rows(dims, lw, x, sel, k, lay["ws"])
+        D.dl_lm_head_rows(dims, mw["final_norm"], mw["lm_head"], x, sel, k, conf, am, hf, lg, lay["ws"])
+        torch.cuda.synchronize()
+        outs.append((x, kc, vc, conf, am, hf, lg))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    del packed, outs
+
+
 @pytest.mark.parametrize("keep", [1.0, 0.25, 0.04])
 def test_row_map_reuse_is_bit_identical(lay, keep):
     """A selection carrying its own row map (filled by dl_score_select with
