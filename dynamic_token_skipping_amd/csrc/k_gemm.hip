@@ -150,6 +150,51 @@ __device__ __forceinline__ void tile_epilogue(const Epilogue& e, float* __restri
       Ti[m * TS + BN + 1] = p - e.row_seq[m] * e.S;
     }
     lds_barrier();
+    if constexpr (BN == 192) {
+      if (w.mode == 2 && hd == 128) {
+        // Rope-pair tile of several 64-column groups: group g holds dims
+        // r0_g + [0, 32) and r0_g + 64 + [0, 32) of one head of its own
+        // segment (a tile may cross from q to k or k to v between groups).
+        // Pair p of the tile: group p / 32, columns (64 g + i, 64 g + 32 + i),
+        // i = p % 32, rows r0_g + i and r0_g + i + 64.
+        constexpr int NG = BN / 64, NP = BN / 2;
+        constexpr int kIt = (MAXM * NP + NT - 1) / NT;
+        int gsg[NG], gr0[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) wrow_index<BN>(w, n0 + g * 64, gsg[g], gr0[g]);
+        float2 cs[kIt];
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {            // every rotation factor first: independent loads
+          const int idx = t + it * NT;
+          cs[it] = make_float2(1.f, 0.f);
+          if (idx < M * NP) {
+            const int m = idx / NP, pr = idx - m * NP, g = pr >> 5;
+            if (gsg[g] != 2) cs[it] = e.rope[Ti[m * TS + BN + 1] * half + (gr0[g] + (pr & 31)) % hd];
+          }
+        }
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+          const int idx = t + it * NT;
+          if (idx < M * NP) {
+            const int m = idx / NP, pr = idx - m * NP, g = pr >> 5, i = pr & 31;
+            const int c1 = g * 64 + i, r1 = gr0[g] + i;
+            const float a = T[m * TS + c1], b = T[m * TS + c1 + 32];
+            const size_t pos = (size_t)Ti[m * TS + BN];
+            if (gsg[g] == 2) {
+              uint16_t* vc = reinterpret_cast<uint16_t*>(e.v_cache) + pos * e.d;
+              vc[r1] = from_f32<bf16_t>(a).u;
+              vc[r1 + half] = from_f32<bf16_t>(b).u;
+            } else {
+              uint16_t* dst = reinterpret_cast<uint16_t*>(gsg[g] == 0 ? e.q_out : e.k_cache) +
+                              (gsg[g] == 0 ? (size_t)m * e.d : pos * e.d);
+              dst[r1] = from_f32<bf16_t>(a * cs[it].x - b * cs[it].y).u;
+              dst[r1 + half] = from_f32<bf16_t>(b * cs[it].x + a * cs[it].y).u;
+            }
+          }
+        }
+        return;
+      }
+    }
     // Fast column map: a 64-wide rope-pair tile (mode 2) holds dims r0 + [0, 32)
     // and r0 + 64 + [0, 32) of one head; a BN-wide segmented tile with
     // head_dim == BN holds one whole head r0 + [0, BN).  Other shapes take the
@@ -347,6 +392,9 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #endif
 #ifndef DTSK_QKV96
 #define DTSK_QKV96 1
+#endif
+#ifndef DTSK_QKV192
+#define DTSK_QKV192 1
 #endif
 #ifndef DTSK_SMALL_DEPTH
 #define DTSK_SMALL_DEPTH 4
@@ -735,7 +783,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
     if (e.row_pos) e.row_pos += r0;
     if (e.row_seq) e.row_seq += r0;
     if (e.kind == EPI_LM) e.lm_part += (size_t)r0 * e.lm_tiles * 4;
-    tile_epilogue<BN, TS, NT, ER, (BN == 192)>(e, T, W, n0, Mt);
+    tile_epilogue<BN, TS, NT, ER, (BN == 192 && BM == kBigBM)>(e, T, W, n0, Mt);
   }
 }
 
@@ -957,6 +1005,15 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
       p.tiles = kBigRagged;
     }
   }
+  // QKV on 385..512 rows: 192-wide tiles in rope-pair order, 64 column tiles
+  // x 4 row tiles = 256 workgroups in one round (128-wide tiles make 96 x 4 =
+  // 384, a round and a half)
+  if (DTSK_QKV192 && epi_kind == EPI_QKV && head_dim == 128 && n_seg % 64 == 0 && N % 192 == 0 &&
+      M > 3 * kBM && M <= 4 * kBM && (N / 192) * 4 <= 256) {
+    p.bn = 192;
+    p.wmode = 2;
+    p.nw = 8;
+  }
   if (epi_kind == EPI_NONE) {
     const int tiles = cdiv(M, big ? kBigBM : kBM) * (N / kBN);
     int s = 1;
@@ -1003,6 +1060,8 @@ hipError_t launch_gemm(dl_dtype dt, const GemmPlan& plan, const void* A, int M_m
       return launch_tiled<kBN, kBM, 16, DTSK_SMALL_DEPTH>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
 #endif
     if (plan.nw == 8) {
+      if (plan.bn == 192)  // QKV in rope-pair order
+        return launch_tiled<192, kBM, 8, DTSK_SMALL_DEPTH>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
       if (plan.bn == 96)   // the ragged gate|up tiles only
         return launch_tiled<96, kBM, 8, DTSK_SMALL_DEPTH>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
       if (plan.bn == 64)
