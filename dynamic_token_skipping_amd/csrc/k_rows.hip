@@ -260,13 +260,18 @@ __device__ __forceinline__ bool score_row_wg(const int32_t* __restrict__ rm_pos,
   return true;
 }
 
-// bf16 storage, fused update, d a multiple of 512: one 256-thread workgroup
-// per row (a 512-row step fills 512 workgroups, two per CU), thread t owning
-// 8 consecutive columns of every 2048-column slice.  The slices are taken
-// four at a time: every load of a group is issued before any of the group's
-// H_prev stores.  Each thread's sums, then the four waves' sums added in wave
-// order through LDS.  Same sums as k_score in a different summation order.
+// bf16 storage, d a multiple of 512: one 256-thread workgroup per row (a
+// 512-row step fills 512 workgroups, two per CU), thread t owning 8
+// consecutive columns of every 2048-column slice.  kFused: X comes from the
+// packed fp32 rows, rounded to bf16, and replaces H_prev in the same pass
+// (the slices are taken four at a time: every load of a group is issued
+// before any of the group's H_prev stores); otherwise X is the bf16 tensor
+// h_cur and nothing is written but the score.  Each thread's sums, then the
+// four waves' sums added in wave order through LDS.  Same sums as k_score in a
+// different summation order.
+template <bool kFused>
 __global__ __launch_bounds__(256) void k_score_bf16x8(const float* __restrict__ x_packed,
+                                                      const uint16_t* __restrict__ h_cur,
                                                       const int32_t* __restrict__ off_all,
                                                       const int32_t* __restrict__ rm_pos,
                                                       const int32_t* __restrict__ rm_n, bf16_t* __restrict__ h_prev,
@@ -279,25 +284,48 @@ __global__ __launch_bounds__(256) void k_score_bf16x8(const float* __restrict__ 
   size_t row, xrow;
   if (!score_row_wg(rm_pos, rm_n, off_all, seq_len, S, &row, &xrow)) return;   // uniform over the workgroup
   uint16_t* hp = reinterpret_cast<uint16_t*>(h_prev) + row * d;
-  const float* xr = x_packed + xrow * d;
+  const float* xr = kFused ? x_packed + xrow * d : nullptr;
+  const uint16_t* xc = kFused ? nullptr : h_cur + row * d;
   float l1 = 0.f, dd = 0.f, hh = 0.f, xx = 0.f, xh = 0.f;
   const int n_slices = (d + 2047) / 2048;
   for (int s0 = 0; s0 < n_slices; s0 += G) {
     float4 xa[G], xb[G];
-    uint4 hv[G];
+    uint4 hv[G], xv[G];
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
       const int c = (s0 + gi) * 2048 + t * 8;
       if (s0 + gi < n_slices && c < d) {
-        xa[gi] = *reinterpret_cast<const float4*>(xr + c);
-        xb[gi] = *reinterpret_cast<const float4*>(xr + c + 4);
+        if constexpr (kFused) {
+          xa[gi] = *reinterpret_cast<const float4*>(xr + c);
+          xb[gi] = *reinterpret_cast<const float4*>(xr + c + 4);
+        } else {
+          xv[gi] = *reinterpret_cast<const uint4*>(xc + c);
+        }
         hv[gi] = *reinterpret_cast<const uint4*>(hp + c);
       }
     }
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
       const int c = (s0 + gi) * 2048 + t * 8;
-      if (s0 + gi < n_slices && c < d) {
+      if (!kFused && s0 + gi < n_slices && c < d) {
+        const uint32_t xw[4] = {xv[gi].x, xv[gi].y, xv[gi].z, xv[gi].w};
+        const uint32_t hw[4] = {hv[gi].x, hv[gi].y, hv[gi].z, hv[gi].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xf[2] = {__uint_as_float(xw[e] << 16), __uint_as_float(xw[e] & 0xffff0000u)};
+          const float hf[2] = {__uint_as_float(hw[e] << 16), __uint_as_float(hw[e] & 0xffff0000u)};
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const float df = xf[q] - hf[q];
+            l1 += fabsf(df);
+            dd += df * df;
+            hh += hf[q] * hf[q];
+            xx += xf[q] * xf[q];
+            xh += xf[q] * hf[q];
+          }
+        }
+      }
+      if (kFused && s0 + gi < n_slices && c < d) {
         const float xs[8] = {xa[gi].x, xa[gi].y, xa[gi].z, xa[gi].w, xb[gi].x, xb[gi].y, xb[gi].z, xb[gi].w};
         const uint32_t hw[4] = {hv[gi].x, hv[gi].y, hv[gi].z, hv[gi].w};
         uint32_t ow[4];
@@ -1249,10 +1277,16 @@ hipError_t launch_score(dl_dtype dt, const void* h_cur, const float* x_packed, c
       DTSK_LAUNCH((k_score<float, false>), grid, dim3(256), 0, st, (const float*)h_cur, x_packed, off_all, rp,
                          rn, (float*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
   } else {
-    if (x_packed && d % 512 == 0)   // one workgroup per row
-      DTSK_LAUNCH(k_score_bf16x8, rm ? dim3(rm->R_max) : dim3(S, B), dim3(256), 0, st, x_packed, off_all, rp, rn,
-                  (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
-    else if (x_packed)
+    if (d % 512 == 0) {   // one workgroup per row
+      if (x_packed)
+        DTSK_LAUNCH(k_score_bf16x8<true>, rm ? dim3(rm->R_max) : dim3(S, B), dim3(256), 0, st, x_packed,
+                    (const uint16_t*)nullptr, off_all, rp, rn, (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha,
+                    scores);
+      else
+        DTSK_LAUNCH(k_score_bf16x8<false>, rm ? dim3(rm->R_max) : dim3(S, B), dim3(256), 0, st, x_packed,
+                    (const uint16_t*)h_cur, off_all, rp, rn, (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha,
+                    scores);
+    } else if (x_packed)
       DTSK_LAUNCH((k_score<bf16_t, true>), grid, dim3(256), 0, st, (const bf16_t*)h_cur, x_packed, off_all, rp,
                          rn, (bf16_t*)h_prev, conf, seq_len, S, d, (int)kind, alpha, scores);
     else

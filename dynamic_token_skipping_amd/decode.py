@@ -22,7 +22,7 @@ PRODUCT_WEIGHTS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
 def pack_model(tensors: dict, free_source: bool = False, stream=None) -> dict:
     """The same model with its product weights (every layer's wq, wk, wv, wo,
-    w_gate, w_up, w_down and the LM head) in the blocked order
+    w_gate, w_up, w_down and the LM head, if the dict has one) in the blocked order
     (DL_WEIGHTS_BLOCKED), written by dl_pack_weights into new device tensors;
     the embedding table and norm gains are shared.  With ``free_source`` the
     dict's row-major tensors are dropped as their copies are made (the caller
@@ -40,9 +40,10 @@ def pack_model(tensors: dict, free_source: bool = False, stream=None) -> dict:
             tensors["layers"][i] = {k: v for k, v in lw.items() if k not in PRODUCT_WEIGHTS}
             del lw
     out["layers"] = layers
-    out["lm_head"] = packed(tensors["lm_head"])
-    if free_source:
-        del tensors["lm_head"]
+    if "lm_head" in tensors:
+        out["lm_head"] = packed(tensors["lm_head"])
+        if free_source:
+            del tensors["lm_head"]
     return out
 
 

@@ -10,8 +10,9 @@ against the oracle's score function and a brute-force sort:
 * k = 1 and k = len; a threshold equal to a score keeps that row out (strict);
 * an empty sequence selects nothing.
 
-Both scoring kernels are covered: the standalone one behind dl_score_select
-and the fused one of the decode step (d a multiple of 512)."""
+Every scoring kernel is covered: behind dl_score_select the one-wave-per-row
+kernel (d = 256) and, in bf16 with d a multiple of 512, the
+one-workgroup-per-row kernel; and the fused one of the decode step."""
 import numpy as np
 import pytest
 import torch
@@ -55,10 +56,10 @@ def _inputs(B, S, d, lens, seed):
     return h_prev, h_cur, conf
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_score_select_degenerate_inputs(dtype):
+@pytest.mark.parametrize("dtype,d", [("f32", 256), ("bf16", 256), ("bf16", 512), ("bf16", 2560)])
+def test_score_select_degenerate_inputs(dtype, d):
     import dynamic_token_skipping_amd as D
-    B, S, d = 3, 40, 256
+    B, S = 3, 40
     lens = [40, 0, 17]
     h_prev, h_cur, conf = _inputs(B, S, d, lens, seed=11)
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
@@ -66,7 +67,7 @@ def test_score_select_degenerate_inputs(dtype):
     hc = torch.as_tensor(h_cur).to(tdt).cuda()
     cf = torch.as_tensor(conf).cuda()
     hp64, hc64 = host(hp), host(hc)             # exactly what the kernel reads
-    dims = D.make_dims(B, S, d, 2, 128, 512, 1024, 1, dtype)
+    dims = D.make_dims(B, S, d, d // 128, 128, 512, 1024, 1, dtype)
     ws = D.workspace(dims, B * S)
     seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
     sel = D.SelectionTensors(B, S)
