@@ -847,9 +847,12 @@ dl_status dl_partial_attn(const dl_dims* dims, const dl_layer_w* layer, float* x
   RowMap rm;
   DL_TRY(prep_rows(dims, sel, k_total_max, ws, ws_bytes, &L, &rm, st));
   if (k_total_max == 0) return DL_OK;
-  DL_CHECK_HIP(launch_rope_table(dims->S, dims->head_dim, dims->rope_base, at<float2>(ws, L.rope), st));
+  // the rows' RMSNorm and the RoPE table in one launch
+  DL_CHECK_HIP(launch_rmsnorm_rope(dims->dtype, x_rows, layer->attn_norm, rm, dims->d, dims->rms_eps,
+                                   at<void>(ws, L.act), dims->S, dims->head_dim, dims->rope_base,
+                                   at<float2>(ws, L.rope), st));
   Ctx c{dims, ws, &L, st, (long long)dims->B * dims->S, (long long)k_total_max * dims->S};
-  DL_TRY(attn_block(c, layer, x_rows, rm, seq_len, k_cache, v_cache, false, lse_or_null));
+  DL_TRY(attn_block(c, layer, x_rows, rm, seq_len, k_cache, v_cache, true, lse_or_null));
   return DL_OK;
 }
 

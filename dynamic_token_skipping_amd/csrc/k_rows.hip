@@ -701,15 +701,45 @@ __global__ __launch_bounds__(kRowThreads) void k_store_rows4(const float* __rest
 #endif
 constexpr int kRedSplits = 8;   // partials loaded together (more are added in a second loop)
 
+// RoPE table entry idx of S * half: (cos, sin) of pos * base^(-2j/dh),
+// pos = idx / half, j = idx % half, computed in double.
+__device__ __forceinline__ void rope_entry(int idx, int half, int head_dim, double base, float2* __restrict__ tab) {
+  const int pos = idx / half, j = idx % half;
+  const double inv = pow(base, -2.0 * (double)j / (double)head_dim);
+  double sn, cs;
+  sincos((double)pos * inv, &sn, &cs);
+  tab[idx] = make_float2((float)cs, (float)sn);
+}
+
+// Optional work of a row-reduction launch: the RoPE table, in the blocks past
+// the rows (block M_max + i fills entries i * blockDim .. + blockDim), so that
+// a call that needs both pays one launch.
+struct RopeJob {
+  float2* tab;      // nullptr: no table
+  int n;            // entries (S * half)
+  int half;
+  int head_dim;
+  double base;
+};
+__device__ __forceinline__ void rope_block(const RopeJob& rj, int blk) {
+  const int idx = blk * (int)blockDim.x + (int)threadIdx.x;
+  if (rj.tab && idx < rj.n) rope_entry(idx, rj.half, rj.head_dim, rj.base, rj.tab);
+}
+
 template <typename T, int kChunks, int NT = kRowThreads>
 __global__ __launch_bounds__(NT) void k_reduce_rows(const float* __restrict__ P, int splits, int M_max,
                                                     const int32_t* __restrict__ n_rows, int d, float* __restrict__ x,
-                                                    const T* __restrict__ g, float eps, T* __restrict__ out) {
+                                                    const T* __restrict__ g, float eps, T* __restrict__ out,
+                                                    RopeJob rj) {
   // d == kChunks * 4 * NT: every thread owns kChunks float4 of the
   // row; its row, partial and gain loads are all issued before the first is
   // used, and the partials are added in split order
   __shared__ float red[16];
   const int r = blockIdx.x;
+  if (r >= M_max) {
+    rope_block(rj, r - M_max);
+    return;
+  }
   if (r >= *n_rows) return;
   const size_t sstride = (size_t)M_max * d;
   float4* xr = reinterpret_cast<float4*>(x + (size_t)r * d);
@@ -761,9 +791,13 @@ template <typename T>
 __global__ __launch_bounds__(kRowThreads) void k_reduce_rows_any(const float* __restrict__ P, int splits, int M_max,
                                                                  const int32_t* __restrict__ n_rows, int d,
                                                                  float* __restrict__ x, const T* __restrict__ g,
-                                                                 float eps, T* __restrict__ out) {
+                                                                 float eps, T* __restrict__ out, RopeJob rj) {
   __shared__ float red[16];
   const int r = blockIdx.x;
+  if (r >= M_max) {
+    rope_block(rj, r - M_max);
+    return;
+  }
   if (r >= *n_rows) return;
   const size_t sstride = (size_t)M_max * d;
   float* xr = x + (size_t)r * d;
@@ -790,11 +824,7 @@ __global__ __launch_bounds__(kRowThreads) void k_reduce_rows_any(const float* __
 __global__ void k_rope_table(int S, int half, int head_dim, double base, float2* __restrict__ tab) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= S * half) return;
-  const int pos = idx / half, j = idx % half;
-  const double inv = pow(base, -2.0 * (double)j / (double)head_dim);
-  double sn, cs;
-  sincos((double)pos * inv, &sn, &cs);
-  tab[idx] = make_float2((float)cs, (float)sn);
+  rope_entry(idx, half, head_dim, base, tab);
 }
 
 // q/k/v epilogue: sum the split-K partials, rotate q and k, write q rows and
@@ -1484,29 +1514,40 @@ hipError_t launch_lm_reduce(const float* P, int splits, const RowMap& rm, int m_
 
 template <typename T>
 static hipError_t reduce_rows_t(const float* P, int splits, const RowMap& rm, int d, float* x, const void* g,
-                                float eps, void* out, hipStream_t st) {
+                                float eps, void* out, hipStream_t st, const RopeJob& rj) {
   const T* gg = (const T*)g;
   T* oo = (T*)out;
+  // the rows, then the table's blocks (if any) of the same width
+  const auto blocks = [&](int nt) { return rm.R_max + (rj.tab ? cdiv(rj.n, nt) : 0); };
   if (d == 4096)
-    DTSK_LAUNCH((k_reduce_rows<T, 4096 / 4 / DTSK_RED_THREADS, DTSK_RED_THREADS>), dim3(rm.R_max),
-                dim3(DTSK_RED_THREADS), 0, st, P, splits, rm.R_max, rm.n_rows, d, x, gg, eps, oo);
+    DTSK_LAUNCH((k_reduce_rows<T, 4096 / 4 / DTSK_RED_THREADS, DTSK_RED_THREADS>), dim3(blocks(DTSK_RED_THREADS)),
+                dim3(DTSK_RED_THREADS), 0, st, P, splits, rm.R_max, rm.n_rows, d, x, gg, eps, oo, rj);
   else if (d == 2048)
-    DTSK_LAUNCH((k_reduce_rows<T, 2>), dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
-                       rm.n_rows, d, x, gg, eps, oo);
+    DTSK_LAUNCH((k_reduce_rows<T, 2>), dim3(blocks(kRowThreads)), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
+                rm.n_rows, d, x, gg, eps, oo, rj);
   else if (d == 1024)
-    DTSK_LAUNCH((k_reduce_rows<T, 1>), dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
-                       rm.n_rows, d, x, gg, eps, oo);
+    DTSK_LAUNCH((k_reduce_rows<T, 1>), dim3(blocks(kRowThreads)), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
+                rm.n_rows, d, x, gg, eps, oo, rj);
   else
-    DTSK_LAUNCH(k_reduce_rows_any<T>, dim3(rm.R_max), dim3(kRowThreads), 0, st, P, splits, rm.R_max, rm.n_rows,
-                       d, x, gg, eps, oo);
+    DTSK_LAUNCH(k_reduce_rows_any<T>, dim3(blocks(kRowThreads)), dim3(kRowThreads), 0, st, P, splits, rm.R_max,
+                rm.n_rows, d, x, gg, eps, oo, rj);
   return hipGetLastError();
 }
 
 hipError_t launch_reduce_rows(dl_dtype dt, const float* P, int splits, const RowMap& rm, int d, float* x,
                               const void* g, float eps, void* out, hipStream_t st) {
   if (rm.R_max <= 0) return hipSuccess;
-  if (dt == DL_F32) return reduce_rows_t<float>(P, splits, rm, d, x, g, eps, out, st);
-  return reduce_rows_t<bf16_t>(P, splits, rm, d, x, g, eps, out, st);
+  const RopeJob none{nullptr, 0, 1, 2, 1.0};
+  if (dt == DL_F32) return reduce_rows_t<float>(P, splits, rm, d, x, g, eps, out, st, none);
+  return reduce_rows_t<bf16_t>(P, splits, rm, d, x, g, eps, out, st, none);
+}
+
+hipError_t launch_rmsnorm_rope(dl_dtype dt, const float* x, const void* g, const RowMap& rm, int d, float eps,
+                               void* out, int S, int head_dim, float base, float2* table, hipStream_t st) {
+  if (rm.R_max <= 0) return launch_rope_table(S, head_dim, base, table, st);
+  const RopeJob rj{table, S * (head_dim / 2), head_dim / 2, head_dim, (double)base};
+  if (dt == DL_F32) return reduce_rows_t<float>(nullptr, 0, rm, d, const_cast<float*>(x), g, eps, out, st, rj);
+  return reduce_rows_t<bf16_t>(nullptr, 0, rm, d, const_cast<float*>(x), g, eps, out, st, rj);
 }
 
 hipError_t launch_lm_merge(const float* lm_part, int lm_tiles, const RowMap& rm, int m_base, int M_max, float* conf,

@@ -73,6 +73,10 @@ hipError_t launch_store_rows(dl_dtype dt, const float* x, int w, const RowMap& r
 hipError_t launch_rmsnorm(dl_dtype dt, const float* x, const void* g, const RowMap& rm, int d, float eps, void* out,
                           hipStream_t st);
 hipError_t launch_rope_table(int S, int head_dim, float base, float2* table, hipStream_t st);
+// launch_rmsnorm and launch_rope_table in one launch (the table's blocks after
+// the rows').
+hipError_t launch_rmsnorm_rope(dl_dtype dt, const float* x, const void* g, const RowMap& rm, int d, float eps,
+                               void* out, int S, int head_dim, float base, float2* table, hipStream_t st);
 // RoPE in place on fp32 packed rows [R_max, d] of the row map, at each row's position.
 hipError_t launch_rope_rows(float* x, const RowMap& rm, int S, int d, int head_dim, const float2* rope,
                             hipStream_t st);
