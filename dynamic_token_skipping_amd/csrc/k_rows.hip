@@ -397,6 +397,8 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 constexpr int kSelThreads = 1024;
 
 // Exclusive block scan of one int per thread (fixed order).
+constexpr int kSelRegs = 8;   // candidates per thread held in registers by k_select
+
 __device__ __forceinline__ int block_excl_scan(int v, int* buf, int* total) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   int incl = v;
@@ -445,6 +447,32 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   auto pos = [&](int j) { return cl ? cl[j] : j; };
   const int chunk = (n + kSelThreads - 1) / kSelThreads;
   const int i0 = min(n, t * chunk), i1 = min(n, i0 + chunk);
+  // Each thread's keys stay in registers when they fit (up to kSelRegs per
+  // thread, n <= 8192): the radix passes and the output pass then read no
+  // memory.  SEL_FOR_KEYS(body) runs body with (i, key) for the thread's
+  // candidates i0 .. i1-1 in order.
+  const bool in_regs = chunk <= kSelRegs;             // uniform
+  uint32_t kr[kSelRegs];
+  if (in_regs) {
+#pragma unroll
+    for (int q = 0; q < kSelRegs; ++q) kr[q] = i0 + q < i1 ? score_key(sc[pos(i0 + q)]) : 0u;
+  }
+#define SEL_FOR_KEYS(...)                                             \
+  if (in_regs) {                                                      \
+    _Pragma("unroll") for (int q = 0; q < kSelRegs; ++q) {            \
+      if (i0 + q < i1) {                                              \
+        const int i = i0 + q;                                         \
+        const uint32_t key = kr[q];                                   \
+        (void)i;                                                      \
+        __VA_ARGS__                                                   \
+      }                                                               \
+    }                                                                 \
+  } else {                                                            \
+    for (int i = i0; i < i1; ++i) {                                   \
+      const uint32_t key = score_key(sc[pos(i)]);                     \
+      __VA_ARGS__                                                     \
+    }                                                                 \
+  }
 
   uint32_t thr;       // selected: key > thr, plus the first `need_eq` with key == thr
   int need_eq;
@@ -471,10 +499,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
       for (int j = t; j < 256; j += kSelThreads) hist[j] = 0;
       __syncthreads();
       const uint32_t prefix = s_prefix;
-      for (int i = i0; i < i1; ++i) {
-        const uint32_t key = score_key(sc[pos(i)]);
-        if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-      }
+      SEL_FOR_KEYS(if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);)
       __syncthreads();
       if (t < 64) {
         // wave 0 finds the digit holding the need-th largest key: lane l owns
@@ -517,28 +542,23 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   // in: the rank of an equal row is the number of equal rows before it.
   const bool topk = mode == DL_SEL_TOPK;
   int n_eq = 0;
-  for (int i = i0; i < i1; ++i) n_eq += score_key(sc[pos(i)]) == thr;
+  SEL_FOR_KEYS(n_eq += key == thr;)
   int tot;
   const int eq_base = block_excl_scan(n_eq, scan_buf, &tot);
   int n_sel = 0, er = eq_base;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = score_key(sc[pos(i)]);
-    if (key > thr) {
-      ++n_sel;
-    } else if (topk && key == thr) {
-      n_sel += er < need_eq;
-      ++er;
-    }
-  }
+  SEL_FOR_KEYS(if (key > thr) {
+    ++n_sel;
+  } else if (topk && key == thr) {
+    n_sel += er < need_eq;
+    ++er;
+  })
   int out = block_excl_scan(n_sel, scan_buf, &tot);
   int32_t* dst = sel_idx + (size_t)b * S;
   er = eq_base;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = score_key(sc[pos(i)]);
-    bool take = key > thr;
-    if (!take && topk && key == thr) take = er++ < need_eq;
-    if (take) dst[out++] = pos(i);
-  }
+  SEL_FOR_KEYS(bool take = key > thr;
+               if (!take && topk && key == thr) take = er++ < need_eq;
+               if (take) dst[out++] = pos(i);)
+#undef SEL_FOR_KEYS
   if (t == 0) sel_count[b] = tot;
 }
 

@@ -155,3 +155,39 @@ def test_fused_scoring_degenerate_rows_in_a_decode():
         assert got[b] == _expected(o, np.arange(n), k), b
     assert 3 in got[0] and 30 in got[0] and 7 not in got[0]
     assert 0 not in got[2] and 1 not in got[2]
+
+
+def test_select_beyond_register_capacity():
+    """More candidates than the selection kernel holds in registers (over 8
+    per thread of its 1024): 10000 rows of one sequence, top-k and threshold,
+    against the brute force on the kernel's own scores and the oracle's."""
+    import dynamic_token_skipping_amd as D
+    S, d = 10000, 512
+    g = np.random.default_rng(23)
+    h_prev = g.standard_normal((1, S, d)).astype(np.float32)
+    h_cur = (h_prev + 0.3 * g.standard_normal((1, S, d))).astype(np.float32)
+    conf = g.uniform(size=(1, S)).astype(np.float32)
+    h_prev[0, 100:110] = h_prev[0, 99]                    # a tie group
+    h_cur[0, 100:110] = h_cur[0, 99]
+    conf[0, 100:110] = conf[0, 99]
+    hp = torch.as_tensor(h_prev).to(torch.bfloat16).cuda()
+    hc = torch.as_tensor(h_cur).to(torch.bfloat16).cuda()
+    cf = torch.as_tensor(conf).cuda()
+    dims = D.make_dims(1, S, d, 4, 128, 512, 1024, 1, "bf16")
+    ws = D.workspace(dims, S)
+    seq = torch.tensor([S], dtype=torch.int32, device="cuda")
+    sel = D.SelectionTensors(1, S)
+    scores = torch.zeros((1, S), dtype=torch.float32, device="cuda")
+    o = E.score_rows("esdllm", host(hc[0]), host(hp[0]), conf[0].astype(np.float64), 0.5)
+    for keep in (0.3, 0.0101, 1.0):
+        k = E.keep_count(keep, S)
+        D.dl_score_select(dims, hc, hp, cf, seq, "esdllm", 0.5, D.DL_SEL_TOPK, keep, 0.0, sel, scores=scores, ws=ws)
+        torch.cuda.synchronize()
+        g_sc = host(scores[0])
+        assert np.abs(g_sc - o).max() <= 1e-5 * np.abs(o).max()
+        got = sel.rows()[0]
+        assert got == _expected(g_sc, np.arange(S), k), keep
+    tau = float(np.sort(g_sc)[S // 2])
+    D.dl_score_select(dims, hc, hp, cf, seq, "esdllm", 0.5, D.DL_SEL_THRESHOLD, 1.0, tau, sel, ws=ws)
+    torch.cuda.synchronize()
+    assert sel.rows()[0] == [i for i in range(S) if np.float32(g_sc[i]) > np.float32(tau)]
