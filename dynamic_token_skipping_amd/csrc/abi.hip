@@ -778,14 +778,20 @@ dl_status dl_score_select(const dl_dims* dims, const void* h_cur, const void* h_
   hipStream_t st = (hipStream_t)stream;
   DL_CHECK_HIP(launch_score(dims->dtype, h_cur, nullptr, nullptr, const_cast<void*>(h_prev), conf, seq_len, dims->B,
                             dims->S, dims->d, kind, alpha, scores, st));
+  RowMap rm{};
+  if (out->row_map) rm = rowmap_of_sel(out, dims->B, dims->S, dims->B * dims->S);
+  if (dims->B == 1) {   // one sequence: row_off (and the map) from the selection's own launch
+    DL_CHECK_HIP(launch_select(scores, seq_len, 1, dims->S, mode, keep_ratio, threshold, out->sel_idx,
+                               out->sel_count, st, nullptr, nullptr, nullptr, out->row_off,
+                               out->row_map ? &rm : nullptr));
+    return DL_OK;
+  }
   DL_CHECK_HIP(launch_select(scores, seq_len, dims->B, dims->S, mode, keep_ratio, threshold, out->sel_idx,
                              out->sel_count, st));
-  if (out->row_map) {
-    const RowMap rm = rowmap_of_sel(out, dims->B, dims->S, dims->B * dims->S);
+  if (out->row_map)
     DL_CHECK_HIP(launch_row_off_map(out->sel_idx, out->sel_count, out->row_off, dims->B, dims->S, rm, st));
-  } else {
+  else
     DL_CHECK_HIP(launch_row_off(out->sel_count, out->row_off, dims->B, st));
-  }
   return DL_OK;
 }
 
@@ -1090,20 +1096,24 @@ dl_status dl_denoise_step(const dl_model* model, dl_state* s, const dl_step_para
       DL_TRY(scored_kv_rows(c, &model->layers[sl], p->score_tensor, rm_all, t));
       xs = t;
     }
+    const RowMap rm_sel = rowmap_at(ws, L.map_sel, (int)R_sel, tiles(R_sel));
+    // one sequence: the selection's launch writes row_off and the map too
+    int32_t* one_off = d.B == 1 ? s->sel.row_off : nullptr;
+    const RowMap* one_map = d.B == 1 ? &rm_sel : nullptr;
     if (!resp) {
       DL_CHECK_HIP(launch_score(d.dtype, nullptr, xs, all_off, s->h_prev, s->conf, s->seq_len, d.B, d.S, d.d,
                                 p->score, p->alpha, scores, st));
       DL_CHECK_HIP(launch_select(scores, s->seq_len, d.B, d.S, p->mode, p->keep_ratio, p->threshold, s->sel.sel_idx,
-                                 s->sel.sel_count, st));
+                                 s->sel.sel_count, st, nullptr, nullptr, nullptr, one_off, one_map));
     } else {
       DL_CHECK_HIP(launch_fill_scores(scores, -INFINITY, s->seq_len, d.B, d.S, st));
       DL_CHECK_HIP(launch_score(d.dtype, nullptr, xs, nullptr, s->h_prev, s->conf, s->seq_len, d.B, d.S, d.d,
                                 p->score, p->alpha, scores, st, &rm_all));
       DL_CHECK_HIP(launch_select(scores, s->seq_len, d.B, d.S, p->mode, p->keep_ratio, p->threshold, s->sel.sel_idx,
-                                 s->sel.sel_count, st, all_idx, all_cnt, all_cnt));
+                                 s->sel.sel_count, st, all_idx, all_cnt, all_cnt, one_off, one_map));
     }
-    const RowMap rm_sel = rowmap_at(ws, L.map_sel, (int)R_sel, tiles(R_sel));
-    DL_CHECK_HIP(launch_row_off_map(s->sel.sel_idx, s->sel.sel_count, s->sel.row_off, d.B, d.S, rm_sel, st));
+    if (d.B != 1)
+      DL_CHECK_HIP(launch_row_off_map(s->sel.sel_idx, s->sel.sel_count, s->sel.row_off, d.B, d.S, rm_sel, st));
     float* x_sel = at<float>(ws, L.x_sel);
     if (!resp) {
       DL_CHECK_HIP(launch_gather(sizeof(float), x_all, all_off, d.S, d.d, rm_sel, x_sel, st));

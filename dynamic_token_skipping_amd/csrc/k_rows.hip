@@ -424,6 +424,41 @@ __device__ __forceinline__ int block_excl_scan(int v, int* buf, int* total) {
   return buf[w] + incl - v;
 }
 
+// With one sequence, the selection's row offsets and row map can come out of
+// the same launch (what k_rowmap_all writes for B = 1): row_off null = none;
+// row_pos null = row_off only.
+struct SelMap {
+  int32_t* row_off;
+  int32_t* n_rows;
+  int32_t* row_pos;
+  int32_t* row_seq;
+  int32_t* tile_row0;
+  int32_t* tile_rows;
+  int R_max, T_max, tq;
+};
+
+// Row offsets and the map's rows from tot and tiles, by the block of a
+// one-sequence selection (the kept rows' own entries are written as they are
+// found).
+__device__ void sel_map_finish(const SelMap& m, int tot) {
+  const int t = threadIdx.x;
+  if (t == 0) {
+    m.row_off[0] = 0;
+    m.row_off[1] = tot;
+  }
+  if (!m.row_pos) return;
+  if (t == 0) *m.n_rows = tot;
+  for (int r = tot + t; r < m.R_max; r += kSelThreads) {
+    m.row_pos[r] = -1;
+    m.row_seq[r] = 0;
+  }
+  for (int s = t; s < m.T_max; s += kSelThreads) {
+    const int j0 = s * m.tq;
+    m.tile_row0[s] = j0 < tot ? j0 : 0;
+    m.tile_rows[s] = j0 < tot ? min(m.tq, tot - j0) : 0;
+  }
+}
+
 // Candidates of sequence b: positions 0..seq_len[b]-1, or with a candidate
 // list the cand_cnt[b] ascending positions cand_idx[b*S ...].  Top-k keeps
 // k = ceil(keep * base) of them, clamped to [1, base] and to the candidate
@@ -435,7 +470,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
                                                         const int32_t* __restrict__ cand_cnt,
                                                         const int32_t* __restrict__ k_base,
                                                         int32_t* __restrict__ sel_idx,
-                                                        int32_t* __restrict__ sel_count) {
+                                                        int32_t* __restrict__ sel_count, SelMap map) {
   __shared__ int hist[256];
   __shared__ int scan_buf[kSelThreads / 64 + 1];
   __shared__ uint32_t s_prefix;
@@ -486,6 +521,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
     }
     if (k == 0) {
       if (t == 0) sel_count[b] = 0;
+      if (map.row_off) sel_map_finish(map, 0);
       return;
     }
     // radix select of the k-th largest key, 8 bits at a time from the top
@@ -555,11 +591,19 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   int out = block_excl_scan(n_sel, scan_buf, &tot);
   int32_t* dst = sel_idx + (size_t)b * S;
   er = eq_base;
+  const bool rows_too = map.row_pos != nullptr;     // one sequence: b = 0, row position = pos
   SEL_FOR_KEYS(bool take = key > thr;
                if (!take && topk && key == thr) take = er++ < need_eq;
-               if (take) dst[out++] = pos(i);)
+               if (take) {
+                 if (rows_too) {
+                   map.row_pos[out] = pos(i);
+                   map.row_seq[out] = 0;
+                 }
+                 dst[out++] = pos(i);
+               })
 #undef SEL_FOR_KEYS
   if (t == 0) sel_count[b] = tot;
+  if (map.row_off) sel_map_finish(map, tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -1348,9 +1392,25 @@ hipError_t launch_score(dl_dtype dt, const void* h_cur, const float* x_packed, c
 
 hipError_t launch_select(const float* scores, const int32_t* seq_len, int B, int S, dl_select_mode mode, float keep,
                          float threshold, int32_t* sel_idx, int32_t* sel_count, hipStream_t st,
-                         const int32_t* cand_idx, const int32_t* cand_cnt, const int32_t* k_base) {
+                         const int32_t* cand_idx, const int32_t* cand_cnt, const int32_t* k_base, int32_t* row_off,
+                         const RowMap* rm) {
+  SelMap m{};
+  if (row_off) {
+    if (B != 1) return hipErrorInvalidValue;
+    m.row_off = row_off;
+    if (rm) {
+      m.n_rows = rm->n_rows;
+      m.row_pos = rm->row_pos;
+      m.row_seq = rm->row_seq;
+      m.tile_row0 = rm->tile_row0;
+      m.tile_rows = rm->tile_rows;
+      m.R_max = rm->R_max;
+      m.T_max = rm->T_max;
+      m.tq = rm->tq;
+    }
+  }
   DTSK_LAUNCH(k_select, dim3(B), dim3(kSelThreads), 0, st, scores, seq_len, S, (int)mode, keep, threshold,
-                     cand_idx, cand_cnt, k_base, sel_idx, sel_count);
+                     cand_idx, cand_cnt, k_base, sel_idx, sel_count, m);
   return hipGetLastError();
 }
 

@@ -37,11 +37,13 @@ hipError_t launch_score(dl_dtype dt, const void* h_cur, const float* x_packed, c
 // Selection among every valid row, or among the candidate lists (cand_idx,
 // cand_cnt: ascending positions per sequence, a selection's layout); top-k
 // keeps ceil(keep * k_base[b]) (default base: the candidate count), at most
-// the candidate count.  sel_idx must not alias cand_idx.
+// the candidate count.  sel_idx must not alias cand_idx.  With B == 1 the
+// same launch can also write row_off (if non-null) and the row map rm (if
+// non-null; as launch_row_off_map writes it).
 hipError_t launch_select(const float* scores, const int32_t* seq_len, int B, int S, dl_select_mode mode, float keep,
                          float threshold, int32_t* sel_idx, int32_t* sel_count, hipStream_t st,
                          const int32_t* cand_idx = nullptr, const int32_t* cand_cnt = nullptr,
-                         const int32_t* k_base = nullptr);
+                         const int32_t* k_base = nullptr, int32_t* row_off = nullptr, const RowMap* rm = nullptr);
 // v at positions [0, seq_len[b]) of a [B, S] array.
 hipError_t launch_fill_scores(float* scores, float v, const int32_t* seq_len, int B, int S, hipStream_t st);
 
