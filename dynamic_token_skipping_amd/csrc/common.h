@@ -117,6 +117,13 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// The same with the non-temporal hint (cache policy bit nt): for data read
+// once, such as a product's weights, so that it does not push the operands
+// that are read again (the activation rows) out of the caches.
+__device__ __forceinline__ uint4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Row maps of a packed selection: for packed row r, the flat [B,S] row
 // b*S + i it came from, and its sequence b.  Built on the device.

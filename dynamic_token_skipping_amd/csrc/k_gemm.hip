@@ -396,6 +396,10 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #ifndef DTSK_QKV192
 #define DTSK_QKV192 1
 #endif
+// weights of the tiled products loaded with the non-temporal hint
+#ifndef DTSK_W_NT
+#define DTSK_W_NT 1
+#endif
 #ifndef DTSK_SMALL_DEPTH
 #define DTSK_SMALL_DEPTH 4
 #endif
@@ -506,8 +510,8 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const uint32_t o = in ? woff[nb] + ksw : kOob;
-      w[nb][0] = buf_load16(wr, o);
-      w[nb][1] = buf_load16(wr, in ? o + 64u : kOob);
+      w[nb][0] = DTSK_W_NT ? buf_load16_nt(wr, o) : buf_load16(wr, o);
+      w[nb][1] = DTSK_W_NT ? buf_load16_nt(wr, in ? o + 64u : kOob) : buf_load16(wr, in ? o + 64u : kOob);
     }
 #pragma unroll
     for (int i = 0; i < AP; ++i) a[i] = buf_load16(ar, in ? aoff[i] + ks : kOob);
@@ -694,7 +698,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
       if (i < CW) {
         const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<char*>(wbase[i]) + ksw, (short)0, in ? (int)W.seg_bytes - ksw : 0, kBufWord3);
-        w[i] = buf_load16(wr, woff[i]);
+        w[i] = DTSK_W_NT ? buf_load16_nt(wr, woff[i]) : buf_load16(wr, woff[i]);
       }
     }
   };
