@@ -396,6 +396,10 @@ constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer (< 2 G
 #ifndef DTSK_QKV192
 #define DTSK_QKV192 1
 #endif
+// the tiled kernel skips the fragment reads and MFMAs of padding K steps
+#ifndef DTSK_SKIP_PAD
+#define DTSK_SKIP_PAD 1
+#endif
 // weights of the tiled products loaded with the non-temporal hint
 #ifndef DTSK_W_NT
 #define DTSK_W_NT 1
@@ -728,6 +732,13 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
       const int buf = (DEPTH % 2 == 0) ? (u & 1) : ((kt + u) & 1);   // LDS buffer of step kt + u
       const uint16_t* a = As + buf * BM * kLds;
       const uint16_t* w = Ws + buf * WR * kLds;
+      // a padding step (past this split's K steps; its tiles are zeros) adds
+      // nothing: skip its fragment reads and MFMAs (uniform branch)
+      if (DTSK_SKIP_PAD && kt + u >= nk) {
+        store(buf ^ 1, ra[(u + 1) % DEPTH], rw[(u + 1) % DEPTH]);
+        lds_barrier();
+        continue;
+      }
 #pragma unroll
       for (int ks = 0; ks < kBK / 32; ++ks) {
         const int kch = ks * 4 + (lane >> 4);
