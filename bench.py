@@ -476,7 +476,7 @@ def main():
                 "traffic": recorded_traffic(),
                 "kernel": ("layer products on the 128 kept rows (128-row tiles, 8 waves): k_gemm_mfma BN 64 with 4 K "
                            "splits (O, down), BN 96 with 2 K splits + k_epi_qkv_rows4 (QKV), BN 96 on 256 "
-                           "ragged tiles (gate|up)"),
+                           f"ragged tiles (gate|up); weights {args.weights.replace('_', '-')}, loaded non-temporal"),
                 "sample": (f"a separate pass of {sample_steps} decode steps after the headline steps, about one "
                            f"launch in {max(1, args.timing_stride)} timed"),
                 "launches_timed": g["launches"], "launches_total": g["launches"] + g["dropped"],
