@@ -1004,14 +1004,13 @@ GemmPlan plan_gemm(dl_dtype dt, int M, int N, int K, int epi_kind, int head_dim,
   p.wmode = epi_kind == EPI_SWIGLU ? 1 : 0;
   if (DTSK_LM256 && epi_kind == EPI_LM && N % 256 == 0) p.bn = 256;   // as on fewer rows
   if (p.bn == kBN) p.nw = DTSK_MID_NW;
-  // 257..512 rows, gate|up and the split-K products: two 256-row tiles, which
-  // read every weight tile half as often as four 128-row tiles; gate|up on
+  // More than 256 rows, gate|up and the split-K products: 256-row tiles,
+  // which read every weight tile half as often as 128-row tiles; gate|up on
   // kBigRagged ragged 192-wide tiles (up to 96 gate rows and the matching up
-  // rows each), so that the two row tiles fill 256 compute units.  (QKV and
-  // the LM head ran slower on 256-row tiles at 512 rows, and the long-context
-  // shape, 4608 rows, ran slower with them too.)
-  const bool big = DTSK_BIG_TILES && M > kBigBM && M <= 2 * kBigBM &&
-                   (epi_kind == EPI_SWIGLU || epi_kind == EPI_NONE);
+  // rows each), so that at 512 rows the two row tiles fill 256 compute units.
+  // (QKV and the LM head ran slower on 256-row tiles at 512 rows, QKV also at
+  // 4608 rows.)
+  const bool big = DTSK_BIG_TILES && M > kBigBM && (epi_kind == EPI_SWIGLU || epi_kind == EPI_NONE);
   if (big) {
     p.bm = kBigBM;
     if (epi_kind == EPI_SWIGLU && F <= 96 * kBigRagged) {
