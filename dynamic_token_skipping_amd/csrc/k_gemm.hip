@@ -625,7 +625,9 @@ constexpr int large_lds() {
              : epi_rows<BM>() * (BN + 4) * 4;
 }
 
-template <int BN, int BM, int NW, int DEPTH>
+// WNT: weights loaded with the non-temporal hint (for products whose weight
+// tiles are read by few row tiles; with many, the L2 copy serves the others)
+template <int BN, int BM, int NW, int DEPTH, bool WNT = true>
 __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restrict__ A, int M_max,
                                                        const int32_t* __restrict__ n_rows, int m_base, int K, WMap W,
                                                        int N, int splits, int n_mt, int n_nt, float* __restrict__ P,
@@ -702,7 +704,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
       if (i < CW) {
         const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<char*>(wbase[i]) + ksw, (short)0, in ? (int)W.seg_bytes - ksw : 0, kBufWord3);
-        w[i] = DTSK_W_NT ? buf_load16_nt(wr, woff[i]) : buf_load16(wr, woff[i]);
+        w[i] = WNT && DTSK_W_NT ? buf_load16_nt(wr, woff[i]) : buf_load16(wr, woff[i]);
       }
     }
   };
@@ -878,13 +880,19 @@ hipError_t launch_skinny_bn(const GemmPlan& plan, const void* A, int M_max, cons
   }
 }
 
-template <int BN, int BM = kBM, int NW = 4, int DEPTH = kDepthL>
-hipError_t launch_tiled(const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows, int m_base, int K,
-                        const WMap& w, int N, float* P, const Epilogue& epi, hipStream_t st) {
+// Row tiles up to which the weights are loaded non-temporal: on the kept rows
+// (one row tile) and at 512 rows they are read once or twice and the hint
+// keeps the activation rows cached; with many row tiles each weight tile is
+// read again by the others, from L2 if it stayed there.
+constexpr int kNtMaxRowTiles = 4;
+
+template <int BN, int BM, int NW, int DEPTH, bool WNT>
+hipError_t launch_tiled_k(const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows, int m_base, int K,
+                          const WMap& w, int N, float* P, const Epilogue& epi, hipStream_t st) {
   constexpr int lds_bytes = large_lds<BN, BM, NW>();
   static bool attr_set = false;  // the tile may need more than the default 64 KiB of LDS
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma<BN, BM, NW, DEPTH>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma<BN, BM, NW, DEPTH, WNT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -893,9 +901,17 @@ hipError_t launch_tiled(const GemmPlan& plan, const void* A, int M_max, const in
   // one block per (row tile, column tile, split), in tile_of_block_mn's order
   const bool by_split = plan.splits > 1 && 8 % plan.splits == 0;
   const int grid = by_split ? cdiv(n_nt, 8 / plan.splits) * n_mt * 8 : cdiv(n_nt, 8) * 8 * n_mt * plan.splits;
-  DTSK_LAUNCH((k_gemm_mfma<BN, BM, NW, DEPTH>), dim3(grid), dim3(NW * 64), lds_bytes, st, (const uint16_t*)A, M_max,
-              n_rows, m_base, K, w, N, plan.splits, n_mt, n_nt, P, epi);
+  DTSK_LAUNCH((k_gemm_mfma<BN, BM, NW, DEPTH, WNT>), dim3(grid), dim3(NW * 64), lds_bytes, st, (const uint16_t*)A,
+              M_max, n_rows, m_base, K, w, N, plan.splits, n_mt, n_nt, P, epi);
   return hipGetLastError();
+}
+
+template <int BN, int BM = kBM, int NW = 4, int DEPTH = kDepthL>
+hipError_t launch_tiled(const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows, int m_base, int K,
+                        const WMap& w, int N, float* P, const Epilogue& epi, hipStream_t st) {
+  if (cdiv(M_max, BM) <= kNtMaxRowTiles)
+    return launch_tiled_k<BN, BM, NW, DEPTH, true>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
+  return launch_tiled_k<BN, BM, NW, DEPTH, false>(plan, A, M_max, n_rows, m_base, K, w, N, P, epi, st);
 }
 
 }  // namespace
