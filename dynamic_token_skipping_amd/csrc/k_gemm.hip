@@ -881,10 +881,13 @@ hipError_t launch_skinny_bn(const GemmPlan& plan, const void* A, int M_max, cons
 }
 
 // Row tiles up to which the weights are loaded non-temporal: on the kept rows
-// (one row tile) and at 512 rows they are read once or twice and the hint
-// keeps the activation rows cached; with many row tiles each weight tile is
-// read again by the others, from L2 if it stayed there.
-constexpr int kNtMaxRowTiles = 4;
+// (one row tile) and on 512 rows in 256-row tiles they are read once or
+// twice and the hint keeps the activation rows cached; with more row tiles
+// each weight tile is read again by the others, from L2 if it stayed there.
+#ifndef DTSK_NT_MAX_ROW_TILES
+#define DTSK_NT_MAX_ROW_TILES 2
+#endif
+constexpr int kNtMaxRowTiles = DTSK_NT_MAX_ROW_TILES;
 
 template <int BN, int BM, int NW, int DEPTH, bool WNT>
 hipError_t launch_tiled_k(const GemmPlan& plan, const void* A, int M_max, const int32_t* n_rows, int m_base, int K,
