@@ -405,7 +405,7 @@ dl_status attn_block(const Ctx& c, const dl_layer_w* w, float* x, const RowMap& 
                              c.L->attn_splits, attention_splits(d.dtype, d.head_dim, d.S, d.n_heads, rm, c.L->R_part));
                          return launch_attention(d.dtype, q, kc, vc, seq_len, rm, d.S, d.n_heads, d.head_dim, splits,
                                                  at<float>(c.ws, c.L->attn_o), at<float2>(c.ws, c.L->attn_ml),
-                                                 c.L->R_part, attn, c.st, nullptr, nullptr, nullptr, lse_rows);
+                                                 c.L->R_part, attn, c.st, nullptr, nullptr, nullptr, lse_rows, d.B);
                        }));
   }
   {

@@ -490,7 +490,7 @@ __global__ __launch_bounds__(G * H * 64) void k_attn_rows(const uint16_t* __rest
                                                           const int32_t* __restrict__ tile_rows, int S, int d,
                                                           int n_heads, float scale_log2, int n_tiles,
                                                           uint16_t* __restrict__ out,
-                                                          float* __restrict__ lse_rows) {
+                                                          float* __restrict__ lse_rows, int one_seq) {
   constexpr int NT = G * H * 64;               // threads
   constexpr int KW = TK / H;                   // keys of a tile per wave
   constexpr int NSB = KW / 16;                 // S^T blocks per wave and tile
@@ -519,11 +519,15 @@ __global__ __launch_bounds__(G * H * 64) void k_attn_rows(const uint16_t* __rest
   const int tile = rem / SUB, sub = rem - tile * SUB;
   const int h = unit_on_xcd(pq, xcd, n_heads);
   if (h < 0) return;
+  // With one sequence its key count is read beside the tile's entries
+  // instead of after the row's sequence: one dependent load fewer before the
+  // first key tile.
   const int nrows = __builtin_amdgcn_readfirstlane(tile_rows[tile]);
-  if (nrows <= sub * 16 * G) return;               // also an unused tile (0 rows)
   const int r0 = __builtin_amdgcn_readfirstlane(tile_row0[tile]);
-  const int b = __builtin_amdgcn_readfirstlane(row_seq[r0]);   // uniform: the resources below stay scalar
-  const int n = __builtin_amdgcn_readfirstlane(seq_len[b]);
+  const int n_one = one_seq ? __builtin_amdgcn_readfirstlane(seq_len[0]) : 0;
+  if (nrows <= sub * 16 * G) return;               // also an unused tile (0 rows)
+  const int b = one_seq ? 0 : __builtin_amdgcn_readfirstlane(row_seq[r0]);   // uniform: the resources below stay scalar
+  const int n = one_seq ? n_one : __builtin_amdgcn_readfirstlane(seq_len[b]);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int grp = wave % G, part = wave / G;
   const int ql = lane & 15, g = lane >> 4;
@@ -897,7 +901,7 @@ int attention_splits(dl_dtype dt, int head_dim, int S, int n_heads, const RowMap
 hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* seq_len, const RowMap& rm, int S, int n_heads, int head_dim, int splits,
                             float* o_part, float2* ml_part, int R_part, void* out, hipStream_t st, float* ctx_out,
-                            const int32_t* ctx_off, float* lse_out, float* lse_rows) {
+                            const int32_t* ctx_off, float* lse_out, float* lse_rows, int n_seq) {
   const int d = n_heads * head_dim;
   const float scale = 1.f / sqrtf((float)head_dim);
   const CtxOut co{ctx_out, lse_out, rm.row_pos, ctx_off, lse_rows};
@@ -919,13 +923,13 @@ hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, con
       if (query_tiles * n_heads >= kRowsMinBlocks) {
         DTSK_LAUNCH((k_attn_rows<4, 2, DTSK_ROWS_AHEAD, 64>), dim3(grid), dim3(512), 0, st, (const uint16_t*)q, (const uint16_t*)k_cache,
                     (const uint16_t*)v_cache, seq_len, rm.row_seq, rm.tile_row0, rm.tile_rows, S, d, n_heads,
-                    scale_log2, rm.T_max, (uint16_t*)out, lse_rows);
+                    scale_log2, rm.T_max, (uint16_t*)out, lse_rows, n_seq == 1);
         return hipGetLastError();
       }
       if (DTSK_ATTN_Q16) {
         DTSK_LAUNCH((k_attn_rows<1, DTSK_Q16_PARTS, DTSK_Q16_AHEAD, DTSK_Q16_PARTS * 16>), dim3(grid * (kTQ / 16)), dim3(DTSK_Q16_PARTS * 64), 0, st, (const uint16_t*)q,
                     (const uint16_t*)k_cache, (const uint16_t*)v_cache, seq_len, rm.row_seq, rm.tile_row0,
-                    rm.tile_rows, S, d, n_heads, scale_log2, rm.T_max, (uint16_t*)out, lse_rows);
+                    rm.tile_rows, S, d, n_heads, scale_log2, rm.T_max, (uint16_t*)out, lse_rows, n_seq == 1);
         return hipGetLastError();
       }
     }

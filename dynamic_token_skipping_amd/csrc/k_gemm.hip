@@ -76,6 +76,11 @@ __device__ __forceinline__ uint32_t w_step(bool blocked) { return blocked ? 1024
 
 // Mode 3: the rows [a, a + h) of each segment that tile t holds.
 __device__ __forceinline__ void ragged_run(const WMap& w, int t, int& a, int& h) {
+  if ((unsigned)w.n_seg < (1u << 23) && (unsigned)w.n_tiles <= 256u) {   // (t + 1) n_seg < 2^31
+    a = (int)((unsigned)t * (unsigned)w.n_seg / (unsigned)w.n_tiles);
+    h = (int)((unsigned)(t + 1) * (unsigned)w.n_seg / (unsigned)w.n_tiles) - a;
+    return;
+  }
   a = (int)((long long)t * w.n_seg / w.n_tiles);
   h = (int)((long long)(t + 1) * w.n_seg / w.n_tiles) - a;
 }
@@ -129,11 +134,13 @@ __device__ __forceinline__ void tile_epilogue(const Epilogue& e, float* __restri
     int a = (n0 / BN) * H, h = H;         // the tile's inner columns [a, a + h)
     if (w.mode == 3) ragged_run(w, n0 / BN, a, h);
     uint16_t* out = reinterpret_cast<uint16_t*>(e.act_out);
-    for (int idx = t; idx < M * h; idx += NT) {
-      const int m = idx / h, c = idx - m * h;
-      const float gt = T[m * TS + c], up = T[m * TS + H + c];
-      out[(size_t)m * e.F + a + c] = from_f32<bf16_t>(gt / (1.f + expf(-gt)) * up).u;
-    }
+    // one column per lane, the rows over the waves: no division in the loop
+    static_assert(NT % 64 == 0, "whole waves");
+    for (int c = t & 63; c < h; c += 64)
+      for (int m = t >> 6; m < M; m += NT / 64) {
+        const float gt = T[m * TS + c], up = T[m * TS + H + c];
+        out[(size_t)m * e.F + a + c] = from_f32<bf16_t>(gt / (1.f + expf(-gt)) * up).u;
+      }
     return;
   }
   if constexpr (SWIGLU_ONLY) return;
@@ -647,9 +654,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
   int mt, nt, split;
   tile_of_block_mn(blockIdx.x, n_mt, splits, mt, nt, split);
   if (nt >= n_nt) return;
-  const int M = min(*n_rows - m_base, M_max);
   const int m0 = mt * BM;
-  if (m0 >= M) return;
   const int n0 = nt * BN;
   const int nk_all = K / kBK;
   const int ks0 = split * nk_all / splits, ks1 = (split + 1) * nk_all / splits;
@@ -665,8 +670,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
   // The per-lane offsets are fixed; each K step moves the buffer descriptors'
   // base (scalar arithmetic only), and a padding step gets descriptors with no
   // records, so every lane reads zeros through the range check.
+  // A's rows up to M_max are read (rows >= M_max are past the records at
+  // every step): a row at or past the row count feeds only its own output
+  // row, which is never stored, so the first loads need not wait for *n_rows
   const char* abase = reinterpret_cast<const char*>(A + (size_t)m0 * K);
-  const int arec = min(M - m0, BM) * K * 2;    // rows >= M are past the records at every step
+  const int arec = max(min(M_max - m0, BM), 0) * K * 2;
   const char* wbase[CW];
   uint32_t aoff[CH], woff[CW];
 #pragma unroll
@@ -725,6 +733,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_mfma(const uint16_t* __restric
 
 #pragma unroll
   for (int s = 0; s < DEPTH - 1; ++s) issue(s, ra[s], rw[s]);
+  // the row count decides the early exit and which rows are stored
+  const int M = min(*n_rows - m_base, M_max);
+  if (m0 >= M) return;
   store(0, ra[0], rw[0]);
   lds_barrier();
   for (int kt = 0; kt < nk_pad; kt += DEPTH) {

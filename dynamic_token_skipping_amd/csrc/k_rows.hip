@@ -804,7 +804,8 @@ __global__ __launch_bounds__(NT) void k_reduce_rows(const float* __restrict__ P,
     rope_block(rj, r - M_max);
     return;
   }
-  if (r >= *n_rows) return;
+  // rows r < M_max are in every buffer: their loads go out before the row
+  // count arrives, which then decides whether anything is stored
   const size_t sstride = (size_t)M_max * d;
   float4* xr = reinterpret_cast<float4*>(x + (size_t)r * d);
   const float4* pr = reinterpret_cast<const float4*>(P + (size_t)r * d);
@@ -819,6 +820,7 @@ __global__ __launch_bounds__(NT) void k_reduce_rows(const float* __restrict__ P,
   if (g)
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) gv[c] = load4(g + (threadIdx.x + c * NT) * 4);
+  if (r >= *n_rows) return;                          // uniform over the workgroup
   auto add = [&](float4& a, const float4& b) {
     a.x += b.x;
     a.y += b.y;
@@ -1002,7 +1004,6 @@ __global__ __launch_bounds__(1024) void k_epi_qkv_rows4(const float* __restrict_
                                                         T* __restrict__ q_out, T* __restrict__ k_cache,
                                                         T* __restrict__ v_cache) {
   const int r = blockIdx.x;
-  if (r >= *n_rows) return;
   const int seg = blockIdx.y, t = threadIdx.x;
   const int half = head_dim >> 1, tph = half >> 2;   // threads per head
   if (t >= d >> 3) return;                           // d / 8 = heads x threads per head
@@ -1016,6 +1017,10 @@ __global__ __launch_bounds__(1024) void k_epi_qkv_rows4(const float* __restrict_
       v1[s] = *reinterpret_cast<const float4*>(base + s * stride);
       v2[s] = *reinterpret_cast<const float4*>(base + s * stride + half);
     }
+  // rows r < M_max are in the partials and the row map: their loads go out
+  // before the row count arrives, which then decides whether anything is stored
+  const int p = row_pos[r], sq = row_seq[r];
+  if (r >= *n_rows) return;                          // uniform over the workgroup
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
 #pragma unroll
   for (int s = 0; s < kEpiMaxSplits; ++s)
@@ -1023,14 +1028,13 @@ __global__ __launch_bounds__(1024) void k_epi_qkv_rows4(const float* __restrict_
       a.x += v1[s].x; a.y += v1[s].y; a.z += v1[s].z; a.w += v1[s].w;
       b.x += v2[s].x; b.y += v2[s].y; b.z += v2[s].z; b.w += v2[s].w;
     }
-  const int p = row_pos[r];
   const size_t col = (size_t)h * head_dim + c;
   if (seg == 2) {
     store4(v_cache + (size_t)p * d + col, a);
     store4(v_cache + (size_t)p * d + col + half, b);
     return;
   }
-  const int pos = p - row_seq[r] * S;
+  const int pos = p - sq * S;
   const float4 c01 = *reinterpret_cast<const float4*>(rope + (size_t)pos * half + c);       // (cos, sin) of c, c + 1
   const float4 c23 = *reinterpret_cast<const float4*>(rope + (size_t)pos * half + c + 2);   // of c + 2, c + 3
   const float4 o1 = make_float4(a.x * c01.x - b.x * c01.y, a.y * c01.z - b.y * c01.w, a.z * c23.x - b.z * c23.y,

@@ -159,12 +159,13 @@ int attention_splits(dl_dtype dt, int head_dim, int S, int n_heads, const RowMap
 // row ctx_off[b] + position (the packed row of an all-rows map), and each
 // (row, head)'s log normaliser to lse_out[row_pos * n_heads + head].  Without
 // ctx_out, lse_rows (if set) takes that normaliser at the packed row,
-// lse_rows[row * n_heads + head], beside `out`.
+// lse_rows[row * n_heads + head], beside `out`.  n_seq: the sequences of the
+// caches when known (1 spares the kernels a dependent load), else 0.
 hipError_t launch_attention(dl_dtype dt, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* seq_len, const RowMap& rm, int S, int n_heads, int head_dim, int splits,
                             float* o_part, float2* ml_part, int R_part, void* out, hipStream_t st,
                             float* ctx_out = nullptr, const int32_t* ctx_off = nullptr, float* lse_out = nullptr,
-                            float* lse_rows = nullptr);
+                            float* lse_rows = nullptr, int n_seq = 0);
 // Approximate context of every row of rm_all that is not active (inv < 0):
 // ctx_new[r] = ctx_cache[pos] + sum_j exp(q_cache[pos].k_j / sqrt(dh) - lse[pos]) dv_j
 // per head, j over the active rows of the row's sequence (k_act / dv_act packed

@@ -34,8 +34,9 @@
  *     positions in sel_idx[b*S ...]; packed row r of sequence b is
  *     row_off[b] + j for its j-th selected position.  Row buffers such as
  *     x_rows are [k_total_max, width]; only the first row_off[B] rows are
- *     touched (row_off lives on the device, so threshold selections need no
- *     host synchronisation).
+ *     written (row_off lives on the device, so threshold selections need no
+ *     host synchronisation), and kernels may read any of the k_total_max rows
+ *     before the row count arrives.
  */
 #ifndef DL_H
 #define DL_H
