@@ -334,3 +334,50 @@ def test_row_map_reuse_is_bit_identical(lay, keep):
         assert torch.equal(u, v)
     del outs
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("keep,extra", [(0.25, 64), (0.25, 8), (0.04, 64)])
+def test_stale_tail_rows_and_workspace_do_not_leak(lay, keep, extra):
+    """The row kernels may read packed rows past the selection's count (up to
+    k_total_max) and stale workspace bytes before the device-side row count
+    arrives; what they store must not depend on them.  NaN in the tail rows
+    of x_rows and in every workspace byte leaves the first k rows, the K/V
+    caches, h_final, the logits and the confidence statistics bit-identical
+    to a run over zeroed buffers, and the tail rows unwritten."""
+    D = lay["D"]
+    S, d, V = lay["S"], lay["wl"].dims.d, lay["wl"].dims.vocab
+    st = lay["st"]
+    sel = D.SelectionTensors(1, S, row_map=True)
+    D.dl_score_select(lay["dims"], st["h_cur"], st["h_prev"], st["conf"], lay["seq_len"], "esdllm", 0.5,
+                      D.DL_SEL_TOPK, keep, 0.0, sel, ws=lay["ws"])
+    torch.cuda.synchronize()
+    k = int(sel.sel_count[0])
+    kmax = min(S, k + extra)
+    assert k == E.keep_count(keep, S) and kmax > k
+    rows = sel.sel_idx[0, :k].long()
+    lw = lay["m"]["layers"][0]
+    outs = []
+    for poison in (False, True):
+        ws = D.workspace(lay["dims"], kmax)
+        ws.fill_(255 if poison else 0)                # 0xff bytes: NaN in fp32 and bf16
+        x = torch.full((kmax, d), float("nan") if poison else 0.0, dtype=torch.float32, device="cuda")
+        x[:k] = st["h_cur"][0:S].float()[rows]
+        kc = st["k"].clone().reshape(1, S, d)
+        vc = st["v"].clone().reshape(1, S, d)
+        D.dl_partial_attn(lay["dims"], lw, x, sel, lay["seq_len"], kmax, kc, vc, ws)
+        D.dl_ffn_rows(lay["dims"], lw, x, sel, kmax, ws)
+        conf = torch.full((1, S), -1.0, device="cuda")
+        amax = torch.full((1, S), -1, dtype=torch.int32, device="cuda")
+        hfin = torch.zeros((1, S, d), dtype=torch.bfloat16, device="cuda")
+        logits = torch.zeros((1, S, V), dtype=torch.float32, device="cuda")
+        D.dl_lm_head_rows(lay["dims"], lay["m"]["final_norm"], lay["m"]["lm_head"], x, sel, kmax, conf, amax, hfin,
+                          logits, ws)
+        torch.cuda.synchronize()
+        if poison:
+            assert torch.isnan(x[k:]).all()              # tail rows read at most, never written
+        assert torch.isfinite(x[:k]).all()
+        outs.append((x[:k].clone(), kc, vc, conf, amax, hfin, logits))
+        del ws
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    del outs
