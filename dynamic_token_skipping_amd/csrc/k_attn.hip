@@ -363,29 +363,44 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = k0 + kb * 16 + g * 4 + i;
-        float v = st[kb][i] * scale_log2;
-        if (key >= kend) v = -INFINITY;
-        st[kb][i] = v;
-        tmax = fmaxf(tmax, v);
+        st[kb][i] *= scale_log2;
+        tmax = fmaxf(tmax, st[kb][i]);
       }
+    if (k0 + kTK > kend) {                          // the tile that crosses kend (uniform): mask the keys past it
+      tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (k0 + kb * 16 + g * 4 + i >= kend) st[kb][i] = -INFINITY;
+          tmax = fmaxf(tmax, st[kb][i]);
+        }
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float corr = exp2_fast(m_run - m_new);
+    // Lazy rescale (as in k_attn_rows): the reference max m_run moves only
+    // when a tile brings a score more than 8 above it, so p <= 2^8 and O, l
+    // stay relative to m_run; a wave rescales only when one of its queries
+    // moved.  The softmax vector work per score roughly halves.
+    const bool grow = tmax > m_run + 8.f;
+    const float m_new = grow ? tmax : m_run;
+    if (__builtin_amdgcn_ballot_w64(grow)) {        // uniform over the wave
+      const float corr = grow ? exp2_fast(m_run - m_new) : 1.f;
+      l_run *= corr;
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) o[blk] *= corr;
+    }
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2_fast(st[kb][i] - m_new);
+        const float p = m_new == -INFINITY ? 0.f : exp2_fast(st[kb][i] - m_new);
         st[kb][i] = p;
         psum += p;
       }
-    l_run = l_run * corr + psum;
-#pragma unroll
-    for (int blk = 0; blk < 8; ++blk) o[blk] *= corr;
+    l_run += psum;
     }
     // O^T += V^T P^T over the two 32-key chunks
 #pragma unroll
