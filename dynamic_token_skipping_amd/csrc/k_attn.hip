@@ -358,14 +358,13 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
         }
     } else {
     // online softmax for query ql over this tile
+    // unscaled scores, their max scaled once, the scale of each probability
+    // in one fma (as in k_attn_rows)
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        st[kb][i] *= scale_log2;
-        tmax = fmaxf(tmax, st[kb][i]);
-      }
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, st[kb][i]);
     if (k0 + kTK > kend) {                          // the tile that crosses kend (uniform): mask the keys past it
       tmax = -INFINITY;
 #pragma unroll
@@ -378,6 +377,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax *= scale_log2;
     // Lazy rescale (as in k_attn_rows): the reference max m_run moves only
     // when a tile brings a score more than 8 above it, so p <= 2^8 and O, l
     // stay relative to m_run; a wave rescales only when one of its queries
@@ -391,12 +391,13 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
       for (int blk = 0; blk < 8; ++blk) o[blk] *= corr;
     }
     m_run = m_new;
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;   // no key seen yet: every p is 2^-inf = 0
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = m_new == -INFINITY ? 0.f : exp2_fast(st[kb][i] - m_new);
+        const float p = exp2_fast(fmaf(st[kb][i], scale_log2, -m_ref));
         st[kb][i] = p;
         psum += p;
       }
@@ -647,14 +648,14 @@ __global__ __launch_bounds__(G * H * 64) void k_attn_rows(const uint16_t* __rest
         st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c], st[j], 0, 0, 0);
       }
     }
+    // scores stay unscaled: the max is taken on them and scaled once (the
+    // scale is positive, so that is the max of the scaled scores exactly),
+    // and each probability takes its scale in one fma below
     float tmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NSB; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        st[j][i] *= scale_log2;
-        tmax = fmaxf(tmax, st[j][i]);
-      }
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, st[j][i]);
     if (k0 + TK > n) {                            // the tile that crosses n (uniform): mask the keys past it
       tmax = -INFINITY;
 #pragma unroll
@@ -667,6 +668,7 @@ __global__ __launch_bounds__(G * H * 64) void k_attn_rows(const uint16_t* __rest
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax *= scale_log2;
     // Lazy rescale: the reference max m_run of a query moves only when a tile
     // brings a score more than 8 above it, so p = 2^(s - m_run) <= 2^8 (exact
     // range in fp32 and bf16) and O, l stay relative to m_run; the normalised
@@ -682,12 +684,15 @@ __global__ __launch_bounds__(G * H * 64) void k_attn_rows(const uint16_t* __rest
       for (int blk = 0; blk < 8; ++blk) o[blk] *= corr;
     }
     m_run = m_new;
+    // a query that has seen no key yet (m = -inf) has only masked scores
+    // here: a finite reference makes each of them 2^-inf = 0
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < NSB; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = m_new == -INFINITY ? 0.f : exp2_fast(st[j][i] - m_new);
+        const float p = exp2_fast(fmaf(st[j][i], scale_log2, -m_ref));
         st[j][i] = p;
         psum += p;
       }
