@@ -220,8 +220,20 @@ __device__ __forceinline__ int unit_on_xcd(int pq, int xcd, int n_units) {
 // active rows' previous keys and value changes (packed, a.key_off / a.key_cnt),
 // and the softmax has the row's cached normaliser in place of the running one:
 // C_new = C_cached + sum_j 2^(s_j - lse2) dV_j, written for non-active rows.
+// Waves per SIMD the key-chunk kernel is built for: 3 (168 VGPRs, no
+// spills, against 184 and 2 waves left to the compiler) lets the softmax
+// vector work of one wave overlap the matrix-core work of the others; 0:
+// the compiler's choice.
+#ifndef DTSK_ATTN_MFMA_OCC
+#define DTSK_ATTN_MFMA_OCC 3
+#endif
+#if DTSK_ATTN_MFMA_OCC > 0
+#define DTSK_ATTN_MFMA_BOUNDS __launch_bounds__(256, DTSK_ATTN_MFMA_OCC)
+#else
+#define DTSK_ATTN_MFMA_BOUNDS __launch_bounds__(256)
+#endif
 template <bool kApprox>
-__global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
+__global__ DTSK_ATTN_MFMA_BOUNDS void k_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
                                                    const uint16_t* __restrict__ Vc,
                                                    const int32_t* __restrict__ seq_len,
                                                    const int32_t* __restrict__ row_seq,
