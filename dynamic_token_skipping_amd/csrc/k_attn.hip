@@ -360,14 +360,19 @@ __global__ DTSK_ATTN_MFMA_BOUNDS void k_attn_mfma(const uint16_t* __restrict__ q
       }
     }
     if constexpr (kApprox) {
-      // cached probabilities: 2^(s - lse2), no running normaliser
+      // cached probabilities: 2^(s - lse2), no running normaliser; keys past
+      // kend masked only in the tile that crosses it (uniform)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + kb * 16 + g * 4 + i;
-          st[kb][i] = key < kend ? exp2_fast(st[kb][i] * scale_log2 - lse2) : 0.f;
-        }
+        for (int i = 0; i < 4; ++i) st[kb][i] = exp2_fast(fmaf(st[kb][i], scale_log2, -lse2));
+      if (k0 + kTK > kend) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (k0 + kb * 16 + g * 4 + i >= kend) st[kb][i] = 0.f;
+      }
     } else {
     // online softmax for query ql over this tile
     // unscaled scores, their max scaled once, the scale of each probability
