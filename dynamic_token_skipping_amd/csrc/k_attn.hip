@@ -209,17 +209,6 @@ __device__ __forceinline__ int unit_on_xcd(int pq, int xcd, int n_units) {
   return u < n_units ? u : -1;
 }
 
-// One workgroup = (64-query tile, head, key chunk [kbeg, kbeg + chunk)).
-// With one chunk the normalised output goes straight to `out` (or in fp32 to
-// co.ctx with the log normaliser to co.lse); with several, the chunk's
-// unnormalised O and its (running max, sum) go to o_part/ml_part and
-// k_attn_combine merges them.
-// kApprox: the approximate context update instead (DyLLM's saliency-aware
-// approximate attention): the query tiles are those of the all-rows map, each
-// row's cached query is read at its position, the keys and values are the
-// active rows' previous keys and value changes (packed, a.key_off / a.key_cnt),
-// and the softmax has the row's cached normaliser in place of the running one:
-// C_new = C_cached + sum_j 2^(s_j - lse2) dV_j, written for non-active rows.
 // Waves per SIMD the key-chunk kernel is built for: 3 (168 VGPRs, no
 // spills, against 184 and 2 waves left to the compiler) lets the softmax
 // vector work of one wave overlap the matrix-core work of the others; 0:
@@ -232,6 +221,18 @@ __device__ __forceinline__ int unit_on_xcd(int pq, int xcd, int n_units) {
 #else
 #define DTSK_ATTN_MFMA_BOUNDS __launch_bounds__(256)
 #endif
+
+// One workgroup = (64-query tile, head, key chunk [kbeg, kbeg + chunk)).
+// With one chunk the normalised output goes straight to `out` (or in fp32 to
+// co.ctx with the log normaliser to co.lse); with several, the chunk's
+// unnormalised O and its (running max, sum) go to o_part/ml_part and
+// k_attn_combine merges them.
+// kApprox: the approximate context update instead (DyLLM's saliency-aware
+// approximate attention): the query tiles are those of the all-rows map, each
+// row's cached query is read at its position, the keys and values are the
+// active rows' previous keys and value changes (packed, a.key_off / a.key_cnt),
+// and the softmax has the row's cached normaliser in place of the running one:
+// C_new = C_cached + sum_j 2^(s_j - lse2) dV_j, written for non-active rows.
 template <bool kApprox>
 __global__ DTSK_ATTN_MFMA_BOUNDS void k_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
                                                    const uint16_t* __restrict__ Vc,
