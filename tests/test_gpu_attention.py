@@ -181,3 +181,54 @@ def test_fp32_partial_attn_lse_matches_oracle():
         y, _, _, o_lse = E.layer_parts(host(x0[b])[rows[b]], rows[b], lw_np, K, V, n, dims)
         assert row_rel_err(xg[off[b]:off[b + 1]], y) <= 1e-5, f"sequence {b}"
         assert lse_err(lg[off[b]:off[b + 1]], o_lse) <= 1e-5, f"sequence {b}"
+
+
+@pytest.mark.parametrize("keep", [1.0, 0.25])
+def test_key_chunk_attention_with_jumping_scores(keep):
+    """Beyond 1024 keys the key-chunk kernel runs (k_attn_mfma), its softmax
+    rescaled lazily: a query's reference max moves only when a tile brings a
+    score more than 8 (log2 units) above it, and the probabilities of the
+    other tiles stay relative to the old max (up to 2^8).  Cached keys that
+    are exactly zero up to position 700 and 15 times the usual size after it
+    make every query's max jump by more than 8 inside a key chunk and then
+    drift by less; the layer output and the log normalisers still match the
+    oracle, a ragged sequence (its last tile masked) included."""
+    import dynamic_token_skipping_amd as D
+    lens, S_l = (1600, 1111), 1600
+    B = len(lens)
+    m = workloads.make_model(DIMS, 41, "bf16", "cuda")
+    g = torch.Generator(device="cuda").manual_seed(42)
+    kscale = torch.full((1, S_l, 1), 15.0 * 0.5, device="cuda")
+    kscale[:, :700] = 0.0
+    kc0 = (torch.randn((B, S_l, DIMS.d), generator=g, device="cuda") * kscale).to(torch.bfloat16)
+    vc0 = torch.randn((B, S_l, DIMS.d), generator=g, device="cuda").to(torch.bfloat16)
+    x0 = torch.randn((B, S_l, DIMS.d), generator=g, device="cuda")
+    dims = D.make_dims(B, S_l, DIMS.d, DIMS.n_heads, DIMS.head_dim, DIMS.d_ffn, DIMS.vocab, 1, "bf16")
+    ws = D.workspace(dims, B * S_l)
+    seq_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    lw_np = {k: host(v) for k, v in m["layers"][0].items()}
+    sel = D.SelectionTensors(B, S_l)
+    rows = []
+    for b, n in enumerate(lens):
+        r = np.unique(np.linspace(0, n - 1, E.keep_count(keep, n)).round().astype(np.int64))
+        rows.append(r)
+        sel.sel_idx[b, :len(r)] = torch.as_tensor(r, dtype=torch.int32)
+        sel.sel_count[b] = len(r)
+    off = np.concatenate([[0], np.cumsum([len(r) for r in rows])])
+    sel.row_off.copy_(torch.as_tensor(off, dtype=torch.int32))
+    R = int(off[-1])
+    x = torch.cat([x0[b, torch.as_tensor(rows[b], device="cuda")] for b in range(B)]).contiguous()
+    kc, vc = kc0.clone(), vc0.clone()
+    lse = torch.full((R, DIMS.n_heads), float("nan"), dtype=torch.float32, device="cuda")
+    D.dl_partial_attn(dims, m["layers"][0], x, sel, seq_len, R, kc, vc, ws, lse=lse)
+    torch.cuda.synchronize()
+    xg, lg = host(x), host(lse)
+    for b, n in enumerate(lens):
+        K, V = host(kc0[b, :n]), host(vc0[b, :n])
+        xb = host(x0[b])[rows[b]]
+        _, _, ctx, o_lse = E.layer_parts(xb, rows[b], lw_np, K, V, n, DIMS)
+        # the sub-block adds Wo(attention) to x: compare that increment itself
+        # (bf16 rounding of q, K and V alone accounts for about 1% of it here)
+        att = ctx @ np.asarray(lw_np["wo"], np.float64).T
+        assert row_rel_err(xg[off[b]:off[b + 1]] - xb, att) <= TOL, f"sequence {b}"
+        assert lse_err(lg[off[b]:off[b + 1]], o_lse) <= TOL, f"sequence {b}"
