@@ -183,27 +183,42 @@ def test_fp32_partial_attn_lse_matches_oracle():
         assert lse_err(lg[off[b]:off[b + 1]], o_lse) <= 1e-5, f"sequence {b}"
 
 
-@pytest.mark.parametrize("keep", [1.0, 0.25])
-def test_key_chunk_attention_with_jumping_scores(keep):
-    """Beyond 1024 keys the key-chunk kernel runs (k_attn_mfma), its softmax
-    rescaled lazily: a query's reference max moves only when a tile brings a
-    score more than 8 (log2 units) above it, and the probabilities of the
-    other tiles stay relative to the old max (up to 2^8).  Cached keys that
-    are exactly zero up to position 700 and 15 times the usual size after it
-    make every query's max jump by more than 8 inside a key chunk and then
-    drift by less; the layer output and the log normalisers still match the
-    oracle, a ragged sequence (its last tile masked) included."""
+# (model, sequence lengths, cached keys zero below this position, key size
+# factor after it).  keep < 1, so that most keys stay the cached ones (a
+# selected row's key is recomputed); the scores then reach 23-31 (log2
+# units) and each case sees a few hundred jumps of more than 8 and many
+# smaller rises, with about 1% of the increment from bf16 rounding alone
+JUMP_CASES = {
+    "key_chunks": (DIMS, (1600, 1111), 700, 15.0),     # > 1024 keys: k_attn_mfma, keys in chunks
+    "rows_16q": (DIMS, (1000, 777), 400, 15.0),        # k_attn_rows, 16 queries x 8 key parts
+    "rows_64q": (DIMS32, (900, 333), 400, 7.0),        # k_attn_rows, 64 queries x 2 key parts
+}
+
+
+@pytest.mark.parametrize("case,keep", [("key_chunks", 0.5), ("key_chunks", 0.25), ("rows_16q", 0.25),
+                                       ("rows_64q", 0.5)])
+def test_attention_with_jumping_scores(case, keep):
+    """The attention kernels rescale their softmax lazily: a query's
+    reference max moves only when a tile brings a score more than 8 (log2
+    units) above it, and the probabilities of the other tiles stay relative
+    to the old max (up to 2^8).  Cached keys that are exactly zero up to a
+    position and a few times the usual size after it make every query's max
+    jump by more than 8 inside a key range and then drift by less; the
+    attention increment of each row and the log normalisers still match the
+    oracle, ragged sequences (a last tile masked, or keys all zero) included.
+    Each case drives one kernel shape (at keep 0.5 the key-chunk kernel runs
+    in one chunk over 1356 rows, at keep 0.25 in chunks merged afterwards)."""
     import dynamic_token_skipping_amd as D
-    lens, S_l = (1600, 1111), 1600
-    B = len(lens)
-    m = workloads.make_model(DIMS, 41, "bf16", "cuda")
+    dm, lens, zero_until, kmul = JUMP_CASES[case]
+    S_l, B = max(lens), len(lens)
+    m = workloads.make_model(dm, 41, "bf16", "cuda")
     g = torch.Generator(device="cuda").manual_seed(42)
-    kscale = torch.full((1, S_l, 1), 15.0 * 0.5, device="cuda")
-    kscale[:, :700] = 0.0
-    kc0 = (torch.randn((B, S_l, DIMS.d), generator=g, device="cuda") * kscale).to(torch.bfloat16)
-    vc0 = torch.randn((B, S_l, DIMS.d), generator=g, device="cuda").to(torch.bfloat16)
-    x0 = torch.randn((B, S_l, DIMS.d), generator=g, device="cuda")
-    dims = D.make_dims(B, S_l, DIMS.d, DIMS.n_heads, DIMS.head_dim, DIMS.d_ffn, DIMS.vocab, 1, "bf16")
+    kscale = torch.full((1, S_l, 1), kmul * 0.5, device="cuda")
+    kscale[:, :zero_until] = 0.0
+    kc0 = (torch.randn((B, S_l, dm.d), generator=g, device="cuda") * kscale).to(torch.bfloat16)
+    vc0 = torch.randn((B, S_l, dm.d), generator=g, device="cuda").to(torch.bfloat16)
+    x0 = torch.randn((B, S_l, dm.d), generator=g, device="cuda")
+    dims = D.make_dims(B, S_l, dm.d, dm.n_heads, dm.head_dim, dm.d_ffn, dm.vocab, 1, "bf16")
     ws = D.workspace(dims, B * S_l)
     seq_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
     lw_np = {k: host(v) for k, v in m["layers"][0].items()}
@@ -219,14 +234,14 @@ def test_key_chunk_attention_with_jumping_scores(keep):
     R = int(off[-1])
     x = torch.cat([x0[b, torch.as_tensor(rows[b], device="cuda")] for b in range(B)]).contiguous()
     kc, vc = kc0.clone(), vc0.clone()
-    lse = torch.full((R, DIMS.n_heads), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((R, dm.n_heads), float("nan"), dtype=torch.float32, device="cuda")
     D.dl_partial_attn(dims, m["layers"][0], x, sel, seq_len, R, kc, vc, ws, lse=lse)
     torch.cuda.synchronize()
     xg, lg = host(x), host(lse)
     for b, n in enumerate(lens):
         K, V = host(kc0[b, :n]), host(vc0[b, :n])
         xb = host(x0[b])[rows[b]]
-        _, _, ctx, o_lse = E.layer_parts(xb, rows[b], lw_np, K, V, n, DIMS)
+        _, _, ctx, o_lse = E.layer_parts(xb, rows[b], lw_np, K, V, n, dm)
         # the sub-block adds Wo(attention) to x: compare that increment itself
         # (bf16 rounding of q, K and V alone accounts for about 1% of it here)
         att = ctx @ np.asarray(lw_np["wo"], np.float64).T
